@@ -1,0 +1,252 @@
+"""CPU oracle for the AsyncTLS two-level sparse-attention decode operator.
+
+TEST INFRASTRUCTURE ONLY. Only the test suite, the package smoke check and
+the benchmark's CPU-baseline leg may import this module. The product path
+(the HIP library and its Python binding) never imports or calls it.
+
+Plain, slow, fp64 NumPy. Every function works on one unit u = (batch b,
+KV head g) and follows the method's steps in the order the pages give:
+
+1. The KV cache of a unit is cut into fixed-size token blocks
+   [AsyncTLS, gist.science/de explainer, section 2.A "Stufe 1";
+   gist.science/es explainer, section 2.A item 1].
+2. Each block is summarised by its channelwise key maximum and minimum
+   [gist.science/de, section 2.A "Stufe 1": Max/Min der Keys].
+3. Block importance is the Quest upper bound of q.k over the block,
+   sum_c max(q_c*Kmax_c, q_c*Kmin_c) [gist.science/es, section 2.A item 1,
+   "based on Quest"; Quest is in the "Builds on" list of the mlsanity index
+   page]. The same bound written as the dense product q+ . Kmax + q- . Kmin
+   (the GEMM form the pages introduce for shared-KV heads; gist.science/de
+   section 2.A "Optimierung", gist.science/es section 2.A "Innovacion") is
+   given by ``quest_bound_gemm``; the two are the same number up to rounding.
+4. The top K_b blocks are kept [gist.science/es, section 2.A item 1].
+5. Inside the kept blocks, tokens are scored on a few label channels of q
+   and k (Double Sparsity) and the top K_t tokens are kept
+   [gist.science/de, section 2.A "Stufe 2"; gist.science/es section 2.A
+   item 2].
+6. Exact softmax attention runs over the kept tokens [gist.science/es,
+   section 2.A item 2, "final attention"].
+
+Readings where the pages are silent (all fixed here, none printed there):
+* query heads that share one KV head are combined by the MAX over the group,
+  for both block and token scores; one selection per (batch, KV head);
+* top-k ties go to the lower index, and results are returned ascending;
+* the last, partial block is summarised over its valid tokens only; K_b and
+  K_t clamp to what exists, unused output slots hold -1;
+* label scores are the plain bf16-valued dot product on the label channels
+  (no quantisation);
+* attention logits are sm_scale * q.k; out is fp64 here (fp32 on the GPU);
+  lse is the natural-log logsumexp of those logits.
+
+Offload (``offload_*``): the fine stage of step t runs over the blocks
+selected at step t-1 while step t's new blocks are fetched; only the set
+difference of consecutive block selections is transferred
+[gist.science/de, section 2.B; gist.science/es, section 2.B].
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "bf16_to_f64", "n_blocks", "block_meta", "append_meta", "quest_bound",
+    "quest_bound_gemm", "block_scores", "topk_stable", "candidate_tokens",
+    "label_scores", "attend", "select_tokens_unit", "decode_unit",
+    "decode_all", "offload_delta", "offload_run",
+]
+
+
+# ---------------------------------------------------------------- bf16 input
+def bf16_to_f64(bits) -> np.ndarray:
+    """Exact value of bf16 bit patterns (uint16) as float64."""
+    b = np.asarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+# ------------------------------------------------------------ step 1: blocks
+def n_blocks(n: int, bs: int) -> int:
+    """Number of blocks covering n tokens: block j holds [j*bs, min((j+1)*bs, n))."""
+    return -(-n // bs)
+
+
+# ---------------------------------------------------------- step 2: metadata
+def block_meta(K: np.ndarray, n: int, bs: int):
+    """Channelwise max and min of the keys of every block, over valid tokens.
+
+    K: [>=n, d] float64 keys of one unit. Returns (kmax, kmin), each [nb, d]."""
+    nb = n_blocks(n, bs)
+    d = K.shape[1]
+    kmax = np.empty((nb, d))
+    kmin = np.empty((nb, d))
+    for j in range(nb):
+        rows = K[j * bs: min((j + 1) * bs, n)]
+        kmax[j] = rows.max(axis=0)
+        kmin[j] = rows.min(axis=0)
+    return kmax, kmin
+
+
+def append_meta(kmax: np.ndarray, kmin: np.ndarray, k: np.ndarray, pos: int, bs: int):
+    """Metadata after appending key k at position pos (incremental update):
+    a new block starts with k as both bounds, otherwise the tail block's
+    bounds widen to include k. Returns new (kmax, kmin) arrays."""
+    j = pos // bs
+    kmax = kmax.copy()
+    kmin = kmin.copy()
+    if pos % bs == 0:
+        if j != kmax.shape[0]:
+            raise ValueError("a new block must be appended right after the last one")
+        kmax = np.vstack([kmax, k[None, :]])
+        kmin = np.vstack([kmin, k[None, :]])
+    else:
+        kmax[j] = np.maximum(kmax[j], k)
+        kmin[j] = np.minimum(kmin[j], k)
+    return kmax, kmin
+
+
+# ----------------------------------------------------- step 3: block scoring
+def quest_bound(q: np.ndarray, kmax: np.ndarray, kmin: np.ndarray) -> np.ndarray:
+    """Quest upper bound, elementwise definition.
+
+    q: [G, d], kmax/kmin: [nb, d]. UB[h, j] = sum_c max(q[h,c]*kmax[j,c], q[h,c]*kmin[j,c])."""
+    G, nb = q.shape[0], kmax.shape[0]
+    ub = np.empty((G, nb))
+    for h in range(G):
+        ub[h] = np.maximum(q[h] * kmax, q[h] * kmin).sum(axis=1)
+    return ub
+
+
+def quest_bound_gemm(q: np.ndarray, kmax: np.ndarray, kmin: np.ndarray) -> np.ndarray:
+    """The same bound as one dense product: [q+, q-] @ [kmax; kmin]^T with
+    q+ = max(q, 0) and q- = min(q, 0)."""
+    qq = np.concatenate([np.maximum(q, 0.0), np.minimum(q, 0.0)], axis=1)   # [G, 2d]
+    kk = np.concatenate([kmax, kmin], axis=1)                               # [nb, 2d]
+    return qq @ kk.T
+
+
+def block_scores(q: np.ndarray, kmax: np.ndarray, kmin: np.ndarray) -> np.ndarray:
+    """Block score of a KV head shared by the query heads q [G, d]: the
+    largest Quest bound over the group."""
+    return quest_bound(q, kmax, kmin).max(axis=0)
+
+
+# --------------------------------------------------------- steps 4, 5: top-k
+def topk_stable(scores: np.ndarray, k: int) -> np.ndarray:
+    """Indices of the min(k, len) largest scores; on equal scores the lower
+    index wins. Returned in ascending index order (int64)."""
+    s = np.asarray(scores, dtype=np.float64)
+    k = min(int(k), s.shape[0])
+    order = np.argsort(-s, kind="stable")      # stable: equal keys keep index order
+    return np.sort(order[:k])
+
+
+def candidate_tokens(blk_idx: np.ndarray, n: int, bs: int) -> np.ndarray:
+    """Valid token positions of the kept blocks, ascending."""
+    toks = [np.arange(j * bs, min((j + 1) * bs, n)) for j in np.sort(np.asarray(blk_idx))]
+    return np.concatenate(toks) if toks else np.zeros(0, dtype=np.int64)
+
+
+def label_scores(q: np.ndarray, K_rows: np.ndarray, label_ch: np.ndarray) -> np.ndarray:
+    """Approximate token scores on the label channels: for each key row,
+    the largest over the group of sum_{c in label_ch} q[h,c]*k[c]."""
+    qc = q[:, label_ch]                  # [G, r]
+    kc = K_rows[:, label_ch]             # [T, r]
+    return (qc @ kc.T).max(axis=0)
+
+
+# ------------------------------------------------------ step 6: attention
+def attend(q: np.ndarray, K_sel: np.ndarray, V_sel: np.ndarray, sm_scale: float):
+    """Exact softmax attention of each query head over the selected rows.
+
+    q [G, d_k], K_sel [T, d_k], V_sel [T, d_v]. Returns (out [G, d_v], lse [G])
+    with logits z = sm_scale * q.k and lse = log(sum exp z)."""
+    G = q.shape[0]
+    if K_sel.shape[0] == 0:
+        return np.zeros((G, V_sel.shape[1])), np.full(G, -np.inf)
+    z = sm_scale * (q @ K_sel.T)                         # [G, T]
+    m = z.max(axis=1, keepdims=True)
+    e = np.exp(z - m)
+    l = e.sum(axis=1, keepdims=True)
+    out = (e @ V_sel) / l
+    lse = (m + np.log(l))[:, 0]
+    return out, lse
+
+
+# -------------------------------------------------------- whole-unit pipeline
+def select_tokens_unit(q, K, n, bs, blk_idx, label_ch, k_tokens):
+    """Token stage given a block set: candidates, label scores, top-K_t.
+    Returns (tok_idx ascending positions, cand positions, label scores of cand)."""
+    cand = candidate_tokens(blk_idx, n, bs)
+    s_tok = label_scores(q, K[cand], label_ch)
+    keep = topk_stable(s_tok, k_tokens)
+    return cand[keep], cand, s_tok
+
+
+def decode_unit(q, K, V, n, bs, k_blocks, label_ch, k_tokens, sm_scale, meta=None):
+    """One decode step of one unit over its first n tokens (the appended
+    token included). q [G, d_k] float64; K [>=n, d_k], V [>=n, d_v] float64.
+
+    Returns a dict with the intermediate results of every stage."""
+    kmax, kmin = block_meta(K, n, bs) if meta is None else meta
+    s_blk = block_scores(q, kmax, kmin)
+    blk = topk_stable(s_blk, k_blocks)
+    tok, cand, s_tok = select_tokens_unit(q, K, n, bs, blk, label_ch, k_tokens)
+    out, lse = attend(q, K[tok], V[tok], sm_scale)
+    return {"blk_score": s_blk, "blk_idx": blk, "cand": cand, "tok_score": s_tok,
+            "tok_idx": tok, "out": out, "lse": lse, "kmax": kmax, "kmin": kmin}
+
+
+def decode_all(q_bits, K_bits, V_bits, ctx_len, n_kv_heads, bs, k_blocks, label_ch,
+               k_tokens, sm_scale, units=None):
+    """Decode step over all (or the listed) units of a batch.
+
+    q_bits [B, Hq, d_k]; K_bits [B, Hkv, cap, d_k]; V_bits [B, Hkv, cap, d_v],
+    or the int d_v when values are the first d_v key dims (absorbed MLA);
+    ctx_len [B]; label_ch [Hkv, r]. Query head h reads KV head h // G.
+    Returns {(b, g): decode_unit result}."""
+    B, Hq, _ = q_bits.shape
+    G = Hq // n_kv_heads
+    res = {}
+    todo = units if units is not None else [(b, g) for b in range(B) for g in range(n_kv_heads)]
+    for b, g in todo:
+        n = int(ctx_len[b])
+        q = bf16_to_f64(q_bits[b, g * G:(g + 1) * G])
+        K = bf16_to_f64(K_bits[b, g, :n])
+        if isinstance(V_bits, (int, np.integer)):
+            V = K[:, : int(V_bits)]
+        else:
+            V = bf16_to_f64(V_bits[b, g, :n])
+        res[(b, g)] = decode_unit(q, K, V, n, bs, k_blocks, np.asarray(label_ch[g]),
+                                  k_tokens, sm_scale)
+    return res
+
+
+# ------------------------------------------------------------------ offload
+def offload_delta(prev_blocks, cur_blocks) -> np.ndarray:
+    """Blocks that must cross the host link at a step: selected now, not
+    resident from the previous step (set difference, ascending)."""
+    return np.setdiff1d(np.asarray(cur_blocks), np.asarray(prev_blocks))
+
+
+def offload_run(steps, bs, d_k, d_v, v_alias=False):
+    """Lagged offload schedule over a sequence of decode steps of one unit.
+
+    ``steps`` is a list of (q [G,d_k], K [>=n,d_k], V [>=n,d_v], n, k_blocks,
+    label_ch, k_tokens, sm_scale). Step t selects S_b(t) from its own query,
+    but its token stage and attention run over the resident set R(t) =
+    S_b(t-1) (R(0) = S_b(0): the cold start is a synchronous fill).
+    Bytes per transferred block = bs * (d_k + d_v) * 2 (bf16; d_k only when
+    values alias keys). Returns a list of per-step dicts."""
+    row_bytes = (d_k if v_alias else d_k + d_v) * 2
+    out = []
+    prev = None
+    for t, (q, K, V, n, k_blocks, label_ch, k_tokens, sm_scale) in enumerate(steps):
+        kmax, kmin = block_meta(K, n, bs)
+        cur = topk_stable(block_scores(q, kmax, kmin), k_blocks)
+        resident = cur if prev is None else prev
+        tok, _, _ = select_tokens_unit(q, K, n, bs, resident, label_ch, k_tokens)
+        o, lse = attend(q, K[tok], V[tok], sm_scale)
+        delta = cur if prev is None else offload_delta(prev, cur)
+        out.append({"sel": cur, "resident": resident, "delta": delta,
+                    "delta_bytes": int(len(delta)) * bs * row_bytes,
+                    "cold": prev is None, "tok_idx": tok, "out": o, "lse": lse})
+        prev = cur
+    return out

@@ -1,0 +1,312 @@
+"""Pins of the CPU oracle against facts fixed outside the oracle itself:
+hand-worked examples, algebraic identities, the Quest bound property,
+special cases that reduce to exact top-k or dense attention (checked against
+torch's scaled_dot_product_attention), brute-force selection, and the
+offload delta count. CPU only."""
+import itertools
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from hierarchical_sparse_attention_block_amd import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _read_golden(name):
+    vals = {}
+    for line in open(os.path.join(GOLDEN, name)):
+        line = line.split("#", 1)[0].strip()
+        if not line:
+            continue
+        k, v = [x.strip() for x in line.split("=", 1)]
+        rows = []
+        for part in v.split(";"):
+            rows.append([eval(t, {"exp": math.exp, "log": math.log}) for t in part.split()])
+        vals[k] = rows if len(rows) > 1 else rows[0]
+    return vals
+
+
+def _bf16(x, rng_=None):
+    """float64 values that are exactly representable in bf16."""
+    return O.bf16_to_f64(W.f32_to_bf16_bits(np.asarray(x, dtype=np.float32)))
+
+
+def _rand_unit(seed, G, d, n, dv=None, scale=1.0):
+    r = np.random.default_rng(seed)
+    q = _bf16(r.standard_normal((G, d)))
+    K = _bf16(scale * r.standard_normal((n, d)))
+    V = _bf16(r.standard_normal((n, dv or d)))
+    return q, K, V
+
+
+# ------------------------------------------------------------ golden examples
+def test_worked_example_every_stage():
+    g = _read_golden("worked_example.txt")
+    q = np.array([g["q0"], g["q1"]], dtype=np.float64)
+    K = np.array([g[f"k{i}"] for i in range(5)], dtype=np.float64)
+    V = np.array([g[f"v{i}"] for i in range(5)], dtype=np.float64)
+    kmax, kmin = O.block_meta(K, 5, 2)
+    np.testing.assert_array_equal(kmax, np.array(g["kmax"]))
+    np.testing.assert_array_equal(kmin, np.array(g["kmin"]))
+    ub = O.quest_bound(q, kmax, kmin)
+    np.testing.assert_array_equal(ub, np.array([g["ub0"], g["ub1"]]))
+    r = O.decode_unit(q, K, V, 5, 2, 2, np.array([0]), 2, 1.0)
+    np.testing.assert_array_equal(r["blk_score"], g["blk_score"])
+    np.testing.assert_array_equal(r["blk_idx"], g["blk_idx"])
+    np.testing.assert_array_equal(r["cand"], g["cand"])
+    np.testing.assert_array_equal(r["tok_score"], g["tok_score"])
+    np.testing.assert_array_equal(r["tok_idx"], g["tok_idx"])
+    np.testing.assert_allclose(r["out"], np.array([g["out0"], g["out1"]]), rtol=0, atol=1e-15)
+    np.testing.assert_allclose(r["lse"], [g["lse0"][0], g["lse1"][0]], rtol=1e-15)
+
+
+def test_tie_example_lower_index_wins():
+    g = _read_golden("tie_example.txt")
+    q = np.array([[g["q0"]]], dtype=np.float64)
+    K = np.array(g["k"], dtype=np.float64)[:, None]
+    kmax, kmin = O.block_meta(K, 6, 1)
+    s = O.block_scores(q, kmax, kmin)
+    np.testing.assert_array_equal(O.topk_stable(s, 3), g["blk_idx"])
+    np.testing.assert_array_equal(O.topk_stable(s, 4), g["blk_idx_k4"])
+    np.testing.assert_array_equal(O.topk_stable(s, 5), g["blk_idx_k5"])
+
+
+# ---------------------------------------------------------- metadata (step 2)
+@pytest.mark.parametrize("n,bs", [(1, 16), (15, 16), (16, 16), (17, 16), (100, 16), (65, 32), (7, 1)])
+def test_block_meta_brackets_every_key(n, bs):
+    """Every valid key lies inside its block's [kmin, kmax], and both bounds
+    are attained by some key of the block (closed form of channelwise max/min)."""
+    _, K, _ = _rand_unit(n * 7 + bs, 1, 8, n)
+    kmax, kmin = O.block_meta(K, n, bs)
+    assert kmax.shape[0] == -(-n // bs)
+    for t in range(n):
+        j = t // bs
+        assert np.all(kmin[j] <= K[t]) and np.all(K[t] <= kmax[j])
+    for j in range(kmax.shape[0]):
+        rows = K[j * bs: min(n, (j + 1) * bs)]
+        assert np.all((rows == kmax[j]).any(axis=0)) and np.all((rows == kmin[j]).any(axis=0))
+
+
+@pytest.mark.parametrize("bs", [1, 4, 16])
+def test_incremental_meta_equals_bulk(bs):
+    _, K, _ = _rand_unit(bs, 1, 16, 70)
+    kmax, kmin = O.block_meta(K, 1, bs)
+    for pos in range(1, 70):
+        kmax, kmin = O.append_meta(kmax, kmin, K[pos], pos, bs)
+        bmax, bmin = O.block_meta(K, pos + 1, bs)
+        np.testing.assert_array_equal(kmax, bmax)
+        np.testing.assert_array_equal(kmin, bmin)
+
+
+# ------------------------------------------------------- block bound (step 3)
+@pytest.mark.parametrize("seed", range(4))
+def test_gemm_form_equals_elementwise_quest_bound(seed):
+    q, K, _ = _rand_unit(seed, 5, 24, 203)
+    kmax, kmin = O.block_meta(K, 203, 16)
+    a = O.quest_bound(q, kmax, kmin)
+    b = O.quest_bound_gemm(q, kmax, kmin)
+    np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("n,bs,scale", [(200, 16, 1.0), (97, 8, 3.0), (33, 32, 1.0)])
+def test_bound_dominates_true_block_max(n, bs, scale):
+    """Quest property: every head's bound is >= the largest q.k in the block,
+    so the group score is >= every head's true block maximum."""
+    q, K, _ = _rand_unit(n + bs, 4, 32, n, scale=scale)
+    kmax, kmin = O.block_meta(K, n, bs)
+    ub = O.quest_bound(q, kmax, kmin)
+    s = O.block_scores(q, kmax, kmin)
+    for j in range(kmax.shape[0]):
+        true = q @ K[j * bs: min(n, (j + 1) * bs)].T     # [G, tokens]
+        assert np.all(ub[:, j] >= true.max(axis=1) - 1e-12)
+        assert s[j] >= true.max() - 1e-12
+
+
+def test_bound_is_tight_for_a_single_token_block():
+    """With one token per block, kmax = kmin = k and the bound is exactly q.k."""
+    q, K, _ = _rand_unit(9, 3, 16, 40)
+    kmax, kmin = O.block_meta(K, 40, 1)
+    np.testing.assert_allclose(O.quest_bound(q, kmax, kmin), q @ K.T, rtol=1e-13, atol=1e-13)
+
+
+@pytest.mark.parametrize("G", [1, 4])
+def test_block1_reduces_to_exact_token_topk(G):
+    """Block size 1: the block stage is an exact top-K over tokens of
+    max_h q_h.k, which we rank with an independent full sort."""
+    q, K, V = _rand_unit(G, G, 16, 300)
+    r = O.decode_unit(q, K, V, 300, 1, 37, np.arange(4), 10, 0.25)
+    true = (q @ K.T).max(axis=0)
+    want = np.sort(np.lexsort((np.arange(300), -true))[:37])
+    np.testing.assert_array_equal(r["blk_idx"], want)
+
+
+# ------------------------------------------------------------- top-k (4, 5)
+def test_topk_stable_brute_force_with_ties():
+    """Exhaustive check on small integer scores with many ties: index i is
+    kept iff fewer than k indices beat it, where j beats i when s_j > s_i or
+    (s_j == s_i and j < i)."""
+    rng = np.random.default_rng(0)
+    for n in range(1, 9):
+        for trial in range(30):
+            s = rng.integers(-2, 3, size=n).astype(np.float64)
+            for k in range(0, n + 3):
+                got = O.topk_stable(s, k)
+                want = [i for i in range(n)
+                        if sum((s[j] > s[i]) or (s[j] == s[i] and j < i) for j in range(n)) < k]
+                assert list(got) == want
+
+
+def test_topk_matches_enumeration_of_subsets():
+    """The kept set maximises the score sum over all subsets of size k and,
+    among maximisers, is the lexicographically smallest index set."""
+    s = np.array([3., 1., 3., 2., 2., 0., 3.])
+    for k in range(len(s) + 1):
+        best = max(itertools.combinations(range(len(s)), k),
+                   key=lambda c: (sum(s[list(c)]), [-i for i in c]))
+        assert tuple(O.topk_stable(s, k)) == best
+
+
+# --------------------------------------------------------- token stage (5)
+def test_label_score_is_exact_dot_when_keys_live_on_label_channels():
+    """If keys are zero outside the label channels, the label score equals
+    the exact max_h q_h.k (full-vector dot), whatever the channel order."""
+    rng = np.random.default_rng(3)
+    q, K, _ = _rand_unit(3, 4, 32, 50)
+    ch = np.sort(rng.choice(32, size=6, replace=False))
+    Km = np.zeros_like(K)
+    Km[:, ch] = K[:, ch]
+    np.testing.assert_allclose(O.label_scores(q, Km, ch), (q @ Km.T).max(axis=0), rtol=1e-13, atol=1e-13)
+
+
+def test_full_label_set_equals_exact_scores():
+    q, K, _ = _rand_unit(4, 4, 16, 64)
+    np.testing.assert_allclose(O.label_scores(q, K, np.arange(16)), (q @ K.T).max(axis=0),
+                               rtol=1e-13, atol=1e-13)
+
+
+def test_candidates_cover_valid_tokens_of_kept_blocks():
+    c = O.candidate_tokens(np.array([4, 0, 2]), 37, 8)
+    np.testing.assert_array_equal(c, list(range(0, 8)) + list(range(16, 24)) + list(range(32, 37)))
+
+
+# ------------------------------------------------------------ attention (6)
+def _sdpa(q, K, V, scale):
+    qt = torch.tensor(q)[None, :, None, :]                     # [1, G, 1, d]
+    kt = torch.tensor(K)[None, None].expand(1, q.shape[0], -1, -1)
+    vt = torch.tensor(V)[None, None].expand(1, q.shape[0], -1, -1)
+    out = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, scale=scale)
+    lse = torch.logsumexp(scale * (torch.tensor(q) @ torch.tensor(K).T), dim=1)
+    return out[0, :, 0].numpy(), lse.numpy()
+
+
+@pytest.mark.parametrize("n,bs,G,dk,dv", [(1, 16, 4, 16, 16), (37, 16, 4, 32, 32), (64, 8, 2, 24, 16), (70, 32, 8, 40, 32)])
+def test_dense_limit_equals_sdpa(n, bs, G, dk, dv):
+    """K_b >= number of blocks and K_t >= n keep every token: the operator is
+    then dense attention, checked against torch's SDPA in fp64."""
+    q, K, V = _rand_unit(n + G, G, dk, n, dv=dv)
+    r = O.decode_unit(q, K, V, n, bs, 10 ** 6, np.arange(min(4, dk)), 10 ** 6, 1 / math.sqrt(dk))
+    np.testing.assert_array_equal(r["tok_idx"], np.arange(n))
+    out, lse = _sdpa(q, K, V, 1 / math.sqrt(dk))
+    np.testing.assert_allclose(r["out"], out, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(r["lse"], lse, rtol=1e-13)
+
+
+def test_decode_all_maps_query_heads_to_kv_heads():
+    """GQA grouping: query head h attends KV head h // G. With every token
+    kept, decode_all equals SDPA with K/V repeated per group (an independent
+    formulation of the same mapping)."""
+    B, Hq, Hkv, d, n = 2, 6, 3, 16, 21
+    rng = np.random.default_rng(11)
+    qb = W.f32_to_bf16_bits(rng.standard_normal((B, Hq, d)).astype(np.float32))
+    Kb = W.f32_to_bf16_bits(rng.standard_normal((B, Hkv, 32, d)).astype(np.float32))
+    Vb = W.f32_to_bf16_bits(rng.standard_normal((B, Hkv, 32, d)).astype(np.float32))
+    ctx = np.array([n, n - 5])
+    res = O.decode_all(qb, Kb, Vb, ctx, Hkv, 4, 100, np.tile(np.arange(4), (Hkv, 1)), 100, 0.3)
+    q = torch.tensor(O.bf16_to_f64(qb))
+    K = torch.tensor(O.bf16_to_f64(Kb)).repeat_interleave(Hq // Hkv, dim=1)
+    V = torch.tensor(O.bf16_to_f64(Vb)).repeat_interleave(Hq // Hkv, dim=1)
+    for b in range(B):
+        nb_ = int(ctx[b])
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            q[b][:, None], K[b, :, :nb_], V[b, :, :nb_], scale=0.3)[:, 0]
+        got = np.concatenate([res[(b, g)]["out"] for g in range(Hkv)])
+        np.testing.assert_allclose(got, ref.numpy(), rtol=0, atol=1e-12)
+
+
+def test_lse_merges_disjoint_token_sets():
+    """lse is the true log-partition: attention over A u B equals the
+    lse-weighted merge of attention over A and over B."""
+    q, K, V = _rand_unit(5, 3, 16, 40)
+    oa, la = O.attend(q, K[:17], V[:17], 0.7)
+    ob, lb = O.attend(q, K[17:], V[17:], 0.7)
+    o, l = O.attend(q, K, V, 0.7)
+    M = np.logaddexp(la, lb)
+    np.testing.assert_allclose(M, l, rtol=1e-14)
+    np.testing.assert_allclose(oa * np.exp(la - M)[:, None] + ob * np.exp(lb - M)[:, None], o, atol=1e-14)
+
+
+def test_single_selected_token_returns_its_value():
+    q, K, V = _rand_unit(6, 2, 8, 10)
+    o, l = O.attend(q, K[3:4], V[3:4], 0.5)
+    np.testing.assert_array_equal(o, np.repeat(V[3:4], 2, axis=0))
+    np.testing.assert_allclose(l, 0.5 * (q @ K[3]), rtol=1e-15)
+
+
+# ------------------------------------------------------------ clamps, edges
+def test_budgets_clamp_to_what_exists():
+    q, K, V = _rand_unit(8, 2, 16, 20)
+    r = O.decode_unit(q, K, V, 20, 16, 5, np.arange(4), 999, 0.25)
+    np.testing.assert_array_equal(r["blk_idx"], [0, 1])
+    np.testing.assert_array_equal(r["tok_idx"], np.arange(20))
+
+
+# -------------------------------------------------------------- planted keys
+def test_planted_keys_survive_both_stages_tiny4k():
+    w = W.WORKLOADS["tiny4k"]
+    qb = W.queries(w)
+    kb, vb = W.unit_kv(w, 0, 0, qb)
+    knew, vnew = W.new_token(w)
+    K = O.bf16_to_f64(np.concatenate([kb, knew[0, :, :]]))
+    V = O.bf16_to_f64(np.concatenate([vb, vnew[0, :, :]]))
+    q = O.bf16_to_f64(qb[0])
+    lab = W.label_channels(w)[0]
+    r = O.decode_unit(q, K, V, w.ctx, w.block, w.k_blocks, lab, w.k_tokens, w.sm_scale)
+    pos, _ = W.planted_positions(w, 0, 0)
+    assert set(pos // w.block) <= set(r["blk_idx"])
+    assert set(pos) <= set(r["tok_idx"])
+    # margin: every planted block bound exceeds every unplanted block score
+    planted_blk = set(pos // w.block)
+    others = [s for j, s in enumerate(r["blk_score"]) if j not in planted_blk]
+    assert min(r["blk_score"][list(planted_blk)]) > 1.5 * max(others)
+
+
+# ------------------------------------------------------------------ offload
+def test_offload_delta_bytes_hand_sequence():
+    """Selections {1,2,3} -> {2,3,4} -> {2,3,4} -> {0,4,5}: the transfers are
+    the cold fill (3 blocks) then 1, 0 and 2 blocks. Bytes per block at
+    block=16, d_k=d_v=128 in bf16: 16*256*2 = 8192."""
+    assert list(O.offload_delta([1, 2, 3], [2, 3, 4])) == [4]
+    assert list(O.offload_delta([2, 3, 4], [2, 3, 4])) == []
+    assert list(O.offload_delta([2, 3, 4], [0, 4, 5])) == [0, 5]
+    rng = np.random.default_rng(1)
+    G, d, bs, n = 2, 8, 4, 32
+    K = _bf16(rng.standard_normal((n, d)))
+    V = _bf16(rng.standard_normal((n, d)))
+    qs = [_bf16(rng.standard_normal((G, d))) for _ in range(4)]
+    steps = [(qs[t], K, V, n, 3, np.arange(2), 6, 0.3) for t in range(4)]
+    res = O.offload_run(steps, bs, d, d)
+    for t, r in enumerate(res):
+        if t == 0:
+            assert r["cold"] and r["delta_bytes"] == 3 * bs * 2 * d * 2
+            np.testing.assert_array_equal(r["resident"], r["sel"])
+        else:
+            np.testing.assert_array_equal(r["resident"], res[t - 1]["sel"])
+            want = len(set(r["sel"]) - set(res[t - 1]["sel"]))
+            assert r["delta_bytes"] == want * bs * 2 * d * 2
+        # the token stage ran on the resident set only
+        assert set(np.asarray(r["tok_idx"]) // bs) <= set(r["resident"])
