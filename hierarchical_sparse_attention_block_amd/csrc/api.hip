@@ -1,0 +1,194 @@
+// C ABI of libhsab: argument checks, workspace layout and kernel sequencing.
+// The library never allocates, frees or synchronises; every call enqueues
+// its kernels on the caller's stream.
+#include <math.h>
+#include <string.h>
+
+#include "kernels.h"
+
+namespace hsab {
+
+static thread_local int g_last_hip = 0;
+
+Shape make_shape(const hsab_dims& d) {
+    Shape s;
+    s.B = d.batch; s.Hq = d.n_q_heads; s.Hkv = d.n_kv_heads;
+    s.G = d.n_kv_heads > 0 ? d.n_q_heads / d.n_kv_heads : 0;
+    s.dk = d.d_k; s.dv = d.d_v; s.valias = d.v_alias_k != 0;
+    s.bs = d.block; s.r = d.r; s.kb = d.k_blocks; s.kt = d.k_tokens; s.max_ctx = d.max_ctx;
+    s.nb_cap = d.block > 0 ? (d.max_ctx + d.block - 1) / d.block : 0;
+    s.sm_scale = d.sm_scale;
+    return s;
+}
+
+int attn_splits(const Shape& s) {
+    const int tps = s.valias ? MLA_TOK_PER_SPLIT : ATT_TOK_PER_SPLIT;
+    return (s.kt + tps - 1) / tps;
+}
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+WsLayout ws_layout(const Shape& s) {
+    WsLayout w;
+    size_t off = 0;
+    w.blk_score = off; off = align256(off + (size_t)s.B * s.Hkv * s.nb_cap * sizeof(float));
+    w.tok_score = off;   // unused: token scores live in LDS
+    w.part_ml = off;   off = align256(off + (size_t)s.B * s.Hq * attn_splits(s) * 2 * sizeof(float));
+    w.part_acc = off;  off = align256(off + (size_t)s.B * s.Hq * attn_splits(s) * s.dv * sizeof(float));
+    w.total = off;
+    return w;
+}
+
+// Shape checks shared by every entry point.
+static int check_dims(const hsab_dims* d) {
+    if (!d) return HSAB_EINVAL;
+    if (d->batch < 1 || d->n_kv_heads < 1 || d->n_q_heads < 1) return HSAB_EINVAL;
+    if (d->n_q_heads % d->n_kv_heads != 0) return HSAB_EINVAL;
+    const int G = d->n_q_heads / d->n_kv_heads;
+    if (G > MAX_G) return HSAB_EINVAL;
+    if (d->d_k < 16 || d->d_k > 1024 || d->d_k % 16 != 0) return HSAB_EINVAL;
+    if (d->d_v < 8 || d->d_v % 8 != 0) return HSAB_EINVAL;
+    if (d->v_alias_k && d->d_v > d->d_k) return HSAB_EINVAL;
+    if (d->block < 1 || d->max_ctx < 1) return HSAB_EINVAL;
+    if (d->r < 16 || d->r % 16 != 0 || d->r > MAX_R || d->r > d->d_k) return HSAB_EINVAL;
+    if (d->k_blocks < 1 || d->k_blocks > MAX_KB) return HSAB_EINVAL;
+    if ((long)d->k_blocks * d->block > MAX_CAND) return HSAB_EINVAL;
+    if (d->k_tokens < 1) return HSAB_EINVAL;
+    if ((d->max_ctx + d->block - 1) / d->block > MAX_NB) return HSAB_EINVAL;
+    if (!isfinite(d->sm_scale)) return HSAB_EINVAL;
+    return HSAB_OK;
+}
+
+static bool attend_supported(const Shape& s) {
+    if (s.valias) return false;
+    if (s.dk != s.dv) return false;
+    if (s.dk != 64 && s.dk != 128 && s.dk != 256) return false;
+    return s.G == 1 || s.G == 2 || s.G == 4 || s.G == 8;
+}
+
+static int hip_status(hipError_t e) {
+    if (e == hipSuccess) return HSAB_OK;
+    g_last_hip = (int)e;
+    return HSAB_EHIP;
+}
+
+}  // namespace hsab
+
+using namespace hsab;
+
+extern "C" {
+
+size_t hsab_workspace_bytes(const hsab_dims* dims) {
+    if (check_dims(dims) != HSAB_OK) return 0;
+    return ws_layout(make_shape(*dims)).total;
+}
+
+const char* hsab_status_string(int status) {
+    switch (status) {
+        case HSAB_OK: return "ok";
+        case HSAB_EINVAL: return "invalid argument";
+        case HSAB_EHIP: return "HIP launch or runtime error";
+        case HSAB_EUNSUPPORTED: return "shape not supported by the available kernels";
+        default: return "unknown status";
+    }
+}
+
+int hsab_last_hip_error(void) { return g_last_hip; }
+
+int hsab_build_meta(const hsab_dims* dims, const uint16_t* K, const int32_t* ctx_len,
+                    const int32_t* label_ch, uint16_t* meta, uint16_t* klabel, hipStream_t stream) {
+    int rc = check_dims(dims);
+    if (rc) return rc;
+    if (!K || !ctx_len || !label_ch || !meta || !klabel) return HSAB_EINVAL;
+    return hip_status(launch_build_meta(make_shape(*dims), K, ctx_len, label_ch, meta, klabel, stream));
+}
+
+int hsab_score_blocks(const hsab_dims* dims, const uint16_t* q, const uint16_t* meta,
+                      const int32_t* ctx_len, float* blk_score, hipStream_t stream) {
+    int rc = check_dims(dims);
+    if (rc) return rc;
+    if (!q || !meta || !ctx_len || !blk_score) return HSAB_EINVAL;
+    return hip_status(launch_block_score(make_shape(*dims), q, meta, ctx_len, blk_score, stream));
+}
+
+int hsab_select_blocks(const hsab_dims* dims, const uint16_t* q, const uint16_t* meta,
+                       const int32_t* ctx_len, int32_t* blk_idx, float* blk_score, void* ws,
+                       size_t ws_bytes, hipStream_t stream) {
+    int rc = check_dims(dims);
+    if (rc) return rc;
+    if (!q || !meta || !ctx_len || !blk_idx) return HSAB_EINVAL;
+    const Shape s = make_shape(*dims);
+    const WsLayout L = ws_layout(s);
+    float* scores = blk_score;
+    if (!scores) {
+        if (!ws || ws_bytes < L.total) return HSAB_EINVAL;
+        scores = reinterpret_cast<float*>(static_cast<char*>(ws) + L.blk_score);
+    }
+    rc = hip_status(launch_block_score(s, q, meta, ctx_len, scores, stream));
+    if (rc) return rc;
+    return hip_status(launch_select(s, 1, q, scores, nullptr, nullptr, ctx_len, blk_idx, nullptr,
+                                    nullptr, stream));
+}
+
+int hsab_select_tokens(const hsab_dims* dims, const uint16_t* q, const uint16_t* klabel,
+                       const int32_t* label_ch, const int32_t* blk_idx, const int32_t* ctx_len,
+                       int32_t* tok_idx, float* tok_score, void* ws, size_t ws_bytes,
+                       hipStream_t stream) {
+    (void)ws; (void)ws_bytes;
+    int rc = check_dims(dims);
+    if (rc) return rc;
+    if (!q || !klabel || !label_ch || !blk_idx || !ctx_len || !tok_idx) return HSAB_EINVAL;
+    return hip_status(launch_select(make_shape(*dims), 2, q, nullptr, klabel, label_ch, ctx_len,
+                                    const_cast<int32_t*>(blk_idx), tok_idx, tok_score, stream));
+}
+
+int hsab_sparse_attend(const hsab_dims* dims, const uint16_t* q, const uint16_t* K,
+                       const uint16_t* V, const int32_t* tok_idx, const int32_t* ctx_len,
+                       const int32_t* slot_of, int32_t n_slots, float* out, float* lse, void* ws,
+                       size_t ws_bytes, hipStream_t stream) {
+    (void)ctx_len;
+    int rc = check_dims(dims);
+    if (rc) return rc;
+    const Shape s = make_shape(*dims);
+    if (!q || !K || !tok_idx || !out || !lse) return HSAB_EINVAL;
+    if (!s.valias && !V) return HSAB_EINVAL;
+    if (slot_of && n_slots < 1) return HSAB_EINVAL;
+    const WsLayout L = ws_layout(s);
+    if (!ws || ws_bytes < L.total) return HSAB_EINVAL;
+    if (!attend_supported(s)) return HSAB_EUNSUPPORTED;
+    char* w = static_cast<char*>(ws);
+    return hip_status(launch_attend(s, q, K, s.valias ? K : V, tok_idx, slot_of, n_slots,
+                                    reinterpret_cast<float*>(w + L.part_ml),
+                                    reinterpret_cast<float*>(w + L.part_acc), out, lse, stream));
+}
+
+int hsab_decode_step(const hsab_dims* dims, const uint16_t* q, const uint16_t* k_new,
+                     const uint16_t* v_new, uint16_t* K, uint16_t* V, uint16_t* meta,
+                     uint16_t* klabel, const int32_t* label_ch, const int32_t* ctx_len,
+                     int32_t* blk_idx, int32_t* tok_idx, float* out, float* lse, void* ws,
+                     size_t ws_bytes, hipStream_t stream) {
+    int rc = check_dims(dims);
+    if (rc) return rc;
+    const Shape s = make_shape(*dims);
+    if (!q || !k_new || !K || !meta || !klabel || !label_ch || !ctx_len || !blk_idx || !tok_idx ||
+        !out || !lse)
+        return HSAB_EINVAL;
+    if (!s.valias && (!V || !v_new)) return HSAB_EINVAL;
+    const WsLayout L = ws_layout(s);
+    if (!ws || ws_bytes < L.total) return HSAB_EINVAL;
+    if (!attend_supported(s)) return HSAB_EUNSUPPORTED;
+    char* w = static_cast<char*>(ws);
+    float* scores = reinterpret_cast<float*>(w + L.blk_score);
+    rc = hip_status(launch_append(s, k_new, v_new, K, V, meta, klabel, label_ch, ctx_len, stream));
+    if (rc) return rc;
+    rc = hip_status(launch_block_score(s, q, meta, ctx_len, scores, stream));
+    if (rc) return rc;
+    rc = hip_status(launch_select(s, 3, q, scores, klabel, label_ch, ctx_len, blk_idx, tok_idx,
+                                  nullptr, stream));
+    if (rc) return rc;
+    return hip_status(launch_attend(s, q, K, s.valias ? K : V, tok_idx, nullptr, 0,
+                                    reinterpret_cast<float*>(w + L.part_ml),
+                                    reinterpret_cast<float*>(w + L.part_acc), out, lse, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,239 @@
+// Exact attention over the kept tokens (AsyncTLS, gist.science/es
+// explainer, section 2.A item 2: the final attention runs on the K_t
+// selected tokens only), split over workgroups and merged by log-sum-exp.
+//
+// GQA path (d_k == d_v == D, G query heads per KV head): one workgroup of
+// four waves takes 64 consecutive entries of the unit's token list; D/8
+// lanes share a token (8 channels = 16 bytes each), so one wave load
+// gathers 64/(D/8) whole key rows. Logits are fp32 (bf16 products are
+// exact in fp32), kept in base-2 units (q pre-scaled by sm_scale*log2 e).
+// Each wave keeps (max, sum, weighted values) per head; the workgroup
+// merges its four waves and writes one partial per head. The combine
+// kernel merges the partials of all splits.
+#include "common.h"
+#include "kernels.h"
+
+namespace hsab {
+
+namespace {
+
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+
+__device__ __forceinline__ void widen8(uint4 v, float (&f)[8]) {
+    f[0] = lo_f32(v.x); f[1] = hi_f32(v.x); f[2] = lo_f32(v.y); f[3] = hi_f32(v.y);
+    f[4] = lo_f32(v.z); f[5] = hi_f32(v.z); f[6] = lo_f32(v.w); f[7] = hi_f32(v.w);
+}
+
+// Row index (in units of rows of the K/V arrays) of token t of unit, or -1.
+__device__ __forceinline__ long row_of(int t, int unit, int bs, int max_ctx, int nb_cap,
+                                       const int32_t* __restrict__ slot_of, int n_slots) {
+    if (t < 0) return -1;
+    if (!slot_of) return (t < max_ctx) ? (long)unit * max_ctx + t : -1;
+    const int blk = t / bs;
+    if (blk >= nb_cap) return -1;
+    const int slot = slot_of[(size_t)unit * nb_cap + blk];
+    if (slot < 0 || slot >= n_slots) return -1;
+    return ((long)unit * n_slots + slot) * bs + (t - blk * bs);
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(256) void attend_gqa_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const int32_t* __restrict__ tok_idx, const int32_t* __restrict__ slot_of, int n_slots,
+    float* __restrict__ part_ml, float* __restrict__ part_acc, int Hkv, int bs, int kt,
+    int max_ctx, int nb_cap, int n_splits, float scale2) {
+    constexpr int LPT = D / 8;                         // lanes per token
+    constexpr int TPI = 64 / LPT;                      // tokens per wave load
+    constexpr int TPW = ATT_TOK_PER_SPLIT / 4;         // tokens per wave
+    constexpr int IT = TPW / TPI;
+    static_assert(IT >= 1 && TPW % TPI == 0, "bad D");
+    __shared__ float s_m[4][G], s_l[4][G];
+    __shared__ float s_acc[4][G][D];
+
+    const int split = blockIdx.x, unit = blockIdx.y, b = unit / Hkv, g = unit % Hkv;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int cc = lane % LPT, ts = lane / LPT;
+
+    float qf[G][8];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        const uint4 v = ldg16(q + ((size_t)(b * Hkv + g) * G + h) * D + cc * 8);
+        widen8(v, qf[h]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qf[h][e] *= scale2;
+    }
+
+    uint4 kr[IT], vr[IT];
+    bool ok[IT];
+    const int32_t* tl = tok_idx + (size_t)unit * kt;
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+        const int ti = split * ATT_TOK_PER_SPLIT + wave * TPW + it * TPI + ts;
+        const int t = ti < kt ? tl[ti] : -1;
+        const long row = row_of(t, unit, bs, max_ctx, nb_cap, slot_of, n_slots);
+        ok[it] = row >= 0;
+        if (ok[it]) {
+            kr[it] = ldg16(K + row * D + cc * 8);
+            vr[it] = ldg16(V + row * D + cc * 8);
+        } else {
+            kr[it] = vr[it] = make_uint4(0u, 0u, 0u, 0u);
+        }
+    }
+
+    float z[IT][G];
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+        float kf[8];
+        widen8(kr[it], kf);
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            float p = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) p = fmaf(qf[h][e], kf[e], p);
+#pragma unroll
+            for (int o = LPT / 2; o >= 1; o >>= 1) p += __shfl_xor(p, o);
+            z[it][h] = ok[it] ? p : -INFINITY;
+        }
+    }
+
+    float m[G], l[G], acc[G][8];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        float mm = z[0][h];
+#pragma unroll
+        for (int it = 1; it < IT; ++it) mm = fmaxf(mm, z[it][h]);
+#pragma unroll
+        for (int o = LPT; o < 64; o <<= 1) mm = fmaxf(mm, __shfl_xor(mm, o));
+        m[h] = mm;
+        l[h] = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+    }
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+        float vf[8];
+        widen8(vr[it], vf);
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            const float p = ok[it] ? exp2f(z[it][h] - m[h]) : 0.f;
+            l[h] += p;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(p, vf[e], acc[h][e]);
+        }
+    }
+    // sum over the token slots of the wave (lanes that share a channel chunk)
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+#pragma unroll
+        for (int o = LPT; o < 64; o <<= 1) {
+            l[h] += __shfl_xor(l[h], o);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[h][e] += __shfl_xor(acc[h][e], o);
+        }
+    }
+    if (ts == 0) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s_acc[wave][h][cc * 8 + e] = acc[h][e];
+            if (cc == 0) { s_m[wave][h] = m[h]; s_l[wave][h] = l[h]; }
+        }
+    }
+    __syncthreads();
+
+    for (int p = threadIdx.x; p < G * D; p += blockDim.x) {
+        const int h = p / D, c = p - h * D;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) M = fmaxf(M, s_m[w][h]);
+        float L = 0.f, A = 0.f;
+        if (M != -INFINITY) {
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const float mw = s_m[w][h];
+                const float wt = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
+                L = fmaf(s_l[w][h], wt, L);
+                A = fmaf(s_acc[w][h][c], wt, A);
+            }
+        }
+        const size_t bh = (size_t)(b * Hkv + g) * G + h;
+        part_acc[(bh * n_splits + split) * D + c] = A;
+        if (c == 0) {
+            part_ml[(bh * n_splits + split) * 2 + 0] = M;
+            part_ml[(bh * n_splits + split) * 2 + 1] = L;
+        }
+    }
+}
+
+// grid: (B*Hq). Merges the split partials of one query head.
+__global__ __launch_bounds__(256) void combine_kernel(
+    const float* __restrict__ part_ml, const float* __restrict__ part_acc, float* __restrict__ out,
+    float* __restrict__ lse, int dv, int n_splits) {
+    const size_t bh = blockIdx.x;
+    const float* ml = part_ml + bh * n_splits * 2;
+    float M = -INFINITY;
+    for (int s = 0; s < n_splits; ++s) M = fmaxf(M, ml[2 * s]);
+    float L = 0.f;
+    if (M != -INFINITY)
+        for (int s = 0; s < n_splits; ++s) {
+            const float ms = ml[2 * s];
+            if (ms != -INFINITY) L = fmaf(ml[2 * s + 1], exp2f(ms - M), L);
+        }
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    for (int c = threadIdx.x; c < dv; c += blockDim.x) {
+        float A = 0.f;
+        if (M != -INFINITY)
+            for (int s = 0; s < n_splits; ++s) {
+                const float ms = ml[2 * s];
+                if (ms != -INFINITY) A = fmaf(part_acc[(bh * n_splits + s) * dv + c], exp2f(ms - M), A);
+            }
+        out[bh * dv + c] = A * inv;
+    }
+    if (threadIdx.x == 0) lse[bh] = L > 0.f ? (M + log2f(L)) * LN2 : -INFINITY;
+}
+
+template <int D, int G>
+hipError_t launch_gqa(const Shape& s, const uint16_t* q, const uint16_t* K, const uint16_t* V,
+                      const int32_t* tok_idx, const int32_t* slot_of, int n_slots, float* part_ml,
+                      float* part_acc, hipStream_t st) {
+    const int ns = attn_splits(s);
+    hipLaunchKernelGGL((attend_gqa_kernel<D, G>), dim3(ns, s.B * s.Hkv), dim3(256), 0, st, q, K, V,
+                       tok_idx, slot_of, n_slots, part_ml, part_acc, s.Hkv, s.bs, s.kt, s.max_ctx,
+                       s.nb_cap, ns, s.sm_scale * LOG2E);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_gqa_d(const Shape& s, const uint16_t* q, const uint16_t* K, const uint16_t* V,
+                        const int32_t* tok_idx, const int32_t* slot_of, int n_slots, float* part_ml,
+                        float* part_acc, hipStream_t st) {
+    switch (s.G) {
+        case 1: return launch_gqa<D, 1>(s, q, K, V, tok_idx, slot_of, n_slots, part_ml, part_acc, st);
+        case 2: return launch_gqa<D, 2>(s, q, K, V, tok_idx, slot_of, n_slots, part_ml, part_acc, st);
+        case 4: return launch_gqa<D, 4>(s, q, K, V, tok_idx, slot_of, n_slots, part_ml, part_acc, st);
+        case 8: return launch_gqa<D, 8>(s, q, K, V, tok_idx, slot_of, n_slots, part_ml, part_acc, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_attend(const Shape& s, const uint16_t* q, const uint16_t* K, const uint16_t* V,
+                         const int32_t* tok_idx, const int32_t* slot_of, int n_slots,
+                         float* part_ml, float* part_acc, float* out, float* lse, hipStream_t st) {
+    hipError_t e;
+    if (s.valias || s.dk != s.dv) return hipErrorInvalidValue;
+    switch (s.dk) {
+        case 64: e = launch_gqa_d<64>(s, q, K, V, tok_idx, slot_of, n_slots, part_ml, part_acc, st); break;
+        case 128: e = launch_gqa_d<128>(s, q, K, V, tok_idx, slot_of, n_slots, part_ml, part_acc, st); break;
+        case 256: e = launch_gqa_d<256>(s, q, K, V, tok_idx, slot_of, n_slots, part_ml, part_acc, st); break;
+        default: return hipErrorInvalidValue;
+    }
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(combine_kernel, dim3(s.B * s.Hq), dim3(s.dv < 256 ? 128 : 256), 0, st, part_ml,
+                       part_acc, out, lse, s.dv, attn_splits(s));
+    return hipGetLastError();
+}
+
+}  // namespace hsab

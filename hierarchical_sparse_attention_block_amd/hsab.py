@@ -1,0 +1,221 @@
+"""Python binding of libhsab.so: argument marshalling only.
+
+Each function takes torch tensors that live on the GPU, checks that every
+buffer has the dtype, contiguity and size the C ABI documents (the library
+itself only sees raw pointers), and forwards the pointers. All computation
+happens in the HIP kernels. There is no fallback: if the shared library is
+missing or cannot be loaded, importing this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libhsab.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run `python -m hierarchical_sparse_attention_block_amd.build`")
+_lib = ctypes.CDLL(LIB_PATH)
+
+HSAB_OK, HSAB_EINVAL, HSAB_EHIP, HSAB_EUNSUPPORTED = 0, -1, -2, -3
+EXPORTS = ("hsab_workspace_bytes", "hsab_status_string", "hsab_last_hip_error", "hsab_build_meta",
+           "hsab_score_blocks", "hsab_select_blocks", "hsab_select_tokens", "hsab_sparse_attend",
+           "hsab_decode_step")
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32), ("v_alias_k", ctypes.c_int32),
+                ("block", ctypes.c_int32), ("r", ctypes.c_int32), ("k_blocks", ctypes.c_int32),
+                ("k_tokens", ctypes.c_int32), ("max_ctx", ctypes.c_int32), ("sm_scale", ctypes.c_float)]
+
+    @property
+    def group(self):
+        return self.n_q_heads // self.n_kv_heads
+
+    @property
+    def nb_cap(self):
+        return -(-self.max_ctx // self.block)
+
+    def __repr__(self):
+        return "Dims(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
+
+
+def dims(batch, n_q_heads, n_kv_heads, d_k, d_v, v_alias_k, block, r, k_blocks, k_tokens, max_ctx,
+         sm_scale) -> Dims:
+    return Dims(batch, n_q_heads, n_kv_heads, d_k, d_v, int(bool(v_alias_k)), block, r, k_blocks,
+                k_tokens, max_ctx, float(sm_scale))
+
+
+_vp, _sz, _i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32
+_D = ctypes.POINTER(Dims)
+_lib.hsab_workspace_bytes.argtypes = [_D]
+_lib.hsab_workspace_bytes.restype = _sz
+_lib.hsab_status_string.argtypes = [ctypes.c_int]
+_lib.hsab_status_string.restype = ctypes.c_char_p
+_lib.hsab_last_hip_error.argtypes = []
+_lib.hsab_last_hip_error.restype = ctypes.c_int
+_lib.hsab_build_meta.argtypes = [_D, _vp, _vp, _vp, _vp, _vp, _vp]
+_lib.hsab_score_blocks.argtypes = [_D, _vp, _vp, _vp, _vp, _vp]
+_lib.hsab_select_blocks.argtypes = [_D, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+_lib.hsab_select_tokens.argtypes = [_D, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+_lib.hsab_sparse_attend.argtypes = [_D, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _sz, _vp]
+_lib.hsab_decode_step.argtypes = [_D, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                  _vp, _sz, _vp]
+for _f in EXPORTS[3:]:
+    getattr(_lib, _f).restype = ctypes.c_int
+
+
+class HsabError(RuntimeError):
+    def __init__(self, fn, status):
+        msg = _lib.hsab_status_string(status).decode()
+        if status == HSAB_EHIP:
+            msg += f" (hipError {_lib.hsab_last_hip_error()})"
+        super().__init__(f"{fn}: {msg}")
+        self.status = status
+
+
+def _check(fn, status):
+    if status != HSAB_OK:
+        raise HsabError(fn, status)
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+_u16, _i, _f = torch.uint16, torch.int32, torch.float32
+# bf16 buffers may be passed as bfloat16 tensors or as raw 16-bit patterns
+_BF16_BITS = (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def _buf(name, t, dtype, numel, allow_none=False):
+    """Pointer of a device buffer after checking dtype, layout and size."""
+    if t is None:
+        if allow_none:
+            return None
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    ok = t.dtype in _BF16_BITS if dtype is _u16 else t.dtype == dtype
+    if not ok:
+        raise ValueError(f"{name} must be {'bf16 bits' if dtype is _u16 else dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, needs {numel}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def workspace_bytes(d: Dims) -> int:
+    return int(_lib.hsab_workspace_bytes(ctypes.byref(d)))
+
+
+def status_string(status: int) -> str:
+    return _lib.hsab_status_string(status).decode()
+
+
+def alloc_workspace(d: Dims, device="cuda") -> torch.Tensor:
+    n = workspace_bytes(d)
+    if n == 0:
+        raise ValueError(f"invalid dims {d}")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def _sizes(d: Dims):
+    U = d.batch * d.n_kv_heads
+    return {
+        "q": d.batch * d.n_q_heads * d.d_k, "K": U * d.max_ctx * d.d_k, "V": U * d.max_ctx * d.d_v,
+        "meta": U * d.nb_cap * 2 * d.d_k, "klabel": U * d.max_ctx * d.r, "label": d.n_kv_heads * d.r,
+        "ctx": d.batch, "blk": U * d.k_blocks, "tok": U * d.k_tokens, "score": U * d.nb_cap,
+        "tscore": U * d.k_blocks * d.block, "out": d.batch * d.n_q_heads * d.d_v,
+        "lse": d.batch * d.n_q_heads, "knew": U * d.d_k, "vnew": U * d.d_v,
+    }
+
+
+def _ws(d, ws):
+    if ws is None:
+        raise ValueError("workspace is required (alloc_workspace)")
+    return _buf("ws", ws, torch.uint8, workspace_bytes(d)), ctypes.c_size_t(ws.numel())
+
+
+def build_meta(d: Dims, K, ctx_len, label_ch, meta, klabel, stream=None):
+    s = _sizes(d)
+    _check("hsab_build_meta", _lib.hsab_build_meta(
+        ctypes.byref(d), _buf("K", K, _u16, s["K"]), _buf("ctx_len", ctx_len, _i, s["ctx"]),
+        _buf("label_ch", label_ch, _i, s["label"]), _buf("meta", meta, _u16, s["meta"]),
+        _buf("klabel", klabel, _u16, s["klabel"]), _stream(stream)))
+
+
+def score_blocks(d: Dims, q, meta, ctx_len, blk_score, stream=None):
+    s = _sizes(d)
+    _check("hsab_score_blocks", _lib.hsab_score_blocks(
+        ctypes.byref(d), _buf("q", q, _u16, s["q"]), _buf("meta", meta, _u16, s["meta"]),
+        _buf("ctx_len", ctx_len, _i, s["ctx"]), _buf("blk_score", blk_score, _f, s["score"]),
+        _stream(stream)))
+
+
+def select_blocks(d: Dims, q, meta, ctx_len, blk_idx, blk_score=None, ws=None, stream=None):
+    s = _sizes(d)
+    if blk_score is None:
+        wp, wn = _ws(d, ws)
+    else:
+        wp, wn = (None, 0) if ws is None else _ws(d, ws)
+    _check("hsab_select_blocks", _lib.hsab_select_blocks(
+        ctypes.byref(d), _buf("q", q, _u16, s["q"]), _buf("meta", meta, _u16, s["meta"]),
+        _buf("ctx_len", ctx_len, _i, s["ctx"]), _buf("blk_idx", blk_idx, _i, s["blk"]),
+        _buf("blk_score", blk_score, _f, s["score"], allow_none=True), wp, wn, _stream(stream)))
+
+
+def select_tokens(d: Dims, q, klabel, label_ch, blk_idx, ctx_len, tok_idx, tok_score=None, ws=None,
+                  stream=None):
+    s = _sizes(d)
+    wp, wn = (None, 0) if ws is None else _ws(d, ws)
+    _check("hsab_select_tokens", _lib.hsab_select_tokens(
+        ctypes.byref(d), _buf("q", q, _u16, s["q"]), _buf("klabel", klabel, _u16, s["klabel"]),
+        _buf("label_ch", label_ch, _i, s["label"]), _buf("blk_idx", blk_idx, _i, s["blk"]),
+        _buf("ctx_len", ctx_len, _i, s["ctx"]), _buf("tok_idx", tok_idx, _i, s["tok"]),
+        _buf("tok_score", tok_score, _f, s["tscore"], allow_none=True), wp, wn, _stream(stream)))
+
+
+def sparse_attend(d: Dims, q, K, V, tok_idx, ctx_len, out, lse, ws, slot_of=None, n_slots=0,
+                  stream=None):
+    s = _sizes(d)
+    U = d.batch * d.n_kv_heads
+    if slot_of is None:
+        kn, vn = s["K"], s["V"]
+    else:
+        kn, vn = U * n_slots * d.block * d.d_k, U * n_slots * d.block * d.d_v
+    wp, wn = _ws(d, ws)
+    _check("hsab_sparse_attend", _lib.hsab_sparse_attend(
+        ctypes.byref(d), _buf("q", q, _u16, s["q"]), _buf("K", K, _u16, kn),
+        _buf("V", V, _u16, vn, allow_none=bool(d.v_alias_k)), _buf("tok_idx", tok_idx, _i, s["tok"]),
+        _buf("ctx_len", ctx_len, _i, s["ctx"]),
+        _buf("slot_of", slot_of, _i, U * d.nb_cap, allow_none=True), ctypes.c_int32(n_slots),
+        _buf("out", out, _f, s["out"]), _buf("lse", lse, _f, s["lse"]), wp, wn, _stream(stream)))
+
+
+def decode_step(d: Dims, q, k_new, v_new, K, V, meta, klabel, label_ch, ctx_len, blk_idx, tok_idx,
+                out, lse, ws, stream=None):
+    s = _sizes(d)
+    alias = bool(d.v_alias_k)
+    wp, wn = _ws(d, ws)
+    _check("hsab_decode_step", _lib.hsab_decode_step(
+        ctypes.byref(d), _buf("q", q, _u16, s["q"]), _buf("k_new", k_new, _u16, s["knew"]),
+        _buf("v_new", v_new, _u16, s["vnew"], allow_none=alias), _buf("K", K, _u16, s["K"]),
+        _buf("V", V, _u16, s["V"], allow_none=alias), _buf("meta", meta, _u16, s["meta"]),
+        _buf("klabel", klabel, _u16, s["klabel"]), _buf("label_ch", label_ch, _i, s["label"]),
+        _buf("ctx_len", ctx_len, _i, s["ctx"]), _buf("blk_idx", blk_idx, _i, s["blk"]),
+        _buf("tok_idx", tok_idx, _i, s["tok"]), _buf("out", out, _f, s["out"]),
+        _buf("lse", lse, _f, s["lse"]), wp, wn, _stream(stream)))
+
+
+def raw_call(name, *args):
+    """Call an exported entry point with raw ctypes arguments and return its
+    status (used by the host-side error-path tests)."""
+    return getattr(_lib, name)(*args)

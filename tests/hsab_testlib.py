@@ -1,0 +1,183 @@
+"""Helpers shared by the GPU parity tests, the smoke check and the bench:
+staging seeded inputs on the device, running the library, and the parity
+rules that compare its results with the CPU oracle.
+
+Parity rules:
+* index sets (blocks, tokens): let s_(1) >= s_(2) >= ... be the oracle's
+  fp64 scores. If s_(k) - s_(k+1) > 1e-4*|s_(k)| the GPU set must equal the
+  oracle set exactly; otherwise (a near tie at the cut) the GPU set is
+  accepted if it holds every index scoring above s_(k) + 1e-4|s_(k)| and only
+  indices scoring at least s_(k) - 1e-4|s_(k)|, and later stages of the
+  oracle are recomputed on the GPU's set;
+* attention outputs: max-abs difference <= 2e-3 on fp32 out; lse within
+  1e-4 relative;
+* metadata and label rows: exact.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+import oracle as O
+from hierarchical_sparse_attention_block_amd import workloads as W
+
+REL_GAP = 1e-4
+OUT_ATOL = 2e-3
+LSE_RTOL = 1e-4
+
+
+def dims_of(w: W.Workload):
+    from hierarchical_sparse_attention_block_amd import hsab as H
+    return H.dims(w.batch, w.n_q_heads, w.n_kv_heads, w.d_k, w.d_v, w.v_alias_k, w.block, w.r,
+                  w.k_blocks, w.k_tokens, w.max_ctx, w.sm_scale)
+
+
+def host_inputs(w: W.Workload, ctx_len=None, threads=8):
+    """Seeded host arrays of a workload. ctx_len (per batch row, counting the
+    appended token) defaults to w.ctx for every row; rows beyond a shorter
+    ctx_len are zeroed so the cache holds exactly ctx_len-1 prefill tokens."""
+    q = W.queries(w)
+    K, V = W.full_cache(w, q, threads=threads)
+    ctx = np.full(w.batch, w.ctx, np.int32) if ctx_len is None else np.asarray(ctx_len, np.int32)
+    for b in range(w.batch):
+        K[b, :, ctx[b] - 1:] = 0
+        if V is not None:
+            V[b, :, ctx[b] - 1:] = 0
+    k_new, v_new = W.new_token(w)
+    return {"q": q, "K": K, "V": V, "ctx": ctx, "k_new": k_new, "v_new": v_new,
+            "label": W.label_channels(w)}
+
+
+def dev16(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
+
+
+def host16(t: torch.Tensor) -> np.ndarray:
+    return t.cpu().numpy().view(np.uint16)
+
+
+def appended_cache(w, h):
+    """Host K/V with the new token written at ctx-1 (what the oracle sees)."""
+    K = h["K"].copy()
+    V = None if h["V"] is None else h["V"].copy()
+    for b in range(w.batch):
+        p = int(h["ctx"][b]) - 1
+        K[b, :, p] = h["k_new"][b]
+        if V is not None:
+            V[b, :, p] = h["v_new"][b]
+    return K, V
+
+
+class Device:
+    """Device copies of a workload's inputs plus output buffers."""
+
+    def __init__(self, w: W.Workload, h: dict):
+        from hierarchical_sparse_attention_block_amd import hsab as H
+        self.H, self.w, self.d = H, w, dims_of(w)
+        d = self.d
+        U = w.units
+        self.q = dev16(h["q"])
+        self.K = dev16(h["K"])
+        self.V = None if h["V"] is None else dev16(h["V"])
+        self.k_new = dev16(h["k_new"])
+        self.v_new = dev16(h["v_new"])
+        self.label = torch.from_numpy(h["label"]).cuda()
+        self.ctx = torch.from_numpy(h["ctx"]).cuda()
+        self.ctx_prefill = torch.from_numpy(h["ctx"] - 1).cuda()
+        self.meta = torch.zeros(U * d.nb_cap * 2 * w.d_k, dtype=torch.int16, device="cuda")
+        self.klabel = torch.zeros(U * w.max_ctx * w.r, dtype=torch.int16, device="cuda")
+        self.blk = torch.full((U * w.k_blocks,), -7, dtype=torch.int32, device="cuda")
+        self.tok = torch.full((U * w.k_tokens,), -7, dtype=torch.int32, device="cuda")
+        self.out = torch.full((w.batch * w.n_q_heads * w.d_v,), float("nan"), device="cuda")
+        self.lse = torch.full((w.batch * w.n_q_heads,), float("nan"), device="cuda")
+        self.ws = H.alloc_workspace(d)
+
+    def prefill_meta(self):
+        self.H.build_meta(self.d, self.K, self.ctx_prefill, self.label, self.meta, self.klabel)
+
+    def decode_step(self):
+        self.H.decode_step(self.d, self.q, self.k_new, self.v_new, self.K, self.V, self.meta,
+                           self.klabel, self.label, self.ctx, self.blk, self.tok, self.out, self.lse,
+                           self.ws)
+
+    def results(self):
+        torch.cuda.synchronize()
+        w = self.w
+        return {
+            "blk": self.blk.cpu().numpy().reshape(w.batch, w.n_kv_heads, w.k_blocks),
+            "tok": self.tok.cpu().numpy().reshape(w.batch, w.n_kv_heads, w.k_tokens),
+            "out": self.out.cpu().numpy().reshape(w.batch, w.n_q_heads, w.d_v),
+            "lse": self.lse.cpu().numpy().reshape(w.batch, w.n_q_heads),
+        }
+
+
+# ------------------------------------------------------------------ parity
+def check_index_set(scores, gpu_idx, k, what=""):
+    """Apply the near-tie rule. scores: oracle fp64 scores over the index
+    space; gpu_idx: the GPU's list (ascending, -1 padded). Returns the GPU's
+    set as an int64 array and whether the cut was a near tie."""
+    s = np.asarray(scores, np.float64)
+    g = np.asarray(gpu_idx)
+    k_eff = min(int(k), s.shape[0])
+    sel = g[:k_eff]
+    assert np.all(g[k_eff:] == -1), f"{what}: padding after {k_eff} entries is not -1: {g[k_eff:][:8]}"
+    assert np.all(sel >= 0) and np.all(sel < s.shape[0]), f"{what}: index out of range {sel[:8]}"
+    assert np.all(np.diff(sel) > 0), f"{what}: not strictly ascending"
+    want = O.topk_stable(s, k_eff)
+    if k_eff == s.shape[0]:
+        assert np.array_equal(sel, want), f"{what}: must keep everything"
+        return sel.astype(np.int64), False
+    srt = np.sort(s)[::-1]
+    sk, sk1 = srt[k_eff - 1], srt[k_eff]
+    band = REL_GAP * abs(sk)
+    if sk - sk1 > band:
+        if not np.array_equal(sel, want):
+            diff = np.setxor1d(sel, want)
+            raise AssertionError(f"{what}: sets differ at a clear cut (gap {sk - sk1:.3g} > {band:.3g}); "
+                                 f"xor {diff[:8]} scores {s[diff[:8]]}")
+        return sel.astype(np.int64), False
+    must = np.nonzero(s > sk + band)[0]
+    assert np.all(np.isin(must, sel)), f"{what}: misses an index clearly above the cut"
+    assert np.all(s[sel] >= sk - band), f"{what}: holds an index clearly below the cut"
+    return sel.astype(np.int64), True
+
+
+def oracle_unit_vs_gpu(w, q_bits, K_bits, V_bits, ctx, label, b, g, gpu_blk, gpu_tok, gpu_out, gpu_lse):
+    """Check one unit against the oracle under the parity rules; stage two
+    and three of the oracle run on the GPU's accepted sets."""
+    G = w.group
+    n = int(ctx[b])
+    q = O.bf16_to_f64(q_bits[b, g * G:(g + 1) * G])
+    K = O.bf16_to_f64(K_bits[b, g, :n])
+    V = K[:, : w.d_v] if w.v_alias_k else O.bf16_to_f64(V_bits[b, g, :n])
+    kmax, kmin = O.block_meta(K, n, w.block)
+    s_blk = O.block_scores(q, kmax, kmin)
+    blk, tie_b = check_index_set(s_blk, gpu_blk, w.k_blocks, f"blocks of unit ({b},{g})")
+    cand = O.candidate_tokens(blk, n, w.block)
+    s_tok = O.label_scores(q, K[cand], label[g])
+    # the GPU reports positions; map them to candidate indices
+    k_eff = min(w.k_tokens, len(cand))
+    pos = np.asarray(gpu_tok[:k_eff])
+    assert np.all(gpu_tok[k_eff:] == -1), f"unit ({b},{g}): token padding"
+    ci = np.searchsorted(cand, pos)
+    assert np.all(ci < len(cand)) and np.array_equal(cand[np.minimum(ci, len(cand) - 1)], pos), \
+        f"unit ({b},{g}): a selected token is not a candidate"
+    gpu_ci = np.concatenate([ci, np.full(len(gpu_tok) - k_eff, -1)])
+    ci_sel, tie_t = check_index_set(s_tok, gpu_ci, w.k_tokens, f"tokens of unit ({b},{g})")
+    tok = cand[ci_sel]
+    out, lse = O.attend(q, K[tok], V[tok], w.sm_scale)
+    err = np.max(np.abs(out - gpu_out))
+    assert err <= OUT_ATOL, f"unit ({b},{g}): out max-abs {err:.3g} > {OUT_ATOL}"
+    np.testing.assert_allclose(gpu_lse, lse, rtol=LSE_RTOL, err_msg=f"unit ({b},{g}) lse")
+    return {"tie_blocks": tie_b, "tie_tokens": tie_t, "max_abs": float(err)}
+
+
+def score_tolerance(q, kmax, kmin):
+    """Worst-case fp32 summation bound of the block scores:
+    gamma_{2d} * sum_c |q_c| max(|kmax_c|, |kmin_c|), gamma_n = n 2^-24,
+    taken over the heads of the group (max)."""
+    n = 2 * q.shape[1]
+    mag = np.abs(q) @ np.maximum(np.abs(kmax), np.abs(kmin)).T      # [G, nb]
+    return n * 2.0 ** -24 * mag.max(axis=0) + 1e-30

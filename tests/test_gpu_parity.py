@@ -1,0 +1,333 @@
+"""GPU parity: every stage of the HIP path through the C ABI against the
+CPU oracle, on seeded inputs that span several tiles and ragged tails, plus
+edge cases (n=1, partial blocks, budgets larger than what exists, exact
+ties, the dense limit) and the full-size 48k GQA layer on sampled units."""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from hierarchical_sparse_attention_block_amd import workloads as W
+from tests import hsab_testlib as T
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _wl(**kw):
+    base = dict(name="t", batch=2, n_q_heads=8, n_kv_heads=2, d_k=128, d_v=128, v_alias_k=False,
+                block=16, r=16, k_blocks=16, k_tokens=64, ctx=1000, max_ctx=1024, scaled_keys=True,
+                label_mode="top_scale", n_planted=4, seed=11)
+    base.update(kw)
+    return W.Workload(**base)
+
+
+def _run_decode(w, ctx=None):
+    say(f"[decode_step] {w}")
+    h = T.host_inputs(w, ctx_len=ctx)
+    dev = T.Device(w, h)
+    dev.prefill_meta()
+    dev.decode_step()
+    r = dev.results()
+    return w, h, dev, r
+
+
+def _check_all_units(w, h, r, units=None):
+    K, V = T.appended_cache(w, h)
+    Vb = w.d_v if w.v_alias_k else V
+    stats = []
+    todo = units or [(b, g) for b in range(w.batch) for g in range(w.n_kv_heads)]
+    for b, g in todo:
+        G = w.group
+        stats.append(T.oracle_unit_vs_gpu(
+            w, h["q"], K, V, h["ctx"], h["label"], b, g, r["blk"][b, g], r["tok"][b, g],
+            r["out"][b, g * G:(g + 1) * G], r["lse"][b, g * G:(g + 1) * G]))
+    return stats
+
+
+# --------------------------------------------------------------- metadata
+@pytest.mark.parametrize("dk,bs,r", [(128, 16, 16), (64, 8, 32), (576, 32, 32)])
+def test_build_meta_and_append_exact(dk, bs, r):
+    w = _wl(d_k=dk, d_v=dk if dk != 576 else 512, v_alias_k=dk == 576, block=bs, r=r,
+            n_q_heads=4, n_kv_heads=2, max_ctx=700, ctx=700, n_planted=0)
+    ctx = np.array([700, 333], np.int32)
+    say(f"[build_meta+append] dk={dk} bs={bs} r={r} ctx={ctx}")
+    h = T.host_inputs(w, ctx_len=ctx)
+    dev = T.Device(w, h)
+    dev.prefill_meta()
+    torch.cuda.synchronize()
+    d = dev.d
+    meta = T.host16(dev.meta).reshape(w.batch, w.n_kv_heads, d.nb_cap, 2, w.d_k)
+    klab = T.host16(dev.klabel).reshape(w.batch, w.n_kv_heads, w.max_ctx, w.r)
+    for b in range(w.batch):
+        for g in range(w.n_kv_heads):
+            n = int(ctx[b]) - 1
+            K = O.bf16_to_f64(h["K"][b, g, :n])
+            kmax, kmin = O.block_meta(K, n, bs)
+            nb = kmax.shape[0]
+            np.testing.assert_array_equal(O.bf16_to_f64(meta[b, g, :nb, 0]), kmax)
+            np.testing.assert_array_equal(O.bf16_to_f64(meta[b, g, :nb, 1]), kmin)
+            np.testing.assert_array_equal(klab[b, g, :n], h["K"][b, g, :n][:, h["label"][g]])
+    # the append of decode_step (attention is not needed for this check)
+    H = dev.H
+    if not w.v_alias_k:
+        dev.decode_step()
+    else:
+        with pytest.raises(H.HsabError):
+            dev.decode_step()
+        return
+    torch.cuda.synchronize()
+    meta = T.host16(dev.meta).reshape(w.batch, w.n_kv_heads, d.nb_cap, 2, w.d_k)
+    Kd = T.host16(dev.K).reshape(h["K"].shape)
+    Ka, _ = T.appended_cache(w, h)
+    for b in range(w.batch):
+        n = int(ctx[b])
+        np.testing.assert_array_equal(Kd[b, :, :n], Ka[b, :, :n])
+        for g in range(w.n_kv_heads):
+            kmax, kmin = O.block_meta(O.bf16_to_f64(Ka[b, g, :n]), n, bs)
+            kmax0, kmin0 = O.block_meta(O.bf16_to_f64(Ka[b, g, :n - 1]), n - 1, bs) if n > 1 else (None, None)
+            if kmax0 is not None:
+                kmax1, kmin1 = O.append_meta(kmax0, kmin0, O.bf16_to_f64(Ka[b, g, n - 1]), n - 1, bs)
+                np.testing.assert_array_equal(kmax1, kmax)
+            np.testing.assert_array_equal(O.bf16_to_f64(meta[b, g, :kmax.shape[0], 0]), kmax)
+            np.testing.assert_array_equal(O.bf16_to_f64(meta[b, g, :kmax.shape[0], 1]), kmin)
+
+
+# ----------------------------------------------------------- block scores
+@pytest.mark.parametrize("G,dk", [(4, 128), (1, 64), (8, 256), (32, 576), (16, 128), (3, 128)])
+def test_block_scores_within_fp32_bound(G, dk):
+    w = _wl(n_q_heads=2 * G, n_kv_heads=2, d_k=dk, d_v=dk if dk != 576 else 512,
+            v_alias_k=dk == 576, max_ctx=1500, ctx=1500, n_planted=0, r=16)
+    ctx = np.array([1500, 1093], np.int32)
+    say(f"[score_blocks] G={G} dk={dk} ctx={ctx}")
+    h = T.host_inputs(w, ctx_len=ctx)
+    dev = T.Device(w, h)
+    dev.prefill_meta()
+    d = dev.d
+    sc = torch.full((w.units * d.nb_cap,), float("nan"), device="cuda")
+    dev.H.score_blocks(d, dev.q, dev.meta, dev.ctx_prefill, sc)
+    sc = sc.cpu().numpy().reshape(w.batch, w.n_kv_heads, d.nb_cap)
+    for b in range(w.batch):
+        for g in range(w.n_kv_heads):
+            n = int(ctx[b]) - 1
+            q = O.bf16_to_f64(h["q"][b, g * G:(g + 1) * G])
+            kmax, kmin = O.block_meta(O.bf16_to_f64(h["K"][b, g, :n]), n, w.block)
+            want = O.block_scores(q, kmax, kmin)
+            tol = T.score_tolerance(q, kmax, kmin)
+            nb = len(want)
+            err = np.abs(sc[b, g, :nb] - want)
+            assert np.all(err <= tol), f"unit ({b},{g}) worst {np.max(err / tol):.3g}x the bound"
+            assert np.all(np.isnan(sc[b, g, nb:])), "wrote past the unit's blocks"
+
+
+# ---------------------------------------------------------- whole step
+def test_decode_step_tiny4k_all_stages():
+    w = W.WORKLOADS["tiny4k"]
+    w, h, dev, r = _run_decode(w)
+    st = _check_all_units(w, h, r)
+    pos, _ = W.planted_positions(w, 0, 0)
+    assert set(pos) <= set(r["tok"][0, 0]), "planted tokens must be selected"
+    say("tiny4k", st)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(),                                                         # GQA G=4, ragged
+    dict(n_q_heads=4, n_kv_heads=4, n_planted=2),                   # MHA, G=1
+    dict(n_q_heads=16, n_kv_heads=2, d_k=64, d_v=64),               # G=8, d=64
+    dict(n_q_heads=4, n_kv_heads=2, d_k=256, d_v=256, r=32),        # G=2, d=256, r=32
+    dict(block=32, k_blocks=8, r=32, k_tokens=100),                 # block 32, K_t not a split multiple
+    dict(block=1, k_blocks=200, k_tokens=50, max_ctx=300, ctx=300, n_planted=2),   # block 1: exact top-k
+    dict(label_mode="random", scaled_keys=False, k_tokens=256),
+])
+def test_decode_step_ragged(kw):
+    w = _wl(**kw)
+    ctx = np.array([w.ctx, max(2, (w.ctx * 5) // 7)], np.int32)
+    w, h, dev, r = _run_decode(w, ctx)
+    st = _check_all_units(w, h, r)
+    say(kw, st)
+
+
+def test_decode_step_single_token_and_partial_block():
+    w = _wl(batch=3, max_ctx=64, ctx=64, k_blocks=4, k_tokens=32, n_planted=0)
+    ctx = np.array([1, 7, 64], np.int32)
+    w, h, dev, r = _run_decode(w, ctx)
+    _check_all_units(w, h, r)
+    # n = 1: one block, one token, attention returns that token's value
+    assert list(r["blk"][0, 0]) == [0, -1, -1, -1]
+    assert r["tok"][0, 0][0] == 0 and np.all(r["tok"][0, 0][1:] == -1)
+    v = O.bf16_to_f64(h["v_new"][0, 0])
+    np.testing.assert_allclose(r["out"][0, :w.group], np.tile(v, (w.group, 1)), atol=1e-6)
+
+
+def test_decode_step_dense_limit_equals_full_attention():
+    """K_b >= nb and K_t >= n: every token is kept, the output is dense
+    attention, compared with torch SDPA in fp64 on the CPU."""
+    w = _wl(max_ctx=512, ctx=512, k_blocks=32, k_tokens=512, n_planted=0)
+    ctx = np.array([512, 300], np.int32)
+    w, h, dev, r = _run_decode(w, ctx)
+    K, V = T.appended_cache(w, h)
+    G = w.group
+    for b in range(w.batch):
+        n = int(ctx[b])
+        for g in range(w.n_kv_heads):
+            assert np.array_equal(r["tok"][b, g][:n], np.arange(n))
+            q = torch.tensor(O.bf16_to_f64(h["q"][b, g * G:(g + 1) * G]))
+            k = torch.tensor(O.bf16_to_f64(K[b, g, :n]))
+            v = torch.tensor(O.bf16_to_f64(V[b, g, :n]))
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                q[:, None], k[None].expand(G, -1, -1), v[None].expand(G, -1, -1), scale=w.sm_scale)[:, 0]
+            assert np.max(np.abs(r["out"][b, g * G:(g + 1) * G] - ref.numpy())) <= T.OUT_ATOL
+
+
+def test_exact_ties_go_to_the_lower_index():
+    """Seven bit-identical key blocks, scaled 4x so they outrank every other
+    block, with K_b = 5: scores tie exactly on both sides, and the five
+    lowest block indices must be kept, as in the oracle's stable top-k."""
+    w = _wl(batch=1, n_q_heads=4, n_kv_heads=1, max_ctx=512, ctx=512, k_blocks=5, k_tokens=40, n_planted=0)
+    h = T.host_inputs(w)
+    blk0 = W.f32_to_bf16_bits(W.bf16_bits_to_f32(h["K"][0, 0, 16:32]) * 4.0)
+    tied = [1, 3, 9, 17, 20, 25, 30]
+    for j in tied:
+        h["K"][0, 0, j * 16:(j + 1) * 16] = blk0
+    say("[ties] decode_step with seven duplicated blocks, K_b=5")
+    dev = T.Device(w, h)
+    dev.prefill_meta()
+    dev.decode_step()
+    r = dev.results()
+    assert list(r["blk"][0, 0]) == tied[:5]
+    _check_all_units(w, h, r)
+    # candidates repeat in groups of five identical rows: lower positions win
+    K, _ = T.appended_cache(w, h)
+    q = O.bf16_to_f64(h["q"][0])
+    cand = O.candidate_tokens(np.array(tied[:5]), w.ctx, w.block)
+    s_tok = O.label_scores(q, O.bf16_to_f64(K[0, 0][cand]), h["label"][0])
+    assert list(r["tok"][0, 0]) == list(cand[O.topk_stable(s_tok, w.k_tokens)])
+
+
+def test_decode_step_is_deterministic_and_idempotent():
+    w = _wl()
+    w, h, dev, r1 = _run_decode(w)
+    dev.decode_step()
+    r2 = dev.results()
+    for k in r1:
+        assert np.array_equal(r1[k], r2[k], equal_nan=True), k
+
+
+# ------------------------------------------------------ separate entry points
+def test_select_blocks_tokens_attend_match_decode_step():
+    w = _wl(max_ctx=2048, ctx=2048, k_blocks=24, k_tokens=128)
+    ctx = np.array([2048, 1500], np.int32)
+    w, h, dev, r = _run_decode(w, ctx)
+    H, d = dev.H, dev.d
+    blk = torch.empty_like(dev.blk)
+    H.select_blocks(d, dev.q, dev.meta, dev.ctx, blk, ws=dev.ws)
+    tok = torch.empty_like(dev.tok)
+    ts = torch.empty(w.units * w.k_blocks * w.block, device="cuda")
+    H.select_tokens(d, dev.q, dev.klabel, dev.label, blk, dev.ctx, tok, tok_score=ts)
+    out = torch.empty_like(dev.out)
+    lse = torch.empty_like(dev.lse)
+    H.sparse_attend(d, dev.q, dev.K, dev.V, tok, dev.ctx, out, lse, dev.ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(blk.cpu().numpy().reshape(r["blk"].shape), r["blk"])
+    assert np.array_equal(tok.cpu().numpy().reshape(r["tok"].shape), r["tok"])
+    assert np.array_equal(out.cpu().numpy().reshape(r["out"].shape), r["out"])
+    # token scores: every candidate of every unit within the fp32 bound of the oracle
+    K, V = T.appended_cache(w, h)
+    ts = ts.cpu().numpy().reshape(w.batch, w.n_kv_heads, w.k_blocks * w.block)
+    G = w.group
+    for b in range(w.batch):
+        n = int(ctx[b])
+        for g in range(w.n_kv_heads):
+            q = O.bf16_to_f64(h["q"][b, g * G:(g + 1) * G])
+            Kf = O.bf16_to_f64(K[b, g, :n])
+            bl = r["blk"][b, g]
+            for slot, j in enumerate(bl):
+                seg = ts[b, g, slot * w.block:(slot + 1) * w.block]
+                if j < 0:
+                    assert np.all(seg == -np.inf)
+                    continue
+                toks = np.arange(j * w.block, min(n, (j + 1) * w.block))
+                want = O.label_scores(q, Kf[toks], h["label"][g])
+                lab = h["label"][g]
+                mag = (np.abs(q[:, lab]) @ np.abs(Kf[toks][:, lab]).T).max(axis=0)
+                assert np.all(np.abs(seg[:len(toks)] - want) <= w.r * 2.0 ** -24 * mag + 1e-30)
+                assert np.all(seg[len(toks):] == -np.inf)
+
+
+def test_sparse_attend_skips_padding_and_handles_empty():
+    w = _wl(batch=1, n_q_heads=4, n_kv_heads=1, max_ctx=256, ctx=256, k_tokens=70, n_planted=0)
+    h = T.host_inputs(w)
+    dev = T.Device(w, h)
+    sel = np.sort(np.random.default_rng(5).choice(255, size=33, replace=False)).astype(np.int32)
+    tok = np.full(w.k_tokens, -1, np.int32)
+    tok[:33] = sel
+    out = torch.empty_like(dev.out)
+    lse = torch.empty_like(dev.lse)
+    say("[sparse_attend] 33 of 70 slots used")
+    dev.H.sparse_attend(dev.d, dev.q, dev.K, dev.V, torch.from_numpy(tok).cuda(), dev.ctx, out, lse, dev.ws)
+    torch.cuda.synchronize()
+    q = O.bf16_to_f64(h["q"][0])
+    K = O.bf16_to_f64(h["K"][0, 0])
+    V = O.bf16_to_f64(h["V"][0, 0])
+    o, l = O.attend(q, K[sel], V[sel], w.sm_scale)
+    assert np.max(np.abs(out.cpu().numpy().reshape(4, -1) - o)) <= T.OUT_ATOL
+    np.testing.assert_allclose(lse.cpu().numpy(), l, rtol=T.LSE_RTOL)
+    # all slots empty: out 0, lse -inf
+    dev.H.sparse_attend(dev.d, dev.q, dev.K, dev.V, torch.full((w.k_tokens,), -1, dtype=torch.int32,
+                        device="cuda"), dev.ctx, out, lse, dev.ws)
+    torch.cuda.synchronize()
+    assert np.all(out.cpu().numpy() == 0) and np.all(lse.cpu().numpy() == -np.inf)
+
+
+def test_mla_selection_stages():
+    """Absorbed-MLA shapes (32 heads on one 576-dim latent key, r=32,
+    block 32): block and token selection against the oracle."""
+    w = _wl(batch=2, n_q_heads=32, n_kv_heads=1, d_k=576, d_v=512, v_alias_k=True, block=32, r=32,
+            k_blocks=16, k_tokens=128, max_ctx=2048, ctx=2048, n_planted=0)
+    ctx = np.array([2048, 1111], np.int32)
+    say("[mla select] ", w)
+    h = T.host_inputs(w, ctx_len=ctx)
+    dev = T.Device(w, h)
+    dev.prefill_meta()
+    H, d = dev.H, dev.d
+    H.select_blocks(d, dev.q, dev.meta, dev.ctx_prefill, dev.blk, ws=dev.ws)
+    H.select_tokens(d, dev.q, dev.klabel, dev.label, dev.blk, dev.ctx_prefill, dev.tok)
+    torch.cuda.synchronize()
+    blk = dev.blk.cpu().numpy().reshape(w.batch, 1, w.k_blocks)
+    tok = dev.tok.cpu().numpy().reshape(w.batch, 1, w.k_tokens)
+    for b in range(w.batch):
+        n = int(ctx[b]) - 1
+        q = O.bf16_to_f64(h["q"][b])
+        K = O.bf16_to_f64(h["K"][b, 0, :n])
+        kmax, kmin = O.block_meta(K, n, w.block)
+        bsel, _ = T.check_index_set(O.block_scores(q, kmax, kmin), blk[b, 0], w.k_blocks, "mla blocks")
+        cand = O.candidate_tokens(bsel, n, w.block)
+        s_tok = O.label_scores(q, K[cand], h["label"][0])
+        k_eff = min(w.k_tokens, len(cand))
+        ci = np.searchsorted(cand, tok[b, 0, :k_eff])
+        T.check_index_set(s_tok, np.concatenate([ci, tok[b, 0, k_eff:]]), w.k_tokens, "mla tokens")
+
+
+# ---------------------------------------------------------- full-size layer
+def test_gqa48k_full_size_sampled_units():
+    """The 48k GQA layer in the benchmark's launch configuration: every unit
+    is checked for structural properties and planted-key recall, three
+    sampled units against the oracle."""
+    w = W.WORKLOADS["gqa48k"]
+    w, h, dev, r = _run_decode(w)
+    for b in range(w.batch):
+        for g in range(w.n_kv_heads):
+            pos, _ = W.planted_positions(w, b, g)
+            assert set(pos // w.block) <= set(r["blk"][b, g]), f"planted block missed in ({b},{g})"
+            assert set(pos) <= set(r["tok"][b, g]), f"planted token missed in ({b},{g})"
+            assert np.all(np.diff(r["blk"][b, g]) > 0) and np.all(np.diff(r["tok"][b, g]) > 0)
+    assert np.all(np.isfinite(r["out"])) and np.all(np.isfinite(r["lse"]))
+    st = _check_all_units(w, h, r, units=[(0, 0), (3, 5), (7, 7)])
+    say("gqa48k sampled", st)
