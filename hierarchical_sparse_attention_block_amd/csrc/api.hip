@@ -32,9 +32,9 @@ WsLayout ws_layout(const Shape& s) {
     WsLayout w;
     size_t off = 0;
     w.blk_score = off; off = align256(off + (size_t)s.B * s.Hkv * s.nb_cap * sizeof(float));
-    w.tok_score = off;   // unused: token scores live in LDS
     w.part_ml = off;   off = align256(off + (size_t)s.B * s.Hq * attn_splits(s) * 2 * sizeof(float));
     w.part_acc = off;  off = align256(off + (size_t)s.B * s.Hq * attn_splits(s) * s.dv * sizeof(float));
+    w.arrivals = off;  off = align256(off + (size_t)s.B * s.Hkv * sizeof(int32_t));
     w.total = off;
     return w;
 }
@@ -50,20 +50,13 @@ static int check_dims(const hsab_dims* d) {
     if (d->d_v < 8 || d->d_v % 8 != 0) return HSAB_EINVAL;
     if (d->v_alias_k && d->d_v > d->d_k) return HSAB_EINVAL;
     if (d->block < 1 || d->max_ctx < 1) return HSAB_EINVAL;
-    if (d->r < 16 || d->r % 16 != 0 || d->r > MAX_R || d->r > d->d_k) return HSAB_EINVAL;
+    if ((d->r != 16 && d->r != 32 && d->r != 64 && d->r != 128) || d->r > d->d_k) return HSAB_EINVAL;
     if (d->k_blocks < 1 || d->k_blocks > MAX_KB) return HSAB_EINVAL;
     if ((long)d->k_blocks * d->block > MAX_CAND) return HSAB_EINVAL;
     if (d->k_tokens < 1) return HSAB_EINVAL;
     if ((d->max_ctx + d->block - 1) / d->block > MAX_NB) return HSAB_EINVAL;
     if (!isfinite(d->sm_scale)) return HSAB_EINVAL;
     return HSAB_OK;
-}
-
-static bool attend_supported(const Shape& s) {
-    if (s.valias) return false;
-    if (s.dk != s.dv) return false;
-    if (s.dk != 64 && s.dk != 128 && s.dk != 256) return false;
-    return s.G == 1 || s.G == 2 || s.G == 4 || s.G == 8;
 }
 
 static int hip_status(hipError_t e) {
@@ -108,7 +101,9 @@ int hsab_score_blocks(const hsab_dims* dims, const uint16_t* q, const uint16_t* 
     int rc = check_dims(dims);
     if (rc) return rc;
     if (!q || !meta || !ctx_len || !blk_score) return HSAB_EINVAL;
-    return hip_status(launch_block_score(make_shape(*dims), q, meta, ctx_len, blk_score, stream));
+    return hip_status(launch_block_score(make_shape(*dims), q, const_cast<uint16_t*>(meta), ctx_len,
+                                         blk_score, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                         stream));
 }
 
 int hsab_select_blocks(const hsab_dims* dims, const uint16_t* q, const uint16_t* meta,
@@ -124,10 +119,11 @@ int hsab_select_blocks(const hsab_dims* dims, const uint16_t* q, const uint16_t*
         if (!ws || ws_bytes < L.total) return HSAB_EINVAL;
         scores = reinterpret_cast<float*>(static_cast<char*>(ws) + L.blk_score);
     }
-    rc = hip_status(launch_block_score(s, q, meta, ctx_len, scores, stream));
+    rc = hip_status(launch_block_score(s, q, const_cast<uint16_t*>(meta), ctx_len, scores, nullptr,
+                                       nullptr, nullptr, nullptr, nullptr, nullptr, stream));
     if (rc) return rc;
     return hip_status(launch_select(s, 1, q, scores, nullptr, nullptr, ctx_len, blk_idx, nullptr,
-                                    nullptr, stream));
+                                    nullptr, nullptr, stream));
 }
 
 int hsab_select_tokens(const hsab_dims* dims, const uint16_t* q, const uint16_t* klabel,
@@ -139,7 +135,7 @@ int hsab_select_tokens(const hsab_dims* dims, const uint16_t* q, const uint16_t*
     if (rc) return rc;
     if (!q || !klabel || !label_ch || !blk_idx || !ctx_len || !tok_idx) return HSAB_EINVAL;
     return hip_status(launch_select(make_shape(*dims), 2, q, nullptr, klabel, label_ch, ctx_len,
-                                    const_cast<int32_t*>(blk_idx), tok_idx, tok_score, stream));
+                                    const_cast<int32_t*>(blk_idx), tok_idx, tok_score, nullptr, stream));
 }
 
 int hsab_sparse_attend(const hsab_dims* dims, const uint16_t* q, const uint16_t* K,
@@ -159,7 +155,7 @@ int hsab_sparse_attend(const hsab_dims* dims, const uint16_t* q, const uint16_t*
     char* w = static_cast<char*>(ws);
     return hip_status(launch_attend(s, q, K, s.valias ? K : V, tok_idx, slot_of, n_slots,
                                     reinterpret_cast<float*>(w + L.part_ml),
-                                    reinterpret_cast<float*>(w + L.part_acc), out, lse, stream));
+                                    reinterpret_cast<float*>(w + L.part_acc), nullptr, out, lse, stream));
 }
 
 int hsab_decode_step(const hsab_dims* dims, const uint16_t* q, const uint16_t* k_new,
@@ -179,16 +175,17 @@ int hsab_decode_step(const hsab_dims* dims, const uint16_t* q, const uint16_t* k
     if (!attend_supported(s)) return HSAB_EUNSUPPORTED;
     char* w = static_cast<char*>(ws);
     float* scores = reinterpret_cast<float*>(w + L.blk_score);
-    rc = hip_status(launch_append(s, k_new, v_new, K, V, meta, klabel, label_ch, ctx_len, stream));
+    // 1) append + block scores; 2) top-K_b, label scores, top-K_t (one
+    // workgroup per unit); 3) split attention and the merge of its partials
+    rc = hip_status(launch_block_score(s, q, meta, ctx_len, scores, k_new, v_new, K, V, klabel, label_ch,
+                                       stream));
     if (rc) return rc;
-    rc = hip_status(launch_block_score(s, q, meta, ctx_len, scores, stream));
-    if (rc) return rc;
-    rc = hip_status(launch_select(s, 3, q, scores, klabel, label_ch, ctx_len, blk_idx, tok_idx,
+    rc = hip_status(launch_select(s, 3, q, scores, klabel, label_ch, ctx_len, blk_idx, tok_idx, nullptr,
                                   nullptr, stream));
     if (rc) return rc;
     return hip_status(launch_attend(s, q, K, s.valias ? K : V, tok_idx, nullptr, 0,
                                     reinterpret_cast<float*>(w + L.part_ml),
-                                    reinterpret_cast<float*>(w + L.part_acc), out, lse, stream));
+                                    reinterpret_cast<float*>(w + L.part_acc), nullptr, out, lse, stream));
 }
 
 }  // extern "C"

@@ -8,8 +8,15 @@
 // gathers 64/(D/8) whole key rows. Logits are fp32 (bf16 products are
 // exact in fp32), kept in base-2 units (q pre-scaled by sm_scale*log2 e).
 // Each wave keeps (max, sum, weighted values) per head; the workgroup
-// merges its four waves and writes one partial per head. The combine
-// kernel merges the partials of all splits.
+// merges its four waves and writes one partial per head. The partials of
+// all splits are merged either by a separate combine kernel or by the last
+// split of the unit to finish (arrival counter per unit, zeroed by the
+// selection kernel that runs before): fence, count, and the last arrival
+// reads every split's partial.
+//
+// Workgroup numbering: the dispatcher hands consecutive workgroups to the
+// eight XCDs in turn, so workgroup L runs on XCD L % 8. All splits of a unit
+// are given the same L % 8, which keeps that unit's partials in one L2.
 #include "common.h"
 #include "kernels.h"
 
@@ -37,12 +44,13 @@ __device__ __forceinline__ long row_of(int t, int unit, int bs, int max_ctx, int
     return ((long)unit * n_slots + slot) * bs + (t - blk * bs);
 }
 
-template <int D, int G>
+template <int D, int G, bool MERGE>
 __global__ __launch_bounds__(256) void attend_gqa_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const int32_t* __restrict__ tok_idx, const int32_t* __restrict__ slot_of, int n_slots,
     float* __restrict__ part_ml, float* __restrict__ part_acc, int Hkv, int bs, int kt,
-    int max_ctx, int nb_cap, int n_splits, float scale2) {
+    int max_ctx, int nb_cap, int n_splits, int units, float scale2, int32_t* __restrict__ arrivals,
+    float* __restrict__ out, float* __restrict__ lse) {
     constexpr int LPT = D / 8;                         // lanes per token
     constexpr int TPI = 64 / LPT;                      // tokens per wave load
     constexpr int TPW = ATT_TOK_PER_SPLIT / 4;         // tokens per wave
@@ -51,7 +59,10 @@ __global__ __launch_bounds__(256) void attend_gqa_kernel(
     __shared__ float s_m[4][G], s_l[4][G];
     __shared__ float s_acc[4][G][D];
 
-    const int split = blockIdx.x, unit = blockIdx.y, b = unit / Hkv, g = unit % Hkv;
+    const int xcd = blockIdx.x & 7, y = blockIdx.x >> 3;
+    const int unit = (y / n_splits) * 8 + xcd, split = y % n_splits;
+    if (unit >= units) return;
+    const int b = unit / Hkv, g = unit % Hkv;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int cc = lane % LPT, ts = lane / LPT;
 
@@ -164,6 +175,35 @@ __global__ __launch_bounds__(256) void attend_gqa_kernel(
             part_ml[(bh * n_splits + split) * 2 + 1] = L;
         }
     }
+    if constexpr (MERGE) {
+        __shared__ int s_last;
+        __threadfence();
+        __syncthreads();
+        if (threadIdx.x == 0) s_last = atomicAdd(&arrivals[unit], 1) == n_splits - 1;
+        __syncthreads();
+        if (!s_last) return;
+        __threadfence();
+        for (int p = threadIdx.x; p < G * D; p += blockDim.x) {
+            const int h = p / D, c = p - h * D;
+            const size_t bh = (size_t)(b * Hkv + g) * G + h;
+            const float* ml = part_ml + bh * n_splits * 2;
+            float M = -INFINITY;
+            for (int sp = 0; sp < n_splits; ++sp) M = fmaxf(M, ml[2 * sp]);
+            float L = 0.f, A = 0.f;
+            if (M != -INFINITY) {
+                for (int sp = 0; sp < n_splits; ++sp) {
+                    const float ms = ml[2 * sp];
+                    if (ms == -INFINITY) continue;
+                    const float wt = exp2f(ms - M);
+                    L = fmaf(ml[2 * sp + 1], wt, L);
+                    A = fmaf(part_acc[(bh * n_splits + sp) * D + c], wt, A);
+                }
+            }
+            out[bh * D + c] = L > 0.f ? A / L : 0.f;
+            if (c == 0) lse[bh] = L > 0.f ? (M + log2f(L)) * LN2 : -INFINITY;
+        }
+        if (threadIdx.x == 0) arrivals[unit] = 0;
+    }
 }
 
 // grid: (B*Hq). Merges the split partials of one query head.
@@ -196,44 +236,57 @@ __global__ __launch_bounds__(256) void combine_kernel(
 template <int D, int G>
 hipError_t launch_gqa(const Shape& s, const uint16_t* q, const uint16_t* K, const uint16_t* V,
                       const int32_t* tok_idx, const int32_t* slot_of, int n_slots, float* part_ml,
-                      float* part_acc, hipStream_t st) {
+                      float* part_acc, int32_t* arrivals, float* out, float* lse, hipStream_t st) {
     const int ns = attn_splits(s);
-    hipLaunchKernelGGL((attend_gqa_kernel<D, G>), dim3(ns, s.B * s.Hkv), dim3(256), 0, st, q, K, V,
-                       tok_idx, slot_of, n_slots, part_ml, part_acc, s.Hkv, s.bs, s.kt, s.max_ctx,
-                       s.nb_cap, ns, s.sm_scale * LOG2E);
+    const int units = s.B * s.Hkv;
+    const dim3 grid(((units + 7) / 8) * 8 * ns);
+    if (arrivals) {
+        hipLaunchKernelGGL((attend_gqa_kernel<D, G, true>), grid, dim3(256), 0, st, q, K, V, tok_idx, slot_of,
+                           n_slots, part_ml, part_acc, s.Hkv, s.bs, s.kt, s.max_ctx, s.nb_cap, ns, units,
+                           s.sm_scale * LOG2E, arrivals, out, lse);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL((attend_gqa_kernel<D, G, false>), grid, dim3(256), 0, st, q, K, V, tok_idx, slot_of,
+                       n_slots, part_ml, part_acc, s.Hkv, s.bs, s.kt, s.max_ctx, s.nb_cap, ns, units,
+                       s.sm_scale * LOG2E, nullptr, nullptr, nullptr);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(combine_kernel, dim3(s.B * s.Hq), dim3(s.dv < 256 ? 128 : 256), 0, st, part_ml,
+                       part_acc, out, lse, s.dv, ns);
     return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_gqa_d(const Shape& s, const uint16_t* q, const uint16_t* K, const uint16_t* V,
                         const int32_t* tok_idx, const int32_t* slot_of, int n_slots, float* part_ml,
-                        float* part_acc, hipStream_t st) {
+                        float* part_acc, int32_t* arrivals, float* out, float* lse, hipStream_t st) {
     switch (s.G) {
-        case 1: return launch_gqa<D, 1>(s, q, K, V, tok_idx, slot_of, n_slots, part_ml, part_acc, st);
-        case 2: return launch_gqa<D, 2>(s, q, K, V, tok_idx, slot_of, n_slots, part_ml, part_acc, st);
-        case 4: return launch_gqa<D, 4>(s, q, K, V, tok_idx, slot_of, n_slots, part_ml, part_acc, st);
-        case 8: return launch_gqa<D, 8>(s, q, K, V, tok_idx, slot_of, n_slots, part_ml, part_acc, st);
+        case 1: return launch_gqa<D, 1>(s, q, K, V, tok_idx, slot_of, n_slots, part_ml, part_acc, arrivals, out, lse, st);
+        case 2: return launch_gqa<D, 2>(s, q, K, V, tok_idx, slot_of, n_slots, part_ml, part_acc, arrivals, out, lse, st);
+        case 4: return launch_gqa<D, 4>(s, q, K, V, tok_idx, slot_of, n_slots, part_ml, part_acc, arrivals, out, lse, st);
+        case 8: return launch_gqa<D, 8>(s, q, K, V, tok_idx, slot_of, n_slots, part_ml, part_acc, arrivals, out, lse, st);
         default: return hipErrorInvalidValue;
     }
 }
 
 }  // namespace
 
+bool attend_supported(const Shape& s) {
+    return !s.valias && s.dk == s.dv && (s.dk == 64 || s.dk == 128 || s.dk == 256) &&
+           (s.G == 1 || s.G == 2 || s.G == 4 || s.G == 8);
+}
+
 hipError_t launch_attend(const Shape& s, const uint16_t* q, const uint16_t* K, const uint16_t* V,
                          const int32_t* tok_idx, const int32_t* slot_of, int n_slots,
-                         float* part_ml, float* part_acc, float* out, float* lse, hipStream_t st) {
-    hipError_t e;
-    if (s.valias || s.dk != s.dv) return hipErrorInvalidValue;
+                         float* part_ml, float* part_acc, int32_t* arrivals, float* out, float* lse,
+                         hipStream_t st) {
+    if (!attend_supported(s)) return hipErrorInvalidValue;
     switch (s.dk) {
-        case 64: e = launch_gqa_d<64>(s, q, K, V, tok_idx, slot_of, n_slots, part_ml, part_acc, st); break;
-        case 128: e = launch_gqa_d<128>(s, q, K, V, tok_idx, slot_of, n_slots, part_ml, part_acc, st); break;
-        case 256: e = launch_gqa_d<256>(s, q, K, V, tok_idx, slot_of, n_slots, part_ml, part_acc, st); break;
+        case 64: return launch_gqa_d<64>(s, q, K, V, tok_idx, slot_of, n_slots, part_ml, part_acc, arrivals, out, lse, st);
+        case 128: return launch_gqa_d<128>(s, q, K, V, tok_idx, slot_of, n_slots, part_ml, part_acc, arrivals, out, lse, st);
+        case 256: return launch_gqa_d<256>(s, q, K, V, tok_idx, slot_of, n_slots, part_ml, part_acc, arrivals, out, lse, st);
         default: return hipErrorInvalidValue;
     }
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(combine_kernel, dim3(s.B * s.Hq), dim3(s.dv < 256 ? 128 : 256), 0, st, part_ml,
-                       part_acc, out, lse, s.dv, attn_splits(s));
-    return hipGetLastError();
 }
 
 }  // namespace hsab

@@ -8,7 +8,7 @@
 namespace hsab {
 
 // Limits enforced by the C-ABI validation and assumed by the kernels.
-constexpr int MAX_NB = 16384;        // blocks per unit (block-score top-k keys)
+constexpr int MAX_NB = 8192;         // blocks per unit (block-score top-k keys)
 constexpr int MAX_CAND = 8192;       // K_b * block (token-score top-k keys)
 constexpr int MAX_KB = 2048;         // K_b
 constexpr int MAX_G = 32;            // query heads per KV head
@@ -26,24 +26,30 @@ int attn_splits(const Shape& s);
 
 // workspace carve-up (byte offsets, 256-aligned)
 struct WsLayout {
-    size_t blk_score, tok_score, part_ml, part_acc, total;
+    size_t blk_score, part_ml, part_acc, arrivals, total;
 };
 WsLayout ws_layout(const Shape& s);
 
 hipError_t launch_build_meta(const Shape& s, const uint16_t* K, const int32_t* ctx_len,
                              const int32_t* label_ch, uint16_t* meta, uint16_t* klabel,
                              hipStream_t st);
-hipError_t launch_append(const Shape& s, const uint16_t* k_new, const uint16_t* v_new,
-                         uint16_t* K, uint16_t* V, uint16_t* meta, uint16_t* klabel,
-                         const int32_t* label_ch, const int32_t* ctx_len, hipStream_t st);
-hipError_t launch_block_score(const Shape& s, const uint16_t* q, const uint16_t* meta,
-                              const int32_t* ctx_len, float* score, hipStream_t st);
-// mode bit 1: select blocks from block scores; bit 2: score + select tokens
+// Block scores; with k_new non-null the decode-step append runs first
+// (inside the workgroup that owns each unit's tail block).
+hipError_t launch_block_score(const Shape& s, const uint16_t* q, uint16_t* meta, const int32_t* ctx_len,
+                              float* score, const uint16_t* k_new, const uint16_t* v_new, uint16_t* K,
+                              uint16_t* V, uint16_t* klabel, const int32_t* label_ch, hipStream_t st);
+// mode bit 1: select blocks from block scores; bit 2: score + select tokens.
+// arrivals (nullable): per-unit counters zeroed for the attention merge.
 hipError_t launch_select(const Shape& s, int mode, const uint16_t* q, const float* blk_score,
                          const uint16_t* klabel, const int32_t* label_ch, const int32_t* ctx_len,
-                         int32_t* blk_idx, int32_t* tok_idx, float* tok_score, hipStream_t st);
+                         int32_t* blk_idx, int32_t* tok_idx, float* tok_score, int32_t* arrivals,
+                         hipStream_t st);
+bool attend_supported(const Shape& s);
+// Split attention; with arrivals non-null (zeroed beforehand) the last split
+// of each unit merges the partials, otherwise a combine kernel follows.
 hipError_t launch_attend(const Shape& s, const uint16_t* q, const uint16_t* K, const uint16_t* V,
                          const int32_t* tok_idx, const int32_t* slot_of, int n_slots,
-                         float* part_ml, float* part_acc, float* out, float* lse, hipStream_t st);
+                         float* part_ml, float* part_acc, int32_t* arrivals, float* out, float* lse,
+                         hipStream_t st);
 
 }  // namespace hsab

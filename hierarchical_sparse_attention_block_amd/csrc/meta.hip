@@ -1,5 +1,6 @@
-// Block metadata: channelwise key max/min per block and the label-channel
-// key copy. Blocks summarised by key max/min follow the AsyncTLS coarse
+// Block metadata from a prefilled cache: channelwise key max/min per block
+// and the label-channel key copy (the per-step append lives with the block
+// scoring kernel). Blocks summarised by key max/min follow the AsyncTLS coarse
 // stage (gist.science/de explainer, section 2.A "Stufe 1"); the label copy
 // is the compressed key of the fine stage (gist.science/es explainer,
 // section 2.A item 2). Both are exact bf16 copies / comparisons.
@@ -60,45 +61,6 @@ __global__ __launch_bounds__(256) void build_meta_kernel(
     }
 }
 
-// grid: (B). Appends the token at position ctx_len[b]-1 of every KV head.
-__global__ __launch_bounds__(256) void append_kernel(
-    const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
-    uint16_t* __restrict__ K, uint16_t* __restrict__ V, uint16_t* __restrict__ meta,
-    uint16_t* __restrict__ klabel, const int32_t* __restrict__ label_ch,
-    const int32_t* __restrict__ ctx_len, int Hkv, int dk, int dv, int valias, int bs, int r,
-    int max_ctx, int nb_cap) {
-    const int b = blockIdx.x;
-    const int pos = ctx_len[b] - 1;
-    if (pos < 0 || pos >= max_ctx) return;
-    const int j = pos / bs;
-    const bool first = (pos % bs) == 0;
-    for (int g = 0; g < Hkv; ++g) {
-        const int unit = b * Hkv + g;
-        const uint16_t* kn = k_new + (size_t)unit * dk;
-        uint16_t* Krow = K + ((size_t)unit * max_ctx + pos) * dk;
-        uint16_t* M = meta + ((size_t)unit * nb_cap + j) * 2 * dk;
-        for (int c = threadIdx.x; c < dk; c += blockDim.x) {
-            const uint16_t kb = kn[c];
-            Krow[c] = kb;
-            if (first) {
-                M[c] = kb;
-                M[dk + c] = kb;
-            } else {
-                const float kf = bf16_f32(kb);
-                if (kf > bf16_f32(M[c])) M[c] = kb;
-                if (kf < bf16_f32(M[dk + c])) M[dk + c] = kb;
-            }
-        }
-        if (!valias) {
-            const uint16_t* vn = v_new + (size_t)unit * dv;
-            uint16_t* Vrow = V + ((size_t)unit * max_ctx + pos) * dv;
-            for (int c = threadIdx.x; c < dv; c += blockDim.x) Vrow[c] = vn[c];
-        }
-        uint16_t* Lrow = klabel + ((size_t)unit * max_ctx + pos) * r;
-        for (int c = threadIdx.x; c < r; c += blockDim.x) Lrow[c] = kn[clamp_ch(label_ch[g * r + c], dk)];
-    }
-}
-
 }  // namespace
 
 hipError_t launch_build_meta(const Shape& s, const uint16_t* K, const int32_t* ctx_len,
@@ -107,14 +69,6 @@ hipError_t launch_build_meta(const Shape& s, const uint16_t* K, const int32_t* c
     dim3 grid((s.nb_cap + META_BLOCKS_PER_WG - 1) / META_BLOCKS_PER_WG, s.B * s.Hkv);
     hipLaunchKernelGGL(build_meta_kernel, grid, dim3(256), 0, st, K, ctx_len, label_ch, meta, klabel,
                        s.Hkv, s.dk, s.bs, s.r, s.max_ctx, s.nb_cap);
-    return hipGetLastError();
-}
-
-hipError_t launch_append(const Shape& s, const uint16_t* k_new, const uint16_t* v_new,
-                         uint16_t* K, uint16_t* V, uint16_t* meta, uint16_t* klabel,
-                         const int32_t* label_ch, const int32_t* ctx_len, hipStream_t st) {
-    hipLaunchKernelGGL(append_kernel, dim3(s.B), dim3(256), 0, st, k_new, v_new, K, V, meta, klabel,
-                       label_ch, ctx_len, s.Hkv, s.dk, s.dv, s.valias, s.bs, s.r, s.max_ctx, s.nb_cap);
     return hipGetLastError();
 }
 

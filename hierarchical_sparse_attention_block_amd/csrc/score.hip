@@ -27,19 +27,63 @@ namespace {
 
 constexpr int SCORE_WAVES = 4;
 
+// Token append of a decode step (optional): the new key/value rows land at
+// position n-1, the tail block's max/min widen to include the key (or start
+// from it when it opens a new block), and the label row is copied.
+struct Append {
+    const uint16_t* k_new;    // [B][Hkv][dk], null: no append
+    const uint16_t* v_new;    // [B][Hkv][dv]
+    uint16_t* K;
+    uint16_t* V;              // null when values alias keys
+    uint16_t* klabel;
+    const int32_t* label_ch;
+    int dv, r;
+};
+
 template <int MT, int KSMAX>
 __global__ __launch_bounds__(256) void block_score_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ meta,
+    const uint16_t* __restrict__ q, uint16_t* __restrict__ meta,
     const int32_t* __restrict__ ctx_len, float* __restrict__ score,
-    int Hkv, int G, int dk, int bs, int max_ctx, int nb_cap, int tiles_per_wave) {
+    int Hkv, int G, int dk, int bs, int max_ctx, int nb_cap, int tiles_per_wave, Append ap) {
     __shared__ uint4 qa[MT * KSMAX * 64];   // A fragments [mt][step][lane]
 
     const int unit = blockIdx.y, b = unit / Hkv, g = unit % Hkv;
     int n = ctx_len[b];
     n = n < 1 ? 1 : (n > max_ctx ? max_ctx : n);
     const int nb = (n + bs - 1) / bs;
-    const int j_wg = blockIdx.x * (SCORE_WAVES * tiles_per_wave * 16);
+    const int per_wg = SCORE_WAVES * tiles_per_wave * 16;
+    const int j_wg = blockIdx.x * per_wg;
     if (j_wg >= nb) return;
+
+    if (ap.k_new && nb - 1 < j_wg + per_wg) {
+        // this workgroup owns the tail block: append before scoring it
+        const int pos = n - 1, jt = pos / bs;
+        const bool first = (pos % bs) == 0;
+        const uint16_t* kn = ap.k_new + (size_t)unit * dk;
+        uint16_t* Mt = meta + ((size_t)unit * nb_cap + jt) * 2 * dk;
+        uint16_t* Krow = ap.K + ((size_t)unit * max_ctx + pos) * dk;
+        for (int c = threadIdx.x; c < dk; c += blockDim.x) {
+            const uint16_t kb = kn[c];
+            Krow[c] = kb;
+            if (first) {
+                Mt[c] = kb;
+                Mt[dk + c] = kb;
+            } else {
+                const float kf = bf16_f32(kb);
+                if (kf > bf16_f32(Mt[c])) Mt[c] = kb;
+                if (kf < bf16_f32(Mt[dk + c])) Mt[dk + c] = kb;
+            }
+        }
+        if (ap.V) {
+            const uint16_t* vn = ap.v_new + (size_t)unit * ap.dv;
+            uint16_t* Vrow = ap.V + ((size_t)unit * max_ctx + pos) * ap.dv;
+            for (int c = threadIdx.x; c < ap.dv; c += blockDim.x) Vrow[c] = vn[c];
+        }
+        uint16_t* Lrow = ap.klabel + ((size_t)unit * max_ctx + pos) * ap.r;
+        for (int c = threadIdx.x; c < ap.r; c += blockDim.x)
+            Lrow[c] = kn[clamp_ch(ap.label_ch[g * ap.r + c], dk)];
+        __syncthreads();   // the tail block's new bounds are read below
+    }
 
     const int KS = dk / 16;        // steps of 32 over 2*dk stacked channels
     const int CH = dk / 8;         // 8-channel chunks in one half
@@ -99,8 +143,8 @@ __global__ __launch_bounds__(256) void block_score_kernel(
 }
 
 template <int MT, int KSMAX>
-hipError_t launch_t(const Shape& s, const uint16_t* q, const uint16_t* meta, const int32_t* ctx_len,
-                    float* score, hipStream_t st) {
+hipError_t launch_t(const Shape& s, const uint16_t* q, uint16_t* meta, const int32_t* ctx_len,
+                    float* score, const Append& ap, hipStream_t st) {
     const int tiles_per_unit = (s.nb_cap + 15) / 16;
     const long total_wave_tiles = (long)tiles_per_unit * s.B * s.Hkv / SCORE_WAVES;
     // aim for ~2048 workgroups (8 per CU) before giving a wave more tiles
@@ -109,25 +153,27 @@ hipError_t launch_t(const Shape& s, const uint16_t* q, const uint16_t* meta, con
     const int per_wg = SCORE_WAVES * tpw * 16;
     dim3 grid((s.nb_cap + per_wg - 1) / per_wg, s.B * s.Hkv);
     hipLaunchKernelGGL((block_score_kernel<MT, KSMAX>), grid, dim3(64 * SCORE_WAVES), 0, st, q, meta,
-                       ctx_len, score, s.Hkv, s.G, s.dk, s.bs, s.max_ctx, s.nb_cap, tpw);
+                       ctx_len, score, s.Hkv, s.G, s.dk, s.bs, s.max_ctx, s.nb_cap, tpw, ap);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_block_score(const Shape& s, const uint16_t* q, const uint16_t* meta,
-                              const int32_t* ctx_len, float* score, hipStream_t st) {
+hipError_t launch_block_score(const Shape& s, const uint16_t* q, uint16_t* meta, const int32_t* ctx_len,
+                              float* score, const uint16_t* k_new, const uint16_t* v_new, uint16_t* K,
+                              uint16_t* V, uint16_t* klabel, const int32_t* label_ch, hipStream_t st) {
+    const Append ap{k_new, v_new, K, s.valias ? nullptr : V, klabel, label_ch, s.dv, s.r};
     const int ks = s.dk / 16;
     if (s.G <= 16) {
-        if (ks <= 8) return launch_t<1, 8>(s, q, meta, ctx_len, score, st);
-        if (ks <= 16) return launch_t<1, 16>(s, q, meta, ctx_len, score, st);
-        if (ks <= 36) return launch_t<1, 36>(s, q, meta, ctx_len, score, st);
-        return launch_t<1, 64>(s, q, meta, ctx_len, score, st);
+        if (ks <= 8) return launch_t<1, 8>(s, q, meta, ctx_len, score, ap, st);
+        if (ks <= 16) return launch_t<1, 16>(s, q, meta, ctx_len, score, ap, st);
+        if (ks <= 36) return launch_t<1, 36>(s, q, meta, ctx_len, score, ap, st);
+        return launch_t<1, 64>(s, q, meta, ctx_len, score, ap, st);
     }
-    if (ks <= 8) return launch_t<2, 8>(s, q, meta, ctx_len, score, st);
-    if (ks <= 16) return launch_t<2, 16>(s, q, meta, ctx_len, score, st);
-    if (ks <= 36) return launch_t<2, 36>(s, q, meta, ctx_len, score, st);
-    return launch_t<2, 64>(s, q, meta, ctx_len, score, st);
+    if (ks <= 8) return launch_t<2, 8>(s, q, meta, ctx_len, score, ap, st);
+    if (ks <= 16) return launch_t<2, 16>(s, q, meta, ctx_len, score, ap, st);
+    if (ks <= 36) return launch_t<2, 36>(s, q, meta, ctx_len, score, ap, st);
+    return launch_t<2, 64>(s, q, meta, ctx_len, score, ap, st);
 }
 
 }  // namespace hsab

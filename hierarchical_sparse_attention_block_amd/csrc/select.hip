@@ -7,8 +7,9 @@
 // Label score of token t: max over the group's query heads of
 // sum_c q_h[label_ch[c]] * klabel[t][c], on v_mfma_f32_16x16x16_bf16 with
 // 16 candidate tokens per tile (lane l: token l % 16, 4 channels of step s
-// at 16*s + 4*(l/16)); the group's label-channel queries are A.
-// Selection keeps all scores in registers/LDS; see TopK in common.h.
+// at 16*s + 4*(l/16)); the group's label-channel queries are A. Each wave
+// issues eight label-row loads before its MFMAs. Selection keeps all
+// scores in registers and LDS (TopK in common.h).
 #include "common.h"
 #include "kernels.h"
 
@@ -24,19 +25,40 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
     int mode, const uint16_t* __restrict__ q, const float* __restrict__ blk_score,
     const uint16_t* __restrict__ klabel, const int32_t* __restrict__ label_ch,
     const int32_t* __restrict__ ctx_len, int32_t* __restrict__ blk_idx, int32_t* __restrict__ tok_idx,
-    float* __restrict__ tok_score, int Hkv, int G, int dk, int bs, int r, int kb, int kt,
-    int max_ctx, int nb_cap) {
+    float* __restrict__ tok_score, int32_t* __restrict__ arrivals, int Hkv, int G, int dk, int bs, int r,
+    int kb, int kt, int max_ctx, int nb_cap) {
     using Sel = TopK<SEL_WAVES, PT>;
     __shared__ uint32_t s_key[MAX_CAND];
     __shared__ int32_t s_blk[MAX_KB];
     __shared__ uint2 s_qa[2 * (MAX_R / 16) * 64];
-    __shared__ uint32_t s_red[Sel::LDS_WORDS];
+    __shared__ typename Sel::Smem s_sel;
 
     const int unit = blockIdx.x, b = unit / Hkv, g = unit % Hkv;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    if (arrivals && threadIdx.x == 0) arrivals[unit] = 0;   // for the attention split merge
     int n = ctx_len[b];
     n = n < 1 ? 1 : (n > max_ctx ? max_ctx : n);
     const int nb = (n + bs - 1) / bs;
+    const uint16_t* qg = q + ((size_t)b * Hkv * G + (size_t)g * G) * dk;
+
+    // label-channel A fragments (independent of the block selection)
+    const int MT = (G + 15) / 16;
+    const int KSr = r / 16;
+    if (mode & 2) {
+        const int32_t* lab = label_ch + g * r;
+        for (int e = threadIdx.x; e < MT * KSr * 64; e += SEL_THREADS) {
+            const int l = e & 63, s = (e >> 6) % KSr, mt = e / (64 * KSr);
+            const int m = mt * 16 + (l & 15);
+            const int c0 = s * 16 + (l >> 4) * 4;
+            uint32_t x = 0, y = 0;
+            if (m < G) {
+                const uint16_t* qh = qg + (size_t)m * dk;
+                x = (uint32_t)qh[clamp_ch(lab[c0], dk)] | ((uint32_t)qh[clamp_ch(lab[c0 + 1], dk)] << 16);
+                y = (uint32_t)qh[clamp_ch(lab[c0 + 2], dk)] | ((uint32_t)qh[clamp_ch(lab[c0 + 3], dk)] << 16);
+            }
+            s_qa[(mt * (MAX_R / 16) + s) * 64 + l] = make_uint2(x, y);
+        }
+    }
 
     // ------------------------------------------------------------ blocks
     if (mode & 1) {
@@ -48,37 +70,19 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
             const int i = (w * pt + j) * 64 + lane;
             key[j] = (j < pt && i < nb) ? f32_key(S[i]) : 0u;
         }
-        int32_t* out = blk_idx + (size_t)unit * kb;
-        const int keff = Sel::select(key, pt, kb, s_red, [&](int pos, int i) {
+        int32_t* bo = blk_idx + (size_t)unit * kb;
+        const int keff = Sel::select(key, pt, kb, s_sel, [&](int pos, int i) {
             s_blk[pos] = i;
-            out[pos] = i;
+            bo[pos] = i;
         });
         for (int p = keff + threadIdx.x; p < kb; p += SEL_THREADS) {
             s_blk[p] = -1;
-            out[p] = -1;
+            bo[p] = -1;
         }
     } else {
         for (int p = threadIdx.x; p < kb; p += SEL_THREADS) s_blk[p] = blk_idx[(size_t)unit * kb + p];
     }
     if (!(mode & 2)) return;
-
-    // --------------------------------------------- label-channel A fragments
-    const int MT = (G + 15) / 16;
-    const int KSr = r / 16;
-    const uint16_t* qg = q + ((size_t)b * Hkv * G + (size_t)g * G) * dk;
-    const int32_t* lab = label_ch + g * r;
-    for (int e = threadIdx.x; e < MT * KSr * 64; e += SEL_THREADS) {
-        const int l = e & 63, s = (e >> 6) % KSr, mt = e / (64 * KSr);
-        const int m = mt * 16 + (l & 15);
-        const int c0 = s * 16 + (l >> 4) * 4;
-        uint32_t x = 0, y = 0;
-        if (m < G) {
-            const uint16_t* qh = qg + (size_t)m * dk;
-            x = (uint32_t)qh[clamp_ch(lab[c0], dk)] | ((uint32_t)qh[clamp_ch(lab[c0 + 1], dk)] << 16);
-            y = (uint32_t)qh[clamp_ch(lab[c0 + 2], dk)] | ((uint32_t)qh[clamp_ch(lab[c0 + 3], dk)] << 16);
-        }
-        s_qa[(mt * (MAX_R / 16) + s) * 64 + l] = make_uint2(x, y);
-    }
     __syncthreads();   // s_blk and s_qa complete
 
     // -------------------------------------------------- token label scores
@@ -86,62 +90,79 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
     const uint16_t* Lu = klabel + (size_t)unit * max_ctx * r;
     float* TS = tok_score ? tok_score + (size_t)unit * ncand : nullptr;
     const int n_tiles = (ncand + 15) / 16;
-    for (int tile = w; tile < n_tiles; tile += SEL_WAVES) {
-        const int i = tile * 16 + (lane & 15);
-        const int slot = i / bs, off = i - slot * bs;
-        const int blk = (i < ncand) ? s_blk[slot] : -1;
-        const int pos = blk * bs + off;
-        const bool valid = blk >= 0 && blk < nb && pos < n;
-        const uint16_t* row = Lu + (size_t)(valid ? pos : 0) * r + (lane >> 4) * 4;
+    // eight 8-byte label loads in flight per lane: load u feeds step
+    // u % KSr of tile u / KSr of the batch (KSr is a power of two <= 8)
+    const int lg = KSr == 1 ? 0 : KSr == 2 ? 1 : KSr == 4 ? 2 : 3;
+    const int tb = 8 >> lg;                         // tiles per batch
+    for (int t0 = w; t0 < n_tiles; t0 += SEL_WAVES * tb) {
+        uint2 bf[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int tile = t0 + (u >> lg) * SEL_WAVES, st = u & (KSr - 1);
+            const int i = tile * 16 + (lane & 15);
+            const int slot = i / bs, off = i - slot * bs;
+            const int blk = (tile < n_tiles && i < ncand) ? s_blk[slot] : -1;
+            const int pos = blk * bs + off;
+            const bool valid = blk >= 0 && blk < nb && pos < n;
+            bf[u] = ldg8(Lu + (size_t)(valid ? pos : 0) * r + (lane >> 4) * 4 + st * 16);
+        }
         f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-        for (int s = 0; s < KSr; ++s) {
-            const i16x4_t bfrag = as_i16x4(ldg8(row + s * 16));
-            acc0 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_i16x4(s_qa[s * 64 + lane]), bfrag, acc0, 0, 0, 0);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int tile = t0 + (u >> lg) * SEL_WAVES, st = u & (KSr - 1);
+            if (st == 0) acc0 = acc1 = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            const i16x4_t bfrag = as_i16x4(bf[u]);
+            acc0 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_i16x4(s_qa[st * 64 + lane]), bfrag, acc0, 0, 0, 0);
             if (MT > 1)
                 acc1 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-                    as_i16x4(s_qa[((MAX_R / 16) + s) * 64 + lane]), bfrag, acc1, 0, 0, 0);
-        }
-        float v = -INFINITY;
+                    as_i16x4(s_qa[((MAX_R / 16) + st) * 64 + lane]), bfrag, acc1, 0, 0, 0);
+            if (st == KSr - 1 && tile < n_tiles) {
+                float v = -INFINITY;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int h = (lane >> 4) * 4 + e;
-            if (h < G) v = fmaxf(v, acc0[e]);
-            if (16 + h < G) v = fmaxf(v, acc1[e]);
-        }
-        v = fmaxf(v, __shfl_xor(v, 16));
-        v = fmaxf(v, __shfl_xor(v, 32));
-        if (lane < 16 && i < ncand) {
-            s_key[i] = valid ? f32_key(v) : 0u;
-            if (TS) TS[i] = valid ? v : -INFINITY;
+                for (int e = 0; e < 4; ++e) {
+                    const int h = (lane >> 4) * 4 + e;
+                    if (h < G) v = fmaxf(v, acc0[e]);
+                    if (16 + h < G) v = fmaxf(v, acc1[e]);
+                }
+                v = fmaxf(v, __shfl_xor(v, 16));
+                v = fmaxf(v, __shfl_xor(v, 32));
+                const int i = tile * 16 + (lane & 15);
+                if (lane < 16 && i < ncand) {
+                    const int slot = i / bs, off = i - slot * bs;
+                    const int blk = s_blk[slot];
+                    const int pos = blk * bs + off;
+                    const bool valid = blk >= 0 && blk < nb && pos < n;
+                    s_key[i] = valid ? f32_key(v) : 0u;
+                    if (TS) TS[i] = valid ? v : -INFINITY;
+                }
+            }
         }
     }
     __syncthreads();
 
     // ----------------------------------------------------------- top-K_t
-    {
-        const int pt = (ncand + SEL_THREADS - 1) / SEL_THREADS;
-        uint32_t key[PT];
+    const int pt = (ncand + SEL_THREADS - 1) / SEL_THREADS;
+    uint32_t key[PT];
 #pragma unroll
-        for (int j = 0; j < PT; ++j) {
-            const int i = (w * pt + j) * 64 + lane;
-            key[j] = (j < pt && i < ncand) ? s_key[i] : 0u;
-        }
-        int32_t* out = tok_idx + (size_t)unit * kt;
-        const int keff = Sel::select(key, pt, kt, s_red, [&](int p, int i) {
-            const int slot = i / bs;
-            out[p] = s_blk[slot] * bs + (i - slot * bs);
-        });
-        for (int p = keff + threadIdx.x; p < kt; p += SEL_THREADS) out[p] = -1;
+    for (int j = 0; j < PT; ++j) {
+        const int i = (w * pt + j) * 64 + lane;
+        key[j] = (j < pt && i < ncand) ? s_key[i] : 0u;
     }
+    int32_t* to = tok_idx + (size_t)unit * kt;
+    const int keff_t = Sel::select(key, pt, kt, s_sel, [&](int p, int i) {
+        const int slot = i / bs;
+        to[p] = s_blk[slot] * bs + (i - slot * bs);
+    });
+    for (int p = keff_t + threadIdx.x; p < kt; p += SEL_THREADS) to[p] = -1;
 }
 
 template <int PT>
 hipError_t launch_t(const Shape& s, int mode, const uint16_t* q, const float* blk_score,
                     const uint16_t* klabel, const int32_t* label_ch, const int32_t* ctx_len,
-                    int32_t* blk_idx, int32_t* tok_idx, float* tok_score, hipStream_t st) {
-    hipLaunchKernelGGL((select_kernel<PT>), dim3(s.B * s.Hkv), dim3(SEL_THREADS), 0, st, mode, q,
-                       blk_score, klabel, label_ch, ctx_len, blk_idx, tok_idx, tok_score, s.Hkv, s.G,
-                       s.dk, s.bs, s.r, s.kb, s.kt, s.max_ctx, s.nb_cap);
+                    int32_t* blk_idx, int32_t* tok_idx, float* tok_score, int32_t* arrivals, hipStream_t st) {
+    hipLaunchKernelGGL((select_kernel<PT>), dim3(s.B * s.Hkv), dim3(SEL_THREADS), 0, st, mode, q, blk_score,
+                       klabel, label_ch, ctx_len, blk_idx, tok_idx, tok_score, arrivals, s.Hkv, s.G, s.dk,
+                       s.bs, s.r, s.kb, s.kt, s.max_ctx, s.nb_cap);
     return hipGetLastError();
 }
 
@@ -149,18 +170,18 @@ hipError_t launch_t(const Shape& s, int mode, const uint16_t* q, const float* bl
 
 hipError_t launch_select(const Shape& s, int mode, const uint16_t* q, const float* blk_score,
                          const uint16_t* klabel, const int32_t* label_ch, const int32_t* ctx_len,
-                         int32_t* blk_idx, int32_t* tok_idx, float* tok_score, hipStream_t st) {
+                         int32_t* blk_idx, int32_t* tok_idx, float* tok_score, int32_t* arrivals,
+                         hipStream_t st) {
     int need = 1;
     if (mode & 1) need = (s.nb_cap + SEL_THREADS - 1) / SEL_THREADS;
     if (mode & 2) {
         const int t = (s.kb * s.bs + SEL_THREADS - 1) / SEL_THREADS;
         need = t > need ? t : need;
     }
-    if (need <= 1) return launch_t<1>(s, mode, q, blk_score, klabel, label_ch, ctx_len, blk_idx, tok_idx, tok_score, st);
-    if (need <= 2) return launch_t<2>(s, mode, q, blk_score, klabel, label_ch, ctx_len, blk_idx, tok_idx, tok_score, st);
-    if (need <= 4) return launch_t<4>(s, mode, q, blk_score, klabel, label_ch, ctx_len, blk_idx, tok_idx, tok_score, st);
-    if (need <= 8) return launch_t<8>(s, mode, q, blk_score, klabel, label_ch, ctx_len, blk_idx, tok_idx, tok_score, st);
-    return launch_t<16>(s, mode, q, blk_score, klabel, label_ch, ctx_len, blk_idx, tok_idx, tok_score, st);
+    if (need <= 1) return launch_t<1>(s, mode, q, blk_score, klabel, label_ch, ctx_len, blk_idx, tok_idx, tok_score, arrivals, st);
+    if (need <= 2) return launch_t<2>(s, mode, q, blk_score, klabel, label_ch, ctx_len, blk_idx, tok_idx, tok_score, arrivals, st);
+    if (need <= 4) return launch_t<4>(s, mode, q, blk_score, klabel, label_ch, ctx_len, blk_idx, tok_idx, tok_score, arrivals, st);
+    return launch_t<8>(s, mode, q, blk_score, klabel, label_ch, ctx_len, blk_idx, tok_idx, tok_score, arrivals, st);
 }
 
 }  // namespace hsab

@@ -41,6 +41,8 @@
  *   lse      [B][Hq]                              fp32 natural-log
  *            logsumexp of the logits sm_scale*q.k over the kept tokens.
  *
+ * Inputs must be finite (no inf/NaN in q, K, V or the new token).
+ *
  * Selection rules (the pages leave them open; fixed here):
  *   - query heads sharing a KV head are combined by the maximum over the
  *     group, for block scores and token scores; one selection per unit;
@@ -72,10 +74,11 @@ extern "C" {
 
 /* Shape and budget of one decode layer.
  * Limits: 1 <= G <= 32; d_k % 16 == 0, 16 <= d_k <= 1024; d_v % 8 == 0;
- * r % 16 == 0, 16 <= r <= min(d_k, 128); 1 <= K_b <= 2048;
- * K_b * block <= 8192; nb_cap <= 16384; K_t >= 1.
- * Attention kernels exist for d_k == d_v in {64, 128, 256} with G <= 8
- * (GQA/MQA/MHA) and for v_alias_k with d_v <= d_k (absorbed MLA). */
+ * r in {16, 32, 64, 128}, r <= d_k; 1 <= K_b <= 2048;
+ * K_b * block <= 8192; nb_cap <= 8192; K_t >= 1.
+ * Attention kernels exist for d_k == d_v in {64, 128, 256} with G in
+ * {1, 2, 4, 8} (GQA/MQA/MHA); other shapes return HSAB_EUNSUPPORTED from
+ * hsab_sparse_attend and hsab_decode_step. */
 typedef struct hsab_dims {
     int32_t batch;        /* B */
     int32_t n_q_heads;    /* Hq */

@@ -237,7 +237,9 @@ def test_select_blocks_tokens_attend_match_decode_step():
     torch.cuda.synchronize()
     assert np.array_equal(blk.cpu().numpy().reshape(r["blk"].shape), r["blk"])
     assert np.array_equal(tok.cpu().numpy().reshape(r["tok"].shape), r["tok"])
-    assert np.array_equal(out.cpu().numpy().reshape(r["out"].shape), r["out"])
+    # the standalone split-K attention and the fused per-unit attention sum
+    # in different orders: fp32 rounding apart, not bit-identical
+    assert np.max(np.abs(out.cpu().numpy().reshape(r["out"].shape) - r["out"])) <= 1e-5
     # token scores: every candidate of every unit within the fp32 bound of the oracle
     K, V = T.appended_cache(w, h)
     ts = ts.cpu().numpy().reshape(w.batch, w.n_kv_heads, w.k_blocks * w.block)

@@ -1,0 +1,113 @@
+"""GPU top-k selection (K_b <= 2048) on crafted score distributions, compared exactly with
+the oracle's stable top-k.
+
+The scores are made exact on both sides: one KV head, block size 1, a
+one-hot query (1.0 on channel 0) and metadata rows whose channel 0 holds the
+wanted bf16 score in both the max and the min row, so every block bound is
+exactly that value in fp32 and in fp64. Distributions cover exact ties,
+signed zeros, a value range that overflows fp32, huge outliers, a pivot bin too full for the
+histogram path (forcing the bit-serial fallback) and the largest block count.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from hierarchical_sparse_attention_block_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+DK = 16
+
+
+def _select(scores_f32, k, G=1):
+    from hierarchical_sparse_attention_block_amd import hsab as H
+    bits = W.f32_to_bf16_bits(np.asarray(scores_f32, np.float32))
+    n = len(bits)
+    d = H.dims(1, G, 1, DK, DK, 0, 1, 16, k, 1, n, 1.0)
+    meta = np.zeros((n, 2, DK), np.uint16)
+    meta[:, 0, 0] = bits
+    meta[:, 1, 0] = bits
+    q = np.zeros((1, G, DK), np.uint16)
+    q[:, :, 0] = W.f32_to_bf16_bits(np.ones(1, np.float32))[0]
+    dev16 = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
+    blk = torch.full((k,), -7, dtype=torch.int32, device="cuda")
+    sc = torch.empty(n, device="cuda")
+    ctx = torch.tensor([n], dtype=torch.int32, device="cuda")
+    print(f"[select_blocks] n={n} k={k} G={G}", flush=True)
+    H.select_blocks(d, dev16(q), dev16(meta), ctx, blk, blk_score=sc)
+    torch.cuda.synchronize()
+    vals = O.bf16_to_f64(bits)
+    got_scores = sc.cpu().numpy().astype(np.float64)
+    assert np.array_equal(got_scores, vals)
+    return blk.cpu().numpy(), vals
+
+
+def _check(scores, k, G=1):
+    got, vals = _select(scores, k, G)
+    want = O.topk_stable(vals, k)
+    k_eff = len(want)
+    assert np.array_equal(got[:k_eff], want), f"first diffs {np.setxor1d(got[:k_eff], want)[:10]}"
+    assert np.all(got[k_eff:] == -1)
+
+
+rng = np.random.default_rng(123)
+
+
+@pytest.mark.parametrize("n,k", [(3000, 1), (3000, 100), (3000, 2048), (1500, 1500), (1500, 2048)])
+def test_all_equal(n, k):
+    _check(np.full(n, 0.5), k)
+
+
+def test_two_values_alternating():
+    s = np.where(np.arange(3001) % 2 == 0, 1.0, 2.0)
+    for k in (1, 700, 1500, 1501, 2000):
+        _check(s, k)
+
+
+def test_few_distinct_values_cut_inside_a_tie():
+    s = rng.integers(0, 4, size=3072).astype(np.float64)
+    for k in (128, 777, 1536):
+        _check(s, k)
+
+
+def test_signed_zeros_tie():
+    s = np.concatenate([np.full(500, -0.0), np.full(500, 0.0), rng.standard_normal(200)])
+    rng.shuffle(s)
+    for k in (10, 150, 600):
+        _check(s, k)
+
+
+def test_range_overflow_uses_the_fallback():
+    """Finite scores whose spread overflows fp32 (max - min = inf): the
+    histogram cannot be formed and the bit-serial search decides."""
+    s = rng.standard_normal(2048)
+    s[[3, 900, 1500]] = -3.0e38
+    s[[10, 11]] = 3.0e38
+    for k in (1, 2, 5, 2045, 2046):
+        _check(s, k)
+
+
+def test_huge_outliers():
+    s = rng.standard_normal(4096)
+    s[rng.choice(4096, 20, replace=False)] = 1e30
+    s[rng.choice(4096, 5, replace=False)] = -1e30
+    for k in (10, 20, 25, 128, 2048):
+        _check(s, k)
+
+
+def test_overfull_pivot_bin_falls_back_to_bitserial():
+    s = np.full(3000, 1.0)
+    s[17] = 2.0
+    s[2000] = 0.0
+    for k in (1, 2, 50, 2048):
+        _check(s, k)
+
+
+def test_random_normal_many_sizes():
+    for n, k in [(1, 1), (2, 1), (63, 17), (64, 64), (65, 3), (1023, 512), (1025, 1000), (6144, 256), (8192, 2048)]:
+        _check(rng.standard_normal(n), k)
+
+
+def test_group_max_of_identical_heads():
+    _check(rng.standard_normal(3072), 128, G=4)
