@@ -136,8 +136,10 @@ __global__ __launch_bounds__(256) void block_score_kernel(
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 if (mt * 16 + (lane >> 4) * 4 + i < G) v = fmaxf(v, acc[mt][i]);
-        v = fmaxf(v, __shfl_xor(v, 16));
-        v = fmaxf(v, __shfl_xor(v, 32));
+        if (G > 4) {   // heads 4.. sit in the other 16-lane rows
+            v = fmaxf(v, __shfl_xor(v, 16));
+            v = fmaxf(v, __shfl_xor(v, 32));
+        }
         if (lane < 16 && jl < nb) Su[jl] = v;
     }
 }

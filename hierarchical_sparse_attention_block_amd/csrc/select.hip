@@ -9,9 +9,10 @@
 // 16 candidate tokens per tile (lane l: token l % 16, 4 channels of step s
 // at 16*s + 4*(l/16)); the group's label-channel queries are A. Each wave
 // issues eight label-row loads before its MFMAs. Selection keeps all
-// scores in registers and LDS (TopK in common.h).
+// scores in registers and LDS (TopK in topk.h).
 #include "common.h"
 #include "kernels.h"
+#include "topk.h"
 
 namespace hsab {
 
@@ -26,8 +27,10 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
     const uint16_t* __restrict__ klabel, const int32_t* __restrict__ label_ch,
     const int32_t* __restrict__ ctx_len, int32_t* __restrict__ blk_idx, int32_t* __restrict__ tok_idx,
     float* __restrict__ tok_score, int32_t* __restrict__ arrivals, int Hkv, int G, int dk, int bs, int r,
-    int kb, int kt, int max_ctx, int nb_cap) {
+    int kb, int kt, int max_ctx, int nb_cap, int bs_shift) {
     using Sel = TopK<SEL_WAVES, PT>;
+    // candidate i sits in slot i / bs of the block list (a shift when bs is a power of two)
+    auto slot_of = [&](int i) { return bs_shift >= 0 ? (i >> bs_shift) : i / bs; };
     __shared__ uint32_t s_key[MAX_CAND];
     __shared__ int32_t s_blk[MAX_KB];
     __shared__ uint2 s_qa[2 * (MAX_R / 16) * 64];
@@ -35,6 +38,19 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
 
     const int unit = blockIdx.x, b = unit / Hkv, g = unit % Hkv;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    // block scores are loaded over the whole capacity in the same round trip
+    // as ctx_len and masked once n is known; the entry layout of the block
+    // selection uses the capacity's slot count
+    const int pt_b = (nb_cap + SEL_THREADS - 1) / SEL_THREADS;
+    float sraw[PT];
+    if (mode & 1) {
+        const float* S = blk_score + (size_t)unit * nb_cap;
+#pragma unroll
+        for (int j = 0; j < PT; ++j) {
+            const int i = (w * pt_b + j) * 64 + lane;
+            sraw[j] = (j < pt_b && i < nb_cap) ? S[i] : 0.f;
+        }
+    }
     if (arrivals && threadIdx.x == 0) arrivals[unit] = 0;   // for the attention split merge
     int n = ctx_len[b];
     n = n < 1 ? 1 : (n > max_ctx ? max_ctx : n);
@@ -62,16 +78,14 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
 
     // ------------------------------------------------------------ blocks
     if (mode & 1) {
-        const int pt = (nb + SEL_THREADS - 1) / SEL_THREADS;
-        const float* S = blk_score + (size_t)unit * nb_cap;
-        uint32_t key[PT];
+        uint32_t bkey[PT];
 #pragma unroll
         for (int j = 0; j < PT; ++j) {
-            const int i = (w * pt + j) * 64 + lane;
-            key[j] = (j < pt && i < nb) ? f32_key(S[i]) : 0u;
+            const int i = (w * pt_b + j) * 64 + lane;
+            bkey[j] = (j < pt_b && i < nb) ? f32_key(sraw[j]) : 0u;
         }
         int32_t* bo = blk_idx + (size_t)unit * kb;
-        const int keff = Sel::select(key, pt, kb, s_sel, [&](int pos, int i) {
+        const int keff = Sel::select(bkey, pt_b, kb, s_sel, [&](int pos, int i) {
             s_blk[pos] = i;
             bo[pos] = i;
         });
@@ -83,7 +97,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
         for (int p = threadIdx.x; p < kb; p += SEL_THREADS) s_blk[p] = blk_idx[(size_t)unit * kb + p];
     }
     if (!(mode & 2)) return;
-    __syncthreads();   // s_blk and s_qa complete
+    __syncthreads();   // s_blk, s_qa and the selector's scratch settled
 
     // -------------------------------------------------- token label scores
     const int ncand = kb * bs;
@@ -96,14 +110,16 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
     const int tb = 8 >> lg;                         // tiles per batch
     for (int t0 = w; t0 < n_tiles; t0 += SEL_WAVES * tb) {
         uint2 bf[8];
+        uint32_t vmask = 0;   // bit u: the token this lane loads for load u is valid
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             const int tile = t0 + (u >> lg) * SEL_WAVES, st = u & (KSr - 1);
             const int i = tile * 16 + (lane & 15);
-            const int slot = i / bs, off = i - slot * bs;
+            const int slot = slot_of(i), off = i - slot * bs;
             const int blk = (tile < n_tiles && i < ncand) ? s_blk[slot] : -1;
             const int pos = blk * bs + off;
             const bool valid = blk >= 0 && blk < nb && pos < n;
+            vmask |= (valid ? 1u : 0u) << u;
             bf[u] = ldg8(Lu + (size_t)(valid ? pos : 0) * r + (lane >> 4) * 4 + st * 16);
         }
         f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
@@ -124,14 +140,13 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
                     if (h < G) v = fmaxf(v, acc0[e]);
                     if (16 + h < G) v = fmaxf(v, acc1[e]);
                 }
-                v = fmaxf(v, __shfl_xor(v, 16));
-                v = fmaxf(v, __shfl_xor(v, 32));
+                if (G > 4) {   // heads 4.. sit in the other 16-lane rows
+                    v = fmaxf(v, __shfl_xor(v, 16));
+                    v = fmaxf(v, __shfl_xor(v, 32));
+                }
                 const int i = tile * 16 + (lane & 15);
                 if (lane < 16 && i < ncand) {
-                    const int slot = i / bs, off = i - slot * bs;
-                    const int blk = s_blk[slot];
-                    const int pos = blk * bs + off;
-                    const bool valid = blk >= 0 && blk < nb && pos < n;
+                    const bool valid = (vmask >> u) & 1u;
                     s_key[i] = valid ? f32_key(v) : 0u;
                     if (TS) TS[i] = valid ? v : -INFINITY;
                 }
@@ -150,7 +165,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
     }
     int32_t* to = tok_idx + (size_t)unit * kt;
     const int keff_t = Sel::select(key, pt, kt, s_sel, [&](int p, int i) {
-        const int slot = i / bs;
+        const int slot = slot_of(i);
         to[p] = s_blk[slot] * bs + (i - slot * bs);
     });
     for (int p = keff_t + threadIdx.x; p < kt; p += SEL_THREADS) to[p] = -1;
@@ -162,7 +177,7 @@ hipError_t launch_t(const Shape& s, int mode, const uint16_t* q, const float* bl
                     int32_t* blk_idx, int32_t* tok_idx, float* tok_score, int32_t* arrivals, hipStream_t st) {
     hipLaunchKernelGGL((select_kernel<PT>), dim3(s.B * s.Hkv), dim3(SEL_THREADS), 0, st, mode, q, blk_score,
                        klabel, label_ch, ctx_len, blk_idx, tok_idx, tok_score, arrivals, s.Hkv, s.G, s.dk,
-                       s.bs, s.r, s.kb, s.kt, s.max_ctx, s.nb_cap);
+                       s.bs, s.r, s.kb, s.kt, s.max_ctx, s.nb_cap, (s.bs & (s.bs - 1)) ? -1 : __builtin_ctz(s.bs));
     return hipGetLastError();
 }
 
