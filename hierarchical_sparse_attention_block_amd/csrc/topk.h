@@ -94,158 +94,157 @@ struct TopK {
         }
         const int k_eff = k < (int)nval ? k : (int)nval;
         if (k_eff <= 0) return 0;
-        if (k_eff == (int)nval) {   // every nonempty key is kept
-            compact(key, pt, [&](int j) { return key[j] != 0u; }, red, emit);
-            return k_eff;
-        }
-        const float vmin = key_f32(kmin), vmax = key_f32(kmax);
-        const float range = vmax - vmin;
-        const float scale = (float)NBIN / range;
-        const bool binned = isfinite(range) && range > 0.f && isfinite(scale);
-        auto bin = [&](uint32_t kk) {
-            const int b = (int)((key_f32(kk) - vmin) * scale);
-            return b < 0 ? 0 : (b >= NBIN ? NBIN - 1 : b);
-        };
-        if (binned) {
-            // 2) histogram
+
+        bool keep[PT];
 #pragma unroll
-            for (int j = 0; j < PT; ++j)
-                if (j < pt && key[j] != 0u) atomicAdd(&sm.hist[bin(key[j])], 1u);
-            __syncthreads();
-            // 3) wave v owns the bins NBIN-1-(v*BPW + i), i < BPW (top down);
-            //    per-wave totals locate the wave whose range holds the k-th
-            //    key, then every wave rescans that range itself
-            uint32_t loc = 0;
+        for (int j = 0; j < PT; ++j) keep[j] = key[j] != 0u;   // right when every key is kept
+        if (k_eff < (int)nval) {
+            const float vmin = key_f32(kmin), vmax = key_f32(kmax);
+            const float range = vmax - vmin;
+            const float scale = (float)NBIN / range;
+            auto bin = [&](uint32_t kk) {
+                const int b = (int)((key_f32(kk) - vmin) * scale);
+                return b < 0 ? 0 : (b >= NBIN ? NBIN - 1 : b);
+            };
+            bool done = false;
+            if (isfinite(range) && range > 0.f && isfinite(scale)) {
+                // 2) histogram
 #pragma unroll
-            for (int e = 0; e < BPT; ++e) loc += sm.hist[NBIN - 1 - (w * BPW + lane * BPT + e)];
-            uint32_t tot = loc;
-#pragma unroll
-            for (int o = 32; o >= 1; o >>= 1) tot += __shfl_xor(tot, o);
-            if (lane == 0) red[11 * NW + w] = tot;
-            __syncthreads();
-            uint32_t above = 0;
-            int wp = 0;
-            for (; wp < NW; ++wp) {
-                const uint32_t t = red[11 * NW + wp];
-                if (above + t >= (uint32_t)k_eff) break;
-                above += t;
-            }
-            uint32_t hv[BPT], ploc = 0;
-#pragma unroll
-            for (int e = 0; e < BPT; ++e) { hv[e] = sm.hist[NBIN - 1 - (wp * BPW + lane * BPT + e)]; ploc += hv[e]; }
-            uint32_t run = above + wave_incl_scan(ploc) - ploc;
-            int bstar = -1;
-            uint32_t need = 0;
-#pragma unroll
-            for (int e = 0; e < BPT; ++e) {
-                if (run < (uint32_t)k_eff && run + hv[e] >= (uint32_t)k_eff) {
-                    bstar = NBIN - 1 - (wp * BPW + lane * BPT + e);
-                    need = (uint32_t)k_eff - run;
-                }
-                run += hv[e];
-            }
-            // exactly one lane found it; make it wave-uniform
-            const uint64_t who = __ballot(bstar >= 0);
-            const int src = __ffsll((unsigned long long)who) - 1;
-            bstar = __builtin_amdgcn_readlane(bstar, src);
-            need = __builtin_amdgcn_readlane((int)need, src);
-            const uint32_t m = sm.hist[bstar];
-            if (m <= (uint32_t)CMAX) {
-                // 4) gather the pivot bin, rank its entries by (key desc, entry asc)
-#pragma unroll
-                for (int j = 0; j < PT; ++j) {
-                    if (j < pt && key[j] != 0u && bin(key[j]) == bstar) {
-                        const uint32_t slot = atomicAdd(ccount, 1u);
-                        sm.ckey[slot] = key[j];
-                        sm.cidx[slot] = (w * pt + j) * 64 + lane;
-                    }
-                }
+                for (int j = 0; j < PT; ++j)
+                    if (j < pt && key[j] != 0u) atomicAdd(&sm.hist[bin(key[j])], 1u);
                 __syncthreads();
-                bool keep[PT];
+                // 3) wave v owns the bins NBIN-1-(v*BPW + i), i < BPW (top down);
+                //    per-wave totals locate the wave whose range holds the k-th
+                //    key, then every wave rescans that range itself
+                uint32_t loc = 0;
 #pragma unroll
-                for (int j = 0; j < PT; ++j) {
-                    keep[j] = false;
-                    if (j < pt && key[j] != 0u) {
-                        const int bj = bin(key[j]);
-                        if (bj > bstar) {
-                            keep[j] = true;
-                        } else if (bj == bstar) {
-                            const int me = (w * pt + j) * 64 + lane;
-                            uint32_t rank = 0;
-                            for (uint32_t c = 0; c < m; ++c) {
-                                const uint32_t ck = sm.ckey[c];
-                                rank += (ck > key[j]) || (ck == key[j] && sm.cidx[c] < me);
-                            }
-                            keep[j] = rank < need;
+                for (int e = 0; e < BPT; ++e) loc += sm.hist[NBIN - 1 - (w * BPW + lane * BPT + e)];
+                uint32_t tot = loc;
+#pragma unroll
+                for (int o = 32; o >= 1; o >>= 1) tot += __shfl_xor(tot, o);
+                if (lane == 0) red[11 * NW + w] = tot;
+                __syncthreads();
+                uint32_t above = 0;
+                int wp = 0;
+                for (; wp < NW; ++wp) {
+                    const uint32_t t = red[11 * NW + wp];
+                    if (above + t >= (uint32_t)k_eff) break;
+                    above += t;
+                }
+                uint32_t hv[BPT], ploc = 0;
+#pragma unroll
+                for (int e = 0; e < BPT; ++e) { hv[e] = sm.hist[NBIN - 1 - (wp * BPW + lane * BPT + e)]; ploc += hv[e]; }
+                uint32_t run = above + wave_incl_scan(ploc) - ploc;
+                int bstar = -1;
+                uint32_t need = 0;
+#pragma unroll
+                for (int e = 0; e < BPT; ++e) {
+                    if (run < (uint32_t)k_eff && run + hv[e] >= (uint32_t)k_eff) {
+                        bstar = NBIN - 1 - (wp * BPW + lane * BPT + e);
+                        need = (uint32_t)k_eff - run;
+                    }
+                    run += hv[e];
+                }
+                // exactly one lane found it; make it wave-uniform
+                const int src = __ffsll((unsigned long long)__ballot(bstar >= 0)) - 1;
+                bstar = __builtin_amdgcn_readlane(bstar, src);
+                need = __builtin_amdgcn_readlane((int)need, src);
+                const uint32_t m = sm.hist[bstar];
+                if (m <= (uint32_t)CMAX) {
+                    // 4) gather the pivot bin, rank its entries by (key desc, entry asc)
+#pragma unroll
+                    for (int j = 0; j < PT; ++j) {
+                        if (j < pt && key[j] != 0u && bin(key[j]) == bstar) {
+                            const uint32_t slot = atomicAdd(ccount, 1u);
+                            sm.ckey[slot] = key[j];
+                            sm.cidx[slot] = (w * pt + j) * 64 + lane;
                         }
                     }
+                    __syncthreads();
+#pragma unroll
+                    for (int j = 0; j < PT; ++j) {
+                        if (j < pt && key[j] != 0u) {
+                            const int bj = bin(key[j]);
+                            if (bj == bstar) {
+                                const int me = (w * pt + j) * 64 + lane;
+                                uint32_t rank = 0;
+                                for (uint32_t c = 0; c < m; ++c) {
+                                    const uint32_t ck = sm.ckey[c];
+                                    rank += (ck > key[j]) || (ck == key[j] && sm.cidx[c] < me);
+                                }
+                                keep[j] = rank < need;
+                            } else {
+                                keep[j] = bj > bstar;
+                            }
+                        }
+                    }
+                    done = true;
                 }
-                compact(key, pt, [&](int j) { return keep[j]; }, red, emit);
-                return k_eff;
             }
-        }
-        // fallback: bit-serial search for the k-th largest key T
-        uint32_t prefix = 0;
-        int round = 1;
-        for (int bit = 30; bit >= 0; bit -= 2, ++round) {
-            const uint32_t c1 = prefix | (1u << bit), c2 = prefix | (2u << bit), c3 = prefix | (3u << bit);
-            uint32_t n1 = 0, n2 = 0, n3 = 0;
+            if (!done) {
+                // fallback: bit-serial search for the k-th largest key T
+                uint32_t prefix = 0;
+                int round = 1;
+                for (int bit = 30; bit >= 0; bit -= 2, ++round) {
+                    const uint32_t c1 = prefix | (1u << bit), c2 = prefix | (2u << bit), c3 = prefix | (3u << bit);
+                    uint32_t n1 = 0, n2 = 0, n3 = 0;
 #pragma unroll
-            for (int j = 0; j < PT; ++j) {
-                if (j < pt) {
-                    n1 += __popcll(__ballot(key[j] >= c1));
-                    n2 += __popcll(__ballot(key[j] >= c2));
-                    n3 += __popcll(__ballot(key[j] >= c3));
+                    for (int j = 0; j < PT; ++j) {
+                        if (j < pt) {
+                            n1 += __popcll(__ballot(key[j] >= c1));
+                            n2 += __popcll(__ballot(key[j] >= c2));
+                            n3 += __popcll(__ballot(key[j] >= c3));
+                        }
+                    }
+                    uint32_t* slot = red + (round & 1) * 4 * NW;
+                    if (lane == 0) { slot[w] = n1; slot[NW + w] = n2; slot[2 * NW + w] = n3; }
+                    __syncthreads();
+                    uint32_t t1 = 0, t2 = 0, t3 = 0;
+#pragma unroll
+                    for (int i = 0; i < NW; ++i) { t1 += slot[i]; t2 += slot[NW + i]; t3 += slot[2 * NW + i]; }
+                    if (t3 >= (uint32_t)k_eff) prefix = c3;
+                    else if (t2 >= (uint32_t)k_eff) prefix = c2;
+                    else if (t1 >= (uint32_t)k_eff) prefix = c1;
+                }
+                const uint32_t T = prefix;
+                // keys > T are kept; among keys == T the first (k_eff - #{> T}) in entry order
+                uint32_t gt = 0, eq = 0;
+#pragma unroll
+                for (int j = 0; j < PT; ++j)
+                    if (j < pt) { gt += __popcll(__ballot(key[j] > T)); eq += __popcll(__ballot(key[j] == T)); }
+                uint32_t* cnt2 = red + 8 * NW;
+                if (lane == 0) { cnt2[w] = gt; cnt2[NW + w] = eq; }
+                __syncthreads();
+                uint32_t gt_tot = 0, eq_before = 0;
+#pragma unroll
+                for (int i = 0; i < NW; ++i) { gt_tot += cnt2[i]; if (i < w) eq_before += cnt2[NW + i]; }
+                const uint32_t need_eq = (uint32_t)k_eff - gt_tot;
+                const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+                uint32_t eq_run = eq_before;
+#pragma unroll
+                for (int j = 0; j < PT; ++j) {
+                    if (j < pt) {
+                        const uint64_t meq = __ballot(key[j] == T);
+                        keep[j] = key[j] > T || (key[j] == T && eq_run + __popcll(meq & lt) < need_eq);
+                        eq_run += __popcll(meq);
+                    }
                 }
             }
-            uint32_t* slot = red + (round & 1) * 4 * NW;
-            if (lane == 0) { slot[w] = n1; slot[NW + w] = n2; slot[2 * NW + w] = n3; }
-            __syncthreads();
-            uint32_t t1 = 0, t2 = 0, t3 = 0;
-#pragma unroll
-            for (int i = 0; i < NW; ++i) { t1 += slot[i]; t2 += slot[NW + i]; t3 += slot[2 * NW + i]; }
-            if (t3 >= (uint32_t)k_eff) prefix = c3;
-            else if (t2 >= (uint32_t)k_eff) prefix = c2;
-            else if (t1 >= (uint32_t)k_eff) prefix = c1;
         }
-        const uint32_t T = prefix;
-        // keys > T are kept; among keys == T the first (k_eff - #{> T}) in entry order
-        uint32_t gt = 0, eq = 0;
-#pragma unroll
-        for (int j = 0; j < PT; ++j)
-            if (j < pt) { gt += __popcll(__ballot(key[j] > T)); eq += __popcll(__ballot(key[j] == T)); }
-        uint32_t* cnt2 = red + 8 * NW;
-        if (lane == 0) { cnt2[w] = gt; cnt2[NW + w] = eq; }
-        __syncthreads();
-        uint32_t gt_tot = 0, eq_before = 0;
-#pragma unroll
-        for (int i = 0; i < NW; ++i) { gt_tot += cnt2[i]; if (i < w) eq_before += cnt2[NW + i]; }
-        const uint32_t need_eq = (uint32_t)k_eff - gt_tot;
-        const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-        bool keep[PT];
-        uint32_t eq_run = eq_before;
-#pragma unroll
-        for (int j = 0; j < PT; ++j) {
-            keep[j] = false;
-            if (j < pt) {
-                const uint64_t meq = __ballot(key[j] == T);
-                keep[j] = key[j] > T || (key[j] == T && eq_run + __popcll(meq & lt) < need_eq);
-                eq_run += __popcll(meq);
-            }
-        }
-        compact(key, pt, [&](int j) { return keep[j]; }, red, emit);
+        compact(key, pt, keep, red, emit);
         return k_eff;
     }
 
-    // Emit the entries whose predicate holds, ranked in entry order.
-    template <typename Pred, typename Emit>
-    __device__ static void compact(const uint32_t (&key)[PT], int pt, Pred pred, uint32_t* red, Emit emit) {
+    // Emit the entries with keep[j] set, ranked in entry order.
+    template <typename Emit>
+    __device__ static void compact(const uint32_t (&key)[PT], int pt, const bool (&keep)[PT], uint32_t* red,
+                                   Emit emit) {
         const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
         const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
         uint32_t cntw = 0;
 #pragma unroll
         for (int j = 0; j < PT; ++j)
-            if (j < pt) cntw += __popcll(__ballot(pred(j)));
+            if (j < pt) cntw += __popcll(__ballot(keep[j]));
         uint32_t* c = red + 10 * NW;
         if (lane == 0) c[w] = cntw;
         __syncthreads();
@@ -254,9 +253,8 @@ struct TopK {
 #pragma unroll
         for (int j = 0; j < PT; ++j) {
             if (j < pt) {
-                const bool p = pred(j);
-                const uint64_t mk = __ballot(p);
-                if (p) emit((int)(run + __popcll(mk & lt)), (w * pt + j) * 64 + lane);
+                const uint64_t mk = __ballot(keep[j]);
+                if (keep[j]) emit((int)(run + __popcll(mk & lt)), (w * pt + j) * 64 + lane);
                 run += __popcll(mk);
             }
         }
