@@ -8,15 +8,20 @@
 // gathers 64/(D/8) whole key rows. Logits are fp32 (bf16 products are
 // exact in fp32), kept in base-2 units (q pre-scaled by sm_scale*log2 e).
 // Each wave keeps (max, sum, weighted values) per head; the workgroup
-// merges its four waves and writes one partial per head. The partials of
-// all splits are merged either by a separate combine kernel or by the last
-// split of the unit to finish (arrival counter per unit, zeroed by the
-// selection kernel that runs before): fence, count, and the last arrival
-// reads every split's partial.
+// merges its four waves and writes one partial per head; the combine
+// kernel merges the partials of all splits.
+//
+// MLA path (values are the first d_v dims of the d_k-dim latent key rows,
+// 32 query heads on one KV head): a workgroup takes 32 kept tokens; the
+// 32x32 logit tile (tokens x heads) is four 16x16 tiles of
+// v_mfma_f32_16x16x32_bf16, one per wave, with key rows and queries read
+// straight from memory as A and B fragments; softmax runs in LDS; P.V runs
+// in fp32 on the VALU from the value rows staged in LDS (each thread: one
+// head, d_v/8 interleaved channels).
 //
 // Workgroup numbering: the dispatcher hands consecutive workgroups to the
 // eight XCDs in turn, so workgroup L runs on XCD L % 8. All splits of a unit
-// are given the same L % 8, which keeps that unit's partials in one L2.
+// are given the same L % 8, which keeps a unit's rows and partials in one L2.
 #include "common.h"
 #include "kernels.h"
 
@@ -44,13 +49,12 @@ __device__ __forceinline__ long row_of(int t, int unit, int bs, int max_ctx, int
     return ((long)unit * n_slots + slot) * bs + (t - blk * bs);
 }
 
-template <int D, int G, bool MERGE>
+template <int D, int G>
 __global__ __launch_bounds__(256) void attend_gqa_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const int32_t* __restrict__ tok_idx, const int32_t* __restrict__ slot_of, int n_slots,
     float* __restrict__ part_ml, float* __restrict__ part_acc, int Hkv, int bs, int kt,
-    int max_ctx, int nb_cap, int n_splits, int units, float scale2, int32_t* __restrict__ arrivals,
-    float* __restrict__ out, float* __restrict__ lse) {
+    int max_ctx, int nb_cap, int n_splits, int units, float scale2) {
     constexpr int LPT = D / 8;                         // lanes per token
     constexpr int TPI = 64 / LPT;                      // tokens per wave load
     constexpr int TPW = ATT_TOK_PER_SPLIT / 4;         // tokens per wave
@@ -175,34 +179,116 @@ __global__ __launch_bounds__(256) void attend_gqa_kernel(
             part_ml[(bh * n_splits + split) * 2 + 1] = L;
         }
     }
-    if constexpr (MERGE) {
-        __shared__ int s_last;
-        __threadfence();
-        __syncthreads();
-        if (threadIdx.x == 0) s_last = atomicAdd(&arrivals[unit], 1) == n_splits - 1;
-        __syncthreads();
-        if (!s_last) return;
-        __threadfence();
-        for (int p = threadIdx.x; p < G * D; p += blockDim.x) {
-            const int h = p / D, c = p - h * D;
-            const size_t bh = (size_t)(b * Hkv + g) * G + h;
-            const float* ml = part_ml + bh * n_splits * 2;
-            float M = -INFINITY;
-            for (int sp = 0; sp < n_splits; ++sp) M = fmaxf(M, ml[2 * sp]);
-            float L = 0.f, A = 0.f;
-            if (M != -INFINITY) {
-                for (int sp = 0; sp < n_splits; ++sp) {
-                    const float ms = ml[2 * sp];
-                    if (ms == -INFINITY) continue;
-                    const float wt = exp2f(ms - M);
-                    L = fmaf(ml[2 * sp + 1], wt, L);
-                    A = fmaf(part_acc[(bh * n_splits + sp) * D + c], wt, A);
-                }
-            }
-            out[bh * D + c] = L > 0.f ? A / L : 0.f;
-            if (c == 0) lse[bh] = L > 0.f ? (M + log2f(L)) * LN2 : -INFINITY;
+}
+
+// grid: as the GQA kernel; block 256. Hq = 32 * Hkv, d_k % 32 == 0,
+// d_v % 64 == 0, d_v <= 512, values alias the first d_v key dims.
+__global__ __launch_bounds__(256) void attend_mla_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ K, const int32_t* __restrict__ tok_idx,
+    const int32_t* __restrict__ slot_of, int n_slots, float* __restrict__ part_ml,
+    float* __restrict__ part_acc, int Hkv, int dk, int dv, int bs, int kt, int max_ctx, int nb_cap,
+    int n_splits, int units, float scale2) {
+    constexpr int T = MLA_TOK_PER_SPLIT;   // 32 tokens
+    constexpr int H = 32;                  // query heads per KV head
+    __shared__ uint16_t sV[T][512];
+    __shared__ float sS[T][H + 1];
+    __shared__ float sm[H], sl[H];
+    __shared__ long s_row[T];
+
+    const int xcd = blockIdx.x & 7, y = blockIdx.x >> 3;
+    const int unit = (y / n_splits) * 8 + xcd, split = y % n_splits;
+    if (unit >= units) return;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+    if (tid < T) {
+        const int ti = split * T + tid;
+        const int t = ti < kt ? tok_idx[(size_t)unit * kt + ti] : -1;
+        s_row[tid] = row_of(t, unit, bs, max_ctx, nb_cap, slot_of, n_slots);
+    }
+    __syncthreads();
+
+    // value rows (first dv dims of each kept key row) into LDS
+    const int cpr = dv / 8;
+    for (int c = tid; c < T * cpr; c += 256) {
+        const int tok = c / cpr, ch = c - tok * cpr;
+        const long row = s_row[tok];
+        const uint4 v = row >= 0 ? ldg16(K + row * dk + ch * 8) : make_uint4(0u, 0u, 0u, 0u);
+        *reinterpret_cast<uint4*>(&sV[tok][ch * 8]) = v;
+    }
+
+    // logits: wave w computes tokens 16*(w & 1).. x heads 16*(w >> 1)..
+    {
+        const int mt = wave & 1, nt = wave >> 1;
+        const long ra = s_row[mt * 16 + (lane & 15)];
+        const uint16_t* arow = K + (ra >= 0 ? ra : 0) * dk + (lane >> 4) * 8;
+        const uint16_t* brow = q + ((size_t)unit * H + nt * 16 + (lane & 15)) * dk + (lane >> 4) * 8;
+        const int KS = dk / 32;
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        for (int s0 = 0; s0 < KS; s0 += 6) {
+            uint4 af[6], bf[6];
+#pragma unroll
+            for (int u = 0; u < 6; ++u)
+                if (s0 + u < KS) { af[u] = ldg16(arow + (s0 + u) * 32); bf[u] = ldg16(brow + (s0 + u) * 32); }
+#pragma unroll
+            for (int u = 0; u < 6; ++u)
+                if (s0 + u < KS)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(af[u]), as_bf16x8(bf[u]), acc, 0, 0, 0);
         }
-        if (threadIdx.x == 0) arrivals[unit] = 0;
+        const int h = nt * 16 + (lane & 15);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int tok = mt * 16 + (lane >> 4) * 4 + i;
+            sS[tok][h] = s_row[tok] >= 0 ? acc[i] * scale2 : -INFINITY;
+        }
+    }
+    __syncthreads();
+
+    if (tid < H) {
+        float m = -INFINITY;
+        for (int t = 0; t < T; ++t) m = fmaxf(m, sS[t][tid]);
+        float l = 0.f;
+        for (int t = 0; t < T; ++t) {
+            const float z = sS[t][tid];
+            const float p = (z == -INFINITY) ? 0.f : exp2f(z - m);
+            sS[t][tid] = p;
+            l += p;
+        }
+        sm[tid] = m;
+        sl[tid] = l;
+    }
+    __syncthreads();
+
+    // P.V: thread -> head tid/8, channels (tid%8)*8 + 64*j + e
+    const int h = tid >> 3, c8 = tid & 7;
+    const int nj = dv / 64;
+    float acc[8][8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[j][e] = 0.f;
+    for (int t = 0; t < T; ++t) {
+        const float p = sS[t][h];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if (j < nj) {
+                float vf[8];
+                widen8(*reinterpret_cast<const uint4*>(&sV[t][c8 * 8 + 64 * j]), vf);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[j][e] = fmaf(p, vf[e], acc[j][e]);
+            }
+        }
+    }
+    const size_t bh = (size_t)unit * H + h;
+    float* dst = part_acc + (bh * n_splits + split) * dv;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        if (j < nj) {
+            *reinterpret_cast<float4*>(dst + c8 * 8 + 64 * j) = make_float4(acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
+            *reinterpret_cast<float4*>(dst + c8 * 8 + 64 * j + 4) = make_float4(acc[j][4], acc[j][5], acc[j][6], acc[j][7]);
+        }
+    if (c8 == 0) {
+        part_ml[(bh * n_splits + split) * 2 + 0] = sm[h];
+        part_ml[(bh * n_splits + split) * 2 + 1] = sl[h];
     }
 }
 
@@ -236,42 +322,36 @@ __global__ __launch_bounds__(256) void combine_kernel(
 template <int D, int G>
 hipError_t launch_gqa(const Shape& s, const uint16_t* q, const uint16_t* K, const uint16_t* V,
                       const int32_t* tok_idx, const int32_t* slot_of, int n_slots, float* part_ml,
-                      float* part_acc, int32_t* arrivals, float* out, float* lse, hipStream_t st) {
+                      float* part_acc, hipStream_t st) {
     const int ns = attn_splits(s);
     const int units = s.B * s.Hkv;
-    const dim3 grid(((units + 7) / 8) * 8 * ns);
-    if (arrivals) {
-        hipLaunchKernelGGL((attend_gqa_kernel<D, G, true>), grid, dim3(256), 0, st, q, K, V, tok_idx, slot_of,
-                           n_slots, part_ml, part_acc, s.Hkv, s.bs, s.kt, s.max_ctx, s.nb_cap, ns, units,
-                           s.sm_scale * LOG2E, arrivals, out, lse);
-        return hipGetLastError();
-    }
-    hipLaunchKernelGGL((attend_gqa_kernel<D, G, false>), grid, dim3(256), 0, st, q, K, V, tok_idx, slot_of,
-                       n_slots, part_ml, part_acc, s.Hkv, s.bs, s.kt, s.max_ctx, s.nb_cap, ns, units,
-                       s.sm_scale * LOG2E, nullptr, nullptr, nullptr);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(combine_kernel, dim3(s.B * s.Hq), dim3(s.dv < 256 ? 128 : 256), 0, st, part_ml,
-                       part_acc, out, lse, s.dv, ns);
+    hipLaunchKernelGGL((attend_gqa_kernel<D, G>), dim3(((units + 7) / 8) * 8 * ns), dim3(256), 0, st, q, K, V,
+                       tok_idx, slot_of, n_slots, part_ml, part_acc, s.Hkv, s.bs, s.kt, s.max_ctx, s.nb_cap, ns,
+                       units, s.sm_scale * LOG2E);
     return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_gqa_d(const Shape& s, const uint16_t* q, const uint16_t* K, const uint16_t* V,
                         const int32_t* tok_idx, const int32_t* slot_of, int n_slots, float* part_ml,
-                        float* part_acc, int32_t* arrivals, float* out, float* lse, hipStream_t st) {
+                        float* part_acc, hipStream_t st) {
     switch (s.G) {
-        case 1: return launch_gqa<D, 1>(s, q, K, V, tok_idx, slot_of, n_slots, part_ml, part_acc, arrivals, out, lse, st);
-        case 2: return launch_gqa<D, 2>(s, q, K, V, tok_idx, slot_of, n_slots, part_ml, part_acc, arrivals, out, lse, st);
-        case 4: return launch_gqa<D, 4>(s, q, K, V, tok_idx, slot_of, n_slots, part_ml, part_acc, arrivals, out, lse, st);
-        case 8: return launch_gqa<D, 8>(s, q, K, V, tok_idx, slot_of, n_slots, part_ml, part_acc, arrivals, out, lse, st);
+        case 1: return launch_gqa<D, 1>(s, q, K, V, tok_idx, slot_of, n_slots, part_ml, part_acc, st);
+        case 2: return launch_gqa<D, 2>(s, q, K, V, tok_idx, slot_of, n_slots, part_ml, part_acc, st);
+        case 4: return launch_gqa<D, 4>(s, q, K, V, tok_idx, slot_of, n_slots, part_ml, part_acc, st);
+        case 8: return launch_gqa<D, 8>(s, q, K, V, tok_idx, slot_of, n_slots, part_ml, part_acc, st);
         default: return hipErrorInvalidValue;
     }
+}
+
+bool mla_shape(const Shape& s) {
+    return s.valias && s.G == 32 && s.dk % 32 == 0 && s.dv % 64 == 0 && s.dv <= 512 && s.dv <= s.dk;
 }
 
 }  // namespace
 
 bool attend_supported(const Shape& s) {
+    if (mla_shape(s)) return true;
     return !s.valias && s.dk == s.dv && (s.dk == 64 || s.dk == 128 || s.dk == 256) &&
            (s.G == 1 || s.G == 2 || s.G == 4 || s.G == 8);
 }
@@ -280,13 +360,28 @@ hipError_t launch_attend(const Shape& s, const uint16_t* q, const uint16_t* K, c
                          const int32_t* tok_idx, const int32_t* slot_of, int n_slots,
                          float* part_ml, float* part_acc, int32_t* arrivals, float* out, float* lse,
                          hipStream_t st) {
+    (void)arrivals;
     if (!attend_supported(s)) return hipErrorInvalidValue;
-    switch (s.dk) {
-        case 64: return launch_gqa_d<64>(s, q, K, V, tok_idx, slot_of, n_slots, part_ml, part_acc, arrivals, out, lse, st);
-        case 128: return launch_gqa_d<128>(s, q, K, V, tok_idx, slot_of, n_slots, part_ml, part_acc, arrivals, out, lse, st);
-        case 256: return launch_gqa_d<256>(s, q, K, V, tok_idx, slot_of, n_slots, part_ml, part_acc, arrivals, out, lse, st);
-        default: return hipErrorInvalidValue;
+    const int ns = attn_splits(s);
+    hipError_t e = hipSuccess;
+    if (mla_shape(s)) {
+        const int units = s.B * s.Hkv;
+        hipLaunchKernelGGL(attend_mla_kernel, dim3(((units + 7) / 8) * 8 * ns), dim3(256), 0, st, q, K, tok_idx,
+                           slot_of, n_slots, part_ml, part_acc, s.Hkv, s.dk, s.dv, s.bs, s.kt, s.max_ctx, s.nb_cap,
+                           ns, units, s.sm_scale * LOG2E);
+        e = hipGetLastError();
+    } else {
+        switch (s.dk) {
+            case 64: e = launch_gqa_d<64>(s, q, K, V, tok_idx, slot_of, n_slots, part_ml, part_acc, st); break;
+            case 128: e = launch_gqa_d<128>(s, q, K, V, tok_idx, slot_of, n_slots, part_ml, part_acc, st); break;
+            case 256: e = launch_gqa_d<256>(s, q, K, V, tok_idx, slot_of, n_slots, part_ml, part_acc, st); break;
+            default: return hipErrorInvalidValue;
+        }
     }
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(combine_kernel, dim3(s.B * s.Hq), dim3(s.dv < 256 ? 128 : 256), 0, st, part_ml,
+                       part_acc, out, lse, s.dv, ns);
+    return hipGetLastError();
 }
 
 }  // namespace hsab

@@ -333,3 +333,54 @@ def test_gqa48k_full_size_sampled_units():
     assert np.all(np.isfinite(r["out"])) and np.all(np.isfinite(r["lse"]))
     st = _check_all_units(w, h, r, units=[(0, 0), (3, 5), (7, 7)])
     say("gqa48k sampled", st)
+
+
+# ------------------------------------------------------------------- MLA
+def _mla(**kw):
+    base = dict(batch=2, n_q_heads=32, n_kv_heads=1, d_k=576, d_v=512, v_alias_k=True, block=32, r=32,
+                k_blocks=16, k_tokens=100, max_ctx=2048, ctx=2048, n_planted=0)
+    base.update(kw)
+    return _wl(**base)
+
+
+def test_mla_decode_step_ragged():
+    """Absorbed MLA: 32 heads on one 576-dim latent key, values are its first
+    512 dims; K_t not a multiple of the 32-token split."""
+    w = _mla()
+    ctx = np.array([2048, 1111], np.int32)
+    w, h, dev, r = _run_decode(w, ctx)
+    st = _check_all_units(w, h, r)
+    say("mla", st)
+
+
+def test_mla_decode_step_single_token():
+    w = _mla(batch=2, max_ctx=64, ctx=64, k_blocks=2, k_tokens=64)
+    ctx = np.array([1, 40], np.int32)
+    w, h, dev, r = _run_decode(w, ctx)
+    _check_all_units(w, h, r)
+    v = O.bf16_to_f64(h["k_new"][0, 0])[: w.d_v]
+    np.testing.assert_allclose(r["out"][0], np.tile(v, (32, 1)), atol=1e-6)
+
+
+def test_mla_dense_limit_equals_full_attention():
+    w = _mla(max_ctx=256, ctx=256, k_blocks=8, k_tokens=256)
+    ctx = np.array([256, 97], np.int32)
+    w, h, dev, r = _run_decode(w, ctx)
+    K, _ = T.appended_cache(w, h)
+    for b in range(w.batch):
+        n = int(ctx[b])
+        q = torch.tensor(O.bf16_to_f64(h["q"][b]))
+        k = torch.tensor(O.bf16_to_f64(K[b, 0, :n]))
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            q[:, None], k[None].expand(32, -1, -1), k[None, :, :512].expand(32, -1, -1), scale=w.sm_scale)[:, 0]
+        assert np.max(np.abs(r["out"][b] - ref.numpy())) <= T.OUT_ATOL
+
+
+def test_mla64k_full_size_sampled_units():
+    w = W.WORKLOADS["mla64k"]
+    w, h, dev, r = _run_decode(w)
+    assert np.all(np.isfinite(r["out"])) and np.all(np.isfinite(r["lse"]))
+    for b in range(w.batch):
+        assert np.all(np.diff(r["blk"][b, 0]) > 0) and np.all(np.diff(r["tok"][b, 0]) > 0)
+    st = _check_all_units(w, h, r, units=[(0, 0), (5, 0)])
+    say("mla64k sampled", st)
