@@ -41,7 +41,9 @@ Readings where the pages are silent (all fixed here, none printed there):
 Offload (``offload_*``): the fine stage of step t runs over the blocks
 selected at step t-1 while step t's new blocks are fetched; only the set
 difference of consecutive block selections is transferred
-[gist.science/de, section 2.B; gist.science/es, section 2.B].
+[gist.science/de, section 2.B; gist.science/es, section 2.B]. Reading: the
+block being appended to (and the one completed just before it) stays on the
+GPU in a tail slot and never crosses the host link.
 """
 from __future__ import annotations
 
@@ -51,7 +53,7 @@ __all__ = [
     "bf16_to_f64", "n_blocks", "block_meta", "append_meta", "quest_bound",
     "quest_bound_gemm", "block_scores", "topk_stable", "candidate_tokens",
     "label_scores", "attend", "select_tokens_unit", "decode_unit",
-    "decode_all", "offload_delta", "offload_run",
+    "decode_all", "offload_delta", "offload_held", "offload_schedule", "offload_run",
 ]
 
 
@@ -226,17 +228,50 @@ def offload_delta(prev_blocks, cur_blocks) -> np.ndarray:
     return np.setdiff1d(np.asarray(cur_blocks), np.asarray(prev_blocks))
 
 
+def offload_held(n: int, n_prefill: int, bs: int) -> set:
+    """Blocks kept on the GPU outside the selection when the context holds n
+    tokens: the block being appended to, and the block before it if that
+    one was itself appended to during the run (two tail slots). The first
+    such block is the one holding the last prefill token."""
+    jp = (n_prefill - 1) // bs if n_prefill > 0 else 0
+    j = (n - 1) // bs
+    return {j} | ({j - 1} if j - 1 >= jp else set())
+
+
+def offload_schedule(sels, ns, n_prefill, bs):
+    """Transfer schedule of the lagged offload engine from the block
+    selections alone. sels[t] = S_b(t) (selected at step t from the context
+    of ns[t] tokens); step t attends over R(t) = S_b(t-1) (R(0) = S_b(0),
+    filled synchronously before step 0). After the step-t selection the
+    blocks of S_b(t) that are neither resident in a block slot nor held in
+    a tail slot at step t+1 are copied:
+        delta(t) = S_b(t) - (R_slot(t) | held(t+1)),
+        R_slot(t) = R(t) - held(t)   (t >= 1),  R_slot(0) = S_b(0) - held(0).
+    Returns (cold blocks, [delta(t)] per step)."""
+    cold = set(sels[0]) - offload_held(ns[0], n_prefill, bs)
+    out = []
+    for t, sel in enumerate(sels):
+        if t == 0:
+            r_slot = cold
+        else:
+            r_slot = set(sels[t - 1]) - offload_held(ns[t], n_prefill, bs)
+        held_next = offload_held(ns[t] + 1, n_prefill, bs)
+        out.append(np.array(sorted(set(sel) - (r_slot | held_next)), dtype=np.int64))
+    return np.array(sorted(cold), dtype=np.int64), out
+
+
 def offload_run(steps, bs, d_k, d_v, v_alias=False):
     """Lagged offload schedule over a sequence of decode steps of one unit.
 
     ``steps`` is a list of (q [G,d_k], K [>=n,d_k], V [>=n,d_v], n, k_blocks,
-    label_ch, k_tokens, sm_scale). Step t selects S_b(t) from its own query,
-    but its token stage and attention run over the resident set R(t) =
-    S_b(t-1) (R(0) = S_b(0): the cold start is a synchronous fill).
-    Bytes per transferred block = bs * (d_k + d_v) * 2 (bf16; d_k only when
-    values alias keys). Returns a list of per-step dicts."""
+    label_ch, k_tokens, sm_scale), with n growing by one per step. Step t
+    selects S_b(t) from its own query, but its token stage and attention run
+    over the resident set R(t) = S_b(t-1) (R(0) = S_b(0): the cold start is
+    a synchronous fill). Transfers follow offload_schedule. Bytes per block
+    = bs * (d_k + d_v) * 2 (bf16; d_k only when values alias keys).
+    Returns a list of per-step dicts."""
     row_bytes = (d_k if v_alias else d_k + d_v) * 2
-    out = []
+    sels, ns, res = [], [], []
     prev = None
     for t, (q, K, V, n, k_blocks, label_ch, k_tokens, sm_scale) in enumerate(steps):
         kmax, kmin = block_meta(K, n, bs)
@@ -244,9 +279,14 @@ def offload_run(steps, bs, d_k, d_v, v_alias=False):
         resident = cur if prev is None else prev
         tok, _, _ = select_tokens_unit(q, K, n, bs, resident, label_ch, k_tokens)
         o, lse = attend(q, K[tok], V[tok], sm_scale)
-        delta = cur if prev is None else offload_delta(prev, cur)
-        out.append({"sel": cur, "resident": resident, "delta": delta,
-                    "delta_bytes": int(len(delta)) * bs * row_bytes,
-                    "cold": prev is None, "tok_idx": tok, "out": o, "lse": lse})
+        res.append({"sel": cur, "resident": resident, "tok_idx": tok, "out": o, "lse": lse, "n": n})
+        sels.append(cur)
+        ns.append(n)
         prev = cur
-    return out
+    cold, deltas = offload_schedule(sels, ns, steps[0][3] - 1, bs)
+    for t, r in enumerate(res):
+        r["delta"] = deltas[t]
+        r["delta_bytes"] = int(len(deltas[t])) * bs * row_bytes
+        r["cold"] = cold if t == 0 else None
+        r["cold_bytes"] = int(len(cold)) * bs * row_bytes if t == 0 else 0
+    return res

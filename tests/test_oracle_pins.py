@@ -288,25 +288,47 @@ def test_planted_keys_survive_both_stages_tiny4k():
 # ------------------------------------------------------------------ offload
 def test_offload_delta_bytes_hand_sequence():
     """Selections {1,2,3} -> {2,3,4} -> {2,3,4} -> {0,4,5}: the transfers are
-    the cold fill (3 blocks) then 1, 0 and 2 blocks. Bytes per block at
-    block=16, d_k=d_v=128 in bf16: 16*256*2 = 8192."""
+    1, 0 and 2 blocks (set differences). Bytes per block at block=16,
+    d_k=d_v=128 in bf16: 16*256*2 = 8192."""
     assert list(O.offload_delta([1, 2, 3], [2, 3, 4])) == [4]
     assert list(O.offload_delta([2, 3, 4], [2, 3, 4])) == []
     assert list(O.offload_delta([2, 3, 4], [0, 4, 5])) == [0, 5]
+
+
+def test_offload_schedule_hand_sequence_with_tail_rollover():
+    """Hand-worked lagged schedule, block 4, prefill of 9 tokens (blocks
+    0,1 full, block 2 holds token 8). Steps append tokens 9..12, so the
+    contexts are 10, 11, 12, 13 tokens; block 3 opens at step 3.
+      held(n): n=10..12 -> {2} (block 1 was never appended to); n=13 -> {3, 2}
+      sel:  t0 {0,1,2}  t1 {1,2}  t2 {0,2}  t3 {1,3}
+      cold = {0,1,2} - held(10) = {0,1}
+      t0: R_slot = {0,1}; held(11) = {2}; delta = {0,1,2} - {0,1,2} = {}
+      t1: R_slot = {0,1,2} - held(11) = {0,1}; held(12) = {2}; delta = {1,2} - {0,1,2} = {}
+      t2: R_slot = {1,2} - {2} = {1}; held(13) = {2,3}; delta = {0,2} - {1,2,3} = {0}
+      t3: R_slot = {0,2} - held(13) = {0}; held(14) = {2,3}; delta = {1,3} - {0,2,3} = {1}"""
+    sels = [[0, 1, 2], [1, 2], [0, 2], [1, 3]]
+    cold, deltas = O.offload_schedule(sels, [10, 11, 12, 13], 9, 4)
+    assert list(cold) == [0, 1]
+    assert [list(d) for d in deltas] == [[], [], [0], [1]]
+    assert O.offload_held(13, 9, 4) == {2, 3}
+    assert O.offload_held(10, 9, 4) == {2}
+
+
+def test_offload_run_attends_over_previous_selection():
     rng = np.random.default_rng(1)
-    G, d, bs, n = 2, 8, 4, 32
-    K = _bf16(rng.standard_normal((n, d)))
-    V = _bf16(rng.standard_normal((n, d)))
+    G, d, bs, n0 = 2, 8, 4, 31
+    K = _bf16(rng.standard_normal((n0 + 4, d)))
+    V = _bf16(rng.standard_normal((n0 + 4, d)))
     qs = [_bf16(rng.standard_normal((G, d))) for _ in range(4)]
-    steps = [(qs[t], K, V, n, 3, np.arange(2), 6, 0.3) for t in range(4)]
+    steps = [(qs[t], K, V, n0 + 1 + t, 3, np.arange(2), 6, 0.3) for t in range(4)]
     res = O.offload_run(steps, bs, d, d)
     for t, r in enumerate(res):
         if t == 0:
-            assert r["cold"] and r["delta_bytes"] == 3 * bs * 2 * d * 2
             np.testing.assert_array_equal(r["resident"], r["sel"])
         else:
             np.testing.assert_array_equal(r["resident"], res[t - 1]["sel"])
-            want = len(set(r["sel"]) - set(res[t - 1]["sel"]))
-            assert r["delta_bytes"] == want * bs * 2 * d * 2
         # the token stage ran on the resident set only
         assert set(np.asarray(r["tok_idx"]) // bs) <= set(r["resident"])
+        assert r["delta_bytes"] == len(r["delta"]) * bs * 2 * d * 2
+        # every transferred block was selected at this step
+        assert set(r["delta"]) <= set(r["sel"])
