@@ -1,5 +1,6 @@
 // C ABI of libhsab: argument checks, workspace layout and kernel sequencing.
-// The library never allocates, frees or synchronises; every call enqueues
+// Apart from the offload engine object (hsab_offload_create/_begin/_step),
+// the library never allocates, frees or synchronises; every call enqueues
 // its kernels on the caller's stream.
 #include <math.h>
 #include <string.h>
@@ -147,7 +148,7 @@ int hsab_sparse_attend(const hsab_dims* dims, const uint16_t* q, const uint16_t*
     if (rc) return rc;
     const Shape s = make_shape(*dims);
     if (!q || !K || !tok_idx || !out || !lse) return HSAB_EINVAL;
-    if (!s.valias && !V) return HSAB_EINVAL;
+    if (!s.valias && !V && !slot_of) return HSAB_EINVAL;   // a block cache carries its values
     if (slot_of && n_slots < 1) return HSAB_EINVAL;
     const WsLayout L = ws_layout(s);
     if (!ws || ws_bytes < L.total) return HSAB_EINVAL;
@@ -186,6 +187,98 @@ int hsab_decode_step(const hsab_dims* dims, const uint16_t* q, const uint16_t* k
     return hip_status(launch_attend(s, q, K, s.valias ? K : V, tok_idx, nullptr, 0,
                                     reinterpret_cast<float*>(w + L.part_ml),
                                     reinterpret_cast<float*>(w + L.part_acc), nullptr, out, lse, stream));
+}
+
+int hsab_offload_append(const hsab_dims* dims, int32_t n_slots, const uint16_t* k_new,
+                        const uint16_t* v_new, uint16_t* cache, uint16_t* meta, uint16_t* klabel,
+                        const int32_t* label_ch, const int32_t* ctx_len, hipStream_t stream) {
+    int rc = check_dims(dims);
+    if (rc) return rc;
+    const Shape s = make_shape(*dims);
+    if (n_slots < 2 * s.kb + 2) return HSAB_EINVAL;
+    if (!k_new || !cache || !meta || !klabel || !label_ch || !ctx_len) return HSAB_EINVAL;
+    if (!s.valias && !v_new) return HSAB_EINVAL;
+    return hip_status(launch_append_slot(s, n_slots, k_new, v_new, cache, meta, klabel, label_ch, ctx_len, stream));
+}
+
+int hsab_offload_plan(const hsab_dims* dims, int32_t n_slots, const int32_t* resident,
+                      const int32_t* selected, const int32_t* tail, int32_t* slot_map, int32_t* plan,
+                      int64_t* delta_bytes) {
+    int rc = check_dims(dims);
+    if (rc) return rc;
+    const Shape s = make_shape(*dims);
+    if (n_slots < 2 * s.kb + 2) return HSAB_EINVAL;
+    if (!resident || !selected || !tail || !slot_map || !plan) return HSAB_EINVAL;
+    return offload_plan(s, n_slots, resident, selected, tail, slot_map, plan, delta_bytes);
+}
+
+int hsab_offload_copy(const hsab_dims* dims, int32_t n_slots, const uint16_t* host_pool, uint16_t* cache,
+                      const int32_t* plan, int32_t* plan_dev, int32_t* slot_of, hipStream_t copy_stream,
+                      hipEvent_t done, int32_t* n_copies) {
+    int rc = check_dims(dims);
+    if (rc) return rc;
+    const Shape s = make_shape(*dims);
+    if (n_slots < 2 * s.kb + 2) return HSAB_EINVAL;
+    if (!host_pool || !cache || !plan || !plan_dev || !slot_of) return HSAB_EINVAL;
+    int calls = 0;
+    rc = hip_status(offload_copy(s, n_slots, host_pool, cache, plan, plan_dev, slot_of, copy_stream, done, &calls));
+    if (n_copies) *n_copies = calls;
+    return rc;
+}
+
+int hsab_offload_create(const hsab_dims* dims, int32_t n_slots, hsab_offload_engine** engine) {
+    int rc = check_dims(dims);
+    if (rc) return rc;
+    if (!engine) return HSAB_EINVAL;
+    *engine = nullptr;
+    const Shape s = make_shape(*dims);
+    if (n_slots < 2 * s.kb + 2) return HSAB_EINVAL;
+    if (!attend_supported(s)) return HSAB_EUNSUPPORTED;
+    return hip_status(offload_create(s, n_slots, engine));
+}
+
+void hsab_offload_destroy(hsab_offload_engine* engine) { offload_destroy(engine); }
+
+int hsab_offload_begin(hsab_offload_engine* engine, const int32_t* n_prefill, const uint16_t* host_pool,
+                       uint16_t* cache, int32_t* slot_of, hipStream_t stream) {
+    if (!engine || !n_prefill || !host_pool || !cache || !slot_of) return HSAB_EINVAL;
+    const Shape& s = offload_shape(engine);
+    for (int b = 0; b < s.B; ++b)
+        if (n_prefill[b] < 0 || n_prefill[b] >= s.max_ctx) return HSAB_EINVAL;
+    return hip_status(offload_begin(engine, n_prefill, host_pool, cache, slot_of, stream));
+}
+
+int hsab_offload_step(hsab_offload_engine* engine, const uint16_t* q, const uint16_t* k_new,
+                      const uint16_t* v_new, uint16_t* host_pool, uint16_t* cache, uint16_t* meta,
+                      uint16_t* klabel, const int32_t* label_ch, const int32_t* ctx_len,
+                      const int32_t* ctx_len_host, int32_t* slot_of, int32_t* tok_idx, float* out, float* lse,
+                      void* ws, size_t ws_bytes, hipStream_t compute_stream, hipStream_t copy_stream,
+                      hsab_offload_stats* stats) {
+    if (!engine || offload_steps(engine) < 0) return HSAB_EINVAL;   // hsab_offload_begin first
+    const Shape& s = offload_shape(engine);
+    if (!q || !k_new || !host_pool || !cache || !meta || !klabel || !label_ch || !ctx_len || !ctx_len_host ||
+        !slot_of || !tok_idx || !out || !lse)
+        return HSAB_EINVAL;
+    if (!s.valias && !v_new) return HSAB_EINVAL;
+    if (!ws || ws_bytes < ws_layout(s).total) return HSAB_EINVAL;
+    int einval = 0;
+    const int rc = hip_status(offload_step(engine, q, k_new, v_new, host_pool, cache, meta, klabel, label_ch,
+                                           ctx_len, ctx_len_host, slot_of, tok_idx, out, lse, ws, compute_stream,
+                                           copy_stream, stats, &einval));
+    return rc ? rc : (einval ? HSAB_EINVAL : HSAB_OK);
+}
+
+int hsab_offload_timing(hsab_offload_engine* engine, int64_t step, float* ms) {
+    if (!engine || !ms || step < 0 || step >= offload_steps(engine) || step < offload_steps(engine) - 4)
+        return HSAB_EINVAL;
+    return hip_status(offload_timing(engine, step, ms));
+}
+
+int hsab_offload_selection(const hsab_offload_engine* engine, int32_t* blk_idx_host) {
+    if (!engine || !blk_idx_host || offload_steps(engine) < 1) return HSAB_EINVAL;
+    const Shape& s = offload_shape(engine);
+    memcpy(blk_idx_host, offload_last_selection(engine), (size_t)s.B * s.Hkv * s.kb * sizeof(int32_t));
+    return HSAB_OK;
 }
 
 }  // extern "C"

@@ -37,16 +37,19 @@ __device__ __forceinline__ void widen8(uint4 v, float (&f)[8]) {
     f[4] = lo_f32(v.z); f[5] = hi_f32(v.z); f[6] = lo_f32(v.w); f[7] = hi_f32(v.w);
 }
 
-// Row index (in units of rows of the K/V arrays) of token t of unit, or -1.
+// Row index (in rows of d_k elements from the K base) of token t of unit,
+// or -1. Dense caches: unit*max_ctx + t. Block cache: slot s of the unit
+// spans slot_rows rows (key rows first, then value rows), found through
+// slot_of.
 __device__ __forceinline__ long row_of(int t, int unit, int bs, int max_ctx, int nb_cap,
-                                       const int32_t* __restrict__ slot_of, int n_slots) {
+                                       const int32_t* __restrict__ slot_of, int n_slots, int slot_rows) {
     if (t < 0) return -1;
     if (!slot_of) return (t < max_ctx) ? (long)unit * max_ctx + t : -1;
     const int blk = t / bs;
     if (blk >= nb_cap) return -1;
     const int slot = slot_of[(size_t)unit * nb_cap + blk];
     if (slot < 0 || slot >= n_slots) return -1;
-    return ((long)unit * n_slots + slot) * bs + (t - blk * bs);
+    return ((long)unit * n_slots + slot) * slot_rows + (t - blk * bs);
 }
 
 template <int D, int G>
@@ -54,7 +57,7 @@ __global__ __launch_bounds__(256) void attend_gqa_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const int32_t* __restrict__ tok_idx, const int32_t* __restrict__ slot_of, int n_slots,
     float* __restrict__ part_ml, float* __restrict__ part_acc, int Hkv, int bs, int kt,
-    int max_ctx, int nb_cap, int n_splits, int units, float scale2) {
+    int max_ctx, int nb_cap, int n_splits, int units, float scale2, int slot_rows) {
     constexpr int LPT = D / 8;                         // lanes per token
     constexpr int TPI = 64 / LPT;                      // tokens per wave load
     constexpr int TPW = ATT_TOK_PER_SPLIT / 4;         // tokens per wave
@@ -86,7 +89,7 @@ __global__ __launch_bounds__(256) void attend_gqa_kernel(
     for (int it = 0; it < IT; ++it) {
         const int ti = split * ATT_TOK_PER_SPLIT + wave * TPW + it * TPI + ts;
         const int t = ti < kt ? tl[ti] : -1;
-        const long row = row_of(t, unit, bs, max_ctx, nb_cap, slot_of, n_slots);
+        const long row = row_of(t, unit, bs, max_ctx, nb_cap, slot_of, n_slots, slot_rows);
         ok[it] = row >= 0;
         if (ok[it]) {
             kr[it] = ldg16(K + row * D + cc * 8);
@@ -187,7 +190,7 @@ __global__ __launch_bounds__(256) void attend_mla_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ K, const int32_t* __restrict__ tok_idx,
     const int32_t* __restrict__ slot_of, int n_slots, float* __restrict__ part_ml,
     float* __restrict__ part_acc, int Hkv, int dk, int dv, int bs, int kt, int max_ctx, int nb_cap,
-    int n_splits, int units, float scale2) {
+    int n_splits, int units, float scale2, int slot_rows) {
     constexpr int T = MLA_TOK_PER_SPLIT;   // 32 tokens
     constexpr int H = 32;                  // query heads per KV head
     __shared__ uint16_t sV[T][512];
@@ -203,7 +206,7 @@ __global__ __launch_bounds__(256) void attend_mla_kernel(
     if (tid < T) {
         const int ti = split * T + tid;
         const int t = ti < kt ? tok_idx[(size_t)unit * kt + ti] : -1;
-        s_row[tid] = row_of(t, unit, bs, max_ctx, nb_cap, slot_of, n_slots);
+        s_row[tid] = row_of(t, unit, bs, max_ctx, nb_cap, slot_of, n_slots, slot_rows);
     }
     __syncthreads();
 
@@ -327,7 +330,7 @@ hipError_t launch_gqa(const Shape& s, const uint16_t* q, const uint16_t* K, cons
     const int units = s.B * s.Hkv;
     hipLaunchKernelGGL((attend_gqa_kernel<D, G>), dim3(((units + 7) / 8) * 8 * ns), dim3(256), 0, st, q, K, V,
                        tok_idx, slot_of, n_slots, part_ml, part_acc, s.Hkv, s.bs, s.kt, s.max_ctx, s.nb_cap, ns,
-                       units, s.sm_scale * LOG2E);
+                       units, s.sm_scale * LOG2E, 2 * s.bs);
     return hipGetLastError();
 }
 
@@ -362,13 +365,14 @@ hipError_t launch_attend(const Shape& s, const uint16_t* q, const uint16_t* K, c
                          hipStream_t st) {
     (void)arrivals;
     if (!attend_supported(s)) return hipErrorInvalidValue;
+    if (slot_of && !s.valias) V = K + (size_t)s.bs * s.dk;   // value rows follow the key rows in a slot
     const int ns = attn_splits(s);
     hipError_t e = hipSuccess;
     if (mla_shape(s)) {
         const int units = s.B * s.Hkv;
         hipLaunchKernelGGL(attend_mla_kernel, dim3(((units + 7) / 8) * 8 * ns), dim3(256), 0, st, q, K, tok_idx,
                            slot_of, n_slots, part_ml, part_acc, s.Hkv, s.dk, s.dv, s.bs, s.kt, s.max_ctx, s.nb_cap,
-                           ns, units, s.sm_scale * LOG2E);
+                           ns, units, s.sm_scale * LOG2E, s.bs);
         e = hipGetLastError();
     } else {
         switch (s.dk) {

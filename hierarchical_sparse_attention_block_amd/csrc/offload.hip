@@ -1,0 +1,437 @@
+// Offload engine: the full KV cache lives in pinned host memory and a GPU
+// block cache holds the blocks the attention reads. At step t the token
+// stage and attention run over the blocks selected at step t-1 while the
+// blocks newly selected at step t are copied in on a side stream; only the
+// difference between consecutive selections crosses the host link
+// (AsyncTLS, gist.science/de explainer section 2.B; gist.science/es
+// explainer section 2.B).
+//
+// Slot layout of a unit's cache: n_slots slots of block*(d_k+d_v) elements
+// (block*d_k when values alias keys), key rows first then value rows.
+// Slots 0 .. n_slots-3 are "normal" slots; the last two are tail slots,
+// slot n_slots-2 + (j & 1) holds block j while it is being appended to, so
+// a block that has just been completed stays readable while the next one
+// fills. The host pool has the same block layout, [U][nb_cap][slot].
+#include <algorithm>
+#include <chrono>
+#include <cstring>
+#include <vector>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace hsab {
+
+namespace {
+
+// grid: (B). Appends the token at position ctx_len[b]-1 of every KV head
+// into the tail slot of its block, widens that block's max/min and writes
+// its label row.
+__global__ __launch_bounds__(256) void append_slot_kernel(
+    const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new, uint16_t* __restrict__ cache,
+    uint16_t* __restrict__ meta, uint16_t* __restrict__ klabel, const int32_t* __restrict__ label_ch,
+    const int32_t* __restrict__ ctx_len, int Hkv, int dk, int dv, int valias, int bs, int r, int max_ctx,
+    int nb_cap, int n_slots) {
+    const int b = blockIdx.x;
+    const int pos = ctx_len[b] - 1;
+    if (pos < 0 || pos >= max_ctx) return;
+    const int j = pos / bs, off = pos - j * bs;
+    const bool first = off == 0;
+    const size_t slot_elems = (size_t)bs * (valias ? dk : dk + dv);
+    for (int g = 0; g < Hkv; ++g) {
+        const int unit = b * Hkv + g;
+        const uint16_t* kn = k_new + (size_t)unit * dk;
+        uint16_t* slot = cache + ((size_t)unit * n_slots + (n_slots - 2 + (j & 1))) * slot_elems;
+        uint16_t* M = meta + ((size_t)unit * nb_cap + j) * 2 * dk;
+        for (int c = threadIdx.x; c < dk; c += blockDim.x) {
+            const uint16_t kb = kn[c];
+            slot[(size_t)off * dk + c] = kb;
+            if (first) {
+                M[c] = kb;
+                M[dk + c] = kb;
+            } else {
+                const float kf = bf16_f32(kb);
+                if (kf > bf16_f32(M[c])) M[c] = kb;
+                if (kf < bf16_f32(M[dk + c])) M[dk + c] = kb;
+            }
+        }
+        if (!valias) {
+            const uint16_t* vn = v_new + (size_t)unit * dv;
+            for (int c = threadIdx.x; c < dv; c += blockDim.x) slot[(size_t)bs * dk + (size_t)off * dv + c] = vn[c];
+        }
+        uint16_t* Lrow = klabel + ((size_t)unit * max_ctx + pos) * r;
+        for (int c = threadIdx.x; c < r; c += blockDim.x) Lrow[c] = kn[clamp_ch(label_ch[g * r + c], dk)];
+    }
+}
+
+// grid: (U). slot_of[unit][block] = slot for every (block, slot, copy) entry.
+__global__ __launch_bounds__(256) void slot_patch_kernel(const int32_t* __restrict__ plan, int32_t* __restrict__ slot_of,
+                                                         int kb, int nb_cap) {
+    const int unit = blockIdx.x;
+    for (int i = threadIdx.x; i < kb; i += blockDim.x) {
+        const int32_t* e = plan + ((size_t)unit * kb + i) * 3;
+        const int blk = e[0], slot = e[1];
+        if (blk >= 0 && blk < nb_cap) slot_of[(size_t)unit * nb_cap + blk] = slot;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_append_slot(const Shape& s, int n_slots, const uint16_t* k_new, const uint16_t* v_new,
+                              uint16_t* cache, uint16_t* meta, uint16_t* klabel, const int32_t* label_ch,
+                              const int32_t* ctx_len, hipStream_t st) {
+    hipLaunchKernelGGL(append_slot_kernel, dim3(s.B), dim3(256), 0, st, k_new, v_new, cache, meta, klabel,
+                       label_ch, ctx_len, s.Hkv, s.dk, s.dv, s.valias, s.bs, s.r, s.max_ctx, s.nb_cap, n_slots);
+    return hipGetLastError();
+}
+
+// Host planner for one step. resident: blocks the current step's attention
+// reads (R(t)); selected: blocks the next step reads (S_b(t)); tail: per
+// unit the blocks held by the two tail slots at the next step. For every
+// selected block: if it sits in a tail slot, map it there; if it is
+// resident in a normal slot, keep that slot; otherwise copy it into a
+// normal slot that no resident block uses (lowest first).
+int offload_plan(const Shape& s, int n_slots, const int32_t* resident, const int32_t* selected,
+                 const int32_t* tail, int32_t* slot_map, int32_t* plan, int64_t* delta_bytes) {
+    const int U = s.B * s.Hkv, kb = s.kb, n_norm = n_slots - 2;
+    const int64_t blk_bytes = (int64_t)s.bs * (s.valias ? s.dk : s.dk + s.dv) * 2;
+    int64_t bytes = 0;
+    std::vector<char> used(n_norm);
+    std::vector<int> sel;
+    for (int u = 0; u < U; ++u) {
+        const int32_t* R = resident + (size_t)u * kb;
+        const int32_t* S = selected + (size_t)u * kb;
+        int32_t* map = slot_map + (size_t)u * s.nb_cap;
+        int32_t* P = plan + (size_t)u * kb * 3;
+        const int32_t* tl = tail + 2 * u;   // tl[p]: block in tail slot of parity p
+        std::fill(used.begin(), used.end(), 0);
+        for (int i = 0; i < kb; ++i) {
+            const int blk = R[i];
+            if (blk < 0 || blk >= s.nb_cap) continue;
+            const int sl = map[blk];
+            if (sl >= 0 && sl < n_norm) used[sl] = 1;
+        }
+        sel.assign(S, S + kb);
+        std::sort(sel.begin(), sel.end());
+        int np = 0, next_free = 0;
+        for (int blk : sel) {
+            if (blk < 0 || blk >= s.nb_cap) continue;
+            int slot;
+            int copy = 0;
+            if (blk == tl[blk & 1]) {
+                slot = n_slots - 2 + (blk & 1);
+            } else {
+                bool res = false;
+                for (int i = 0; i < kb && !res; ++i) res = R[i] == blk;
+                const int sl = map[blk];
+                if (res && sl >= 0 && sl < n_norm) {
+                    slot = sl;
+                } else {
+                    while (next_free < n_norm && used[next_free]) ++next_free;
+                    if (next_free >= n_norm) return HSAB_EINVAL;   // n_slots too small
+                    slot = next_free;
+                    used[next_free] = 1;
+                    copy = 1;
+                    bytes += blk_bytes;
+                }
+            }
+            map[blk] = slot;
+            P[3 * np + 0] = blk;
+            P[3 * np + 1] = slot;
+            P[3 * np + 2] = copy;
+            ++np;
+        }
+        for (int i = np; i < kb; ++i) P[3 * i] = P[3 * i + 1] = P[3 * i + 2] = -1;
+    }
+    if (delta_bytes) *delta_bytes = bytes;
+    return HSAB_OK;
+}
+
+// Enqueue the plan's copies (contiguous runs of blocks into contiguous
+// slots become one hipMemcpyAsync each), then the slot-table patch, then
+// record `done` on copy_stream.
+hipError_t offload_copy(const Shape& s, int n_slots, const uint16_t* host_pool, uint16_t* cache,
+                        const int32_t* plan, int32_t* plan_dev, int32_t* slot_of, hipStream_t cs,
+                        hipEvent_t done, int* n_copies) {
+    const int U = s.B * s.Hkv, kb = s.kb;
+    const size_t blk_elems = (size_t)s.bs * (s.valias ? s.dk : s.dk + s.dv);
+    int calls = 0;
+    for (int u = 0; u < U; ++u) {
+        const int32_t* P = plan + (size_t)u * kb * 3;
+        int i = 0;
+        while (i < kb && P[3 * i] >= 0) {
+            if (!P[3 * i + 2]) { ++i; continue; }
+            int j = i + 1;
+            while (j < kb && P[3 * j] >= 0 && P[3 * j + 2] && P[3 * j] == P[3 * (j - 1)] + 1 &&
+                   P[3 * j + 1] == P[3 * (j - 1) + 1] + 1)
+                ++j;
+            const int blk = P[3 * i], slot = P[3 * i + 1], run = j - i;
+            hipError_t e = hipMemcpyAsync(cache + ((size_t)u * n_slots + slot) * blk_elems,
+                                          host_pool + ((size_t)u * s.nb_cap + blk) * blk_elems,
+                                          (size_t)run * blk_elems * sizeof(uint16_t), hipMemcpyHostToDevice, cs);
+            if (e != hipSuccess) return e;
+            ++calls;
+            i = j;
+        }
+    }
+    hipError_t e = hipMemcpyAsync(plan_dev, plan, (size_t)U * kb * 3 * sizeof(int32_t), hipMemcpyHostToDevice, cs);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(slot_patch_kernel, dim3(U), dim3(256), 0, cs, plan_dev, slot_of, kb, s.nb_cap);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (n_copies) *n_copies = calls;
+    return done ? hipEventRecord(done, cs) : hipSuccess;
+}
+
+// Blocks the two tail slots hold once the context has n tokens: block
+// j = (n-1)/bs, and j-1 if it was appended to during decoding (j-1 >= the
+// last prefill block jp); -1 where a parity holds none.
+static void tail_blocks(int n, int jp, int bs, int32_t out[2]) {
+    out[0] = out[1] = -1;
+    if (n < 1) return;
+    const int j = (n - 1) / bs;
+    out[j & 1] = j;
+    if (j - 1 >= jp) out[(j - 1) & 1] = j - 1;
+}
+
+}  // namespace hsab
+
+// Engine state; every buffer here is allocated by offload_create.
+struct hsab_offload_engine {
+    hsab::Shape s;
+    int n_slots = 0, U = 0;
+    size_t blk_elems = 0;
+    int64_t step = -1;                        // next step index; -1 before offload_begin
+    std::vector<int32_t> n_ctx, jp;           // [B] tokens so far, last prefill block
+    std::vector<int32_t> prev_sel, cur_sel;   // [U][K_b] S_b(t-1), S_b(t)
+    std::vector<int32_t> none, slot_map, tail;
+    int32_t* sel_h = nullptr;                 // pinned [U][K_b]
+    int32_t* plan_h[2] = {nullptr, nullptr};  // pinned [U][K_b][3]
+    uint16_t* kv_h = nullptr;                 // pinned [U][d_k + d_v]: the new token's rows
+    int32_t* sel_d[2] = {nullptr, nullptr};   // device [U][K_b]
+    int32_t* plan_d[2] = {nullptr, nullptr};  // device [U][K_b][3]
+    hipEvent_t ev_sel = nullptr, ev_copy[2] = {nullptr, nullptr};
+    hipEvent_t tm[4][4] = {};                 // per step % 4: compute begin/end, copy begin/end
+};
+
+namespace hsab {
+
+void offload_destroy(hsab_offload_engine* e) {
+    if (!e) return;
+    if (e->sel_h) (void)hipHostFree(e->sel_h);
+    if (e->kv_h) (void)hipHostFree(e->kv_h);
+    for (int i = 0; i < 2; ++i) {
+        if (e->plan_h[i]) (void)hipHostFree(e->plan_h[i]);
+        if (e->sel_d[i]) (void)hipFree(e->sel_d[i]);
+        if (e->plan_d[i]) (void)hipFree(e->plan_d[i]);
+        if (e->ev_copy[i]) (void)hipEventDestroy(e->ev_copy[i]);
+    }
+    if (e->ev_sel) (void)hipEventDestroy(e->ev_sel);
+    for (auto& row : e->tm)
+        for (auto& ev : row)
+            if (ev) (void)hipEventDestroy(ev);
+    delete e;
+}
+
+hipError_t offload_create(const Shape& s, int n_slots, hsab_offload_engine** out) {
+    auto* e = new hsab_offload_engine();
+    e->s = s;
+    e->n_slots = n_slots;
+    e->U = s.B * s.Hkv;
+    e->blk_elems = (size_t)s.bs * (s.valias ? s.dk : s.dk + s.dv);
+    const size_t nsel = (size_t)e->U * s.kb;
+    e->n_ctx.assign(s.B, 0);
+    e->jp.assign(s.B, 0);
+    e->prev_sel.assign(nsel, -1);
+    e->cur_sel.assign(nsel, -1);
+    e->none.assign(nsel, -1);
+    e->slot_map.assign((size_t)e->U * s.nb_cap, -1);
+    e->tail.assign((size_t)e->U * 2, -1);
+    hipError_t r = hipSuccess;
+    auto ok = [&](hipError_t x) { if (r == hipSuccess) r = x; };
+    ok(hipHostMalloc((void**)&e->sel_h, nsel * sizeof(int32_t), hipHostMallocDefault));
+    ok(hipHostMalloc((void**)&e->kv_h, (size_t)e->U * (s.dk + s.dv) * sizeof(uint16_t), hipHostMallocDefault));
+    for (int i = 0; i < 2; ++i) {
+        ok(hipHostMalloc((void**)&e->plan_h[i], nsel * 3 * sizeof(int32_t), hipHostMallocDefault));
+        ok(hipMalloc((void**)&e->sel_d[i], nsel * sizeof(int32_t)));
+        ok(hipMalloc((void**)&e->plan_d[i], nsel * 3 * sizeof(int32_t)));
+        ok(hipEventCreate(&e->ev_copy[i]));
+    }
+    ok(hipEventCreateWithFlags(&e->ev_sel, hipEventDisableTiming));
+    for (auto& row : e->tm)
+        for (auto& ev : row) ok(hipEventCreate(&ev));
+    if (r != hipSuccess) {
+        offload_destroy(e);
+        return r;
+    }
+    *out = e;
+    return hipSuccess;
+}
+
+// After prefill: each unit's last prefill block goes to its tail slot and
+// the slot table is reset. Synchronous on st.
+hipError_t offload_begin(hsab_offload_engine* e, const int32_t* n_prefill, const uint16_t* host_pool,
+                         uint16_t* cache, int32_t* slot_of, hipStream_t st) {
+    const Shape& s = e->s;
+    std::fill(e->slot_map.begin(), e->slot_map.end(), -1);
+    for (int b = 0; b < s.B; ++b) {
+        const int np = n_prefill[b];
+        e->n_ctx[b] = np;
+        e->jp[b] = np > 0 ? (np - 1) / s.bs : 0;
+        if (np == 0) continue;
+        const int j = e->jp[b], slot = e->n_slots - 2 + (j & 1);
+        for (int g = 0; g < s.Hkv; ++g) {
+            const int u = b * s.Hkv + g;
+            hipError_t r = hipMemcpyAsync(cache + ((size_t)u * e->n_slots + slot) * e->blk_elems,
+                                          host_pool + ((size_t)u * s.nb_cap + j) * e->blk_elems,
+                                          e->blk_elems * sizeof(uint16_t), hipMemcpyHostToDevice, st);
+            if (r != hipSuccess) return r;
+            e->slot_map[(size_t)u * s.nb_cap + j] = slot;
+        }
+    }
+    hipError_t r = hipMemcpyAsync(slot_of, e->slot_map.data(), e->slot_map.size() * sizeof(int32_t),
+                                  hipMemcpyHostToDevice, st);
+    if (r != hipSuccess) return r;
+    r = hipStreamSynchronize(st);
+    if (r != hipSuccess) return r;
+    std::fill(e->prev_sel.begin(), e->prev_sel.end(), -1);
+    e->step = 0;
+    return hipSuccess;
+}
+
+#define HSAB_TRY(x)                            \
+    do {                                       \
+        const hipError_t _e = (x);             \
+        if (_e != hipSuccess) return _e;       \
+    } while (0)
+
+// One decode step under the lagged schedule. Compute stream: append into
+// the tail slot, block scores and S_b(t), its copy to the host, the token
+// stage over R(t), then (after the copies of the previous step) attention
+// through the slot table. Host: wait for S_b(t) only, write the new token
+// into the pool, plan, and enqueue the copies on the copy stream; the
+// copies run while the GPU finishes step t and starts step t+1.
+hipError_t offload_step(hsab_offload_engine* e, const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
+                        uint16_t* host_pool, uint16_t* cache, uint16_t* meta, uint16_t* klabel,
+                        const int32_t* label_ch, const int32_t* ctx_len, const int32_t* ctx_len_host,
+                        int32_t* slot_of, int32_t* tok_idx, float* out, float* lse, void* ws, hipStream_t cs,
+                        hipStream_t xs, hsab_offload_stats* st, int* einval) {
+    using clk = std::chrono::steady_clock;
+    const Shape& s = e->s;
+    *einval = 0;
+    for (int b = 0; b < s.B; ++b)   // one token per sequence per step
+        if (ctx_len_host[b] != e->n_ctx[b] + 1 || ctx_len_host[b] > s.max_ctx) {
+            *einval = 1;
+            return hipSuccess;
+        }
+    const int U = e->U, kb = s.kb, t = (int)(e->step & 0x7fffffff);
+    const size_t nsel = (size_t)U * kb;
+    const WsLayout L = ws_layout(s);
+    char* w = static_cast<char*>(ws);
+    float* blk_score = reinterpret_cast<float*>(w + L.blk_score);
+    float* part_ml = reinterpret_cast<float*>(w + L.part_ml);
+    float* part_acc = reinterpret_cast<float*>(w + L.part_acc);
+    hipEvent_t* tm = e->tm[e->step & 3];
+    int32_t* sel_now = e->sel_d[t & 1];
+    const int32_t* resident = e->step == 0 ? sel_now : e->sel_d[(t - 1) & 1];
+
+    // ---- compute stream, up to the token stage
+    HSAB_TRY(hipEventRecord(tm[0], cs));
+    HSAB_TRY(launch_append_slot(s, e->n_slots, k_new, v_new, cache, meta, klabel, label_ch, ctx_len, cs));
+    HSAB_TRY(hipMemcpyAsync(e->kv_h, k_new, (size_t)U * s.dk * sizeof(uint16_t), hipMemcpyDeviceToHost, cs));
+    if (!s.valias)
+        HSAB_TRY(hipMemcpyAsync(e->kv_h + (size_t)U * s.dk, v_new, (size_t)U * s.dv * sizeof(uint16_t),
+                                hipMemcpyDeviceToHost, cs));
+    HSAB_TRY(launch_block_score(s, q, meta, ctx_len, blk_score, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                nullptr, cs));
+    HSAB_TRY(launch_select(s, 1, q, blk_score, nullptr, nullptr, ctx_len, sel_now, nullptr, nullptr, nullptr, cs));
+    HSAB_TRY(hipMemcpyAsync(e->sel_h, sel_now, nsel * sizeof(int32_t), hipMemcpyDeviceToHost, cs));
+    HSAB_TRY(hipEventRecord(e->ev_sel, cs));
+    HSAB_TRY(launch_select(s, 2, q, nullptr, klabel, label_ch, ctx_len, const_cast<int32_t*>(resident), tok_idx,
+                           nullptr, nullptr, cs));
+    if (e->step > 0) {
+        HSAB_TRY(hipStreamWaitEvent(cs, e->ev_copy[(t - 1) & 1], 0));
+        HSAB_TRY(launch_attend(s, q, cache, cache, tok_idx, slot_of, e->n_slots, part_ml, part_acc, nullptr, out,
+                               lse, cs));
+        HSAB_TRY(hipEventRecord(tm[1], cs));
+    }
+
+    // ---- host: S_b(t), the new rows into the pool, plans
+    const auto t0 = clk::now();
+    HSAB_TRY(hipEventSynchronize(e->ev_sel));
+    const auto t1 = clk::now();
+    std::memcpy(e->cur_sel.data(), e->sel_h, nsel * sizeof(int32_t));
+    for (int u = 0; u < U; ++u) {
+        const int b = u / s.Hkv, pos = e->n_ctx[b];   // the appended token
+        const int j = pos / s.bs, off = pos - j * s.bs;
+        uint16_t* blk = host_pool + ((size_t)u * s.nb_cap + j) * e->blk_elems;
+        std::memcpy(blk + (size_t)off * s.dk, e->kv_h + (size_t)u * s.dk, s.dk * sizeof(uint16_t));
+        if (!s.valias)
+            std::memcpy(blk + (size_t)s.bs * s.dk + (size_t)off * s.dv, e->kv_h + (size_t)U * s.dk + (size_t)u * s.dv,
+                        s.dv * sizeof(uint16_t));
+    }
+    for (int b = 0; b < s.B; ++b) e->n_ctx[b] += 1;
+    int64_t cold_bytes = 0, delta_bytes = 0;
+    int copies = 0, calls = 0;
+    if (e->step == 0) {   // cold start: fill S_b(0) synchronously
+        for (int u = 0; u < U; ++u) tail_blocks(e->n_ctx[u / s.Hkv], e->jp[u / s.Hkv], s.bs, &e->tail[2 * u]);
+        if (offload_plan(s, e->n_slots, e->none.data(), e->cur_sel.data(), e->tail.data(), e->slot_map.data(),
+                         e->plan_h[1], &cold_bytes) != HSAB_OK) {
+            *einval = 1;
+            return hipSuccess;
+        }
+        HSAB_TRY(offload_copy(s, e->n_slots, host_pool, cache, e->plan_h[1], e->plan_d[1], slot_of, xs,
+                              e->ev_copy[1], &calls));
+        copies += calls;
+        HSAB_TRY(hipStreamWaitEvent(cs, e->ev_copy[1], 0));
+        HSAB_TRY(launch_attend(s, q, cache, cache, tok_idx, slot_of, e->n_slots, part_ml, part_acc, nullptr, out,
+                               lse, cs));
+        HSAB_TRY(hipEventRecord(tm[1], cs));
+    }
+    for (int u = 0; u < U; ++u) tail_blocks(e->n_ctx[u / s.Hkv] + 1, e->jp[u / s.Hkv], s.bs, &e->tail[2 * u]);
+    const int32_t* R = e->step == 0 ? e->cur_sel.data() : e->prev_sel.data();
+    if (offload_plan(s, e->n_slots, R, e->cur_sel.data(), e->tail.data(), e->slot_map.data(), e->plan_h[t & 1],
+                     &delta_bytes) != HSAB_OK) {
+        *einval = 1;
+        return hipSuccess;
+    }
+    HSAB_TRY(hipEventRecord(tm[2], xs));
+    HSAB_TRY(offload_copy(s, e->n_slots, host_pool, cache, e->plan_h[t & 1], e->plan_d[t & 1], slot_of, xs,
+                          e->ev_copy[t & 1], &calls));
+    copies += calls;
+    HSAB_TRY(hipEventRecord(tm[3], xs));
+    const auto t2 = clk::now();
+    e->prev_sel.swap(e->cur_sel);
+    if (st) {
+        const int64_t blk_bytes = (int64_t)e->blk_elems * 2;
+        st->step = e->step;
+        st->delta_bytes = delta_bytes;
+        st->delta_blocks = (int32_t)(delta_bytes / blk_bytes);
+        st->cold_bytes = cold_bytes;
+        st->n_copies = copies;
+        st->host_wait_ms = std::chrono::duration<float, std::milli>(t1 - t0).count();
+        st->host_plan_ms = std::chrono::duration<float, std::milli>(t2 - t1).count();
+    }
+    e->step += 1;
+    return hipSuccess;
+}
+
+// GPU times of a finished step (within the last four): compute stream
+// span, copy span, and the copy's start and end relative to the step's
+// compute start. Waits for that step's events.
+hipError_t offload_timing(hsab_offload_engine* e, int64_t step, float* ms4) {
+    hipEvent_t* tm = e->tm[step & 3];
+    HSAB_TRY(hipEventSynchronize(tm[3]));
+    HSAB_TRY(hipEventSynchronize(tm[1]));
+    HSAB_TRY(hipEventElapsedTime(&ms4[0], tm[0], tm[1]));
+    HSAB_TRY(hipEventElapsedTime(&ms4[1], tm[2], tm[3]));
+    HSAB_TRY(hipEventElapsedTime(&ms4[2], tm[0], tm[2]));
+    HSAB_TRY(hipEventElapsedTime(&ms4[3], tm[0], tm[3]));
+    return hipSuccess;
+}
+
+const int32_t* offload_last_selection(const hsab_offload_engine* e) { return e->prev_sel.data(); }
+int64_t offload_steps(const hsab_offload_engine* e) { return e->step; }
+const Shape& offload_shape(const hsab_offload_engine* e) { return e->s; }
+
+}  // namespace hsab

@@ -23,7 +23,9 @@ _lib = ctypes.CDLL(LIB_PATH)
 HSAB_OK, HSAB_EINVAL, HSAB_EHIP, HSAB_EUNSUPPORTED = 0, -1, -2, -3
 EXPORTS = ("hsab_workspace_bytes", "hsab_status_string", "hsab_last_hip_error", "hsab_build_meta",
            "hsab_score_blocks", "hsab_select_blocks", "hsab_select_tokens", "hsab_sparse_attend",
-           "hsab_decode_step")
+           "hsab_decode_step", "hsab_offload_append", "hsab_offload_plan", "hsab_offload_copy", "hsab_offload_create",
+           "hsab_offload_destroy", "hsab_offload_begin", "hsab_offload_step", "hsab_offload_timing",
+           "hsab_offload_selection")
 
 
 class Dims(ctypes.Structure):
@@ -65,8 +67,29 @@ _lib.hsab_select_tokens.argtypes = [_D, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, 
 _lib.hsab_sparse_attend.argtypes = [_D, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _sz, _vp]
 _lib.hsab_decode_step.argtypes = [_D, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                   _vp, _sz, _vp]
+_lib.hsab_offload_append.argtypes = [_D, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+_lib.hsab_offload_plan.argtypes = [_D, _i32, _vp, _vp, _vp, _vp, _vp, _vp]
+_lib.hsab_offload_copy.argtypes = [_D, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+
+
+class OffloadStats(ctypes.Structure):
+    _fields_ = [("step", ctypes.c_int64), ("delta_bytes", ctypes.c_int64), ("cold_bytes", ctypes.c_int64),
+                ("delta_blocks", ctypes.c_int32), ("n_copies", ctypes.c_int32),
+                ("host_wait_ms", ctypes.c_float), ("host_plan_ms", ctypes.c_float)]
+
+    def as_dict(self):
+        return {n: getattr(self, n) for n, _ in self._fields_}
+
+
+_lib.hsab_offload_create.argtypes = [_D, _i32, ctypes.POINTER(_vp)]
+_lib.hsab_offload_destroy.argtypes = [_vp]
+_lib.hsab_offload_begin.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp]
+_lib.hsab_offload_step.argtypes = [_vp] * 16 + [_sz, _vp, _vp, ctypes.POINTER(OffloadStats)]
+_lib.hsab_offload_timing.argtypes = [_vp, ctypes.c_int64, _vp]
+_lib.hsab_offload_selection.argtypes = [_vp, _vp]
 for _f in EXPORTS[3:]:
     getattr(_lib, _f).restype = ctypes.c_int
+_lib.hsab_offload_destroy.restype = None
 
 
 class HsabError(RuntimeError):
@@ -107,6 +130,26 @@ def _buf(name, t, dtype, numel, allow_none=False):
         raise ValueError(f"{name} must be {'bf16 bits' if dtype is _u16 else dtype}, got {t.dtype}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+    if t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, needs {numel}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _hbuf(name, t, dtype, numel, pinned=False, allow_none=False):
+    """Pointer of a host buffer after checking dtype, layout and size."""
+    if t is None:
+        if allow_none:
+            return None
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor) or t.is_cuda:
+        raise ValueError(f"{name} must be a host tensor")
+    ok = t.dtype in _BF16_BITS if dtype is _u16 else t.dtype == dtype
+    if not ok:
+        raise ValueError(f"{name} must be {'bf16 bits' if dtype is _u16 else dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if pinned and not t.is_pinned():
+        raise ValueError(f"{name} must be pinned host memory")
     if t.numel() < numel:
         raise ValueError(f"{name} holds {t.numel()} elements, needs {numel}")
     return ctypes.c_void_p(t.data_ptr())
@@ -189,12 +232,13 @@ def sparse_attend(d: Dims, q, K, V, tok_idx, ctx_len, out, lse, ws, slot_of=None
     U = d.batch * d.n_kv_heads
     if slot_of is None:
         kn, vn = s["K"], s["V"]
-    else:
-        kn, vn = U * n_slots * d.block * d.d_k, U * n_slots * d.block * d.d_v
+    else:   # block cache: key rows then value rows per slot, V unused
+        kn, vn, V = U * n_slots * block_elems(d), 0, None
     wp, wn = _ws(d, ws)
     _check("hsab_sparse_attend", _lib.hsab_sparse_attend(
         ctypes.byref(d), _buf("q", q, _u16, s["q"]), _buf("K", K, _u16, kn),
-        _buf("V", V, _u16, vn, allow_none=bool(d.v_alias_k)), _buf("tok_idx", tok_idx, _i, s["tok"]),
+        _buf("V", V, _u16, vn, allow_none=bool(d.v_alias_k) or slot_of is not None),
+        _buf("tok_idx", tok_idx, _i, s["tok"]),
         _buf("ctx_len", ctx_len, _i, s["ctx"]),
         _buf("slot_of", slot_of, _i, U * d.nb_cap, allow_none=True), ctypes.c_int32(n_slots),
         _buf("out", out, _f, s["out"]), _buf("lse", lse, _f, s["lse"]), wp, wn, _stream(stream)))
@@ -213,6 +257,119 @@ def decode_step(d: Dims, q, k_new, v_new, K, V, meta, klabel, label_ch, ctx_len,
         _buf("ctx_len", ctx_len, _i, s["ctx"]), _buf("blk_idx", blk_idx, _i, s["blk"]),
         _buf("tok_idx", tok_idx, _i, s["tok"]), _buf("out", out, _f, s["out"]),
         _buf("lse", lse, _f, s["lse"]), wp, wn, _stream(stream)))
+
+
+def block_elems(d: Dims) -> int:
+    """bf16 elements of one block in the host pool and the block cache."""
+    return d.block * (d.d_k if d.v_alias_k else d.d_k + d.d_v)
+
+
+def offload_append(d: Dims, n_slots, k_new, v_new, cache, meta, klabel, label_ch, ctx_len, stream=None):
+    s = _sizes(d)
+    U = d.batch * d.n_kv_heads
+    alias = bool(d.v_alias_k)
+    _check("hsab_offload_append", _lib.hsab_offload_append(
+        ctypes.byref(d), ctypes.c_int32(n_slots), _buf("k_new", k_new, _u16, s["knew"]),
+        _buf("v_new", v_new, _u16, s["vnew"], allow_none=alias),
+        _buf("cache", cache, _u16, U * n_slots * block_elems(d)), _buf("meta", meta, _u16, s["meta"]),
+        _buf("klabel", klabel, _u16, s["klabel"]), _buf("label_ch", label_ch, _i, s["label"]),
+        _buf("ctx_len", ctx_len, _i, s["ctx"]), _stream(stream)))
+
+
+def offload_plan(d: Dims, n_slots, resident, selected, tail, slot_map, plan) -> int:
+    """Host planner; every argument is a host int32 tensor. Returns the
+    bytes the plan copies."""
+    U = d.batch * d.n_kv_heads
+    nb = ctypes.c_int64(0)
+    _check("hsab_offload_plan", _lib.hsab_offload_plan(
+        ctypes.byref(d), ctypes.c_int32(n_slots), _hbuf("resident", resident, _i, U * d.k_blocks),
+        _hbuf("selected", selected, _i, U * d.k_blocks), _hbuf("tail", tail, _i, U * 2),
+        _hbuf("slot_map", slot_map, _i, U * d.nb_cap), _hbuf("plan", plan, _i, U * d.k_blocks * 3),
+        ctypes.byref(nb)))
+    return int(nb.value)
+
+
+def offload_copy(d: Dims, n_slots, host_pool, cache, plan, plan_dev, slot_of, copy_stream, done=None) -> int:
+    """Enqueue a plan's copies on copy_stream; returns the memcpy count.
+    host_pool and plan are pinned host tensors; done is a torch.cuda.Event
+    (recorded on copy_stream) or None."""
+    U = d.batch * d.n_kv_heads
+    nc = ctypes.c_int32(0)
+    ev = None
+    if done is not None:
+        ev = ctypes.c_void_p(done.cuda_event)
+    _check("hsab_offload_copy", _lib.hsab_offload_copy(
+        ctypes.byref(d), ctypes.c_int32(n_slots),
+        _hbuf("host_pool", host_pool, _u16, U * d.nb_cap * block_elems(d), pinned=True),
+        _buf("cache", cache, _u16, U * n_slots * block_elems(d)),
+        _hbuf("plan", plan, _i, U * d.k_blocks * 3, pinned=True),
+        _buf("plan_dev", plan_dev, _i, U * d.k_blocks * 3), _buf("slot_of", slot_of, _i, U * d.nb_cap),
+        _stream(copy_stream), ev, ctypes.byref(nc)))
+    return int(nc.value)
+
+
+class OffloadEngine:
+    """Handle of a native offload engine (hsab_offload_create). The caller
+    owns the pool (pinned host), the block cache, metadata and outputs."""
+
+    def __init__(self, d: Dims, n_slots: int):
+        self.d, self.n_slots = d, int(n_slots)
+        h = ctypes.c_void_p()
+        _check("hsab_offload_create", _lib.hsab_offload_create(ctypes.byref(d), ctypes.c_int32(n_slots),
+                                                               ctypes.byref(h)))
+        self._h = h
+
+    def close(self):
+        if self._h:
+            _lib.hsab_offload_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def begin(self, n_prefill, host_pool, cache, slot_of, stream=None):
+        d = self.d
+        U = d.batch * d.n_kv_heads
+        _check("hsab_offload_begin", _lib.hsab_offload_begin(
+            self._h, _hbuf("n_prefill", n_prefill, _i, d.batch),
+            _hbuf("host_pool", host_pool, _u16, U * d.nb_cap * block_elems(d), pinned=True),
+            _buf("cache", cache, _u16, U * self.n_slots * block_elems(d)),
+            _buf("slot_of", slot_of, _i, U * d.nb_cap), _stream(stream)))
+
+    def step(self, q, k_new, v_new, host_pool, cache, meta, klabel, label_ch, ctx_len, ctx_len_host, slot_of,
+             tok_idx, out, lse, ws, compute_stream=None, copy_stream=None) -> OffloadStats:
+        d = self.d
+        s = _sizes(d)
+        U = d.batch * d.n_kv_heads
+        wp, wn = _ws(d, ws)
+        st = OffloadStats()
+        if copy_stream is None:
+            raise ValueError("copy_stream is required")
+        _check("hsab_offload_step", _lib.hsab_offload_step(
+            self._h, _buf("q", q, _u16, s["q"]), _buf("k_new", k_new, _u16, s["knew"]),
+            _buf("v_new", v_new, _u16, s["vnew"], allow_none=bool(d.v_alias_k)),
+            _hbuf("host_pool", host_pool, _u16, U * d.nb_cap * block_elems(d), pinned=True),
+            _buf("cache", cache, _u16, U * self.n_slots * block_elems(d)), _buf("meta", meta, _u16, s["meta"]),
+            _buf("klabel", klabel, _u16, s["klabel"]), _buf("label_ch", label_ch, _i, s["label"]),
+            _buf("ctx_len", ctx_len, _i, s["ctx"]), _hbuf("ctx_len_host", ctx_len_host, _i, d.batch),
+            _buf("slot_of", slot_of, _i, U * d.nb_cap), _buf("tok_idx", tok_idx, _i, s["tok"]),
+            _buf("out", out, _f, s["out"]), _buf("lse", lse, _f, s["lse"]), wp, wn, _stream(compute_stream),
+            _stream(copy_stream), ctypes.byref(st)))
+        return st
+
+    def timing(self, step):
+        ms = (ctypes.c_float * 4)()
+        _check("hsab_offload_timing", _lib.hsab_offload_timing(self._h, ctypes.c_int64(step), ms))
+        return {"compute_ms": ms[0], "copy_ms": ms[1], "copy_start_ms": ms[2], "copy_end_ms": ms[3]}
+
+    def selection(self) -> torch.Tensor:
+        d = self.d
+        outb = torch.empty(d.batch * d.n_kv_heads * d.k_blocks, dtype=torch.int32)
+        _check("hsab_offload_selection", _lib.hsab_offload_selection(self._h, ctypes.c_void_p(outb.data_ptr())))
+        return outb.view(d.batch, d.n_kv_heads, d.k_blocks)
 
 
 def raw_call(name, *args):

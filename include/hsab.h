@@ -77,8 +77,10 @@ extern "C" {
  * r in {16, 32, 64, 128}, r <= d_k; 1 <= K_b <= 2048;
  * K_b * block <= 8192; nb_cap <= 8192; K_t >= 1.
  * Attention kernels exist for d_k == d_v in {64, 128, 256} with G in
- * {1, 2, 4, 8} (GQA/MQA/MHA); other shapes return HSAB_EUNSUPPORTED from
- * hsab_sparse_attend and hsab_decode_step. */
+ * {1, 2, 4, 8} (GQA/MQA/MHA, separate V), and for the absorbed latent
+ * layout (v_alias_k, G == 32, d_k % 32 == 0, d_v % 64 == 0, d_v <= 512);
+ * other shapes return HSAB_EUNSUPPORTED from hsab_sparse_attend and
+ * hsab_decode_step. */
 typedef struct hsab_dims {
     int32_t batch;        /* B */
     int32_t n_q_heads;    /* Hq */
@@ -147,10 +149,11 @@ int hsab_select_tokens(const hsab_dims* dims, const uint16_t* q, const uint16_t*
  *   out[b][h] = sum_t softmax_t(sm_scale * q_h . K_t) V_t,  t in tok_idx[b][h/G]
  * computed as split partials (max, sum, weighted values) merged by
  * log-sum-exp. -1 entries of tok_idx are skipped.
- * slot_of == NULL: K and V are the dense caches above. Otherwise K and V
- * are block caches [B][Hkv][n_slots][block][d] (same row layout) and
- * slot_of [B][Hkv][nb_cap] int32 gives the cache slot of block j
- * (used by the offload engine; a token whose block has slot < 0 is skipped). */
+ * slot_of == NULL: K and V are the dense caches above. Otherwise K is the
+ * offload engine's block cache [B][Hkv][n_slots][slot] (a slot is block
+ * key rows of d_k followed, unless v_alias_k, by block value rows of d_v),
+ * V is ignored, and slot_of [B][Hkv][nb_cap] int32 gives the cache slot of
+ * block j; a token whose block has a slot outside [0, n_slots) is skipped. */
 int hsab_sparse_attend(const hsab_dims* dims, const uint16_t* q, const uint16_t* K,
                        const uint16_t* V, const int32_t* tok_idx, const int32_t* ctx_len,
                        const int32_t* slot_of, int32_t n_slots, float* out, float* lse,
@@ -168,6 +171,115 @@ int hsab_decode_step(const hsab_dims* dims, const uint16_t* q, const uint16_t* k
                      uint16_t* klabel, const int32_t* label_ch, const int32_t* ctx_len,
                      int32_t* blk_idx, int32_t* tok_idx, float* out, float* lse,
                      void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------ offload
+ * Asynchronous offload engine [de 2.B; es 2.B]: the whole KV cache lives in
+ * pinned host memory; a GPU block cache holds the blocks the attention reads.
+ * Step t selects S_b(t) on the GPU (metadata and label rows stay on the GPU),
+ * attends over R(t) = S_b(t-1) through the block cache, and meanwhile copies
+ * only the blocks of S_b(t) not already on the GPU, on a side stream, so
+ * they are resident for step t+1. Step 0 attends over S_b(0) after a
+ * synchronous fill.
+ *
+ * Block layout (pool and cache): a block is block*d_k key values followed by
+ * block*d_v value values (no values when v_alias_k), bf16.
+ *   host_pool  pinned host [B][Hkv][nb_cap][block elements]
+ *   cache      device      [B][Hkv][n_slots][block elements]
+ *   slot_of    device      [B][Hkv][nb_cap] int32: cache slot of a resident
+ *              block; read by hsab_sparse_attend (pass cache as K; V is
+ *              ignored in that mode).
+ * Slots 0 .. n_slots-3 hold selected blocks; slots n_slots-2 and n_slots-1
+ * are tail slots: block j is appended to in slot n_slots-2 + (j & 1), so the
+ * block being appended to and the one completed just before it stay on the
+ * GPU and never cross the host link. n_slots >= 2*K_b + 2.
+ */
+
+/* Append the token at position ctx_len[b]-1 (k_new [B][Hkv][d_k], v_new
+ * [B][Hkv][d_v]) into its block's tail slot, widen that block's key max/min
+ * (or start it) and write its label row. The caller writes the same rows
+ * into host_pool. */
+int hsab_offload_append(const hsab_dims* dims, int32_t n_slots, const uint16_t* k_new,
+                        const uint16_t* v_new, uint16_t* cache, uint16_t* meta, uint16_t* klabel,
+                        const int32_t* label_ch, const int32_t* ctx_len, hipStream_t stream);
+
+/* Host-only planner of one step (no GPU call). All arrays are host memory.
+ *   resident  [B][Hkv][K_b] blocks the current step's attention reads, -1 pad
+ *   selected  [B][Hkv][K_b] blocks the next step reads, -1 pad
+ *   tail      [B][Hkv][2]   block held by tail slot parity p at the next
+ *                           step, -1 if none
+ *   slot_map  [B][Hkv][nb_cap] in/out host mirror of slot_of
+ *   plan      [B][Hkv][K_b][3] out: (block, slot, copy?) for every selected
+ *                           block, ascending by block, -1 padded
+ *   delta_bytes             out (nullable): bytes to copy
+ * A selected block held in a tail slot maps there; one resident in a block
+ * slot keeps it; any other is copied into the lowest block slot no resident
+ * block uses. Returns HSAB_EINVAL if n_slots is too small. */
+int hsab_offload_plan(const hsab_dims* dims, int32_t n_slots, const int32_t* resident,
+                      const int32_t* selected, const int32_t* tail, int32_t* slot_map, int32_t* plan,
+                      int64_t* delta_bytes);
+
+/* Enqueue a plan on copy_stream: one hipMemcpyAsync per run of consecutive
+ * blocks going to consecutive slots, the upload of the plan (plan must be
+ * pinned host memory; plan_dev is device [B][Hkv][K_b][3] int32), a kernel
+ * that writes slot_of for every planned block, then `done` (nullable) is
+ * recorded. n_copies (nullable) receives the number of memcpy calls. */
+int hsab_offload_copy(const hsab_dims* dims, int32_t n_slots, const uint16_t* host_pool, uint16_t* cache,
+                      const int32_t* plan, int32_t* plan_dev, int32_t* slot_of, hipStream_t copy_stream,
+                      hipEvent_t done, int32_t* n_copies);
+
+/* Offload engine object: the lagged schedule above driven step by step.
+ * It owns only small buffers (pinned copies of S_b and of the plan, the new
+ * token's rows, two index buffers on the GPU) and events, allocated by
+ * hsab_offload_create and freed by hsab_offload_destroy; the caller owns
+ * the pool, the block cache, metadata, label rows and outputs. Unlike the
+ * rest of the library, hsab_offload_step waits on the host (for S_b(t),
+ * about 16 KiB D2H) once per step. One engine serves one caller thread. */
+typedef struct hsab_offload_engine hsab_offload_engine;
+
+typedef struct hsab_offload_stats {
+    int64_t step;          /* index of the step just enqueued (0 = cold start) */
+    int64_t delta_bytes;   /* host-to-device bytes of the step's delta */
+    int64_t cold_bytes;    /* bytes of the synchronous fill of S_b(0); step 0 only */
+    int32_t delta_blocks;  /* blocks in the delta */
+    int32_t n_copies;      /* hipMemcpyAsync calls (coalesced runs) */
+    float host_wait_ms;    /* host wait for S_b(t) */
+    float host_plan_ms;    /* pool write, planning and enqueue */
+} hsab_offload_stats;
+
+/* n_slots >= 2*K_b + 2; HSAB_EHIP if an allocation fails. */
+int hsab_offload_create(const hsab_dims* dims, int32_t n_slots, hsab_offload_engine** engine);
+void hsab_offload_destroy(hsab_offload_engine* engine);
+
+/* After prefill (host_pool holds n_prefill[b] tokens of every sequence,
+ * meta/klabel built on the GPU, e.g. by hsab_build_meta): copies each
+ * unit's last prefill block into its tail slot, resets slot_of and the
+ * engine's step counter. n_prefill is host memory, 0 <= n_prefill[b] <
+ * max_ctx. Synchronous. */
+int hsab_offload_begin(hsab_offload_engine* engine, const int32_t* n_prefill, const uint16_t* host_pool,
+                       uint16_t* cache, int32_t* slot_of, hipStream_t stream);
+
+/* Decode step t [de 2.B; es 2.B]: appends k_new/v_new (device, written to
+ * the tail slot, meta, klabel, and to host_pool by the host), selects
+ * S_b(t), runs the token stage and attention over R(t) = S_b(t-1) through
+ * the block cache (R(0) = S_b(0) after a synchronous fill), and enqueues
+ * the delta for step t+1 on copy_stream. ctx_len (device) and ctx_len_host
+ * hold the same lengths, one more than at the previous step. tok_idx, out
+ * and lse are as for hsab_decode_step; ws is a workspace of
+ * hsab_workspace_bytes. stats is nullable. */
+int hsab_offload_step(hsab_offload_engine* engine, const uint16_t* q, const uint16_t* k_new,
+                      const uint16_t* v_new, uint16_t* host_pool, uint16_t* cache, uint16_t* meta,
+                      uint16_t* klabel, const int32_t* label_ch, const int32_t* ctx_len,
+                      const int32_t* ctx_len_host, int32_t* slot_of, int32_t* tok_idx, float* out, float* lse,
+                      void* ws, size_t ws_bytes, hipStream_t compute_stream, hipStream_t copy_stream,
+                      hsab_offload_stats* stats);
+
+/* GPU times (ms) of a step among the last four, waiting for them: ms[0]
+ * compute stream span, ms[1] copy span, ms[2] and ms[3] copy start and
+ * end relative to the step's compute start. */
+int hsab_offload_timing(hsab_offload_engine* engine, int64_t step, float* ms);
+
+/* Host copy of the last step's S_b [B][Hkv][K_b] (ascending, -1 padded). */
+int hsab_offload_selection(const hsab_offload_engine* engine, int32_t* blk_idx_host);
 
 #ifdef __cplusplus
 }
