@@ -160,6 +160,191 @@ def cpu_baseline(w, host, budget_s=10.0, n_units=4):
                       f"the {w.name} step ({done * G} queries), fp64 NumPy, metadata prebuilt, {spent:.1f}s"}
 
 
+PCIE_PEAK_GBS = 64.0   # PCIe 5.0 x16, one direction
+
+
+def offload_bench(args):
+    """The multi-step offload run: 16 decode steps with drifting queries;
+    the full cache sits in a pinned host pool, the GPU holds metadata,
+    label rows and a block cache. One JSON line with the step rate over
+    the steady steps (1..15), the delta bytes per step, the copy time and
+    how much of it the compute stream did not wait for (overlap), next to
+    the same 16 steps on an HBM-resident cache."""
+    w = W.WORKLOADS[args.workload]
+    steps = W.OFFLOAD_STEPS
+    d = dims_of(w)
+    U, B, Hkv, bs = w.units, w.batch, w.n_kv_heads, w.block
+    nb_cap, be = d.nb_cap, H.block_elems(d)
+    n_slots = 2 * w.k_blocks + 2
+    prefill = W.offload_prefill(w, steps)
+    t0 = time.time()
+    q0 = W.queries(w)
+    pool = torch.zeros(U * nb_cap * be, dtype=torch.int16, pin_memory=True)
+    pv = pool.numpy().view(np.uint16).reshape(U, nb_cap, be)
+    Kd = torch.zeros(U * w.max_ctx * w.d_k, dtype=torch.int16, device="cuda")
+    Vd = torch.zeros(U * w.max_ctx * w.d_v, dtype=torch.int16, device="cuda")
+    Kv, Vv = Kd.view(U, w.max_ctx, w.d_k), Vd.view(U, w.max_ctx, w.d_v)
+
+    def fill(u):
+        b, g = divmod(u, Hkv)
+        n = int(prefill[b])
+        kb, vb = W.unit_kv(w, b, g, q0, n)
+        nbk = -(-n // bs)
+        for src, lo, width in ((kb, 0, w.d_k), (vb, bs * w.d_k, w.d_v)):
+            pad = np.zeros((nbk * bs, width), np.uint16)
+            pad[:n] = src
+            pv[u, :nbk, lo:lo + bs * width] = pad.reshape(nbk, bs * width)
+        return u, kb, vb
+
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(max_workers=args.threads) as ex:
+        for u, kb, vb in ex.map(fill, range(U)):
+            n = kb.shape[0]
+            Kv[u, :n] = torch.from_numpy(kb.view(np.int16))
+            Vv[u, :n] = torch.from_numpy(vb.view(np.int16))
+    label = torch.from_numpy(W.label_channels(w)).cuda()
+    meta0 = torch.zeros(U * nb_cap * 2 * w.d_k, dtype=torch.int16, device="cuda")
+    klabel0 = torch.zeros(U * w.max_ctx * w.r, dtype=torch.int16, device="cuda")
+    H.build_meta(d, Kd, torch.from_numpy(prefill).cuda(), label, meta0, klabel0)
+    qs = [q0]
+    for t in range(1, steps):
+        qs.append(W.f32_to_bf16_bits(W.drift_queries(W.bf16_bits_to_f32(qs[-1]), w, t)))
+    dev16 = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
+    q_d = [dev16(q) for q in qs]
+    news = [W.new_token(w, t) for t in range(steps)]
+    kn_d = [dev16(k) for k, _ in news]
+    vn_d = [dev16(v) for _, v in news]
+    ctx_h = [torch.from_numpy(prefill + t + 1) for t in range(steps)]
+    ctx_d = [c.cuda() for c in ctx_h]
+    torch.cuda.synchronize()
+    log(f"[bench] offload run: prefill {prefill.tolist()}, pool {pool.numel() * 2 / 1e9:.2f} GB pinned, "
+        f"staged in {time.time() - t0:.1f}s")
+
+    meta, klabel = meta0.clone(), klabel0.clone()
+    cache = torch.zeros(U * n_slots * be, dtype=torch.int16, device="cuda")
+    slot_of = torch.full((U * nb_cap,), -1, dtype=torch.int32, device="cuda")
+    tok = torch.empty(U * w.k_tokens, dtype=torch.int32, device="cuda")
+    out = torch.empty(B * w.n_q_heads * w.d_v, device="cuda")
+    lse = torch.empty(B * w.n_q_heads, device="cuda")
+    ws = H.alloc_workspace(d)
+    cs, xs = torch.cuda.Stream(), torch.cuda.Stream()
+    full_bytes = U * w.k_blocks * be * 2
+
+    def timed_runs(copy_mode):
+        eng = H.OffloadEngine(d, n_slots, copy_mode)
+        runs = []
+        for run in range(args.offload_runs + 1):   # run 0 warms up
+            meta.copy_(meta0)
+            klabel.copy_(klabel0)
+            torch.cuda.synchronize()
+            eng.begin(torch.from_numpy(prefill.copy()), pool, cache, slot_of, stream=cs)
+            stats = []
+            t_start = time.perf_counter()
+            for t in range(steps):
+                if t == 1:
+                    torch.cuda.synchronize()
+                    t_steady = time.perf_counter()
+                stats.append(eng.step(q_d[t], kn_d[t], vn_d[t], pool, cache, meta, klabel, label, ctx_d[t],
+                                      ctx_h[t], slot_of, tok, out, lse, ws, compute_stream=cs,
+                                      copy_stream=xs).as_dict())
+            torch.cuda.synchronize()
+            t_end = time.perf_counter()
+            tim = [eng.timing(t) for t in range(steps)]
+            runs.append({"cold_s": t_steady - t_start, "steady_s": t_end - t_steady, "stats": stats, "tim": tim})
+        eng.close()
+        runs = runs[1:]
+        best = min(runs, key=lambda r: r["steady_s"])
+        ms_step = best["steady_s"] * 1e3 / (steps - 1)
+        st, tim = best["stats"], best["tim"]
+        delta = np.array([x["delta_bytes"] for x in st[1:]], np.float64)
+        copy_ms = np.array([x["copy_ms"] for x in tim[1:]], np.float64)
+        # the compute stream of step t+1 waits for step t's copies; what it
+        # did not wait is hidden behind compute
+        waits = np.array([x["copy_wait_ms"] for x in tim[2:]], np.float64)
+        hidden = 1.0 - waits.sum() / max(copy_ms[:-1].sum(), 1e-9)
+        link_gbs = delta.sum() / max(copy_ms.sum() * 1e-3, 1e-12) / 1e9
+        return ms_step, {
+            "copy_mode": "gather_kernel" if copy_mode == H.COPY_KERNEL else "dma_memcpy",
+            "ms_per_step": round(ms_step, 6), "runs": len(runs),
+            "cold_ms": round(best["cold_s"] * 1e3, 3), "cold_bytes": st[0]["cold_bytes"],
+            "delta_bytes_per_step": delta.tolist(), "delta_bytes_mean": float(delta.mean()),
+            "full_set_bytes_per_step": full_bytes,
+            "delta_frac_of_full": round(float(delta.mean()) / full_bytes, 4),
+            "copies_mean": float(np.mean([x["n_copies"] for x in st[1:]])),
+            "copy_ms_mean": round(float(copy_ms.mean()), 4), "copy_wait_ms_mean": round(float(waits.mean()), 4),
+            "overlap_hidden_frac": round(float(hidden), 4),
+            "link": {"achieved": round(link_gbs, 2), "peak": PCIE_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(link_gbs / PCIE_PEAK_GBS, 4)},
+            "compute_ms_mean": round(float(np.mean([x["compute_ms"] for x in tim[1:]])), 4),
+            "host_wait_ms_mean": round(float(np.mean([x["host_wait_ms"] for x in st[1:]])), 4),
+            "host_plan_ms_mean": round(float(np.mean([x["host_plan_ms"] for x in st[1:]])), 4),
+        }
+
+    ms_step, off_k = timed_runs(H.COPY_KERNEL)
+    _, off_d = timed_runs(H.COPY_DMA)
+
+    # the same 16 steps on an HBM-resident cache (no offload), for reference
+    meta.copy_(meta0)
+    klabel.copy_(klabel0)
+    blk = torch.empty(U * w.k_blocks, dtype=torch.int32, device="cuda")
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    with torch.cuda.stream(cs):
+        for t in range(steps):
+            if t == 1:
+                evs[0].record(cs)
+            H.decode_step(d, q_d[t], kn_d[t], vn_d[t], Kd, Vd, meta, klabel, label, ctx_d[t], blk, tok, out,
+                          lse, ws, stream=cs)
+        evs[1].record(cs)
+    torch.cuda.synchronize()
+    resident_ms = evs[0].elapsed_time(evs[1]) / (steps - 1)
+
+    queries = B * w.n_q_heads
+    res = {
+        "metric": "offload decode queries/s (batch×heads), 16-step drifting run, 8k-96k ctx",
+        "value": round(queries / (ms_step * 1e-3), 1), "unit": "queries/s", "n_gpus": 1,
+        "steps": steps - 1, "warmup": 1, "ms_per_step": round(ms_step, 6), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "batch": B, "q_heads": w.n_q_heads, "kv_heads": Hkv, "d_k": w.d_k,
+                   "prefill": prefill.tolist(), "block": bs, "k_blocks": w.k_blocks, "r": w.r,
+                   "k_tokens": w.k_tokens, "n_slots": n_slots, "parallelism": "none (1 GPU)"},
+        "resident_ms_per_step": round(resident_ms, 6),
+        "offload": off_k,
+        "offload_dma": off_d,
+    }
+    if not args.no_cpu:
+        log("[bench] timing the CPU oracle on a bounded sample")
+        res["cpu_baseline"] = offload_cpu_baseline(w, prefill, qs, news, Kv, Vv)
+    print(json.dumps(res), flush=True)
+
+
+def offload_cpu_baseline(w, prefill, qs, news, Kv, Vv, budget_s=10.0):
+    """The oracle's offload_run on unit (0, 0) over the 16 steps, repeated
+    for about budget_s seconds (one thread)."""
+    import oracle as O
+    from threadpoolctl import threadpool_limits
+
+    G, n0, steps = w.group, int(prefill[0]), len(qs)
+    K = Kv[0, : n0 + steps].cpu().numpy().view(np.uint16).copy()
+    V = Vv[0, : n0 + steps].cpu().numpy().view(np.uint16).copy()
+    for t, (kn, vn) in enumerate(news):
+        K[n0 + t], V[n0 + t] = kn[0, 0], vn[0, 0]
+    Kf, Vf = O.bf16_to_f64(K), O.bf16_to_f64(V)
+    lab = W.label_channels(w)[0]
+    seq = [(O.bf16_to_f64(qs[t][0, :G]), Kf, Vf, n0 + t + 1, w.k_blocks, lab, w.k_tokens, w.sm_scale)
+           for t in range(steps)]
+    with threadpool_limits(limits=1):
+        done, spent = 0, 0.0
+        while spent < budget_s:
+            t0 = time.perf_counter()
+            O.offload_run(seq, w.block, w.d_k, w.d_v)
+            spent += time.perf_counter() - t0
+            done += 1
+    return {"value": done * steps * G / spent, "unit": "queries/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} x offload_run of unit (0,0) (prefill {n0}) over {steps} steps "
+                      f"({done * steps * G} queries), fp64 NumPy, {spent:.1f}s"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -170,6 +355,7 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of graph replay")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--threads", type=int, default=16)
+    ap.add_argument("--offload-runs", type=int, default=3, help="timed 16-step runs of the offload workload")
     ap.add_argument("--score-only", type=int, default=0,
                     help="only launch the block-score kernel this many times (for counter runs)")
     args = ap.parse_args()
@@ -181,6 +367,9 @@ def main():
 
     w = W.WORKLOADS[args.workload]
     torch.cuda.set_device(0)
+    if w.name == "offload96k":
+        offload_bench(args)
+        return
     d, base, host = stage(w, args.threads)
     sb = step_bytes(w)
     R = args.replicas or max(4, math.ceil(768e6 / sb["total"]))

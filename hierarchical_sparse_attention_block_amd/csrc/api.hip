@@ -212,29 +212,35 @@ int hsab_offload_plan(const hsab_dims* dims, int32_t n_slots, const int32_t* res
     return offload_plan(s, n_slots, resident, selected, tail, slot_map, plan, delta_bytes);
 }
 
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
 int hsab_offload_copy(const hsab_dims* dims, int32_t n_slots, const uint16_t* host_pool, uint16_t* cache,
-                      const int32_t* plan, int32_t* plan_dev, int32_t* slot_of, hipStream_t copy_stream,
-                      hipEvent_t done, int32_t* n_copies) {
+                      const int32_t* plan, int32_t* plan_dev, int32_t* slot_of, int32_t copy_mode,
+                      hipStream_t copy_stream, hipEvent_t done, int32_t* n_copies) {
     int rc = check_dims(dims);
     if (rc) return rc;
     const Shape s = make_shape(*dims);
     if (n_slots < 2 * s.kb + 2) return HSAB_EINVAL;
     if (!host_pool || !cache || !plan || !plan_dev || !slot_of) return HSAB_EINVAL;
+    if (copy_mode != HSAB_OFFLOAD_COPY_KERNEL && copy_mode != HSAB_OFFLOAD_COPY_DMA) return HSAB_EINVAL;
+    if (!aligned16(host_pool) || !aligned16(cache)) return HSAB_EINVAL;
     int calls = 0;
-    rc = hip_status(offload_copy(s, n_slots, host_pool, cache, plan, plan_dev, slot_of, copy_stream, done, &calls));
+    rc = hip_status(offload_copy(s, n_slots, host_pool, cache, plan, plan_dev, slot_of, copy_stream, done, &calls,
+                                 copy_mode));
     if (n_copies) *n_copies = calls;
     return rc;
 }
 
-int hsab_offload_create(const hsab_dims* dims, int32_t n_slots, hsab_offload_engine** engine) {
+int hsab_offload_create(const hsab_dims* dims, int32_t n_slots, int32_t copy_mode, hsab_offload_engine** engine) {
     int rc = check_dims(dims);
     if (rc) return rc;
     if (!engine) return HSAB_EINVAL;
     *engine = nullptr;
     const Shape s = make_shape(*dims);
     if (n_slots < 2 * s.kb + 2) return HSAB_EINVAL;
+    if (copy_mode != HSAB_OFFLOAD_COPY_KERNEL && copy_mode != HSAB_OFFLOAD_COPY_DMA) return HSAB_EINVAL;
     if (!attend_supported(s)) return HSAB_EUNSUPPORTED;
-    return hip_status(offload_create(s, n_slots, engine));
+    return hip_status(offload_create(s, n_slots, copy_mode, engine));
 }
 
 void hsab_offload_destroy(hsab_offload_engine* engine) { offload_destroy(engine); }
@@ -242,6 +248,7 @@ void hsab_offload_destroy(hsab_offload_engine* engine) { offload_destroy(engine)
 int hsab_offload_begin(hsab_offload_engine* engine, const int32_t* n_prefill, const uint16_t* host_pool,
                        uint16_t* cache, int32_t* slot_of, hipStream_t stream) {
     if (!engine || !n_prefill || !host_pool || !cache || !slot_of) return HSAB_EINVAL;
+    if (!aligned16(host_pool) || !aligned16(cache)) return HSAB_EINVAL;
     const Shape& s = offload_shape(engine);
     for (int b = 0; b < s.B; ++b)
         if (n_prefill[b] < 0 || n_prefill[b] >= s.max_ctx) return HSAB_EINVAL;
@@ -260,6 +267,7 @@ int hsab_offload_step(hsab_offload_engine* engine, const uint16_t* q, const uint
         !slot_of || !tok_idx || !out || !lse)
         return HSAB_EINVAL;
     if (!s.valias && !v_new) return HSAB_EINVAL;
+    if (!aligned16(host_pool) || !aligned16(cache)) return HSAB_EINVAL;
     if (!ws || ws_bytes < ws_layout(s).total) return HSAB_EINVAL;
     int einval = 0;
     const int rc = hip_status(offload_step(engine, q, k_new, v_new, host_pool, cache, meta, klabel, label_ch,
@@ -269,7 +277,7 @@ int hsab_offload_step(hsab_offload_engine* engine, const uint16_t* q, const uint
 }
 
 int hsab_offload_timing(hsab_offload_engine* engine, int64_t step, float* ms) {
-    if (!engine || !ms || step < 0 || step >= offload_steps(engine) || step < offload_steps(engine) - 4)
+    if (!engine || !ms || step < 0 || step >= offload_steps(engine) || step < offload_steps(engine) - TIMING_RING)
         return HSAB_EINVAL;
     return hip_status(offload_timing(engine, step, ms));
 }

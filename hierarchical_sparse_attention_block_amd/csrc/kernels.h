@@ -52,16 +52,19 @@ hipError_t launch_attend(const Shape& s, const uint16_t* q, const uint16_t* K, c
                          float* part_ml, float* part_acc, int32_t* arrivals, float* out, float* lse,
                          hipStream_t st);
 
-// offload engine (offload.hip)
+// offload engine (offload.hip); per-step timing events kept for this many steps
+constexpr int TIMING_RING = 32;
 hipError_t launch_append_slot(const Shape& s, int n_slots, const uint16_t* k_new, const uint16_t* v_new,
                               uint16_t* cache, uint16_t* meta, uint16_t* klabel, const int32_t* label_ch,
                               const int32_t* ctx_len, hipStream_t st);
 int offload_plan(const Shape& s, int n_slots, const int32_t* resident, const int32_t* selected,
                  const int32_t* tail, int32_t* slot_map, int32_t* plan, int64_t* delta_bytes);
+constexpr int OFFLOAD_COPY_KERNEL = HSAB_OFFLOAD_COPY_KERNEL;
+constexpr int OFFLOAD_COPY_DMA = HSAB_OFFLOAD_COPY_DMA;
 hipError_t offload_copy(const Shape& s, int n_slots, const uint16_t* host_pool, uint16_t* cache,
                         const int32_t* plan, int32_t* plan_dev, int32_t* slot_of, hipStream_t cs,
-                        hipEvent_t done, int* n_copies);
-hipError_t offload_create(const Shape& s, int n_slots, hsab_offload_engine** out);
+                        hipEvent_t done, int* n_copies, int mode);
+hipError_t offload_create(const Shape& s, int n_slots, int copy_mode, hsab_offload_engine** out);
 void offload_destroy(hsab_offload_engine* e);
 hipError_t offload_begin(hsab_offload_engine* e, const int32_t* n_prefill, const uint16_t* host_pool,
                          uint16_t* cache, int32_t* slot_of, hipStream_t st);

@@ -75,6 +75,38 @@ __global__ __launch_bounds__(256) void slot_patch_kernel(const int32_t* __restri
     }
 }
 
+// grid: (U * K_b), one workgroup per plan entry. Patches slot_of and, for
+// an entry to be copied, pulls the block from the pinned host pool (mapped
+// into the GPU's address space) into its cache slot: 16-byte loads, four
+// per lane in flight, so a few hundred blocks keep many PCIe reads
+// outstanding at once.
+__global__ __launch_bounds__(256) void gather_kernel(const int32_t* __restrict__ plan,
+                                                     const uint16_t* __restrict__ pool, uint16_t* __restrict__ cache,
+                                                     int32_t* __restrict__ slot_of, int kb, int nb_cap, int n_slots,
+                                                     int blk_elems) {
+    const int e = blockIdx.x, unit = e / kb;
+    const int blk = plan[(size_t)e * 3], slot = plan[(size_t)e * 3 + 1], cp = plan[(size_t)e * 3 + 2];
+    if (blk < 0 || blk >= nb_cap || slot < 0 || slot >= n_slots) return;
+    if (threadIdx.x == 0) slot_of[(size_t)unit * nb_cap + blk] = slot;
+    if (!cp) return;
+    const uint4* src = reinterpret_cast<const uint4*>(pool + ((size_t)unit * nb_cap + blk) * blk_elems);
+    uint4* dst = reinterpret_cast<uint4*>(cache + ((size_t)unit * n_slots + slot) * blk_elems);
+    const int n16 = blk_elems / 8;
+    for (int base = 0; base < n16; base += 4 * 256) {
+        uint4 v[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int i = base + k * 256 + (int)threadIdx.x;
+            if (i < n16) v[k] = src[i];
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int i = base + k * 256 + (int)threadIdx.x;
+            if (i < n16) dst[i] = v[k];
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_append_slot(const Shape& s, int n_slots, const uint16_t* k_new, const uint16_t* v_new,
@@ -97,6 +129,7 @@ int offload_plan(const Shape& s, int n_slots, const int32_t* resident, const int
     const int64_t blk_bytes = (int64_t)s.bs * (s.valias ? s.dk : s.dk + s.dv) * 2;
     int64_t bytes = 0;
     std::vector<char> used(n_norm);
+    std::vector<char> is_res(s.nb_cap, 0);   // R of the current unit, cleared after it
     std::vector<int> sel;
     for (int u = 0; u < U; ++u) {
         const int32_t* R = resident + (size_t)u * kb;
@@ -108,32 +141,31 @@ int offload_plan(const Shape& s, int n_slots, const int32_t* resident, const int
         for (int i = 0; i < kb; ++i) {
             const int blk = R[i];
             if (blk < 0 || blk >= s.nb_cap) continue;
+            is_res[blk] = 1;
             const int sl = map[blk];
             if (sl >= 0 && sl < n_norm) used[sl] = 1;
         }
         sel.assign(S, S + kb);
         std::sort(sel.begin(), sel.end());
-        int np = 0, next_free = 0;
+        int np = 0, next_free = 0, rc = HSAB_OK;
         for (int blk : sel) {
             if (blk < 0 || blk >= s.nb_cap) continue;
             int slot;
             int copy = 0;
             if (blk == tl[blk & 1]) {
                 slot = n_slots - 2 + (blk & 1);
+            } else if (is_res[blk] && map[blk] >= 0 && map[blk] < n_norm) {
+                slot = map[blk];
             } else {
-                bool res = false;
-                for (int i = 0; i < kb && !res; ++i) res = R[i] == blk;
-                const int sl = map[blk];
-                if (res && sl >= 0 && sl < n_norm) {
-                    slot = sl;
-                } else {
-                    while (next_free < n_norm && used[next_free]) ++next_free;
-                    if (next_free >= n_norm) return HSAB_EINVAL;   // n_slots too small
-                    slot = next_free;
-                    used[next_free] = 1;
-                    copy = 1;
-                    bytes += blk_bytes;
+                while (next_free < n_norm && used[next_free]) ++next_free;
+                if (next_free >= n_norm) {   // n_slots too small
+                    rc = HSAB_EINVAL;
+                    break;
                 }
+                slot = next_free;
+                used[next_free] = 1;
+                copy = 1;
+                bytes += blk_bytes;
             }
             map[blk] = slot;
             P[3 * np + 0] = blk;
@@ -141,44 +173,70 @@ int offload_plan(const Shape& s, int n_slots, const int32_t* resident, const int
             P[3 * np + 2] = copy;
             ++np;
         }
+        for (int i = 0; i < kb; ++i)
+            if (R[i] >= 0 && R[i] < s.nb_cap) is_res[R[i]] = 0;
+        if (rc != HSAB_OK) return rc;
         for (int i = np; i < kb; ++i) P[3 * i] = P[3 * i + 1] = P[3 * i + 2] = -1;
     }
     if (delta_bytes) *delta_bytes = bytes;
     return HSAB_OK;
 }
 
-// Enqueue the plan's copies (contiguous runs of blocks into contiguous
-// slots become one hipMemcpyAsync each), then the slot-table patch, then
-// record `done` on copy_stream.
+// Enqueue a plan on copy stream cs, then record `done`.
+//  OFFLOAD_COPY_KERNEL: upload the plan, then gather_kernel pulls the
+//    blocks from the mapped pool and patches the slot table in one launch;
+//  OFFLOAD_COPY_DMA: contiguous runs of blocks into contiguous slots
+//    become one hipMemcpyAsync each (DMA engines), then the plan upload
+//    and the slot-table patch.
+// *n_copies: blocks gathered (kernel) or copies issued (DMA).
 hipError_t offload_copy(const Shape& s, int n_slots, const uint16_t* host_pool, uint16_t* cache,
                         const int32_t* plan, int32_t* plan_dev, int32_t* slot_of, hipStream_t cs,
-                        hipEvent_t done, int* n_copies) {
+                        hipEvent_t done, int* n_copies, int mode) {
     const int U = s.B * s.Hkv, kb = s.kb;
     const size_t blk_elems = (size_t)s.bs * (s.valias ? s.dk : s.dk + s.dv);
     int calls = 0;
-    for (int u = 0; u < U; ++u) {
-        const int32_t* P = plan + (size_t)u * kb * 3;
-        int i = 0;
-        while (i < kb && P[3 * i] >= 0) {
-            if (!P[3 * i + 2]) { ++i; continue; }
-            int j = i + 1;
-            while (j < kb && P[3 * j] >= 0 && P[3 * j + 2] && P[3 * j] == P[3 * (j - 1)] + 1 &&
-                   P[3 * j + 1] == P[3 * (j - 1) + 1] + 1)
-                ++j;
-            const int blk = P[3 * i], slot = P[3 * i + 1], run = j - i;
-            hipError_t e = hipMemcpyAsync(cache + ((size_t)u * n_slots + slot) * blk_elems,
-                                          host_pool + ((size_t)u * s.nb_cap + blk) * blk_elems,
-                                          (size_t)run * blk_elems * sizeof(uint16_t), hipMemcpyHostToDevice, cs);
-            if (e != hipSuccess) return e;
-            ++calls;
-            i = j;
+    hipError_t e = hipSuccess;
+    if (mode == OFFLOAD_COPY_KERNEL) {
+        for (int i = 0; i < U * kb; ++i) calls += plan[3 * i] >= 0 && plan[3 * i + 2] > 0;
+        const uint16_t* pool_dev = nullptr;
+        e = hipHostGetDevicePointer((void**)&pool_dev, const_cast<uint16_t*>(host_pool), 0);
+        if (e != hipSuccess) return e;
+        e = hipMemcpyAsync(plan_dev, plan, (size_t)U * kb * 3 * sizeof(int32_t), hipMemcpyHostToDevice, cs);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(gather_kernel, dim3(U * kb), dim3(256), 0, cs, plan_dev, pool_dev, cache, slot_of, kb,
+                           s.nb_cap, n_slots, (int)blk_elems);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    } else {
+        std::vector<void*> dsts, srcs;
+        std::vector<size_t> sizes;
+        for (int u = 0; u < U; ++u) {
+            const int32_t* P = plan + (size_t)u * kb * 3;
+            int i = 0;
+            while (i < kb && P[3 * i] >= 0) {
+                if (!P[3 * i + 2]) { ++i; continue; }
+                int j = i + 1;
+                while (j < kb && P[3 * j] >= 0 && P[3 * j + 2] && P[3 * j] == P[3 * (j - 1)] + 1 &&
+                       P[3 * j + 1] == P[3 * (j - 1) + 1] + 1)
+                    ++j;
+                const int blk = P[3 * i], slot = P[3 * i + 1], run = j - i;
+                dsts.push_back(cache + ((size_t)u * n_slots + slot) * blk_elems);
+                srcs.push_back(const_cast<uint16_t*>(host_pool) + ((size_t)u * s.nb_cap + blk) * blk_elems);
+                sizes.push_back((size_t)run * blk_elems * sizeof(uint16_t));
+                i = j;
+            }
         }
+        calls = (int)dsts.size();
+        for (int c = 0; c < calls; ++c) {
+            e = hipMemcpyAsync(dsts[c], srcs[c], sizes[c], hipMemcpyHostToDevice, cs);
+            if (e != hipSuccess) return e;
+        }
+        e = hipMemcpyAsync(plan_dev, plan, (size_t)U * kb * 3 * sizeof(int32_t), hipMemcpyHostToDevice, cs);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(slot_patch_kernel, dim3(U), dim3(256), 0, cs, plan_dev, slot_of, kb, s.nb_cap);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
     }
-    hipError_t e = hipMemcpyAsync(plan_dev, plan, (size_t)U * kb * 3 * sizeof(int32_t), hipMemcpyHostToDevice, cs);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(slot_patch_kernel, dim3(U), dim3(256), 0, cs, plan_dev, slot_of, kb, s.nb_cap);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
     if (n_copies) *n_copies = calls;
     return done ? hipEventRecord(done, cs) : hipSuccess;
 }
@@ -199,7 +257,7 @@ static void tail_blocks(int n, int jp, int bs, int32_t out[2]) {
 // Engine state; every buffer here is allocated by offload_create.
 struct hsab_offload_engine {
     hsab::Shape s;
-    int n_slots = 0, U = 0;
+    int n_slots = 0, U = 0, copy_mode = 0;
     size_t blk_elems = 0;
     int64_t step = -1;                        // next step index; -1 before offload_begin
     std::vector<int32_t> n_ctx, jp;           // [B] tokens so far, last prefill block
@@ -211,7 +269,9 @@ struct hsab_offload_engine {
     int32_t* sel_d[2] = {nullptr, nullptr};   // device [U][K_b]
     int32_t* plan_d[2] = {nullptr, nullptr};  // device [U][K_b][3]
     hipEvent_t ev_sel = nullptr, ev_copy[2] = {nullptr, nullptr};
-    hipEvent_t tm[4][4] = {};                 // per step % 4: compute begin/end, copy begin/end
+    // per step % TIMING_RING: compute begin, compute end, copy begin, copy
+    // end, and the compute stream before and after its wait for the copies
+    hipEvent_t tm[hsab::TIMING_RING][6] = {};
 };
 
 namespace hsab {
@@ -233,10 +293,11 @@ void offload_destroy(hsab_offload_engine* e) {
     delete e;
 }
 
-hipError_t offload_create(const Shape& s, int n_slots, hsab_offload_engine** out) {
+hipError_t offload_create(const Shape& s, int n_slots, int copy_mode, hsab_offload_engine** out) {
     auto* e = new hsab_offload_engine();
     e->s = s;
     e->n_slots = n_slots;
+    e->copy_mode = copy_mode;
     e->U = s.B * s.Hkv;
     e->blk_elems = (size_t)s.bs * (s.valias ? s.dk : s.dk + s.dv);
     const size_t nsel = (size_t)e->U * s.kb;
@@ -331,7 +392,7 @@ hipError_t offload_step(hsab_offload_engine* e, const uint16_t* q, const uint16_
     float* blk_score = reinterpret_cast<float*>(w + L.blk_score);
     float* part_ml = reinterpret_cast<float*>(w + L.part_ml);
     float* part_acc = reinterpret_cast<float*>(w + L.part_acc);
-    hipEvent_t* tm = e->tm[e->step & 3];
+    hipEvent_t* tm = e->tm[e->step % TIMING_RING];
     int32_t* sel_now = e->sel_d[t & 1];
     const int32_t* resident = e->step == 0 ? sel_now : e->sel_d[(t - 1) & 1];
 
@@ -350,7 +411,9 @@ hipError_t offload_step(hsab_offload_engine* e, const uint16_t* q, const uint16_
     HSAB_TRY(launch_select(s, 2, q, nullptr, klabel, label_ch, ctx_len, const_cast<int32_t*>(resident), tok_idx,
                            nullptr, nullptr, cs));
     if (e->step > 0) {
+        HSAB_TRY(hipEventRecord(tm[4], cs));
         HSAB_TRY(hipStreamWaitEvent(cs, e->ev_copy[(t - 1) & 1], 0));
+        HSAB_TRY(hipEventRecord(tm[5], cs));
         HSAB_TRY(launch_attend(s, q, cache, cache, tok_idx, slot_of, e->n_slots, part_ml, part_acc, nullptr, out,
                                lse, cs));
         HSAB_TRY(hipEventRecord(tm[1], cs));
@@ -381,9 +444,11 @@ hipError_t offload_step(hsab_offload_engine* e, const uint16_t* q, const uint16_
             return hipSuccess;
         }
         HSAB_TRY(offload_copy(s, e->n_slots, host_pool, cache, e->plan_h[1], e->plan_d[1], slot_of, xs,
-                              e->ev_copy[1], &calls));
+                              e->ev_copy[1], &calls, e->copy_mode));
         copies += calls;
+        HSAB_TRY(hipEventRecord(tm[4], cs));
         HSAB_TRY(hipStreamWaitEvent(cs, e->ev_copy[1], 0));
+        HSAB_TRY(hipEventRecord(tm[5], cs));
         HSAB_TRY(launch_attend(s, q, cache, cache, tok_idx, slot_of, e->n_slots, part_ml, part_acc, nullptr, out,
                                lse, cs));
         HSAB_TRY(hipEventRecord(tm[1], cs));
@@ -397,7 +462,7 @@ hipError_t offload_step(hsab_offload_engine* e, const uint16_t* q, const uint16_
     }
     HSAB_TRY(hipEventRecord(tm[2], xs));
     HSAB_TRY(offload_copy(s, e->n_slots, host_pool, cache, e->plan_h[t & 1], e->plan_d[t & 1], slot_of, xs,
-                          e->ev_copy[t & 1], &calls));
+                          e->ev_copy[t & 1], &calls, e->copy_mode));
     copies += calls;
     HSAB_TRY(hipEventRecord(tm[3], xs));
     const auto t2 = clk::now();
@@ -416,17 +481,17 @@ hipError_t offload_step(hsab_offload_engine* e, const uint16_t* q, const uint16_
     return hipSuccess;
 }
 
-// GPU times of a finished step (within the last four): compute stream
-// span, copy span, and the copy's start and end relative to the step's
-// compute start. Waits for that step's events.
-hipError_t offload_timing(hsab_offload_engine* e, int64_t step, float* ms4) {
-    hipEvent_t* tm = e->tm[step & 3];
+// GPU times of a finished step (within the last four), see
+// hsab_offload_timing. Waits for that step's events.
+hipError_t offload_timing(hsab_offload_engine* e, int64_t step, float* ms) {
+    hipEvent_t* tm = e->tm[step % TIMING_RING];
     HSAB_TRY(hipEventSynchronize(tm[3]));
     HSAB_TRY(hipEventSynchronize(tm[1]));
-    HSAB_TRY(hipEventElapsedTime(&ms4[0], tm[0], tm[1]));
-    HSAB_TRY(hipEventElapsedTime(&ms4[1], tm[2], tm[3]));
-    HSAB_TRY(hipEventElapsedTime(&ms4[2], tm[0], tm[2]));
-    HSAB_TRY(hipEventElapsedTime(&ms4[3], tm[0], tm[3]));
+    HSAB_TRY(hipEventElapsedTime(&ms[0], tm[0], tm[1]));
+    HSAB_TRY(hipEventElapsedTime(&ms[1], tm[2], tm[3]));
+    HSAB_TRY(hipEventElapsedTime(&ms[2], tm[0], tm[2]));
+    HSAB_TRY(hipEventElapsedTime(&ms[3], tm[0], tm[3]));
+    HSAB_TRY(hipEventElapsedTime(&ms[4], tm[4], tm[5]));
     return hipSuccess;
 }
 

@@ -21,6 +21,7 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 HSAB_OK, HSAB_EINVAL, HSAB_EHIP, HSAB_EUNSUPPORTED = 0, -1, -2, -3
+COPY_KERNEL, COPY_DMA = 0, 1   # HSAB_OFFLOAD_COPY_*
 EXPORTS = ("hsab_workspace_bytes", "hsab_status_string", "hsab_last_hip_error", "hsab_build_meta",
            "hsab_score_blocks", "hsab_select_blocks", "hsab_select_tokens", "hsab_sparse_attend",
            "hsab_decode_step", "hsab_offload_append", "hsab_offload_plan", "hsab_offload_copy", "hsab_offload_create",
@@ -69,7 +70,7 @@ _lib.hsab_decode_step.argtypes = [_D, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _v
                                   _vp, _sz, _vp]
 _lib.hsab_offload_append.argtypes = [_D, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
 _lib.hsab_offload_plan.argtypes = [_D, _i32, _vp, _vp, _vp, _vp, _vp, _vp]
-_lib.hsab_offload_copy.argtypes = [_D, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+_lib.hsab_offload_copy.argtypes = [_D, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp]
 
 
 class OffloadStats(ctypes.Structure):
@@ -81,7 +82,7 @@ class OffloadStats(ctypes.Structure):
         return {n: getattr(self, n) for n, _ in self._fields_}
 
 
-_lib.hsab_offload_create.argtypes = [_D, _i32, ctypes.POINTER(_vp)]
+_lib.hsab_offload_create.argtypes = [_D, _i32, _i32, ctypes.POINTER(_vp)]
 _lib.hsab_offload_destroy.argtypes = [_vp]
 _lib.hsab_offload_begin.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp]
 _lib.hsab_offload_step.argtypes = [_vp] * 16 + [_sz, _vp, _vp, ctypes.POINTER(OffloadStats)]
@@ -289,10 +290,12 @@ def offload_plan(d: Dims, n_slots, resident, selected, tail, slot_map, plan) -> 
     return int(nb.value)
 
 
-def offload_copy(d: Dims, n_slots, host_pool, cache, plan, plan_dev, slot_of, copy_stream, done=None) -> int:
-    """Enqueue a plan's copies on copy_stream; returns the memcpy count.
-    host_pool and plan are pinned host tensors; done is a torch.cuda.Event
-    (recorded on copy_stream) or None."""
+def offload_copy(d: Dims, n_slots, host_pool, cache, plan, plan_dev, slot_of, copy_stream, done=None,
+                 copy_mode=COPY_KERNEL) -> int:
+    """Enqueue a plan's copies on copy_stream; returns the blocks gathered
+    (kernel mode) or copies issued (DMA mode). host_pool and plan are
+    pinned host tensors; done is a torch.cuda.Event (recorded on
+    copy_stream) or None."""
     U = d.batch * d.n_kv_heads
     nc = ctypes.c_int32(0)
     ev = None
@@ -304,7 +307,7 @@ def offload_copy(d: Dims, n_slots, host_pool, cache, plan, plan_dev, slot_of, co
         _buf("cache", cache, _u16, U * n_slots * block_elems(d)),
         _hbuf("plan", plan, _i, U * d.k_blocks * 3, pinned=True),
         _buf("plan_dev", plan_dev, _i, U * d.k_blocks * 3), _buf("slot_of", slot_of, _i, U * d.nb_cap),
-        _stream(copy_stream), ev, ctypes.byref(nc)))
+        ctypes.c_int32(copy_mode), _stream(copy_stream), ev, ctypes.byref(nc)))
     return int(nc.value)
 
 
@@ -312,11 +315,11 @@ class OffloadEngine:
     """Handle of a native offload engine (hsab_offload_create). The caller
     owns the pool (pinned host), the block cache, metadata and outputs."""
 
-    def __init__(self, d: Dims, n_slots: int):
-        self.d, self.n_slots = d, int(n_slots)
+    def __init__(self, d: Dims, n_slots: int, copy_mode: int = COPY_KERNEL):
+        self.d, self.n_slots, self.copy_mode = d, int(n_slots), int(copy_mode)
         h = ctypes.c_void_p()
         _check("hsab_offload_create", _lib.hsab_offload_create(ctypes.byref(d), ctypes.c_int32(n_slots),
-                                                               ctypes.byref(h)))
+                                                               ctypes.c_int32(copy_mode), ctypes.byref(h)))
         self._h = h
 
     def close(self):
@@ -361,9 +364,10 @@ class OffloadEngine:
         return st
 
     def timing(self, step):
-        ms = (ctypes.c_float * 4)()
+        ms = (ctypes.c_float * 5)()
         _check("hsab_offload_timing", _lib.hsab_offload_timing(self._h, ctypes.c_int64(step), ms))
-        return {"compute_ms": ms[0], "copy_ms": ms[1], "copy_start_ms": ms[2], "copy_end_ms": ms[3]}
+        return {"compute_ms": ms[0], "copy_ms": ms[1], "copy_start_ms": ms[2], "copy_end_ms": ms[3],
+                "copy_wait_ms": ms[4]}
 
     def selection(self) -> torch.Tensor:
         d = self.d

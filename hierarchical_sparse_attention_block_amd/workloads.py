@@ -20,6 +20,10 @@ context, see the AsyncTLS abstract and the German explainer, section 4):
 * ``mla64k``  - B=8, 32 query heads sharing one 576-dim latent key
   (512 latent + 64 rope), values = first 512 key dims, n=65536, block 32,
   K_b=128, r=32, K_t=1024, scaled keys as above, no planted keys.
+* ``offload96k`` - the offload run: B=4, 32/8 heads, d=128, per-row prefill
+  lengths uniform in 8k-96k, 16 decode steps whose queries drift as
+  q_t = sqrt(d) * normalize(q_{t-1} + 0.1 N(0,1)); layer settings as gqa48k
+  (block 16, K_b=128, r=16, K_t=512, scaled keys), no planted keys.
 
 Random streams are keyed by ``SeedSequence([seed, stream, ...])`` so each
 (batch, KV head) unit can be regenerated on its own; this lets a test
@@ -89,7 +93,22 @@ WORKLOADS = {
                        98304, 98304, True, "top_scale", 64, 3),
     "mla64k": Workload("mla64k", 8, 32, 1, 576, 512, True, 32, 32, 128, 1024,
                        65536, 65536, True, "top_scale", 0, 4),
+    # multi-step offload run; ctx is the capacity, per-row prefill lengths
+    # come from offload_prefill
+    "offload96k": Workload("offload96k", 4, 32, 8, 128, 128, False, 16, 16, 128, 512,
+                           98304, 98304, True, "top_scale", 0, 5),
 }
+
+OFFLOAD_STEPS = 16
+OFFLOAD_CTX_RANGE = (8192, 98304)
+
+
+def offload_prefill(w: Workload, steps: int = OFFLOAD_STEPS) -> np.ndarray:
+    """Prefill length of each batch row of a multi-step offload run, drawn
+    uniformly from [8192, 98304 - steps] so every row has room for the run."""
+    lo, hi = OFFLOAD_CTX_RANGE
+    hi = min(hi, w.max_ctx) - steps
+    return rng(w.seed, _S_CTX).integers(lo, hi + 1, size=w.batch).astype(np.int32)
 
 
 def rng(*key: int) -> np.random.Generator:

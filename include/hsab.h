@@ -218,14 +218,25 @@ int hsab_offload_plan(const hsab_dims* dims, int32_t n_slots, const int32_t* res
                       const int32_t* selected, const int32_t* tail, int32_t* slot_map, int32_t* plan,
                       int64_t* delta_bytes);
 
-/* Enqueue a plan on copy_stream: one hipMemcpyAsync per run of consecutive
- * blocks going to consecutive slots, the upload of the plan (plan must be
- * pinned host memory; plan_dev is device [B][Hkv][K_b][3] int32), a kernel
- * that writes slot_of for every planned block, then `done` (nullable) is
- * recorded. n_copies (nullable) receives the number of memcpy calls. */
+/* How the delta crosses the host link:
+ *   HSAB_OFFLOAD_COPY_KERNEL  a GPU kernel reads the blocks from the pinned
+ *       pool (hipHostMalloc memory, mapped into the GPU address space) and
+ *       writes them to their slots, patching slot_of in the same launch;
+ *   HSAB_OFFLOAD_COPY_DMA     the DMA engines copy each run of consecutive
+ *       blocks into consecutive slots (one hipMemcpyAsync per run), then a
+ *       kernel patches slot_of. */
+#define HSAB_OFFLOAD_COPY_KERNEL 0
+#define HSAB_OFFLOAD_COPY_DMA    1
+
+/* Enqueue a plan on copy_stream: the block copies as copy_mode says, the
+ * upload of the plan (plan must be pinned host memory; plan_dev is device
+ * [B][Hkv][K_b][3] int32), slot_of written for every planned block, then
+ * `done` (nullable) is recorded. host_pool (pinned) and cache must be
+ * 16-byte aligned. n_copies (nullable) receives the blocks gathered
+ * (kernel) or the copies issued (DMA). */
 int hsab_offload_copy(const hsab_dims* dims, int32_t n_slots, const uint16_t* host_pool, uint16_t* cache,
-                      const int32_t* plan, int32_t* plan_dev, int32_t* slot_of, hipStream_t copy_stream,
-                      hipEvent_t done, int32_t* n_copies);
+                      const int32_t* plan, int32_t* plan_dev, int32_t* slot_of, int32_t copy_mode,
+                      hipStream_t copy_stream, hipEvent_t done, int32_t* n_copies);
 
 /* Offload engine object: the lagged schedule above driven step by step.
  * It owns only small buffers (pinned copies of S_b and of the plan, the new
@@ -241,13 +252,14 @@ typedef struct hsab_offload_stats {
     int64_t delta_bytes;   /* host-to-device bytes of the step's delta */
     int64_t cold_bytes;    /* bytes of the synchronous fill of S_b(0); step 0 only */
     int32_t delta_blocks;  /* blocks in the delta */
-    int32_t n_copies;      /* hipMemcpyAsync calls (coalesced runs) */
+    int32_t n_copies;      /* blocks gathered (kernel copy) or copies issued (DMA copy) */
     float host_wait_ms;    /* host wait for S_b(t) */
     float host_plan_ms;    /* pool write, planning and enqueue */
 } hsab_offload_stats;
 
-/* n_slots >= 2*K_b + 2; HSAB_EHIP if an allocation fails. */
-int hsab_offload_create(const hsab_dims* dims, int32_t n_slots, hsab_offload_engine** engine);
+/* n_slots >= 2*K_b + 2; copy_mode is HSAB_OFFLOAD_COPY_KERNEL or _DMA;
+ * HSAB_EHIP if an allocation fails. */
+int hsab_offload_create(const hsab_dims* dims, int32_t n_slots, int32_t copy_mode, hsab_offload_engine** engine);
 void hsab_offload_destroy(hsab_offload_engine* engine);
 
 /* After prefill (host_pool holds n_prefill[b] tokens of every sequence,
@@ -273,9 +285,12 @@ int hsab_offload_step(hsab_offload_engine* engine, const uint16_t* q, const uint
                       void* ws, size_t ws_bytes, hipStream_t compute_stream, hipStream_t copy_stream,
                       hsab_offload_stats* stats);
 
-/* GPU times (ms) of a step among the last four, waiting for them: ms[0]
- * compute stream span, ms[1] copy span, ms[2] and ms[3] copy start and
- * end relative to the step's compute start. */
+/* GPU times (ms) of a step among the last 32, waiting for them (ms has
+ * 5 entries): ms[0] compute stream span of the step, ms[1] span of the
+ * step's copies on the copy stream, ms[2] and ms[3] their start and end
+ * relative to the step's compute start, ms[4] how long the compute stream
+ * waited for the previous step's copies (the cold fill at step 0) before
+ * its attention. */
 int hsab_offload_timing(hsab_offload_engine* engine, int64_t step, float* ms);
 
 /* Host copy of the last step's S_b [B][Hkv][K_b] (ascending, -1 padded). */

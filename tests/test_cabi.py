@@ -58,7 +58,7 @@ def test_bad_dims_rejected(bad):
     assert H.raw_call("hsab_score_blocks", ctypes.byref(d), p, p, p, p, None) == H.HSAB_EINVAL
     assert H.raw_call("hsab_build_meta", ctypes.byref(d), p, p, p, p, p, None) == H.HSAB_EINVAL
     h = ctypes.c_void_p()
-    assert H.raw_call("hsab_offload_create", ctypes.byref(d), 64, ctypes.byref(h)) == H.HSAB_EINVAL
+    assert H.raw_call("hsab_offload_create", ctypes.byref(d), 64, 0, ctypes.byref(h)) == H.HSAB_EINVAL
     assert not h.value
 
 
@@ -75,6 +75,12 @@ def test_null_pointers_rejected():
     assert H.raw_call("hsab_offload_begin", n, p, p, p, p, None) == H.HSAB_EINVAL
     assert H.raw_call("hsab_offload_timing", n, 0, p) == H.HSAB_EINVAL
     assert H.raw_call("hsab_offload_selection", n, p) == H.HSAB_EINVAL
+    # unknown copy mode, misaligned pool
+    assert H.raw_call("hsab_offload_copy", ctypes.byref(d), 18, p, p, p, p, p, 7, None, None, None) == H.HSAB_EINVAL
+    q = ctypes.c_void_p(18)
+    assert H.raw_call("hsab_offload_copy", ctypes.byref(d), 18, q, p, p, p, p, 0, None, None, None) == H.HSAB_EINVAL
+    h = ctypes.c_void_p()
+    assert H.raw_call("hsab_offload_create", ctypes.byref(d), 18, 2, ctypes.byref(h)) == H.HSAB_EINVAL
 
 
 def test_small_workspace_and_unsupported_shape():
@@ -89,9 +95,9 @@ def test_small_workspace_and_unsupported_shape():
     assert H.raw_call("hsab_sparse_attend", ctypes.byref(d96), p, p, p, p, p, None, 0, p, p, p, ws96,
                       None) == H.HSAB_EUNSUPPORTED
     h = ctypes.c_void_p()
-    assert H.raw_call("hsab_offload_create", ctypes.byref(d96), 64, ctypes.byref(h)) == H.HSAB_EUNSUPPORTED
+    assert H.raw_call("hsab_offload_create", ctypes.byref(d96), 64, 0, ctypes.byref(h)) == H.HSAB_EUNSUPPORTED
     # the offload engine needs 2 K_b + 2 slots
-    assert H.raw_call("hsab_offload_create", ctypes.byref(d), 17, ctypes.byref(h)) == H.HSAB_EINVAL
+    assert H.raw_call("hsab_offload_create", ctypes.byref(d), 17, 0, ctypes.byref(h)) == H.HSAB_EINVAL
 
 
 def test_status_strings():

@@ -19,7 +19,7 @@ from hsab_testlib import check_index_set, dims_of, dev16, OUT_ATOL, LSE_RTOL
 pytestmark = pytest.mark.gpu
 
 
-def _run_offload(w, prefill, steps, n_slots=None):
+def _run_offload(w, prefill, steps, n_slots=None, copy_mode=0):
     from hierarchical_sparse_attention_block_amd import hsab as H
     d = dims_of(w)
     U, B, Hkv, G = w.units, w.batch, w.n_kv_heads, w.group
@@ -27,8 +27,8 @@ def _run_offload(w, prefill, steps, n_slots=None):
     n_slots = n_slots or 2 * w.k_blocks + 2
     prefill = np.asarray(prefill, np.int32)
     assert prefill.max() + steps <= w.max_ctx
-    print(f"offload run {w.name} B={B} Hkv={Hkv} G={G} d_k={w.d_k} prefill={prefill.tolist()} steps={steps}",
-          flush=True)
+    print(f"offload run {w.name} B={B} Hkv={Hkv} G={G} d_k={w.d_k} prefill={prefill.tolist()} steps={steps} "
+          f"copy_mode={copy_mode}", flush=True)
 
     # host cache: prefill rows plus one new token per step
     q0 = W.queries(w)
@@ -79,7 +79,7 @@ def _run_offload(w, prefill, steps, n_slots=None):
     lse = torch.full((B * w.n_q_heads,), float("nan"), device="cuda")
     ws = H.alloc_workspace(d)
     copy_stream = torch.cuda.Stream()
-    eng = H.OffloadEngine(d, n_slots)
+    eng = H.OffloadEngine(d, n_slots, copy_mode)
     eng.begin(torch.from_numpy(prefill.copy()), pool, cache, slot_of)
 
     res = []
@@ -153,12 +153,13 @@ def _check_against_oracle(w, prefill, K, V, qs, res):
     return ties
 
 
-def test_offload_gqa_matches_lagged_oracle():
+@pytest.mark.parametrize("copy_mode", [0, 1], ids=["gather_kernel", "dma"])
+def test_offload_gqa_matches_lagged_oracle(copy_mode):
     w = W.WORKLOADS["tiny4k"].replace(name="offload_gqa", batch=2, n_q_heads=8, n_kv_heads=2, k_blocks=8,
                                       k_tokens=64, ctx=1024, max_ctx=1024, scaled_keys=True, n_planted=0,
                                       seed=21)
     prefill = [318, 512]          # one crosses a block boundary mid-run, one starts on one
-    K, V, qs, res = _run_offload(w, prefill, steps=12)
+    K, V, qs, res = _run_offload(w, prefill, steps=12, copy_mode=copy_mode)
     _check_against_oracle(w, np.array(prefill), K, V, qs, res)
     assert sum(r["stats"]["delta_bytes"] for r in res[1:]) > 0, "the queries drift, so some blocks move"
 
@@ -189,5 +190,5 @@ def test_offload_mla_latent_blocks():
     w = W.WORKLOADS["mla64k"].replace(name="offload_mla", batch=1, k_blocks=4, k_tokens=64, ctx=700,
                                       max_ctx=700, seed=23)
     prefill = [640]               # 640 = 20 blocks of 32: the first decode token opens block 20
-    K, V, qs, res = _run_offload(w, prefill, steps=6)
+    K, V, qs, res = _run_offload(w, prefill, steps=6, copy_mode=0)
     _check_against_oracle(w, np.array(prefill), K, V, qs, res)
