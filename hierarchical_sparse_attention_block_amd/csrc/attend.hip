@@ -58,13 +58,14 @@ __global__ __launch_bounds__(256) void attend_gqa_kernel(
     const int32_t* __restrict__ tok_idx, const int32_t* __restrict__ slot_of, int n_slots,
     float* __restrict__ part_ml, float* __restrict__ part_acc, int Hkv, int bs, int kt,
     int max_ctx, int nb_cap, int n_splits, int units, float scale2, int slot_rows) {
-    constexpr int LPT = D / 8;                         // lanes per token
-    constexpr int TPI = 64 / LPT;                      // tokens per wave load
+    constexpr int LPT = D / 8;                         // lanes per token (8 channels each)
+    constexpr int TPI = 64 / LPT;                      // tokens per wave load = lane groups per wave
     constexpr int TPW = ATT_TOK_PER_SPLIT / 4;         // tokens per wave
-    constexpr int IT = TPW / TPI;
+    constexpr int IT = TPW / TPI;                      // tokens per lane group
+    constexpr int NP = 4 * TPI;                        // partial softmax states per workgroup
     static_assert(IT >= 1 && TPW % TPI == 0, "bad D");
-    __shared__ float s_m[4][G], s_l[4][G];
-    __shared__ float s_acc[4][G][D];
+    __shared__ float s_m[NP][G], s_l[NP][G];
+    __shared__ float s_acc[NP][G][D];
 
     const int xcd = blockIdx.x & 7, y = blockIdx.x >> 3;
     const int unit = (y / n_splits) * 8 + xcd, split = y % n_splits;
@@ -82,23 +83,51 @@ __global__ __launch_bounds__(256) void attend_gqa_kernel(
         for (int e = 0; e < 8; ++e) qf[h][e] *= scale2;
     }
 
+    // Three dependent rounds, each with all its loads in flight: token
+    // positions, block slots (block cache only), then the K and V rows.
+    // Loads are unconditional (invalid entries read row 0 and are masked)
+    // so no round waits on a previous one's stragglers.
     uint4 kr[IT], vr[IT];
     bool ok[IT];
+    long rows[IT];
     const int32_t* tl = tok_idx + (size_t)unit * kt;
+    int tv[IT];
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
         const int ti = split * ATT_TOK_PER_SPLIT + wave * TPW + it * TPI + ts;
-        const int t = ti < kt ? tl[ti] : -1;
-        const long row = row_of(t, unit, bs, max_ctx, nb_cap, slot_of, n_slots, slot_rows);
-        ok[it] = row >= 0;
-        if (ok[it]) {
-            kr[it] = ldg16(K + row * D + cc * 8);
-            vr[it] = ldg16(V + row * D + cc * 8);
-        } else {
-            kr[it] = vr[it] = make_uint4(0u, 0u, 0u, 0u);
-        }
+        const int t = tl[ti < kt ? ti : kt - 1];
+        tv[it] = ti < kt ? t : -1;
     }
+    if (slot_of) {
+        int sl[IT];
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const int blk = tv[it] >= 0 ? tv[it] / bs : 0;
+            sl[it] = slot_of[(size_t)unit * nb_cap + (blk < nb_cap ? blk : 0)];
+        }
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const int t = tv[it], blk = t >= 0 ? t / bs : 0;
+            const bool v = t >= 0 && blk < nb_cap && sl[it] >= 0 && sl[it] < n_slots;
+            rows[it] = v ? ((long)unit * n_slots + sl[it]) * slot_rows + (t - blk * bs) : -1;
+        }
+    } else {
+#pragma unroll
+        for (int it = 0; it < IT; ++it)
+            rows[it] = (tv[it] >= 0 && tv[it] < max_ctx) ? (long)unit * max_ctx + tv[it] : -1;
+    }
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+        ok[it] = rows[it] >= 0;
+        const long r = ok[it] ? rows[it] : 0;
+        kr[it] = ldg16(K + r * D + cc * 8);
+        vr[it] = ldg16(V + r * D + cc * 8);
+    }
+    // keep the value loads here, in flight with the key loads; left alone
+    // the scheduler sinks them to their use after the logits
+    __builtin_amdgcn_sched_barrier(0);
 
+    // logits: 8-channel partial dots, summed over the token's lane group
     float z[IT][G];
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
@@ -109,53 +138,39 @@ __global__ __launch_bounds__(256) void attend_gqa_kernel(
             float p = 0.f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) p = fmaf(qf[h][e], kf[e], p);
-#pragma unroll
-            for (int o = LPT / 2; o >= 1; o >>= 1) p += __shfl_xor(p, o);
+            p = group_sum<LPT>(p);
             z[it][h] = ok[it] ? p : -INFINITY;
         }
     }
 
-    float m[G], l[G], acc[G][8];
+    // softmax state of this lane group's IT tokens; the groups of the
+    // workgroup are merged once through LDS, no cross-group shuffles
+    const int slot = wave * TPI + ts;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-        float mm = z[0][h];
+        float m = z[0][h];
 #pragma unroll
-        for (int it = 1; it < IT; ++it) mm = fmaxf(mm, z[it][h]);
+        for (int it = 1; it < IT; ++it) m = fmaxf(m, z[it][h]);
+        float l = 0.f, acc[8];
 #pragma unroll
-        for (int o = LPT; o < 64; o <<= 1) mm = fmaxf(mm, __shfl_xor(mm, o));
-        m[h] = mm;
-        l[h] = 0.f;
+        for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+        if (m != -INFINITY) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
-    }
+            for (int it = 0; it < IT; ++it) {
+                float vf[8];
+                widen8(vr[it], vf);
+                const float p = ok[it] ? exp2f(z[it][h] - m) : 0.f;
+                l += p;
 #pragma unroll
-    for (int it = 0; it < IT; ++it) {
-        float vf[8];
-        widen8(vr[it], vf);
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            const float p = ok[it] ? exp2f(z[it][h] - m[h]) : 0.f;
-            l[h] += p;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(p, vf[e], acc[h][e]);
+                for (int e = 0; e < 8; ++e) acc[e] = fmaf(p, vf[e], acc[e]);
+            }
         }
-    }
-    // sum over the token slots of the wave (lanes that share a channel chunk)
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-#pragma unroll
-        for (int o = LPT; o < 64; o <<= 1) {
-            l[h] += __shfl_xor(l[h], o);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[h][e] += __shfl_xor(acc[h][e], o);
-        }
-    }
-    if (ts == 0) {
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) s_acc[wave][h][cc * 8 + e] = acc[h][e];
-            if (cc == 0) { s_m[wave][h] = m[h]; s_l[wave][h] = l[h]; }
+        float4* dst = reinterpret_cast<float4*>(&s_acc[slot][h][cc * 8]);
+        dst[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        dst[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+        if (cc == 0) {
+            s_m[slot][h] = m;
+            s_l[slot][h] = l;
         }
     }
     __syncthreads();
@@ -164,11 +179,11 @@ __global__ __launch_bounds__(256) void attend_gqa_kernel(
         const int h = p / D, c = p - h * D;
         float M = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) M = fmaxf(M, s_m[w][h]);
+        for (int w = 0; w < NP; ++w) M = fmaxf(M, s_m[w][h]);
         float L = 0.f, A = 0.f;
         if (M != -INFINITY) {
 #pragma unroll
-            for (int w = 0; w < 4; ++w) {
+            for (int w = 0; w < NP; ++w) {
                 const float mw = s_m[w][h];
                 const float wt = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
                 L = fmaf(s_l[w][h], wt, L);
@@ -295,30 +310,51 @@ __global__ __launch_bounds__(256) void attend_mla_kernel(
     }
 }
 
-// grid: (B*Hq). Merges the split partials of one query head.
+// grid: (B*Hq). Merges the split partials of one query head. The (max,
+// sum) pairs and the accumulator rows of a chunk of eight splits are all
+// loaded before any arithmetic, so a chunk costs one memory round trip.
 __global__ __launch_bounds__(256) void combine_kernel(
     const float* __restrict__ part_ml, const float* __restrict__ part_acc, float* __restrict__ out,
     float* __restrict__ lse, int dv, int n_splits) {
+    constexpr int CH = 8;
     const size_t bh = blockIdx.x;
     const float* ml = part_ml + bh * n_splits * 2;
-    float M = -INFINITY;
-    for (int s = 0; s < n_splits; ++s) M = fmaxf(M, ml[2 * s]);
-    float L = 0.f;
-    if (M != -INFINITY)
-        for (int s = 0; s < n_splits; ++s) {
-            const float ms = ml[2 * s];
-            if (ms != -INFINITY) L = fmaf(ml[2 * s + 1], exp2f(ms - M), L);
+    const float* pa = part_acc + bh * n_splits * dv;
+    const int c0 = threadIdx.x, c1 = threadIdx.x + blockDim.x;   // dv <= 2 * blockDim.x
+    float M = -INFINITY, L = 0.f, A0 = 0.f, A1 = 0.f;
+    for (int s0 = 0; s0 < n_splits; s0 += CH) {
+        float2 mlv[CH];
+        float a0[CH], a1[CH];
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+            const int sj = s0 + j < n_splits ? s0 + j : n_splits - 1;
+            mlv[j] = *reinterpret_cast<const float2*>(ml + 2 * sj);
+            a0[j] = c0 < dv ? pa[(size_t)sj * dv + c0] : 0.f;
+            a1[j] = c1 < dv ? pa[(size_t)sj * dv + c1] : 0.f;
         }
-    const float inv = L > 0.f ? 1.f / L : 0.f;
-    for (int c = threadIdx.x; c < dv; c += blockDim.x) {
-        float A = 0.f;
-        if (M != -INFINITY)
-            for (int s = 0; s < n_splits; ++s) {
-                const float ms = ml[2 * s];
-                if (ms != -INFINITY) A = fmaf(part_acc[(bh * n_splits + s) * dv + c], exp2f(ms - M), A);
+        float Mc = M;
+#pragma unroll
+        for (int j = 0; j < CH; ++j)
+            if (s0 + j < n_splits) Mc = fmaxf(Mc, mlv[j].x);
+        if (Mc == -INFINITY) continue;
+        const float r = M == -INFINITY ? 0.f : exp2f(M - Mc);   // rescale what is merged so far
+        L *= r;
+        A0 *= r;
+        A1 *= r;
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+            if (s0 + j < n_splits && mlv[j].x != -INFINITY) {
+                const float wt = exp2f(mlv[j].x - Mc);
+                L = fmaf(mlv[j].y, wt, L);
+                A0 = fmaf(a0[j], wt, A0);
+                A1 = fmaf(a1[j], wt, A1);
             }
-        out[bh * dv + c] = A * inv;
+        }
+        M = Mc;
     }
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    if (c0 < dv) out[bh * dv + c0] = A0 * inv;
+    if (c1 < dv) out[bh * dv + c1] = A1 * inv;
     if (threadIdx.x == 0) lse[bh] = L > 0.f ? (M + log2f(L)) * LN2 : -INFINITY;
 }
 

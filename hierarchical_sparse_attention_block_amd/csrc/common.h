@@ -54,6 +54,21 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
+// Sum over aligned groups of N lanes (N = 8, 16 or 32); every lane of a
+// group gets the group's total. Within a 16-lane row the partners come from
+// DPP lane swaps (lane ^ 1, lane ^ 2, half-row mirror, row mirror); the
+// step across two rows is a lane shuffle.
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+    static_assert(N == 8 || N == 16 || N == 32, "group size");
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
+    if (N >= 16) v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));
+    if (N == 32) v += __shfl_xor(v, 16);
+    return v;
+}
+
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 __device__ __forceinline__ i16x4_t as_i16x4(uint2 v) { return __builtin_bit_cast(i16x4_t, v); }
 

@@ -14,10 +14,13 @@
 // 2*d_k stacked channels in steps of 32. Lane l supplies block (l % 16) and
 // the 8-channel chunk 4*s + l/16 of step s, i.e. one 16-byte load per step;
 // the 16 lanes of a chunk read 16 different 64-byte row segments, and four
-// consecutive steps cover each row's cache lines fully. A fragments are
-// built once per workgroup in LDS. The result tile holds block (l % 16) in
-// lane l for head rows 4*(l/16)..+3; a max over valid heads and two lane
-// swaps leave the block score in lanes 0..15.
+// consecutive steps cover each row's cache lines fully. Each wave holds its
+// A fragments in registers (loaded once; the queries stay in L2), so no
+// workgroup barrier precedes the metadata stream. Long rows (more than 16
+// steps, e.g. 576-dim latent keys) split their steps over the four waves of
+// a workgroup, which add their partial tiles through LDS. The result tile
+// holds block (l % 16) in lane l for head rows 4*(l/16)..+3; a max over
+// valid heads and two lane swaps leave the block score in lanes 0..15.
 #include "common.h"
 #include "kernels.h"
 
@@ -40,18 +43,21 @@ struct Append {
     int dv, r;
 };
 
-template <int MT, int KSMAX>
+// MT: 16-row head tiles (G <= 16 or <= 32); KSW: max steps per wave;
+// KSPLIT: waves sharing one block tile (1: each wave scores its own tiles).
+template <int MT, int KSW, int KSPLIT>
 __global__ __launch_bounds__(256) void block_score_kernel(
     const uint16_t* __restrict__ q, uint16_t* __restrict__ meta,
     const int32_t* __restrict__ ctx_len, float* __restrict__ score,
     int Hkv, int G, int dk, int bs, int max_ctx, int nb_cap, int tiles_per_wave, Append ap) {
-    __shared__ uint4 qa[MT * KSMAX * 64];   // A fragments [mt][step][lane]
+    __shared__ f32x4_t red[KSPLIT > 1 ? KSPLIT * MT * 64 : 1];
 
     const int unit = blockIdx.y, b = unit / Hkv, g = unit % Hkv;
     int n = ctx_len[b];
     n = n < 1 ? 1 : (n > max_ctx ? max_ctx : n);
     const int nb = (n + bs - 1) / bs;
-    const int per_wg = SCORE_WAVES * tiles_per_wave * 16;
+    constexpr int TILES_WG = SCORE_WAVES / KSPLIT;     // block tiles side by side in a workgroup
+    const int per_wg = TILES_WG * tiles_per_wave * 16;
     const int j_wg = blockIdx.x * per_wg;
     if (j_wg >= nb) return;
 
@@ -87,76 +93,139 @@ __global__ __launch_bounds__(256) void block_score_kernel(
 
     const int KS = dk / 16;        // steps of 32 over 2*dk stacked channels
     const int CH = dk / 8;         // 8-channel chunks in one half
-    const uint16_t* qg = q + ((size_t)b * Hkv * G + (size_t)g * G) * dk;
-    for (int e = threadIdx.x; e < MT * KS * 64; e += blockDim.x) {
-        const int lane = e & 63, s = (e >> 6) % KS, mt = e / (64 * KS);
-        const int m = mt * 16 + (lane & 15);
-        const int c = s * 4 + (lane >> 4);
-        uint4 v = {0u, 0u, 0u, 0u};
-        if (m < G) {
-            const bool lower = c >= CH;
-            const uint4 raw = ldg16(qg + (size_t)m * dk + (lower ? c - CH : c) * 8);
-            if (lower) v = {bf16x2_neg(raw.x), bf16x2_neg(raw.y), bf16x2_neg(raw.z), bf16x2_neg(raw.w)};
-            else v = {bf16x2_pos(raw.x), bf16x2_pos(raw.y), bf16x2_pos(raw.z), bf16x2_pos(raw.w)};
-        }
-        qa[(mt * KSMAX + s) * 64 + lane] = v;
-    }
-    __syncthreads();
-
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int part = KSPLIT > 1 ? wave : 0;              // step range of this wave
+    const int tslot = KSPLIT > 1 ? 0 : wave;             // tile column of this wave
+    const int s_lo = part * KS / KSPLIT, s_hi = (part + 1) * KS / KSPLIT;
     const uint16_t* Mu = meta + (size_t)unit * nb_cap * 2 * dk;
     float* Su = score + (size_t)unit * nb_cap;
-    for (int t = 0; t < tiles_per_wave; ++t) {
-        const int j0 = j_wg + (t * SCORE_WAVES + wave) * 16;
-        if (j0 >= nb) break;
-        const int jl = j0 + (lane & 15);
+    auto tile_j0 = [&](int t) { return j_wg + (t * TILES_WG + tslot) * 16; };
+    auto tile_row = [&](int t) {
+        const int jl = tile_j0(t) + (lane & 15);
         const int jc = jl < nb ? jl : nb - 1;          // keep loads inside the unit's blocks
-        const uint16_t* row = Mu + (size_t)jc * 2 * dk + (lane >> 4) * 8;
-        f32x4_t acc[MT];
+        return Mu + (size_t)jc * 2 * dk + (lane >> 4) * 8;
+    };
+
+    // the first tile's rows are requested first; the A fragments follow
+    // Steps past this wave's range hold zeros in both operands: the matrix
+    // instructions below run for every step, so their products must vanish
+    // rather than depend on stale register contents.
+    uint4 cur[KSW], nxt[KSW];
+    {
+        const uint16_t* row = tile_row(0);
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        for (int s0 = 0; s0 < KS; s0 += 8) {
-            uint4 bf[8];
+        for (int u = 0; u < KSW; ++u)
+            cur[u] = s_lo + u < s_hi ? ldg16(row + (s_lo + u) * 32) : make_uint4(0u, 0u, 0u, 0u);
+    }
+    const uint16_t* qg = q + ((size_t)b * Hkv * G + (size_t)g * G) * dk;
+    uint4 af[MT][KSW];
 #pragma unroll
-            for (int u = 0; u < 8; ++u)
-                if (s0 + u < KS) bf[u] = ldg16(row + (s0 + u) * 32);
+    for (int mt = 0; mt < MT; ++mt) {
+        const int m = mt * 16 + (lane & 15);
+        const uint16_t* qm = qg + (size_t)(m < G ? m : 0) * dk;
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                if (s0 + u < KS) {
+        for (int u = 0; u < KSW; ++u) {
+            const int c = (s_lo + u) * 4 + (lane >> 4);
+            af[mt][u] = make_uint4(0u, 0u, 0u, 0u);
+            if (m < G && s_lo + u < s_hi) af[mt][u] = ldg16(qm + (c >= CH ? c - CH : c) * 8);
+        }
+    }
 #pragma unroll
-                    for (int mt = 0; mt < MT; ++mt)
-                        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            as_bf16x8(qa[(mt * KSMAX + s0 + u) * 64 + lane]), as_bf16x8(bf[u]), acc[mt], 0, 0, 0);
-                }
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int u = 0; u < KSW; ++u) {
+            const uint4 r = af[mt][u];
+            const bool lower = (s_lo + u) * 4 + (lane >> 4) >= CH;
+            af[mt][u] = lower ? make_uint4(bf16x2_neg(r.x), bf16x2_neg(r.y), bf16x2_neg(r.z), bf16x2_neg(r.w))
+                              : make_uint4(bf16x2_pos(r.x), bf16x2_pos(r.y), bf16x2_pos(r.z), bf16x2_pos(r.w));
+        }
+
+    for (int t = 0; t < tiles_per_wave; ++t) {
+        const bool live = tile_j0(t) < nb;
+        if (KSPLIT == 1 && !live) break;
+        if (KSPLIT > 1 && tile_j0(t) >= nb) break;   // uniform over the workgroup
+        const bool more = t + 1 < tiles_per_wave && tile_j0(t + 1) < nb;
+        if (more) {
+            const uint16_t* row1 = tile_row(t + 1);
+#pragma unroll
+            for (int u = 0; u < KSW; ++u)
+                nxt[u] = s_lo + u < s_hi ? ldg16(row1 + (s_lo + u) * 32) : make_uint4(0u, 0u, 0u, 0u);
+        }
+        // two accumulators per head tile shorten the dependent MFMA chain
+        f32x4_t acc[MT][2];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[mt][0] = acc[mt][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < KSW; ++u) {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+                acc[mt][u & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(af[mt][u]), as_bf16x8(cur[u]),
+                                                                       acc[mt][u & 1], 0, 0, 0);
+        }
+        f32x4_t tot[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) tot[mt] = acc[mt][0] + acc[mt][1];
+        bool emit = true;
+        if (KSPLIT > 1) {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) red[(wave * MT + mt) * 64 + lane] = tot[mt];
+            __syncthreads();
+            emit = wave == 0;
+            if (emit) {
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int w = 1; w < KSPLIT; ++w) tot[mt] += red[(w * MT + mt) * 64 + lane];
             }
+            __syncthreads();   // red is reused by the next tile
         }
-        float v = -INFINITY;
+        if (emit) {
+            float v = -INFINITY;
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+            for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (mt * 16 + (lane >> 4) * 4 + i < G) v = fmaxf(v, acc[mt][i]);
-        if (G > 4) {   // heads 4.. sit in the other 16-lane rows
-            v = fmaxf(v, __shfl_xor(v, 16));
-            v = fmaxf(v, __shfl_xor(v, 32));
+                for (int i = 0; i < 4; ++i)
+                    if (mt * 16 + (lane >> 4) * 4 + i < G) v = fmaxf(v, tot[mt][i]);
+            if (G > 4) {   // heads 4.. sit in the other 16-lane rows
+                v = fmaxf(v, __shfl_xor(v, 16));
+                v = fmaxf(v, __shfl_xor(v, 32));
+            }
+            const int jl = tile_j0(t) + (lane & 15);
+            if (lane < 16 && jl < nb) Su[jl] = v;
         }
-        if (lane < 16 && jl < nb) Su[jl] = v;
+        if (more) {
+#pragma unroll
+            for (int u = 0; u < KSW; ++u) cur[u] = nxt[u];
+        }
     }
 }
 
-template <int MT, int KSMAX>
+template <int MT, int KSW, int KSPLIT>
 hipError_t launch_t(const Shape& s, const uint16_t* q, uint16_t* meta, const int32_t* ctx_len,
                     float* score, const Append& ap, hipStream_t st) {
-    const int tiles_per_unit = (s.nb_cap + 15) / 16;
-    const long total_wave_tiles = (long)tiles_per_unit * s.B * s.Hkv / SCORE_WAVES;
+    constexpr int TILES_WG = SCORE_WAVES / KSPLIT;
+    const long tiles = (long)((s.nb_cap + 15) / 16) * s.B * s.Hkv;
     // aim for ~2048 workgroups (8 per CU) before giving a wave more tiles
-    int tpw = (int)((total_wave_tiles + 2047) / 2048);
+    int tpw = (int)((tiles / TILES_WG + 2047) / 2048);
     tpw = tpw < 1 ? 1 : (tpw > 8 ? 8 : tpw);
-    const int per_wg = SCORE_WAVES * tpw * 16;
+    const int per_wg = TILES_WG * tpw * 16;
     dim3 grid((s.nb_cap + per_wg - 1) / per_wg, s.B * s.Hkv);
-    hipLaunchKernelGGL((block_score_kernel<MT, KSMAX>), grid, dim3(64 * SCORE_WAVES), 0, st, q, meta,
+    hipLaunchKernelGGL((block_score_kernel<MT, KSW, KSPLIT>), grid, dim3(64 * SCORE_WAVES), 0, st, q, meta,
                        ctx_len, score, s.Hkv, s.G, s.dk, s.bs, s.max_ctx, s.nb_cap, tpw, ap);
     return hipGetLastError();
+}
+
+template <int MT>
+hipError_t launch_mt(const Shape& s, const uint16_t* q, uint16_t* meta, const int32_t* ctx_len, float* score,
+                     const Append& ap, hipStream_t st) {
+    const int ks = s.dk / 16;
+    if (ks <= 4) return launch_t<MT, 4, 1>(s, q, meta, ctx_len, score, ap, st);
+    if (ks <= 8) return launch_t<MT, 8, 1>(s, q, meta, ctx_len, score, ap, st);
+    if (ks <= 16) return launch_t<MT, 16, 1>(s, q, meta, ctx_len, score, ap, st);
+    if (ks <= 32) return launch_t<MT, 8, 4>(s, q, meta, ctx_len, score, ap, st);
+    if (ks <= 36) return launch_t<MT, 9, 4>(s, q, meta, ctx_len, score, ap, st);    // 576-dim latent keys
+    if (ks <= 40) return launch_t<MT, 10, 4>(s, q, meta, ctx_len, score, ap, st);
+    return launch_t<MT, 16, 4>(s, q, meta, ctx_len, score, ap, st);   // d_k <= 1024: <= 64 steps
 }
 
 }  // namespace
@@ -165,17 +234,8 @@ hipError_t launch_block_score(const Shape& s, const uint16_t* q, uint16_t* meta,
                               float* score, const uint16_t* k_new, const uint16_t* v_new, uint16_t* K,
                               uint16_t* V, uint16_t* klabel, const int32_t* label_ch, hipStream_t st) {
     const Append ap{k_new, v_new, K, s.valias ? nullptr : V, klabel, label_ch, s.dv, s.r};
-    const int ks = s.dk / 16;
-    if (s.G <= 16) {
-        if (ks <= 8) return launch_t<1, 8>(s, q, meta, ctx_len, score, ap, st);
-        if (ks <= 16) return launch_t<1, 16>(s, q, meta, ctx_len, score, ap, st);
-        if (ks <= 36) return launch_t<1, 36>(s, q, meta, ctx_len, score, ap, st);
-        return launch_t<1, 64>(s, q, meta, ctx_len, score, ap, st);
-    }
-    if (ks <= 8) return launch_t<2, 8>(s, q, meta, ctx_len, score, ap, st);
-    if (ks <= 16) return launch_t<2, 16>(s, q, meta, ctx_len, score, ap, st);
-    if (ks <= 36) return launch_t<2, 36>(s, q, meta, ctx_len, score, ap, st);
-    return launch_t<2, 64>(s, q, meta, ctx_len, score, ap, st);
+    return s.G <= 16 ? launch_mt<1>(s, q, meta, ctx_len, score, ap, st)
+                     : launch_mt<2>(s, q, meta, ctx_len, score, ap, st);
 }
 
 }  // namespace hsab

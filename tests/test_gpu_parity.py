@@ -101,7 +101,10 @@ def test_build_meta_and_append_exact(dk, bs, r):
 
 
 # ----------------------------------------------------------- block scores
-@pytest.mark.parametrize("G,dk", [(4, 128), (1, 64), (8, 256), (32, 576), (16, 128), (3, 128)])
+# (32, 592) and (2, 1008): rows of 37 and 63 steps split unevenly over the
+# four waves that share a block tile
+@pytest.mark.parametrize("G,dk", [(4, 128), (1, 64), (8, 256), (32, 576), (16, 128), (3, 128), (32, 592),
+                                  (2, 1008)])
 def test_block_scores_within_fp32_bound(G, dk):
     w = _wl(n_q_heads=2 * G, n_kv_heads=2, d_k=dk, d_v=dk if dk != 576 else 512,
             v_alias_k=dk == 576, max_ctx=1500, ctx=1500, n_planted=0, r=16)
