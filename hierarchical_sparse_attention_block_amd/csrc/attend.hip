@@ -199,8 +199,21 @@ __global__ __launch_bounds__(256) void attend_gqa_kernel(
     }
 }
 
-// grid: as the GQA kernel; block 256. Hq = 32 * Hkv, d_k % 32 == 0,
-// d_v % 64 == 0, d_v <= 512, values alias the first d_v key dims.
+// grid: as the GQA kernel; block 256 (4 waves). Hq = 32 * Hkv, d_k % 32 ==
+// 0, d_k <= DKMAX, d_v % 64 == 0, d_v <= 512, values alias the first d_v
+// key dims (absorbed latent). One workgroup takes T = 32 kept tokens:
+//  1. the group's query fragments are requested first (registers), the
+//     token rows and slots next; the 32 key rows (which hold the values)
+//     are staged in LDS with every load in flight;
+//  2. logits on v_mfma_f32_16x16x32_bf16: wave w multiplies token tile
+//     w & 1 by head tile w >> 1 over the d_k / 32 steps;
+//  3. softmax per head over the 32 tokens (8 lanes per head, DPP);
+//  4. P.V on the same instruction with M = heads, N = 16 value channels,
+//     K = the 32 tokens. P enters as two bf16 terms (hi + lo) so the
+//     weights keep ~16 mantissa bits; V is exact in bf16.
+// Operands of steps past d_k are zeros: the matrix instructions run for
+// every step.
+template <int DKMAX>
 __global__ __launch_bounds__(256) void attend_mla_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ K, const int32_t* __restrict__ tok_idx,
     const int32_t* __restrict__ slot_of, int n_slots, float* __restrict__ part_ml,
@@ -208,7 +221,9 @@ __global__ __launch_bounds__(256) void attend_mla_kernel(
     int n_splits, int units, float scale2, int slot_rows) {
     constexpr int T = MLA_TOK_PER_SPLIT;   // 32 tokens
     constexpr int H = 32;                  // query heads per KV head
-    __shared__ uint16_t sV[T][512];
+    constexpr int KSMAX = DKMAX / 32;      // logit steps
+    constexpr int RS = DKMAX + 8;          // LDS row stride (elements): spreads rows over banks
+    __shared__ __align__(16) uint16_t sK[T * RS];
     __shared__ float sS[T][H + 1];
     __shared__ float sm[H], sl[H];
     __shared__ long s_row[T];
@@ -217,41 +232,72 @@ __global__ __launch_bounds__(256) void attend_mla_kernel(
     const int unit = (y / n_splits) * 8 + xcd, split = y % n_splits;
     if (unit >= units) return;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int KS = dk / 32;
+    const int mt = wave & 1, nt = wave >> 1;   // logit tile: tokens 16*mt.., heads 16*nt..
 
+    // 1. query fragments (B operand: head nt*16 + lane%16, channels
+    //    32*s + 8*(lane/16)..), then token rows
+    uint4 qb[KSMAX];
+    {
+        const uint16_t* qr = q + ((size_t)unit * H + nt * 16 + (lane & 15)) * dk + (lane >> 4) * 8;
+#pragma unroll
+        for (int u = 0; u < KSMAX; ++u) qb[u] = u < KS ? ldg16(qr + u * 32) : make_uint4(0u, 0u, 0u, 0u);
+    }
     if (tid < T) {
         const int ti = split * T + tid;
         const int t = ti < kt ? tok_idx[(size_t)unit * kt + ti] : -1;
-        s_row[tid] = row_of(t, unit, bs, max_ctx, nb_cap, slot_of, n_slots, slot_rows);
+        long row = -1;
+        if (!slot_of) {
+            row = (t >= 0 && t < max_ctx) ? (long)unit * max_ctx + t : -1;
+        } else if (t >= 0) {
+            const int blk = t / bs;
+            const int sl_ = blk < nb_cap ? slot_of[(size_t)unit * nb_cap + blk] : -1;
+            row = (sl_ >= 0 && sl_ < n_slots) ? ((long)unit * n_slots + sl_) * slot_rows + (t - blk * bs) : -1;
+        }
+        s_row[tid] = row;
     }
     __syncthreads();
 
-    // value rows (first dv dims of each kept key row) into LDS
-    const int cpr = dv / 8;
-    for (int c = tid; c < T * cpr; c += 256) {
-        const int tok = c / cpr, ch = c - tok * cpr;
-        const long row = s_row[tok];
-        const uint4 v = row >= 0 ? ldg16(K + row * dk + ch * 8) : make_uint4(0u, 0u, 0u, 0u);
-        *reinterpret_cast<uint4*>(&sV[tok][ch * 8]) = v;
-    }
-
-    // logits: wave w computes tokens 16*(w & 1).. x heads 16*(w >> 1)..
+    // key rows into LDS: chunk c of token r at sK[r * RS + 8c]; every load
+    // of the thread is issued before the first store
     {
-        const int mt = wave & 1, nt = wave >> 1;
-        const long ra = s_row[mt * 16 + (lane & 15)];
-        const uint16_t* arow = K + (ra >= 0 ? ra : 0) * dk + (lane >> 4) * 8;
-        const uint16_t* brow = q + ((size_t)unit * H + nt * 16 + (lane & 15)) * dk + (lane >> 4) * 8;
-        const int KS = dk / 32;
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-        for (int s0 = 0; s0 < KS; s0 += 6) {
-            uint4 af[6], bf[6];
+        const int cpr = dk / 8;
+        constexpr int PER = (T * DKMAX / 8 + 255) / 256;
+        uint4 v[PER];
 #pragma unroll
-            for (int u = 0; u < 6; ++u)
-                if (s0 + u < KS) { af[u] = ldg16(arow + (s0 + u) * 32); bf[u] = ldg16(brow + (s0 + u) * 32); }
-#pragma unroll
-            for (int u = 0; u < 6; ++u)
-                if (s0 + u < KS)
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(af[u]), as_bf16x8(bf[u]), acc, 0, 0, 0);
+        for (int i = 0; i < PER; ++i) {
+            const int c = tid + i * 256;
+            const int r = c / cpr, ch = c - r * cpr;
+            const long row = c < T * cpr ? s_row[r] : -1;
+            v[i] = row >= 0 ? ldg16(K + row * dk + ch * 8) : make_uint4(0u, 0u, 0u, 0u);
         }
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int c = tid + i * 256;
+            if (c < T * cpr) {
+                const int r = c / cpr, ch = c - r * cpr;
+                *reinterpret_cast<uint4*>(&sK[r * RS + ch * 8]) = v[i];
+            }
+        }
+    }
+    __syncthreads();
+
+    // 2. logits: A = key rows of tile mt from LDS, B = query fragments
+    {
+        const uint16_t* ar = &sK[(mt * 16 + (lane & 15)) * RS + (lane >> 4) * 8];
+        f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < KSMAX; u += 2) {
+            const uint4 a0 = u < KS ? *reinterpret_cast<const uint4*>(ar + u * 32) : make_uint4(0u, 0u, 0u, 0u);
+            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a0), as_bf16x8(qb[u]), acc0, 0, 0, 0);
+            if (u + 1 < KSMAX) {
+                const uint4 a1 =
+                    u + 1 < KS ? *reinterpret_cast<const uint4*>(ar + (u + 1) * 32) : make_uint4(0u, 0u, 0u, 0u);
+                acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a1), as_bf16x8(qb[u + 1]), acc1, 0, 0, 0);
+            }
+        }
+        const f32x4_t acc = acc0 + acc1;
+        // lane: head nt*16 + lane%16, tokens mt*16 + 4*(lane/16) + i
         const int h = nt * 16 + (lane & 15);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -261,52 +307,78 @@ __global__ __launch_bounds__(256) void attend_mla_kernel(
     }
     __syncthreads();
 
-    if (tid < H) {
-        float m = -INFINITY;
-        for (int t = 0; t < T; ++t) m = fmaxf(m, sS[t][tid]);
+    // 3. softmax per head: 8 lanes per head, 4 tokens each
+    {
+        const int h = tid >> 3, part = tid & 7;
+        float z[4], m = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            z[i] = sS[part * 4 + i][h];
+            m = fmaxf(m, z[i]);
+        }
+        m = group_max<8>(m);
         float l = 0.f;
-        for (int t = 0; t < T; ++t) {
-            const float z = sS[t][tid];
-            const float p = (z == -INFINITY) ? 0.f : exp2f(z - m);
-            sS[t][tid] = p;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float p = (z[i] == -INFINITY) ? 0.f : exp2f(z[i] - m);
+            sS[part * 4 + i][h] = p;
             l += p;
         }
-        sm[tid] = m;
-        sl[tid] = l;
+        l = group_sum<8>(l);
+        if (part == 0) {
+            sm[h] = m;
+            sl[h] = l;
+        }
     }
     __syncthreads();
 
-    // P.V: thread -> head tid/8, channels (tid%8)*8 + 64*j + e
-    const int h = tid >> 3, c8 = tid & 7;
-    const int nj = dv / 64;
-    float acc[8][8];
+    // 4. P.V: wave w takes value channels [dv/4 * w, dv/4 * (w+1)) in
+    //    16-channel tiles, both head tiles. A = P (head lane%16, tokens
+    //    8*(lane/16)..+8), B = V (channel lane%16, same tokens).
+    const int NT = dv / 16;            // channel tiles (<= 32)
+    bf16x8_t pa_hi[2], pa_lo[2];
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
+    for (int m2 = 0; m2 < 2; ++m2) {
+        const int h = m2 * 16 + (lane & 15);
+        uint32_t hi[4], lo[4];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[j][e] = 0.f;
-    for (int t = 0; t < T; ++t) {
-        const float p = sS[t][h];
+        for (int j = 0; j < 4; ++j) {
+            const float p0 = sS[(lane >> 4) * 8 + 2 * j][h], p1 = sS[(lane >> 4) * 8 + 2 * j + 1][h];
+            const uint32_t h0 = f32_bf16_rne(p0), h1 = f32_bf16_rne(p1);
+            const uint32_t l0 = f32_bf16_rne(p0 - bf16_f32(h0)), l1 = f32_bf16_rne(p1 - bf16_f32(h1));
+            hi[j] = h0 | (h1 << 16);
+            lo[j] = l0 | (l1 << 16);
+        }
+        pa_hi[m2] = as_bf16x8(make_uint4(hi[0], hi[1], hi[2], hi[3]));
+        pa_lo[m2] = as_bf16x8(make_uint4(lo[0], lo[1], lo[2], lo[3]));
+    }
+    const size_t bh0 = (size_t)unit * H;
+    for (int n = wave; n < NT; n += 4) {
+        // B fragment: 8 tokens of channel n*16 + lane%16
+        const int c = n * 16 + (lane & 15);
+        uint32_t w4[4];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            if (j < nj) {
-                float vf[8];
-                widen8(*reinterpret_cast<const uint4*>(&sV[t][c8 * 8 + 64 * j]), vf);
+        for (int j = 0; j < 4; ++j) {
+            const int t0 = (lane >> 4) * 8 + 2 * j;
+            w4[j] = (uint32_t)sK[t0 * RS + c] | ((uint32_t)sK[(t0 + 1) * RS + c] << 16);
+        }
+        const bf16x8_t vb = as_bf16x8(make_uint4(w4[0], w4[1], w4[2], w4[3]));
 #pragma unroll
-                for (int e = 0; e < 8; ++e) acc[j][e] = fmaf(p, vf[e], acc[j][e]);
+        for (int m2 = 0; m2 < 2; ++m2) {
+            f32x4_t o = {0.f, 0.f, 0.f, 0.f};
+            o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_hi[m2], vb, o, 0, 0, 0);
+            o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_lo[m2], vb, o, 0, 0, 0);
+            // lane: channel c, heads m2*16 + 4*(lane/16) + i
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int h = m2 * 16 + (lane >> 4) * 4 + i;
+                part_acc[((bh0 + h) * n_splits + split) * dv + c] = o[i];
             }
         }
     }
-    const size_t bh = (size_t)unit * H + h;
-    float* dst = part_acc + (bh * n_splits + split) * dv;
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-        if (j < nj) {
-            *reinterpret_cast<float4*>(dst + c8 * 8 + 64 * j) = make_float4(acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
-            *reinterpret_cast<float4*>(dst + c8 * 8 + 64 * j + 4) = make_float4(acc[j][4], acc[j][5], acc[j][6], acc[j][7]);
-        }
-    if (c8 == 0) {
-        part_ml[(bh * n_splits + split) * 2 + 0] = sm[h];
-        part_ml[(bh * n_splits + split) * 2 + 1] = sl[h];
+    if (tid < H) {
+        part_ml[((bh0 + tid) * n_splits + split) * 2 + 0] = sm[tid];
+        part_ml[((bh0 + tid) * n_splits + split) * 2 + 1] = sl[tid];
     }
 }
 
@@ -406,9 +478,15 @@ hipError_t launch_attend(const Shape& s, const uint16_t* q, const uint16_t* K, c
     hipError_t e = hipSuccess;
     if (mla_shape(s)) {
         const int units = s.B * s.Hkv;
-        hipLaunchKernelGGL(attend_mla_kernel, dim3(((units + 7) / 8) * 8 * ns), dim3(256), 0, st, q, K, tok_idx,
-                           slot_of, n_slots, part_ml, part_acc, s.Hkv, s.dk, s.dv, s.bs, s.kt, s.max_ctx, s.nb_cap,
-                           ns, units, s.sm_scale * LOG2E, s.bs);
+        const dim3 grid(((units + 7) / 8) * 8 * ns);
+        if (s.dk <= 576)
+            hipLaunchKernelGGL(attend_mla_kernel<576>, grid, dim3(256), 0, st, q, K, tok_idx, slot_of, n_slots,
+                               part_ml, part_acc, s.Hkv, s.dk, s.dv, s.bs, s.kt, s.max_ctx, s.nb_cap, ns, units,
+                               s.sm_scale * LOG2E, s.bs);
+        else
+            hipLaunchKernelGGL(attend_mla_kernel<1024>, grid, dim3(256), 0, st, q, K, tok_idx, slot_of, n_slots,
+                               part_ml, part_acc, s.Hkv, s.dk, s.dv, s.bs, s.kt, s.max_ctx, s.nb_cap, ns, units,
+                               s.sm_scale * LOG2E, s.bs);
         e = hipGetLastError();
     } else {
         switch (s.dk) {

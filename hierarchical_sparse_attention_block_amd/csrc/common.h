@@ -69,6 +69,23 @@ __device__ __forceinline__ float group_sum(float v) {
     return v;
 }
 
+// Maximum over aligned groups of N lanes (N = 8 or 16), same lane swaps.
+template <int N>
+__device__ __forceinline__ float group_max(float v) {
+    static_assert(N == 8 || N == 16, "group size");
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false)));
+    if (N == 16) v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false)));
+    return v;
+}
+
+// float -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_bf16_rne(float f) {
+    const uint32_t u = __float_as_uint(f);
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 __device__ __forceinline__ i16x4_t as_i16x4(uint2 v) { return __builtin_bit_cast(i16x4_t, v); }
 
