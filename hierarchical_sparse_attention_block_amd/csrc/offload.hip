@@ -24,44 +24,37 @@ namespace hsab {
 
 namespace {
 
-// grid: (B). Appends the token at position ctx_len[b]-1 of every KV head
-// into the tail slot of its block, widens that block's max/min and writes
-// its label row.
+// grid: (B*Hkv), one workgroup per unit. Appends the token at position
+// ctx_len[b]-1 into the tail slot of its block, widens that block's
+// max/min and writes its label row.
 __global__ __launch_bounds__(256) void append_slot_kernel(
     const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new, uint16_t* __restrict__ cache,
     uint16_t* __restrict__ meta, uint16_t* __restrict__ klabel, const int32_t* __restrict__ label_ch,
     const int32_t* __restrict__ ctx_len, int Hkv, int dk, int dv, int valias, int bs, int r, int max_ctx,
     int nb_cap, int n_slots) {
-    const int b = blockIdx.x;
+    const int unit = blockIdx.x, b = unit / Hkv, g = unit % Hkv;
     const int pos = ctx_len[b] - 1;
     if (pos < 0 || pos >= max_ctx) return;
     const int j = pos / bs, off = pos - j * bs;
     const bool first = off == 0;
     const size_t slot_elems = (size_t)bs * (valias ? dk : dk + dv);
-    for (int g = 0; g < Hkv; ++g) {
-        const int unit = b * Hkv + g;
-        const uint16_t* kn = k_new + (size_t)unit * dk;
-        uint16_t* slot = cache + ((size_t)unit * n_slots + (n_slots - 2 + (j & 1))) * slot_elems;
-        uint16_t* M = meta + ((size_t)unit * nb_cap + j) * 2 * dk;
-        for (int c = threadIdx.x; c < dk; c += blockDim.x) {
-            const uint16_t kb = kn[c];
-            slot[(size_t)off * dk + c] = kb;
-            if (first) {
-                M[c] = kb;
-                M[dk + c] = kb;
-            } else {
-                const float kf = bf16_f32(kb);
-                if (kf > bf16_f32(M[c])) M[c] = kb;
-                if (kf < bf16_f32(M[dk + c])) M[dk + c] = kb;
-            }
-        }
-        if (!valias) {
-            const uint16_t* vn = v_new + (size_t)unit * dv;
-            for (int c = threadIdx.x; c < dv; c += blockDim.x) slot[(size_t)bs * dk + (size_t)off * dv + c] = vn[c];
-        }
-        uint16_t* Lrow = klabel + ((size_t)unit * max_ctx + pos) * r;
-        for (int c = threadIdx.x; c < r; c += blockDim.x) Lrow[c] = kn[clamp_ch(label_ch[g * r + c], dk)];
+    const uint16_t* kn = k_new + (size_t)unit * dk;
+    uint16_t* slot = cache + ((size_t)unit * n_slots + (n_slots - 2 + (j & 1))) * slot_elems;
+    uint16_t* M = meta + ((size_t)unit * nb_cap + j) * 2 * dk;
+    for (int c = threadIdx.x; c < dk; c += blockDim.x) {
+        const uint16_t kb = kn[c];
+        const uint16_t mx = M[c], mn = M[dk + c];
+        slot[(size_t)off * dk + c] = kb;
+        const float kf = bf16_f32(kb);
+        M[c] = (first || kf > bf16_f32(mx)) ? kb : mx;
+        M[dk + c] = (first || kf < bf16_f32(mn)) ? kb : mn;
     }
+    if (!valias) {
+        const uint16_t* vn = v_new + (size_t)unit * dv;
+        for (int c = threadIdx.x; c < dv; c += blockDim.x) slot[(size_t)bs * dk + (size_t)off * dv + c] = vn[c];
+    }
+    uint16_t* Lrow = klabel + ((size_t)unit * max_ctx + pos) * r;
+    for (int c = threadIdx.x; c < r; c += blockDim.x) Lrow[c] = kn[clamp_ch(label_ch[g * r + c], dk)];
 }
 
 // grid: (U). slot_of[unit][block] = slot for every (block, slot, copy) entry.
@@ -75,35 +68,64 @@ __global__ __launch_bounds__(256) void slot_patch_kernel(const int32_t* __restri
     }
 }
 
-// grid: (U * K_b), one workgroup per plan entry. Patches slot_of and, for
-// an entry to be copied, pulls the block from the pinned host pool (mapped
-// into the GPU's address space) into its cache slot: 16-byte loads, four
-// per lane in flight, so a few hundred blocks keep many PCIe reads
-// outstanding at once.
+// grid: up to GATHER_WGS workgroups, each taking chunks of 64 plan entries
+// (one per lane of the first wave). A chunk patches slot_of for its entries
+// and lists the blocks to copy in LDS; its four waves then pull those
+// blocks from the pinned host pool (mapped into the GPU's address space)
+// into their cache slots, one block per wave at a time with the whole
+// block (eight 16-byte loads per lane for 8 KiB) in flight. The grid is
+// kept small so the next step's kernels find free compute units while the
+// copy waits on the host link.
+constexpr int GATHER_WGS = 256;
+constexpr int GATHER_CHUNK = 64;
 __global__ __launch_bounds__(256) void gather_kernel(const int32_t* __restrict__ plan,
                                                      const uint16_t* __restrict__ pool, uint16_t* __restrict__ cache,
                                                      int32_t* __restrict__ slot_of, int kb, int nb_cap, int n_slots,
-                                                     int blk_elems) {
-    const int e = blockIdx.x, unit = e / kb;
-    const int blk = plan[(size_t)e * 3], slot = plan[(size_t)e * 3 + 1], cp = plan[(size_t)e * 3 + 2];
-    if (blk < 0 || blk >= nb_cap || slot < 0 || slot >= n_slots) return;
-    if (threadIdx.x == 0) slot_of[(size_t)unit * nb_cap + blk] = slot;
-    if (!cp) return;
-    const uint4* src = reinterpret_cast<const uint4*>(pool + ((size_t)unit * nb_cap + blk) * blk_elems);
-    uint4* dst = reinterpret_cast<uint4*>(cache + ((size_t)unit * n_slots + slot) * blk_elems);
+                                                     int blk_elems, int n_entries) {
+    __shared__ int s_src[GATHER_CHUNK], s_dst[GATHER_CHUNK];
+    __shared__ int s_n;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int n16 = blk_elems / 8;
-    for (int base = 0; base < n16; base += 4 * 256) {
-        uint4 v[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int i = base + k * 256 + (int)threadIdx.x;
-            if (i < n16) v[k] = src[i];
+    for (int base = blockIdx.x * GATHER_CHUNK; base < n_entries; base += gridDim.x * GATHER_CHUNK) {
+        if (threadIdx.x == 0) s_n = 0;
+        __syncthreads();
+        if (wave == 0) {
+            const int e = base + lane;
+            int blk = -1, slot = -1, cp = 0;
+            if (e < n_entries) {
+                blk = plan[(size_t)e * 3];
+                slot = plan[(size_t)e * 3 + 1];
+                cp = plan[(size_t)e * 3 + 2];
+            }
+            const bool ok = e < n_entries && blk >= 0 && blk < nb_cap && slot >= 0 && slot < n_slots;
+            const int unit = e / kb;
+            if (ok) slot_of[(size_t)unit * nb_cap + blk] = slot;
+            if (ok && cp) {
+                const int i = atomicAdd(&s_n, 1);
+                s_src[i] = unit * nb_cap + blk;
+                s_dst[i] = unit * n_slots + slot;
+            }
         }
+        __syncthreads();
+        const int n = s_n;
+        for (int i = wave; i < n; i += 4) {
+            const uint4* src = reinterpret_cast<const uint4*>(pool + (size_t)s_src[i] * blk_elems);
+            uint4* dst = reinterpret_cast<uint4*>(cache + (size_t)s_dst[i] * blk_elems);
+            for (int c0 = 0; c0 < n16; c0 += 8 * 64) {
+                uint4 v[8];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int i = base + k * 256 + (int)threadIdx.x;
-            if (i < n16) dst[i] = v[k];
+                for (int k = 0; k < 8; ++k) {
+                    const int c = c0 + k * 64 + lane;
+                    if (c < n16) v[k] = src[c];
+                }
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const int c = c0 + k * 64 + lane;
+                    if (c < n16) dst[c] = v[k];
+                }
+            }
         }
+        __syncthreads();   // s_n and the lists are reused by the next chunk
     }
 }
 
@@ -112,7 +134,7 @@ __global__ __launch_bounds__(256) void gather_kernel(const int32_t* __restrict__
 hipError_t launch_append_slot(const Shape& s, int n_slots, const uint16_t* k_new, const uint16_t* v_new,
                               uint16_t* cache, uint16_t* meta, uint16_t* klabel, const int32_t* label_ch,
                               const int32_t* ctx_len, hipStream_t st) {
-    hipLaunchKernelGGL(append_slot_kernel, dim3(s.B), dim3(256), 0, st, k_new, v_new, cache, meta, klabel,
+    hipLaunchKernelGGL(append_slot_kernel, dim3(s.B * s.Hkv), dim3(256), 0, st, k_new, v_new, cache, meta, klabel,
                        label_ch, ctx_len, s.Hkv, s.dk, s.dv, s.valias, s.bs, s.r, s.max_ctx, s.nb_cap, n_slots);
     return hipGetLastError();
 }
@@ -203,8 +225,9 @@ hipError_t offload_copy(const Shape& s, int n_slots, const uint16_t* host_pool, 
         if (e != hipSuccess) return e;
         e = hipMemcpyAsync(plan_dev, plan, (size_t)U * kb * 3 * sizeof(int32_t), hipMemcpyHostToDevice, cs);
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(gather_kernel, dim3(U * kb), dim3(256), 0, cs, plan_dev, pool_dev, cache, slot_of, kb,
-                           s.nb_cap, n_slots, (int)blk_elems);
+        const int n_entries = U * kb, chunks = (n_entries + GATHER_CHUNK - 1) / GATHER_CHUNK;
+        hipLaunchKernelGGL(gather_kernel, dim3(chunks < GATHER_WGS ? chunks : GATHER_WGS), dim3(256), 0, cs,
+                           plan_dev, pool_dev, cache, slot_of, kb, s.nb_cap, n_slots, (int)blk_elems, n_entries);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     } else {
