@@ -205,8 +205,12 @@ hipError_t launch_t(const Shape& s, const uint16_t* q, uint16_t* meta, const int
                     float* score, const Append& ap, hipStream_t st) {
     constexpr int TILES_WG = SCORE_WAVES / KSPLIT;
     const long tiles = (long)((s.nb_cap + 15) / 16) * s.B * s.Hkv;
-    // aim for ~2048 workgroups (8 per CU) before giving a wave more tiles
-    int tpw = (int)((tiles / TILES_WG + 2047) / 2048);
+    // aim for ~2048 workgroups (8 per CU) before giving a wave more tiles;
+    // split-row workgroups (two waves per SIMD at most) are capped at one
+    // per CU and take several tiles each, the next tile's rows in flight
+    // while the current one is multiplied
+    const long target = KSPLIT > 1 ? 256 : 2048;
+    int tpw = (int)((tiles / TILES_WG + target - 1) / target);
     tpw = tpw < 1 ? 1 : (tpw > 8 ? 8 : tpw);
     const int per_wg = TILES_WG * tpw * 16;
     dim3 grid((s.nb_cap + per_wg - 1) / per_wg, s.B * s.Hkv);
