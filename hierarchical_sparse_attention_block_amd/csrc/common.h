@@ -54,10 +54,38 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
+// Cross-row partners on gfx950 without LDS: v_permlane16_swap pairs row 2i
+// with row 2i+1 (lane ^ 16), v_permlane32_swap pairs the two wave halves
+// (lane ^ 32). Both results of the swap hold the two partners' values.
+__device__ __forceinline__ float max_xor16(float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Inclusive prefix sum over the 64 lanes: DPP row shifts by 1, 2, 4, 8
+// within each 16-lane row, then the row broadcasts of lanes 15 and 31.
+__device__ __forceinline__ uint32_t wave_scan_dpp(uint32_t v) {
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false);
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false);
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false);
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false);
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false);
+    return v;
+}
+
 // Sum over aligned groups of N lanes (N = 8, 16 or 32); every lane of a
 // group gets the group's total. Within a 16-lane row the partners come from
 // DPP lane swaps (lane ^ 1, lane ^ 2, half-row mirror, row mirror); the
-// step across two rows is a lane shuffle.
+// step across two rows is a permlane16 swap.
 template <int N>
 __device__ __forceinline__ float group_sum(float v) {
     static_assert(N == 8 || N == 16 || N == 32, "group size");
@@ -65,7 +93,7 @@ __device__ __forceinline__ float group_sum(float v) {
     v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
     v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
     if (N >= 16) v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));
-    if (N == 32) v += __shfl_xor(v, 16);
+    if (N == 32) v = sum_xor16(v);
     return v;
 }
 

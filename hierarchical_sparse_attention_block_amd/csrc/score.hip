@@ -187,8 +187,8 @@ __global__ __launch_bounds__(256) void block_score_kernel(
                 for (int i = 0; i < 4; ++i)
                     if (mt * 16 + (lane >> 4) * 4 + i < G) v = fmaxf(v, tot[mt][i]);
             if (G > 4) {   // heads 4.. sit in the other 16-lane rows
-                v = fmaxf(v, __shfl_xor(v, 16));
-                v = fmaxf(v, __shfl_xor(v, 32));
+                v = max_xor16(v);
+                v = max_xor32(v);
             }
             const int jl = tile_j0(t) + (lane & 15);
             if (lane < 16 && jl < nb) Su[jl] = v;

@@ -141,8 +141,8 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
                     if (16 + h < G) v = fmaxf(v, acc1[e]);
                 }
                 if (G > 4) {   // heads 4.. sit in the other 16-lane rows
-                    v = fmaxf(v, __shfl_xor(v, 16));
-                    v = fmaxf(v, __shfl_xor(v, 32));
+                    v = max_xor16(v);
+                    v = max_xor32(v);
                 }
                 const int i = tile * 16 + (lane & 15);
                 if (lane < 16 && i < ncand) {

@@ -20,15 +20,7 @@ __device__ __forceinline__ uint32_t wave_minmax(uint32_t v) {
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave.
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t y = __shfl_up(v, o);
-        if (lane >= o) v += y;
-    }
-    return v;
-}
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) { return wave_scan_dpp(v); }
 
 // NW waves hold up to NW*64*PT keys in registers; with pt <= PT slots in
 // use, key j of lane `lane` in wave w is entry i = (w*pt + j)*64 + lane.
@@ -119,9 +111,7 @@ struct TopK {
                 uint32_t loc = 0;
 #pragma unroll
                 for (int e = 0; e < BPT; ++e) loc += sm.hist[NBIN - 1 - (w * BPW + lane * BPT + e)];
-                uint32_t tot = loc;
-#pragma unroll
-                for (int o = 32; o >= 1; o >>= 1) tot += __shfl_xor(tot, o);
+                const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)wave_scan_dpp(loc), 63);
                 if (lane == 0) red[11 * NW + w] = tot;
                 __syncthreads();
                 uint32_t above = 0;
