@@ -464,6 +464,39 @@ def main():
         if c.get("source_hash") == source_hash(SCORE_SOURCES):
             traffic = c.get("bytes_per_launch")
 
+    # full attention over every token on the same caches: the operator the
+    # sparse step replaces (the pages report the sparse speedup over it)
+    dense = None
+    dws = H.dense_workspace_bytes(d)
+    if dws:
+        dout = torch.empty(w.batch * w.n_q_heads * w.d_v, device="cuda")
+        dlse = torch.empty(w.batch * w.n_q_heads, device="cuda")
+        dwsb = torch.empty(dws, dtype=torch.uint8, device="cuda")
+        gd = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            H.dense_attend(d, base["q"], reps[0].K, reps[0].V, base["ctx"], dout, dlse, dwsb, stream=stream)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(gd, stream=stream):
+            for r in reps:
+                H.dense_attend(d, base["q"], r.K, r.V, base["ctx"], dout, dlse, dwsb, stream=stream)
+        with torch.cuda.stream(stream):
+            gd.replay()
+        torch.cuda.synchronize()
+        n_rep = max(1, args.steps // (4 * R))
+        with torch.cuda.stream(stream):
+            ev0.record(stream)
+            for _ in range(n_rep):
+                gd.replay()
+            ev1.record(stream)
+        torch.cuda.synchronize()
+        ms_dense = ev0.elapsed_time(ev1) / (n_rep * R)
+        dbytes = w.units * w.ctx * (w.d_k + w.d_v) * 2
+        dense = {"ms_per_call": round(ms_dense, 6), "kv_bytes": dbytes,
+                 "achieved_gbs": round(dbytes / (ms_dense * 1e-3) / 1e9, 1),
+                 "speedup_sparse_step_vs_dense": round(ms_dense / ms_step, 3)}
+        log(f"[bench] dense attention {ms_dense * 1e3:.1f} us/call, sparse step {ms_step * 1e3:.1f} us "
+            f"({ms_dense / ms_step:.2f}x)")
+
     queries = w.batch * w.n_q_heads
     value = queries / (ms_step * 1e-3)
     res = {
@@ -481,6 +514,8 @@ def main():
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes": kb, "us_per_launch": round(us_score, 3)},
     }
+    if dense is not None:
+        res["dense_reference"] = dense
     if not args.no_cpu:
         log("[bench] timing the CPU oracle on a bounded sample")
         res["cpu_baseline"] = cpu_baseline(w, host)

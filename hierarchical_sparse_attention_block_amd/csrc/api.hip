@@ -189,6 +189,24 @@ int hsab_decode_step(const hsab_dims* dims, const uint16_t* q, const uint16_t* k
                                     reinterpret_cast<float*>(w + L.part_acc), nullptr, out, lse, stream));
 }
 
+size_t hsab_dense_workspace_bytes(const hsab_dims* dims) {
+    if (check_dims(dims) != HSAB_OK) return 0;
+    const Shape s = make_shape(*dims);
+    return dense_supported(s) ? dense_workspace_bytes(s) : 0;
+}
+
+int hsab_dense_attend(const hsab_dims* dims, const uint16_t* q, const uint16_t* K, const uint16_t* V,
+                      const int32_t* ctx_len, float* out, float* lse, void* ws, size_t ws_bytes,
+                      hipStream_t stream) {
+    int rc = check_dims(dims);
+    if (rc) return rc;
+    if (!q || !K || !V || !ctx_len || !out || !lse) return HSAB_EINVAL;
+    const Shape s = make_shape(*dims);
+    if (!dense_supported(s)) return HSAB_EUNSUPPORTED;
+    if (!ws || ws_bytes < dense_workspace_bytes(s)) return HSAB_EINVAL;
+    return hip_status(launch_dense(s, q, K, V, ctx_len, out, lse, ws, stream));
+}
+
 int hsab_offload_append(const hsab_dims* dims, int32_t n_slots, const uint16_t* k_new,
                         const uint16_t* v_new, uint16_t* cache, uint16_t* meta, uint16_t* klabel,
                         const int32_t* label_ch, const int32_t* ctx_len, hipStream_t stream) {

@@ -29,14 +29,6 @@ namespace hsab {
 
 namespace {
 
-constexpr float LOG2E = 1.4426950408889634f;
-constexpr float LN2 = 0.6931471805599453f;
-
-__device__ __forceinline__ void widen8(uint4 v, float (&f)[8]) {
-    f[0] = lo_f32(v.x); f[1] = hi_f32(v.x); f[2] = lo_f32(v.y); f[3] = hi_f32(v.y);
-    f[4] = lo_f32(v.z); f[5] = hi_f32(v.z); f[6] = lo_f32(v.w); f[7] = hi_f32(v.w);
-}
-
 // Row index (in rows of d_k elements from the K base) of token t of unit,
 // or -1. Dense caches: unit*max_ctx + t. Block cache: slot s of the unit
 // spans slot_rows rows (key rows first, then value rows), found through
@@ -460,6 +452,13 @@ bool mla_shape(const Shape& s) {
 }
 
 }  // namespace
+
+hipError_t launch_combine(const Shape& s, const float* part_ml, const float* part_acc, float* out, float* lse,
+                          int n_splits, hipStream_t st) {
+    hipLaunchKernelGGL(combine_kernel, dim3(s.B * s.Hq), dim3(s.dv < 256 ? 128 : 256), 0, st, part_ml, part_acc,
+                       out, lse, s.dv, n_splits);
+    return hipGetLastError();
+}
 
 bool attend_supported(const Shape& s) {
     if (mla_shape(s)) return true;

@@ -11,6 +11,8 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int WAVE = 64;
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
 
 __device__ __forceinline__ float bf16_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
@@ -52,6 +54,12 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 // a.lo*b.lo + a.hi*b.hi + c for packed bf16 pairs, fp32 accumulate
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// Eight packed bf16 widened to fp32, exactly.
+__device__ __forceinline__ void widen8(uint4 v, float (&f)[8]) {
+    f[0] = lo_f32(v.x); f[1] = hi_f32(v.x); f[2] = lo_f32(v.y); f[3] = hi_f32(v.y);
+    f[4] = lo_f32(v.z); f[5] = hi_f32(v.z); f[6] = lo_f32(v.w); f[7] = hi_f32(v.w);
 }
 
 // Cross-row partners on gfx950 without LDS: v_permlane16_swap pairs row 2i

@@ -52,6 +52,18 @@ hipError_t launch_attend(const Shape& s, const uint16_t* q, const uint16_t* K, c
                          float* part_ml, float* part_acc, int32_t* arrivals, float* out, float* lse,
                          hipStream_t st);
 
+// Merge of per-split (max, sum, weighted values) partials into out / lse.
+hipError_t launch_combine(const Shape& s, const float* part_ml, const float* part_acc, float* out, float* lse,
+                          int n_splits, hipStream_t st);
+
+// Dense decode attention over every token of the context (dense.hip): the
+// full-attention reference the sparse operator is measured against.
+constexpr int DENSE_CHUNK = 1024;     // tokens per workgroup
+bool dense_supported(const Shape& s);
+size_t dense_workspace_bytes(const Shape& s);
+hipError_t launch_dense(const Shape& s, const uint16_t* q, const uint16_t* K, const uint16_t* V,
+                        const int32_t* ctx_len, float* out, float* lse, void* ws, hipStream_t st);
+
 // offload engine (offload.hip); per-step timing events kept for this many steps
 constexpr int TIMING_RING = 32;
 hipError_t launch_append_slot(const Shape& s, int n_slots, const uint16_t* k_new, const uint16_t* v_new,

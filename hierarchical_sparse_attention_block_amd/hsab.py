@@ -26,7 +26,7 @@ EXPORTS = ("hsab_workspace_bytes", "hsab_status_string", "hsab_last_hip_error", 
            "hsab_score_blocks", "hsab_select_blocks", "hsab_select_tokens", "hsab_sparse_attend",
            "hsab_decode_step", "hsab_offload_append", "hsab_offload_plan", "hsab_offload_copy", "hsab_offload_create",
            "hsab_offload_destroy", "hsab_offload_begin", "hsab_offload_step", "hsab_offload_timing",
-           "hsab_offload_selection")
+           "hsab_offload_selection", "hsab_dense_workspace_bytes", "hsab_dense_attend")
 
 
 class Dims(ctypes.Structure):
@@ -83,6 +83,8 @@ class OffloadStats(ctypes.Structure):
 
 
 _lib.hsab_offload_create.argtypes = [_D, _i32, _i32, ctypes.POINTER(_vp)]
+_lib.hsab_dense_workspace_bytes.argtypes = [_D]
+_lib.hsab_dense_attend.argtypes = [_D, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
 _lib.hsab_offload_destroy.argtypes = [_vp]
 _lib.hsab_offload_begin.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp]
 _lib.hsab_offload_step.argtypes = [_vp] * 16 + [_sz, _vp, _vp, ctypes.POINTER(OffloadStats)]
@@ -91,6 +93,7 @@ _lib.hsab_offload_selection.argtypes = [_vp, _vp]
 for _f in EXPORTS[3:]:
     getattr(_lib, _f).restype = ctypes.c_int
 _lib.hsab_offload_destroy.restype = None
+_lib.hsab_dense_workspace_bytes.restype = _sz
 
 
 class HsabError(RuntimeError):
@@ -374,6 +377,27 @@ class OffloadEngine:
         outb = torch.empty(d.batch * d.n_kv_heads * d.k_blocks, dtype=torch.int32)
         _check("hsab_offload_selection", _lib.hsab_offload_selection(self._h, ctypes.c_void_p(outb.data_ptr())))
         return outb.view(d.batch, d.n_kv_heads, d.k_blocks)
+
+
+def dense_workspace_bytes(d: Dims) -> int:
+    return int(_lib.hsab_dense_workspace_bytes(ctypes.byref(d)))
+
+
+def alloc_dense_workspace(d: Dims, device="cuda") -> torch.Tensor:
+    n = dense_workspace_bytes(d)
+    if n == 0:
+        raise ValueError(f"dense attention unsupported or invalid dims {d}")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def dense_attend(d: Dims, q, K, V, ctx_len, out, lse, ws, stream=None):
+    """Full attention over every token (the reference the sparse operator
+    is measured against)."""
+    s = _sizes(d)
+    _check("hsab_dense_attend", _lib.hsab_dense_attend(
+        ctypes.byref(d), _buf("q", q, _u16, s["q"]), _buf("K", K, _u16, s["K"]), _buf("V", V, _u16, s["V"]),
+        _buf("ctx_len", ctx_len, _i, s["ctx"]), _buf("out", out, _f, s["out"]), _buf("lse", lse, _f, s["lse"]),
+        _buf("ws", ws, torch.uint8, dense_workspace_bytes(d)), ctypes.c_size_t(ws.numel()), _stream(stream)))
 
 
 def raw_call(name, *args):

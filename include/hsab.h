@@ -172,6 +172,19 @@ int hsab_decode_step(const hsab_dims* dims, const uint16_t* q, const uint16_t* k
                      int32_t* blk_idx, int32_t* tok_idx, float* out, float* lse,
                      void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* ------------------------------------------------------------ dense reference
+ * Full attention over every token, the operator the sparse step replaces
+ * (the pages report the sparse operator's speedup over full attention
+ * [abstract; de 4; es 4]):
+ *   out[b][h] = sum_{t < n} softmax_t(sm_scale * q_h . K_t) V_t, n = ctx_len[b]
+ * with lse as for hsab_sparse_attend. K and V are the dense caches; k_blocks,
+ * k_tokens, block and r are ignored. Supported for d_k == d_v in
+ * {64, 128, 256} and G in {1, 2, 4, 8} (HSAB_EUNSUPPORTED otherwise). */
+size_t hsab_dense_workspace_bytes(const hsab_dims* dims);   /* 0 if dims invalid or unsupported */
+int hsab_dense_attend(const hsab_dims* dims, const uint16_t* q, const uint16_t* K, const uint16_t* V,
+                      const int32_t* ctx_len, float* out, float* lse, void* ws, size_t ws_bytes,
+                      hipStream_t stream);
+
 /* ------------------------------------------------------------------ offload
  * Asynchronous offload engine [de 2.B; es 2.B]: the whole KV cache lives in
  * pinned host memory; a GPU block cache holds the blocks the attention reads.
