@@ -490,7 +490,7 @@ def main():
             ev1.record(stream)
         torch.cuda.synchronize()
         ms_dense = ev0.elapsed_time(ev1) / (n_rep * R)
-        dbytes = w.units * w.ctx * (w.d_k + w.d_v) * 2
+        dbytes = w.units * w.ctx * (w.d_k + (0 if w.v_alias_k else w.d_v)) * 2
         dense = {"ms_per_call": round(ms_dense, 6), "kv_bytes": dbytes,
                  "achieved_gbs": round(dbytes / (ms_dense * 1e-3) / 1e9, 1),
                  "speedup_sparse_step_vs_dense": round(ms_dense / ms_step, 3)}

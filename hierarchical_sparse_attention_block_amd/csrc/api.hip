@@ -200,8 +200,9 @@ int hsab_dense_attend(const hsab_dims* dims, const uint16_t* q, const uint16_t* 
                       hipStream_t stream) {
     int rc = check_dims(dims);
     if (rc) return rc;
-    if (!q || !K || !V || !ctx_len || !out || !lse) return HSAB_EINVAL;
+    if (!q || !K || !ctx_len || !out || !lse) return HSAB_EINVAL;
     const Shape s = make_shape(*dims);
+    if (!s.valias && !V) return HSAB_EINVAL;
     if (!dense_supported(s)) return HSAB_EUNSUPPORTED;
     if (!ws || ws_bytes < dense_workspace_bytes(s)) return HSAB_EINVAL;
     return hip_status(launch_dense(s, q, K, V, ctx_len, out, lse, ws, stream));

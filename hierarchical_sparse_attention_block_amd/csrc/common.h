@@ -77,6 +77,10 @@ __device__ __forceinline__ float sum_xor16(float v) {
     const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
+__device__ __forceinline__ float sum_xor32(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 // Inclusive prefix sum over the 64 lanes: DPP row shifts by 1, 2, 4, 8
 // within each 16-lane row, then the row broadcasts of lanes 15 and 31.
@@ -123,6 +127,12 @@ __device__ __forceinline__ uint32_t f32_bf16_rne(float f) {
 }
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// Operand of the gfx950 transposing LDS read of four 16-bit elements.
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ __attribute__((address_space(3))) s16x4_t* lds_s16x4(const uint16_t* p) {
+    return (__attribute__((address_space(3))) s16x4_t*)(p);
+}
 __device__ __forceinline__ i16x4_t as_i16x4(uint2 v) { return __builtin_bit_cast(i16x4_t, v); }
 
 }  // namespace hsab

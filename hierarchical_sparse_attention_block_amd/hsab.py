@@ -395,7 +395,8 @@ def dense_attend(d: Dims, q, K, V, ctx_len, out, lse, ws, stream=None):
     is measured against)."""
     s = _sizes(d)
     _check("hsab_dense_attend", _lib.hsab_dense_attend(
-        ctypes.byref(d), _buf("q", q, _u16, s["q"]), _buf("K", K, _u16, s["K"]), _buf("V", V, _u16, s["V"]),
+        ctypes.byref(d), _buf("q", q, _u16, s["q"]), _buf("K", K, _u16, s["K"]),
+        _buf("V", V, _u16, s["V"], allow_none=bool(d.v_alias_k)),
         _buf("ctx_len", ctx_len, _i, s["ctx"]), _buf("out", out, _f, s["out"]), _buf("lse", lse, _f, s["lse"]),
         _buf("ws", ws, torch.uint8, dense_workspace_bytes(d)), ctypes.c_size_t(ws.numel()), _stream(stream)))
 

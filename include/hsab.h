@@ -177,9 +177,10 @@ int hsab_decode_step(const hsab_dims* dims, const uint16_t* q, const uint16_t* k
  * (the pages report the sparse operator's speedup over full attention
  * [abstract; de 4; es 4]):
  *   out[b][h] = sum_{t < n} softmax_t(sm_scale * q_h . K_t) V_t, n = ctx_len[b]
- * with lse as for hsab_sparse_attend. K and V are the dense caches; k_blocks,
- * k_tokens, block and r are ignored. Supported for d_k == d_v in
- * {64, 128, 256} and G in {1, 2, 4, 8} (HSAB_EUNSUPPORTED otherwise). */
+ * with lse as for hsab_sparse_attend. K and V are the dense caches (V NULL
+ * when values alias keys); k_blocks, k_tokens, block and r are ignored.
+ * Supported for the shapes hsab_sparse_attend supports (HSAB_EUNSUPPORTED
+ * otherwise). */
 size_t hsab_dense_workspace_bytes(const hsab_dims* dims);   /* 0 if dims invalid or unsupported */
 int hsab_dense_attend(const hsab_dims* dims, const uint16_t* q, const uint16_t* K, const uint16_t* V,
                       const int32_t* ctx_len, float* out, float* lse, void* ws, size_t ws_bytes,

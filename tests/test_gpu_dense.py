@@ -25,7 +25,8 @@ def _run(w, ctx):
     print(f"[dense] {w} ctx={list(ctx)}", flush=True)
     h = T.host_inputs(w, ctx_len=np.asarray(ctx, np.int32) + 1)   # prefill holds ctx tokens
     d = T.dims_of(w)
-    q, K, V = T.dev16(h["q"]), T.dev16(h["K"]), T.dev16(h["V"])
+    q, K = T.dev16(h["q"]), T.dev16(h["K"])
+    V = None if w.v_alias_k else T.dev16(h["V"])
     ctx_d = torch.from_numpy(np.asarray(ctx, np.int32)).cuda()
     out = torch.full((w.batch * w.n_q_heads * w.d_v,), float("nan"), device="cuda")
     lse = torch.full((w.batch * w.n_q_heads,), float("nan"), device="cuda")
@@ -40,7 +41,7 @@ def _run(w, ctx):
         for g in range(w.n_kv_heads):
             qq = O.bf16_to_f64(h["q"][b, g * G:(g + 1) * G])
             Kf = O.bf16_to_f64(h["K"][b, g, :n])
-            Vf = O.bf16_to_f64(h["V"][b, g, :n])
+            Vf = Kf[:, :w.d_v] if w.v_alias_k else O.bf16_to_f64(h["V"][b, g, :n])
             o, l = O.attend(qq, Kf, Vf, w.sm_scale)
             err = np.max(np.abs(o - out[b, g * G:(g + 1) * G]))
             assert err <= T.OUT_ATOL, f"unit ({b},{g}) n={n}: max-abs {err:.3g}"
@@ -81,7 +82,17 @@ def test_dense_equals_sparse_dense_limit():
     np.testing.assert_allclose(lse, r["lse"], rtol=1e-5)
 
 
-def test_dense_rejects_latent_layout():
+@pytest.mark.parametrize("B,dk,dv,ctx", [(2, 576, 512, [2100, 33]), (1, 1024, 512, [1031]),
+                                         (3, 128, 64, [1, 1056, 32])])
+def test_dense_latent(B, dk, dv, ctx):
+    """Absorbed latent layout (32 query heads on one latent key, values its
+    first d_v dims): ragged rounds of 32 tokens and 1024-token chunks."""
+    w = _wl(batch=B, n_q_heads=32, n_kv_heads=1, d_k=dk, d_v=dv, v_alias_k=True, block=32, r=32,
+            k_blocks=4, k_tokens=64, ctx=max(ctx), max_ctx=max(ctx))
+    _run(w, ctx)
+
+
+def test_dense_rejects_unsupported():
     from hierarchical_sparse_attention_block_amd import hsab as H
-    w = _wl(n_q_heads=32, n_kv_heads=1, d_k=576, d_v=512, v_alias_k=True, block=32, r=32)
+    w = _wl(n_q_heads=12, n_kv_heads=4, d_k=96, d_v=96)
     assert H.dense_workspace_bytes(T.dims_of(w)) == 0
