@@ -29,6 +29,7 @@ namespace hsab {
 namespace {
 
 constexpr int SCORE_WAVES = 4;
+constexpr int SPLIT_TILES = 4;   // tiles of a split-row workgroup
 
 // Token append of a decode step (optional): the new key/value rows land at
 // position n-1, the tail block's max/min widen to include the key (or start
@@ -50,7 +51,7 @@ __global__ __launch_bounds__(256) void block_score_kernel(
     const uint16_t* __restrict__ q, uint16_t* __restrict__ meta,
     const int32_t* __restrict__ ctx_len, float* __restrict__ score,
     int Hkv, int G, int dk, int bs, int max_ctx, int nb_cap, int tiles_per_wave, Append ap) {
-    __shared__ f32x4_t red[KSPLIT > 1 ? KSPLIT * MT * 64 : 1];
+    __shared__ f32x4_t red[KSPLIT > 1 ? SPLIT_TILES * KSPLIT * MT * 64 : 1];
 
     const int unit = blockIdx.y, b = unit / Hkv, g = unit % Hkv;
     int n = ctx_len[b];
@@ -106,17 +107,13 @@ __global__ __launch_bounds__(256) void block_score_kernel(
         return Mu + (size_t)jc * 2 * dk + (lane >> 4) * 8;
     };
 
-    // the first tile's rows are requested first; the A fragments follow
-    // Steps past this wave's range hold zeros in both operands: the matrix
-    // instructions below run for every step, so their products must vanish
-    // rather than depend on stale register contents.
-    uint4 cur[KSW], nxt[KSW];
-    {
-        const uint16_t* row = tile_row(0);
-#pragma unroll
-        for (int u = 0; u < KSW; ++u)
-            cur[u] = s_lo + u < s_hi ? ldg16(row + (s_lo + u) * 32) : make_uint4(0u, 0u, 0u, 0u);
-    }
+    // A fragments are requested first (they come from L2), then the tile
+    // rows, so converting the fragments waits for none of the rows. Every
+    // load is unconditional: steps past this wave's range re-read its last
+    // step and meet zero A fragments (the matrix instructions run for every
+    // step, so their products must vanish rather than depend on stale
+    // registers), and tiles past the workgroup's range re-read its last
+    // tile, which keeps each wait count exact.
     const uint16_t* qg = q + ((size_t)b * Hkv * G + (size_t)g * G) * dk;
     uint4 af[MT][KSW];
 #pragma unroll
@@ -125,32 +122,39 @@ __global__ __launch_bounds__(256) void block_score_kernel(
         const uint16_t* qm = qg + (size_t)(m < G ? m : 0) * dk;
 #pragma unroll
         for (int u = 0; u < KSW; ++u) {
-            const int c = (s_lo + u) * 4 + (lane >> 4);
-            af[mt][u] = make_uint4(0u, 0u, 0u, 0u);
-            if (m < G && s_lo + u < s_hi) af[mt][u] = ldg16(qm + (c >= CH ? c - CH : c) * 8);
+            const int st = s_lo + u < s_hi ? s_lo + u : s_hi - 1;
+            const int c = st * 4 + (lane >> 4);
+            af[mt][u] = ldg16(qm + (c >= CH ? c - CH : c) * 8);
         }
     }
+    auto load_tile = [&](int t, uint4 (&dst)[KSW]) {
+        const uint16_t* row = tile_row(t < tiles_per_wave ? t : tiles_per_wave - 1);
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+        for (int u = 0; u < KSW; ++u) dst[u] = ldg16(row + (s_lo + u < s_hi ? s_lo + u : s_hi - 1) * 32);
+    };
+    // split-row workgroups take SPLIT_TILES tiles, all requested at once
+    constexpr int NBUF = KSPLIT > 1 ? SPLIT_TILES : 2;
+    uint4 tl[NBUF][KSW];
+    load_tile(0, tl[0]);
+    if constexpr (KSPLIT > 1) {
+#pragma unroll
+        for (int d = 1; d < NBUF; ++d) load_tile(d, tl[d]);
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const bool head = mt * 16 + (lane & 15) < G;
 #pragma unroll
         for (int u = 0; u < KSW; ++u) {
             const uint4 r = af[mt][u];
             const bool lower = (s_lo + u) * 4 + (lane >> 4) >= CH;
-            af[mt][u] = lower ? make_uint4(bf16x2_neg(r.x), bf16x2_neg(r.y), bf16x2_neg(r.z), bf16x2_neg(r.w))
-                              : make_uint4(bf16x2_pos(r.x), bf16x2_pos(r.y), bf16x2_pos(r.z), bf16x2_pos(r.w));
+            af[mt][u] = !head || s_lo + u >= s_hi ? make_uint4(0u, 0u, 0u, 0u)
+                        : lower ? make_uint4(bf16x2_neg(r.x), bf16x2_neg(r.y), bf16x2_neg(r.z), bf16x2_neg(r.w))
+                                : make_uint4(bf16x2_pos(r.x), bf16x2_pos(r.y), bf16x2_pos(r.z), bf16x2_pos(r.w));
         }
+    }
 
-    for (int t = 0; t < tiles_per_wave; ++t) {
-        const bool live = tile_j0(t) < nb;
-        if (KSPLIT == 1 && !live) break;
-        if (KSPLIT > 1 && tile_j0(t) >= nb) break;   // uniform over the workgroup
-        const bool more = t + 1 < tiles_per_wave && tile_j0(t + 1) < nb;
-        if (more) {
-            const uint16_t* row1 = tile_row(t + 1);
-#pragma unroll
-            for (int u = 0; u < KSW; ++u)
-                nxt[u] = s_lo + u < s_hi ? ldg16(row1 + (s_lo + u) * 32) : make_uint4(0u, 0u, 0u, 0u);
-        }
+    // partial bound tile of this wave's steps
+    auto mul_tile = [&](const uint4 (&rows)[KSW], f32x4_t (&tot)[MT]) {
         // two accumulators per head tile shorten the dependent MFMA chain
         f32x4_t acc[MT][2];
 #pragma unroll
@@ -159,43 +163,65 @@ __global__ __launch_bounds__(256) void block_score_kernel(
         for (int u = 0; u < KSW; ++u) {
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
-                acc[mt][u & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(af[mt][u]), as_bf16x8(cur[u]),
+                acc[mt][u & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(af[mt][u]), as_bf16x8(rows[u]),
                                                                        acc[mt][u & 1], 0, 0, 0);
         }
-        f32x4_t tot[MT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) tot[mt] = acc[mt][0] + acc[mt][1];
-        bool emit = true;
-        if (KSPLIT > 1) {
+    };
+    // group maximum of the bound of tile t's blocks, stored
+    auto emit = [&](int t, const f32x4_t (&tot)[MT]) {
+        float v = -INFINITY;
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) red[(wave * MT + mt) * 64 + lane] = tot[mt];
-            __syncthreads();
-            emit = wave == 0;
-            if (emit) {
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                    for (int w = 1; w < KSPLIT; ++w) tot[mt] += red[(w * MT + mt) * 64 + lane];
-            }
-            __syncthreads();   // red is reused by the next tile
+            for (int i = 0; i < 4; ++i)
+                if (mt * 16 + (lane >> 4) * 4 + i < G) v = fmaxf(v, tot[mt][i]);
+        if (G > 4) {   // heads 4.. sit in the other 16-lane rows
+            v = max_xor16(v);
+            v = max_xor32(v);
         }
-        if (emit) {
-            float v = -INFINITY;
+        const int jl = tile_j0(t) + (lane & 15);
+        if (lane < 16 && jl < nb) Su[jl] = v;
+    };
+
+    if constexpr (KSPLIT > 1) {
+        // every wave multiplies its steps of each tile as the rows land, the
+        // partial tiles meet in LDS once, and wave d adds up and emits tile d
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
+        for (int d = 0; d < NBUF; ++d) {
+            f32x4_t tot[MT];
+            mul_tile(tl[d], tot);
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if (mt * 16 + (lane >> 4) * 4 + i < G) v = fmaxf(v, tot[mt][i]);
-            if (G > 4) {   // heads 4.. sit in the other 16-lane rows
-                v = max_xor16(v);
-                v = max_xor32(v);
-            }
-            const int jl = tile_j0(t) + (lane & 15);
-            if (lane < 16 && jl < nb) Su[jl] = v;
+            for (int mt = 0; mt < MT; ++mt) red[((d * KSPLIT + wave) * MT + mt) * 64 + lane] = tot[mt];
         }
-        if (more) {
+        __syncthreads();
+        static_assert(NBUF <= SCORE_WAVES, "one emitting wave per tile");
+        if (wave < NBUF && tile_j0(wave) < nb) {
+            f32x4_t tot[MT];
 #pragma unroll
-            for (int u = 0; u < KSW; ++u) cur[u] = nxt[u];
+            for (int mt = 0; mt < MT; ++mt) {
+                tot[mt] = red[((wave * KSPLIT) * MT + mt) * 64 + lane];
+#pragma unroll
+                for (int w = 1; w < KSPLIT; ++w) tot[mt] += red[((wave * KSPLIT + w) * MT + mt) * 64 + lane];
+            }
+            emit(wave, tot);
+        }
+    } else {
+        // the next tile's rows are requested before the current tile is
+        // multiplied and awaited after it: one tile in flight per wave,
+        // which at this occupancy keeps the memory system busier than two
+        for (int t = 0; t < tiles_per_wave; ++t) {
+            if (tile_j0(t) >= nb) break;
+            const bool more = t + 1 < tiles_per_wave && tile_j0(t + 1) < nb;
+            if (more) load_tile(t + 1, tl[1]);
+            f32x4_t tot[MT];
+            mul_tile(tl[0], tot);
+            emit(t, tot);
+            if (more) {
+#pragma unroll
+                for (int u = 0; u < KSW; ++u) tl[0][u] = tl[1][u];
+            }
         }
     }
 }
@@ -206,12 +232,11 @@ hipError_t launch_t(const Shape& s, const uint16_t* q, uint16_t* meta, const int
     constexpr int TILES_WG = SCORE_WAVES / KSPLIT;
     const long tiles = (long)((s.nb_cap + 15) / 16) * s.B * s.Hkv;
     // aim for ~2048 workgroups (8 per CU) before giving a wave more tiles;
-    // split-row workgroups (two waves per SIMD at most) are capped at one
-    // per CU and take several tiles each, the next tile's rows in flight
-    // while the current one is multiplied
-    const long target = KSPLIT > 1 ? 256 : 2048;
+    // split-row workgroups take SPLIT_TILES tiles each, all in flight at once
+    const long target = 2048;
     int tpw = (int)((tiles / TILES_WG + target - 1) / target);
     tpw = tpw < 1 ? 1 : (tpw > 8 ? 8 : tpw);
+    if (KSPLIT > 1) tpw = SPLIT_TILES;
     const int per_wg = TILES_WG * tpw * 16;
     dim3 grid((s.nb_cap + per_wg - 1) / per_wg, s.B * s.Hkv);
     hipLaunchKernelGGL((block_score_kernel<MT, KSW, KSPLIT>), grid, dim3(64 * SCORE_WAVES), 0, st, q, meta,
