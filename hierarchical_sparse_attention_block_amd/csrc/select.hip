@@ -5,11 +5,15 @@
 //     top-K_t (fine stage, Double-Sparsity style; gist.science/de explainer
 //     section 2.A "Stufe 2", gist.science/es section 2.A item 2).
 // Label score of token t: max over the group's query heads of
-// sum_c q_h[label_ch[c]] * klabel[t][c], on v_mfma_f32_16x16x16_bf16 with
-// 16 candidate tokens per tile (lane l: token l % 16, 4 channels of step s
-// at 16*s + 4*(l/16)); the group's label-channel queries are A. Each wave
-// issues eight label-row loads before its MFMAs. Selection keeps all
-// scores in registers and LDS (TopK in topk.h).
+// sum_c q_h[label_ch[c]] * klabel[t][c] on the matrix cores with 16
+// candidate tokens per tile and the group's label-channel queries as A.
+// With 16 label channels a step is v_mfma_f32_16x16x16_bf16 (lane l: token
+// l % 16, channels 4*(l/16)..+3, an 8-byte load); with 32 or more it is
+// v_mfma_f32_16x16x32_bf16 (channels 32*s + 8*(l/16)..+7, a 16-byte load),
+// which halves the load round trips of long label rows. Each wave issues
+// eight label-row loads before its MFMAs. Selection keeps all scores in
+// registers and LDS (TopK in topk.h).
+#include <type_traits>
 #include "common.h"
 #include "kernels.h"
 #include "topk.h"
@@ -21,7 +25,8 @@ namespace {
 constexpr int SEL_WAVES = 16;
 constexpr int SEL_THREADS = SEL_WAVES * 64;
 
-template <int PT>
+// KK: channels per matrix step (16, or 32 when r >= 32)
+template <int PT, int KK>
 __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
     int mode, const uint16_t* __restrict__ q, const float* __restrict__ blk_score,
     const uint16_t* __restrict__ klabel, const int32_t* __restrict__ label_ch,
@@ -33,7 +38,10 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
     auto slot_of = [&](int i) { return bs_shift >= 0 ? (i >> bs_shift) : i / bs; };
     __shared__ uint32_t s_key[MAX_CAND];
     __shared__ int32_t s_blk[MAX_KB];
-    __shared__ uint2 s_qa[2 * (MAX_R / 16) * 64];
+    // A fragments [head tile][step][lane]: uint2 per lane for KK = 16,
+    // uint4 for KK = 32 (same bytes)
+    __shared__ uint4 s_qa4[2 * (MAX_R / 32) * 64];
+    uint2* s_qa = reinterpret_cast<uint2*>(s_qa4);
     __shared__ typename Sel::Smem s_sel;
 
     const int unit = blockIdx.x, b = unit / Hkv, g = unit % Hkv;
@@ -59,20 +67,29 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
 
     // label-channel A fragments (independent of the block selection)
     const int MT = (G + 15) / 16;
-    const int KSr = r / 16;
+    const int KSr = r / KK;               // matrix steps per label row
+    constexpr int CPL = KK / 4;           // channels per lane per step
+    constexpr int SMAX = MAX_R / KK;      // step stride of the fragment table
     if (mode & 2) {
         const int32_t* lab = label_ch + g * r;
         for (int e = threadIdx.x; e < MT * KSr * 64; e += SEL_THREADS) {
             const int l = e & 63, s = (e >> 6) % KSr, mt = e / (64 * KSr);
             const int m = mt * 16 + (l & 15);
-            const int c0 = s * 16 + (l >> 4) * 4;
-            uint32_t x = 0, y = 0;
+            const int c0 = s * KK + (l >> 4) * CPL;
+            uint32_t x[CPL / 2];
+#pragma unroll
+            for (int j = 0; j < CPL / 2; ++j) x[j] = 0u;
             if (m < G) {
                 const uint16_t* qh = qg + (size_t)m * dk;
-                x = (uint32_t)qh[clamp_ch(lab[c0], dk)] | ((uint32_t)qh[clamp_ch(lab[c0 + 1], dk)] << 16);
-                y = (uint32_t)qh[clamp_ch(lab[c0 + 2], dk)] | ((uint32_t)qh[clamp_ch(lab[c0 + 3], dk)] << 16);
+#pragma unroll
+                for (int j = 0; j < CPL / 2; ++j)
+                    x[j] = (uint32_t)qh[clamp_ch(lab[c0 + 2 * j], dk)] |
+                           ((uint32_t)qh[clamp_ch(lab[c0 + 2 * j + 1], dk)] << 16);
             }
-            s_qa[(mt * (MAX_R / 16) + s) * 64 + l] = make_uint2(x, y);
+            if constexpr (KK == 32)
+                s_qa4[(mt * SMAX + s) * 64 + l] = make_uint4(x[0], x[1], x[2], x[3]);
+            else
+                s_qa[(mt * SMAX + s) * 64 + l] = make_uint2(x[0], x[1]);
         }
     }
 
@@ -104,12 +121,13 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
     const uint16_t* Lu = klabel + (size_t)unit * max_ctx * r;
     float* TS = tok_score ? tok_score + (size_t)unit * ncand : nullptr;
     const int n_tiles = (ncand + 15) / 16;
-    // eight 8-byte label loads in flight per lane: load u feeds step
-    // u % KSr of tile u / KSr of the batch (KSr is a power of two <= 8)
+    // eight label loads in flight per lane: load u feeds step u % KSr of
+    // tile u / KSr of the batch (KSr is a power of two <= 8)
     const int lg = KSr == 1 ? 0 : KSr == 2 ? 1 : KSr == 4 ? 2 : 3;
     const int tb = 8 >> lg;                         // tiles per batch
+    using Frag = typename std::conditional<KK == 32, uint4, uint2>::type;
     for (int t0 = w; t0 < n_tiles; t0 += SEL_WAVES * tb) {
-        uint2 bf[8];
+        Frag bf[8];
         uint32_t vmask = 0;   // bit u: the token this lane loads for load u is valid
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
@@ -120,18 +138,30 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
             const int pos = blk * bs + off;
             const bool valid = blk >= 0 && blk < nb && pos < n;
             vmask |= (valid ? 1u : 0u) << u;
-            bf[u] = ldg8(Lu + (size_t)(valid ? pos : 0) * r + (lane >> 4) * 4 + st * 16);
+            const uint16_t* src = Lu + (size_t)(valid ? pos : 0) * r + (lane >> 4) * CPL + st * KK;
+            if constexpr (KK == 32)
+                bf[u] = ldg16(src);
+            else
+                bf[u] = ldg8(src);
         }
         f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             const int tile = t0 + (u >> lg) * SEL_WAVES, st = u & (KSr - 1);
             if (st == 0) acc0 = acc1 = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            const i16x4_t bfrag = as_i16x4(bf[u]);
-            acc0 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_i16x4(s_qa[st * 64 + lane]), bfrag, acc0, 0, 0, 0);
-            if (MT > 1)
-                acc1 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-                    as_i16x4(s_qa[((MAX_R / 16) + st) * 64 + lane]), bfrag, acc1, 0, 0, 0);
+            if constexpr (KK == 32) {
+                const bf16x8_t bfrag = as_bf16x8(bf[u]);
+                acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(s_qa4[st * 64 + lane]), bfrag, acc0, 0, 0, 0);
+                if (MT > 1)
+                    acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(s_qa4[(SMAX + st) * 64 + lane]), bfrag,
+                                                                   acc1, 0, 0, 0);
+            } else {
+                const i16x4_t bfrag = as_i16x4(bf[u]);
+                acc0 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_i16x4(s_qa[st * 64 + lane]), bfrag, acc0, 0, 0, 0);
+                if (MT > 1)
+                    acc1 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_i16x4(s_qa[(SMAX + st) * 64 + lane]), bfrag,
+                                                                     acc1, 0, 0, 0);
+            }
             if (st == KSr - 1 && tile < n_tiles) {
                 float v = -INFINITY;
 #pragma unroll
@@ -175,9 +205,15 @@ template <int PT>
 hipError_t launch_t(const Shape& s, int mode, const uint16_t* q, const float* blk_score,
                     const uint16_t* klabel, const int32_t* label_ch, const int32_t* ctx_len,
                     int32_t* blk_idx, int32_t* tok_idx, float* tok_score, int32_t* arrivals, hipStream_t st) {
-    hipLaunchKernelGGL((select_kernel<PT>), dim3(s.B * s.Hkv), dim3(SEL_THREADS), 0, st, mode, q, blk_score,
-                       klabel, label_ch, ctx_len, blk_idx, tok_idx, tok_score, arrivals, s.Hkv, s.G, s.dk,
-                       s.bs, s.r, s.kb, s.kt, s.max_ctx, s.nb_cap, (s.bs & (s.bs - 1)) ? -1 : __builtin_ctz(s.bs));
+    const int shift = (s.bs & (s.bs - 1)) ? -1 : __builtin_ctz(s.bs);
+    if (s.r >= 32)
+        hipLaunchKernelGGL((select_kernel<PT, 32>), dim3(s.B * s.Hkv), dim3(SEL_THREADS), 0, st, mode, q, blk_score,
+                           klabel, label_ch, ctx_len, blk_idx, tok_idx, tok_score, arrivals, s.Hkv, s.G, s.dk, s.bs,
+                           s.r, s.kb, s.kt, s.max_ctx, s.nb_cap, shift);
+    else
+        hipLaunchKernelGGL((select_kernel<PT, 16>), dim3(s.B * s.Hkv), dim3(SEL_THREADS), 0, st, mode, q, blk_score,
+                           klabel, label_ch, ctx_len, blk_idx, tok_idx, tok_score, arrivals, s.Hkv, s.G, s.dk, s.bs,
+                           s.r, s.kb, s.kt, s.max_ctx, s.nb_cap, shift);
     return hipGetLastError();
 }
 

@@ -146,6 +146,8 @@ def test_decode_step_tiny4k_all_stages():
     dict(n_q_heads=16, n_kv_heads=2, d_k=64, d_v=64),               # G=8, d=64
     dict(n_q_heads=4, n_kv_heads=2, d_k=256, d_v=256, r=32),        # G=2, d=256, r=32
     dict(block=32, k_blocks=8, r=32, k_tokens=100),                 # block 32, K_t not a split multiple
+    dict(n_q_heads=8, n_kv_heads=2, r=64),                          # label rows of two 32-channel steps
+    dict(n_q_heads=16, n_kv_heads=2, d_k=256, d_v=256, r=128),      # label rows of four 32-channel steps
     dict(block=1, k_blocks=200, k_tokens=50, max_ctx=300, ctx=300, n_planted=2),   # block 1: exact top-k
     dict(label_mode="random", scaled_keys=False, k_tokens=256),
 ])
