@@ -12,12 +12,9 @@
 // kernel merges the partials of all splits.
 //
 // MLA path (values are the first d_v dims of the d_k-dim latent key rows,
-// 32 query heads on one KV head): a workgroup takes 32 kept tokens; the
-// 32x32 logit tile (tokens x heads) is four 16x16 tiles of
-// v_mfma_f32_16x16x32_bf16, one per wave, with key rows and queries read
-// straight from memory as A and B fragments; softmax runs in LDS; P.V runs
-// in fp32 on the VALU from the value rows staged in LDS (each thread: one
-// head, d_v/8 interleaved channels).
+// 32 query heads on one KV head): a workgroup takes rounds of 32 kept
+// tokens; logits and P.V run on v_mfma_f32_16x16x32_bf16 from key rows and
+// queries staged in LDS, with an online softmax across the rounds.
 //
 // Workgroup numbering: the dispatcher hands consecutive workgroups to the
 // eight XCDs in turn, so workgroup L runs on XCD L % 8. All splits of a unit
@@ -193,184 +190,203 @@ __global__ __launch_bounds__(256) void attend_gqa_kernel(
 
 // grid: as the GQA kernel; block 256 (4 waves). Hq = 32 * Hkv, d_k % 32 ==
 // 0, d_k <= DKMAX, d_v % 64 == 0, d_v <= 512, values alias the first d_v
-// key dims (absorbed latent). One workgroup takes T = 32 kept tokens:
-//  1. the group's query fragments are requested first (registers), the
-//     token rows and slots next; the 32 key rows (which hold the values)
-//     are staged in LDS with every load in flight;
-//  2. logits on v_mfma_f32_16x16x32_bf16: wave w multiplies token tile
-//     w & 1 by head tile w >> 1 over the d_k / 32 steps;
-//  3. softmax per head over the 32 tokens (8 lanes per head, DPP);
-//  4. P.V on the same instruction with M = heads, N = 16 value channels,
-//     K = the 32 tokens. P enters as two bf16 terms (hi + lo) so the
-//     weights keep ~16 mantissa bits; V is exact in bf16.
-// Operands of steps past d_k are zeros: the matrix instructions run for
-// every step.
+// key dims (absorbed latent). A split of 32 * rounds consecutive entries of
+// the unit's token list (32 per round) is shared by vsplit workgroups, each
+// owning a range of value channels (all of them gather the split's rows and
+// compute its logits; the splits of a unit share an XCD):
+//  * the round's 32 key rows (which hold the values) are staged in LDS; the
+//    next round's rows are gathered into registers meanwhile; absent
+//    tokens (-1) are zero rows;
+//  * wave w owns head tile w & 1 (query fragments in registers): it
+//    multiplies token tile w >> 1 of the round by its heads on
+//    v_mfma_f32_16x16x32_bf16, swaps that tile
+//    through LDS with the wave holding the other token tile, and keeps its
+//    heads' running max and sum over the rounds itself;
+//  * P.V is accumulated transposed, O^T += V^T P^T, over value tiles
+//    w >> 1, w >> 1 + 2, ...: the logit accumulators already hold P^T in
+//    the B-operand layout (tokens permuted alike on both operands), each
+//    accumulator lane's rescale factor is its own head's, and the V^T
+//    operand comes from LDS through the gfx950 transposing 16-bit read
+//    (within each 16-lane group, lane i receives element i % 4 of the 8
+//    bytes that lane 4j + i / 4 addressed). P enters as two bf16 terms
+//    (hi + lo) so the weights keep ~16 mantissa bits; V is exact in bf16.
 template <int DKMAX>
-__global__ __launch_bounds__(256) void attend_mla_kernel(
+__global__ __launch_bounds__(256, 1) void attend_mla_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ K, const int32_t* __restrict__ tok_idx,
     const int32_t* __restrict__ slot_of, int n_slots, float* __restrict__ part_ml,
     float* __restrict__ part_acc, int Hkv, int dk, int dv, int bs, int kt, int max_ctx, int nb_cap,
-    int n_splits, int units, float scale2, int slot_rows) {
-    constexpr int T = MLA_TOK_PER_SPLIT;   // 32 tokens
+    int n_splits, int units, float scale2, int slot_rows, int rounds, int vsplit) {
+    constexpr int T = 32;                  // tokens per round
     constexpr int H = 32;                  // query heads per KV head
     constexpr int KSMAX = DKMAX / 32;      // logit steps
     constexpr int RS = DKMAX + 8;          // LDS row stride (elements): spreads rows over banks
+    constexpr int PER = (T * DKMAX / 8 + 255) / 256;
+    constexpr int NTW = 16;                // value tiles of 16 channels per wave (d_v <= 512)
+    constexpr int RMAX = MLA_TOK_PER_SPLIT / T;
     __shared__ __align__(16) uint16_t sK[T * RS];
-    __shared__ float sS[T][H + 1];
-    __shared__ float sm[H], sl[H];
-    __shared__ long s_row[T];
+    __shared__ __align__(16) float sZ[4][64][4];   // logit tile of each wave
+    __shared__ long s_row[RMAX * T];
+    __shared__ uint32_t s_vm[RMAX];                // valid-token mask of each round
 
     const int xcd = blockIdx.x & 7, y = blockIdx.x >> 3;
-    const int unit = (y / n_splits) * 8 + xcd, split = y % n_splits;
+    const int per_unit = n_splits * vsplit;
+    const int unit = (y / per_unit) * 8 + xcd, split = (y % per_unit) / vsplit, vpart = y % vsplit;
     if (unit >= units) return;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int KS = dk / 32;
-    const int mt = wave & 1, nt = wave >> 1;   // logit tile: tokens 16*mt.., heads 16*nt..
+    const int g = lane >> 4, c16 = lane & 15, nt = wave & 1, half = wave >> 1;
+    const int cpr = dk / 8, nchunk = T * cpr;
+    const int TS = rounds * T;
+    // value tiles [nt_lo, nt_hi) of this workgroup
+    const int NTall = dv / 16, nt_lo = vpart * NTall / vsplit, nt_hi = (vpart + 1) * NTall / vsplit;
 
-    // 1. query fragments (B operand: head nt*16 + lane%16, channels
-    //    32*s + 8*(lane/16)..), then token rows
+    // the token list is requested before the query fragments (loads
+    // complete in order, so the rows wait for no fragment)
+    const int ti = split * TS + tid;
+    const int t_raw = tok_idx[(size_t)unit * kt + (ti < kt ? ti : kt - 1)];   // unconditional load
+    const int t = tid < TS && ti < kt ? t_raw : -1;
+    // query fragments of head nt*16 + c16 (B operand, zero past d_k)
     uint4 qb[KSMAX];
     {
-        const uint16_t* qr = q + ((size_t)unit * H + nt * 16 + (lane & 15)) * dk + (lane >> 4) * 8;
+        const uint16_t* qr = q + ((size_t)unit * H + nt * 16 + c16) * dk + g * 8;
 #pragma unroll
-        for (int u = 0; u < KSMAX; ++u) qb[u] = u < KS ? ldg16(qr + u * 32) : make_uint4(0u, 0u, 0u, 0u);
+        for (int u = 0; u < KSMAX; ++u) qb[u] = u < dk / 32 ? ldg16(qr + u * 32) : make_uint4(0u, 0u, 0u, 0u);
     }
-    if (tid < T) {
-        const int ti = split * T + tid;
-        const int t = ti < kt ? tok_idx[(size_t)unit * kt + ti] : -1;
+
+    // token rows of the split and each round's valid mask
+    if (tid < RMAX * T) {
         long row = -1;
-        if (!slot_of) {
-            row = (t >= 0 && t < max_ctx) ? (long)unit * max_ctx + t : -1;
-        } else if (t >= 0) {
-            const int blk = t / bs;
-            const int sl_ = blk < nb_cap ? slot_of[(size_t)unit * nb_cap + blk] : -1;
-            row = (sl_ >= 0 && sl_ < n_slots) ? ((long)unit * n_slots + sl_) * slot_rows + (t - blk * bs) : -1;
+        if (tid < TS) {
+            if (!slot_of) {
+                row = (t >= 0 && t < max_ctx) ? (long)unit * max_ctx + t : -1;
+            } else if (t >= 0) {
+                const int blk = t / bs;
+                const int sl_ = blk < nb_cap ? slot_of[(size_t)unit * nb_cap + blk] : -1;
+                row = (sl_ >= 0 && sl_ < n_slots) ? ((long)unit * n_slots + sl_) * slot_rows + (t - blk * bs) : -1;
+            }
         }
         s_row[tid] = row;
-    }
-    __syncthreads();
-
-    // key rows into LDS: chunk c of token r at sK[r * RS + 8c]; every load
-    // of the thread is issued before the first store
-    {
-        const int cpr = dk / 8;
-        constexpr int PER = (T * DKMAX / 8 + 255) / 256;
-        uint4 v[PER];
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int c = tid + i * 256;
-            const int r = c / cpr, ch = c - r * cpr;
-            const long row = c < T * cpr ? s_row[r] : -1;
-            v[i] = row >= 0 ? ldg16(K + row * dk + ch * 8) : make_uint4(0u, 0u, 0u, 0u);
-        }
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int c = tid + i * 256;
-            if (c < T * cpr) {
-                const int r = c / cpr, ch = c - r * cpr;
-                *reinterpret_cast<uint4*>(&sK[r * RS + ch * 8]) = v[i];
-            }
+        const uint64_t bal = __ballot(row >= 0);
+        if ((tid & 63) == 0) {
+            s_vm[tid >> 5] = (uint32_t)bal;
+            if ((tid >> 5) + 1 < RMAX) s_vm[(tid >> 5) + 1] = (uint32_t)(bal >> 32);
         }
     }
+    // key columns past d_k stay zero (row stores never touch them)
+    for (int c = tid; c < T * (DKMAX / 8); c += 256)
+        *reinterpret_cast<uint4*>(&sK[(c / (DKMAX / 8)) * RS + (c % (DKMAX / 8)) * 8]) = make_uint4(0u, 0u, 0u, 0u);
     __syncthreads();
 
-    // 2. logits: A = key rows of tile mt from LDS, B = query fragments
-    {
-        const uint16_t* ar = &sK[(mt * 16 + (lane & 15)) * RS + (lane >> 4) * 8];
-        f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    // chunk c of a round: 16 bytes at column 8 (c % cpr) of row c / cpr;
+    // chunks past the row count repeat the last one
+    int soff[PER], rsel[PER], coff[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        int c = tid + i * 256;
+        c = c < nchunk ? c : nchunk - 1;
+        rsel[i] = c / cpr;
+        coff[i] = (c - rsel[i] * cpr) * 8;
+        soff[i] = rsel[i] * RS + coff[i];
+    }
+    auto load_rows = [&](int rd, uint4 (&v)[PER]) {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const long row = s_row[rd * T + rsel[i]];
+            v[i] = row >= 0 ? ldg16(K + row * dk + coff[i]) : make_uint4(0u, 0u, 0u, 0u);
+        }
+    };
+    uint4 v[PER];
+    load_rows(0, v);
+
+    float m_run = -INFINITY, l_run = 0.f;
+    f32x4_t acc[NTW];
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    const uint16_t* ka = &sK[(half * 16 + c16) * RS + g * 8];
+    // transposed-read address: token 4g + c16 / 4, channels 4 (c16 % 4) ..
+    const uint16_t* va = &sK[(g * 4 + (c16 >> 2)) * RS + (c16 & 3) * 4];
+    for (int rd = 0; rd < rounds; ++rd) {
+        if (rd > 0) __syncthreads();   // every wave is done with the previous round's rows
+#pragma unroll
+        for (int i = 0; i < PER; ++i) *reinterpret_cast<uint4*>(&sK[soff[i]]) = v[i];
+        __syncthreads();
+        if (rd + 1 < rounds) load_rows(rd + 1, v);   // next round in flight
+        const uint32_t vm = s_vm[rd];
+
+        // this wave's logit tile: tokens half*16 + 4g + i, head nt*16 + c16
+        f32x4_t za = {0.f, 0.f, 0.f, 0.f}, zb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int u = 0; u < KSMAX; u += 2) {
-            const uint4 a0 = u < KS ? *reinterpret_cast<const uint4*>(ar + u * 32) : make_uint4(0u, 0u, 0u, 0u);
-            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a0), as_bf16x8(qb[u]), acc0, 0, 0, 0);
-            if (u + 1 < KSMAX) {
-                const uint4 a1 =
-                    u + 1 < KS ? *reinterpret_cast<const uint4*>(ar + (u + 1) * 32) : make_uint4(0u, 0u, 0u, 0u);
-                acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a1), as_bf16x8(qb[u + 1]), acc1, 0, 0, 0);
-            }
+            za = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(*reinterpret_cast<const uint4*>(ka + u * 32)),
+                                                         as_bf16x8(qb[u]), za, 0, 0, 0);
+            if (u + 1 < KSMAX)
+                zb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    as_bf16x8(*reinterpret_cast<const uint4*>(ka + (u + 1) * 32)), as_bf16x8(qb[u + 1]), zb, 0, 0,
+                    0);
         }
-        const f32x4_t acc = acc0 + acc1;
-        // lane: head nt*16 + lane%16, tokens mt*16 + 4*(lane/16) + i
-        const int h = nt * 16 + (lane & 15);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int tok = mt * 16 + (lane >> 4) * 4 + i;
-            sS[tok][h] = s_row[tok] >= 0 ? acc[i] * scale2 : -INFINITY;
-        }
-    }
-    __syncthreads();
+        *reinterpret_cast<f32x4_t*>(sZ[wave][lane]) = za + zb;
+        __syncthreads();
+        const f32x4_t z0 = *reinterpret_cast<const f32x4_t*>(sZ[nt][lane]);
+        const f32x4_t z1 = *reinterpret_cast<const f32x4_t*>(sZ[2 + nt][lane]);
 
-    // 3. softmax per head: 8 lanes per head, 4 tokens each
-    {
-        const int h = tid >> 3, part = tid & 7;
-        float z[4], m = -INFINITY;
+        // online softmax of head nt*16 + c16 over the round's tokens
+        float p[8], mc = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            z[i] = sS[part * 4 + i][h];
-            m = fmaxf(m, z[i]);
+            p[i] = (vm >> (g * 4 + i)) & 1u ? z0[i] * scale2 : -INFINITY;
+            p[4 + i] = (vm >> (16 + g * 4 + i)) & 1u ? z1[i] * scale2 : -INFINITY;
         }
-        m = group_max<8>(m);
-        float l = 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float p = (z[i] == -INFINITY) ? 0.f : exp2f(z[i] - m);
-            sS[part * 4 + i][h] = p;
-            l += p;
-        }
-        l = group_sum<8>(l);
-        if (part == 0) {
-            sm[h] = m;
-            sl[h] = l;
-        }
-    }
-    __syncthreads();
-
-    // 4. P.V: wave w takes value channels [dv/4 * w, dv/4 * (w+1)) in
-    //    16-channel tiles, both head tiles. A = P (head lane%16, tokens
-    //    8*(lane/16)..+8), B = V (channel lane%16, same tokens).
-    const int NT = dv / 16;            // channel tiles (<= 32)
-    bf16x8_t pa_hi[2], pa_lo[2];
-#pragma unroll
-    for (int m2 = 0; m2 < 2; ++m2) {
-        const int h = m2 * 16 + (lane & 15);
+        for (int i = 0; i < 8; ++i) mc = fmaxf(mc, p[i]);
+        mc = max_xor32(max_xor16(mc));
+        const float mn = fmaxf(m_run, mc);
+        // -inf only while no valid token has been seen: nothing to rescale
+        const float rs = m_run == -INFINITY ? 0.f : exp2f(m_run - mn);
+        float ls = 0.f;
         uint32_t hi[4], lo[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const float p0 = sS[(lane >> 4) * 8 + 2 * j][h], p1 = sS[(lane >> 4) * 8 + 2 * j + 1][h];
-            const uint32_t h0 = f32_bf16_rne(p0), h1 = f32_bf16_rne(p1);
-            const uint32_t l0 = f32_bf16_rne(p0 - bf16_f32(h0)), l1 = f32_bf16_rne(p1 - bf16_f32(h1));
-            hi[j] = h0 | (h1 << 16);
-            lo[j] = l0 | (l1 << 16);
+        for (int k = 0; k < 4; ++k) {
+            const float p0 = p[2 * k] == -INFINITY ? 0.f : exp2f(p[2 * k] - mn);
+            const float p1 = p[2 * k + 1] == -INFINITY ? 0.f : exp2f(p[2 * k + 1] - mn);
+            ls += p0 + p1;
+            split_bf16x2(p0, p1, hi[k], lo[k]);
         }
-        pa_hi[m2] = as_bf16x8(make_uint4(hi[0], hi[1], hi[2], hi[3]));
-        pa_lo[m2] = as_bf16x8(make_uint4(lo[0], lo[1], lo[2], lo[3]));
-    }
-    const size_t bh0 = (size_t)unit * H;
-    for (int n = wave; n < NT; n += 4) {
-        // B fragment: 8 tokens of channel n*16 + lane%16
-        const int c = n * 16 + (lane & 15);
-        uint32_t w4[4];
+        ls = sum_xor32(sum_xor16(ls));
+        l_run = l_run * rs + ls;
+        m_run = mn;
+        const bf16x8_t pb_hi = as_bf16x8(make_uint4(hi[0], hi[1], hi[2], hi[3]));
+        const bf16x8_t pb_lo = as_bf16x8(make_uint4(lo[0], lo[1], lo[2], lo[3]));
+
+        // O^T tile (channels nn*16.., heads nt*16..) += V^T P^T; the k index
+        // 8g + j stands for token 4g + j (j < 4) or 16 + 4g + j - 4
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int t0 = (lane >> 4) * 8 + 2 * j;
-            w4[j] = (uint32_t)sK[t0 * RS + c] | ((uint32_t)sK[(t0 + 1) * RS + c] << 16);
-        }
-        const bf16x8_t vb = as_bf16x8(make_uint4(w4[0], w4[1], w4[2], w4[3]));
-#pragma unroll
-        for (int m2 = 0; m2 < 2; ++m2) {
-            f32x4_t o = {0.f, 0.f, 0.f, 0.f};
-            o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_hi[m2], vb, o, 0, 0, 0);
-            o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_lo[m2], vb, o, 0, 0, 0);
-            // lane: channel c, heads m2*16 + 4*(lane/16) + i
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int h = m2 * 16 + (lane >> 4) * 4 + i;
-                part_acc[((bh0 + h) * n_splits + split) * dv + c] = o[i];
+        for (int j = 0; j < NTW; ++j) {
+            const int nn = nt_lo + half + 2 * j;
+            if (nn < nt_hi) {
+                const s16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_s16x4(va + nn * 16));
+                const s16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_s16x4(va + 16 * RS + nn * 16));
+                const uint2 w0 = __builtin_bit_cast(uint2, v0), w1 = __builtin_bit_cast(uint2, v1);
+                const bf16x8_t vt = as_bf16x8(make_uint4(w0.x, w0.y, w1.x, w1.y));
+                f32x4_t o = acc[j] * rs;
+                o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, pb_hi, o, 0, 0, 0);
+                o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, pb_lo, o, 0, 0, 0);
+                acc[j] = o;
             }
         }
     }
-    if (tid < H) {
-        part_ml[((bh0 + tid) * n_splits + split) * 2 + 0] = sm[tid];
-        part_ml[((bh0 + tid) * n_splits + split) * 2 + 1] = sl[tid];
+
+    // partials: channel nn*16 + 4g + i, head nt*16 + c16
+    const size_t bh = (size_t)unit * H + nt * 16 + c16;
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) {
+        const int nn = nt_lo + half + 2 * j;
+        if (nn < nt_hi)
+            *reinterpret_cast<float4*>(&part_acc[(bh * n_splits + split) * dv + nn * 16 + g * 4]) =
+                make_float4(acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
+    }
+    if (vpart == 0 && half == 0 && g == 0) {
+        part_ml[(bh * n_splits + split) * 2] = m_run;
+        part_ml[(bh * n_splits + split) * 2 + 1] = l_run;
     }
 }
 
@@ -477,15 +493,18 @@ hipError_t launch_attend(const Shape& s, const uint16_t* q, const uint16_t* K, c
     hipError_t e = hipSuccess;
     if (mla_shape(s)) {
         const int units = s.B * s.Hkv;
-        const dim3 grid(((units + 7) / 8) * 8 * ns);
+        // value channels are split over two workgroups while the splits
+        // alone would leave CUs idle
+        const int vs = (long)units * ns < 256 && s.dv >= 128 ? 2 : 1;
+        const dim3 grid(((units + 7) / 8) * 8 * ns * vs);
         if (s.dk <= 576)
             hipLaunchKernelGGL(attend_mla_kernel<576>, grid, dim3(256), 0, st, q, K, tok_idx, slot_of, n_slots,
                                part_ml, part_acc, s.Hkv, s.dk, s.dv, s.bs, s.kt, s.max_ctx, s.nb_cap, ns, units,
-                               s.sm_scale * LOG2E, s.bs);
+                               s.sm_scale * LOG2E, s.bs, MLA_TOK_PER_SPLIT / 32, vs);
         else
             hipLaunchKernelGGL(attend_mla_kernel<1024>, grid, dim3(256), 0, st, q, K, tok_idx, slot_of, n_slots,
                                part_ml, part_acc, s.Hkv, s.dk, s.dv, s.bs, s.kt, s.max_ctx, s.nb_cap, ns, units,
-                               s.sm_scale * LOG2E, s.bs);
+                               s.sm_scale * LOG2E, s.bs, MLA_TOK_PER_SPLIT / 32, vs);
         e = hipGetLastError();
     } else {
         switch (s.dk) {

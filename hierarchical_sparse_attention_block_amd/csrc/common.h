@@ -120,13 +120,23 @@ __device__ __forceinline__ float group_max(float v) {
     return v;
 }
 
-// float -> bf16 bits, round to nearest even (finite inputs).
-__device__ __forceinline__ uint32_t f32_bf16_rne(float f) {
-    const uint32_t u = __float_as_uint(f);
-    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-}
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// Two floats as a packed bf16 pair (a in the low half), rounded to nearest
+// even by the gfx950 packed conversion.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{a, b}), bf16x2_t));
+}
+// a = hi + lo with hi, lo bf16 pairs: hi holds a's leading 8 mantissa
+// bits, lo the next 8 (the product of either with a bf16 value is exact in
+// fp32 accumulation)
+__device__ __forceinline__ void split_bf16x2(float a, float b, uint32_t& hi, uint32_t& lo) {
+    hi = pk_bf16(a, b);
+    lo = pk_bf16(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u));
+}
 
 // Operand of the gfx950 transposing LDS read of four 16-bit elements.
 typedef short s16x4_t __attribute__((ext_vector_type(4)));

@@ -293,9 +293,7 @@ __global__ __launch_bounds__(256, DKMAX <= 576 ? 2 : 1) void dense_mla_kernel(
         for (int k = 0; k < 4; ++k) {
             const float p0 = exp2f(p[2 * k] - mn), p1 = exp2f(p[2 * k + 1] - mn);
             ls += p0 + p1;
-            const uint32_t h0 = f32_bf16_rne(p0), h1 = f32_bf16_rne(p1);
-            hi[k] = h0 | (h1 << 16);
-            lo[k] = f32_bf16_rne(p0 - bf16_f32(h0)) | (f32_bf16_rne(p1 - bf16_f32(h1)) << 16);
+            split_bf16x2(p0, p1, hi[k], lo[k]);
         }
         ls = sum_xor32(sum_xor16(ls));
         l_run = l_run * rs + ls;
@@ -311,9 +309,8 @@ __global__ __launch_bounds__(256, DKMAX <= 576 ? 2 : 1) void dense_mla_kernel(
             if (nn < NT) {
                 const s16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_s16x4(va + nn * 16));
                 const s16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_s16x4(va + 16 * RS + nn * 16));
-                const bf16x8_t vt = as_bf16x8(make_uint4(
-                    (uint16_t)v0[0] | ((uint32_t)(uint16_t)v0[1] << 16), (uint16_t)v0[2] | ((uint32_t)(uint16_t)v0[3] << 16),
-                    (uint16_t)v1[0] | ((uint32_t)(uint16_t)v1[1] << 16), (uint16_t)v1[2] | ((uint32_t)(uint16_t)v1[3] << 16)));
+                const uint2 w0 = __builtin_bit_cast(uint2, v0), w1 = __builtin_bit_cast(uint2, v1);
+                const bf16x8_t vt = as_bf16x8(make_uint4(w0.x, w0.y, w1.x, w1.y));
                 f32x4_t o = acc[j] * rs;
                 o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, pb_hi, o, 0, 0, 0);
                 o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, pb_lo, o, 0, 0, 0);

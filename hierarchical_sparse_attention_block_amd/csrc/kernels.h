@@ -14,7 +14,7 @@ constexpr int MAX_KB = 2048;         // K_b
 constexpr int MAX_G = 32;            // query heads per KV head
 constexpr int MAX_R = 128;           // label channels
 constexpr int ATT_TOK_PER_SPLIT = 64;    // tokens per attention workgroup (GQA path)
-constexpr int MLA_TOK_PER_SPLIT = 32;    // tokens per attention workgroup (MLA path)
+constexpr int MLA_TOK_PER_SPLIT = 64;    // tokens per attention workgroup (MLA path)
 
 struct Shape {
     int B, Hq, Hkv, G, dk, dv, valias, bs, r, kb, kt, max_ctx, nb_cap;
