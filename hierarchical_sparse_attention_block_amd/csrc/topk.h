@@ -77,13 +77,11 @@ struct TopK {
         if (lane == 0) { red[12 * NW + w] = lmin; red[13 * NW + w] = lmax; red[14 * NW + w] = cnt; }
         if (tid == 0) *ccount = 0u;
         __syncthreads();
-        uint32_t kmin = 0xffffffffu, kmax = 0u, nval = 0u;
-#pragma unroll
-        for (int i = 0; i < NW; ++i) {
-            kmin = min(kmin, red[12 * NW + i]);
-            kmax = max(kmax, red[13 * NW + i]);
-            nval += red[14 * NW + i];
-        }
+        // over the waves: lane i reads wave i's entries
+        const uint32_t kmin = wave_minmax<false>(lane < NW ? red[12 * NW + lane] : 0xffffffffu);
+        const uint32_t kmax = wave_minmax<true>(lane < NW ? red[13 * NW + lane] : 0u);
+        const uint32_t nval =
+            (uint32_t)__builtin_amdgcn_readlane((int)wave_scan_dpp(lane < NW ? red[14 * NW + lane] : 0u), 63);
         const int k_eff = k < (int)nval ? k : (int)nval;
         if (k_eff <= 0) return 0;
 
@@ -114,13 +112,13 @@ struct TopK {
                 const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)wave_scan_dpp(loc), 63);
                 if (lane == 0) red[11 * NW + w] = tot;
                 __syncthreads();
-                uint32_t above = 0;
-                int wp = 0;
-                for (; wp < NW; ++wp) {
-                    const uint32_t t = red[11 * NW + wp];
-                    if (above + t >= (uint32_t)k_eff) break;
-                    above += t;
-                }
+                // the first wave whose running total reaches k_eff, from one
+                // lane-parallel read and a scan (the totals cover nval keys)
+                const uint32_t tw = lane < NW ? red[11 * NW + lane] : 0u;
+                const uint32_t incl = wave_scan_dpp(tw);
+                int wp = __ffsll((unsigned long long)__ballot(lane < NW && incl >= (uint32_t)k_eff)) - 1;
+                wp = wp < 0 ? NW - 1 : wp;   // unreachable: the totals reach nval >= k_eff
+                const uint32_t above = (uint32_t)__builtin_amdgcn_readlane((int)(incl - tw), wp);
                 uint32_t hv[BPT], ploc = 0;
 #pragma unroll
                 for (int e = 0; e < BPT; ++e) { hv[e] = sm.hist[NBIN - 1 - (wp * BPW + lane * BPT + e)]; ploc += hv[e]; }
@@ -157,8 +155,16 @@ struct TopK {
                             const int bj = bin(key[j]);
                             if (bj == bstar) {
                                 const int me = (w * pt + j) * 64 + lane;
-                                uint32_t rank = 0;
-                                for (uint32_t c = 0; c < m; ++c) {
+                                uint32_t rank = 0, c = 0;
+                                for (; c + 4 <= m; c += 4) {   // four candidates per LDS read
+                                    const uint4 ck = *reinterpret_cast<const uint4*>(&sm.ckey[c]);
+                                    const int4 ci = *reinterpret_cast<const int4*>(&sm.cidx[c]);
+                                    rank += (ck.x > key[j]) || (ck.x == key[j] && ci.x < me);
+                                    rank += (ck.y > key[j]) || (ck.y == key[j] && ci.y < me);
+                                    rank += (ck.z > key[j]) || (ck.z == key[j] && ci.z < me);
+                                    rank += (ck.w > key[j]) || (ck.w == key[j] && ci.w < me);
+                                }
+                                for (; c < m; ++c) {
                                     const uint32_t ck = sm.ckey[c];
                                     rank += (ck > key[j]) || (ck == key[j] && sm.cidx[c] < me);
                                 }
@@ -238,8 +244,9 @@ struct TopK {
         uint32_t* c = red + 10 * NW;
         if (lane == 0) c[w] = cntw;
         __syncthreads();
-        uint32_t run = 0;
-        for (int i = 0; i < w; ++i) run += c[i];
+        // entries kept by the waves before this one: lane-parallel read + scan
+        const uint32_t cv = lane < NW ? c[lane] : 0u;
+        uint32_t run = (uint32_t)__builtin_amdgcn_readlane((int)(wave_scan_dpp(cv) - cv), w);
 #pragma unroll
         for (int j = 0; j < PT; ++j) {
             if (j < pt) {
