@@ -35,7 +35,8 @@ WsLayout ws_layout(const Shape& s) {
     w.blk_score = off; off = align256(off + (size_t)s.B * s.Hkv * s.nb_cap * sizeof(float));
     w.part_ml = off;   off = align256(off + (size_t)s.B * s.Hq * attn_splits(s) * 2 * sizeof(float));
     w.part_acc = off;  off = align256(off + (size_t)s.B * s.Hq * attn_splits(s) * s.dv * sizeof(float));
-    w.arrivals = off;  off = align256(off + (size_t)s.B * s.Hkv * sizeof(int32_t));
+    w.sel_keys = off;  off = align256(off + (size_t)s.B * s.Hkv * s.kb * s.bs * sizeof(uint32_t));
+    w.sel_cnt = off;   off = align256(off + (size_t)s.B * s.Hkv * sizeof(int32_t));
     w.total = off;
     return w;
 }
@@ -104,7 +105,7 @@ int hsab_score_blocks(const hsab_dims* dims, const uint16_t* q, const uint16_t* 
     if (!q || !meta || !ctx_len || !blk_score) return HSAB_EINVAL;
     return hip_status(launch_block_score(make_shape(*dims), q, const_cast<uint16_t*>(meta), ctx_len,
                                          blk_score, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
-                                         stream));
+                                         nullptr, stream));
 }
 
 int hsab_select_blocks(const hsab_dims* dims, const uint16_t* q, const uint16_t* meta,
@@ -121,10 +122,10 @@ int hsab_select_blocks(const hsab_dims* dims, const uint16_t* q, const uint16_t*
         scores = reinterpret_cast<float*>(static_cast<char*>(ws) + L.blk_score);
     }
     rc = hip_status(launch_block_score(s, q, const_cast<uint16_t*>(meta), ctx_len, scores, nullptr,
-                                       nullptr, nullptr, nullptr, nullptr, nullptr, stream));
+                                       nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, stream));
     if (rc) return rc;
     return hip_status(launch_select(s, 1, q, scores, nullptr, nullptr, ctx_len, blk_idx, nullptr,
-                                    nullptr, nullptr, stream));
+                                    nullptr, nullptr, nullptr, stream));
 }
 
 int hsab_select_tokens(const hsab_dims* dims, const uint16_t* q, const uint16_t* klabel,
@@ -136,7 +137,8 @@ int hsab_select_tokens(const hsab_dims* dims, const uint16_t* q, const uint16_t*
     if (rc) return rc;
     if (!q || !klabel || !label_ch || !blk_idx || !ctx_len || !tok_idx) return HSAB_EINVAL;
     return hip_status(launch_select(make_shape(*dims), 2, q, nullptr, klabel, label_ch, ctx_len,
-                                    const_cast<int32_t*>(blk_idx), tok_idx, tok_score, nullptr, stream));
+                                    const_cast<int32_t*>(blk_idx), tok_idx, tok_score, nullptr, nullptr,
+                                    stream));
 }
 
 int hsab_sparse_attend(const hsab_dims* dims, const uint16_t* q, const uint16_t* K,
@@ -156,7 +158,7 @@ int hsab_sparse_attend(const hsab_dims* dims, const uint16_t* q, const uint16_t*
     char* w = static_cast<char*>(ws);
     return hip_status(launch_attend(s, q, K, s.valias ? K : V, tok_idx, slot_of, n_slots,
                                     reinterpret_cast<float*>(w + L.part_ml),
-                                    reinterpret_cast<float*>(w + L.part_acc), nullptr, out, lse, stream));
+                                    reinterpret_cast<float*>(w + L.part_acc), out, lse, stream));
 }
 
 int hsab_decode_step(const hsab_dims* dims, const uint16_t* q, const uint16_t* k_new,
@@ -176,17 +178,19 @@ int hsab_decode_step(const hsab_dims* dims, const uint16_t* q, const uint16_t* k
     if (!attend_supported(s)) return HSAB_EUNSUPPORTED;
     char* w = static_cast<char*>(ws);
     float* scores = reinterpret_cast<float*>(w + L.blk_score);
-    // 1) append + block scores; 2) top-K_b, label scores, top-K_t (one
-    // workgroup per unit); 3) split attention and the merge of its partials
+    uint32_t* sel_keys = reinterpret_cast<uint32_t*>(w + L.sel_keys);
+    int32_t* sel_cnt = reinterpret_cast<int32_t*>(w + L.sel_cnt);
+    // 1) append + block scores (and zeroed selection counters); 2) top-K_b,
+    // label scores, top-K_t; 3) split attention and the merge of its partials
     rc = hip_status(launch_block_score(s, q, meta, ctx_len, scores, k_new, v_new, K, V, klabel, label_ch,
-                                       stream));
+                                       sel_cnt, stream));
     if (rc) return rc;
     rc = hip_status(launch_select(s, 3, q, scores, klabel, label_ch, ctx_len, blk_idx, tok_idx, nullptr,
-                                  nullptr, stream));
+                                  sel_keys, sel_cnt, stream));
     if (rc) return rc;
     return hip_status(launch_attend(s, q, K, s.valias ? K : V, tok_idx, nullptr, 0,
                                     reinterpret_cast<float*>(w + L.part_ml),
-                                    reinterpret_cast<float*>(w + L.part_acc), nullptr, out, lse, stream));
+                                    reinterpret_cast<float*>(w + L.part_acc), out, lse, stream));
 }
 
 size_t hsab_dense_workspace_bytes(const hsab_dims* dims) {

@@ -484,9 +484,7 @@ bool attend_supported(const Shape& s) {
 
 hipError_t launch_attend(const Shape& s, const uint16_t* q, const uint16_t* K, const uint16_t* V,
                          const int32_t* tok_idx, const int32_t* slot_of, int n_slots,
-                         float* part_ml, float* part_acc, int32_t* arrivals, float* out, float* lse,
-                         hipStream_t st) {
-    (void)arrivals;
+                         float* part_ml, float* part_acc, float* out, float* lse, hipStream_t st) {
     if (!attend_supported(s)) return hipErrorInvalidValue;
     if (slot_of && !s.valias) V = K + (size_t)s.bs * s.dk;   // value rows follow the key rows in a slot
     const int ns = attn_splits(s);

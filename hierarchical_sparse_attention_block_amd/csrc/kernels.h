@@ -26,7 +26,7 @@ int attn_splits(const Shape& s);
 
 // workspace carve-up (byte offsets, 256-aligned)
 struct WsLayout {
-    size_t blk_score, part_ml, part_acc, arrivals, total;
+    size_t blk_score, part_ml, part_acc, sel_keys, sel_cnt, total;
 };
 WsLayout ws_layout(const Shape& s);
 
@@ -34,23 +34,25 @@ hipError_t launch_build_meta(const Shape& s, const uint16_t* K, const int32_t* c
                              const int32_t* label_ch, uint16_t* meta, uint16_t* klabel,
                              hipStream_t st);
 // Block scores; with k_new non-null the decode-step append runs first
-// (inside the workgroup that owns each unit's tail block).
+// (inside the workgroup that owns each unit's tail block). sel_cnt
+// (nullable): the per-unit arrival counters of a following split token
+// selection, set to zero here.
 hipError_t launch_block_score(const Shape& s, const uint16_t* q, uint16_t* meta, const int32_t* ctx_len,
                               float* score, const uint16_t* k_new, const uint16_t* v_new, uint16_t* K,
-                              uint16_t* V, uint16_t* klabel, const int32_t* label_ch, hipStream_t st);
+                              uint16_t* V, uint16_t* klabel, const int32_t* label_ch, int32_t* sel_cnt,
+                              hipStream_t st);
 // mode bit 1: select blocks from block scores; bit 2: score + select tokens.
-// arrivals (nullable): per-unit counters zeroed for the attention merge.
+// With sel_keys and sel_cnt non-null (counters zero on entry, zero again on
+// exit) the token stage of each unit is spread over several workgroups.
 hipError_t launch_select(const Shape& s, int mode, const uint16_t* q, const float* blk_score,
                          const uint16_t* klabel, const int32_t* label_ch, const int32_t* ctx_len,
-                         int32_t* blk_idx, int32_t* tok_idx, float* tok_score, int32_t* arrivals,
-                         hipStream_t st);
+                         int32_t* blk_idx, int32_t* tok_idx, float* tok_score, uint32_t* sel_keys,
+                         int32_t* sel_cnt, hipStream_t st);
 bool attend_supported(const Shape& s);
-// Split attention; with arrivals non-null (zeroed beforehand) the last split
-// of each unit merges the partials, otherwise a combine kernel follows.
+// Split attention over the kept tokens, then the merge of the partials.
 hipError_t launch_attend(const Shape& s, const uint16_t* q, const uint16_t* K, const uint16_t* V,
                          const int32_t* tok_idx, const int32_t* slot_of, int n_slots,
-                         float* part_ml, float* part_acc, int32_t* arrivals, float* out, float* lse,
-                         hipStream_t st);
+                         float* part_ml, float* part_acc, float* out, float* lse, hipStream_t st);
 
 // Merge of per-split (max, sum, weighted values) partials into out / lse.
 hipError_t launch_combine(const Shape& s, const float* part_ml, const float* part_acc, float* out, float* lse,

@@ -415,6 +415,8 @@ hipError_t offload_step(hsab_offload_engine* e, const uint16_t* q, const uint16_
     float* blk_score = reinterpret_cast<float*>(w + L.blk_score);
     float* part_ml = reinterpret_cast<float*>(w + L.part_ml);
     float* part_acc = reinterpret_cast<float*>(w + L.part_acc);
+    uint32_t* sel_keys = reinterpret_cast<uint32_t*>(w + L.sel_keys);
+    int32_t* sel_cnt = reinterpret_cast<int32_t*>(w + L.sel_cnt);
     hipEvent_t* tm = e->tm[e->step % TIMING_RING];
     int32_t* sel_now = e->sel_d[t & 1];
     const int32_t* resident = e->step == 0 ? sel_now : e->sel_d[(t - 1) & 1];
@@ -427,17 +429,18 @@ hipError_t offload_step(hsab_offload_engine* e, const uint16_t* q, const uint16_
         HSAB_TRY(hipMemcpyAsync(e->kv_h + (size_t)U * s.dk, v_new, (size_t)U * s.dv * sizeof(uint16_t),
                                 hipMemcpyDeviceToHost, cs));
     HSAB_TRY(launch_block_score(s, q, meta, ctx_len, blk_score, nullptr, nullptr, nullptr, nullptr, nullptr,
-                                nullptr, cs));
-    HSAB_TRY(launch_select(s, 1, q, blk_score, nullptr, nullptr, ctx_len, sel_now, nullptr, nullptr, nullptr, cs));
+                                nullptr, sel_cnt, cs));
+    HSAB_TRY(launch_select(s, 1, q, blk_score, nullptr, nullptr, ctx_len, sel_now, nullptr, nullptr, nullptr,
+                           nullptr, cs));
     HSAB_TRY(hipMemcpyAsync(e->sel_h, sel_now, nsel * sizeof(int32_t), hipMemcpyDeviceToHost, cs));
     HSAB_TRY(hipEventRecord(e->ev_sel, cs));
     HSAB_TRY(launch_select(s, 2, q, nullptr, klabel, label_ch, ctx_len, const_cast<int32_t*>(resident), tok_idx,
-                           nullptr, nullptr, cs));
+                           nullptr, sel_keys, sel_cnt, cs));
     if (e->step > 0) {
         HSAB_TRY(hipEventRecord(tm[4], cs));
         HSAB_TRY(hipStreamWaitEvent(cs, e->ev_copy[(t - 1) & 1], 0));
         HSAB_TRY(hipEventRecord(tm[5], cs));
-        HSAB_TRY(launch_attend(s, q, cache, cache, tok_idx, slot_of, e->n_slots, part_ml, part_acc, nullptr, out,
+        HSAB_TRY(launch_attend(s, q, cache, cache, tok_idx, slot_of, e->n_slots, part_ml, part_acc, out,
                                lse, cs));
         HSAB_TRY(hipEventRecord(tm[1], cs));
     }
@@ -472,7 +475,7 @@ hipError_t offload_step(hsab_offload_engine* e, const uint16_t* q, const uint16_
         HSAB_TRY(hipEventRecord(tm[4], cs));
         HSAB_TRY(hipStreamWaitEvent(cs, e->ev_copy[1], 0));
         HSAB_TRY(hipEventRecord(tm[5], cs));
-        HSAB_TRY(launch_attend(s, q, cache, cache, tok_idx, slot_of, e->n_slots, part_ml, part_acc, nullptr, out,
+        HSAB_TRY(launch_attend(s, q, cache, cache, tok_idx, slot_of, e->n_slots, part_ml, part_acc, out,
                                lse, cs));
         HSAB_TRY(hipEventRecord(tm[1], cs));
     }

@@ -50,7 +50,8 @@ template <int MT, int KSW, int KSPLIT>
 __global__ __launch_bounds__(256) void block_score_kernel(
     const uint16_t* __restrict__ q, uint16_t* __restrict__ meta,
     const int32_t* __restrict__ ctx_len, float* __restrict__ score,
-    int Hkv, int G, int dk, int bs, int max_ctx, int nb_cap, int tiles_per_wave, Append ap) {
+    int Hkv, int G, int dk, int bs, int max_ctx, int nb_cap, int tiles_per_wave, Append ap,
+    int32_t* __restrict__ sel_cnt) {
     __shared__ f32x4_t red[KSPLIT > 1 ? SPLIT_TILES * KSPLIT * MT * 64 : 1];
 
     const int unit = blockIdx.y, b = unit / Hkv, g = unit % Hkv;
@@ -60,6 +61,8 @@ __global__ __launch_bounds__(256) void block_score_kernel(
     constexpr int TILES_WG = SCORE_WAVES / KSPLIT;     // block tiles side by side in a workgroup
     const int per_wg = TILES_WG * tiles_per_wave * 16;
     const int j_wg = blockIdx.x * per_wg;
+    if (sel_cnt && blockIdx.x == 0 && threadIdx.x == 0)   // arrival counter of the split token selection
+        __hip_atomic_store(&sel_cnt[unit], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (j_wg >= nb) return;
 
     if (ap.k_new && nb - 1 < j_wg + per_wg) {
@@ -228,7 +231,7 @@ __global__ __launch_bounds__(256) void block_score_kernel(
 
 template <int MT, int KSW, int KSPLIT>
 hipError_t launch_t(const Shape& s, const uint16_t* q, uint16_t* meta, const int32_t* ctx_len,
-                    float* score, const Append& ap, hipStream_t st) {
+                    float* score, const Append& ap, int32_t* sel_cnt, hipStream_t st) {
     constexpr int TILES_WG = SCORE_WAVES / KSPLIT;
     const long tiles = (long)((s.nb_cap + 15) / 16) * s.B * s.Hkv;
     // aim for ~2048 workgroups (8 per CU) before giving a wave more tiles;
@@ -240,31 +243,32 @@ hipError_t launch_t(const Shape& s, const uint16_t* q, uint16_t* meta, const int
     const int per_wg = TILES_WG * tpw * 16;
     dim3 grid((s.nb_cap + per_wg - 1) / per_wg, s.B * s.Hkv);
     hipLaunchKernelGGL((block_score_kernel<MT, KSW, KSPLIT>), grid, dim3(64 * SCORE_WAVES), 0, st, q, meta,
-                       ctx_len, score, s.Hkv, s.G, s.dk, s.bs, s.max_ctx, s.nb_cap, tpw, ap);
+                       ctx_len, score, s.Hkv, s.G, s.dk, s.bs, s.max_ctx, s.nb_cap, tpw, ap, sel_cnt);
     return hipGetLastError();
 }
 
 template <int MT>
 hipError_t launch_mt(const Shape& s, const uint16_t* q, uint16_t* meta, const int32_t* ctx_len, float* score,
-                     const Append& ap, hipStream_t st) {
+                     const Append& ap, int32_t* sel_cnt, hipStream_t st) {
     const int ks = s.dk / 16;
-    if (ks <= 4) return launch_t<MT, 4, 1>(s, q, meta, ctx_len, score, ap, st);
-    if (ks <= 8) return launch_t<MT, 8, 1>(s, q, meta, ctx_len, score, ap, st);
-    if (ks <= 16) return launch_t<MT, 16, 1>(s, q, meta, ctx_len, score, ap, st);
-    if (ks <= 32) return launch_t<MT, 8, 4>(s, q, meta, ctx_len, score, ap, st);
-    if (ks <= 36) return launch_t<MT, 9, 4>(s, q, meta, ctx_len, score, ap, st);    // 576-dim latent keys
-    if (ks <= 40) return launch_t<MT, 10, 4>(s, q, meta, ctx_len, score, ap, st);
-    return launch_t<MT, 16, 4>(s, q, meta, ctx_len, score, ap, st);   // d_k <= 1024: <= 64 steps
+    if (ks <= 4) return launch_t<MT, 4, 1>(s, q, meta, ctx_len, score, ap, sel_cnt, st);
+    if (ks <= 8) return launch_t<MT, 8, 1>(s, q, meta, ctx_len, score, ap, sel_cnt, st);
+    if (ks <= 16) return launch_t<MT, 16, 1>(s, q, meta, ctx_len, score, ap, sel_cnt, st);
+    if (ks <= 32) return launch_t<MT, 8, 4>(s, q, meta, ctx_len, score, ap, sel_cnt, st);
+    if (ks <= 36) return launch_t<MT, 9, 4>(s, q, meta, ctx_len, score, ap, sel_cnt, st);    // 576-dim latent keys
+    if (ks <= 40) return launch_t<MT, 10, 4>(s, q, meta, ctx_len, score, ap, sel_cnt, st);
+    return launch_t<MT, 16, 4>(s, q, meta, ctx_len, score, ap, sel_cnt, st);   // d_k <= 1024: <= 64 steps
 }
 
 }  // namespace
 
 hipError_t launch_block_score(const Shape& s, const uint16_t* q, uint16_t* meta, const int32_t* ctx_len,
                               float* score, const uint16_t* k_new, const uint16_t* v_new, uint16_t* K,
-                              uint16_t* V, uint16_t* klabel, const int32_t* label_ch, hipStream_t st) {
+                              uint16_t* V, uint16_t* klabel, const int32_t* label_ch, int32_t* sel_cnt,
+                              hipStream_t st) {
     const Append ap{k_new, v_new, K, s.valias ? nullptr : V, klabel, label_ch, s.dv, s.r};
-    return s.G <= 16 ? launch_mt<1>(s, q, meta, ctx_len, score, ap, st)
-                     : launch_mt<2>(s, q, meta, ctx_len, score, ap, st);
+    return s.G <= 16 ? launch_mt<1>(s, q, meta, ctx_len, score, ap, sel_cnt, st)
+                     : launch_mt<2>(s, q, meta, ctx_len, score, ap, sel_cnt, st);
 }
 
 }  // namespace hsab

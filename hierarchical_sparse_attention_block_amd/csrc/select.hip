@@ -13,6 +13,14 @@
 // which halves the load round trips of long label rows. Each wave issues
 // eight label-row loads before its MFMAs. Selection keeps all scores in
 // registers and LDS (TopK in topk.h).
+//
+// Split token stage: the label-row gather of one unit is bound by how many
+// misses one CU keeps in flight, so with few units each unit gets `parts`
+// workgroups (on one XCD). Every part selects the blocks itself (part 0
+// writes them), scores its share of the candidate tiles and publishes the
+// keys with agent-scope stores; after its stores have completed, each part
+// bumps the unit's arrival counter, and the part that arrives last reads
+// all keys back (agent-scope loads), runs top-K_t and resets the counter.
 #include <type_traits>
 #include "common.h"
 #include "kernels.h"
@@ -31,8 +39,8 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
     int mode, const uint16_t* __restrict__ q, const float* __restrict__ blk_score,
     const uint16_t* __restrict__ klabel, const int32_t* __restrict__ label_ch,
     const int32_t* __restrict__ ctx_len, int32_t* __restrict__ blk_idx, int32_t* __restrict__ tok_idx,
-    float* __restrict__ tok_score, int32_t* __restrict__ arrivals, int Hkv, int G, int dk, int bs, int r,
-    int kb, int kt, int max_ctx, int nb_cap, int bs_shift) {
+    float* __restrict__ tok_score, uint32_t* __restrict__ gkeys, int32_t* __restrict__ cnt, int parts,
+    int units, int Hkv, int G, int dk, int bs, int r, int kb, int kt, int max_ctx, int nb_cap, int bs_shift) {
     using Sel = TopK<SEL_WAVES, PT>;
     // candidate i sits in slot i / bs of the block list (a shift when bs is a power of two)
     auto slot_of = [&](int i) { return bs_shift >= 0 ? (i >> bs_shift) : i / bs; };
@@ -43,8 +51,13 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
     __shared__ uint4 s_qa4[2 * (MAX_R / 32) * 64];
     uint2* s_qa = reinterpret_cast<uint2*>(s_qa4);
     __shared__ typename Sel::Smem s_sel;
+    __shared__ int s_last;
 
-    const int unit = blockIdx.x, b = unit / Hkv, g = unit % Hkv;
+    // the parts of a unit share an XCD (workgroup L runs on XCD L % 8)
+    const int xcd = blockIdx.x & 7, y = blockIdx.x >> 3;
+    const int unit = (y / parts) * 8 + xcd, part = y % parts;
+    if (unit >= units) return;
+    const int b = unit / Hkv, g = unit % Hkv;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     // block scores are loaded over the whole capacity in the same round trip
     // as ctx_len and masked once n is known; the entry layout of the block
@@ -59,7 +72,6 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
             sraw[j] = (j < pt_b && i < nb_cap) ? S[i] : 0.f;
         }
     }
-    if (arrivals && threadIdx.x == 0) arrivals[unit] = 0;   // for the attention split merge
     int n = ctx_len[b];
     n = n < 1 ? 1 : (n > max_ctx ? max_ctx : n);
     const int nb = (n + bs - 1) / bs;
@@ -104,11 +116,11 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
         int32_t* bo = blk_idx + (size_t)unit * kb;
         const int keff = Sel::select(bkey, pt_b, kb, s_sel, [&](int pos, int i) {
             s_blk[pos] = i;
-            bo[pos] = i;
+            if (part == 0) bo[pos] = i;
         });
         for (int p = keff + threadIdx.x; p < kb; p += SEL_THREADS) {
             s_blk[p] = -1;
-            bo[p] = -1;
+            if (part == 0) bo[p] = -1;
         }
     } else {
         for (int p = threadIdx.x; p < kb; p += SEL_THREADS) s_blk[p] = blk_idx[(size_t)unit * kb + p];
@@ -121,12 +133,13 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
     const uint16_t* Lu = klabel + (size_t)unit * max_ctx * r;
     float* TS = tok_score ? tok_score + (size_t)unit * ncand : nullptr;
     const int n_tiles = (ncand + 15) / 16;
+    const int t_lo = part * n_tiles / parts, t_hi = (part + 1) * n_tiles / parts;   // this part's tiles
     // eight label loads in flight per lane: load u feeds step u % KSr of
     // tile u / KSr of the batch (KSr is a power of two <= 8)
     const int lg = KSr == 1 ? 0 : KSr == 2 ? 1 : KSr == 4 ? 2 : 3;
     const int tb = 8 >> lg;                         // tiles per batch
     using Frag = typename std::conditional<KK == 32, uint4, uint2>::type;
-    for (int t0 = w; t0 < n_tiles; t0 += SEL_WAVES * tb) {
+    for (int t0 = t_lo + w; t0 < t_hi; t0 += SEL_WAVES * tb) {
         Frag bf[8];
         uint32_t vmask = 0;   // bit u: the token this lane loads for load u is valid
 #pragma unroll
@@ -134,7 +147,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
             const int tile = t0 + (u >> lg) * SEL_WAVES, st = u & (KSr - 1);
             const int i = tile * 16 + (lane & 15);
             const int slot = slot_of(i), off = i - slot * bs;
-            const int blk = (tile < n_tiles && i < ncand) ? s_blk[slot] : -1;
+            const int blk = (tile < t_hi && i < ncand) ? s_blk[slot] : -1;
             const int pos = blk * bs + off;
             const bool valid = blk >= 0 && blk < nb && pos < n;
             vmask |= (valid ? 1u : 0u) << u;
@@ -162,7 +175,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
                     acc1 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_i16x4(s_qa[(SMAX + st) * 64 + lane]), bfrag,
                                                                      acc1, 0, 0, 0);
             }
-            if (st == KSr - 1 && tile < n_tiles) {
+            if (st == KSr - 1 && tile < t_hi) {
                 float v = -INFINITY;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -177,13 +190,28 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
                 const int i = tile * 16 + (lane & 15);
                 if (lane < 16 && i < ncand) {
                     const bool valid = (vmask >> u) & 1u;
-                    s_key[i] = valid ? f32_key(v) : 0u;
+                    const uint32_t kv = valid ? f32_key(v) : 0u;
+                    if (parts > 1)
+                        __hip_atomic_store(&gkeys[(size_t)unit * ncand + i], kv, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+                    else
+                        s_key[i] = kv;
                     if (TS) TS[i] = valid ? v : -INFINITY;
                 }
             }
         }
     }
-    __syncthreads();
+    if (parts > 1) {
+        // this part's key stores are complete before the arrival is counted
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+        __syncthreads();
+        if (threadIdx.x == 0)
+            s_last = __hip_atomic_fetch_add(&cnt[unit], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == parts - 1;
+        __syncthreads();
+        if (!s_last) return;
+    } else {
+        __syncthreads();
+    }
 
     // ----------------------------------------------------------- top-K_t
     const int pt = (ncand + SEL_THREADS - 1) / SEL_THREADS;
@@ -191,7 +219,13 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
 #pragma unroll
     for (int j = 0; j < PT; ++j) {
         const int i = (w * pt + j) * 64 + lane;
-        key[j] = (j < pt && i < ncand) ? s_key[i] : 0u;
+        const bool in = j < pt && i < ncand;
+        if (parts > 1)
+            key[j] = in ? __hip_atomic_load(&gkeys[(size_t)unit * ncand + i], __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT)
+                        : 0u;
+        else
+            key[j] = in ? s_key[i] : 0u;
     }
     int32_t* to = tok_idx + (size_t)unit * kt;
     const int keff_t = Sel::select(key, pt, kt, s_sel, [&](int p, int i) {
@@ -199,21 +233,33 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
         to[p] = s_blk[slot] * bs + (i - slot * bs);
     });
     for (int p = keff_t + threadIdx.x; p < kt; p += SEL_THREADS) to[p] = -1;
+    if (parts > 1 && threadIdx.x == 0)   // ready for the next call
+        __hip_atomic_store(&cnt[unit], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int PT>
 hipError_t launch_t(const Shape& s, int mode, const uint16_t* q, const float* blk_score,
                     const uint16_t* klabel, const int32_t* label_ch, const int32_t* ctx_len,
-                    int32_t* blk_idx, int32_t* tok_idx, float* tok_score, int32_t* arrivals, hipStream_t st) {
+                    int32_t* blk_idx, int32_t* tok_idx, float* tok_score, uint32_t* gkeys, int32_t* cnt,
+                    hipStream_t st) {
     const int shift = (s.bs & (s.bs - 1)) ? -1 : __builtin_ctz(s.bs);
+    const int units = s.B * s.Hkv;
+    // parts per unit: enough workgroups to cover the CUs, at least eight
+    // candidate tiles (half a tile per wave) each
+    int parts = 1;
+    if ((mode & 2) && gkeys && cnt) {
+        const int n_tiles = (s.kb * s.bs + 15) / 16;
+        while (parts < 32 && (long)parts * 2 * units <= 256 && parts * 2 * 8 <= n_tiles) parts *= 2;
+    }
+    const dim3 grid(((units + 7) / 8) * 8 * parts);
     if (s.r >= 32)
-        hipLaunchKernelGGL((select_kernel<PT, 32>), dim3(s.B * s.Hkv), dim3(SEL_THREADS), 0, st, mode, q, blk_score,
-                           klabel, label_ch, ctx_len, blk_idx, tok_idx, tok_score, arrivals, s.Hkv, s.G, s.dk, s.bs,
-                           s.r, s.kb, s.kt, s.max_ctx, s.nb_cap, shift);
+        hipLaunchKernelGGL((select_kernel<PT, 32>), grid, dim3(SEL_THREADS), 0, st, mode, q, blk_score, klabel,
+                           label_ch, ctx_len, blk_idx, tok_idx, tok_score, gkeys, cnt, parts, units, s.Hkv, s.G,
+                           s.dk, s.bs, s.r, s.kb, s.kt, s.max_ctx, s.nb_cap, shift);
     else
-        hipLaunchKernelGGL((select_kernel<PT, 16>), dim3(s.B * s.Hkv), dim3(SEL_THREADS), 0, st, mode, q, blk_score,
-                           klabel, label_ch, ctx_len, blk_idx, tok_idx, tok_score, arrivals, s.Hkv, s.G, s.dk, s.bs,
-                           s.r, s.kb, s.kt, s.max_ctx, s.nb_cap, shift);
+        hipLaunchKernelGGL((select_kernel<PT, 16>), grid, dim3(SEL_THREADS), 0, st, mode, q, blk_score, klabel,
+                           label_ch, ctx_len, blk_idx, tok_idx, tok_score, gkeys, cnt, parts, units, s.Hkv, s.G,
+                           s.dk, s.bs, s.r, s.kb, s.kt, s.max_ctx, s.nb_cap, shift);
     return hipGetLastError();
 }
 
@@ -221,18 +267,18 @@ hipError_t launch_t(const Shape& s, int mode, const uint16_t* q, const float* bl
 
 hipError_t launch_select(const Shape& s, int mode, const uint16_t* q, const float* blk_score,
                          const uint16_t* klabel, const int32_t* label_ch, const int32_t* ctx_len,
-                         int32_t* blk_idx, int32_t* tok_idx, float* tok_score, int32_t* arrivals,
-                         hipStream_t st) {
+                         int32_t* blk_idx, int32_t* tok_idx, float* tok_score, uint32_t* sel_keys,
+                         int32_t* sel_cnt, hipStream_t st) {
     int need = 1;
     if (mode & 1) need = (s.nb_cap + SEL_THREADS - 1) / SEL_THREADS;
     if (mode & 2) {
         const int t = (s.kb * s.bs + SEL_THREADS - 1) / SEL_THREADS;
         need = t > need ? t : need;
     }
-    if (need <= 1) return launch_t<1>(s, mode, q, blk_score, klabel, label_ch, ctx_len, blk_idx, tok_idx, tok_score, arrivals, st);
-    if (need <= 2) return launch_t<2>(s, mode, q, blk_score, klabel, label_ch, ctx_len, blk_idx, tok_idx, tok_score, arrivals, st);
-    if (need <= 4) return launch_t<4>(s, mode, q, blk_score, klabel, label_ch, ctx_len, blk_idx, tok_idx, tok_score, arrivals, st);
-    return launch_t<8>(s, mode, q, blk_score, klabel, label_ch, ctx_len, blk_idx, tok_idx, tok_score, arrivals, st);
+    if (need <= 1) return launch_t<1>(s, mode, q, blk_score, klabel, label_ch, ctx_len, blk_idx, tok_idx, tok_score, sel_keys, sel_cnt, st);
+    if (need <= 2) return launch_t<2>(s, mode, q, blk_score, klabel, label_ch, ctx_len, blk_idx, tok_idx, tok_score, sel_keys, sel_cnt, st);
+    if (need <= 4) return launch_t<4>(s, mode, q, blk_score, klabel, label_ch, ctx_len, blk_idx, tok_idx, tok_score, sel_keys, sel_cnt, st);
+    return launch_t<8>(s, mode, q, blk_score, klabel, label_ch, ctx_len, blk_idx, tok_idx, tok_score, sel_keys, sel_cnt, st);
 }
 
 }  // namespace hsab

@@ -97,8 +97,11 @@ typedef struct hsab_dims {
 } hsab_dims;
 
 /* Bytes of device workspace the calls below need for these dims (the same
- * size serves every call). The workspace holds block scores, token scores
- * and split-attention partials; it needs no initialisation. */
+ * size serves every call). The workspace holds block scores, token scores,
+ * split-attention partials and the keys and arrival counters of a token
+ * selection spread over several workgroups per (batch, KV head); it needs
+ * no initialisation (the calls that use the counters set them first).
+ * Calls that overlap on one workspace race. */
 size_t hsab_workspace_bytes(const hsab_dims* dims);
 
 /* Static text for a status code. */

@@ -40,7 +40,10 @@ def test_workspace_layout():
     U, Hq = 4, 16
     splits = -(-64 // 64)
     al = lambda x: (x + 255) // 256 * 256
-    want = al(U * d.nb_cap * 4) + al(Hq * splits * 2 * 4) + al(Hq * splits * 128 * 4) + al(U * 4)
+    # block scores, split (max, sum), split accumulators, selection keys
+    # (K_b * block candidates per unit), selection arrival counters
+    want = (al(U * d.nb_cap * 4) + al(Hq * splits * 2 * 4) + al(Hq * splits * 128 * 4)
+            + al(U * d.k_blocks * d.block * 4) + al(U * 4))
     assert H.workspace_bytes(d) == want
     assert H.workspace_bytes(_dims(n_q_heads=7)) == 0          # Hq % Hkv != 0
 
