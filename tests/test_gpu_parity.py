@@ -159,6 +159,17 @@ def test_decode_step_ragged(kw):
     say(kw, st)
 
 
+def test_decode_step_many_units_one_workgroup_each():
+    """256 (batch, KV head) units: the token stage runs one workgroup per
+    unit (no split over workgroups); every unit against the oracle."""
+    w = _wl(batch=64, n_q_heads=16, n_kv_heads=4, max_ctx=320, ctx=320, k_blocks=8, k_tokens=48, n_planted=2)
+    rng = np.random.default_rng(5)
+    ctx = rng.integers(2, 321, size=w.batch).astype(np.int32)
+    w, h, dev, r = _run_decode(w, ctx)
+    st = _check_all_units(w, h, r)
+    say("256 units", st[:3])
+
+
 def test_decode_step_single_token_and_partial_block():
     w = _wl(batch=3, max_ctx=64, ctx=64, k_blocks=4, k_tokens=32, n_planted=0)
     ctx = np.array([1, 7, 64], np.int32)
