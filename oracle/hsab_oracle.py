@@ -38,6 +38,17 @@ Readings where the pages are silent (all fixed here, none printed there):
 * attention logits are sm_scale * q.k; out is fp64 here (fp32 on the GPU);
   lse is the natural-log logsumexp of those logits.
 
+Quantised block metadata (``e4m3_*``, ``block_meta_e4m3``): the pages name
+quantisation of the index data as a way to cut the indexing cost
+[gist.science/de, section 2.A "Stufe 2"] and give no scheme. Reading taken
+here: the block max row rounded up and the min row rounded down to the fp8
+e4m3 grid (OCP "fn" variant: bias 7, 3 mantissa bits, subnormals, no
+infinities, largest finite 448, saturating), so every block bound stays an
+upper bound of the true block maximum. These functions are pinned to the
+format's bit-field definition, to an independent fp8 decoder and to that
+bound invariant; against the pages themselves the scheme is a reading
+(parity unpinned: the pages print no quantised value).
+
 Offload (``offload_*``): the fine stage of step t runs over the blocks
 selected at step t-1 while step t's new blocks are fetched; only the set
 difference of consecutive block selections is transferred
@@ -53,6 +64,7 @@ __all__ = [
     "bf16_to_f64", "n_blocks", "block_meta", "append_meta", "quest_bound",
     "quest_bound_gemm", "block_scores", "topk_stable", "candidate_tokens",
     "label_scores", "attend", "select_tokens_unit", "decode_unit",
+    "e4m3_grid", "e4m3_round", "block_meta_e4m3",
     "decode_all", "offload_delta", "offload_held", "offload_schedule", "offload_run",
 ]
 
@@ -102,6 +114,45 @@ def append_meta(kmax: np.ndarray, kmin: np.ndarray, k: np.ndarray, pos: int, bs:
         kmax[j] = np.maximum(kmax[j], k)
         kmin[j] = np.minimum(kmin[j], k)
     return kmax, kmin
+
+
+# ------------------------------------------- quantised metadata (fp8 e4m3)
+def e4m3_grid():
+    """Every finite fp8 e4m3 ("fn") value by code: sign bit, exponent field
+    e (4 bits, bias 7), mantissa m (3 bits); e = 0 is subnormal, m/8 * 2^-6;
+    otherwise (1 + m/8) * 2^(e-7); codes 0x7f and 0xff are NaN.
+
+    Returns (codes uint8 [254], values float64 [254])."""
+    codes, vals = [], []
+    for c in range(256):
+        if c & 0x7F == 0x7F:
+            continue
+        sgn, e, m = c >> 7, (c >> 3) & 0xF, c & 0x7
+        v = (m / 8.0) * 2.0 ** -6 if e == 0 else (1.0 + m / 8.0) * 2.0 ** (e - 7)
+        codes.append(c)
+        vals.append(-v if sgn else v)
+    return np.array(codes, np.uint8), np.array(vals, np.float64)
+
+
+def e4m3_round(x, up: bool) -> np.ndarray:
+    """Outward rounding to the e4m3 grid: up = the smallest grid value >= x,
+    down = the largest grid value <= x; beyond the largest magnitude (448)
+    the result saturates at +-448."""
+    _, vals = e4m3_grid()
+    grid = np.unique(vals)                          # sorted, +0 and -0 merged
+    x = np.asarray(x, np.float64)
+    if up:
+        i = np.searchsorted(grid, x, side="left")   # first grid value >= x
+        return grid[np.minimum(i, grid.size - 1)]
+    i = np.searchsorted(grid, x, side="right") - 1  # last grid value <= x
+    return grid[np.maximum(i, 0)]
+
+
+def block_meta_e4m3(K: np.ndarray, n: int, bs: int):
+    """Block metadata quantised outward to e4m3: (round_up(kmax),
+    round_down(kmin)) of ``block_meta``."""
+    kmax, kmin = block_meta(K, n, bs)
+    return e4m3_round(kmax, True), e4m3_round(kmin, False)
 
 
 # ----------------------------------------------------- step 3: block scoring
@@ -182,12 +233,15 @@ def select_tokens_unit(q, K, n, bs, blk_idx, label_ch, k_tokens):
     return cand[keep], cand, s_tok
 
 
-def decode_unit(q, K, V, n, bs, k_blocks, label_ch, k_tokens, sm_scale, meta=None):
+def decode_unit(q, K, V, n, bs, k_blocks, label_ch, k_tokens, sm_scale, meta=None, meta_fp8=False):
     """One decode step of one unit over its first n tokens (the appended
     token included). q [G, d_k] float64; K [>=n, d_k], V [>=n, d_v] float64.
+    meta_fp8: block metadata quantised outward to e4m3 (``block_meta_e4m3``).
 
     Returns a dict with the intermediate results of every stage."""
-    kmax, kmin = block_meta(K, n, bs) if meta is None else meta
+    if meta is None:
+        meta = block_meta_e4m3(K, n, bs) if meta_fp8 else block_meta(K, n, bs)
+    kmax, kmin = meta
     s_blk = block_scores(q, kmax, kmin)
     blk = topk_stable(s_blk, k_blocks)
     tok, cand, s_tok = select_tokens_unit(q, K, n, bs, blk, label_ch, k_tokens)
@@ -197,7 +251,7 @@ def decode_unit(q, K, V, n, bs, k_blocks, label_ch, k_tokens, sm_scale, meta=Non
 
 
 def decode_all(q_bits, K_bits, V_bits, ctx_len, n_kv_heads, bs, k_blocks, label_ch,
-               k_tokens, sm_scale, units=None):
+               k_tokens, sm_scale, units=None, meta_fp8=False):
     """Decode step over all (or the listed) units of a batch.
 
     q_bits [B, Hq, d_k]; K_bits [B, Hkv, cap, d_k]; V_bits [B, Hkv, cap, d_v],
@@ -217,7 +271,7 @@ def decode_all(q_bits, K_bits, V_bits, ctx_len, n_kv_heads, bs, k_blocks, label_
         else:
             V = bf16_to_f64(V_bits[b, g, :n])
         res[(b, g)] = decode_unit(q, K, V, n, bs, k_blocks, np.asarray(label_ch[g]),
-                                  k_tokens, sm_scale)
+                                  k_tokens, sm_scale, meta_fp8=meta_fp8)
     return res
 
 

@@ -332,3 +332,71 @@ def test_offload_run_attends_over_previous_selection():
         assert r["delta_bytes"] == len(r["delta"]) * bs * 2 * d * 2
         # every transferred block was selected at this step
         assert set(r["delta"]) <= set(r["sel"])
+
+
+# ------------------------------------------- quantised metadata (fp8 e4m3)
+def test_e4m3_grid_matches_an_independent_decoder():
+    """The grid built from the bit-field definition equals torch's
+    float8_e4m3fn decode of the same 256 codes (NaN codes excluded)."""
+    codes, vals = O.e4m3_grid()
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).float().double().numpy()
+    assert len(codes) == 254 and 0x7F not in codes and 0xFF not in codes
+    assert np.all(np.isnan(ref[[0x7F, 0xFF]]))
+    np.testing.assert_array_equal(vals, ref[codes])
+
+
+def test_e4m3_landmarks_of_the_format():
+    """Largest finite 448 (0x7e), smallest normal 2^-6 (0x08), smallest
+    subnormal 2^-9 (0x01), one at 0x38 with a step of 1/8 above it."""
+    codes, vals = O.e4m3_grid()
+    v = dict(zip(codes.tolist(), vals.tolist()))
+    assert v[0x7E] == 448.0 and vals.max() == 448.0 and vals.min() == -448.0
+    assert v[0x08] == 2.0 ** -6 and v[0x01] == 2.0 ** -9 and v[0x38] == 1.0 and v[0x39] == 1.125
+    assert v[0x80 | 0x38] == -1.0
+
+
+def test_e4m3_outward_rounding_brute_force():
+    """round_up(x) is the smallest grid value >= x and round_down(x) the
+    largest <= x (by a scan of the grid), saturating at +-448; grid values
+    map to themselves; torch's round-to-nearest result lies between them."""
+    _, vals = O.e4m3_grid()
+    r = np.random.default_rng(3)
+    x = np.concatenate([r.uniform(-500, 500, 3000), r.uniform(-0.05, 0.05, 2000),
+                        r.standard_normal(2000) * 2.0 ** r.integers(-12, 9, 2000), vals])
+    x = O.bf16_to_f64(W.f32_to_bf16_bits(x.astype(np.float32)))
+    up, dn = O.e4m3_round(x, True), O.e4m3_round(x, False)
+    for xi, u, d in zip(x, up, dn):
+        above, below = vals[vals >= xi], vals[vals <= xi]
+        assert u == (above.min() if above.size else 448.0)
+        assert d == (below.max() if below.size else -448.0)
+    on = np.isin(x, vals)
+    np.testing.assert_array_equal(up[on], x[on])
+    np.testing.assert_array_equal(dn[on], x[on])
+    inr = np.abs(x) <= 448
+    rne = torch.from_numpy(x[inr]).float().to(torch.float8_e4m3fn).double().numpy()
+    assert np.all((dn[inr] <= rne) & (rne <= up[inr]))
+    assert np.all((rne == dn[inr]) | (rne == up[inr]))
+
+
+@pytest.mark.parametrize("n,bs,scale", [(200, 16, 1.0), (97, 8, 30.0), (64, 32, 0.01)])
+def test_quantised_bound_dominates_exact_bound_and_true_max(n, bs, scale):
+    """Outward-rounded metadata keeps the Quest property: its bound is >= the
+    exact-metadata bound, which is >= the true block maximum of q.k."""
+    q, K, _ = _rand_unit(n + 7 * bs, 4, 32, n, scale=scale)
+    kmax, kmin = O.block_meta(K, n, bs)
+    qmax, qmin = O.block_meta_e4m3(K, n, bs)
+    assert np.all(qmax >= kmax) and np.all(qmin <= kmin)
+    ub, ubq = O.quest_bound(q, kmax, kmin), O.quest_bound(q, qmax, qmin)
+    assert np.all(ubq >= ub - 1e-12)
+    for j in range(kmax.shape[0]):
+        true = q @ K[j * bs: min(n, (j + 1) * bs)].T
+        assert np.all(ubq[:, j] >= true.max(axis=1) - 1e-12)
+
+
+def test_quantised_meta_is_exact_for_keys_on_the_grid():
+    """Keys that are e4m3 values give the same metadata either way."""
+    _, vals = O.e4m3_grid()
+    r = np.random.default_rng(8)
+    K = r.choice(vals[np.abs(vals) <= 64], size=(50, 16))
+    for a, b in zip(O.block_meta(K, 50, 8), O.block_meta_e4m3(K, 50, 8)):
+        np.testing.assert_array_equal(a, b)
