@@ -17,6 +17,7 @@ Prints one JSON line.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import math
@@ -46,7 +47,11 @@ def log(*a):
 
 def dims_of(w):
     return H.dims(w.batch, w.n_q_heads, w.n_kv_heads, w.d_k, w.d_v, w.v_alias_k, w.block, w.r,
-                  w.k_blocks, w.k_tokens, w.max_ctx, w.sm_scale)
+                  w.k_blocks, w.k_tokens, w.max_ctx, w.sm_scale, H.META_FP8 if w.meta_fp8 else H.META_BF16)
+
+
+def meta_value_bytes(w):
+    return 1 if w.meta_fp8 else 2
 
 
 def step_bytes(w):
@@ -54,7 +59,7 @@ def step_bytes(w):
     block metadata, label rows of the kept blocks, gathered K/V rows of the
     kept tokens, queries and outputs."""
     U, nb = w.units, -(-w.ctx // w.block)
-    meta = U * nb * 2 * w.d_k * 2
+    meta = U * nb * 2 * w.d_k * meta_value_bytes(w)
     labels = U * min(w.k_blocks, nb) * w.block * w.r * 2
     kv_row = (w.d_k if w.v_alias_k else w.d_k + w.d_v) * 2
     gather = U * min(w.k_tokens, min(w.k_blocks, nb) * w.block) * kv_row
@@ -67,7 +72,7 @@ def score_kernel_bytes(w):
     """Algorithmic bytes of one block-score launch: every metadata row read
     once, the queries read once, one fp32 score written per block."""
     U, nb = w.units, -(-w.ctx // w.block)
-    return U * nb * (2 * w.d_k * 2 + 4) + w.batch * w.n_q_heads * w.d_k * 2
+    return U * nb * (2 * w.d_k * meta_value_bytes(w) + 4) + w.batch * w.n_q_heads * w.d_k * 2
 
 
 def source_hash(paths):
@@ -110,13 +115,100 @@ def stage(w, threads):
         "label": torch.from_numpy(lab).cuda(),
         "ctx": torch.full((w.batch,), w.ctx, dtype=torch.int32, device="cuda"),
         "ctx_prefill": torch.full((w.batch,), w.ctx - 1, dtype=torch.int32, device="cuda"),
-        "meta": torch.zeros(U * d.nb_cap * 2 * w.d_k, dtype=torch.int16, device="cuda"),
+        "meta": H.alloc_meta(d),
         "klabel": torch.zeros(U * w.max_ctx * w.r, dtype=torch.int16, device="cuda"),
     }
     H.build_meta(d, base["K"], base["ctx_prefill"], base["label"], base["meta"], base["klabel"])
     torch.cuda.synchronize()
     host = {"q": q, "K": K, "V": V, "k_new": k_new, "v_new": v_new, "label": lab}
     return d, base, host
+
+
+def time_replays(fns, stream, warmup, steps, graphs=True):
+    """Average ms per call of fns[i % len(fns)] over `steps` calls, each
+    captured once as a HIP graph and replayed (after an eager warmup call of
+    every fn and `warmup` untimed calls)."""
+    with torch.cuda.stream(stream):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    gr = []
+    if graphs:
+        for f in fns:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                f()
+            gr.append(g)
+        torch.cuda.synchronize()
+    call = (lambda i: gr[i % len(gr)].replay()) if graphs else (lambda i: fns[i % len(fns)]())
+    with torch.cuda.stream(stream):
+        for i in range(warmup):
+            call(i)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        ev0.record(stream)
+        for i in range(steps):
+            call(i)
+        ev1.record(stream)
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) / steps
+
+
+def time_score_launches(d, base, metas, reps, stream, steps):
+    """us per block-score launch: a graph of 8 launches per cache copy,
+    back to back, replayed; HIP events on the launching stream."""
+    R = len(reps)
+    n_score = 8 * R
+    with torch.cuda.stream(stream):
+        for m, r in zip(metas, reps):
+            H.score_blocks(d, base["q"], m, base["ctx"], r.score, stream=stream)
+    torch.cuda.synchronize()
+    gs = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gs, stream=stream):
+        for i in range(n_score):
+            H.score_blocks(d, base["q"], metas[i % R], base["ctx"], reps[i % R].score, stream=stream)
+    with torch.cuda.stream(stream):
+        gs.replay()
+    torch.cuda.synchronize()
+    n_rep = max(1, steps // n_score)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        ev0.record(stream)
+        for _ in range(n_rep):
+            gs.replay()
+        ev1.record(stream)
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) * 1e3 / (n_rep * n_score)
+
+
+def fp8_meta_leg(w, base, reps, stream, args, ms_step_bf16):
+    """The same decode step with block metadata in outward-rounded fp8 e4m3
+    (half the bytes of the block-score stream): own metadata per cache copy,
+    built from the same keys; the rest of the step is unchanged."""
+    w8 = dataclasses.replace(w, meta_fp8=True)
+    d8 = dims_of(w8)
+    metas = []
+    for r in reps:
+        m = H.alloc_meta(d8)
+        H.build_meta(d8, r.K, base["ctx_prefill"], base["label"], m, r.klabel)
+        metas.append(m)
+    torch.cuda.synchronize()
+
+    def dec(i):
+        r = reps[i]
+        return lambda: H.decode_step(d8, base["q"], base["k_new"], base["v_new"], r.K, r.V, metas[i], r.klabel,
+                                     base["label"], base["ctx"], r.blk, r.tok, r.out, r.lse, r.ws, stream=stream)
+    ms = time_replays([dec(i) for i in range(len(reps))], stream, args.warmup, args.steps, not args.no_graph)
+    us_score = time_score_launches(d8, base, metas, reps, stream, args.steps)
+    kb = score_kernel_bytes(w8)
+    ach = kb / (us_score * 1e-6) / 1e9
+    log(f"[bench] fp8 metadata: {ms * 1e3:.1f} us/step, block score {us_score:.2f} us/launch ({ach:.0f} GB/s)")
+    return {"format": "e4m3, max rounded up, min rounded down", "ms_per_step": round(ms, 6),
+            "queries_per_s": round(w.batch * w.n_q_heads / (ms * 1e-3), 1),
+            "step_speedup_vs_bf16_meta": round(ms_step_bf16 / ms, 3),
+            "block_score": {"us_per_launch": round(us_score, 3), "algorithmic_bytes": kb,
+                            "achieved": round(ach, 1), "frac": round(ach / HBM_PEAK_GBS, 4)}}
 
 
 def decode(d, base, rep, stream):
@@ -146,7 +238,8 @@ def cpu_baseline(w, host, budget_s=10.0, n_units=4):
             Vb[n - 1] = host["v_new"][b, g]
             V = O.bf16_to_f64(Vb)
         q = O.bf16_to_f64(host["q"][b, g * G:(g + 1) * G])
-        units.append((q, K, V, O.block_meta(K, n, w.block), host["label"][g]))
+        meta_fn = O.block_meta_e4m3 if w.meta_fp8 else O.block_meta
+        units.append((q, K, V, meta_fn(K, n, w.block), host["label"][g]))
     done, spent = 0, 0.0
     with threadpool_limits(limits=1):
         while spent < budget_s:
@@ -171,6 +264,8 @@ def offload_bench(args):
     how much of it the compute stream did not wait for (overlap), next to
     the same 16 steps on an HBM-resident cache."""
     w = W.WORKLOADS[args.workload]
+    if args.meta == "fp8":
+        w = dataclasses.replace(w, meta_fp8=True)
     steps = W.OFFLOAD_STEPS
     d = dims_of(w)
     U, B, Hkv, bs = w.units, w.batch, w.n_kv_heads, w.block
@@ -203,7 +298,7 @@ def offload_bench(args):
             Kv[u, :n] = torch.from_numpy(kb.view(np.int16))
             Vv[u, :n] = torch.from_numpy(vb.view(np.int16))
     label = torch.from_numpy(W.label_channels(w)).cuda()
-    meta0 = torch.zeros(U * nb_cap * 2 * w.d_k, dtype=torch.int16, device="cuda")
+    meta0 = H.alloc_meta(d)
     klabel0 = torch.zeros(U * w.max_ctx * w.r, dtype=torch.int16, device="cuda")
     H.build_meta(d, Kd, torch.from_numpy(prefill).cuda(), label, meta0, klabel0)
     qs = [q0]
@@ -355,6 +450,10 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of graph replay")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--threads", type=int, default=16)
+    ap.add_argument("--meta", default="bf16", choices=["bf16", "fp8"],
+                    help="block metadata format of the timed step (fp8: e4m3, rounded outward)")
+    ap.add_argument("--no-fp8-leg", action="store_true",
+                    help="skip the extra timing of the step with fp8 metadata")
     ap.add_argument("--offload-runs", type=int, default=3, help="timed 16-step runs of the offload workload")
     ap.add_argument("--score-only", type=int, default=0,
                     help="only launch the block-score kernel this many times (for counter runs)")
@@ -366,6 +465,8 @@ def main():
         sys.exit(2)
 
     w = W.WORKLOADS[args.workload]
+    if args.meta == "fp8":
+        w = dataclasses.replace(w, meta_fp8=True)
     torch.cuda.set_device(0)
     if w.name == "offload96k":
         offload_bench(args)
@@ -395,70 +496,18 @@ def main():
         log(f"[bench] score-only: {args.score_only} launches, then a copy of {a.numel() * 4} bytes")
         return
 
-    # eager warmup (loads code objects before any capture)
-    with torch.cuda.stream(stream):
-        for r in reps:
-            decode(d, base, r, stream)
-    torch.cuda.synchronize()
-
-    graphs = []
-    if not args.no_graph:
-        for r in reps:
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=stream):
-                decode(d, base, r, stream)
-            graphs.append(g)
-        torch.cuda.synchronize()
-
-    def run(i):
-        if graphs:
-            graphs[i % R].replay()
-        else:
-            decode(d, base, reps[i % R], stream)
-
-    with torch.cuda.stream(stream):
-        for i in range(args.warmup):
-            run(i)
-    torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    with torch.cuda.stream(stream):
-        t0 = time.perf_counter()
-        ev0.record(stream)
-        for i in range(args.steps):
-            run(i)
-        ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = ev0.elapsed_time(ev1) / args.steps
-    log(f"[bench] {args.steps} steps: {ms_step * 1e3:.1f} us/step (events), wall {wall / args.steps * 1e6:.1f} us/step")
+    ms_step = time_replays([(lambda r=r: decode(d, base, r, stream)) for r in reps], stream, args.warmup,
+                           args.steps, not args.no_graph)
+    log(f"[bench] {args.steps} steps: {ms_step * 1e3:.1f} us/step (events)")
 
     # dominant kernel alone: a graph of back-to-back block-score launches
-    n_score = 8 * R
-    gs = torch.cuda.CUDAGraph()
-    with torch.cuda.stream(stream):
-        for r in reps:
-            H.score_blocks(d, base["q"], r.meta, base["ctx"], r.score, stream=stream)
-    torch.cuda.synchronize()
-    with torch.cuda.graph(gs, stream=stream):
-        for i in range(n_score):
-            r = reps[i % R]
-            H.score_blocks(d, base["q"], r.meta, base["ctx"], r.score, stream=stream)
-    with torch.cuda.stream(stream):
-        gs.replay()
-    torch.cuda.synchronize()
-    reps_score = max(1, args.steps // n_score)
-    with torch.cuda.stream(stream):
-        ev0.record(stream)
-        for _ in range(reps_score):
-            gs.replay()
-        ev1.record(stream)
-    torch.cuda.synchronize()
-    us_score = ev0.elapsed_time(ev1) * 1e3 / (reps_score * n_score)
+    us_score = time_score_launches(d, base, [r.meta for r in reps], reps, stream, args.steps)
     kb = score_kernel_bytes(w)
     achieved = kb / (us_score * 1e-6) / 1e9
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
     traffic = None
-    cpath = COUNTERS.format(wl=w.name)
+    cpath = COUNTERS.format(wl=w.name + ("_fp8" if w.meta_fp8 else ""))
     if os.path.exists(cpath):
         c = json.load(open(cpath))
         if c.get("source_hash") == source_hash(SCORE_SOURCES):
@@ -506,7 +555,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "q_heads": w.n_q_heads, "kv_heads": w.n_kv_heads,
                    "d_k": w.d_k, "d_v": w.d_v, "ctx": w.ctx, "block": w.block, "k_blocks": w.k_blocks,
-                   "r": w.r, "k_tokens": w.k_tokens, "cache_replicas": R, "hip_graph": bool(graphs),
+                   "r": w.r, "k_tokens": w.k_tokens, "meta": "fp8_e4m3_outward" if w.meta_fp8 else "bf16",
+                   "cache_replicas": R, "hip_graph": not args.no_graph,
                    "parallelism": "none (1 GPU)"},
         "hbm_frac_step": round(sb["total"] / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "step_bytes": sb["total"],
@@ -516,6 +566,8 @@ def main():
     }
     if dense is not None:
         res["dense_reference"] = dense
+    if not w.meta_fp8 and not args.no_fp8_leg and w.d_k % 32 == 0:
+        res["meta_fp8"] = fp8_meta_leg(w, base, reps, stream, args, ms_step)
     if not args.no_cpu:
         log("[bench] timing the CPU oracle on a bounded sample")
         res["cpu_baseline"] = cpu_baseline(w, host)

@@ -19,6 +19,7 @@ Shape make_shape(const hsab_dims& d) {
     s.bs = d.block; s.r = d.r; s.kb = d.k_blocks; s.kt = d.k_tokens; s.max_ctx = d.max_ctx;
     s.nb_cap = d.block > 0 ? (d.max_ctx + d.block - 1) / d.block : 0;
     s.sm_scale = d.sm_scale;
+    s.meta8 = d.meta_format == HSAB_META_FP8;
     return s;
 }
 
@@ -58,6 +59,8 @@ static int check_dims(const hsab_dims* d) {
     if (d->k_tokens < 1) return HSAB_EINVAL;
     if ((d->max_ctx + d->block - 1) / d->block > MAX_NB) return HSAB_EINVAL;
     if (!isfinite(d->sm_scale)) return HSAB_EINVAL;
+    if (d->meta_format != HSAB_META_BF16 && d->meta_format != HSAB_META_FP8) return HSAB_EINVAL;
+    if (d->meta_format == HSAB_META_FP8 && d->d_k % 32 != 0) return HSAB_EINVAL;   // whole 64-byte row loads
     return HSAB_OK;
 }
 

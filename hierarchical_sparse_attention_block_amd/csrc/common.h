@@ -138,6 +138,71 @@ __device__ __forceinline__ void split_bf16x2(float a, float b, uint32_t& hi, uin
     lo = pk_bf16(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u));
 }
 
+// fp8 e4m3 (OCP "fn": sign, 4 exponent bits with bias 7, 3 mantissa bits,
+// exponent 0 subnormal with step 2^-9, 0x7f/0xff NaN, largest finite 448)
+// from a bf16 value, rounded outward: up (toward +inf) or down (toward
+// -inf) to the nearest grid value, saturating at +-448. The magnitude is
+// first truncated; an inexact result then steps one code away from zero
+// when that is the rounding direction (codes are monotone in magnitude).
+__device__ __forceinline__ uint32_t f8_outward(uint32_t b, bool up) {
+    const uint32_t sgn = (b >> 15) & 1u, E = (b >> 7) & 0xffu, M = b & 0x7fu;
+    uint32_t code;
+    bool inexact;
+    if (E == 0) {                       // bf16 zero or subnormal: below every nonzero e4m3 value
+        code = 0;
+        inexact = M != 0;
+    } else {
+        const int e = (int)E - 120;     // e4m3 exponent field (unbiased + 7)
+        if (e >= 1) {
+            code = ((uint32_t)e << 3) | (M >> 4);
+            inexact = (M & 0xfu) != 0;
+            if (code > 0x7eu) {         // beyond 448
+                code = 0x7eu;
+                inexact = true;
+            }
+        } else {                        // e4m3 subnormal range: |x| / 2^-9 = (128 + M) * 2^(e - 5)
+            const int sh = 5 - e;       // >= 5
+            const uint32_t F = 128u + M;
+            code = sh >= 9 ? 0u : (F >> sh);
+            inexact = sh >= 9 ? true : (F & ((1u << sh) - 1u)) != 0;
+        }
+    }
+    if (inexact && (up != (sgn != 0u))) code = code + 1u > 0x7eu ? 0x7eu : code + 1u;
+    return (sgn << 7) | code;
+}
+// value of an e4m3 code (finite codes only)
+__device__ __forceinline__ float f8_value(uint32_t code) {
+    return __builtin_amdgcn_cvt_f32_fp8((int)code, 0);
+}
+// eight e4m3 values (bytes of w, lowest first) as eight bf16 (exact)
+__device__ __forceinline__ uint4 f8x8_bf16(uint2 w) {
+    const f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8(w.x, false), b = __builtin_amdgcn_cvt_pk_f32_fp8(w.x, true);
+    const f32x2_t c = __builtin_amdgcn_cvt_pk_f32_fp8(w.y, false), d = __builtin_amdgcn_cvt_pk_f32_fp8(w.y, true);
+    return make_uint4(pk_bf16(a[0], a[1]), pk_bf16(b[0], b[1]), pk_bf16(c[0], c[1]), pk_bf16(d[0], d[1]));
+}
+
+// Metadata of block blk: its max row then its min row, d_k values each,
+// bf16 or (meta8) e4m3 bytes.
+__device__ __forceinline__ uint8_t* meta_block(uint16_t* meta, size_t blk, int dk, bool meta8) {
+    return reinterpret_cast<uint8_t*>(meta) + blk * (size_t)(2 * dk) * (meta8 ? 1u : 2u);
+}
+// Channel c of a block's metadata widened to include key value kb (bf16
+// bits), or started from it when the block opens. In e4m3 the max rounds
+// up and the min down; rounding is monotone, so widening rounded bounds
+// equals rounding the widened ones.
+__device__ __forceinline__ void meta_widen(uint8_t* M, int dk, int c, uint16_t kb, bool first, bool meta8) {
+    if (meta8) {
+        const uint32_t up = f8_outward(kb, true), dn = f8_outward(kb, false);
+        if (first || f8_value(up) > f8_value(M[c])) M[c] = (uint8_t)up;
+        if (first || f8_value(dn) < f8_value(M[dk + c])) M[dk + c] = (uint8_t)dn;
+    } else {
+        uint16_t* M16 = reinterpret_cast<uint16_t*>(M);
+        const float kf = __uint_as_float((uint32_t)kb << 16);
+        if (first || kf > __uint_as_float((uint32_t)M16[c] << 16)) M16[c] = kb;
+        if (first || kf < __uint_as_float((uint32_t)M16[dk + c] << 16)) M16[dk + c] = kb;
+    }
+}
+
 // Operand of the gfx950 transposing LDS read of four 16-bit elements.
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ __attribute__((address_space(3))) s16x4_t* lds_s16x4(const uint16_t* p) {

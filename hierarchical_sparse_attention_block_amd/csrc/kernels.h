@@ -19,6 +19,7 @@ constexpr int MLA_TOK_PER_SPLIT = 64;    // tokens per attention workgroup (MLA 
 struct Shape {
     int B, Hq, Hkv, G, dk, dv, valias, bs, r, kb, kt, max_ctx, nb_cap;
     float sm_scale;
+    int meta8;   // block metadata in fp8 e4m3 (outward rounded) instead of bf16
 };
 
 Shape make_shape(const hsab_dims& d);

@@ -3,7 +3,8 @@
 // scoring kernel). Blocks summarised by key max/min follow the AsyncTLS coarse
 // stage (gist.science/de explainer, section 2.A "Stufe 1"); the label copy
 // is the compressed key of the fine stage (gist.science/es explainer,
-// section 2.A item 2). Both are exact bf16 copies / comparisons.
+// section 2.A item 2). Both are exact bf16 copies / comparisons; with fp8
+// metadata the max and min are then rounded outward to e4m3.
 #include "common.h"
 #include "kernels.h"
 
@@ -28,7 +29,7 @@ __device__ __forceinline__ uint4 vmin(uint4 a, uint4 b) { return {bmin2(a.x, b.x
 __global__ __launch_bounds__(256) void build_meta_kernel(
     const uint16_t* __restrict__ K, const int32_t* __restrict__ ctx_len,
     const int32_t* __restrict__ label_ch, uint16_t* __restrict__ meta, uint16_t* __restrict__ klabel,
-    int Hkv, int dk, int bs, int r, int max_ctx, int nb_cap) {
+    int Hkv, int dk, int bs, int r, int max_ctx, int nb_cap, int meta8) {
     const int unit = blockIdx.y, b = unit / Hkv, g = unit % Hkv;
     int n = ctx_len[b];
     n = n < 0 ? 0 : (n > max_ctx ? max_ctx : n);
@@ -36,7 +37,6 @@ __global__ __launch_bounds__(256) void build_meta_kernel(
     const int j0 = blockIdx.x * META_BLOCKS_PER_WG;
     if (j0 >= nb) return;
     const uint16_t* Ku = K + (size_t)unit * max_ctx * dk;
-    uint16_t* Mu = meta + (size_t)unit * nb_cap * 2 * dk;
 
     const int cpb = dk / 8;   // 16-byte chunks per key row
     for (int p = threadIdx.x; p < META_BLOCKS_PER_WG * cpb; p += blockDim.x) {
@@ -49,8 +49,23 @@ __global__ __launch_bounds__(256) void build_meta_kernel(
             mx = vmax(mx, v);
             mn = vmin(mn, v);
         }
-        *reinterpret_cast<uint4*>(Mu + (size_t)j * 2 * dk + c * 8) = mx;
-        *reinterpret_cast<uint4*>(Mu + (size_t)j * 2 * dk + dk + c * 8) = mn;
+        uint8_t* M = meta_block(meta, (size_t)unit * nb_cap + j, dk, meta8);
+        if (meta8) {
+            const uint32_t hx[4] = {mx.x, mx.y, mx.z, mx.w}, hn[4] = {mn.x, mn.y, mn.z, mn.w};
+            uint32_t ux[2] = {0u, 0u}, dn[2] = {0u, 0u};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t bx = (hx[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+                const uint32_t bn = (hn[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+                ux[e >> 2] |= f8_outward(bx, true) << (8 * (e & 3));
+                dn[e >> 2] |= f8_outward(bn, false) << (8 * (e & 3));
+            }
+            *reinterpret_cast<uint2*>(M + c * 8) = make_uint2(ux[0], ux[1]);
+            *reinterpret_cast<uint2*>(M + dk + c * 8) = make_uint2(dn[0], dn[1]);
+        } else {
+            *reinterpret_cast<uint4*>(M + c * 16) = mx;
+            *reinterpret_cast<uint4*>(M + 2 * dk + c * 16) = mn;
+        }
     }
     const int32_t* lab = label_ch + g * r;
     uint16_t* Lu = klabel + (size_t)unit * max_ctx * r;
@@ -68,7 +83,7 @@ hipError_t launch_build_meta(const Shape& s, const uint16_t* K, const int32_t* c
                              hipStream_t st) {
     dim3 grid((s.nb_cap + META_BLOCKS_PER_WG - 1) / META_BLOCKS_PER_WG, s.B * s.Hkv);
     hipLaunchKernelGGL(build_meta_kernel, grid, dim3(256), 0, st, K, ctx_len, label_ch, meta, klabel,
-                       s.Hkv, s.dk, s.bs, s.r, s.max_ctx, s.nb_cap);
+                       s.Hkv, s.dk, s.bs, s.r, s.max_ctx, s.nb_cap, s.meta8);
     return hipGetLastError();
 }
 

@@ -31,7 +31,7 @@ __global__ __launch_bounds__(256) void append_slot_kernel(
     const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new, uint16_t* __restrict__ cache,
     uint16_t* __restrict__ meta, uint16_t* __restrict__ klabel, const int32_t* __restrict__ label_ch,
     const int32_t* __restrict__ ctx_len, int Hkv, int dk, int dv, int valias, int bs, int r, int max_ctx,
-    int nb_cap, int n_slots) {
+    int nb_cap, int n_slots, int meta8) {
     const int unit = blockIdx.x, b = unit / Hkv, g = unit % Hkv;
     const int pos = ctx_len[b] - 1;
     if (pos < 0 || pos >= max_ctx) return;
@@ -40,14 +40,11 @@ __global__ __launch_bounds__(256) void append_slot_kernel(
     const size_t slot_elems = (size_t)bs * (valias ? dk : dk + dv);
     const uint16_t* kn = k_new + (size_t)unit * dk;
     uint16_t* slot = cache + ((size_t)unit * n_slots + (n_slots - 2 + (j & 1))) * slot_elems;
-    uint16_t* M = meta + ((size_t)unit * nb_cap + j) * 2 * dk;
+    uint8_t* M = meta_block(meta, (size_t)unit * nb_cap + j, dk, meta8);
     for (int c = threadIdx.x; c < dk; c += blockDim.x) {
         const uint16_t kb = kn[c];
-        const uint16_t mx = M[c], mn = M[dk + c];
         slot[(size_t)off * dk + c] = kb;
-        const float kf = bf16_f32(kb);
-        M[c] = (first || kf > bf16_f32(mx)) ? kb : mx;
-        M[dk + c] = (first || kf < bf16_f32(mn)) ? kb : mn;
+        meta_widen(M, dk, c, kb, first, meta8);
     }
     if (!valias) {
         const uint16_t* vn = v_new + (size_t)unit * dv;
@@ -135,7 +132,8 @@ hipError_t launch_append_slot(const Shape& s, int n_slots, const uint16_t* k_new
                               uint16_t* cache, uint16_t* meta, uint16_t* klabel, const int32_t* label_ch,
                               const int32_t* ctx_len, hipStream_t st) {
     hipLaunchKernelGGL(append_slot_kernel, dim3(s.B * s.Hkv), dim3(256), 0, st, k_new, v_new, cache, meta, klabel,
-                       label_ch, ctx_len, s.Hkv, s.dk, s.dv, s.valias, s.bs, s.r, s.max_ctx, s.nb_cap, n_slots);
+                       label_ch, ctx_len, s.Hkv, s.dk, s.dv, s.valias, s.bs, s.r, s.max_ctx, s.nb_cap, n_slots,
+                       s.meta8);
     return hipGetLastError();
 }
 

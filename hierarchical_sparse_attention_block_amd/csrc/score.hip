@@ -21,6 +21,12 @@
 // a workgroup, which add their partial tiles through LDS. The result tile
 // holds block (l % 16) in lane l for head rows 4*(l/16)..+3; a max over
 // valid heads and two lane swaps leave the block score in lanes 0..15.
+//
+// Metadata in fp8 e4m3 (max rounded up, min rounded down, so the bound
+// still holds; quantised index data, gist.science/de explainer section 2.A
+// "Stufe 2"): a 16-byte load then carries 16 channels, which
+// v_cvt_pk_f32_fp8 and v_cvt_pk_bf16_f32 widen exactly to the B fragments
+// of two consecutive steps; the A fragments follow the same channel order.
 #include "common.h"
 #include "kernels.h"
 
@@ -44,9 +50,11 @@ struct Append {
     int dv, r;
 };
 
-// MT: 16-row head tiles (G <= 16 or <= 32); KSW: max steps per wave;
-// KSPLIT: waves sharing one block tile (1: each wave scores its own tiles).
-template <int MT, int KSW, int KSPLIT>
+// MT: 16-row head tiles (G <= 16 or <= 32); KSW: max row loads (16 bytes
+// per lane) per wave and tile; KSPLIT: waves sharing one block tile (1: each
+// wave scores its own tiles); F8: metadata in e4m3 bytes, widened to bf16 in
+// registers (one load then feeds two matrix steps).
+template <int MT, int KSW, int KSPLIT, bool F8>
 __global__ __launch_bounds__(256) void block_score_kernel(
     const uint16_t* __restrict__ q, uint16_t* __restrict__ meta,
     const int32_t* __restrict__ ctx_len, float* __restrict__ score,
@@ -70,19 +78,12 @@ __global__ __launch_bounds__(256) void block_score_kernel(
         const int pos = n - 1, jt = pos / bs;
         const bool first = (pos % bs) == 0;
         const uint16_t* kn = ap.k_new + (size_t)unit * dk;
-        uint16_t* Mt = meta + ((size_t)unit * nb_cap + jt) * 2 * dk;
+        uint8_t* Mt = meta_block(meta, (size_t)unit * nb_cap + jt, dk, F8);
         uint16_t* Krow = ap.K + ((size_t)unit * max_ctx + pos) * dk;
         for (int c = threadIdx.x; c < dk; c += blockDim.x) {
             const uint16_t kb = kn[c];
             Krow[c] = kb;
-            if (first) {
-                Mt[c] = kb;
-                Mt[dk + c] = kb;
-            } else {
-                const float kf = bf16_f32(kb);
-                if (kf > bf16_f32(Mt[c])) Mt[c] = kb;
-                if (kf < bf16_f32(Mt[dk + c])) Mt[dk + c] = kb;
-            }
+            meta_widen(Mt, dk, c, kb, first, F8);
         }
         if (ap.V) {
             const uint16_t* vn = ap.v_new + (size_t)unit * ap.dv;
@@ -95,20 +96,25 @@ __global__ __launch_bounds__(256) void block_score_kernel(
         __syncthreads();   // the tail block's new bounds are read below
     }
 
-    const int KS = dk / 16;        // steps of 32 over 2*dk stacked channels
-    const int CH = dk / 8;         // 8-channel chunks in one half
+    // row loads of 64 bytes per 16 lanes over the 2*dk stacked channels:
+    // 32 channels of bf16 (one matrix step) or 64 of e4m3 (two steps)
+    constexpr int LS = F8 ? 2 : 1;             // matrix steps per load
+    const int KS = F8 ? dk / 32 : dk / 16;     // loads per metadata row
+    const int CH = dk / 8;                     // 8-channel chunks in one half
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int part = KSPLIT > 1 ? wave : 0;              // step range of this wave
     const int tslot = KSPLIT > 1 ? 0 : wave;             // tile column of this wave
     const int s_lo = part * KS / KSPLIT, s_hi = (part + 1) * KS / KSPLIT;
-    const uint16_t* Mu = meta + (size_t)unit * nb_cap * 2 * dk;
     float* Su = score + (size_t)unit * nb_cap;
     auto tile_j0 = [&](int t) { return j_wg + (t * TILES_WG + tslot) * 16; };
     auto tile_row = [&](int t) {
         const int jl = tile_j0(t) + (lane & 15);
         const int jc = jl < nb ? jl : nb - 1;          // keep loads inside the unit's blocks
-        return Mu + (size_t)jc * 2 * dk + (lane >> 4) * 8;
+        return meta_block(meta, (size_t)unit * nb_cap + jc, dk, F8) + (lane >> 4) * 16;
     };
+    // 8-channel chunk of the stacked row that matrix step w of load st feeds
+    // to this lane (the A fragments follow the same order)
+    auto chunk = [&](int st, int w) { return F8 ? 2 * (st * 4 + (lane >> 4)) + w : st * 4 + (lane >> 4); };
 
     // A fragments are requested first (they come from L2), then the tile
     // rows, so converting the fragments waits for none of the rows. Every
@@ -118,7 +124,7 @@ __global__ __launch_bounds__(256) void block_score_kernel(
     // registers), and tiles past the workgroup's range re-read its last
     // tile, which keeps each wait count exact.
     const uint16_t* qg = q + ((size_t)b * Hkv * G + (size_t)g * G) * dk;
-    uint4 af[MT][KSW];
+    uint4 af[MT][KSW * LS];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
         const int m = mt * 16 + (lane & 15);
@@ -126,17 +132,20 @@ __global__ __launch_bounds__(256) void block_score_kernel(
 #pragma unroll
         for (int u = 0; u < KSW; ++u) {
             const int st = s_lo + u < s_hi ? s_lo + u : s_hi - 1;
-            const int c = st * 4 + (lane >> 4);
-            af[mt][u] = ldg16(qm + (c >= CH ? c - CH : c) * 8);
+#pragma unroll
+            for (int w = 0; w < LS; ++w) {
+                const int c = chunk(st, w);
+                af[mt][u * LS + w] = ldg16(qm + (c >= CH ? c - CH : c) * 8);
+            }
         }
     }
     auto load_tile = [&](int t, uint4 (&dst)[KSW]) {
-        const uint16_t* row = tile_row(t < tiles_per_wave ? t : tiles_per_wave - 1);
+        const uint8_t* row = tile_row(t < tiles_per_wave ? t : tiles_per_wave - 1);
 #pragma unroll
-        for (int u = 0; u < KSW; ++u) dst[u] = ldg16(row + (s_lo + u < s_hi ? s_lo + u : s_hi - 1) * 32);
+        for (int u = 0; u < KSW; ++u) dst[u] = ldg16(row + (s_lo + u < s_hi ? s_lo + u : s_hi - 1) * 64);
     };
     // split-row workgroups take SPLIT_TILES tiles, all requested at once
-    constexpr int NBUF = KSPLIT > 1 ? SPLIT_TILES : 2;
+    constexpr int NBUF = KSPLIT > 1 ? SPLIT_TILES : 1;
     uint4 tl[NBUF][KSW];
     load_tile(0, tl[0]);
     if constexpr (KSPLIT > 1) {
@@ -147,10 +156,10 @@ __global__ __launch_bounds__(256) void block_score_kernel(
     for (int mt = 0; mt < MT; ++mt) {
         const bool head = mt * 16 + (lane & 15) < G;
 #pragma unroll
-        for (int u = 0; u < KSW; ++u) {
+        for (int u = 0; u < KSW * LS; ++u) {
             const uint4 r = af[mt][u];
-            const bool lower = (s_lo + u) * 4 + (lane >> 4) >= CH;
-            af[mt][u] = !head || s_lo + u >= s_hi ? make_uint4(0u, 0u, 0u, 0u)
+            const bool lower = chunk(s_lo + u / LS, u % LS) >= CH;
+            af[mt][u] = !head || s_lo + u / LS >= s_hi ? make_uint4(0u, 0u, 0u, 0u)
                         : lower ? make_uint4(bf16x2_neg(r.x), bf16x2_neg(r.y), bf16x2_neg(r.z), bf16x2_neg(r.w))
                                 : make_uint4(bf16x2_pos(r.x), bf16x2_pos(r.y), bf16x2_pos(r.z), bf16x2_pos(r.w));
         }
@@ -165,9 +174,17 @@ __global__ __launch_bounds__(256) void block_score_kernel(
 #pragma unroll
         for (int u = 0; u < KSW; ++u) {
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-                acc[mt][u & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(af[mt][u]), as_bf16x8(rows[u]),
-                                                                       acc[mt][u & 1], 0, 0, 0);
+            for (int w = 0; w < LS; ++w) {
+                // e4m3 bytes 8w..8w+7 of the load widened to bf16 (exact)
+                const uint4 bv = F8 ? f8x8_bf16(w == 0 ? make_uint2(rows[u].x, rows[u].y)
+                                                       : make_uint2(rows[u].z, rows[u].w))
+                                    : rows[u];
+                const int k = u * LS + w;
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    acc[mt][k & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(af[mt][k]), as_bf16x8(bv),
+                                                                           acc[mt][k & 1], 0, 0, 0);
+            }
         }
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) tot[mt] = acc[mt][0] + acc[mt][1];
@@ -211,25 +228,21 @@ __global__ __launch_bounds__(256) void block_score_kernel(
             emit(wave, tot);
         }
     } else {
-        // the next tile's rows are requested before the current tile is
-        // multiplied and awaited after it: one tile in flight per wave,
-        // which at this occupancy keeps the memory system busier than two
+        // one tile in flight per wave: the next tile's rows are requested
+        // once the current one is multiplied (with this many waves per CU
+        // the memory system is kept busy; prefetching one or more tiles
+        // ahead measured no faster with bf16 rows and slower with e4m3)
         for (int t = 0; t < tiles_per_wave; ++t) {
             if (tile_j0(t) >= nb) break;
-            const bool more = t + 1 < tiles_per_wave && tile_j0(t + 1) < nb;
-            if (more) load_tile(t + 1, tl[1]);
             f32x4_t tot[MT];
             mul_tile(tl[0], tot);
             emit(t, tot);
-            if (more) {
-#pragma unroll
-                for (int u = 0; u < KSW; ++u) tl[0][u] = tl[1][u];
-            }
+            if (t + 1 < tiles_per_wave && tile_j0(t + 1) < nb) load_tile(t + 1, tl[0]);
         }
     }
 }
 
-template <int MT, int KSW, int KSPLIT>
+template <int MT, int KSW, int KSPLIT, bool F8>
 hipError_t launch_t(const Shape& s, const uint16_t* q, uint16_t* meta, const int32_t* ctx_len,
                     float* score, const Append& ap, int32_t* sel_cnt, hipStream_t st) {
     constexpr int TILES_WG = SCORE_WAVES / KSPLIT;
@@ -242,7 +255,7 @@ hipError_t launch_t(const Shape& s, const uint16_t* q, uint16_t* meta, const int
     if (KSPLIT > 1) tpw = SPLIT_TILES;
     const int per_wg = TILES_WG * tpw * 16;
     dim3 grid((s.nb_cap + per_wg - 1) / per_wg, s.B * s.Hkv);
-    hipLaunchKernelGGL((block_score_kernel<MT, KSW, KSPLIT>), grid, dim3(64 * SCORE_WAVES), 0, st, q, meta,
+    hipLaunchKernelGGL((block_score_kernel<MT, KSW, KSPLIT, F8>), grid, dim3(64 * SCORE_WAVES), 0, st, q, meta,
                        ctx_len, score, s.Hkv, s.G, s.dk, s.bs, s.max_ctx, s.nb_cap, tpw, ap, sel_cnt);
     return hipGetLastError();
 }
@@ -250,14 +263,23 @@ hipError_t launch_t(const Shape& s, const uint16_t* q, uint16_t* meta, const int
 template <int MT>
 hipError_t launch_mt(const Shape& s, const uint16_t* q, uint16_t* meta, const int32_t* ctx_len, float* score,
                      const Append& ap, int32_t* sel_cnt, hipStream_t st) {
+    if (s.meta8) {   // e4m3 rows: d_k / 32 loads of 64 channels, two matrix steps each
+        const int kl = s.dk / 32;
+        if (kl <= 2) return launch_t<MT, 2, 1, true>(s, q, meta, ctx_len, score, ap, sel_cnt, st);
+        if (kl <= 4) return launch_t<MT, 4, 1, true>(s, q, meta, ctx_len, score, ap, sel_cnt, st);
+        if (kl <= 8) return launch_t<MT, 8, 1, true>(s, q, meta, ctx_len, score, ap, sel_cnt, st);
+        if (kl <= 16) return launch_t<MT, 4, 4, true>(s, q, meta, ctx_len, score, ap, sel_cnt, st);
+        if (kl <= 20) return launch_t<MT, 5, 4, true>(s, q, meta, ctx_len, score, ap, sel_cnt, st);
+        return launch_t<MT, 8, 4, true>(s, q, meta, ctx_len, score, ap, sel_cnt, st);   // d_k <= 1024
+    }
     const int ks = s.dk / 16;
-    if (ks <= 4) return launch_t<MT, 4, 1>(s, q, meta, ctx_len, score, ap, sel_cnt, st);
-    if (ks <= 8) return launch_t<MT, 8, 1>(s, q, meta, ctx_len, score, ap, sel_cnt, st);
-    if (ks <= 16) return launch_t<MT, 16, 1>(s, q, meta, ctx_len, score, ap, sel_cnt, st);
-    if (ks <= 32) return launch_t<MT, 8, 4>(s, q, meta, ctx_len, score, ap, sel_cnt, st);
-    if (ks <= 36) return launch_t<MT, 9, 4>(s, q, meta, ctx_len, score, ap, sel_cnt, st);    // 576-dim latent keys
-    if (ks <= 40) return launch_t<MT, 10, 4>(s, q, meta, ctx_len, score, ap, sel_cnt, st);
-    return launch_t<MT, 16, 4>(s, q, meta, ctx_len, score, ap, sel_cnt, st);   // d_k <= 1024: <= 64 steps
+    if (ks <= 4) return launch_t<MT, 4, 1, false>(s, q, meta, ctx_len, score, ap, sel_cnt, st);
+    if (ks <= 8) return launch_t<MT, 8, 1, false>(s, q, meta, ctx_len, score, ap, sel_cnt, st);
+    if (ks <= 16) return launch_t<MT, 16, 1, false>(s, q, meta, ctx_len, score, ap, sel_cnt, st);
+    if (ks <= 32) return launch_t<MT, 8, 4, false>(s, q, meta, ctx_len, score, ap, sel_cnt, st);
+    if (ks <= 36) return launch_t<MT, 9, 4, false>(s, q, meta, ctx_len, score, ap, sel_cnt, st);    // 576-dim latent keys
+    if (ks <= 40) return launch_t<MT, 10, 4, false>(s, q, meta, ctx_len, score, ap, sel_cnt, st);
+    return launch_t<MT, 16, 4, false>(s, q, meta, ctx_len, score, ap, sel_cnt, st);   // d_k <= 1024: <= 64 steps
 }
 
 }  // namespace

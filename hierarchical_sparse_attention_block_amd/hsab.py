@@ -33,7 +33,8 @@ class Dims(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
                 ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32), ("v_alias_k", ctypes.c_int32),
                 ("block", ctypes.c_int32), ("r", ctypes.c_int32), ("k_blocks", ctypes.c_int32),
-                ("k_tokens", ctypes.c_int32), ("max_ctx", ctypes.c_int32), ("sm_scale", ctypes.c_float)]
+                ("k_tokens", ctypes.c_int32), ("max_ctx", ctypes.c_int32), ("sm_scale", ctypes.c_float),
+                ("meta_format", ctypes.c_int32)]
 
     @property
     def group(self):
@@ -47,10 +48,13 @@ class Dims(ctypes.Structure):
         return "Dims(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
 
 
+META_BF16, META_FP8 = 0, 1   # block metadata formats (HSAB_META_BF16 / HSAB_META_FP8)
+
+
 def dims(batch, n_q_heads, n_kv_heads, d_k, d_v, v_alias_k, block, r, k_blocks, k_tokens, max_ctx,
-         sm_scale) -> Dims:
+         sm_scale, meta_format=META_BF16) -> Dims:
     return Dims(batch, n_q_heads, n_kv_heads, d_k, d_v, int(bool(v_alias_k)), block, r, k_blocks,
-                k_tokens, max_ctx, float(sm_scale))
+                k_tokens, max_ctx, float(sm_scale), int(meta_format))
 
 
 _vp, _sz, _i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32
@@ -185,6 +189,18 @@ def _sizes(d: Dims):
     }
 
 
+def _meta(d: Dims, meta):
+    """Metadata buffer: bf16 bits, or uint8 e4m3 bytes with fp8 metadata;
+    B*Hkv*nb_cap*2*d_k values either way."""
+    n = d.batch * d.n_kv_heads * d.nb_cap * 2 * d.d_k
+    return _buf("meta", meta, torch.uint8 if d.meta_format == META_FP8 else _u16, n)
+
+
+def alloc_meta(d: Dims, device="cuda") -> torch.Tensor:
+    n = d.batch * d.n_kv_heads * d.nb_cap * 2 * d.d_k
+    return torch.zeros(n, dtype=torch.uint8 if d.meta_format == META_FP8 else torch.int16, device=device)
+
+
 def _ws(d, ws):
     if ws is None:
         raise ValueError("workspace is required (alloc_workspace)")
@@ -195,14 +211,14 @@ def build_meta(d: Dims, K, ctx_len, label_ch, meta, klabel, stream=None):
     s = _sizes(d)
     _check("hsab_build_meta", _lib.hsab_build_meta(
         ctypes.byref(d), _buf("K", K, _u16, s["K"]), _buf("ctx_len", ctx_len, _i, s["ctx"]),
-        _buf("label_ch", label_ch, _i, s["label"]), _buf("meta", meta, _u16, s["meta"]),
+        _buf("label_ch", label_ch, _i, s["label"]), _meta(d, meta),
         _buf("klabel", klabel, _u16, s["klabel"]), _stream(stream)))
 
 
 def score_blocks(d: Dims, q, meta, ctx_len, blk_score, stream=None):
     s = _sizes(d)
     _check("hsab_score_blocks", _lib.hsab_score_blocks(
-        ctypes.byref(d), _buf("q", q, _u16, s["q"]), _buf("meta", meta, _u16, s["meta"]),
+        ctypes.byref(d), _buf("q", q, _u16, s["q"]), _meta(d, meta),
         _buf("ctx_len", ctx_len, _i, s["ctx"]), _buf("blk_score", blk_score, _f, s["score"]),
         _stream(stream)))
 
@@ -214,7 +230,7 @@ def select_blocks(d: Dims, q, meta, ctx_len, blk_idx, blk_score=None, ws=None, s
     else:
         wp, wn = (None, 0) if ws is None else _ws(d, ws)
     _check("hsab_select_blocks", _lib.hsab_select_blocks(
-        ctypes.byref(d), _buf("q", q, _u16, s["q"]), _buf("meta", meta, _u16, s["meta"]),
+        ctypes.byref(d), _buf("q", q, _u16, s["q"]), _meta(d, meta),
         _buf("ctx_len", ctx_len, _i, s["ctx"]), _buf("blk_idx", blk_idx, _i, s["blk"]),
         _buf("blk_score", blk_score, _f, s["score"], allow_none=True), wp, wn, _stream(stream)))
 
@@ -256,7 +272,7 @@ def decode_step(d: Dims, q, k_new, v_new, K, V, meta, klabel, label_ch, ctx_len,
     _check("hsab_decode_step", _lib.hsab_decode_step(
         ctypes.byref(d), _buf("q", q, _u16, s["q"]), _buf("k_new", k_new, _u16, s["knew"]),
         _buf("v_new", v_new, _u16, s["vnew"], allow_none=alias), _buf("K", K, _u16, s["K"]),
-        _buf("V", V, _u16, s["V"], allow_none=alias), _buf("meta", meta, _u16, s["meta"]),
+        _buf("V", V, _u16, s["V"], allow_none=alias), _meta(d, meta),
         _buf("klabel", klabel, _u16, s["klabel"]), _buf("label_ch", label_ch, _i, s["label"]),
         _buf("ctx_len", ctx_len, _i, s["ctx"]), _buf("blk_idx", blk_idx, _i, s["blk"]),
         _buf("tok_idx", tok_idx, _i, s["tok"]), _buf("out", out, _f, s["out"]),
@@ -275,7 +291,7 @@ def offload_append(d: Dims, n_slots, k_new, v_new, cache, meta, klabel, label_ch
     _check("hsab_offload_append", _lib.hsab_offload_append(
         ctypes.byref(d), ctypes.c_int32(n_slots), _buf("k_new", k_new, _u16, s["knew"]),
         _buf("v_new", v_new, _u16, s["vnew"], allow_none=alias),
-        _buf("cache", cache, _u16, U * n_slots * block_elems(d)), _buf("meta", meta, _u16, s["meta"]),
+        _buf("cache", cache, _u16, U * n_slots * block_elems(d)), _meta(d, meta),
         _buf("klabel", klabel, _u16, s["klabel"]), _buf("label_ch", label_ch, _i, s["label"]),
         _buf("ctx_len", ctx_len, _i, s["ctx"]), _stream(stream)))
 
@@ -358,7 +374,7 @@ class OffloadEngine:
             self._h, _buf("q", q, _u16, s["q"]), _buf("k_new", k_new, _u16, s["knew"]),
             _buf("v_new", v_new, _u16, s["vnew"], allow_none=bool(d.v_alias_k)),
             _hbuf("host_pool", host_pool, _u16, U * d.nb_cap * block_elems(d), pinned=True),
-            _buf("cache", cache, _u16, U * self.n_slots * block_elems(d)), _buf("meta", meta, _u16, s["meta"]),
+            _buf("cache", cache, _u16, U * self.n_slots * block_elems(d)), _meta(d, meta),
             _buf("klabel", klabel, _u16, s["klabel"]), _buf("label_ch", label_ch, _i, s["label"]),
             _buf("ctx_len", ctx_len, _i, s["ctx"]), _hbuf("ctx_len_host", ctx_len_host, _i, d.batch),
             _buf("slot_of", slot_of, _i, U * d.nb_cap), _buf("tok_idx", tok_idx, _i, s["tok"]),

@@ -67,6 +67,7 @@ class Workload:
     label_mode: str      # "random" (seeded channel set) or "top_scale"
     n_planted: int       # planted keys per (batch, KV head)
     seed: int
+    meta_fp8: bool = False   # block metadata as outward-rounded fp8 e4m3 instead of bf16
 
     @property
     def group(self) -> int:

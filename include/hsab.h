@@ -28,8 +28,18 @@
  *   V        [B][Hkv][max_ctx][d_v]               bf16 value cache; when
  *            dims.v_alias_k != 0 there is no V array: the value of a token
  *            is the first d_v entries of its key row (absorbed MLA latent).
- *   meta     [B][Hkv][nb_cap][2][d_k]             bf16: per block, the
- *            channelwise key max row followed by the key min row.
+ *   meta     [B][Hkv][nb_cap][2][d_k]             per block, the
+ *            channelwise key max row followed by the key min row; bf16
+ *            values, or with dims.meta_format == HSAB_META_FP8 one byte
+ *            per value in fp8 e4m3 (OCP "fn": bias 7, no infinities, max
+ *            448), the max rounded up and the min rounded down to that
+ *            grid so every block bound stays >= the true block maximum
+ *            (keys with |k| > 448 saturate and lose that guarantee). The
+ *            pointer type stays uint16_t*; the array then holds
+ *            B*Hkv*nb_cap*2*d_k bytes. Quantised index data: AsyncTLS
+ *            (gist.science/de explainer, section 2.A "Stufe 2") names
+ *            quantisation as a way to cut the indexing cost without giving
+ *            a scheme; outward rounding is this library's reading.
  *   klabel   [B][Hkv][max_ctx][r]                 bf16: K restricted to the
  *            label channels, klabel[..][t][c] = K[..][t][label_ch[g][c]].
  *   label_ch [Hkv][r]                             int32 channel indices.
@@ -73,7 +83,8 @@ extern "C" {
 #define HSAB_EUNSUPPORTED -3   /* valid shape with no kernel instantiation (see limits below) */
 
 /* Shape and budget of one decode layer.
- * Limits: 1 <= G <= 32; d_k % 16 == 0, 16 <= d_k <= 1024; d_v % 8 == 0;
+ * Limits: 1 <= G <= 32; d_k % 16 == 0, 16 <= d_k <= 1024 (d_k % 32 == 0
+ * with fp8 metadata); d_v % 8 == 0;
  * r in {16, 32, 64, 128}, r <= d_k; 1 <= K_b <= 2048;
  * K_b * block <= 8192; nb_cap <= 8192; K_t >= 1.
  * Attention kernels exist for d_k == d_v in {64, 128, 256} with G in
@@ -94,7 +105,11 @@ typedef struct hsab_dims {
     int32_t k_tokens;     /* K_t */
     int32_t max_ctx;      /* cache capacity (tokens) per unit */
     float   sm_scale;     /* logit scale, typically 1/sqrt(d_k) */
+    int32_t meta_format;  /* HSAB_META_BF16 (0) or HSAB_META_FP8 (1) */
 } hsab_dims;
+
+#define HSAB_META_BF16 0   /* block metadata in bf16 (exact key max/min) */
+#define HSAB_META_FP8  1   /* fp8 e4m3, max rounded up, min rounded down */
 
 /* Bytes of device workspace the calls below need for these dims (the same
  * size serves every call). The workspace holds block scores, token scores,

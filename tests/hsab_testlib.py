@@ -31,7 +31,8 @@ LSE_RTOL = 1e-4
 def dims_of(w: W.Workload):
     from hierarchical_sparse_attention_block_amd import hsab as H
     return H.dims(w.batch, w.n_q_heads, w.n_kv_heads, w.d_k, w.d_v, w.v_alias_k, w.block, w.r,
-                  w.k_blocks, w.k_tokens, w.max_ctx, w.sm_scale)
+                  w.k_blocks, w.k_tokens, w.max_ctx, w.sm_scale,
+                  H.META_FP8 if w.meta_fp8 else H.META_BF16)
 
 
 def host_inputs(w: W.Workload, ctx_len=None, threads=8):
@@ -86,7 +87,7 @@ class Device:
         self.label = torch.from_numpy(h["label"]).cuda()
         self.ctx = torch.from_numpy(h["ctx"]).cuda()
         self.ctx_prefill = torch.from_numpy(h["ctx"] - 1).cuda()
-        self.meta = torch.zeros(U * d.nb_cap * 2 * w.d_k, dtype=torch.int16, device="cuda")
+        self.meta = H.alloc_meta(d)
         self.klabel = torch.zeros(U * w.max_ctx * w.r, dtype=torch.int16, device="cuda")
         self.blk = torch.full((U * w.k_blocks,), -7, dtype=torch.int32, device="cuda")
         self.tok = torch.full((U * w.k_tokens,), -7, dtype=torch.int32, device="cuda")
@@ -152,7 +153,7 @@ def oracle_unit_vs_gpu(w, q_bits, K_bits, V_bits, ctx, label, b, g, gpu_blk, gpu
     q = O.bf16_to_f64(q_bits[b, g * G:(g + 1) * G])
     K = O.bf16_to_f64(K_bits[b, g, :n])
     V = K[:, : w.d_v] if w.v_alias_k else O.bf16_to_f64(V_bits[b, g, :n])
-    kmax, kmin = O.block_meta(K, n, w.block)
+    kmax, kmin = (O.block_meta_e4m3 if w.meta_fp8 else O.block_meta)(K, n, w.block)
     s_blk = O.block_scores(q, kmax, kmin)
     blk, tie_b = check_index_set(s_blk, gpu_blk, w.k_blocks, f"blocks of unit ({b},{g})")
     cand = O.candidate_tokens(blk, n, w.block)

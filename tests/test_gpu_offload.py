@@ -68,7 +68,7 @@ def _run_offload(w, prefill, steps, n_slots=None, copy_mode=0):
     Kpre = K.copy()
     for b in range(B):
         Kpre[b, :, prefill[b]:] = 0
-    meta = torch.zeros(U * nb_cap * 2 * w.d_k, dtype=torch.int16, device="cuda")
+    meta = H.alloc_meta(d)
     klabel = torch.zeros(U * w.max_ctx * w.r, dtype=torch.int16, device="cuda")
     label = torch.from_numpy(W.label_channels(w)).cuda()
     H.build_meta(d, dev16(Kpre), torch.from_numpy(prefill).cuda(), label, meta, klabel)
@@ -120,7 +120,7 @@ def _check_against_oracle(w, prefill, K, V, qs, res):
             for t in range(steps):
                 n = int(prefill[b]) + t + 1
                 q = O.bf16_to_f64(qs[t][b, g * G:(g + 1) * G])
-                kmax, kmin = O.block_meta(Kf, n, bs)
+                kmax, kmin = (O.block_meta_e4m3 if w.meta_fp8 else O.block_meta)(Kf, n, bs)
                 s_blk = O.block_scores(q, kmax, kmin)
                 sel, tie = check_index_set(s_blk, res[t]["sel"][b, g], w.k_blocks, f"S_b step {t} unit ({b},{g})")
                 ties += tie
@@ -162,6 +162,17 @@ def test_offload_gqa_matches_lagged_oracle(copy_mode):
     K, V, qs, res = _run_offload(w, prefill, steps=12, copy_mode=copy_mode)
     _check_against_oracle(w, np.array(prefill), K, V, qs, res)
     assert sum(r["stats"]["delta_bytes"] for r in res[1:]) > 0, "the queries drift, so some blocks move"
+
+
+def test_offload_gqa_fp8_metadata():
+    """The same lagged run with block metadata in outward-rounded e4m3: the
+    offload append widens the quantised bounds of the tail block."""
+    w = W.WORKLOADS["tiny4k"].replace(name="offload_gqa_f8", batch=2, n_q_heads=8, n_kv_heads=2, k_blocks=8,
+                                      k_tokens=64, ctx=1024, max_ctx=1024, scaled_keys=True, n_planted=0,
+                                      seed=24, meta_fp8=True)
+    prefill = [300, 511]
+    K, V, qs, res = _run_offload(w, prefill, steps=8, copy_mode=0)
+    _check_against_oracle(w, np.array(prefill), K, V, qs, res)
 
 
 def test_offload_gqa_without_oracle_ties_equals_oracle_run():
