@@ -38,6 +38,16 @@ Readings where the pages are silent (all fixed here, none printed there):
 * attention logits are sm_scale * q.k; out is fp64 here (fp32 on the GPU);
   lse is the natural-log logsumexp of those logits.
 
+Selection variants (``agg="sum"``, ``select_blocks`` with sink and local
+blocks): the pages combine no query-head scores and force no tokens; their
+related-work list names StreamingLLM (attention sinks) [mlsanity index
+page, "Builds on"]. Readings taken here, both opt-in: a group score may be
+the SUM of the heads' scores instead of the max (a query group's total
+attention mass rather than its most demanding head), and the first
+`sink` blocks and the last `local` blocks (the newest, holding the
+appended token) may be kept unconditionally, the remaining K_b - forced
+slots going to the best of the other blocks.
+
 Quantised block metadata (``e4m3_*``, ``block_meta_e4m3``): the pages name
 quantisation of the index data as a way to cut the indexing cost
 [gist.science/de, section 2.A "Stufe 2"] and give no scheme. Reading taken
@@ -63,7 +73,7 @@ import numpy as np
 __all__ = [
     "bf16_to_f64", "n_blocks", "block_meta", "append_meta", "quest_bound",
     "quest_bound_gemm", "block_scores", "topk_stable", "candidate_tokens",
-    "label_scores", "attend", "select_tokens_unit", "decode_unit",
+    "label_scores", "attend", "select_tokens_unit", "decode_unit", "select_blocks",
     "e4m3_grid", "e4m3_round", "block_meta_e4m3",
     "decode_all", "offload_delta", "offload_held", "offload_schedule", "offload_run",
 ]
@@ -175,10 +185,12 @@ def quest_bound_gemm(q: np.ndarray, kmax: np.ndarray, kmin: np.ndarray) -> np.nd
     return qq @ kk.T
 
 
-def block_scores(q: np.ndarray, kmax: np.ndarray, kmin: np.ndarray) -> np.ndarray:
+def block_scores(q: np.ndarray, kmax: np.ndarray, kmin: np.ndarray, agg: str = "max") -> np.ndarray:
     """Block score of a KV head shared by the query heads q [G, d]: the
-    largest Quest bound over the group."""
-    return quest_bound(q, kmax, kmin).max(axis=0)
+    largest Quest bound over the group (agg="max"), or their sum
+    (agg="sum", a selection variant)."""
+    ub = quest_bound(q, kmax, kmin)
+    return ub.sum(axis=0) if agg == "sum" else ub.max(axis=0)
 
 
 # --------------------------------------------------------- steps 4, 5: top-k
@@ -191,18 +203,34 @@ def topk_stable(scores: np.ndarray, k: int) -> np.ndarray:
     return np.sort(order[:k])
 
 
+def select_blocks(s_blk: np.ndarray, k_blocks: int, sink: int = 0, local: int = 0) -> np.ndarray:
+    """Block stage with forced blocks: the first `sink` and the last `local`
+    blocks are kept whatever their scores; the other K_b - (forced count)
+    slots take the best remaining blocks (ties to the lower index).
+    Ascending. Without forced blocks this is ``topk_stable``."""
+    nb = len(s_blk)
+    forced = sorted(set(range(min(sink, nb))) | set(range(max(0, nb - local), nb)))
+    if len(forced) > k_blocks:
+        raise ValueError("more forced blocks than the block budget")
+    others = np.array([j for j in range(nb) if j not in set(forced)], np.int64)
+    pick = others[topk_stable(np.asarray(s_blk)[others], k_blocks - len(forced))] if others.size else others
+    return np.sort(np.concatenate([np.array(forced, np.int64), pick]))
+
+
 def candidate_tokens(blk_idx: np.ndarray, n: int, bs: int) -> np.ndarray:
     """Valid token positions of the kept blocks, ascending."""
     toks = [np.arange(j * bs, min((j + 1) * bs, n)) for j in np.sort(np.asarray(blk_idx))]
     return np.concatenate(toks) if toks else np.zeros(0, dtype=np.int64)
 
 
-def label_scores(q: np.ndarray, K_rows: np.ndarray, label_ch: np.ndarray) -> np.ndarray:
+def label_scores(q: np.ndarray, K_rows: np.ndarray, label_ch: np.ndarray, agg: str = "max") -> np.ndarray:
     """Approximate token scores on the label channels: for each key row,
-    the largest over the group of sum_{c in label_ch} q[h,c]*k[c]."""
+    the largest over the group of sum_{c in label_ch} q[h,c]*k[c] (or the
+    sum over the group with agg="sum")."""
     qc = q[:, label_ch]                  # [G, r]
     kc = K_rows[:, label_ch]             # [T, r]
-    return (qc @ kc.T).max(axis=0)
+    s = qc @ kc.T
+    return s.sum(axis=0) if agg == "sum" else s.max(axis=0)
 
 
 # ------------------------------------------------------ step 6: attention
@@ -224,27 +252,29 @@ def attend(q: np.ndarray, K_sel: np.ndarray, V_sel: np.ndarray, sm_scale: float)
 
 
 # -------------------------------------------------------- whole-unit pipeline
-def select_tokens_unit(q, K, n, bs, blk_idx, label_ch, k_tokens):
+def select_tokens_unit(q, K, n, bs, blk_idx, label_ch, k_tokens, agg="max"):
     """Token stage given a block set: candidates, label scores, top-K_t.
     Returns (tok_idx ascending positions, cand positions, label scores of cand)."""
     cand = candidate_tokens(blk_idx, n, bs)
-    s_tok = label_scores(q, K[cand], label_ch)
+    s_tok = label_scores(q, K[cand], label_ch, agg)
     keep = topk_stable(s_tok, k_tokens)
     return cand[keep], cand, s_tok
 
 
-def decode_unit(q, K, V, n, bs, k_blocks, label_ch, k_tokens, sm_scale, meta=None, meta_fp8=False):
+def decode_unit(q, K, V, n, bs, k_blocks, label_ch, k_tokens, sm_scale, meta=None, meta_fp8=False,
+                agg="max", sink=0, local=0):
     """One decode step of one unit over its first n tokens (the appended
     token included). q [G, d_k] float64; K [>=n, d_k], V [>=n, d_v] float64.
-    meta_fp8: block metadata quantised outward to e4m3 (``block_meta_e4m3``).
+    meta_fp8: block metadata quantised outward to e4m3 (``block_meta_e4m3``);
+    agg, sink, local: the selection variants (group sum, forced blocks).
 
     Returns a dict with the intermediate results of every stage."""
     if meta is None:
         meta = block_meta_e4m3(K, n, bs) if meta_fp8 else block_meta(K, n, bs)
     kmax, kmin = meta
-    s_blk = block_scores(q, kmax, kmin)
-    blk = topk_stable(s_blk, k_blocks)
-    tok, cand, s_tok = select_tokens_unit(q, K, n, bs, blk, label_ch, k_tokens)
+    s_blk = block_scores(q, kmax, kmin, agg)
+    blk = select_blocks(s_blk, k_blocks, sink, local)
+    tok, cand, s_tok = select_tokens_unit(q, K, n, bs, blk, label_ch, k_tokens, agg)
     out, lse = attend(q, K[tok], V[tok], sm_scale)
     return {"blk_score": s_blk, "blk_idx": blk, "cand": cand, "tok_score": s_tok,
             "tok_idx": tok, "out": out, "lse": lse, "kmax": kmax, "kmin": kmin}

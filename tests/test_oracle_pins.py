@@ -400,3 +400,61 @@ def test_quantised_meta_is_exact_for_keys_on_the_grid():
     K = r.choice(vals[np.abs(vals) <= 64], size=(50, 16))
     for a, b in zip(O.block_meta(K, 50, 8), O.block_meta_e4m3(K, 50, 8)):
         np.testing.assert_array_equal(a, b)
+
+
+# ------------------------------------ selection variants: forced blocks, sum
+@pytest.mark.parametrize("scores,k,sink,local,want", [
+    # worked by hand: block 0 and block 5 are forced, one slot left -> the best other (9 at block 2)
+    ([5, 1, 9, 3, 7, 2], 3, 1, 1, [0, 2, 5]),
+    ([5, 1, 9, 3, 7, 2], 2, 1, 1, [0, 5]),                 # no slot left beyond the forced ones
+    ([5, 1, 9, 3, 7, 2], 6, 1, 1, [0, 1, 2, 3, 4, 5]),     # budget covers everything
+    ([5, 1, 9, 3, 7, 2], 3, 2, 0, [0, 1, 2]),              # two sink blocks, then 9
+    ([5, 1, 9, 3, 7, 2], 4, 0, 2, [0, 2, 4, 5]),           # blocks 4, 5 forced, then 9 (2) and 5 (0)
+    ([3, 8], 2, 1, 1, [0, 1]),                             # the forced sets overlap the whole range
+    ([1, 2, 3], 3, 2, 2, [0, 1, 2]),                       # sink and local windows overlap
+    ([4, 4, 4, 4], 2, 0, 1, [0, 3]),                       # tie among the others: the lower index
+])
+def test_forced_blocks_hand_examples(scores, k, sink, local, want):
+    np.testing.assert_array_equal(O.select_blocks(np.array(scores, float), k, sink, local), want)
+
+
+def test_forced_blocks_brute_force():
+    """The kept set holds every forced block, has min(K_b, nb) entries, and
+    no dropped block beats a kept non-forced one (ties: lower index kept)."""
+    r = np.random.default_rng(4)
+    for _ in range(400):
+        nb = int(r.integers(1, 12))
+        s = r.integers(0, 5, nb).astype(float)      # many ties
+        sink, local = int(r.integers(0, 4)), int(r.integers(0, 4))
+        forced = set(range(min(sink, nb))) | set(range(max(0, nb - local), nb))
+        k = int(r.integers(len(forced), nb + 3)) if len(forced) <= nb + 2 else len(forced)
+        got = O.select_blocks(s, k, sink, local)
+        assert forced <= set(got.tolist()) and len(got) == min(k, nb) and np.all(np.diff(got) > 0)
+        kept = [j for j in got if j not in forced]
+        dropped = [j for j in range(nb) if j not in set(got.tolist())]
+        for a in kept:
+            for b in dropped:
+                assert s[a] > s[b] or (s[a] == s[b] and a < b)
+    with pytest.raises(ValueError):
+        O.select_blocks(np.zeros(8), 2, 2, 1)
+
+
+def test_sum_aggregation_closed_forms():
+    """One token per block: every head's bound is exact, so the summed group
+    bound is (sum_h q_h).k; the summed label score over all channels is the
+    same number; with one head, sum and max agree."""
+    q, K, _ = _rand_unit(12, 4, 16, 30)
+    kmax, kmin = O.block_meta(K, 30, 1)
+    np.testing.assert_allclose(O.block_scores(q, kmax, kmin, "sum"), K @ q.sum(axis=0), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(O.label_scores(q, K, np.arange(16), "sum"), K @ q.sum(axis=0), rtol=1e-12,
+                               atol=1e-12)
+    np.testing.assert_array_equal(O.block_scores(q[:1], kmax, kmin, "sum"), O.block_scores(q[:1], kmax, kmin))
+
+
+def test_sum_aggregated_bound_dominates_summed_block_maxima():
+    q, K, _ = _rand_unit(13, 4, 32, 120, scale=2.0)
+    kmax, kmin = O.block_meta(K, 120, 16)
+    s = O.block_scores(q, kmax, kmin, "sum")
+    for j in range(kmax.shape[0]):
+        true = (q @ K[j * 16: (j + 1) * 16].T).max(axis=1).sum()
+        assert s[j] >= true - 1e-12
