@@ -20,6 +20,8 @@ struct Shape {
     int B, Hq, Hkv, G, dk, dv, valias, bs, r, kb, kt, max_ctx, nb_cap;
     float sm_scale;
     int meta8;   // block metadata in fp8 e4m3 (outward rounded) instead of bf16
+    int agg_sum; // group scores summed over the query heads instead of their max
+    int sink, local;   // always-kept first / last blocks
 };
 
 Shape make_shape(const hsab_dims& d);

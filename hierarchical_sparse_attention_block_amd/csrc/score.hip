@@ -59,7 +59,7 @@ __global__ __launch_bounds__(256) void block_score_kernel(
     const uint16_t* __restrict__ q, uint16_t* __restrict__ meta,
     const int32_t* __restrict__ ctx_len, float* __restrict__ score,
     int Hkv, int G, int dk, int bs, int max_ctx, int nb_cap, int tiles_per_wave, Append ap,
-    int32_t* __restrict__ sel_cnt) {
+    int32_t* __restrict__ sel_cnt, int agg_sum) {
     __shared__ f32x4_t red[KSPLIT > 1 ? SPLIT_TILES * KSPLIT * MT * 64 : 1];
 
     const int unit = blockIdx.y, b = unit / Hkv, g = unit % Hkv;
@@ -189,17 +189,16 @@ __global__ __launch_bounds__(256) void block_score_kernel(
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) tot[mt] = acc[mt][0] + acc[mt][1];
     };
-    // group maximum of the bound of tile t's blocks, stored
+    // group maximum (or sum) of the bound of tile t's blocks, stored
     auto emit = [&](int t, const f32x4_t (&tot)[MT]) {
-        float v = -INFINITY;
+        float v = agg_sum ? 0.f : -INFINITY;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                if (mt * 16 + (lane >> 4) * 4 + i < G) v = fmaxf(v, tot[mt][i]);
+                if (mt * 16 + (lane >> 4) * 4 + i < G) v = agg_sum ? v + tot[mt][i] : fmaxf(v, tot[mt][i]);
         if (G > 4) {   // heads 4.. sit in the other 16-lane rows
-            v = max_xor16(v);
-            v = max_xor32(v);
+            v = agg_sum ? sum_xor32(sum_xor16(v)) : max_xor32(max_xor16(v));
         }
         const int jl = tile_j0(t) + (lane & 15);
         if (lane < 16 && jl < nb) Su[jl] = v;
@@ -256,7 +255,7 @@ hipError_t launch_t(const Shape& s, const uint16_t* q, uint16_t* meta, const int
     const int per_wg = TILES_WG * tpw * 16;
     dim3 grid((s.nb_cap + per_wg - 1) / per_wg, s.B * s.Hkv);
     hipLaunchKernelGGL((block_score_kernel<MT, KSW, KSPLIT, F8>), grid, dim3(64 * SCORE_WAVES), 0, st, q, meta,
-                       ctx_len, score, s.Hkv, s.G, s.dk, s.bs, s.max_ctx, s.nb_cap, tpw, ap, sel_cnt);
+                       ctx_len, score, s.Hkv, s.G, s.dk, s.bs, s.max_ctx, s.nb_cap, tpw, ap, sel_cnt, s.agg_sum);
     return hipGetLastError();
 }
 

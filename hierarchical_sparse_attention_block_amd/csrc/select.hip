@@ -40,7 +40,8 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
     const uint16_t* __restrict__ klabel, const int32_t* __restrict__ label_ch,
     const int32_t* __restrict__ ctx_len, int32_t* __restrict__ blk_idx, int32_t* __restrict__ tok_idx,
     float* __restrict__ tok_score, uint32_t* __restrict__ gkeys, int32_t* __restrict__ cnt, int parts,
-    int units, int Hkv, int G, int dk, int bs, int r, int kb, int kt, int max_ctx, int nb_cap, int bs_shift) {
+    int units, int Hkv, int G, int dk, int bs, int r, int kb, int kt, int max_ctx, int nb_cap, int bs_shift,
+    int agg_sum, int sink, int local) {
     using Sel = TopK<SEL_WAVES, PT>;
     // candidate i sits in slot i / bs of the block list (a shift when bs is a power of two)
     auto slot_of = [&](int i) { return bs_shift >= 0 ? (i >> bs_shift) : i / bs; };
@@ -107,18 +108,28 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
 
     // ------------------------------------------------------------ blocks
     if (mode & 1) {
+        // forced blocks [0, s1) and [l0, nb) stay out of the ranking; the
+        // list is [0, s1), the top kb - forced of the rest, [l0, nb)
+        const int s1 = sink < nb ? sink : nb;
+        const int l0 = nb - local > s1 ? nb - local : s1;
+        const int nforced = s1 + (nb - l0);
         uint32_t bkey[PT];
 #pragma unroll
         for (int j = 0; j < PT; ++j) {
             const int i = (w * pt_b + j) * 64 + lane;
-            bkey[j] = (j < pt_b && i < nb) ? f32_key(sraw[j]) : 0u;
+            bkey[j] = (j < pt_b && i < nb && i >= s1 && i < l0) ? f32_key(sraw[j]) : 0u;
         }
         int32_t* bo = blk_idx + (size_t)unit * kb;
-        const int keff = Sel::select(bkey, pt_b, kb, s_sel, [&](int pos, int i) {
-            s_blk[pos] = i;
-            if (part == 0) bo[pos] = i;
+        const int keff = Sel::select(bkey, pt_b, kb - nforced, s_sel, [&](int pos, int i) {
+            s_blk[s1 + pos] = i;
+            if (part == 0) bo[s1 + pos] = i;
         });
-        for (int p = keff + threadIdx.x; p < kb; p += SEL_THREADS) {
+        for (int p = threadIdx.x; p < nforced; p += SEL_THREADS) {
+            const int at = p < s1 ? p : keff + p, blk = p < s1 ? p : l0 + (p - s1);
+            s_blk[at] = blk;
+            if (part == 0) bo[at] = blk;
+        }
+        for (int p = nforced + keff + threadIdx.x; p < kb; p += SEL_THREADS) {
             s_blk[p] = -1;
             if (part == 0) bo[p] = -1;
         }
@@ -176,16 +187,15 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
                                                                      acc1, 0, 0, 0);
             }
             if (st == KSr - 1 && tile < t_hi) {
-                float v = -INFINITY;
+                float v = agg_sum ? 0.f : -INFINITY;   // group max (or sum) of the label scores
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int h = (lane >> 4) * 4 + e;
-                    if (h < G) v = fmaxf(v, acc0[e]);
-                    if (16 + h < G) v = fmaxf(v, acc1[e]);
+                    if (h < G) v = agg_sum ? v + acc0[e] : fmaxf(v, acc0[e]);
+                    if (16 + h < G) v = agg_sum ? v + acc1[e] : fmaxf(v, acc1[e]);
                 }
                 if (G > 4) {   // heads 4.. sit in the other 16-lane rows
-                    v = max_xor16(v);
-                    v = max_xor32(v);
+                    v = agg_sum ? sum_xor32(sum_xor16(v)) : max_xor32(max_xor16(v));
                 }
                 const int i = tile * 16 + (lane & 15);
                 if (lane < 16 && i < ncand) {
@@ -255,11 +265,11 @@ hipError_t launch_t(const Shape& s, int mode, const uint16_t* q, const float* bl
     if (s.r >= 32)
         hipLaunchKernelGGL((select_kernel<PT, 32>), grid, dim3(SEL_THREADS), 0, st, mode, q, blk_score, klabel,
                            label_ch, ctx_len, blk_idx, tok_idx, tok_score, gkeys, cnt, parts, units, s.Hkv, s.G,
-                           s.dk, s.bs, s.r, s.kb, s.kt, s.max_ctx, s.nb_cap, shift);
+                           s.dk, s.bs, s.r, s.kb, s.kt, s.max_ctx, s.nb_cap, shift, s.agg_sum, s.sink, s.local);
     else
         hipLaunchKernelGGL((select_kernel<PT, 16>), grid, dim3(SEL_THREADS), 0, st, mode, q, blk_score, klabel,
                            label_ch, ctx_len, blk_idx, tok_idx, tok_score, gkeys, cnt, parts, units, s.Hkv, s.G,
-                           s.dk, s.bs, s.r, s.kb, s.kt, s.max_ctx, s.nb_cap, shift);
+                           s.dk, s.bs, s.r, s.kb, s.kt, s.max_ctx, s.nb_cap, shift, s.agg_sum, s.sink, s.local);
     return hipGetLastError();
 }
 

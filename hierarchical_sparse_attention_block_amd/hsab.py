@@ -34,7 +34,8 @@ class Dims(ctypes.Structure):
                 ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32), ("v_alias_k", ctypes.c_int32),
                 ("block", ctypes.c_int32), ("r", ctypes.c_int32), ("k_blocks", ctypes.c_int32),
                 ("k_tokens", ctypes.c_int32), ("max_ctx", ctypes.c_int32), ("sm_scale", ctypes.c_float),
-                ("meta_format", ctypes.c_int32)]
+                ("meta_format", ctypes.c_int32), ("group_agg", ctypes.c_int32), ("sink_blocks", ctypes.c_int32),
+                ("local_blocks", ctypes.c_int32)]
 
     @property
     def group(self):
@@ -49,12 +50,14 @@ class Dims(ctypes.Structure):
 
 
 META_BF16, META_FP8 = 0, 1   # block metadata formats (HSAB_META_BF16 / HSAB_META_FP8)
+AGG_MAX, AGG_SUM = 0, 1      # group score combination (HSAB_AGG_MAX / HSAB_AGG_SUM)
 
 
 def dims(batch, n_q_heads, n_kv_heads, d_k, d_v, v_alias_k, block, r, k_blocks, k_tokens, max_ctx,
-         sm_scale, meta_format=META_BF16) -> Dims:
+         sm_scale, meta_format=META_BF16, group_agg=AGG_MAX, sink_blocks=0, local_blocks=0) -> Dims:
     return Dims(batch, n_q_heads, n_kv_heads, d_k, d_v, int(bool(v_alias_k)), block, r, k_blocks,
-                k_tokens, max_ctx, float(sm_scale), int(meta_format))
+                k_tokens, max_ctx, float(sm_scale), int(meta_format), int(group_agg), int(sink_blocks),
+                int(local_blocks))
 
 
 _vp, _sz, _i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32

@@ -68,6 +68,9 @@ class Workload:
     n_planted: int       # planted keys per (batch, KV head)
     seed: int
     meta_fp8: bool = False   # block metadata as outward-rounded fp8 e4m3 instead of bf16
+    agg_sum: bool = False    # group scores summed over the query heads (selection variant)
+    sink_blocks: int = 0     # always-kept first blocks (selection variant)
+    local_blocks: int = 0    # always-kept last blocks (selection variant)
 
     @property
     def group(self) -> int:

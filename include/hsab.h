@@ -106,7 +106,22 @@ typedef struct hsab_dims {
     int32_t max_ctx;      /* cache capacity (tokens) per unit */
     float   sm_scale;     /* logit scale, typically 1/sqrt(d_k) */
     int32_t meta_format;  /* HSAB_META_BF16 (0) or HSAB_META_FP8 (1) */
+    int32_t group_agg;    /* HSAB_AGG_MAX (0) or HSAB_AGG_SUM (1): how the query heads of a
+                             group combine block and token scores */
+    int32_t sink_blocks;  /* the first sink_blocks blocks are always kept */
+    int32_t local_blocks; /* the last local_blocks blocks (newest) are always kept;
+                             sink_blocks + local_blocks <= k_blocks */
 } hsab_dims;
+
+/* Selection variants (opt-in; zero-initialised dims select the default).
+ * The pages combine no query-head scores and force no blocks; their
+ * related-work list names StreamingLLM (AsyncTLS index page, "Builds on").
+ * HSAB_AGG_SUM scores a block (token) by the sum of the group's bounds
+ * (label scores) instead of their maximum. Forced blocks occupy K_b slots;
+ * the remaining slots take the best other blocks; hsab_select_blocks and
+ * the block stage of hsab_decode_step and the offload engine apply them. */
+#define HSAB_AGG_MAX 0
+#define HSAB_AGG_SUM 1
 
 #define HSAB_META_BF16 0   /* block metadata in bf16 (exact key max/min) */
 #define HSAB_META_FP8  1   /* fp8 e4m3, max rounded up, min rounded down */

@@ -32,7 +32,8 @@ def dims_of(w: W.Workload):
     from hierarchical_sparse_attention_block_amd import hsab as H
     return H.dims(w.batch, w.n_q_heads, w.n_kv_heads, w.d_k, w.d_v, w.v_alias_k, w.block, w.r,
                   w.k_blocks, w.k_tokens, w.max_ctx, w.sm_scale,
-                  H.META_FP8 if w.meta_fp8 else H.META_BF16)
+                  H.META_FP8 if w.meta_fp8 else H.META_BF16, H.AGG_SUM if w.agg_sum else H.AGG_MAX,
+                  w.sink_blocks, w.local_blocks)
 
 
 def host_inputs(w: W.Workload, ctx_len=None, threads=8):
@@ -145,6 +146,30 @@ def check_index_set(scores, gpu_idx, k, what=""):
     return sel.astype(np.int64), True
 
 
+def check_block_set(s_blk, gpu_blk, k_blocks, sink, local, what=""):
+    """Block list with forced blocks: the first `sink` and last `local`
+    blocks must be present; the rest of the list is checked as a top-k of
+    the other blocks under the near-tie rule."""
+    nb = len(s_blk)
+    forced = sorted(set(range(min(sink, nb))) | set(range(max(0, nb - local), nb)))
+    if not forced:
+        return check_index_set(s_blk, gpu_blk, k_blocks, what)
+    g = np.asarray(gpu_blk)
+    sel = g[g >= 0]
+    assert np.all(g[len(sel):] == -1) and np.all(np.diff(sel) > 0), f"{what}: list layout"
+    assert set(forced) <= set(sel.tolist()), f"{what}: a forced block is missing"
+    others = np.array([j for j in range(nb) if j not in set(forced)], np.int64)
+    rest = np.array([j for j in sel if j not in set(forced)], np.int64)
+    pos = np.searchsorted(others, rest)
+    k_rest = k_blocks - len(forced)
+    if k_rest == 0 or others.size == 0:
+        assert rest.size == 0, f"{what}: blocks beyond the forced ones with no slot left"
+        return np.array(forced, np.int64), False
+    padded = np.concatenate([pos, np.full(max(0, k_rest - len(pos)), -1)])
+    got, tie = check_index_set(np.asarray(s_blk)[others], padded, k_rest, what)
+    return np.sort(np.concatenate([np.array(forced, np.int64), others[got]])), tie
+
+
 def oracle_unit_vs_gpu(w, q_bits, K_bits, V_bits, ctx, label, b, g, gpu_blk, gpu_tok, gpu_out, gpu_lse):
     """Check one unit against the oracle under the parity rules; stage two
     and three of the oracle run on the GPU's accepted sets."""
@@ -153,11 +178,13 @@ def oracle_unit_vs_gpu(w, q_bits, K_bits, V_bits, ctx, label, b, g, gpu_blk, gpu
     q = O.bf16_to_f64(q_bits[b, g * G:(g + 1) * G])
     K = O.bf16_to_f64(K_bits[b, g, :n])
     V = K[:, : w.d_v] if w.v_alias_k else O.bf16_to_f64(V_bits[b, g, :n])
+    agg = "sum" if w.agg_sum else "max"
     kmax, kmin = (O.block_meta_e4m3 if w.meta_fp8 else O.block_meta)(K, n, w.block)
-    s_blk = O.block_scores(q, kmax, kmin)
-    blk, tie_b = check_index_set(s_blk, gpu_blk, w.k_blocks, f"blocks of unit ({b},{g})")
+    s_blk = O.block_scores(q, kmax, kmin, agg)
+    blk, tie_b = check_block_set(s_blk, gpu_blk, w.k_blocks, w.sink_blocks, w.local_blocks,
+                                 f"blocks of unit ({b},{g})")
     cand = O.candidate_tokens(blk, n, w.block)
-    s_tok = O.label_scores(q, K[cand], label[g])
+    s_tok = O.label_scores(q, K[cand], label[g], agg)
     # the GPU reports positions; map them to candidate indices
     k_eff = min(w.k_tokens, len(cand))
     pos = np.asarray(gpu_tok[:k_eff])
