@@ -48,6 +48,13 @@ attention mass rather than its most demanding head), and the first
 appended token) may be kept unconditionally, the remaining K_b - forced
 slots going to the best of the other blocks.
 
+Label-channel calibration (``calibrate_labels``): the fine stage scores
+tokens on a few important channels chosen offline (Double Sparsity)
+[gist.science/de, section 2.A "Stufe 2"; gist.science/es, section 2.A item
+2]; the pages do not define "important". Reading taken here: channel c of
+a KV head weighs sum |q_c * k_c| over sampled (query, key) pairs of that
+head's group, and the r heaviest channels form the label set.
+
 Quantised block metadata (``e4m3_*``, ``block_meta_e4m3``): the pages name
 quantisation of the index data as a way to cut the indexing cost
 [gist.science/de, section 2.A "Stufe 2"] and give no scheme. Reading taken
@@ -74,7 +81,7 @@ __all__ = [
     "bf16_to_f64", "n_blocks", "block_meta", "append_meta", "quest_bound",
     "quest_bound_gemm", "block_scores", "topk_stable", "candidate_tokens",
     "label_scores", "attend", "select_tokens_unit", "decode_unit", "select_blocks",
-    "e4m3_grid", "e4m3_round", "block_meta_e4m3",
+    "e4m3_grid", "e4m3_round", "block_meta_e4m3", "calibrate_labels",
     "decode_all", "offload_delta", "offload_held", "offload_schedule", "offload_run",
 ]
 
@@ -231,6 +238,15 @@ def label_scores(q: np.ndarray, K_rows: np.ndarray, label_ch: np.ndarray, agg: s
     kc = K_rows[:, label_ch]             # [T, r]
     s = qc @ kc.T
     return s.sum(axis=0) if agg == "sum" else s.max(axis=0)
+
+
+def calibrate_labels(q_samples: np.ndarray, k_samples: np.ndarray, r: int) -> np.ndarray:
+    """Label channels of one KV head from sampled activations: channel
+    importance = sum over samples s and the group's query heads h of
+    |q[s,h,c] * k[s,c]|; the r most important channels, ties to the lower
+    channel, ascending. q_samples [S, G, d], k_samples [S, d] float64."""
+    imp = np.abs(q_samples * k_samples[:, None, :]).sum(axis=(0, 1))
+    return topk_stable(imp, r)
 
 
 # ------------------------------------------------------ step 6: attention

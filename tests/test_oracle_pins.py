@@ -458,3 +458,46 @@ def test_sum_aggregated_bound_dominates_summed_block_maxima():
     for j in range(kmax.shape[0]):
         true = (q @ K[j * 16: (j + 1) * 16].T).max(axis=1).sum()
         assert s[j] >= true - 1e-12
+
+
+# ------------------------------------------------- label-channel calibration
+def test_calibration_hand_example():
+    """Two samples, one head, four channels: |q*k| per channel sums to
+    [0.5+0, 4+1, 0+3, 1+1] = [0.5, 5, 3, 2] -> the two heaviest are 1 and 2."""
+    q = np.array([[[1.0, -2.0, 0.0, 1.0]], [[0.0, 1.0, 3.0, -1.0]]])
+    k = np.array([[0.5, 2.0, 7.0, 1.0], [4.0, -1.0, 1.0, 1.0]])
+    np.testing.assert_array_equal(O.calibrate_labels(q, k, 2), [1, 2])
+    np.testing.assert_array_equal(O.calibrate_labels(q, k, 3), [1, 2, 3])
+
+
+def test_calibration_brute_force_and_symmetries():
+    """The chosen set has the largest total importance among all r-subsets
+    (enumerated); it is unchanged by scaling the samples and follows a
+    permutation of the channels; r = d keeps every channel."""
+    r_ = np.random.default_rng(6)
+    for _ in range(30):
+        d, G, S, r = 8, int(r_.integers(1, 4)), int(r_.integers(1, 6)), int(r_.integers(1, 8))
+        q = r_.standard_normal((S, G, d)) * r_.uniform(0.1, 3, d)
+        k = r_.standard_normal((S, d)) * r_.uniform(0.1, 3, d)
+        imp = np.abs(q * k[:, None, :]).sum(axis=(0, 1))
+        got = O.calibrate_labels(q, k, r)
+        best = max(itertools.combinations(range(d), r), key=lambda c: imp[list(c)].sum())
+        assert math.isclose(imp[got].sum(), imp[list(best)].sum(), rel_tol=1e-12)
+        np.testing.assert_array_equal(O.calibrate_labels(3.5 * q, 0.25 * k, r), got)
+        perm = r_.permutation(d)
+        np.testing.assert_array_equal(np.sort(perm[O.calibrate_labels(q[:, :, perm], k[:, perm], r)]), got)
+    q = r_.standard_normal((3, 2, 6))
+    np.testing.assert_array_equal(O.calibrate_labels(q, r_.standard_normal((3, 6)), 6), np.arange(6))
+
+
+def test_calibration_recovers_outlier_channels():
+    """Keys with a few large-scale channels (the workloads' scaled keys):
+    those channels dominate |q*k| and are the label set."""
+    r_ = np.random.default_rng(7)
+    d, r = 64, 8
+    scale = np.full(d, 0.2)
+    hot = r_.choice(d, r, replace=False)
+    scale[hot] = 10.0
+    q = r_.standard_normal((256, 4, d))
+    k = r_.standard_normal((256, d)) * scale
+    np.testing.assert_array_equal(O.calibrate_labels(q, k, r), np.sort(hot))
