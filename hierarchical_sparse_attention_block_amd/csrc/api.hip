@@ -202,6 +202,15 @@ int hsab_decode_step(const hsab_dims* dims, const uint16_t* q, const uint16_t* k
                                     reinterpret_cast<float*>(w + L.part_acc), out, lse, stream));
 }
 
+int hsab_calibrate_labels(const hsab_dims* dims, const uint16_t* q_samples, const uint16_t* k_samples,
+                          int32_t n_samples, float* importance, int32_t* label_ch, hipStream_t stream) {
+    int rc = check_dims(dims);
+    if (rc) return rc;
+    if (!q_samples || !k_samples || !importance || !label_ch || n_samples < 1) return HSAB_EINVAL;
+    return hip_status(launch_calibrate(make_shape(*dims), q_samples, k_samples, n_samples, importance, label_ch,
+                                       stream));
+}
+
 size_t hsab_dense_workspace_bytes(const hsab_dims* dims) {
     if (check_dims(dims) != HSAB_OK) return 0;
     const Shape s = make_shape(*dims);

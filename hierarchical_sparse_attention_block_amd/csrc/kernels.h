@@ -69,6 +69,10 @@ size_t dense_workspace_bytes(const Shape& s);
 hipError_t launch_dense(const Shape& s, const uint16_t* q, const uint16_t* K, const uint16_t* V,
                         const int32_t* ctx_len, float* out, float* lse, void* ws, hipStream_t st);
 
+// Label-channel calibration from n_samples sampled (query, key) pairs (calib.hip).
+hipError_t launch_calibrate(const Shape& s, const uint16_t* q_samples, const uint16_t* k_samples, int n_samples,
+                            float* importance, int32_t* label_ch, hipStream_t st);
+
 // offload engine (offload.hip); per-step timing events kept for this many steps
 constexpr int TIMING_RING = 32;
 hipError_t launch_append_slot(const Shape& s, int n_slots, const uint16_t* k_new, const uint16_t* v_new,

@@ -26,7 +26,8 @@ EXPORTS = ("hsab_workspace_bytes", "hsab_status_string", "hsab_last_hip_error", 
            "hsab_score_blocks", "hsab_select_blocks", "hsab_select_tokens", "hsab_sparse_attend",
            "hsab_decode_step", "hsab_offload_append", "hsab_offload_plan", "hsab_offload_copy", "hsab_offload_create",
            "hsab_offload_destroy", "hsab_offload_begin", "hsab_offload_step", "hsab_offload_timing",
-           "hsab_offload_selection", "hsab_dense_workspace_bytes", "hsab_dense_attend")
+           "hsab_offload_selection", "hsab_dense_workspace_bytes", "hsab_dense_attend",
+           "hsab_calibrate_labels")
 
 
 class Dims(ctypes.Structure):
@@ -90,6 +91,7 @@ class OffloadStats(ctypes.Structure):
 
 
 _lib.hsab_offload_create.argtypes = [_D, _i32, _i32, ctypes.POINTER(_vp)]
+_lib.hsab_calibrate_labels.argtypes = [_D, _vp, _vp, _i32, _vp, _vp, _vp]
 _lib.hsab_dense_workspace_bytes.argtypes = [_D]
 _lib.hsab_dense_attend.argtypes = [_D, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
 _lib.hsab_offload_destroy.argtypes = [_vp]
@@ -424,3 +426,15 @@ def raw_call(name, *args):
     """Call an exported entry point with raw ctypes arguments and return its
     status (used by the host-side error-path tests)."""
     return getattr(_lib, name)(*args)
+
+
+def calibrate_labels(d: Dims, q_samples, k_samples, n_samples, importance, label_ch, stream=None):
+    """Label channels per KV head from n_samples sampled query rows
+    [n][Hq][d_k] and key rows [n][Hkv][d_k] (bf16 bits); writes importance
+    [Hkv][d_k] fp32 and label_ch [Hkv][r] int32."""
+    n = int(n_samples)
+    _check("hsab_calibrate_labels", _lib.hsab_calibrate_labels(
+        ctypes.byref(d), _buf("q_samples", q_samples, _u16, n * d.n_q_heads * d.d_k),
+        _buf("k_samples", k_samples, _u16, n * d.n_kv_heads * d.d_k), ctypes.c_int32(n),
+        _buf("importance", importance, _f, d.n_kv_heads * d.d_k), _buf("label_ch", label_ch, _i, d.n_kv_heads * d.r),
+        _stream(stream)))

@@ -205,6 +205,22 @@ int hsab_decode_step(const hsab_dims* dims, const uint16_t* q, const uint16_t* k
                      int32_t* blk_idx, int32_t* tok_idx, float* out, float* lse,
                      void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* ------------------------------------------------- label-channel calibration
+ * The offline step that chooses the label channels the fine stage scores
+ * tokens on (Double Sparsity; AsyncTLS, gist.science/de explainer section
+ * 2.A "Stufe 2", gist.science/es explainer section 2.A item 2; the pages do
+ * not define "important", this library reads it as below):
+ *   importance[g][c] = sum_{s < n_samples} sum_{h in group g} |q_s[h][c] * k_s[g][c]|
+ *   label_ch[g]      = the r channels of largest importance (ties to the
+ *                      lower channel), ascending
+ * q_samples [n_samples][Hq][d_k] bf16 and k_samples [n_samples][Hkv][d_k]
+ * bf16 are sampled query / key rows (device); importance [Hkv][d_k] fp32 and
+ * label_ch [Hkv][r] int32 are written (device). The sums are fp32 in a fixed
+ * order (deterministic). Only batch-independent dims fields are used (Hq,
+ * Hkv, d_k, r). HSAB_EINVAL for null pointers or n_samples < 1. */
+int hsab_calibrate_labels(const hsab_dims* dims, const uint16_t* q_samples, const uint16_t* k_samples,
+                          int32_t n_samples, float* importance, int32_t* label_ch, hipStream_t stream);
+
 /* ------------------------------------------------------------ dense reference
  * Full attention over every token, the operator the sparse step replaces
  * (the pages report the sparse operator's speedup over full attention
