@@ -211,6 +211,33 @@ def fp8_meta_leg(w, base, reps, stream, args, ms_step_bf16):
                             "achieved": round(ach, 1), "frac": round(ach / HBM_PEAK_GBS, 4)}}
 
 
+def variants_leg(w, base, reps, stream, args, ms_step):
+    """Cost of the opt-in selection variants (group sum, one sink block and
+    two local blocks) on the same step, and of one label-channel
+    calibration over 1024 sampled (query, key) rows of every KV head."""
+    wv = dataclasses.replace(w, agg_sum=True, sink_blocks=1, local_blocks=2)
+    dv = dims_of(wv)
+
+    def dec(r):
+        return lambda: H.decode_step(dv, base["q"], base["k_new"], base["v_new"], r.K, r.V, r.meta, r.klabel,
+                                     base["label"], base["ctx"], r.blk, r.tok, r.out, r.lse, r.ws, stream=stream)
+    ms = time_replays([dec(r) for r in reps], stream, args.warmup, args.steps, not args.no_graph)
+    S = 1024
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    qs = torch.randn(S * w.n_q_heads * w.d_k, generator=gen, device="cuda").to(torch.bfloat16)
+    ks = torch.randn(S * w.n_kv_heads * w.d_k, generator=gen, device="cuda").to(torch.bfloat16)
+    imp = torch.empty(w.n_kv_heads * w.d_k, device="cuda")
+    lab = torch.empty(w.n_kv_heads * w.r, dtype=torch.int32, device="cuda")
+    d = dims_of(w)
+    ms_cal = time_replays([lambda: H.calibrate_labels(d, qs, ks, S, imp, lab, stream=stream)], stream, 3, 20,
+                          not args.no_graph)
+    cal_bytes = S * (w.n_q_heads + w.n_kv_heads) * w.d_k * 2
+    log(f"[bench] variants step {ms * 1e3:.1f} us; calibration {ms_cal * 1e3:.1f} us")
+    return {"agg_sum_sink1_local2": {"ms_per_step": round(ms, 6), "vs_default_step": round(ms / ms_step, 3)},
+            "calibration": {"samples": S, "us_per_call": round(ms_cal * 1e3, 2), "bytes_read": cal_bytes,
+                            "achieved_gbs": round(cal_bytes / (ms_cal * 1e-3) / 1e9, 1)}}
+
+
 def decode(d, base, rep, stream):
     H.decode_step(d, base["q"], base["k_new"], base["v_new"], rep.K, rep.V, rep.meta, rep.klabel,
                   base["label"], base["ctx"], rep.blk, rep.tok, rep.out, rep.lse, rep.ws, stream=stream)
@@ -453,7 +480,7 @@ def main():
     ap.add_argument("--meta", default="bf16", choices=["bf16", "fp8"],
                     help="block metadata format of the timed step (fp8: e4m3, rounded outward)")
     ap.add_argument("--no-fp8-leg", action="store_true",
-                    help="skip the extra timing of the step with fp8 metadata")
+                    help="skip the extra timings (fp8 metadata, selection variants, calibration)")
     ap.add_argument("--offload-runs", type=int, default=3, help="timed 16-step runs of the offload workload")
     ap.add_argument("--score-only", type=int, default=0,
                     help="only launch the block-score kernel this many times (for counter runs)")
@@ -568,6 +595,8 @@ def main():
         res["dense_reference"] = dense
     if not w.meta_fp8 and not args.no_fp8_leg and w.d_k % 32 == 0:
         res["meta_fp8"] = fp8_meta_leg(w, base, reps, stream, args, ms_step)
+    if not args.no_fp8_leg:
+        res["variants"] = variants_leg(w, base, reps, stream, args, ms_step)
     if not args.no_cpu:
         log("[bench] timing the CPU oracle on a bounded sample")
         res["cpu_baseline"] = cpu_baseline(w, host)

@@ -24,11 +24,22 @@ __global__ __launch_bounds__(CAL_WAVES * 64) void channel_weight_kernel(
     __shared__ float part[CAL_WAVES][64];
     const int g = blockIdx.x, c = blockIdx.y * 64 + (threadIdx.x & 63), w = threadIdx.x >> 6;
     const int cc = c < dk ? c : dk - 1;   // lanes past d_k read a valid channel and drop it
+    // each product of two bf16 values is exact in fp32; the group's heads
+    // are read four at a time so their loads are in flight together
     float acc = 0.f;
     for (int s = w; s < n_samples; s += CAL_WAVES) {
         const float kv = bf16_f32(ks[((size_t)s * Hkv + g) * dk + cc]);
         const uint16_t* qr = qs + ((size_t)s * Hq + (size_t)g * G) * dk + cc;
-        for (int h = 0; h < G; ++h) acc += fabsf(bf16_f32(qr[(size_t)h * dk]) * kv);   // product exact in fp32
+        int h = 0;
+        for (; h + 4 <= G; h += 4) {
+            const float q0 = bf16_f32(qr[(size_t)h * dk]), q1 = bf16_f32(qr[(size_t)(h + 1) * dk]);
+            const float q2 = bf16_f32(qr[(size_t)(h + 2) * dk]), q3 = bf16_f32(qr[(size_t)(h + 3) * dk]);
+            acc += fabsf(q0 * kv);
+            acc += fabsf(q1 * kv);
+            acc += fabsf(q2 * kv);
+            acc += fabsf(q3 * kv);
+        }
+        for (; h < G; ++h) acc += fabsf(bf16_f32(qr[(size_t)h * dk]) * kv);
     }
     part[w][threadIdx.x & 63] = acc;
     __syncthreads();
