@@ -19,89 +19,113 @@ from hsab_testlib import check_index_set, dims_of, dev16, OUT_ATOL, LSE_RTOL
 pytestmark = pytest.mark.gpu
 
 
-def _run_offload(w, prefill, steps, n_slots=None, copy_mode=0):
-    from hierarchical_sparse_attention_block_amd import hsab as H
-    d = dims_of(w)
-    U, B, Hkv, G = w.units, w.batch, w.n_kv_heads, w.group
-    bs, nb_cap = w.block, d.nb_cap
-    n_slots = n_slots or 2 * w.k_blocks + 2
-    prefill = np.asarray(prefill, np.int32)
-    assert prefill.max() + steps <= w.max_ctx
-    print(f"offload run {w.name} B={B} Hkv={Hkv} G={G} d_k={w.d_k} prefill={prefill.tolist()} steps={steps} "
-          f"copy_mode={copy_mode}", flush=True)
+class _Layer:
+    """One attention layer of an offload run: its host pool, GPU state and
+    engine. step(t) enqueues decode step t without waiting; collect(t)
+    reads its results after the caller synchronised."""
 
-    # host cache: prefill rows plus one new token per step
-    q0 = W.queries(w)
-    n_all = int(prefill.max()) + steps
-    K = np.zeros((B, Hkv, w.max_ctx, w.d_k), np.uint16)
-    V = None if w.v_alias_k else np.zeros((B, Hkv, w.max_ctx, w.d_v), np.uint16)
-    for b in range(B):
-        for g in range(Hkv):
-            kb, vb = W.unit_kv(w, b, g, q0, n_all)
-            K[b, g, : prefill[b]] = kb[: prefill[b]]
-            if V is not None:
-                V[b, g, : prefill[b]] = vb[: prefill[b]]
-    news = [W.new_token(w, t) for t in range(steps)]
-    for t, (kn, vn) in enumerate(news):
+    def __init__(self, w, prefill, steps, n_slots=None, copy_mode=0, copy_stream=None):
+        from hierarchical_sparse_attention_block_amd import hsab as H
+        self.w, self.H = w, H
+        d = dims_of(w)
+        U, B, Hkv, G = w.units, w.batch, w.n_kv_heads, w.group
+        bs, nb_cap = w.block, d.nb_cap
+        n_slots = n_slots or 2 * w.k_blocks + 2
+        prefill = np.asarray(prefill, np.int32)
+        assert prefill.max() + steps <= w.max_ctx
+        print(f"offload run {w.name} B={B} Hkv={Hkv} G={G} d_k={w.d_k} prefill={prefill.tolist()} steps={steps} "
+              f"copy_mode={copy_mode}", flush=True)
+
+        # host cache: prefill rows plus one new token per step
+        q0 = W.queries(w)
+        n_all = int(prefill.max()) + steps
+        K = np.zeros((B, Hkv, w.max_ctx, w.d_k), np.uint16)
+        V = None if w.v_alias_k else np.zeros((B, Hkv, w.max_ctx, w.d_v), np.uint16)
         for b in range(B):
-            K[b, :, prefill[b] + t] = kn[b]
-            if V is not None:
-                V[b, :, prefill[b] + t] = vn[b]
-    qs = [q0]
-    for t in range(1, steps):
-        qs.append(W.f32_to_bf16_bits(W.drift_queries(W.bf16_bits_to_f32(qs[-1]), w, t)))
-
-    # pinned pool [U][nb_cap][block keys | block values], prefill rows only
-    be = H.block_elems(d)
-    pool = torch.zeros(U * nb_cap * be, dtype=torch.int16, pin_memory=True)
-    pv = pool.numpy().view(np.uint16).reshape(U, nb_cap, be)
-    for b in range(B):
-        for g in range(Hkv):
-            u = b * Hkv + g
-            for p in range(prefill[b]):
-                j, off = divmod(p, bs)
-                pv[u, j, off * w.d_k:(off + 1) * w.d_k] = K[b, g, p]
+            for g in range(Hkv):
+                kb, vb = W.unit_kv(w, b, g, q0, n_all)
+                K[b, g, : prefill[b]] = kb[: prefill[b]]
                 if V is not None:
-                    pv[u, j, bs * w.d_k + off * w.d_v: bs * w.d_k + (off + 1) * w.d_v] = V[b, g, p]
+                    V[b, g, : prefill[b]] = vb[: prefill[b]]
+        news = [W.new_token(w, t) for t in range(steps)]
+        for t, (kn, vn) in enumerate(news):
+            for b in range(B):
+                K[b, :, prefill[b] + t] = kn[b]
+                if V is not None:
+                    V[b, :, prefill[b] + t] = vn[b]
+        qs = [q0]
+        for t in range(1, steps):
+            qs.append(W.f32_to_bf16_bits(W.drift_queries(W.bf16_bits_to_f32(qs[-1]), w, t)))
 
-    # GPU side: metadata and label rows of the prefill, block cache, outputs
-    Kpre = K.copy()
-    for b in range(B):
-        Kpre[b, :, prefill[b]:] = 0
-    meta = H.alloc_meta(d)
-    klabel = torch.zeros(U * w.max_ctx * w.r, dtype=torch.int16, device="cuda")
-    label = torch.from_numpy(W.label_channels(w)).cuda()
-    H.build_meta(d, dev16(Kpre), torch.from_numpy(prefill).cuda(), label, meta, klabel)
-    cache = torch.zeros(U * n_slots * be, dtype=torch.int16, device="cuda")
-    slot_of = torch.full((U * nb_cap,), -1, dtype=torch.int32, device="cuda")
-    tok = torch.full((U * w.k_tokens,), -7, dtype=torch.int32, device="cuda")
-    out = torch.full((B * w.n_q_heads * w.d_v,), float("nan"), device="cuda")
-    lse = torch.full((B * w.n_q_heads,), float("nan"), device="cuda")
-    ws = H.alloc_workspace(d)
-    copy_stream = torch.cuda.Stream()
-    eng = H.OffloadEngine(d, n_slots, copy_mode)
-    eng.begin(torch.from_numpy(prefill.copy()), pool, cache, slot_of)
+        # pinned pool [U][nb_cap][block keys | block values], prefill rows only
+        be = H.block_elems(d)
+        pool = torch.zeros(U * nb_cap * be, dtype=torch.int16, pin_memory=True)
+        pv = pool.numpy().view(np.uint16).reshape(U, nb_cap, be)
+        for b in range(B):
+            for g in range(Hkv):
+                u = b * Hkv + g
+                for p in range(prefill[b]):
+                    j, off = divmod(p, bs)
+                    pv[u, j, off * w.d_k:(off + 1) * w.d_k] = K[b, g, p]
+                    if V is not None:
+                        pv[u, j, bs * w.d_k + off * w.d_v: bs * w.d_k + (off + 1) * w.d_v] = V[b, g, p]
 
-    res = []
+        # GPU side: metadata and label rows of the prefill, block cache, outputs
+        Kpre = K.copy()
+        for b in range(B):
+            Kpre[b, :, prefill[b]:] = 0
+        self.meta = H.alloc_meta(d)
+        self.klabel = torch.zeros(U * w.max_ctx * w.r, dtype=torch.int16, device="cuda")
+        self.label = torch.from_numpy(W.label_channels(w)).cuda()
+        H.build_meta(d, dev16(Kpre), torch.from_numpy(prefill).cuda(), self.label, self.meta, self.klabel)
+        self.cache = torch.zeros(U * n_slots * be, dtype=torch.int16, device="cuda")
+        self.slot_of = torch.full((U * nb_cap,), -1, dtype=torch.int32, device="cuda")
+        self.tok = torch.full((U * w.k_tokens,), -7, dtype=torch.int32, device="cuda")
+        self.out = torch.full((B * w.n_q_heads * w.d_v,), float("nan"), device="cuda")
+        self.lse = torch.full((B * w.n_q_heads,), float("nan"), device="cuda")
+        self.ws = H.alloc_workspace(d)
+        self.copy_stream = copy_stream or torch.cuda.Stream()
+        self.eng = H.OffloadEngine(d, n_slots, copy_mode)
+        self.eng.begin(torch.from_numpy(prefill.copy()), pool, self.cache, self.slot_of)
+        self.K, self.V, self.qs, self.news, self.pool, self.pv = K, V, qs, news, pool, pv
+        self.prefill, self.steps, self.res = prefill, steps, []
+
+    def step(self, t):
+        ctx_h = torch.from_numpy(self.prefill + t + 1)
+        V = self.V
+        return self.eng.step(dev16(self.qs[t]), dev16(self.news[t][0]),
+                             None if V is None else dev16(self.news[t][1]), self.pool, self.cache, self.meta,
+                             self.klabel, self.label, ctx_h.cuda(), ctx_h, self.slot_of, self.tok, self.out,
+                             self.lse, self.ws, copy_stream=self.copy_stream)
+
+    def collect(self, st):
+        w, B, Hkv = self.w, self.w.batch, self.w.n_kv_heads
+        self.res.append({"sel": self.eng.selection().numpy().copy(), "stats": st.as_dict(),
+                         "tok": self.tok.cpu().numpy().reshape(B, Hkv, w.k_tokens),
+                         "out": self.out.cpu().numpy().reshape(B, w.n_q_heads, w.d_v),
+                         "lse": self.lse.cpu().numpy().reshape(B, w.n_q_heads)})
+
+    def finish(self):
+        self.eng.close()
+        w, bs = self.w, self.w.block
+        # the pool now holds every appended token
+        for b in range(w.batch):
+            for g in range(w.n_kv_heads):
+                u = b * w.n_kv_heads + g
+                for p in range(self.prefill[b], self.prefill[b] + self.steps):
+                    j, off = divmod(p, bs)
+                    assert np.array_equal(self.pv[u, j, off * w.d_k:(off + 1) * w.d_k], self.K[b, g, p]), \
+                        "pool key row"
+        return self.K, self.V, self.qs, self.res
+
+
+def _run_offload(w, prefill, steps, n_slots=None, copy_mode=0):
+    layer = _Layer(w, prefill, steps, n_slots, copy_mode)
     for t in range(steps):
-        ctx_h = torch.from_numpy(prefill + t + 1)
-        st = eng.step(dev16(qs[t]), dev16(news[t][0]), None if V is None else dev16(news[t][1]), pool, cache,
-                      meta, klabel, label, ctx_h.cuda(), ctx_h, slot_of, tok, out, lse, ws,
-                      copy_stream=copy_stream)
+        st = layer.step(t)
         torch.cuda.synchronize()
-        res.append({"sel": eng.selection().numpy().copy(), "stats": st.as_dict(),
-                    "tok": tok.cpu().numpy().reshape(B, Hkv, w.k_tokens),
-                    "out": out.cpu().numpy().reshape(B, w.n_q_heads, w.d_v),
-                    "lse": lse.cpu().numpy().reshape(B, w.n_q_heads)})
-    eng.close()
-    # the pool now holds every appended token
-    for b in range(B):
-        for g in range(Hkv):
-            u = b * Hkv + g
-            for p in range(prefill[b], prefill[b] + steps):
-                j, off = divmod(p, bs)
-                assert np.array_equal(pv[u, j, off * w.d_k:(off + 1) * w.d_k], K[b, g, p]), "pool key row"
-    return K, V, qs, res
+        layer.collect(st)
+    return layer.finish()
 
 
 def _check_against_oracle(w, prefill, K, V, qs, res):
@@ -173,6 +197,25 @@ def test_offload_gqa_fp8_metadata():
     prefill = [300, 511]
     K, V, qs, res = _run_offload(w, prefill, steps=8, copy_mode=0)
     _check_against_oracle(w, np.array(prefill), K, V, qs, res)
+
+
+def test_offload_layers_interleaved():
+    """Three layers (own pools, caches, engines; different keys and queries)
+    stepped in turn on one compute and one copy stream: every layer still
+    matches the lagged oracle, step by step."""
+    base = W.WORKLOADS["tiny4k"].replace(name="offload_layers", batch=2, n_q_heads=8, n_kv_heads=2, k_blocks=8,
+                                         k_tokens=64, ctx=1024, max_ctx=1024, scaled_keys=True, n_planted=0)
+    prefill, steps = [300, 511], 6
+    xs = torch.cuda.Stream()
+    layers = [_Layer(base.replace(seed=40 + l), prefill, steps, copy_stream=xs) for l in range(3)]
+    for t in range(steps):
+        sts = [layer.step(t) for layer in layers]
+        torch.cuda.synchronize()
+        for layer, st in zip(layers, sts):
+            layer.collect(st)
+    for layer in layers:
+        K, V, qs, res = layer.finish()
+        _check_against_oracle(layer.w, np.array(prefill), K, V, qs, res)
 
 
 def test_offload_gqa_without_oracle_ties_equals_oracle_run():
