@@ -69,12 +69,21 @@ __global__ __launch_bounds__(256) void block_score_kernel(
     constexpr int TILES_WG = SCORE_WAVES / KSPLIT;     // block tiles side by side in a workgroup
     const int per_wg = TILES_WG * tiles_per_wave * 16;
     const int j_wg = blockIdx.x * per_wg;
+    // With an append and one tile per wave, an extra last column of
+    // workgroups appends the token and then scores the tile holding the tail
+    // block, which the workgroup covering that tile skips: the append then
+    // delays no streaming workgroup, and the tile is scored by the same code
+    // either way. Split-row workgroups (one per CU, a grid of about one
+    // round) append in the workgroup that owns the tail block instead, as an
+    // extra workgroup there would run in a second round.
+    constexpr bool SEP = KSPLIT == 1;
+    const bool app_wg = SEP && ap.k_new && blockIdx.x == gridDim.x - 1;
+    const int tail_j0 = SEP && ap.k_new ? ((nb - 1) & ~15) : -1;
     if (sel_cnt && blockIdx.x == 0 && threadIdx.x == 0)   // arrival counter of the split token selection
         __hip_atomic_store(&sel_cnt[unit], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (j_wg >= nb) return;
+    if (!app_wg && j_wg >= nb) return;
 
-    if (ap.k_new && nb - 1 < j_wg + per_wg) {
-        // this workgroup owns the tail block: append before scoring it
+    if (app_wg || (!SEP && ap.k_new && nb - 1 < j_wg + per_wg)) {
         const int pos = n - 1, jt = pos / bs;
         const bool first = (pos % bs) == 0;
         const uint16_t* kn = ap.k_new + (size_t)unit * dk;
@@ -106,7 +115,10 @@ __global__ __launch_bounds__(256) void block_score_kernel(
     const int tslot = KSPLIT > 1 ? 0 : wave;             // tile column of this wave
     const int s_lo = part * KS / KSPLIT, s_hi = (part + 1) * KS / KSPLIT;
     float* Su = score + (size_t)unit * nb_cap;
-    auto tile_j0 = [&](int t) { return j_wg + (t * TILES_WG + tslot) * 16; };
+    // first block of tile t of this wave (nb or more: no such tile)
+    auto tile_j0 = [&](int t) {
+        return app_wg ? (t == 0 && tslot == 0 ? tail_j0 : nb) : j_wg + (t * TILES_WG + tslot) * 16;
+    };
     auto tile_row = [&](int t) {
         const int jl = tile_j0(t) + (lane & 15);
         const int jc = jl < nb ? jl : nb - 1;          // keep loads inside the unit's blocks
@@ -200,8 +212,8 @@ __global__ __launch_bounds__(256) void block_score_kernel(
         if (G > 4) {   // heads 4.. sit in the other 16-lane rows
             v = agg_sum ? sum_xor32(sum_xor16(v)) : max_xor32(max_xor16(v));
         }
-        const int jl = tile_j0(t) + (lane & 15);
-        if (lane < 16 && jl < nb) Su[jl] = v;
+        const int j0 = tile_j0(t), jl = j0 + (lane & 15);
+        if (lane < 16 && jl < nb && (app_wg || j0 != tail_j0)) Su[jl] = v;
     };
 
     if constexpr (KSPLIT > 1) {
@@ -253,7 +265,7 @@ hipError_t launch_t(const Shape& s, const uint16_t* q, uint16_t* meta, const int
     tpw = tpw < 1 ? 1 : (tpw > 8 ? 8 : tpw);
     if (KSPLIT > 1) tpw = SPLIT_TILES;
     const int per_wg = TILES_WG * tpw * 16;
-    dim3 grid((s.nb_cap + per_wg - 1) / per_wg, s.B * s.Hkv);
+    dim3 grid((s.nb_cap + per_wg - 1) / per_wg + (KSPLIT == 1 && ap.k_new ? 1 : 0), s.B * s.Hkv);
     hipLaunchKernelGGL((block_score_kernel<MT, KSW, KSPLIT, F8>), grid, dim3(64 * SCORE_WAVES), 0, st, q, meta,
                        ctx_len, score, s.Hkv, s.G, s.dk, s.bs, s.max_ctx, s.nb_cap, tpw, ap, sel_cnt, s.agg_sum);
     return hipGetLastError();
