@@ -9,8 +9,10 @@ append the new token, block scores over the full context, top-K_b, label
 scores over the kept blocks, top-K_t, exact attention and the split merge.
 Inputs are resident in HBM before timing starts. Steps rotate over several
 copies of the cache (distinct addresses, as consecutive layers would be) so
-the 256 MB Infinity Cache cannot serve a step from the previous one; each
-copy's step is captured once as a HIP graph and replayed.
+the 256 MB Infinity Cache cannot serve a step from the previous one. Steps
+are captured as HIP graphs of several consecutive steps each (as a model's
+decode graph holds all its layers) and replayed; the rate with one graph
+launch per step is reported beside it.
 
 Prints one JSON line.
 """
@@ -124,31 +126,46 @@ def stage(w, threads):
     return d, base, host
 
 
-def time_replays(fns, stream, warmup, steps, graphs=True):
-    """Average ms per call of fns[i % len(fns)] over `steps` calls, each
-    captured once as a HIP graph and replayed (after an eager warmup call of
-    every fn and `warmup` untimed calls)."""
+def graph_group(steps, cap=16):
+    """Steps per captured graph: the largest divisor of `steps` up to cap,
+    so that exactly `steps` steps are timed."""
+    return max(g for g in range(1, min(cap, steps) + 1) if steps % g == 0)
+
+
+def time_replays(fns, stream, warmup, steps, graphs=True, group=1):
+    """Average ms per call of fns[i % len(fns)] over `steps` calls (after an
+    eager warmup call of every fn and about `warmup` untimed calls). With
+    graphs, calls are captured as HIP graphs of `group` consecutive calls
+    each (len(fns) graphs, graph k holding calls k*group .. k*group+group-1,
+    so replaying them in turn continues the rotation over fns) and
+    steps / group graphs are replayed; group must divide steps."""
+    assert steps % group == 0
     with torch.cuda.stream(stream):
         for f in fns:
             f()
     torch.cuda.synchronize()
+    n = len(fns)
     gr = []
     if graphs:
-        for f in fns:
+        for k in range(n):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=stream):
-                f()
+                for j in range(group):
+                    fns[(k * group + j) % n]()
             gr.append(g)
         torch.cuda.synchronize()
-    call = (lambda i: gr[i % len(gr)].replay()) if graphs else (lambda i: fns[i % len(fns)]())
+        calls, call = steps // group, (lambda i: gr[i % n].replay())
+        wcalls = max(1, -(-warmup // group))
+    else:
+        calls, call, wcalls = steps, (lambda i: fns[i % n]()), warmup
     with torch.cuda.stream(stream):
-        for i in range(warmup):
+        for i in range(wcalls):
             call(i)
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     with torch.cuda.stream(stream):
         ev0.record(stream)
-        for i in range(steps):
+        for i in range(calls):
             call(i)
         ev1.record(stream)
     torch.cuda.synchronize()
@@ -199,7 +216,8 @@ def fp8_meta_leg(w, base, reps, stream, args, ms_step_bf16):
         r = reps[i]
         return lambda: H.decode_step(d8, base["q"], base["k_new"], base["v_new"], r.K, r.V, metas[i], r.klabel,
                                      base["label"], base["ctx"], r.blk, r.tok, r.out, r.lse, r.ws, stream=stream)
-    ms = time_replays([dec(i) for i in range(len(reps))], stream, args.warmup, args.steps, not args.no_graph)
+    ms = time_replays([dec(i) for i in range(len(reps))], stream, args.warmup, args.steps, not args.no_graph,
+                      graph_group(args.steps))
     us_score = time_score_launches(d8, base, metas, reps, stream, args.steps)
     kb = score_kernel_bytes(w8)
     ach = kb / (us_score * 1e-6) / 1e9
@@ -221,7 +239,8 @@ def variants_leg(w, base, reps, stream, args, ms_step):
     def dec(r):
         return lambda: H.decode_step(dv, base["q"], base["k_new"], base["v_new"], r.K, r.V, r.meta, r.klabel,
                                      base["label"], base["ctx"], r.blk, r.tok, r.out, r.lse, r.ws, stream=stream)
-    ms = time_replays([dec(r) for r in reps], stream, args.warmup, args.steps, not args.no_graph)
+    ms = time_replays([dec(r) for r in reps], stream, args.warmup, args.steps, not args.no_graph,
+                      graph_group(args.steps))
     S = 1024
     gen = torch.Generator(device="cuda").manual_seed(5)
     qs = torch.randn(S * w.n_q_heads * w.d_k, generator=gen, device="cuda").to(torch.bfloat16)
@@ -230,7 +249,7 @@ def variants_leg(w, base, reps, stream, args, ms_step):
     lab = torch.empty(w.n_kv_heads * w.r, dtype=torch.int32, device="cuda")
     d = dims_of(w)
     ms_cal = time_replays([lambda: H.calibrate_labels(d, qs, ks, S, imp, lab, stream=stream)], stream, 3, 20,
-                          not args.no_graph)
+                          not args.no_graph, graph_group(20))
     cal_bytes = S * (w.n_q_heads + w.n_kv_heads) * w.d_k * 2
     log(f"[bench] variants step {ms * 1e3:.1f} us; calibration {ms_cal * 1e3:.1f} us")
     return {"agg_sum_sink1_local2": {"ms_per_step": round(ms, 6), "vs_default_step": round(ms / ms_step, 3)},
@@ -577,8 +596,13 @@ def main():
         log(f"[bench] score-only: {args.score_only} launches, then a copy of {a.numel() * 4} bytes")
         return
 
-    ms_step = time_replays([(lambda r=r: decode(d, base, r, stream)) for r in reps], stream, args.warmup,
-                           args.steps, not args.no_graph)
+    # the timed loop replays graphs of `group` consecutive steps (the way a
+    # model captures the layers of one token step in one graph); one graph
+    # launch per step is timed too and reported beside it
+    group = graph_group(args.steps) if not args.no_graph else 1
+    step_fns = [(lambda r=r: decode(d, base, r, stream)) for r in reps]
+    ms_step = time_replays(step_fns, stream, args.warmup, args.steps, not args.no_graph, group)
+    ms_step_single = time_replays(step_fns, stream, args.warmup, args.steps, True, 1) if not args.no_graph else None
     log(f"[bench] {args.steps} steps: {ms_step * 1e3:.1f} us/step (events)")
 
     # dominant kernel alone: a graph of back-to-back block-score launches
@@ -637,8 +661,9 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "q_heads": w.n_q_heads, "kv_heads": w.n_kv_heads,
                    "d_k": w.d_k, "d_v": w.d_v, "ctx": w.ctx, "block": w.block, "k_blocks": w.k_blocks,
                    "r": w.r, "k_tokens": w.k_tokens, "meta": "fp8_e4m3_outward" if w.meta_fp8 else "bf16",
-                   "cache_replicas": R, "hip_graph": not args.no_graph,
+                   "cache_replicas": R, "hip_graph": not args.no_graph, "steps_per_graph": group,
                    "parallelism": "none (1 GPU)"},
+        "ms_per_step_one_graph_per_step": None if ms_step_single is None else round(ms_step_single, 6),
         "hbm_frac_step": round(sb["total"] / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "step_bytes": sb["total"],
         "roofline": {"kernel": "block_score", "bound": "hbm", "achieved": round(achieved, 1),
