@@ -48,6 +48,14 @@ attention mass rather than its most demanding head), and the first
 appended token) may be kept unconditionally, the remaining K_b - forced
 slots going to the best of the other blocks.
 
+Per-query-head selection (``decode_unit_heads``): the pages score blocks
+for the heads that share a KV head in one product and say nothing of
+combining them; Quest, which the pages build on, selects per query head.
+Reading taken here (opt-in): every query head of the group runs both
+selection stages on its own scores, exactly as a group of one head, and
+attends over its own tokens; the rows a KV head needs are then the union
+of its heads' token sets.
+
 Label-channel calibration (``calibrate_labels``): the fine stage scores
 tokens on a few important channels chosen offline (Double Sparsity)
 [gist.science/de, section 2.A "Stufe 2"; gist.science/es, section 2.A item
@@ -82,7 +90,7 @@ __all__ = [
     "quest_bound_gemm", "block_scores", "topk_stable", "candidate_tokens",
     "label_scores", "attend", "select_tokens_unit", "decode_unit", "select_blocks",
     "e4m3_grid", "e4m3_round", "block_meta_e4m3", "calibrate_labels",
-    "decode_all", "offload_delta", "offload_held", "offload_schedule", "offload_run",
+    "decode_unit_heads", "token_union", "decode_all", "offload_delta", "offload_held", "offload_schedule", "offload_run",
 ]
 
 
@@ -294,6 +302,34 @@ def decode_unit(q, K, V, n, bs, k_blocks, label_ch, k_tokens, sm_scale, meta=Non
     out, lse = attend(q, K[tok], V[tok], sm_scale)
     return {"blk_score": s_blk, "blk_idx": blk, "cand": cand, "tok_score": s_tok,
             "tok_idx": tok, "out": out, "lse": lse, "kmax": kmax, "kmin": kmin}
+
+
+def decode_unit_heads(q, K, V, n, bs, k_blocks, label_ch, k_tokens, sm_scale, meta=None, meta_fp8=False,
+                      sink=0, local=0):
+    """Per-query-head selection (a selection variant): query head h of the
+    group runs ``decode_unit`` on its own query as a group of one, so its
+    block and token scores are its own bounds and label scores. Returns
+    {"heads": [decode_unit result per head], "out" [G, d_v], "lse" [G],
+    "union": the ascending union of the heads' token sets, "mask": for each
+    union entry the bit set of the heads that selected it}."""
+    if meta is None:
+        meta = block_meta_e4m3(K, n, bs) if meta_fp8 else block_meta(K, n, bs)
+    heads = [decode_unit(q[h:h + 1], K, V, n, bs, k_blocks, label_ch, k_tokens, sm_scale, meta=meta,
+                         agg="max", sink=sink, local=local) for h in range(q.shape[0])]
+    union, mask = token_union([r["tok_idx"] for r in heads])
+    return {"heads": heads, "out": np.concatenate([r["out"] for r in heads]),
+            "lse": np.concatenate([r["lse"] for r in heads]), "union": union, "mask": mask}
+
+
+def token_union(token_sets):
+    """Ascending union of the heads' token sets and, per union entry, the
+    bit mask of the heads (bit h for set h) that hold it."""
+    union = np.unique(np.concatenate([np.asarray(s, np.int64) for s in token_sets])) if token_sets else \
+        np.zeros(0, np.int64)
+    mask = np.zeros(union.shape[0], np.int64)
+    for h, s in enumerate(token_sets):
+        mask |= np.isin(union, np.asarray(s)).astype(np.int64) << h
+    return union, mask
 
 
 def decode_all(q_bits, K_bits, V_bits, ctx_len, n_kv_heads, bs, k_blocks, label_ch,

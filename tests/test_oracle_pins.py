@@ -501,3 +501,69 @@ def test_calibration_recovers_outlier_channels():
     q = r_.standard_normal((256, 4, d))
     k = r_.standard_normal((256, d)) * scale
     np.testing.assert_array_equal(O.calibrate_labels(q, k, r), np.sort(hot))
+
+
+# ------------------------------------------------ per-query-head selection
+def test_per_head_selection_hand_example():
+    """Two heads that prefer different one-token blocks: with one block and
+    one token per head, each head keeps and attends its own token, while the
+    group maximum gives both heads the first one (hand-worked values)."""
+    q = np.array([[1.0, 0.0], [0.0, 1.0]])
+    K = np.array([[3.0, 0.0], [0.0, 3.0], [1.0, 1.0], [2.0, 2.0]])
+    V = np.array([[1.0, 0.0], [0.0, 1.0], [5.0, 5.0], [7.0, 7.0]])
+    r = O.decode_unit_heads(q, K, V, 4, 1, 1, np.array([0, 1]), 1, 0.5)
+    np.testing.assert_array_equal(r["heads"][0]["blk_score"], [3, 0, 1, 2])
+    np.testing.assert_array_equal(r["heads"][1]["blk_score"], [0, 3, 1, 2])
+    assert [list(h["tok_idx"]) for h in r["heads"]] == [[0], [1]]
+    np.testing.assert_array_equal(r["out"], [[1.0, 0.0], [0.0, 1.0]])
+    np.testing.assert_array_equal(r["lse"], [1.5, 1.5])
+    np.testing.assert_array_equal(r["union"], [0, 1])
+    np.testing.assert_array_equal(r["mask"], [1, 2])
+    g = O.decode_unit(q, K, V, 4, 1, 1, np.array([0, 1]), 1, 0.5)
+    np.testing.assert_array_equal(g["tok_idx"], [0])
+    np.testing.assert_array_equal(g["out"], [[1.0, 0.0], [1.0, 0.0]])
+
+
+def test_per_head_single_head_equals_group_mode():
+    q, K, V = _rand_unit(31, 1, 32, 90)
+    a = O.decode_unit_heads(q, K, V, 90, 8, 4, np.arange(0, 32, 4), 12, 0.2)
+    b = O.decode_unit(q, K, V, 90, 8, 4, np.arange(0, 32, 4), 12, 0.2)
+    np.testing.assert_array_equal(a["heads"][0]["blk_idx"], b["blk_idx"])
+    np.testing.assert_array_equal(a["union"], b["tok_idx"])
+    np.testing.assert_array_equal(a["out"], b["out"])
+    np.testing.assert_array_equal(a["mask"], np.ones(len(b["tok_idx"])))
+
+
+@pytest.mark.parametrize("G,n,kt", [(2, 40, 5), (4, 64, 9), (8, 33, 33)])
+def test_per_head_exact_limit_is_topk_of_each_heads_logits(G, n, kt):
+    """One-token blocks make the block bound the exact q_h.k, and a label set
+    of every channel makes the label score exact too: each head then keeps
+    the K_t keys of largest q_h.k (torch.topk on the logits, no ties in
+    continuous data) and attends over them (torch SDPA)."""
+    d = 16
+    q, K, V = _rand_unit(100 + G, G, d, n)
+    r = O.decode_unit_heads(q, K, V, n, 1, n, np.arange(d), kt, 0.3)
+    for h in range(G):
+        want = np.sort(torch.topk(torch.tensor(q[h] @ K.T), min(kt, n)).indices.numpy())
+        np.testing.assert_array_equal(r["heads"][h]["tok_idx"], want)
+        out, lse = _sdpa(q[h:h + 1], K[want], V[want], 0.3)
+        np.testing.assert_allclose(r["out"][h], out[0], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(r["lse"][h], lse[0], rtol=1e-13)
+
+
+def test_token_union_brute_force():
+    rng = np.random.default_rng(3)
+    for _ in range(50):
+        G = int(rng.integers(1, 9))
+        sets = [np.sort(rng.choice(60, size=int(rng.integers(0, 20)), replace=False)) for _ in range(G)]
+        u, m = O.token_union(sets)
+        assert list(u) == sorted(set().union(*[set(s.tolist()) for s in sets]))
+        for x, bits in zip(u, m):
+            assert all(((int(bits) >> h) & 1) == (int(x) in set(s.tolist())) for h, s in enumerate(sets))
+
+
+def test_per_head_forced_blocks_apply_to_every_head():
+    q, K, V = _rand_unit(77, 3, 16, 100)
+    r = O.decode_unit_heads(q, K, V, 100, 10, 4, np.arange(4), 20, 0.25, sink=1, local=1)
+    for h in r["heads"]:
+        assert 0 in h["blk_idx"] and 9 in h["blk_idx"] and len(h["blk_idx"]) == 4
