@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libhsab.so")
 SOURCES = ["api.hip", "meta.hip", "score.hip", "select.hip", "attend.hip", "offload.hip", "dense.hip",
-           "calib.hip"]
+           "calib.hip", "union.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

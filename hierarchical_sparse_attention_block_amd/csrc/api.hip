@@ -20,15 +20,19 @@ Shape make_shape(const hsab_dims& d) {
     s.nb_cap = d.block > 0 ? (d.max_ctx + d.block - 1) / d.block : 0;
     s.sm_scale = d.sm_scale;
     s.meta8 = d.meta_format == HSAB_META_FP8;
+    s.agg = d.group_agg;
     s.agg_sum = d.group_agg == HSAB_AGG_SUM;
+    s.heads = d.group_agg == HSAB_AGG_HEAD ? s.G : 1;
     s.sink = d.sink_blocks;
     s.local = d.local_blocks;
     return s;
 }
 
+int attn_list_len(const Shape& s) { return s.kt * s.heads; }
+
 int attn_splits(const Shape& s) {
     const int tps = s.valias ? MLA_TOK_PER_SPLIT : ATT_TOK_PER_SPLIT;
-    return (s.kt + tps - 1) / tps;
+    return (attn_list_len(s) + tps - 1) / tps;
 }
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -36,11 +40,15 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 WsLayout ws_layout(const Shape& s) {
     WsLayout w;
     size_t off = 0;
-    w.blk_score = off; off = align256(off + (size_t)s.B * s.Hkv * s.nb_cap * sizeof(float));
+    const size_t sels = (size_t)s.B * s.Hkv * s.heads;   // selections
+    w.blk_score = off; off = align256(off + sels * s.nb_cap * sizeof(float));
     w.part_ml = off;   off = align256(off + (size_t)s.B * s.Hq * attn_splits(s) * 2 * sizeof(float));
     w.part_acc = off;  off = align256(off + (size_t)s.B * s.Hq * attn_splits(s) * s.dv * sizeof(float));
-    w.sel_keys = off;  off = align256(off + (size_t)s.B * s.Hkv * s.kb * s.bs * sizeof(uint32_t));
-    w.sel_cnt = off;   off = align256(off + (size_t)s.B * s.Hkv * sizeof(int32_t));
+    w.sel_keys = off;  off = align256(off + sels * s.kb * s.bs * sizeof(uint32_t));
+    w.sel_cnt = off;   off = align256(off + sels * sizeof(int32_t));
+    const size_t ulen = s.agg == AGG_HEAD ? (size_t)s.B * s.Hkv * attn_list_len(s) : 0;
+    w.union_idx = off;  off = align256(off + ulen * sizeof(int32_t));
+    w.union_mask = off; off = align256(off + ulen * sizeof(uint32_t));
     w.total = off;
     return w;
 }
@@ -64,7 +72,8 @@ static int check_dims(const hsab_dims* d) {
     if (!isfinite(d->sm_scale)) return HSAB_EINVAL;
     if (d->meta_format != HSAB_META_BF16 && d->meta_format != HSAB_META_FP8) return HSAB_EINVAL;
     if (d->meta_format == HSAB_META_FP8 && d->d_k % 32 != 0) return HSAB_EINVAL;   // whole 64-byte row loads
-    if (d->group_agg != HSAB_AGG_MAX && d->group_agg != HSAB_AGG_SUM) return HSAB_EINVAL;
+    if (d->group_agg != HSAB_AGG_MAX && d->group_agg != HSAB_AGG_SUM && d->group_agg != HSAB_AGG_HEAD)
+        return HSAB_EINVAL;
     if (d->sink_blocks < 0 || d->local_blocks < 0 || d->sink_blocks + d->local_blocks > d->k_blocks)
         return HSAB_EINVAL;
     return HSAB_OK;
@@ -74,6 +83,26 @@ static int hip_status(hipError_t e) {
     if (e == hipSuccess) return HSAB_OK;
     g_last_hip = (int)e;
     return HSAB_EHIP;
+}
+
+// Attention over the kept tokens: with per-head selection the heads' lists
+// are merged into their union (with head masks) in the workspace first.
+static int attend_step(const Shape& s, const uint16_t* q, const uint16_t* K, const uint16_t* V,
+                       const int32_t* tok_idx, const int32_t* slot_of, int n_slots, char* w, const WsLayout& L,
+                       float* out, float* lse, hipStream_t stream) {
+    const int32_t* list = tok_idx;
+    const uint32_t* mask = nullptr;
+    if (s.agg == AGG_HEAD) {
+        int32_t* uidx = reinterpret_cast<int32_t*>(w + L.union_idx);
+        uint32_t* umask = reinterpret_cast<uint32_t*>(w + L.union_mask);
+        const int rc = hip_status(launch_union(s, tok_idx, uidx, umask, stream));
+        if (rc) return rc;
+        list = uidx;
+        mask = umask;
+    }
+    return hip_status(launch_attend(s, q, K, V, list, mask, attn_list_len(s), slot_of, n_slots,
+                                    reinterpret_cast<float*>(w + L.part_ml),
+                                    reinterpret_cast<float*>(w + L.part_acc), out, lse, stream));
 }
 
 }  // namespace hsab
@@ -165,9 +194,7 @@ int hsab_sparse_attend(const hsab_dims* dims, const uint16_t* q, const uint16_t*
     if (!ws || ws_bytes < L.total) return HSAB_EINVAL;
     if (!attend_supported(s)) return HSAB_EUNSUPPORTED;
     char* w = static_cast<char*>(ws);
-    return hip_status(launch_attend(s, q, K, s.valias ? K : V, tok_idx, slot_of, n_slots,
-                                    reinterpret_cast<float*>(w + L.part_ml),
-                                    reinterpret_cast<float*>(w + L.part_acc), out, lse, stream));
+    return attend_step(s, q, K, s.valias ? K : V, tok_idx, slot_of, n_slots, w, L, out, lse, stream);
 }
 
 int hsab_decode_step(const hsab_dims* dims, const uint16_t* q, const uint16_t* k_new,
@@ -197,9 +224,7 @@ int hsab_decode_step(const hsab_dims* dims, const uint16_t* q, const uint16_t* k
     rc = hip_status(launch_select(s, 3, q, scores, klabel, label_ch, ctx_len, blk_idx, tok_idx, nullptr,
                                   sel_keys, sel_cnt, stream));
     if (rc) return rc;
-    return hip_status(launch_attend(s, q, K, s.valias ? K : V, tok_idx, nullptr, 0,
-                                    reinterpret_cast<float*>(w + L.part_ml),
-                                    reinterpret_cast<float*>(w + L.part_acc), out, lse, stream));
+    return attend_step(s, q, K, s.valias ? K : V, tok_idx, nullptr, 0, w, L, out, lse, stream);
 }
 
 int hsab_calibrate_labels(const hsab_dims* dims, const uint16_t* q_samples, const uint16_t* k_samples,
@@ -280,7 +305,7 @@ int hsab_offload_create(const hsab_dims* dims, int32_t n_slots, int32_t copy_mod
     const Shape s = make_shape(*dims);
     if (n_slots < 2 * s.kb + 2) return HSAB_EINVAL;
     if (copy_mode != HSAB_OFFLOAD_COPY_KERNEL && copy_mode != HSAB_OFFLOAD_COPY_DMA) return HSAB_EINVAL;
-    if (!attend_supported(s)) return HSAB_EUNSUPPORTED;
+    if (!attend_supported(s) || s.agg == AGG_HEAD) return HSAB_EUNSUPPORTED;   // blocks move per KV head
     return hip_status(offload_create(s, n_slots, copy_mode, engine));
 }
 

@@ -41,10 +41,13 @@ __device__ __forceinline__ long row_of(int t, int unit, int bs, int max_ctx, int
     return ((long)unit * n_slots + slot) * slot_rows + (t - blk * bs);
 }
 
-template <int D, int G>
+// MASKED: the token list is the union of the heads' own token sets (per-head
+// selection) and tok_mask gives, per entry, the heads that attend it.
+template <int D, int G, bool MASKED>
 __global__ __launch_bounds__(256) void attend_gqa_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    const int32_t* __restrict__ tok_idx, const int32_t* __restrict__ slot_of, int n_slots,
+    const int32_t* __restrict__ tok_idx, const uint32_t* __restrict__ tok_mask,
+    const int32_t* __restrict__ slot_of, int n_slots,
     float* __restrict__ part_ml, float* __restrict__ part_acc, int Hkv, int bs, int kt,
     int max_ctx, int nb_cap, int n_splits, int units, float scale2, int slot_rows) {
     constexpr int LPT = D / 8;                         // lanes per token (8 channels each)
@@ -81,11 +84,14 @@ __global__ __launch_bounds__(256) void attend_gqa_kernel(
     long rows[IT];
     const int32_t* tl = tok_idx + (size_t)unit * kt;
     int tv[IT];
+    uint32_t mk[IT];   // heads that attend the entry
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
         const int ti = split * ATT_TOK_PER_SPLIT + wave * TPW + it * TPI + ts;
-        const int t = tl[ti < kt ? ti : kt - 1];
+        const int tc = ti < kt ? ti : kt - 1;
+        const int t = tl[tc];
         tv[it] = ti < kt ? t : -1;
+        mk[it] = MASKED ? tok_mask[(size_t)unit * kt + tc] : ~0u;
     }
     if (slot_of) {
         int sl[IT];
@@ -128,7 +134,7 @@ __global__ __launch_bounds__(256) void attend_gqa_kernel(
 #pragma unroll
             for (int e = 0; e < 8; ++e) p = fmaf(qf[h][e], kf[e], p);
             p = group_sum<LPT>(p);
-            z[it][h] = ok[it] ? p : -INFINITY;
+            z[it][h] = ok[it] && ((mk[it] >> h) & 1u) ? p : -INFINITY;
         }
     }
 
@@ -440,25 +446,30 @@ __global__ __launch_bounds__(256) void combine_kernel(
 
 template <int D, int G>
 hipError_t launch_gqa(const Shape& s, const uint16_t* q, const uint16_t* K, const uint16_t* V,
-                      const int32_t* tok_idx, const int32_t* slot_of, int n_slots, float* part_ml,
-                      float* part_acc, hipStream_t st) {
-    const int ns = attn_splits(s);
+                      const int32_t* tok_idx, const uint32_t* tok_mask, int list_len, int ns,
+                      const int32_t* slot_of, int n_slots, float* part_ml, float* part_acc, hipStream_t st) {
     const int units = s.B * s.Hkv;
-    hipLaunchKernelGGL((attend_gqa_kernel<D, G>), dim3(((units + 7) / 8) * 8 * ns), dim3(256), 0, st, q, K, V,
-                       tok_idx, slot_of, n_slots, part_ml, part_acc, s.Hkv, s.bs, s.kt, s.max_ctx, s.nb_cap, ns,
-                       units, s.sm_scale * LOG2E, 2 * s.bs);
+    const dim3 grid(((units + 7) / 8) * 8 * ns);
+    if (tok_mask)
+        hipLaunchKernelGGL((attend_gqa_kernel<D, G, true>), grid, dim3(256), 0, st, q, K, V, tok_idx, tok_mask,
+                           slot_of, n_slots, part_ml, part_acc, s.Hkv, s.bs, list_len, s.max_ctx, s.nb_cap, ns,
+                           units, s.sm_scale * LOG2E, 2 * s.bs);
+    else
+        hipLaunchKernelGGL((attend_gqa_kernel<D, G, false>), grid, dim3(256), 0, st, q, K, V, tok_idx, tok_mask,
+                           slot_of, n_slots, part_ml, part_acc, s.Hkv, s.bs, list_len, s.max_ctx, s.nb_cap, ns,
+                           units, s.sm_scale * LOG2E, 2 * s.bs);
     return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_gqa_d(const Shape& s, const uint16_t* q, const uint16_t* K, const uint16_t* V,
-                        const int32_t* tok_idx, const int32_t* slot_of, int n_slots, float* part_ml,
-                        float* part_acc, hipStream_t st) {
+                        const int32_t* tok_idx, const uint32_t* tok_mask, int list_len, int ns,
+                        const int32_t* slot_of, int n_slots, float* part_ml, float* part_acc, hipStream_t st) {
     switch (s.G) {
-        case 1: return launch_gqa<D, 1>(s, q, K, V, tok_idx, slot_of, n_slots, part_ml, part_acc, st);
-        case 2: return launch_gqa<D, 2>(s, q, K, V, tok_idx, slot_of, n_slots, part_ml, part_acc, st);
-        case 4: return launch_gqa<D, 4>(s, q, K, V, tok_idx, slot_of, n_slots, part_ml, part_acc, st);
-        case 8: return launch_gqa<D, 8>(s, q, K, V, tok_idx, slot_of, n_slots, part_ml, part_acc, st);
+        case 1: return launch_gqa<D, 1>(s, q, K, V, tok_idx, tok_mask, list_len, ns, slot_of, n_slots, part_ml, part_acc, st);
+        case 2: return launch_gqa<D, 2>(s, q, K, V, tok_idx, tok_mask, list_len, ns, slot_of, n_slots, part_ml, part_acc, st);
+        case 4: return launch_gqa<D, 4>(s, q, K, V, tok_idx, tok_mask, list_len, ns, slot_of, n_slots, part_ml, part_acc, st);
+        case 8: return launch_gqa<D, 8>(s, q, K, V, tok_idx, tok_mask, list_len, ns, slot_of, n_slots, part_ml, part_acc, st);
         default: return hipErrorInvalidValue;
     }
 }
@@ -477,17 +488,19 @@ hipError_t launch_combine(const Shape& s, const float* part_ml, const float* par
 }
 
 bool attend_supported(const Shape& s) {
-    if (mla_shape(s)) return true;
+    if (mla_shape(s)) return s.agg != AGG_HEAD;
     return !s.valias && s.dk == s.dv && (s.dk == 64 || s.dk == 128 || s.dk == 256) &&
            (s.G == 1 || s.G == 2 || s.G == 4 || s.G == 8);
 }
 
 hipError_t launch_attend(const Shape& s, const uint16_t* q, const uint16_t* K, const uint16_t* V,
-                         const int32_t* tok_idx, const int32_t* slot_of, int n_slots,
-                         float* part_ml, float* part_acc, float* out, float* lse, hipStream_t st) {
+                         const int32_t* tok_idx, const uint32_t* tok_mask, int list_len,
+                         const int32_t* slot_of, int n_slots, float* part_ml, float* part_acc, float* out,
+                         float* lse, hipStream_t st) {
     if (!attend_supported(s)) return hipErrorInvalidValue;
     if (slot_of && !s.valias) V = K + (size_t)s.bs * s.dk;   // value rows follow the key rows in a slot
-    const int ns = attn_splits(s);
+    const int tps = mla_shape(s) ? MLA_TOK_PER_SPLIT : ATT_TOK_PER_SPLIT;
+    const int ns = (list_len + tps - 1) / tps;
     hipError_t e = hipSuccess;
     if (mla_shape(s)) {
         const int units = s.B * s.Hkv;
@@ -506,9 +519,9 @@ hipError_t launch_attend(const Shape& s, const uint16_t* q, const uint16_t* K, c
         e = hipGetLastError();
     } else {
         switch (s.dk) {
-            case 64: e = launch_gqa_d<64>(s, q, K, V, tok_idx, slot_of, n_slots, part_ml, part_acc, st); break;
-            case 128: e = launch_gqa_d<128>(s, q, K, V, tok_idx, slot_of, n_slots, part_ml, part_acc, st); break;
-            case 256: e = launch_gqa_d<256>(s, q, K, V, tok_idx, slot_of, n_slots, part_ml, part_acc, st); break;
+            case 64: e = launch_gqa_d<64>(s, q, K, V, tok_idx, tok_mask, list_len, ns, slot_of, n_slots, part_ml, part_acc, st); break;
+            case 128: e = launch_gqa_d<128>(s, q, K, V, tok_idx, tok_mask, list_len, ns, slot_of, n_slots, part_ml, part_acc, st); break;
+            case 256: e = launch_gqa_d<256>(s, q, K, V, tok_idx, tok_mask, list_len, ns, slot_of, n_slots, part_ml, part_acc, st); break;
             default: return hipErrorInvalidValue;
         }
     }

@@ -16,46 +16,66 @@ constexpr int MAX_R = 128;           // label channels
 constexpr int ATT_TOK_PER_SPLIT = 64;    // tokens per attention workgroup (GQA path)
 constexpr int MLA_TOK_PER_SPLIT = 64;    // tokens per attention workgroup (MLA path)
 
+// group score modes (dims.group_agg)
+constexpr int AGG_MAX = HSAB_AGG_MAX;
+constexpr int AGG_SUM = HSAB_AGG_SUM;
+constexpr int AGG_HEAD = HSAB_AGG_HEAD;
+
 struct Shape {
     int B, Hq, Hkv, G, dk, dv, valias, bs, r, kb, kt, max_ctx, nb_cap;
     float sm_scale;
     int meta8;   // block metadata in fp8 e4m3 (outward rounded) instead of bf16
-    int agg_sum; // group scores summed over the query heads instead of their max
+    int agg;     // AGG_MAX, AGG_SUM or AGG_HEAD (every query head selects on its own)
+    int agg_sum; // agg == AGG_SUM
+    int heads;   // selections per unit: G with AGG_HEAD, else 1
     int sink, local;   // always-kept first / last blocks
 };
 
 Shape make_shape(const hsab_dims& d);
 int attn_splits(const Shape& s);
+// entries of a unit's attention token list: K_t, or G * K_t (the union of
+// the heads' token sets) with per-head selection
+int attn_list_len(const Shape& s);
 
 // workspace carve-up (byte offsets, 256-aligned)
 struct WsLayout {
-    size_t blk_score, part_ml, part_acc, sel_keys, sel_cnt, total;
+    size_t blk_score, part_ml, part_acc, sel_keys, sel_cnt, union_idx, union_mask, total;
 };
 WsLayout ws_layout(const Shape& s);
 
 hipError_t launch_build_meta(const Shape& s, const uint16_t* K, const int32_t* ctx_len,
                              const int32_t* label_ch, uint16_t* meta, uint16_t* klabel,
                              hipStream_t st);
-// Block scores; with k_new non-null the decode-step append runs first
-// (inside the workgroup that owns each unit's tail block). sel_cnt
-// (nullable): the per-unit arrival counters of a following split token
-// selection, set to zero here.
+// Block scores ([U][nb_cap], or [U][G][nb_cap] with per-head selection);
+// with k_new non-null the decode-step append runs first. sel_cnt
+// (nullable): the arrival counters ([U * heads]) of a following split
+// token selection, set to zero here.
 hipError_t launch_block_score(const Shape& s, const uint16_t* q, uint16_t* meta, const int32_t* ctx_len,
                               float* score, const uint16_t* k_new, const uint16_t* v_new, uint16_t* K,
                               uint16_t* V, uint16_t* klabel, const int32_t* label_ch, int32_t* sel_cnt,
                               hipStream_t st);
 // mode bit 1: select blocks from block scores; bit 2: score + select tokens.
 // With sel_keys and sel_cnt non-null (counters zero on entry, zero again on
-// exit) the token stage of each unit is spread over several workgroups.
+// exit) the token stage of each selection is spread over several
+// workgroups. Per-head selection runs U * G selections, each of one query
+// head (block lists [U][G][K_b], token lists [U][G][K_t]).
 hipError_t launch_select(const Shape& s, int mode, const uint16_t* q, const float* blk_score,
                          const uint16_t* klabel, const int32_t* label_ch, const int32_t* ctx_len,
                          int32_t* blk_idx, int32_t* tok_idx, float* tok_score, uint32_t* sel_keys,
                          int32_t* sel_cnt, hipStream_t st);
 bool attend_supported(const Shape& s);
+// Per-head selection: the ascending union of the G token lists of each
+// unit ([U][G][K_t] -> [U][G*K_t], -1 padded) and, per entry, the bit mask
+// of the heads that selected it.
+hipError_t launch_union(const Shape& s, const int32_t* tok_idx, int32_t* union_idx, uint32_t* union_mask,
+                        hipStream_t st);
 // Split attention over the kept tokens, then the merge of the partials.
+// tok_idx: [U][list_len]; tok_mask (nullable): per entry the query heads
+// of the group that attend it (all when null).
 hipError_t launch_attend(const Shape& s, const uint16_t* q, const uint16_t* K, const uint16_t* V,
-                         const int32_t* tok_idx, const int32_t* slot_of, int n_slots,
-                         float* part_ml, float* part_acc, float* out, float* lse, hipStream_t st);
+                         const int32_t* tok_idx, const uint32_t* tok_mask, int list_len,
+                         const int32_t* slot_of, int n_slots, float* part_ml, float* part_acc, float* out,
+                         float* lse, hipStream_t st);
 
 // Merge of per-split (max, sum, weighted values) partials into out / lse.
 hipError_t launch_combine(const Shape& s, const float* part_ml, const float* part_acc, float* out, float* lse,

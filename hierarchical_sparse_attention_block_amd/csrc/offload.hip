@@ -438,8 +438,8 @@ hipError_t offload_step(hsab_offload_engine* e, const uint16_t* q, const uint16_
         HSAB_TRY(hipEventRecord(tm[4], cs));
         HSAB_TRY(hipStreamWaitEvent(cs, e->ev_copy[(t - 1) & 1], 0));
         HSAB_TRY(hipEventRecord(tm[5], cs));
-        HSAB_TRY(launch_attend(s, q, cache, cache, tok_idx, slot_of, e->n_slots, part_ml, part_acc, out,
-                               lse, cs));
+        HSAB_TRY(launch_attend(s, q, cache, cache, tok_idx, nullptr, s.kt, slot_of, e->n_slots, part_ml, part_acc,
+                               out, lse, cs));
         HSAB_TRY(hipEventRecord(tm[1], cs));
     }
 
@@ -473,8 +473,8 @@ hipError_t offload_step(hsab_offload_engine* e, const uint16_t* q, const uint16_
         HSAB_TRY(hipEventRecord(tm[4], cs));
         HSAB_TRY(hipStreamWaitEvent(cs, e->ev_copy[1], 0));
         HSAB_TRY(hipEventRecord(tm[5], cs));
-        HSAB_TRY(launch_attend(s, q, cache, cache, tok_idx, slot_of, e->n_slots, part_ml, part_acc, out,
-                               lse, cs));
+        HSAB_TRY(launch_attend(s, q, cache, cache, tok_idx, nullptr, s.kt, slot_of, e->n_slots, part_ml, part_acc,
+                               out, lse, cs));
         HSAB_TRY(hipEventRecord(tm[1], cs));
     }
     for (int u = 0; u < U; ++u) tail_blocks(e->n_ctx[u / s.Hkv] + 1, e->jp[u / s.Hkv], s.bs, &e->tail[2 * u]);

@@ -7,7 +7,8 @@
 // one dense product, so query heads that share a KV head (GQA groups, MLA)
 // score all blocks in a single GEMM (AsyncTLS, gist.science/de explainer
 // section 2.A "Optimierung"; gist.science/es explainer section 2.A item 1).
-// The block score is the maximum of the bound over the group.
+// The block score is the maximum of the bound over the group (or the sum,
+// or, with per-head selection, every head's own bound).
 //
 // Mapping onto v_mfma_f32_16x16x32_bf16: A = [q+ | q-] (16 head rows per
 // tile, padded with zeros), B = metadata rows (16 blocks per tile), K = the
@@ -59,7 +60,7 @@ __global__ __launch_bounds__(256) void block_score_kernel(
     const uint16_t* __restrict__ q, uint16_t* __restrict__ meta,
     const int32_t* __restrict__ ctx_len, float* __restrict__ score,
     int Hkv, int G, int dk, int bs, int max_ctx, int nb_cap, int tiles_per_wave, Append ap,
-    int32_t* __restrict__ sel_cnt, int agg_sum) {
+    int32_t* __restrict__ sel_cnt, int agg) {
     __shared__ f32x4_t red[KSPLIT > 1 ? SPLIT_TILES * KSPLIT * MT * 64 : 1];
 
     const int unit = blockIdx.y, b = unit / Hkv, g = unit % Hkv;
@@ -79,8 +80,11 @@ __global__ __launch_bounds__(256) void block_score_kernel(
     constexpr bool SEP = KSPLIT == 1;
     const bool app_wg = SEP && ap.k_new && blockIdx.x == gridDim.x - 1;
     const int tail_j0 = SEP && ap.k_new ? ((nb - 1) & ~15) : -1;
-    if (sel_cnt && blockIdx.x == 0 && threadIdx.x == 0)   // arrival counter of the split token selection
-        __hip_atomic_store(&sel_cnt[unit], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // arrival counters of the split token selection: one per unit, or one
+    // per query head with per-head selection
+    const int heads = agg == AGG_HEAD ? G : 1;
+    if (sel_cnt && blockIdx.x == 0 && threadIdx.x < heads)
+        __hip_atomic_store(&sel_cnt[unit * heads + threadIdx.x], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (!app_wg && j_wg >= nb) return;
 
     if (app_wg || (!SEP && ap.k_new && nb - 1 < j_wg + per_wg)) {
@@ -114,7 +118,7 @@ __global__ __launch_bounds__(256) void block_score_kernel(
     const int part = KSPLIT > 1 ? wave : 0;              // step range of this wave
     const int tslot = KSPLIT > 1 ? 0 : wave;             // tile column of this wave
     const int s_lo = part * KS / KSPLIT, s_hi = (part + 1) * KS / KSPLIT;
-    float* Su = score + (size_t)unit * nb_cap;
+    float* Su = score + (size_t)unit * heads * nb_cap;
     // first block of tile t of this wave (nb or more: no such tile)
     auto tile_j0 = [&](int t) {
         return app_wg ? (t == 0 && tslot == 0 ? tail_j0 : nb) : j_wg + (t * TILES_WG + tslot) * 16;
@@ -201,8 +205,23 @@ __global__ __launch_bounds__(256) void block_score_kernel(
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) tot[mt] = acc[mt][0] + acc[mt][1];
     };
-    // group maximum (or sum) of the bound of tile t's blocks, stored
+    // group maximum (or sum) of the bound of tile t's blocks, stored; with
+    // per-head selection every head's bound is stored in its own row
     auto emit = [&](int t, const f32x4_t (&tot)[MT]) {
+        if (agg == AGG_HEAD) {
+            const int j0 = tile_j0(t), jl = j0 + (lane & 15);
+            if (jl < nb && (app_wg || j0 != tail_j0)) {
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int h = mt * 16 + (lane >> 4) * 4 + i;
+                        if (h < G) Su[(size_t)h * nb_cap + jl] = tot[mt][i];
+                    }
+            }
+            return;
+        }
+        const bool agg_sum = agg == AGG_SUM;
         float v = agg_sum ? 0.f : -INFINITY;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
@@ -267,7 +286,7 @@ hipError_t launch_t(const Shape& s, const uint16_t* q, uint16_t* meta, const int
     const int per_wg = TILES_WG * tpw * 16;
     dim3 grid((s.nb_cap + per_wg - 1) / per_wg + (KSPLIT == 1 && ap.k_new ? 1 : 0), s.B * s.Hkv);
     hipLaunchKernelGGL((block_score_kernel<MT, KSW, KSPLIT, F8>), grid, dim3(64 * SCORE_WAVES), 0, st, q, meta,
-                       ctx_len, score, s.Hkv, s.G, s.dk, s.bs, s.max_ctx, s.nb_cap, tpw, ap, sel_cnt, s.agg_sum);
+                       ctx_len, score, s.Hkv, s.G, s.dk, s.bs, s.max_ctx, s.nb_cap, tpw, ap, sel_cnt, s.agg);
     return hipGetLastError();
 }
 

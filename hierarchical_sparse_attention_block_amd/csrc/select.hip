@@ -4,6 +4,9 @@
 //   * label-channel scores of every valid token of the kept blocks, then
 //     top-K_t (fine stage, Double-Sparsity style; gist.science/de explainer
 //     section 2.A "Stufe 2", gist.science/es section 2.A item 2).
+// With per-head selection every query head is a selection of its own (a
+// group of one head: its own block scores, label scores and lists), run by
+// its own workgroups; the label rows are still those of its KV head.
 // Label score of token t: max over the group's query heads of
 // sum_c q_h[label_ch[c]] * klabel[t][c] on the matrix cores with 16
 // candidate tokens per tile and the group's label-channel queries as A.
@@ -40,8 +43,8 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
     const uint16_t* __restrict__ klabel, const int32_t* __restrict__ label_ch,
     const int32_t* __restrict__ ctx_len, int32_t* __restrict__ blk_idx, int32_t* __restrict__ tok_idx,
     float* __restrict__ tok_score, uint32_t* __restrict__ gkeys, int32_t* __restrict__ cnt, int parts,
-    int units, int Hkv, int G, int dk, int bs, int r, int kb, int kt, int max_ctx, int nb_cap, int bs_shift,
-    int agg_sum, int sink, int local) {
+    int units, int heads, int Hkv, int G, int dk, int bs, int r, int kb, int kt, int max_ctx, int nb_cap,
+    int bs_shift, int agg_sum, int sink, int local) {
     using Sel = TopK<SEL_WAVES, PT>;
     // candidate i sits in slot i / bs of the block list (a shift when bs is a power of two)
     auto slot_of = [&](int i) { return bs_shift >= 0 ? (i >> bs_shift) : i / bs; };
@@ -54,11 +57,15 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
     __shared__ typename Sel::Smem s_sel;
     __shared__ int s_last;
 
-    // the parts of a unit share an XCD (workgroup L runs on XCD L % 8)
+    // selection sel (of `units`) belongs to KV unit sel / heads and, with
+    // per-head selection (heads == G), to query head sel % heads of it; the
+    // parts of a selection share an XCD (workgroup L runs on XCD L % 8)
     const int xcd = blockIdx.x & 7, y = blockIdx.x >> 3;
-    const int unit = (y / parts) * 8 + xcd, part = y % parts;
-    if (unit >= units) return;
+    const int sel = (y / parts) * 8 + xcd, part = y % parts;
+    if (sel >= units) return;
+    const int unit = sel / heads, hsel = sel - unit * heads;
     const int b = unit / Hkv, g = unit % Hkv;
+    const int Ge = heads > 1 ? 1 : G;   // query heads scored together
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     // block scores are loaded over the whole capacity in the same round trip
     // as ctx_len and masked once n is known; the entry layout of the block
@@ -66,7 +73,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
     const int pt_b = (nb_cap + SEL_THREADS - 1) / SEL_THREADS;
     float sraw[PT];
     if (mode & 1) {
-        const float* S = blk_score + (size_t)unit * nb_cap;
+        const float* S = blk_score + (size_t)sel * nb_cap;
 #pragma unroll
         for (int j = 0; j < PT; ++j) {
             const int i = (w * pt_b + j) * 64 + lane;
@@ -76,10 +83,10 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
     int n = ctx_len[b];
     n = n < 1 ? 1 : (n > max_ctx ? max_ctx : n);
     const int nb = (n + bs - 1) / bs;
-    const uint16_t* qg = q + ((size_t)b * Hkv * G + (size_t)g * G) * dk;
+    const uint16_t* qg = q + ((size_t)unit * G + hsel) * dk;
 
     // label-channel A fragments (independent of the block selection)
-    const int MT = (G + 15) / 16;
+    const int MT = (Ge + 15) / 16;
     const int KSr = r / KK;               // matrix steps per label row
     constexpr int CPL = KK / 4;           // channels per lane per step
     constexpr int SMAX = MAX_R / KK;      // step stride of the fragment table
@@ -92,7 +99,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
             uint32_t x[CPL / 2];
 #pragma unroll
             for (int j = 0; j < CPL / 2; ++j) x[j] = 0u;
-            if (m < G) {
+            if (m < Ge) {
                 const uint16_t* qh = qg + (size_t)m * dk;
 #pragma unroll
                 for (int j = 0; j < CPL / 2; ++j)
@@ -119,7 +126,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
             const int i = (w * pt_b + j) * 64 + lane;
             bkey[j] = (j < pt_b && i < nb && i >= s1 && i < l0) ? f32_key(sraw[j]) : 0u;
         }
-        int32_t* bo = blk_idx + (size_t)unit * kb;
+        int32_t* bo = blk_idx + (size_t)sel * kb;
         const int keff = Sel::select(bkey, pt_b, kb - nforced, s_sel, [&](int pos, int i) {
             s_blk[s1 + pos] = i;
             if (part == 0) bo[s1 + pos] = i;
@@ -134,7 +141,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
             if (part == 0) bo[p] = -1;
         }
     } else {
-        for (int p = threadIdx.x; p < kb; p += SEL_THREADS) s_blk[p] = blk_idx[(size_t)unit * kb + p];
+        for (int p = threadIdx.x; p < kb; p += SEL_THREADS) s_blk[p] = blk_idx[(size_t)sel * kb + p];
     }
     if (!(mode & 2)) return;
     __syncthreads();   // s_blk, s_qa and the selector's scratch settled
@@ -142,7 +149,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
     // -------------------------------------------------- token label scores
     const int ncand = kb * bs;
     const uint16_t* Lu = klabel + (size_t)unit * max_ctx * r;
-    float* TS = tok_score ? tok_score + (size_t)unit * ncand : nullptr;
+    float* TS = tok_score ? tok_score + (size_t)sel * ncand : nullptr;
     const int n_tiles = (ncand + 15) / 16;
     const int t_lo = part * n_tiles / parts, t_hi = (part + 1) * n_tiles / parts;   // this part's tiles
     // eight label loads in flight per lane: load u feeds step u % KSr of
@@ -191,10 +198,10 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int h = (lane >> 4) * 4 + e;
-                    if (h < G) v = agg_sum ? v + acc0[e] : fmaxf(v, acc0[e]);
-                    if (16 + h < G) v = agg_sum ? v + acc1[e] : fmaxf(v, acc1[e]);
+                    if (h < Ge) v = agg_sum ? v + acc0[e] : fmaxf(v, acc0[e]);
+                    if (16 + h < Ge) v = agg_sum ? v + acc1[e] : fmaxf(v, acc1[e]);
                 }
-                if (G > 4) {   // heads 4.. sit in the other 16-lane rows
+                if (Ge > 4) {   // heads 4.. sit in the other 16-lane rows
                     v = agg_sum ? sum_xor32(sum_xor16(v)) : max_xor32(max_xor16(v));
                 }
                 const int i = tile * 16 + (lane & 15);
@@ -202,7 +209,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
                     const bool valid = (vmask >> u) & 1u;
                     const uint32_t kv = valid ? f32_key(v) : 0u;
                     if (parts > 1)
-                        __hip_atomic_store(&gkeys[(size_t)unit * ncand + i], kv, __ATOMIC_RELAXED,
+                        __hip_atomic_store(&gkeys[(size_t)sel * ncand + i], kv, __ATOMIC_RELAXED,
                                            __HIP_MEMORY_SCOPE_AGENT);
                     else
                         s_key[i] = kv;
@@ -216,7 +223,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
         __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
         __syncthreads();
         if (threadIdx.x == 0)
-            s_last = __hip_atomic_fetch_add(&cnt[unit], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == parts - 1;
+            s_last = __hip_atomic_fetch_add(&cnt[sel], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == parts - 1;
         __syncthreads();
         if (!s_last) return;
     } else {
@@ -231,20 +238,20 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
         const int i = (w * pt + j) * 64 + lane;
         const bool in = j < pt && i < ncand;
         if (parts > 1)
-            key[j] = in ? __hip_atomic_load(&gkeys[(size_t)unit * ncand + i], __ATOMIC_RELAXED,
+            key[j] = in ? __hip_atomic_load(&gkeys[(size_t)sel * ncand + i], __ATOMIC_RELAXED,
                                             __HIP_MEMORY_SCOPE_AGENT)
                         : 0u;
         else
             key[j] = in ? s_key[i] : 0u;
     }
-    int32_t* to = tok_idx + (size_t)unit * kt;
+    int32_t* to = tok_idx + (size_t)sel * kt;
     const int keff_t = Sel::select(key, pt, kt, s_sel, [&](int p, int i) {
         const int slot = slot_of(i);
         to[p] = s_blk[slot] * bs + (i - slot * bs);
     });
     for (int p = keff_t + threadIdx.x; p < kt; p += SEL_THREADS) to[p] = -1;
     if (parts > 1 && threadIdx.x == 0)   // ready for the next call
-        __hip_atomic_store(&cnt[unit], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&cnt[sel], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int PT>
@@ -253,8 +260,8 @@ hipError_t launch_t(const Shape& s, int mode, const uint16_t* q, const float* bl
                     int32_t* blk_idx, int32_t* tok_idx, float* tok_score, uint32_t* gkeys, int32_t* cnt,
                     hipStream_t st) {
     const int shift = (s.bs & (s.bs - 1)) ? -1 : __builtin_ctz(s.bs);
-    const int units = s.B * s.Hkv;
-    // parts per unit: enough workgroups to cover the CUs, at least eight
+    const int units = s.B * s.Hkv * s.heads;   // selections
+    // parts per selection: enough workgroups to cover the CUs, at least eight
     // candidate tiles (half a tile per wave) each
     int parts = 1;
     if ((mode & 2) && gkeys && cnt) {
@@ -264,11 +271,11 @@ hipError_t launch_t(const Shape& s, int mode, const uint16_t* q, const float* bl
     const dim3 grid(((units + 7) / 8) * 8 * parts);
     if (s.r >= 32)
         hipLaunchKernelGGL((select_kernel<PT, 32>), grid, dim3(SEL_THREADS), 0, st, mode, q, blk_score, klabel,
-                           label_ch, ctx_len, blk_idx, tok_idx, tok_score, gkeys, cnt, parts, units, s.Hkv, s.G,
+                           label_ch, ctx_len, blk_idx, tok_idx, tok_score, gkeys, cnt, parts, units, s.heads, s.Hkv, s.G,
                            s.dk, s.bs, s.r, s.kb, s.kt, s.max_ctx, s.nb_cap, shift, s.agg_sum, s.sink, s.local);
     else
         hipLaunchKernelGGL((select_kernel<PT, 16>), grid, dim3(SEL_THREADS), 0, st, mode, q, blk_score, klabel,
-                           label_ch, ctx_len, blk_idx, tok_idx, tok_score, gkeys, cnt, parts, units, s.Hkv, s.G,
+                           label_ch, ctx_len, blk_idx, tok_idx, tok_score, gkeys, cnt, parts, units, s.heads, s.Hkv, s.G,
                            s.dk, s.bs, s.r, s.kb, s.kt, s.max_ctx, s.nb_cap, shift, s.agg_sum, s.sink, s.local);
     return hipGetLastError();
 }

@@ -1,0 +1,101 @@
+// Union of the token sets of the query heads of one KV head, for
+// per-query-head selection: each head keeps its own tokens (Quest-style
+// selection per head, the mode the pages' one-product block scoring for
+// shared-KV heads leaves open), and the attention reads every row the
+// group needs once, masking per head.
+//
+// One 1024-thread workgroup per unit. The heads' lists are ascending token
+// positions (-1 padded); a window of positions gets one LDS bit set per
+// head (bit t of head h: head h kept token t), the words of the window are
+// OR-ed over the heads, counted and prefix-summed over the workgroup, and
+// every set bit becomes one union entry (its position, and the bits of the
+// heads that hold it as the mask). Windows cover max_ctx in turn, so the
+// union comes out ascending; the LDS per window is fixed (64 KiB).
+#include "common.h"
+#include "kernels.h"
+
+namespace hsab {
+
+namespace {
+
+constexpr int UNION_THREADS = 1024;
+constexpr int UNION_LDS_WORDS = 15360;   // 60 KiB of head bitmaps per window
+
+__global__ __launch_bounds__(UNION_THREADS) void union_kernel(const int32_t* __restrict__ tok_idx,
+                                                              int32_t* __restrict__ union_idx,
+                                                              uint32_t* __restrict__ union_mask, int G, int kt,
+                                                              int max_ctx, int wph) {
+    __shared__ uint32_t bits[UNION_LDS_WORDS];   // [G][wph]
+    __shared__ uint32_t s_wsum[UNION_THREADS / 64];
+    const int unit = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int E = G * kt;
+    const int32_t* L = tok_idx + (size_t)unit * E;
+    int32_t* U = union_idx + (size_t)unit * E;
+    uint32_t* M = union_mask + (size_t)unit * E;
+    const int span = wph * 32;                        // positions per window
+    const int per = (wph + UNION_THREADS - 1) / UNION_THREADS;   // words per thread
+    int base = 0;                                     // entries written so far
+    for (int w0 = 0; w0 < max_ctx; w0 += span) {
+        for (int i = tid; i < G * wph; i += UNION_THREADS) bits[i] = 0u;
+        __syncthreads();
+        for (int e = tid; e < E; e += UNION_THREADS) {
+            const int t = L[e];
+            if (t >= w0 && t < w0 + span && t < max_ctx) {
+                const int h = e / kt, o = t - w0;
+                atomicOr(&bits[h * wph + (o >> 5)], 1u << (o & 31));
+            }
+        }
+        __syncthreads();
+        // this thread's words: [k0, k1) of the window
+        const int k0 = tid * per, k1 = min(k0 + per, wph);
+        uint32_t cnt = 0;
+        for (int k = k0; k < k1; ++k) {
+            uint32_t u = 0;
+            for (int h = 0; h < G; ++h) u |= bits[h * wph + k];
+            cnt += __popc(u);
+        }
+        const uint32_t incl = wave_scan_dpp(cnt);
+        if (lane == 63) s_wsum[w] = incl;
+        __syncthreads();
+        uint32_t before = 0, total = 0;
+        for (int i = 0; i < UNION_THREADS / 64; ++i) {
+            const uint32_t x = s_wsum[i];
+            before += i < w ? x : 0u;
+            total += x;
+        }
+        int at = base + (int)(before + incl - cnt);
+        for (int k = k0; k < k1; ++k) {
+            uint32_t u = 0;
+            for (int h = 0; h < G; ++h) u |= bits[h * wph + k];
+            while (u) {
+                const int bit = __ffs(u) - 1;
+                u &= u - 1;
+                uint32_t m = 0;
+                for (int h = 0; h < G; ++h) m |= ((bits[h * wph + k] >> bit) & 1u) << h;
+                U[at] = w0 + k * 32 + bit;
+                M[at] = m;
+                ++at;
+            }
+        }
+        base += (int)total;
+        __syncthreads();   // the next window reuses bits and s_wsum
+    }
+    for (int e = base + tid; e < E; e += UNION_THREADS) {
+        U[e] = -1;
+        M[e] = 0u;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_union(const Shape& s, const int32_t* tok_idx, int32_t* union_idx, uint32_t* union_mask,
+                        hipStream_t st) {
+    const int words = (s.max_ctx + 31) / 32;
+    const int cap = UNION_LDS_WORDS / s.G;
+    const int wph = words < cap ? words : cap;
+    hipLaunchKernelGGL(union_kernel, dim3(s.B * s.Hkv), dim3(UNION_THREADS), 0, st, tok_idx, union_idx, union_mask,
+                       s.G, s.kt, s.max_ctx, wph);
+    return hipGetLastError();
+}
+
+}  // namespace hsab

@@ -52,6 +52,7 @@ class Dims(ctypes.Structure):
 
 META_BF16, META_FP8 = 0, 1   # block metadata formats (HSAB_META_BF16 / HSAB_META_FP8)
 AGG_MAX, AGG_SUM = 0, 1      # group score combination (HSAB_AGG_MAX / HSAB_AGG_SUM)
+AGG_HEAD = 2                 # per-query-head selection (HSAB_AGG_HEAD)
 
 
 def dims(batch, n_q_heads, n_kv_heads, d_k, d_v, v_alias_k, block, r, k_blocks, k_tokens, max_ctx,
@@ -183,13 +184,20 @@ def alloc_workspace(d: Dims, device="cuda") -> torch.Tensor:
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
+def selections(d: Dims) -> int:
+    """Selections per step: one per (batch, KV head), or one per (batch,
+    query head) with per-head selection (AGG_HEAD)."""
+    return d.batch * (d.n_q_heads if d.group_agg == AGG_HEAD else d.n_kv_heads)
+
+
 def _sizes(d: Dims):
     U = d.batch * d.n_kv_heads
+    S = selections(d)
     return {
         "q": d.batch * d.n_q_heads * d.d_k, "K": U * d.max_ctx * d.d_k, "V": U * d.max_ctx * d.d_v,
         "meta": U * d.nb_cap * 2 * d.d_k, "klabel": U * d.max_ctx * d.r, "label": d.n_kv_heads * d.r,
-        "ctx": d.batch, "blk": U * d.k_blocks, "tok": U * d.k_tokens, "score": U * d.nb_cap,
-        "tscore": U * d.k_blocks * d.block, "out": d.batch * d.n_q_heads * d.d_v,
+        "ctx": d.batch, "blk": S * d.k_blocks, "tok": S * d.k_tokens, "score": S * d.nb_cap,
+        "tscore": S * d.k_blocks * d.block, "out": d.batch * d.n_q_heads * d.d_v,
         "lse": d.batch * d.n_q_heads, "knew": U * d.d_k, "vnew": U * d.d_v,
     }
 

@@ -71,6 +71,7 @@ class Workload:
     agg_sum: bool = False    # group scores summed over the query heads (selection variant)
     sink_blocks: int = 0     # always-kept first blocks (selection variant)
     local_blocks: int = 0    # always-kept last blocks (selection variant)
+    per_head: bool = False   # every query head selects its own blocks and tokens (selection variant)
 
     @property
     def group(self) -> int:

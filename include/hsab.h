@@ -44,9 +44,10 @@
  *            label channels, klabel[..][t][c] = K[..][t][label_ch[g][c]].
  *   label_ch [Hkv][r]                             int32 channel indices.
  *   ctx_len  [B]                                  int32, 1 <= n <= max_ctx.
- *   blk_idx  [B][Hkv][K_b]                        int32 ascending, -1 padded.
+ *   blk_idx  [B][Hkv][K_b]                        int32 ascending, -1 padded
+ *            ([B][Hq][K_b] with per-head selection, HSAB_AGG_HEAD).
  *   tok_idx  [B][Hkv][K_t]                        int32 token positions,
- *            ascending, -1 padded.
+ *            ascending, -1 padded ([B][Hq][K_t] with HSAB_AGG_HEAD).
  *   out      [B][Hq][d_v]                         fp32 attention output.
  *   lse      [B][Hq]                              fp32 natural-log
  *            logsumexp of the logits sm_scale*q.k over the kept tokens.
@@ -55,7 +56,9 @@
  *
  * Selection rules (the pages leave them open; fixed here):
  *   - query heads sharing a KV head are combined by the maximum over the
- *     group, for block scores and token scores; one selection per unit;
+ *     group, for block scores and token scores; one selection per unit
+ *     (by default; dims.group_agg selects the sum, or one selection per
+ *     query head);
  *   - top-k ties go to the lower index; index lists are ascending;
  *   - K_b and K_t clamp to what exists; unused slots are -1.
  *
@@ -106,8 +109,8 @@ typedef struct hsab_dims {
     int32_t max_ctx;      /* cache capacity (tokens) per unit */
     float   sm_scale;     /* logit scale, typically 1/sqrt(d_k) */
     int32_t meta_format;  /* HSAB_META_BF16 (0) or HSAB_META_FP8 (1) */
-    int32_t group_agg;    /* HSAB_AGG_MAX (0) or HSAB_AGG_SUM (1): how the query heads of a
-                             group combine block and token scores */
+    int32_t group_agg;    /* HSAB_AGG_MAX (0), HSAB_AGG_SUM (1) or HSAB_AGG_HEAD (2): how the
+                             query heads of a group combine block and token scores */
     int32_t sink_blocks;  /* the first sink_blocks blocks are always kept */
     int32_t local_blocks; /* the last local_blocks blocks (newest) are always kept;
                              sink_blocks + local_blocks <= k_blocks */
@@ -122,6 +125,18 @@ typedef struct hsab_dims {
  * the block stage of hsab_decode_step and the offload engine apply them. */
 #define HSAB_AGG_MAX 0
 #define HSAB_AGG_SUM 1
+/* HSAB_AGG_HEAD: per-query-head selection (Quest, which the pages build on,
+ * selects per head; the pages do not say how heads that share a KV head
+ * combine). Every query head runs both stages on its own bound and label
+ * score, as a group of one: block scores are [B][Hq][nb_cap], blk_idx
+ * [B][Hq][K_b], tok_score [B][Hq][K_b*block], tok_idx [B][Hq][K_t], and
+ * head h attends over its own tokens. The attention reads each row of the
+ * union of a KV head's token sets once (hsab_sparse_attend and
+ * hsab_decode_step build that union in the workspace). The block metadata
+ * is read once per KV head: one product scores every head. Supported for
+ * the separate-V attention shapes (not the absorbed latent layout) and not
+ * by the offload engine (HSAB_EUNSUPPORTED). */
+#define HSAB_AGG_HEAD 2
 
 #define HSAB_META_BF16 0   /* block metadata in bf16 (exact key max/min) */
 #define HSAB_META_FP8  1   /* fp8 e4m3, max rounded up, min rounded down */
@@ -153,8 +168,10 @@ int hsab_build_meta(const hsab_dims* dims, const uint16_t* K, const int32_t* ctx
  * dense product; de 2.A "Optimierung"]:
  *   blk_score[b][g][j] = max_{h in group g} ( q_h+ . Kmax_j + q_h- . Kmin_j )
  * with q+ = max(q, 0), q- = min(q, 0), accumulated in fp32 on the matrix
- * cores. Writes j in [0, nb) of each unit; entries [nb, nb_cap) untouched.
- * blk_score: [B][Hkv][nb_cap] fp32. */
+ * cores (the sum over the group with HSAB_AGG_SUM). Writes j in [0, nb)
+ * of each unit; entries [nb, nb_cap) untouched.
+ * blk_score: [B][Hkv][nb_cap] fp32; with HSAB_AGG_HEAD [B][Hq][nb_cap],
+ * every head's own bound. */
 int hsab_score_blocks(const hsab_dims* dims, const uint16_t* q, const uint16_t* meta,
                       const int32_t* ctx_len, float* blk_score, hipStream_t stream);
 

@@ -32,8 +32,14 @@ def dims_of(w: W.Workload):
     from hierarchical_sparse_attention_block_amd import hsab as H
     return H.dims(w.batch, w.n_q_heads, w.n_kv_heads, w.d_k, w.d_v, w.v_alias_k, w.block, w.r,
                   w.k_blocks, w.k_tokens, w.max_ctx, w.sm_scale,
-                  H.META_FP8 if w.meta_fp8 else H.META_BF16, H.AGG_SUM if w.agg_sum else H.AGG_MAX,
+                  H.META_FP8 if w.meta_fp8 else H.META_BF16,
+                  H.AGG_HEAD if w.per_head else (H.AGG_SUM if w.agg_sum else H.AGG_MAX),
                   w.sink_blocks, w.local_blocks)
+
+
+def sel_heads(w: W.Workload) -> int:
+    """Selections per (batch, KV head): G with per-head selection, else 1."""
+    return w.group if w.per_head else 1
 
 
 def host_inputs(w: W.Workload, ctx_len=None, threads=8):
@@ -90,8 +96,9 @@ class Device:
         self.ctx_prefill = torch.from_numpy(h["ctx"] - 1).cuda()
         self.meta = H.alloc_meta(d)
         self.klabel = torch.zeros(U * w.max_ctx * w.r, dtype=torch.int16, device="cuda")
-        self.blk = torch.full((U * w.k_blocks,), -7, dtype=torch.int32, device="cuda")
-        self.tok = torch.full((U * w.k_tokens,), -7, dtype=torch.int32, device="cuda")
+        S = U * sel_heads(w)
+        self.blk = torch.full((S * w.k_blocks,), -7, dtype=torch.int32, device="cuda")
+        self.tok = torch.full((S * w.k_tokens,), -7, dtype=torch.int32, device="cuda")
         self.out = torch.full((w.batch * w.n_q_heads * w.d_v,), float("nan"), device="cuda")
         self.lse = torch.full((w.batch * w.n_q_heads,), float("nan"), device="cuda")
         self.ws = H.alloc_workspace(d)
@@ -107,9 +114,11 @@ class Device:
     def results(self):
         torch.cuda.synchronize()
         w = self.w
+        # [batch][KV head][K] lists, or [batch][query head][K] with per-head selection
+        sh = w.n_kv_heads * sel_heads(w)
         return {
-            "blk": self.blk.cpu().numpy().reshape(w.batch, w.n_kv_heads, w.k_blocks),
-            "tok": self.tok.cpu().numpy().reshape(w.batch, w.n_kv_heads, w.k_tokens),
+            "blk": self.blk.cpu().numpy().reshape(w.batch, sh, w.k_blocks),
+            "tok": self.tok.cpu().numpy().reshape(w.batch, sh, w.k_tokens),
             "out": self.out.cpu().numpy().reshape(w.batch, w.n_q_heads, w.d_v),
             "lse": self.lse.cpu().numpy().reshape(w.batch, w.n_q_heads),
         }
@@ -170,15 +179,20 @@ def check_block_set(s_blk, gpu_blk, k_blocks, sink, local, what=""):
     return np.sort(np.concatenate([np.array(forced, np.int64), others[got]])), tie
 
 
-def oracle_unit_vs_gpu(w, q_bits, K_bits, V_bits, ctx, label, b, g, gpu_blk, gpu_tok, gpu_out, gpu_lse):
+def oracle_unit_vs_gpu(w, q_bits, K_bits, V_bits, ctx, label, b, g, gpu_blk, gpu_tok, gpu_out, gpu_lse,
+                       head=None):
     """Check one unit against the oracle under the parity rules; stage two
-    and three of the oracle run on the GPU's accepted sets."""
+    and three of the oracle run on the GPU's accepted sets. head: with
+    per-head selection, the query head of the group whose own selection
+    (a group of one, as the oracle's decode_unit_heads defines it) and
+    output are checked; gpu_out / gpu_lse are then that head's rows."""
     G = w.group
     n = int(ctx[b])
-    q = O.bf16_to_f64(q_bits[b, g * G:(g + 1) * G])
+    heads = slice(g * G, (g + 1) * G) if head is None else slice(g * G + head, g * G + head + 1)
+    q = O.bf16_to_f64(q_bits[b, heads])
     K = O.bf16_to_f64(K_bits[b, g, :n])
     V = K[:, : w.d_v] if w.v_alias_k else O.bf16_to_f64(V_bits[b, g, :n])
-    agg = "sum" if w.agg_sum else "max"
+    agg = "sum" if w.agg_sum and head is None else "max"
     kmax, kmin = (O.block_meta_e4m3 if w.meta_fp8 else O.block_meta)(K, n, w.block)
     s_blk = O.block_scores(q, kmax, kmin, agg)
     blk, tie_b = check_block_set(s_blk, gpu_blk, w.k_blocks, w.sink_blocks, w.local_blocks,

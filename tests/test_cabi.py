@@ -46,13 +46,21 @@ def test_workspace_layout():
             + al(U * d.k_blocks * d.block * 4) + al(U * 4))
     assert H.workspace_bytes(d) == want
     assert H.workspace_bytes(_dims(n_q_heads=7)) == 0          # Hq % Hkv != 0
+    # per-head selection: one selection per query head, splits over the
+    # union of the heads' lists (G * K_t entries), the union and its masks
+    dh = _dims(group_agg=H.AGG_HEAD)
+    S, G = U * 4, 4
+    sh = -(-(G * 64) // 64)
+    want_h = (al(S * d.nb_cap * 4) + al(Hq * sh * 2 * 4) + al(Hq * sh * 128 * 4)
+              + al(S * d.k_blocks * d.block * 4) + al(S * 4) + 2 * al(U * G * 64 * 4))
+    assert H.workspace_bytes(dh) == want_h
 
 
 @pytest.mark.parametrize("bad", [
     dict(batch=0), dict(n_q_heads=7), dict(n_q_heads=128, n_kv_heads=2), dict(d_k=100), dict(d_k=2048),
     dict(d_v=12), dict(r=24), dict(r=256), dict(k_blocks=0), dict(k_blocks=4096), dict(k_blocks=1024, block=16),
     dict(k_tokens=0), dict(max_ctx=0), dict(max_ctx=16 * 8193), dict(v_alias_k=True, d_v=256, d_k=128),
-    dict(sm_scale=float("inf")), dict(meta_format=2), dict(meta_format=1, d_k=48), dict(group_agg=2),
+    dict(sm_scale=float("inf")), dict(meta_format=2), dict(meta_format=1, d_k=48), dict(group_agg=3),
     dict(sink_blocks=-1), dict(local_blocks=-1), dict(sink_blocks=5, local_blocks=4),
 ])
 def test_bad_dims_rejected(bad):

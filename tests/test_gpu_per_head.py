@@ -1,0 +1,184 @@
+"""Per-query-head selection (HSAB_AGG_HEAD) on the GPU against the oracle:
+every query head selects its own blocks and tokens as a group of one head
+(oracle.decode_unit_heads), and the attention reads the union of a KV
+head's token sets once, masking per head."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from hierarchical_sparse_attention_block_amd import workloads as W
+from tests import hsab_testlib as T
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def _wl(**kw):
+    base = dict(name="head", batch=2, n_q_heads=8, n_kv_heads=2, d_k=128, d_v=128, v_alias_k=False,
+                block=16, r=16, k_blocks=16, k_tokens=64, ctx=1000, max_ctx=1024, scaled_keys=True,
+                label_mode="top_scale", n_planted=4, seed=41, per_head=True)
+    base.update(kw)
+    return W.Workload(**base)
+
+
+def _decode(w, ctx2=None):
+    ctx = np.array([w.ctx, ctx2 or max(2, (w.ctx * 5) // 7)], np.int32)[: w.batch]
+    say(f"[per-head decode_step] {w}")
+    h = T.host_inputs(w, ctx_len=ctx)
+    dev = T.Device(w, h)
+    dev.prefill_meta()
+    dev.decode_step()
+    r = dev.results()
+    K, V = T.appended_cache(w, h)
+    G = w.group
+    differ = 0
+    for b in range(w.batch):
+        for g in range(w.n_kv_heads):
+            for hh in range(G):
+                a = g * G + hh
+                T.oracle_unit_vs_gpu(w, h["q"], K, V, h["ctx"], h["label"], b, g, r["blk"][b, a], r["tok"][b, a],
+                                     r["out"][b, a:a + 1], r["lse"][b, a:a + 1], head=hh)
+            lists = {tuple(r["tok"][b, g * G + hh]) for hh in range(G)}
+            differ += len(lists) > 1
+    return r, differ
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(n_q_heads=4, n_kv_heads=2, d_k=64, d_v=64),
+                                dict(n_q_heads=16, n_kv_heads=2, k_tokens=100),
+                                dict(n_q_heads=2, n_kv_heads=2, k_tokens=37),
+                                dict(n_q_heads=8, n_kv_heads=1, d_k=256, d_v=256, r=32, block=8, k_blocks=40,
+                                     k_tokens=150)])
+def test_per_head_decode(kw):
+    w = _wl(**kw)
+    _, differ = _decode(w)
+    if w.group > 1:
+        assert differ > 0, "the heads of every group selected identical token lists"
+
+
+def test_per_head_with_fp8_metadata_and_forced_blocks():
+    _decode(_wl(meta_fp8=True, sink_blocks=1, local_blocks=2, k_blocks=8))
+
+
+def test_per_head_budget_covers_everything():
+    """K_b and K_t beyond what exists: every head keeps every token, so each
+    head's output is full attention over the context."""
+    _decode(_wl(ctx=300, max_ctx=320, k_blocks=64, k_tokens=2000), ctx2=77)
+
+
+def test_per_head_block_scores_are_each_heads_bound():
+    w = _wl(max_ctx=1500, ctx=1500, n_planted=0)
+    ctx = np.array([1500, 1093], np.int32)
+    h = T.host_inputs(w, ctx_len=ctx)
+    dev = T.Device(w, h)
+    dev.prefill_meta()
+    d = dev.d
+    sc = torch.full((w.batch * w.n_q_heads * d.nb_cap,), float("nan"), device="cuda")
+    dev.H.score_blocks(d, dev.q, dev.meta, dev.ctx_prefill, sc)
+    sc = sc.cpu().numpy().reshape(w.batch, w.n_q_heads, d.nb_cap)
+    G = w.group
+    for b in range(w.batch):
+        n = int(ctx[b]) - 1
+        for g in range(w.n_kv_heads):
+            kmax, kmin = O.block_meta(O.bf16_to_f64(h["K"][b, g, :n]), n, w.block)
+            for hh in range(G):
+                q = O.bf16_to_f64(h["q"][b, g * G + hh:g * G + hh + 1])
+                want = O.block_scores(q, kmax, kmin)
+                err = np.abs(sc[b, g * G + hh, :len(want)] - want)
+                assert np.all(err <= T.score_tolerance(q, kmax, kmin)), f"({b},{g},{hh})"
+
+
+def test_per_head_stage_entry_points():
+    """hsab_select_blocks then hsab_select_tokens then hsab_sparse_attend,
+    each on per-head lists, against the oracle head by head."""
+    w = _wl(n_planted=2)
+    ctx = np.array([1000, 640], np.int32)
+    h = T.host_inputs(w, ctx_len=ctx)
+    dev = T.Device(w, h)
+    dev.prefill_meta()
+    d, H = dev.d, dev.H
+    H.select_blocks(d, dev.q, dev.meta, dev.ctx_prefill, dev.blk, ws=dev.ws)
+    H.select_tokens(d, dev.q, dev.klabel, dev.label, dev.blk, dev.ctx_prefill, dev.tok, ws=dev.ws)
+    H.sparse_attend(d, dev.q, dev.K, dev.V, dev.tok, dev.ctx_prefill, dev.out, dev.lse, dev.ws)
+    r = dev.results()
+    G = w.group
+    for b in range(w.batch):
+        for g in range(w.n_kv_heads):
+            for hh in range(G):
+                a = g * G + hh
+                T.oracle_unit_vs_gpu(w, h["q"], h["K"], h["V"], ctx - 1, h["label"], b, g, r["blk"][b, a],
+                                     r["tok"][b, a], r["out"][b, a:a + 1], r["lse"][b, a:a + 1], head=hh)
+
+
+@pytest.mark.parametrize("G,max_ctx,seed", [(4, 3000, 1), (8, 140000, 2), (2, 70000, 3), (1, 500, 4)])
+def test_per_head_attention_over_crafted_lists(G, max_ctx, seed):
+    """hsab_sparse_attend with given per-head lists: overlapping, identical,
+    disjoint and empty (all -1) lists, positions spread over several union
+    windows (G = 8 at 140k positions needs three), against the oracle's
+    attention over each head's own tokens."""
+    rng = np.random.default_rng(seed)
+    B, Hkv, d, kt = 2, 2, 64, 96
+    Hq = G * Hkv
+    say(f"[per-head crafted lists] G={G} max_ctx={max_ctx}")
+    q = W.f32_to_bf16_bits(rng.standard_normal((B, Hq, d)).astype(np.float32))
+    K = W.f32_to_bf16_bits(rng.standard_normal((B, Hkv, max_ctx, d)).astype(np.float32))
+    V = W.f32_to_bf16_bits(rng.standard_normal((B, Hkv, max_ctx, d)).astype(np.float32))
+    from hierarchical_sparse_attention_block_amd import hsab as H
+    dm = H.dims(B, Hq, Hkv, d, d, False, 32, 16, 8, kt, max_ctx, 1 / math.sqrt(d), group_agg=H.AGG_HEAD)
+    tok = np.full((B, Hq, kt), -1, np.int32)
+    shared = np.sort(rng.choice(max_ctx, kt, replace=False))
+    for b in range(B):
+        for a in range(Hq):
+            kind = (a + b) % 4
+            if kind == 0:
+                lst = shared
+            elif kind == 1:
+                lst = np.sort(rng.choice(max_ctx, int(rng.integers(1, kt + 1)), replace=False))
+            elif kind == 2:
+                lst = np.sort(np.concatenate([shared[: kt // 2],
+                                              rng.choice(np.setdiff1d(np.arange(max_ctx), shared), kt // 3,
+                                                         replace=False)]))
+            else:
+                lst = np.zeros(0, np.int64) if G > 1 else shared[:5]
+            tok[b, a, :len(lst)] = lst
+    out = torch.full((B * Hq * d,), float("nan"), device="cuda")
+    lse = torch.full((B * Hq,), float("nan"), device="cuda")
+    ws = H.alloc_workspace(dm)
+    H.sparse_attend(dm, T.dev16(q), T.dev16(K), T.dev16(V), torch.from_numpy(tok.ravel()).cuda(),
+                    torch.full((B,), max_ctx, dtype=torch.int32, device="cuda"), out, lse, ws)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy().reshape(B, Hq, d)
+    lse = lse.cpu().numpy().reshape(B, Hq)
+    for b in range(B):
+        for a in range(Hq):
+            g = a // G
+            lst = tok[b, a][tok[b, a] >= 0]
+            qa = O.bf16_to_f64(q[b, a:a + 1])
+            o, l = O.attend(qa, O.bf16_to_f64(K[b, g, lst]), O.bf16_to_f64(V[b, g, lst]), 1 / math.sqrt(d))
+            if len(lst) == 0:
+                assert np.all(out[b, a] == 0) and lse[b, a] == -np.inf, f"empty list ({b},{a})"
+                continue
+            assert np.max(np.abs(out[b, a] - o[0])) <= T.OUT_ATOL, f"({b},{a})"
+            np.testing.assert_allclose(lse[b, a], l[0], rtol=T.LSE_RTOL)
+
+
+def test_per_head_unsupported_shapes():
+    from hierarchical_sparse_attention_block_amd import hsab as H
+    w = _wl(n_q_heads=32, n_kv_heads=1, d_k=576, d_v=512, v_alias_k=True, block=32, r=32, k_blocks=8,
+            k_tokens=100, n_planted=0)
+    d = T.dims_of(w)
+    assert H.workspace_bytes(d) > 0
+    h = T.host_inputs(w, ctx_len=np.array([1000, 700], np.int32))
+    dev = T.Device(w, h)
+    with pytest.raises(H.HsabError) as e:
+        dev.decode_step()
+    assert e.value.status == H.HSAB_EUNSUPPORTED
+    d2 = T.dims_of(_wl())
+    with pytest.raises(H.HsabError) as e:
+        H.OffloadEngine(d2, 2 * d2.k_blocks + 2)
+    assert e.value.status == H.HSAB_EUNSUPPORTED
