@@ -48,8 +48,10 @@ def log(*a):
 
 
 def dims_of(w):
+    agg = H.AGG_HEAD if w.per_head else (H.AGG_SUM if w.agg_sum else H.AGG_MAX)
     return H.dims(w.batch, w.n_q_heads, w.n_kv_heads, w.d_k, w.d_v, w.v_alias_k, w.block, w.r,
-                  w.k_blocks, w.k_tokens, w.max_ctx, w.sm_scale, H.META_FP8 if w.meta_fp8 else H.META_BF16)
+                  w.k_blocks, w.k_tokens, w.max_ctx, w.sm_scale, H.META_FP8 if w.meta_fp8 else H.META_BF16,
+                  agg, w.sink_blocks, w.local_blocks)
 
 
 def meta_value_bytes(w):
@@ -252,9 +254,40 @@ def variants_leg(w, base, reps, stream, args, ms_step):
                           not args.no_graph, graph_group(20))
     cal_bytes = S * (w.n_q_heads + w.n_kv_heads) * w.d_k * 2
     log(f"[bench] variants step {ms * 1e3:.1f} us; calibration {ms_cal * 1e3:.1f} us")
-    return {"agg_sum_sink1_local2": {"ms_per_step": round(ms, 6), "vs_default_step": round(ms / ms_step, 3)},
-            "calibration": {"samples": S, "us_per_call": round(ms_cal * 1e3, 2), "bytes_read": cal_bytes,
-                            "achieved_gbs": round(cal_bytes / (ms_cal * 1e-3) / 1e9, 1)}}
+    res = {"agg_sum_sink1_local2": {"ms_per_step": round(ms, 6), "vs_default_step": round(ms / ms_step, 3)},
+           "calibration": {"samples": S, "us_per_call": round(ms_cal * 1e3, 2), "bytes_read": cal_bytes,
+                           "achieved_gbs": round(cal_bytes / (ms_cal * 1e-3) / 1e9, 1)}}
+    if not w.v_alias_k:
+        res["per_head"] = per_head_leg(w, base, reps, stream, args, ms_step)
+    return res
+
+
+def per_head_leg(w, base, reps, stream, args, ms_step):
+    """The same step with per-query-head selection (every head selects its
+    own blocks and tokens; the attention gathers the union of a KV head's
+    token sets once): step time, and how many rows the union holds per KV
+    head against K_t (one shared set) and G*K_t (every head gathering its
+    own rows)."""
+    wh = dataclasses.replace(w, per_head=True)
+    dh = dims_of(wh)
+    S = w.batch * w.n_q_heads
+    bufs = [{"blk": torch.empty(S * w.k_blocks, dtype=torch.int32, device="cuda"),
+             "tok": torch.empty(S * w.k_tokens, dtype=torch.int32, device="cuda"),
+             "ws": H.alloc_workspace(dh)} for _ in reps]
+
+    def dec(r, x):
+        return lambda: H.decode_step(dh, base["q"], base["k_new"], base["v_new"], r.K, r.V, r.meta, r.klabel,
+                                     base["label"], base["ctx"], x["blk"], x["tok"], r.out, r.lse, x["ws"],
+                                     stream=stream)
+    ms = time_replays([dec(r, x) for r, x in zip(reps, bufs)], stream, args.warmup, args.steps, not args.no_graph,
+                      graph_group(args.steps))
+    tok = bufs[0]["tok"].cpu().numpy().reshape(w.units, w.group, w.k_tokens)
+    union = [len(np.unique(u[u >= 0])) for u in tok]
+    log(f"[bench] per-head selection step {ms * 1e3:.1f} us, union {np.mean(union):.0f} rows per KV head")
+    return {"ms_per_step": round(ms, 6), "vs_default_step": round(ms / ms_step, 3),
+            "union_rows_per_kv_head": round(float(np.mean(union)), 1),
+            "union_vs_k_tokens": round(float(np.mean(union)) / w.k_tokens, 3),
+            "union_vs_heads_times_k_tokens": round(float(np.mean(union)) / (w.group * w.k_tokens), 3)}
 
 
 def decode(d, base, rep, stream):
