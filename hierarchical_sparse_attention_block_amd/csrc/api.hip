@@ -46,7 +46,7 @@ WsLayout ws_layout(const Shape& s) {
     w.part_acc = off;  off = align256(off + (size_t)s.B * s.Hq * attn_splits(s) * s.dv * sizeof(float));
     w.sel_keys = off;  off = align256(off + sels * s.kb * s.bs * sizeof(uint32_t));
     w.sel_cnt = off;   off = align256(off + sels * sizeof(int32_t));
-    const size_t ulen = s.agg == AGG_HEAD ? (size_t)s.B * s.Hkv * attn_list_len(s) : 0;
+    const size_t ulen = s.heads > 1 ? (size_t)s.B * s.Hkv * attn_list_len(s) : 0;
     w.union_idx = off;  off = align256(off + ulen * sizeof(int32_t));
     w.union_mask = off; off = align256(off + ulen * sizeof(uint32_t));
     w.total = off;
@@ -86,13 +86,14 @@ static int hip_status(hipError_t e) {
 }
 
 // Attention over the kept tokens: with per-head selection the heads' lists
-// are merged into their union (with head masks) in the workspace first.
+// are merged into their union (with head masks) in the workspace first
+// (with one head per group the list is already its own union).
 static int attend_step(const Shape& s, const uint16_t* q, const uint16_t* K, const uint16_t* V,
                        const int32_t* tok_idx, const int32_t* slot_of, int n_slots, char* w, const WsLayout& L,
                        float* out, float* lse, hipStream_t stream) {
     const int32_t* list = tok_idx;
     const uint32_t* mask = nullptr;
-    if (s.agg == AGG_HEAD) {
+    if (s.heads > 1) {
         int32_t* uidx = reinterpret_cast<int32_t*>(w + L.union_idx);
         uint32_t* umask = reinterpret_cast<uint32_t*>(w + L.union_mask);
         const int rc = hip_status(launch_union(s, tok_idx, uidx, umask, stream));

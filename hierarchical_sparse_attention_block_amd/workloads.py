@@ -17,6 +17,8 @@ context, see the AsyncTLS abstract and the German explainer, section 4):
   (outlier channels), label set = the r largest scales, 64 planted keys per
   (batch, KV head).
 * ``gqa96k``  - as gqa48k with B=16, n=98304, K_b=256, K_t=1024.
+* ``mha48k``  - as gqa48k with one query head per KV head: B=2, 32/32
+  heads (64 units and the same metadata bytes as gqa48k).
 * ``mla64k``  - B=8, 32 query heads sharing one 576-dim latent key
   (512 latent + 64 rope), values = first 512 key dims, n=65536, block 32,
   K_b=128, r=32, K_t=1024, scaled keys as above, no planted keys.
@@ -96,6 +98,8 @@ WORKLOADS = {
                        49152, 49152, True, "top_scale", 64, 2),
     "gqa96k": Workload("gqa96k", 16, 32, 8, 128, 128, False, 16, 16, 256, 1024,
                        98304, 98304, True, "top_scale", 64, 3),
+    "mha48k": Workload("mha48k", 2, 32, 32, 128, 128, False, 16, 16, 128, 512,
+                       49152, 49152, True, "top_scale", 64, 6),
     "mla64k": Workload("mla64k", 8, 32, 1, 576, 512, True, 32, 32, 128, 1024,
                        65536, 65536, True, "top_scale", 0, 4),
     # multi-step offload run; ctx is the capacity, per-row prefill lengths

@@ -54,6 +54,9 @@ def test_workspace_layout():
     want_h = (al(S * d.nb_cap * 4) + al(Hq * sh * 2 * 4) + al(Hq * sh * 128 * 4)
               + al(S * d.k_blocks * d.block * 4) + al(S * 4) + 2 * al(U * G * 64 * 4))
     assert H.workspace_bytes(dh) == want_h
+    # one head per group: per-head selection is the group mode, no union
+    assert H.workspace_bytes(_dims(n_q_heads=2, group_agg=H.AGG_HEAD)) == \
+        H.workspace_bytes(_dims(n_q_heads=2))
 
 
 @pytest.mark.parametrize("bad", [

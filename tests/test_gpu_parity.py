@@ -351,6 +351,22 @@ def test_gqa48k_full_size_sampled_units():
     say("gqa48k sampled", st)
 
 
+def test_mha48k_full_size_sampled_units():
+    """One query head per KV head (G = 1) at 48k in the benchmark's launch
+    configuration: structure and planted-key recall of every unit, three
+    sampled units against the oracle."""
+    w = W.WORKLOADS["mha48k"]
+    w, h, dev, r = _run_decode(w)
+    for b in range(w.batch):
+        for g in range(w.n_kv_heads):
+            pos, _ = W.planted_positions(w, b, g)
+            assert set(pos // w.block) <= set(r["blk"][b, g]), f"planted block missed in ({b},{g})"
+            assert set(pos) <= set(r["tok"][b, g]), f"planted token missed in ({b},{g})"
+    assert np.all(np.isfinite(r["out"])) and np.all(np.isfinite(r["lse"]))
+    st = _check_all_units(w, h, r, units=[(0, 0), (1, 17), (1, 31)])
+    say("mha48k sampled", st)
+
+
 # ------------------------------------------------------------------- MLA
 def _mla(**kw):
     base = dict(batch=2, n_q_heads=32, n_kv_heads=1, d_k=576, d_v=512, v_alias_k=True, block=32, r=32,
