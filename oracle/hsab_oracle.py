@@ -74,6 +74,15 @@ format's bit-field definition, to an independent fp8 decoder and to that
 bound invariant; against the pages themselves the scheme is a reading
 (parity unpinned: the pages print no quantised value).
 
+Quantised label rows (``e4m3_round_nearest``, ``label_fp8``): Double
+Sparsity keeps its label cache in a few bits, and the pages count
+quantisation among the ways to cut the indexing cost [gist.science/de,
+section 2.A "Stufe 2"]. Reading taken here (opt-in): label rows rounded to
+the nearest e4m3 value (ties to the even mantissa, saturating at +-448);
+the label score is an estimate, so no direction of rounding is needed.
+Pinned to an independent fp8 converter on every bf16 value up to the
+format's rounding limit; against the pages, parity unpinned.
+
 Offload (``offload_*``): the fine stage of step t runs over the blocks
 selected at step t-1 while step t's new blocks are fetched; only the set
 difference of consecutive block selections is transferred
@@ -89,7 +98,7 @@ __all__ = [
     "bf16_to_f64", "n_blocks", "block_meta", "append_meta", "quest_bound",
     "quest_bound_gemm", "block_scores", "topk_stable", "candidate_tokens",
     "label_scores", "attend", "select_tokens_unit", "decode_unit", "select_blocks",
-    "e4m3_grid", "e4m3_round", "block_meta_e4m3", "calibrate_labels",
+    "e4m3_grid", "e4m3_round", "e4m3_round_nearest", "block_meta_e4m3", "calibrate_labels",
     "decode_unit_heads", "token_union", "decode_all", "offload_delta", "offload_held", "offload_schedule", "offload_run",
 ]
 
@@ -171,6 +180,26 @@ def e4m3_round(x, up: bool) -> np.ndarray:
         return grid[np.minimum(i, grid.size - 1)]
     i = np.searchsorted(grid, x, side="right") - 1  # last grid value <= x
     return grid[np.maximum(i, 0)]
+
+
+def e4m3_round_nearest(x) -> np.ndarray:
+    """Rounding to the nearest e4m3 value; a value halfway between two grid
+    values goes to the one whose mantissa field is even; beyond the largest
+    magnitude the nearest finite value is +-448 (saturation)."""
+    codes, vals = e4m3_grid()
+    even = {}
+    for c, v in zip(codes, vals):
+        even[float(v)] = even.get(float(v), False) or (int(c) & 1) == 0
+    grid = np.unique(vals)
+    ev = np.array([even[float(v)] for v in grid])
+    x = np.asarray(x, np.float64)
+    hi = np.minimum(np.searchsorted(grid, x, side="left"), grid.size - 1)   # first grid value >= x (or the top)
+    lo = np.maximum(hi - 1, 0)
+    gl, gh = grid[lo], grid[hi]
+    dl, dh = np.abs(x - gl), np.abs(gh - x)
+    pick_hi = (dh < dl) | ((dh == dl) & ev[hi] & ~ev[lo])
+    out = np.where(pick_hi, gh, gl)
+    return np.where(x >= gh, gh, np.where(x <= grid[0], grid[0], out))
 
 
 def block_meta_e4m3(K: np.ndarray, n: int, bs: int):
@@ -286,10 +315,12 @@ def select_tokens_unit(q, K, n, bs, blk_idx, label_ch, k_tokens, agg="max"):
 
 
 def decode_unit(q, K, V, n, bs, k_blocks, label_ch, k_tokens, sm_scale, meta=None, meta_fp8=False,
-                agg="max", sink=0, local=0):
+                agg="max", sink=0, local=0, label_fp8=False):
     """One decode step of one unit over its first n tokens (the appended
     token included). q [G, d_k] float64; K [>=n, d_k], V [>=n, d_v] float64.
     meta_fp8: block metadata quantised outward to e4m3 (``block_meta_e4m3``);
+    label_fp8: label rows rounded to the nearest e4m3 value
+    (``e4m3_round_nearest``) before the label scores;
     agg, sink, local: the selection variants (group sum, forced blocks).
 
     Returns a dict with the intermediate results of every stage."""
@@ -298,14 +329,15 @@ def decode_unit(q, K, V, n, bs, k_blocks, label_ch, k_tokens, sm_scale, meta=Non
     kmax, kmin = meta
     s_blk = block_scores(q, kmax, kmin, agg)
     blk = select_blocks(s_blk, k_blocks, sink, local)
-    tok, cand, s_tok = select_tokens_unit(q, K, n, bs, blk, label_ch, k_tokens, agg)
+    Klab = e4m3_round_nearest(K) if label_fp8 else K
+    tok, cand, s_tok = select_tokens_unit(q, Klab, n, bs, blk, label_ch, k_tokens, agg)
     out, lse = attend(q, K[tok], V[tok], sm_scale)
     return {"blk_score": s_blk, "blk_idx": blk, "cand": cand, "tok_score": s_tok,
             "tok_idx": tok, "out": out, "lse": lse, "kmax": kmax, "kmin": kmin}
 
 
 def decode_unit_heads(q, K, V, n, bs, k_blocks, label_ch, k_tokens, sm_scale, meta=None, meta_fp8=False,
-                      sink=0, local=0):
+                      sink=0, local=0, label_fp8=False):
     """Per-query-head selection (a selection variant): query head h of the
     group runs ``decode_unit`` on its own query as a group of one, so its
     block and token scores are its own bounds and label scores. Returns
@@ -315,7 +347,7 @@ def decode_unit_heads(q, K, V, n, bs, k_blocks, label_ch, k_tokens, sm_scale, me
     if meta is None:
         meta = block_meta_e4m3(K, n, bs) if meta_fp8 else block_meta(K, n, bs)
     heads = [decode_unit(q[h:h + 1], K, V, n, bs, k_blocks, label_ch, k_tokens, sm_scale, meta=meta,
-                         agg="max", sink=sink, local=local) for h in range(q.shape[0])]
+                         agg="max", sink=sink, local=local, label_fp8=label_fp8) for h in range(q.shape[0])]
     union, mask = token_union([r["tok_idx"] for r in heads])
     return {"heads": heads, "out": np.concatenate([r["out"] for r in heads]),
             "lse": np.concatenate([r["lse"] for r in heads]), "union": union, "mask": mask}

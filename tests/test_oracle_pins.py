@@ -567,3 +567,51 @@ def test_per_head_forced_blocks_apply_to_every_head():
     r = O.decode_unit_heads(q, K, V, 100, 10, 4, np.arange(4), 20, 0.25, sink=1, local=1)
     for h in r["heads"]:
         assert 0 in h["blk_idx"] and 9 in h["blk_idx"] and len(h["blk_idx"]) == 4
+
+
+# ------------------------------------------------------ fp8 label rows
+def test_e4m3_nearest_matches_torch_on_every_bf16_value():
+    """Round-to-nearest-even onto e4m3 equals torch's float8_e4m3fn
+    conversion for every finite bf16 value up to 464 in magnitude (the
+    halfway point above 448, where torch stops rounding to the grid)."""
+    bits = np.arange(65536, dtype=np.uint32)
+    x = (bits << 16).view(np.float32)
+    x = x[np.isfinite(x) & (np.abs(x) <= 464)]
+    ours = O.e4m3_round_nearest(x.astype(np.float64))
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    np.testing.assert_array_equal(ours, ref)
+
+
+def test_e4m3_nearest_landmarks_and_saturation():
+    got = O.e4m3_round_nearest(np.array([0.0, 448.0, 450.0, 464.0, 465.0, 1e6, -1e6, 2.0 ** -9, 2.0 ** -10,
+                                         3 * 2.0 ** -10, 0.0625 + 0.00390625]))
+    # 2^-9 is the smallest subnormal; 2^-10 is halfway to 0 (tie to even: 0);
+    # 3*2^-10 is halfway between 2^-9 and 2^-8 (even mantissa: 2^-8);
+    # 0.0625 + 2^-8 is halfway between 0.0625 (m=0) and 0.0703125 (m=1): 0.0625
+    np.testing.assert_array_equal(got, [0.0, 448.0, 448.0, 448.0, 448.0, 448.0, -448.0, 2.0 ** -9, 0.0,
+                                        2.0 ** -8, 0.0625])
+
+
+def test_e4m3_nearest_error_within_half_spacing():
+    _, vals = O.e4m3_grid()
+    grid = np.unique(vals)
+    x = np.random.default_rng(0).uniform(-448, 448, 20000)
+    r = O.e4m3_round_nearest(x)
+    assert np.all(np.isin(r, grid))
+    i = np.searchsorted(grid, x)
+    gap = grid[np.minimum(i, grid.size - 1)] - grid[np.maximum(i - 1, 0)]
+    assert np.all(np.abs(r - x) <= gap / 2 + 1e-12)
+    np.testing.assert_array_equal(O.e4m3_round_nearest(grid), grid)
+
+
+def test_fp8_labels_change_only_the_token_stage():
+    """Quantised label rows leave the block stage and the attention rows
+    alone: the blocks equal the bf16 run's, and the tokens are the top-K_t
+    of the label scores recomputed on rounded rows."""
+    q, K, V = _rand_unit(55, 4, 32, 300)
+    a = O.decode_unit(q, K, V, 300, 16, 6, np.arange(0, 32, 2), 20, 0.2)
+    b = O.decode_unit(q, K, V, 300, 16, 6, np.arange(0, 32, 2), 20, 0.2, label_fp8=True)
+    np.testing.assert_array_equal(a["blk_idx"], b["blk_idx"])
+    want = O.label_scores(q, O.e4m3_round_nearest(K[b["cand"]]), np.arange(0, 32, 2))
+    np.testing.assert_array_equal(b["tok_score"], want)
+    np.testing.assert_array_equal(b["tok_idx"], b["cand"][O.topk_stable(want, 20)])
