@@ -51,7 +51,7 @@ def dims_of(w):
     agg = H.AGG_HEAD if w.per_head else (H.AGG_SUM if w.agg_sum else H.AGG_MAX)
     return H.dims(w.batch, w.n_q_heads, w.n_kv_heads, w.d_k, w.d_v, w.v_alias_k, w.block, w.r,
                   w.k_blocks, w.k_tokens, w.max_ctx, w.sm_scale, H.META_FP8 if w.meta_fp8 else H.META_BF16,
-                  agg, w.sink_blocks, w.local_blocks)
+                  agg, w.sink_blocks, w.local_blocks, H.LABEL_FP8 if w.label_fp8 else H.LABEL_BF16)
 
 
 def meta_value_bytes(w):
@@ -120,7 +120,7 @@ def stage(w, threads):
         "ctx": torch.full((w.batch,), w.ctx, dtype=torch.int32, device="cuda"),
         "ctx_prefill": torch.full((w.batch,), w.ctx - 1, dtype=torch.int32, device="cuda"),
         "meta": H.alloc_meta(d),
-        "klabel": torch.zeros(U * w.max_ctx * w.r, dtype=torch.int16, device="cuda"),
+        "klabel": H.alloc_klabel(d),
     }
     H.build_meta(d, base["K"], base["ctx_prefill"], base["label"], base["meta"], base["klabel"])
     torch.cuda.synchronize()

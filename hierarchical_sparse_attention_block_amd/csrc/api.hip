@@ -20,6 +20,7 @@ Shape make_shape(const hsab_dims& d) {
     s.nb_cap = d.block > 0 ? (d.max_ctx + d.block - 1) / d.block : 0;
     s.sm_scale = d.sm_scale;
     s.meta8 = d.meta_format == HSAB_META_FP8;
+    s.lab8 = d.label_format == HSAB_LABEL_FP8;
     s.agg = d.group_agg;
     s.agg_sum = d.group_agg == HSAB_AGG_SUM;
     s.heads = d.group_agg == HSAB_AGG_HEAD ? s.G : 1;
@@ -72,6 +73,7 @@ static int check_dims(const hsab_dims* d) {
     if (!isfinite(d->sm_scale)) return HSAB_EINVAL;
     if (d->meta_format != HSAB_META_BF16 && d->meta_format != HSAB_META_FP8) return HSAB_EINVAL;
     if (d->meta_format == HSAB_META_FP8 && d->d_k % 32 != 0) return HSAB_EINVAL;   // whole 64-byte row loads
+    if (d->label_format != HSAB_LABEL_BF16 && d->label_format != HSAB_LABEL_FP8) return HSAB_EINVAL;
     if (d->group_agg != HSAB_AGG_MAX && d->group_agg != HSAB_AGG_SUM && d->group_agg != HSAB_AGG_HEAD)
         return HSAB_EINVAL;
     if (d->sink_blocks < 0 || d->local_blocks < 0 || d->sink_blocks + d->local_blocks > d->k_blocks)

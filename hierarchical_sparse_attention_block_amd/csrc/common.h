@@ -48,6 +48,7 @@ __device__ __forceinline__ int clamp_ch(int c, int dk) { return c < 0 ? 0 : (c >
 
 __device__ __forceinline__ uint4 ldg16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ uint2 ldg8(const void* p) { return *reinterpret_cast<const uint2*>(p); }
+__device__ __forceinline__ uint32_t ldg4(const void* p) { return *reinterpret_cast<const uint32_t*>(p); }
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
@@ -170,6 +171,37 @@ __device__ __forceinline__ uint32_t f8_outward(uint32_t b, bool up) {
     if (inexact && (up != (sgn != 0u))) code = code + 1u > 0x7eu ? 0x7eu : code + 1u;
     return (sgn << 7) | code;
 }
+// bf16 value b (bit pattern) rounded to the nearest e4m3 value, a value
+// halfway between two codes going to the even code, saturating at +-448:
+// the magnitude's truncated code plus one when the dropped bits exceed half
+// a step (or equal it and the code is odd); codes are monotone in
+// magnitude, so a carry into the exponent field is the next value up.
+__device__ __forceinline__ uint32_t f8_nearest(uint32_t b) {
+    const uint32_t sgn = (b >> 15) & 1u, E = (b >> 7) & 0xffu, M = b & 0x7fu;
+    uint32_t code = 0, rem = 0, half = 1;
+    if (E != 0) {                       // bf16 zeros and subnormals round to zero
+        const int e = (int)E - 120;     // e4m3 exponent field (unbiased + 7)
+        if (e >= 1) {
+            code = ((uint32_t)e << 3) | (M >> 4);
+            rem = M & 0xfu;
+            half = 8u;
+        } else {                        // e4m3 subnormal range: |x| / 2^-9 = (128 + M) * 2^(e - 5)
+            const int sh = 5 - e;       // >= 5
+            const uint32_t F = 128u + M;
+            if (sh < 9) {
+                code = F >> sh;
+                rem = F & ((1u << sh) - 1u);
+                half = 1u << (sh - 1);
+            }                           // sh >= 9: below a quarter of the smallest step
+        }
+    }
+    if (code >= 0x7eu) {
+        code = 0x7eu;                   // 448 and beyond: saturate
+    } else if (rem > half || (rem == half && (code & 1u))) {
+        code += 1u;
+    }
+    return (sgn << 7) | (code > 0x7eu ? 0x7eu : code);
+}
 // value of an e4m3 code (finite codes only)
 __device__ __forceinline__ float f8_value(uint32_t code) {
     return __builtin_amdgcn_cvt_f32_fp8((int)code, 0);
@@ -179,6 +211,20 @@ __device__ __forceinline__ uint4 f8x8_bf16(uint2 w) {
     const f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8(w.x, false), b = __builtin_amdgcn_cvt_pk_f32_fp8(w.x, true);
     const f32x2_t c = __builtin_amdgcn_cvt_pk_f32_fp8(w.y, false), d = __builtin_amdgcn_cvt_pk_f32_fp8(w.y, true);
     return make_uint4(pk_bf16(a[0], a[1]), pk_bf16(b[0], b[1]), pk_bf16(c[0], c[1]), pk_bf16(d[0], d[1]));
+}
+
+// four e4m3 values (bytes of w, lowest first) as four bf16 (exact)
+__device__ __forceinline__ uint2 f8x4_bf16(uint32_t w) {
+    const f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8(w, false), b = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+    return make_uint2(pk_bf16(a[0], a[1]), pk_bf16(b[0], b[1]));
+}
+
+// Label row entry idx: bf16 bits, or (lab8) the nearest e4m3 byte.
+__device__ __forceinline__ void label_put(uint16_t* klabel, size_t idx, uint16_t kb, bool lab8) {
+    if (lab8)
+        reinterpret_cast<uint8_t*>(klabel)[idx] = (uint8_t)f8_nearest(kb);
+    else
+        klabel[idx] = kb;
 }
 
 // Metadata of block blk: its max row then its min row, d_k values each,

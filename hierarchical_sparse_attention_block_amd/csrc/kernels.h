@@ -25,6 +25,7 @@ struct Shape {
     int B, Hq, Hkv, G, dk, dv, valias, bs, r, kb, kt, max_ctx, nb_cap;
     float sm_scale;
     int meta8;   // block metadata in fp8 e4m3 (outward rounded) instead of bf16
+    int lab8;    // label rows in fp8 e4m3 (nearest) instead of bf16
     int agg;     // AGG_MAX, AGG_SUM or AGG_HEAD (every query head selects on its own)
     int agg_sum; // agg == AGG_SUM
     int heads;   // selections per unit: G with AGG_HEAD, else 1

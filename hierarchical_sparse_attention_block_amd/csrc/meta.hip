@@ -29,7 +29,7 @@ __device__ __forceinline__ uint4 vmin(uint4 a, uint4 b) { return {bmin2(a.x, b.x
 __global__ __launch_bounds__(256) void build_meta_kernel(
     const uint16_t* __restrict__ K, const int32_t* __restrict__ ctx_len,
     const int32_t* __restrict__ label_ch, uint16_t* __restrict__ meta, uint16_t* __restrict__ klabel,
-    int Hkv, int dk, int bs, int r, int max_ctx, int nb_cap, int meta8) {
+    int Hkv, int dk, int bs, int r, int max_ctx, int nb_cap, int meta8, int lab8) {
     const int unit = blockIdx.y, b = unit / Hkv, g = unit % Hkv;
     int n = ctx_len[b];
     n = n < 0 ? 0 : (n > max_ctx ? max_ctx : n);
@@ -68,11 +68,11 @@ __global__ __launch_bounds__(256) void build_meta_kernel(
         }
     }
     const int32_t* lab = label_ch + g * r;
-    uint16_t* Lu = klabel + (size_t)unit * max_ctx * r;
+    const size_t lu = (size_t)unit * max_ctx * r;
     const int tb = j0 * bs, te = min((j0 + META_BLOCKS_PER_WG) * bs, n);
     for (int p = threadIdx.x; p < (te - tb) * r; p += blockDim.x) {
         const int t = tb + p / r, c = p % r;
-        Lu[(size_t)t * r + c] = Ku[(size_t)t * dk + clamp_ch(lab[c], dk)];
+        label_put(klabel, lu + (size_t)t * r + c, Ku[(size_t)t * dk + clamp_ch(lab[c], dk)], lab8);
     }
 }
 
@@ -83,7 +83,7 @@ hipError_t launch_build_meta(const Shape& s, const uint16_t* K, const int32_t* c
                              hipStream_t st) {
     dim3 grid((s.nb_cap + META_BLOCKS_PER_WG - 1) / META_BLOCKS_PER_WG, s.B * s.Hkv);
     hipLaunchKernelGGL(build_meta_kernel, grid, dim3(256), 0, st, K, ctx_len, label_ch, meta, klabel,
-                       s.Hkv, s.dk, s.bs, s.r, s.max_ctx, s.nb_cap, s.meta8);
+                       s.Hkv, s.dk, s.bs, s.r, s.max_ctx, s.nb_cap, s.meta8, s.lab8);
     return hipGetLastError();
 }
 

@@ -31,7 +31,7 @@ __global__ __launch_bounds__(256) void append_slot_kernel(
     const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new, uint16_t* __restrict__ cache,
     uint16_t* __restrict__ meta, uint16_t* __restrict__ klabel, const int32_t* __restrict__ label_ch,
     const int32_t* __restrict__ ctx_len, int Hkv, int dk, int dv, int valias, int bs, int r, int max_ctx,
-    int nb_cap, int n_slots, int meta8) {
+    int nb_cap, int n_slots, int meta8, int lab8) {
     const int unit = blockIdx.x, b = unit / Hkv, g = unit % Hkv;
     const int pos = ctx_len[b] - 1;
     if (pos < 0 || pos >= max_ctx) return;
@@ -50,8 +50,9 @@ __global__ __launch_bounds__(256) void append_slot_kernel(
         const uint16_t* vn = v_new + (size_t)unit * dv;
         for (int c = threadIdx.x; c < dv; c += blockDim.x) slot[(size_t)bs * dk + (size_t)off * dv + c] = vn[c];
     }
-    uint16_t* Lrow = klabel + ((size_t)unit * max_ctx + pos) * r;
-    for (int c = threadIdx.x; c < r; c += blockDim.x) Lrow[c] = kn[clamp_ch(label_ch[g * r + c], dk)];
+    const size_t lrow = ((size_t)unit * max_ctx + pos) * r;
+    for (int c = threadIdx.x; c < r; c += blockDim.x)
+        label_put(klabel, lrow + c, kn[clamp_ch(label_ch[g * r + c], dk)], lab8);
 }
 
 // grid: (U). slot_of[unit][block] = slot for every (block, slot, copy) entry.
@@ -133,7 +134,7 @@ hipError_t launch_append_slot(const Shape& s, int n_slots, const uint16_t* k_new
                               const int32_t* ctx_len, hipStream_t st) {
     hipLaunchKernelGGL(append_slot_kernel, dim3(s.B * s.Hkv), dim3(256), 0, st, k_new, v_new, cache, meta, klabel,
                        label_ch, ctx_len, s.Hkv, s.dk, s.dv, s.valias, s.bs, s.r, s.max_ctx, s.nb_cap, n_slots,
-                       s.meta8);
+                       s.meta8, s.lab8);
     return hipGetLastError();
 }
 

@@ -49,6 +49,7 @@ struct Append {
     uint16_t* klabel;
     const int32_t* label_ch;
     int dv, r;
+    int lab8;                 // label rows in e4m3 bytes
 };
 
 // MT: 16-row head tiles (G <= 16 or <= 32); KSW: max row loads (16 bytes
@@ -103,9 +104,9 @@ __global__ __launch_bounds__(256) void block_score_kernel(
             uint16_t* Vrow = ap.V + ((size_t)unit * max_ctx + pos) * ap.dv;
             for (int c = threadIdx.x; c < ap.dv; c += blockDim.x) Vrow[c] = vn[c];
         }
-        uint16_t* Lrow = ap.klabel + ((size_t)unit * max_ctx + pos) * ap.r;
+        const size_t lrow = ((size_t)unit * max_ctx + pos) * ap.r;
         for (int c = threadIdx.x; c < ap.r; c += blockDim.x)
-            Lrow[c] = kn[clamp_ch(ap.label_ch[g * ap.r + c], dk)];
+            label_put(ap.klabel, lrow + c, kn[clamp_ch(ap.label_ch[g * ap.r + c], dk)], ap.lab8);
         __syncthreads();   // the tail block's new bounds are read below
     }
 
@@ -318,7 +319,7 @@ hipError_t launch_block_score(const Shape& s, const uint16_t* q, uint16_t* meta,
                               float* score, const uint16_t* k_new, const uint16_t* v_new, uint16_t* K,
                               uint16_t* V, uint16_t* klabel, const int32_t* label_ch, int32_t* sel_cnt,
                               hipStream_t st) {
-    const Append ap{k_new, v_new, K, s.valias ? nullptr : V, klabel, label_ch, s.dv, s.r};
+    const Append ap{k_new, v_new, K, s.valias ? nullptr : V, klabel, label_ch, s.dv, s.r, s.lab8};
     return s.G <= 16 ? launch_mt<1>(s, q, meta, ctx_len, score, ap, sel_cnt, st)
                      : launch_mt<2>(s, q, meta, ctx_len, score, ap, sel_cnt, st);
 }

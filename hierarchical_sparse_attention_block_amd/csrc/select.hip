@@ -36,8 +36,10 @@ namespace {
 constexpr int SEL_WAVES = 16;
 constexpr int SEL_THREADS = SEL_WAVES * 64;
 
-// KK: channels per matrix step (16, or 32 when r >= 32)
-template <int PT, int KK>
+// KK: channels per matrix step (16, or 32 when r >= 32); L8: label rows in
+// e4m3 bytes (half the bytes per load), widened exactly to bf16 at the
+// matrix step so the loads stay back to back
+template <int PT, int KK, bool L8>
 __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
     int mode, const uint16_t* __restrict__ q, const float* __restrict__ blk_score,
     const uint16_t* __restrict__ klabel, const int32_t* __restrict__ label_ch,
@@ -148,7 +150,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
 
     // -------------------------------------------------- token label scores
     const int ncand = kb * bs;
-    const uint16_t* Lu = klabel + (size_t)unit * max_ctx * r;
+    const size_t lu = (size_t)unit * max_ctx * r;   // first label entry of the unit
     float* TS = tok_score ? tok_score + (size_t)sel * ncand : nullptr;
     const int n_tiles = (ncand + 15) / 16;
     const int t_lo = part * n_tiles / parts, t_hi = (part + 1) * n_tiles / parts;   // this part's tiles
@@ -157,8 +159,9 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
     const int lg = KSr == 1 ? 0 : KSr == 2 ? 1 : KSr == 4 ? 2 : 3;
     const int tb = 8 >> lg;                         // tiles per batch
     using Frag = typename std::conditional<KK == 32, uint4, uint2>::type;
+    using Raw = typename std::conditional<L8, typename std::conditional<KK == 32, uint2, uint32_t>::type, Frag>::type;
     for (int t0 = t_lo + w; t0 < t_hi; t0 += SEL_WAVES * tb) {
-        Frag bf[8];
+        Raw bf[8];
         uint32_t vmask = 0;   // bit u: the token this lane loads for load u is valid
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
@@ -169,25 +172,40 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
             const int pos = blk * bs + off;
             const bool valid = blk >= 0 && blk < nb && pos < n;
             vmask |= (valid ? 1u : 0u) << u;
-            const uint16_t* src = Lu + (size_t)(valid ? pos : 0) * r + (lane >> 4) * CPL + st * KK;
-            if constexpr (KK == 32)
-                bf[u] = ldg16(src);
-            else
-                bf[u] = ldg8(src);
+            const size_t e = lu + (size_t)(valid ? pos : 0) * r + (lane >> 4) * CPL + st * KK;
+            if constexpr (L8) {
+                const uint8_t* src = reinterpret_cast<const uint8_t*>(klabel) + e;
+                if constexpr (KK == 32)
+                    bf[u] = ldg8(src);
+                else
+                    bf[u] = ldg4(src);
+            } else {
+                if constexpr (KK == 32)
+                    bf[u] = ldg16(klabel + e);
+                else
+                    bf[u] = ldg8(klabel + e);
+            }
         }
         f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             const int tile = t0 + (u >> lg) * SEL_WAVES, st = u & (KSr - 1);
             if (st == 0) acc0 = acc1 = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            Frag fr;
+            if constexpr (!L8)
+                fr = bf[u];
+            else if constexpr (KK == 32)
+                fr = f8x8_bf16(bf[u]);
+            else
+                fr = f8x4_bf16(bf[u]);
             if constexpr (KK == 32) {
-                const bf16x8_t bfrag = as_bf16x8(bf[u]);
+                const bf16x8_t bfrag = as_bf16x8(fr);
                 acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(s_qa4[st * 64 + lane]), bfrag, acc0, 0, 0, 0);
                 if (MT > 1)
                     acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(s_qa4[(SMAX + st) * 64 + lane]), bfrag,
                                                                    acc1, 0, 0, 0);
             } else {
-                const i16x4_t bfrag = as_i16x4(bf[u]);
+                const i16x4_t bfrag = as_i16x4(fr);
                 acc0 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_i16x4(s_qa[st * 64 + lane]), bfrag, acc0, 0, 0, 0);
                 if (MT > 1)
                     acc1 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_i16x4(s_qa[(SMAX + st) * 64 + lane]), bfrag,
@@ -254,6 +272,17 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
         __hip_atomic_store(&cnt[sel], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+template <int PT, int KK, bool L8>
+hipError_t launch_k(const Shape& s, dim3 grid, int mode, const uint16_t* q, const float* blk_score,
+                    const uint16_t* klabel, const int32_t* label_ch, const int32_t* ctx_len, int32_t* blk_idx,
+                    int32_t* tok_idx, float* tok_score, uint32_t* gkeys, int32_t* cnt, int parts, int units, int shift,
+                    hipStream_t st) {
+    hipLaunchKernelGGL((select_kernel<PT, KK, L8>), grid, dim3(SEL_THREADS), 0, st, mode, q, blk_score, klabel,
+                       label_ch, ctx_len, blk_idx, tok_idx, tok_score, gkeys, cnt, parts, units, s.heads, s.Hkv, s.G,
+                       s.dk, s.bs, s.r, s.kb, s.kt, s.max_ctx, s.nb_cap, shift, s.agg_sum, s.sink, s.local);
+    return hipGetLastError();
+}
+
 template <int PT>
 hipError_t launch_t(const Shape& s, int mode, const uint16_t* q, const float* blk_score,
                     const uint16_t* klabel, const int32_t* label_ch, const int32_t* ctx_len,
@@ -270,14 +299,14 @@ hipError_t launch_t(const Shape& s, int mode, const uint16_t* q, const float* bl
     }
     const dim3 grid(((units + 7) / 8) * 8 * parts);
     if (s.r >= 32)
-        hipLaunchKernelGGL((select_kernel<PT, 32>), grid, dim3(SEL_THREADS), 0, st, mode, q, blk_score, klabel,
-                           label_ch, ctx_len, blk_idx, tok_idx, tok_score, gkeys, cnt, parts, units, s.heads, s.Hkv, s.G,
-                           s.dk, s.bs, s.r, s.kb, s.kt, s.max_ctx, s.nb_cap, shift, s.agg_sum, s.sink, s.local);
-    else
-        hipLaunchKernelGGL((select_kernel<PT, 16>), grid, dim3(SEL_THREADS), 0, st, mode, q, blk_score, klabel,
-                           label_ch, ctx_len, blk_idx, tok_idx, tok_score, gkeys, cnt, parts, units, s.heads, s.Hkv, s.G,
-                           s.dk, s.bs, s.r, s.kb, s.kt, s.max_ctx, s.nb_cap, shift, s.agg_sum, s.sink, s.local);
-    return hipGetLastError();
+        return s.lab8 ? launch_k<PT, 32, true>(s, grid, mode, q, blk_score, klabel, label_ch, ctx_len, blk_idx, tok_idx,
+                                               tok_score, gkeys, cnt, parts, units, shift, st)
+                      : launch_k<PT, 32, false>(s, grid, mode, q, blk_score, klabel, label_ch, ctx_len, blk_idx,
+                                                tok_idx, tok_score, gkeys, cnt, parts, units, shift, st);
+    return s.lab8 ? launch_k<PT, 16, true>(s, grid, mode, q, blk_score, klabel, label_ch, ctx_len, blk_idx, tok_idx,
+                                           tok_score, gkeys, cnt, parts, units, shift, st)
+                  : launch_k<PT, 16, false>(s, grid, mode, q, blk_score, klabel, label_ch, ctx_len, blk_idx, tok_idx,
+                                            tok_score, gkeys, cnt, parts, units, shift, st);
 }
 
 }  // namespace

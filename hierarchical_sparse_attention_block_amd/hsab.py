@@ -36,7 +36,7 @@ class Dims(ctypes.Structure):
                 ("block", ctypes.c_int32), ("r", ctypes.c_int32), ("k_blocks", ctypes.c_int32),
                 ("k_tokens", ctypes.c_int32), ("max_ctx", ctypes.c_int32), ("sm_scale", ctypes.c_float),
                 ("meta_format", ctypes.c_int32), ("group_agg", ctypes.c_int32), ("sink_blocks", ctypes.c_int32),
-                ("local_blocks", ctypes.c_int32)]
+                ("local_blocks", ctypes.c_int32), ("label_format", ctypes.c_int32)]
 
     @property
     def group(self):
@@ -53,13 +53,15 @@ class Dims(ctypes.Structure):
 META_BF16, META_FP8 = 0, 1   # block metadata formats (HSAB_META_BF16 / HSAB_META_FP8)
 AGG_MAX, AGG_SUM = 0, 1      # group score combination (HSAB_AGG_MAX / HSAB_AGG_SUM)
 AGG_HEAD = 2                 # per-query-head selection (HSAB_AGG_HEAD)
+LABEL_BF16, LABEL_FP8 = 0, 1  # label row formats (HSAB_LABEL_BF16 / HSAB_LABEL_FP8)
 
 
 def dims(batch, n_q_heads, n_kv_heads, d_k, d_v, v_alias_k, block, r, k_blocks, k_tokens, max_ctx,
-         sm_scale, meta_format=META_BF16, group_agg=AGG_MAX, sink_blocks=0, local_blocks=0) -> Dims:
+         sm_scale, meta_format=META_BF16, group_agg=AGG_MAX, sink_blocks=0, local_blocks=0,
+         label_format=LABEL_BF16) -> Dims:
     return Dims(batch, n_q_heads, n_kv_heads, d_k, d_v, int(bool(v_alias_k)), block, r, k_blocks,
                 k_tokens, max_ctx, float(sm_scale), int(meta_format), int(group_agg), int(sink_blocks),
-                int(local_blocks))
+                int(local_blocks), int(label_format))
 
 
 _vp, _sz, _i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32
@@ -209,6 +211,18 @@ def _meta(d: Dims, meta):
     return _buf("meta", meta, torch.uint8 if d.meta_format == META_FP8 else _u16, n)
 
 
+def _klabel(d: Dims, klabel):
+    """Label rows: bf16 bits, or uint8 e4m3 bytes with fp8 label rows;
+    B*Hkv*max_ctx*r values either way."""
+    n = d.batch * d.n_kv_heads * d.max_ctx * d.r
+    return _buf("klabel", klabel, torch.uint8 if d.label_format == LABEL_FP8 else _u16, n)
+
+
+def alloc_klabel(d: Dims, device="cuda") -> torch.Tensor:
+    n = d.batch * d.n_kv_heads * d.max_ctx * d.r
+    return torch.zeros(n, dtype=torch.uint8 if d.label_format == LABEL_FP8 else torch.int16, device=device)
+
+
 def alloc_meta(d: Dims, device="cuda") -> torch.Tensor:
     n = d.batch * d.n_kv_heads * d.nb_cap * 2 * d.d_k
     return torch.zeros(n, dtype=torch.uint8 if d.meta_format == META_FP8 else torch.int16, device=device)
@@ -225,7 +239,7 @@ def build_meta(d: Dims, K, ctx_len, label_ch, meta, klabel, stream=None):
     _check("hsab_build_meta", _lib.hsab_build_meta(
         ctypes.byref(d), _buf("K", K, _u16, s["K"]), _buf("ctx_len", ctx_len, _i, s["ctx"]),
         _buf("label_ch", label_ch, _i, s["label"]), _meta(d, meta),
-        _buf("klabel", klabel, _u16, s["klabel"]), _stream(stream)))
+        _klabel(d, klabel), _stream(stream)))
 
 
 def score_blocks(d: Dims, q, meta, ctx_len, blk_score, stream=None):
@@ -253,7 +267,7 @@ def select_tokens(d: Dims, q, klabel, label_ch, blk_idx, ctx_len, tok_idx, tok_s
     s = _sizes(d)
     wp, wn = (None, 0) if ws is None else _ws(d, ws)
     _check("hsab_select_tokens", _lib.hsab_select_tokens(
-        ctypes.byref(d), _buf("q", q, _u16, s["q"]), _buf("klabel", klabel, _u16, s["klabel"]),
+        ctypes.byref(d), _buf("q", q, _u16, s["q"]), _klabel(d, klabel),
         _buf("label_ch", label_ch, _i, s["label"]), _buf("blk_idx", blk_idx, _i, s["blk"]),
         _buf("ctx_len", ctx_len, _i, s["ctx"]), _buf("tok_idx", tok_idx, _i, s["tok"]),
         _buf("tok_score", tok_score, _f, s["tscore"], allow_none=True), wp, wn, _stream(stream)))
@@ -286,7 +300,7 @@ def decode_step(d: Dims, q, k_new, v_new, K, V, meta, klabel, label_ch, ctx_len,
         ctypes.byref(d), _buf("q", q, _u16, s["q"]), _buf("k_new", k_new, _u16, s["knew"]),
         _buf("v_new", v_new, _u16, s["vnew"], allow_none=alias), _buf("K", K, _u16, s["K"]),
         _buf("V", V, _u16, s["V"], allow_none=alias), _meta(d, meta),
-        _buf("klabel", klabel, _u16, s["klabel"]), _buf("label_ch", label_ch, _i, s["label"]),
+        _klabel(d, klabel), _buf("label_ch", label_ch, _i, s["label"]),
         _buf("ctx_len", ctx_len, _i, s["ctx"]), _buf("blk_idx", blk_idx, _i, s["blk"]),
         _buf("tok_idx", tok_idx, _i, s["tok"]), _buf("out", out, _f, s["out"]),
         _buf("lse", lse, _f, s["lse"]), wp, wn, _stream(stream)))
@@ -305,7 +319,7 @@ def offload_append(d: Dims, n_slots, k_new, v_new, cache, meta, klabel, label_ch
         ctypes.byref(d), ctypes.c_int32(n_slots), _buf("k_new", k_new, _u16, s["knew"]),
         _buf("v_new", v_new, _u16, s["vnew"], allow_none=alias),
         _buf("cache", cache, _u16, U * n_slots * block_elems(d)), _meta(d, meta),
-        _buf("klabel", klabel, _u16, s["klabel"]), _buf("label_ch", label_ch, _i, s["label"]),
+        _klabel(d, klabel), _buf("label_ch", label_ch, _i, s["label"]),
         _buf("ctx_len", ctx_len, _i, s["ctx"]), _stream(stream)))
 
 
@@ -388,7 +402,7 @@ class OffloadEngine:
             _buf("v_new", v_new, _u16, s["vnew"], allow_none=bool(d.v_alias_k)),
             _hbuf("host_pool", host_pool, _u16, U * d.nb_cap * block_elems(d), pinned=True),
             _buf("cache", cache, _u16, U * self.n_slots * block_elems(d)), _meta(d, meta),
-            _buf("klabel", klabel, _u16, s["klabel"]), _buf("label_ch", label_ch, _i, s["label"]),
+            _klabel(d, klabel), _buf("label_ch", label_ch, _i, s["label"]),
             _buf("ctx_len", ctx_len, _i, s["ctx"]), _hbuf("ctx_len_host", ctx_len_host, _i, d.batch),
             _buf("slot_of", slot_of, _i, U * d.nb_cap), _buf("tok_idx", tok_idx, _i, s["tok"]),
             _buf("out", out, _f, s["out"]), _buf("lse", lse, _f, s["lse"]), wp, wn, _stream(compute_stream),

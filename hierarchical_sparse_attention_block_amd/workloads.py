@@ -74,6 +74,7 @@ class Workload:
     sink_blocks: int = 0     # always-kept first blocks (selection variant)
     local_blocks: int = 0    # always-kept last blocks (selection variant)
     per_head: bool = False   # every query head selects its own blocks and tokens (selection variant)
+    label_fp8: bool = False  # label rows rounded to the nearest fp8 e4m3 value instead of bf16
 
     @property
     def group(self) -> int:

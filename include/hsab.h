@@ -41,7 +41,11 @@
  *            quantisation as a way to cut the indexing cost without giving
  *            a scheme; outward rounding is this library's reading.
  *   klabel   [B][Hkv][max_ctx][r]                 bf16: K restricted to the
- *            label channels, klabel[..][t][c] = K[..][t][label_ch[g][c]].
+ *            label channels, klabel[..][t][c] = K[..][t][label_ch[g][c]];
+ *            with dims.label_format == HSAB_LABEL_FP8 one byte per value,
+ *            that key value rounded to the nearest fp8 e4m3 value (ties to
+ *            the even mantissa, saturating at +-448); the pointer type stays
+ *            uint16_t* and the array then holds B*Hkv*max_ctx*r bytes.
  *   label_ch [Hkv][r]                             int32 channel indices.
  *   ctx_len  [B]                                  int32, 1 <= n <= max_ctx.
  *   blk_idx  [B][Hkv][K_b]                        int32 ascending, -1 padded
@@ -114,6 +118,8 @@ typedef struct hsab_dims {
     int32_t sink_blocks;  /* the first sink_blocks blocks are always kept */
     int32_t local_blocks; /* the last local_blocks blocks (newest) are always kept;
                              sink_blocks + local_blocks <= k_blocks */
+    int32_t label_format; /* HSAB_LABEL_BF16 (0) or HSAB_LABEL_FP8 (1): label rows in bf16 or
+                             in nearest-rounded fp8 e4m3 */
 } hsab_dims;
 
 /* Selection variants (opt-in; zero-initialised dims select the default).
@@ -140,6 +146,15 @@ typedef struct hsab_dims {
 
 #define HSAB_META_BF16 0   /* block metadata in bf16 (exact key max/min) */
 #define HSAB_META_FP8  1   /* fp8 e4m3, max rounded up, min rounded down */
+
+/* Label rows (the fine stage's compressed keys): Double Sparsity keeps its
+ * label cache in few bits and the pages name quantisation of the index data
+ * (gist.science/de explainer, section 2.A "Stufe 2"). With HSAB_LABEL_FP8
+ * the rows are e4m3 bytes rounded to nearest (the label score is an
+ * estimate, so no rounding direction is needed); queries stay bf16 and the
+ * label products are exact in fp32. */
+#define HSAB_LABEL_BF16 0
+#define HSAB_LABEL_FP8  1
 
 /* Bytes of device workspace the calls below need for these dims (the same
  * size serves every call). The workspace holds block scores, token scores,

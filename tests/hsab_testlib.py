@@ -34,7 +34,7 @@ def dims_of(w: W.Workload):
                   w.k_blocks, w.k_tokens, w.max_ctx, w.sm_scale,
                   H.META_FP8 if w.meta_fp8 else H.META_BF16,
                   H.AGG_HEAD if w.per_head else (H.AGG_SUM if w.agg_sum else H.AGG_MAX),
-                  w.sink_blocks, w.local_blocks)
+                  w.sink_blocks, w.local_blocks, H.LABEL_FP8 if w.label_fp8 else H.LABEL_BF16)
 
 
 def sel_heads(w: W.Workload) -> int:
@@ -95,7 +95,7 @@ class Device:
         self.ctx = torch.from_numpy(h["ctx"]).cuda()
         self.ctx_prefill = torch.from_numpy(h["ctx"] - 1).cuda()
         self.meta = H.alloc_meta(d)
-        self.klabel = torch.zeros(U * w.max_ctx * w.r, dtype=torch.int16, device="cuda")
+        self.klabel = H.alloc_klabel(d)
         S = U * sel_heads(w)
         self.blk = torch.full((S * w.k_blocks,), -7, dtype=torch.int32, device="cuda")
         self.tok = torch.full((S * w.k_tokens,), -7, dtype=torch.int32, device="cuda")
@@ -198,7 +198,8 @@ def oracle_unit_vs_gpu(w, q_bits, K_bits, V_bits, ctx, label, b, g, gpu_blk, gpu
     blk, tie_b = check_block_set(s_blk, gpu_blk, w.k_blocks, w.sink_blocks, w.local_blocks,
                                  f"blocks of unit ({b},{g})")
     cand = O.candidate_tokens(blk, n, w.block)
-    s_tok = O.label_scores(q, K[cand], label[g], agg)
+    Klab = O.e4m3_round_nearest(K[cand]) if w.label_fp8 else K[cand]   # label rows as stored
+    s_tok = O.label_scores(q, Klab, label[g], agg)
     # the GPU reports positions; map them to candidate indices
     k_eff = min(w.k_tokens, len(cand))
     pos = np.asarray(gpu_tok[:k_eff])

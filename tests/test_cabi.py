@@ -63,7 +63,7 @@ def test_workspace_layout():
     dict(batch=0), dict(n_q_heads=7), dict(n_q_heads=128, n_kv_heads=2), dict(d_k=100), dict(d_k=2048),
     dict(d_v=12), dict(r=24), dict(r=256), dict(k_blocks=0), dict(k_blocks=4096), dict(k_blocks=1024, block=16),
     dict(k_tokens=0), dict(max_ctx=0), dict(max_ctx=16 * 8193), dict(v_alias_k=True, d_v=256, d_k=128),
-    dict(sm_scale=float("inf")), dict(meta_format=2), dict(meta_format=1, d_k=48), dict(group_agg=3),
+    dict(sm_scale=float("inf")), dict(meta_format=2), dict(meta_format=1, d_k=48), dict(group_agg=3), dict(label_format=2),
     dict(sink_blocks=-1), dict(local_blocks=-1), dict(sink_blocks=5, local_blocks=4),
 ])
 def test_bad_dims_rejected(bad):

@@ -75,7 +75,7 @@ class _Layer:
         for b in range(B):
             Kpre[b, :, prefill[b]:] = 0
         self.meta = H.alloc_meta(d)
-        self.klabel = torch.zeros(U * w.max_ctx * w.r, dtype=torch.int16, device="cuda")
+        self.klabel = H.alloc_klabel(d)
         self.label = torch.from_numpy(W.label_channels(w)).cuda()
         H.build_meta(d, dev16(Kpre), torch.from_numpy(prefill).cuda(), self.label, self.meta, self.klabel)
         self.cache = torch.zeros(U * n_slots * be, dtype=torch.int16, device="cuda")
@@ -150,7 +150,7 @@ def _check_against_oracle(w, prefill, K, V, qs, res):
                 ties += tie
                 resident = sel if t == 0 else sels[-1]
                 cand = O.candidate_tokens(resident, n, bs)
-                s_tok = O.label_scores(q, Kf[cand], label[g])
+                s_tok = O.label_scores(q, O.e4m3_round_nearest(Kf[cand]) if w.label_fp8 else Kf[cand], label[g])
                 k_eff = min(w.k_tokens, len(cand))
                 pos = res[t]["tok"][b, g]
                 assert np.all(pos[k_eff:] == -1), f"step {t} unit ({b},{g}): token padding"
