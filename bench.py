@@ -224,11 +224,31 @@ def fp8_meta_leg(w, base, reps, stream, args, ms_step_bf16):
     kb = score_kernel_bytes(w8)
     ach = kb / (us_score * 1e-6) / 1e9
     log(f"[bench] fp8 metadata: {ms * 1e3:.1f} us/step, block score {us_score:.2f} us/launch ({ach:.0f} GB/s)")
+    # the same step with the label rows in nearest-rounded e4m3 as well
+    w88 = dataclasses.replace(w8, label_fp8=True)
+    d88 = dims_of(w88)
+    lab8 = []
+    for r, m in zip(reps, metas):
+        kl = H.alloc_klabel(d88)
+        H.build_meta(d88, r.K, base["ctx_prefill"], base["label"], H.alloc_meta(d88), kl)
+        lab8.append(kl)
+    torch.cuda.synchronize()
+
+    def dec8(i):
+        r = reps[i]
+        return lambda: H.decode_step(d88, base["q"], base["k_new"], base["v_new"], r.K, r.V, metas[i], lab8[i],
+                                     base["label"], base["ctx"], r.blk, r.tok, r.out, r.lse, r.ws, stream=stream)
+    ms88 = time_replays([dec8(i) for i in range(len(reps))], stream, args.warmup, args.steps, not args.no_graph,
+                        graph_group(args.steps))
+    log(f"[bench] fp8 metadata and label rows: {ms88 * 1e3:.1f} us/step")
     return {"format": "e4m3, max rounded up, min rounded down", "ms_per_step": round(ms, 6),
             "queries_per_s": round(w.batch * w.n_q_heads / (ms * 1e-3), 1),
             "step_speedup_vs_bf16_meta": round(ms_step_bf16 / ms, 3),
             "block_score": {"us_per_launch": round(us_score, 3), "algorithmic_bytes": kb,
-                            "achieved": round(ach, 1), "frac": round(ach / HBM_PEAK_GBS, 4)}}
+                            "achieved": round(ach, 1), "frac": round(ach / HBM_PEAK_GBS, 4)},
+            "with_fp8_labels": {"label_format": "e4m3, nearest", "ms_per_step": round(ms88, 6),
+                                "queries_per_s": round(w.batch * w.n_q_heads / (ms88 * 1e-3), 1),
+                                "step_speedup_vs_bf16": round(ms_step_bf16 / ms88, 3)}}
 
 
 def variants_leg(w, base, reps, stream, args, ms_step):
