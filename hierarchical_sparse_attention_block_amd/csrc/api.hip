@@ -295,7 +295,7 @@ int hsab_offload_copy(const hsab_dims* dims, int32_t n_slots, const uint16_t* ho
     if (!aligned16(host_pool) || !aligned16(cache)) return HSAB_EINVAL;
     int calls = 0;
     rc = hip_status(offload_copy(s, n_slots, host_pool, cache, plan, plan_dev, slot_of, copy_stream, done, &calls,
-                                 copy_mode));
+                                 copy_mode, nullptr));
     if (n_copies) *n_copies = calls;
     return rc;
 }

@@ -105,7 +105,7 @@ constexpr int OFFLOAD_COPY_KERNEL = HSAB_OFFLOAD_COPY_KERNEL;
 constexpr int OFFLOAD_COPY_DMA = HSAB_OFFLOAD_COPY_DMA;
 hipError_t offload_copy(const Shape& s, int n_slots, const uint16_t* host_pool, uint16_t* cache,
                         const int32_t* plan, int32_t* plan_dev, int32_t* slot_of, hipStream_t cs,
-                        hipEvent_t done, int* n_copies, int mode);
+                        hipEvent_t done, int* n_copies, int mode, int32_t* copy_list);
 hipError_t offload_create(const Shape& s, int n_slots, int copy_mode, hsab_offload_engine** out);
 void offload_destroy(hsab_offload_engine* e);
 hipError_t offload_begin(hsab_offload_engine* e, const int32_t* n_prefill, const uint16_t* host_pool,

@@ -66,64 +66,108 @@ __global__ __launch_bounds__(256) void slot_patch_kernel(const int32_t* __restri
     }
 }
 
-// grid: up to GATHER_WGS workgroups, each taking chunks of 64 plan entries
-// (one per lane of the first wave). A chunk patches slot_of for its entries
-// and lists the blocks to copy in LDS; its four waves then pull those
-// blocks from the pinned host pool (mapped into the GPU's address space)
-// into their cache slots, one block per wave at a time with the whole
-// block (eight 16-byte loads per lane for 8 KiB) in flight. The grid is
-// kept small so the next step's kernels find free compute units while the
-// copy waits on the host link.
-constexpr int GATHER_WGS = 256;
-constexpr int GATHER_CHUNK = 64;
+// Copy one block (blk_elems bf16, 16-byte aligned) per pair of sources and
+// destinations, both blocks in flight at once: eight 16-byte loads per lane
+// and block for 8 KiB, unconditional (clamped) so none waits for another.
+__device__ __forceinline__ void copy_two_blocks(const uint4* src0, const uint4* src1, uint4* dst0, uint4* dst1,
+                                                int n16, int lane) {
+    for (int c0 = 0; c0 < n16; c0 += 8 * 64) {
+        uint4 v0[8], v1[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int c = c0 + k * 64 + lane;
+            const int cc = c < n16 ? c : n16 - 1;
+            v0[k] = src0[cc];
+            v1[k] = src1[cc];
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int c = c0 + k * 64 + lane;
+            if (c < n16) {
+                dst0[c] = v0[k];
+                dst1[c] = v1[k];
+            }
+        }
+    }
+}
+
+// One launch per step: every thread patches slot_of for one plan entry
+// (grid-stride), then the waves copy the blocks marked for copying from the
+// pinned host pool (mapped into the GPU's address space) into their cache
+// slots, two blocks in flight per wave. With a copy list (pairs of pool
+// block index and cache slot index, built by the host) wave v takes copies
+// 2v, 2v+1, then 2v + 2*waves, ... (balanced over the waves, the list
+// entries of all its rounds read in one load); without one, wave v takes
+// the marked entries among plan entries [32v, 32v + 32) (one ballot). A few
+// dozen workgroups keep the host link busy (a probe of scattered 8 KiB
+// reads from pinned memory peaked at 16-32 four-wave workgroups) and leave
+// the compute units to the next step's kernels. plan and copy_list are
+// device memory or coherent pinned memory through its device mapping.
+constexpr int GATHER_EPW = 32;
 __global__ __launch_bounds__(256) void gather_kernel(const int32_t* __restrict__ plan,
+                                                     const int32_t* __restrict__ copy_list, int n_copies,
                                                      const uint16_t* __restrict__ pool, uint16_t* __restrict__ cache,
                                                      int32_t* __restrict__ slot_of, int kb, int nb_cap, int n_slots,
                                                      int blk_elems, int n_entries) {
-    __shared__ int s_src[GATHER_CHUNK], s_dst[GATHER_CHUNK];
-    __shared__ int s_n;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int n16 = blk_elems / 8;
-    for (int base = blockIdx.x * GATHER_CHUNK; base < n_entries; base += gridDim.x * GATHER_CHUNK) {
-        if (threadIdx.x == 0) s_n = 0;
-        __syncthreads();
-        if (wave == 0) {
-            const int e = base + lane;
-            int blk = -1, slot = -1, cp = 0;
-            if (e < n_entries) {
-                blk = plan[(size_t)e * 3];
-                slot = plan[(size_t)e * 3 + 1];
-                cp = plan[(size_t)e * 3 + 2];
-            }
-            const bool ok = e < n_entries && blk >= 0 && blk < nb_cap && slot >= 0 && slot < n_slots;
-            const int unit = e / kb;
-            if (ok) slot_of[(size_t)unit * nb_cap + blk] = slot;
-            if (ok && cp) {
-                const int i = atomicAdd(&s_n, 1);
-                s_src[i] = unit * nb_cap + blk;
-                s_dst[i] = unit * n_slots + slot;
-            }
-        }
-        __syncthreads();
-        const int n = s_n;
-        for (int i = wave; i < n; i += 4) {
-            const uint4* src = reinterpret_cast<const uint4*>(pool + (size_t)s_src[i] * blk_elems);
-            uint4* dst = reinterpret_cast<uint4*>(cache + (size_t)s_dst[i] * blk_elems);
-            for (int c0 = 0; c0 < n16; c0 += 8 * 64) {
-                uint4 v[8];
-#pragma unroll
-                for (int k = 0; k < 8; ++k) {
-                    const int c = c0 + k * 64 + lane;
-                    if (c < n16) v[k] = src[c];
-                }
-#pragma unroll
-                for (int k = 0; k < 8; ++k) {
-                    const int c = c0 + k * 64 + lane;
-                    if (c < n16) dst[c] = v[k];
-                }
+    const int lane = threadIdx.x & 63;
+    const int wv = (blockIdx.x * blockDim.x + threadIdx.x) >> 6, n_waves = (gridDim.x * blockDim.x) >> 6;
+    const int n16 = blk_elems / 8;   // 16-byte chunks per block
+    const uint4* P4 = reinterpret_cast<const uint4*>(pool);
+    uint4* C4 = reinterpret_cast<uint4*>(cache);
+    // this thread's first plan entry is requested now, with the copy list,
+    // and its slot written after the copies
+    const int tid = blockIdx.x * blockDim.x + threadIdx.x, n_thr = gridDim.x * blockDim.x;
+    int pblk = -1, pslot = -1;
+    if (tid < n_entries) {
+        pblk = plan[(size_t)tid * 3];
+        pslot = plan[(size_t)tid * 3 + 1];
+    }
+    if (copy_list) {
+        // copies of this wave, round k: list entries 2(v + k*waves) and the next
+        int src = -1, dst = -1;
+        {
+            const int li = 2 * (wv + (lane >> 1) * n_waves) + (lane & 1);
+            if (li < n_copies) {
+                src = copy_list[2 * (size_t)li];
+                dst = copy_list[2 * (size_t)li + 1];
             }
         }
-        __syncthreads();   // s_n and the lists are reused by the next chunk
+        for (int k = 0; 2 * (wv + k * n_waves) < n_copies; ++k) {
+            if (k == 32) break;   // more than 32 rounds: not reached (checked on the host)
+            const int a = 2 * k, bl = 2 * (wv + k * n_waves) + 1 < n_copies ? 2 * k + 1 : 2 * k;
+            const int s0 = __builtin_amdgcn_readlane(src, a), d0 = __builtin_amdgcn_readlane(dst, a);
+            const int s1 = __builtin_amdgcn_readlane(src, bl), d1 = __builtin_amdgcn_readlane(dst, bl);
+            copy_two_blocks(P4 + (size_t)s0 * n16, P4 + (size_t)s1 * n16, C4 + (size_t)d0 * n16, C4 + (size_t)d1 * n16,
+                            n16, lane);
+        }
+    } else {
+        const int e0 = wv * GATHER_EPW, e = e0 + lane;
+        int blk = -1, slot = -1, cp = 0;
+        if (lane < GATHER_EPW && e < n_entries) {
+            blk = plan[(size_t)e * 3];
+            slot = plan[(size_t)e * 3 + 1];
+            cp = plan[(size_t)e * 3 + 2];
+        }
+        const bool ok = lane < GATHER_EPW && e < n_entries && blk >= 0 && blk < nb_cap && slot >= 0 && slot < n_slots;
+        uint64_t todo = __ballot(ok && cp != 0);
+        while (todo) {
+            const int i0 = __ffsll((unsigned long long)todo) - 1;
+            todo &= todo - 1;
+            const int i1 = todo ? __ffsll((unsigned long long)todo) - 1 : i0;   // i1 == i0: one block left
+            if (todo) todo &= todo - 1;
+            const int u0 = (e0 + i0) / kb, u1 = (e0 + i1) / kb;
+            const size_t s0 = (size_t)u0 * nb_cap + __builtin_amdgcn_readlane(blk, i0);
+            const size_t s1 = (size_t)u1 * nb_cap + __builtin_amdgcn_readlane(blk, i1);
+            const size_t d0 = (size_t)u0 * n_slots + __builtin_amdgcn_readlane(slot, i0);
+            const size_t d1 = (size_t)u1 * n_slots + __builtin_amdgcn_readlane(slot, i1);
+            copy_two_blocks(P4 + s0 * n16, P4 + s1 * n16, C4 + d0 * n16, C4 + d1 * n16, n16, lane);
+        }
+    }
+    // slot table of every planned block
+    if (pblk >= 0 && pblk < nb_cap && pslot >= 0 && pslot < n_slots) slot_of[(size_t)(tid / kb) * nb_cap + pblk] = pslot;
+    for (int e = tid + n_thr; e < n_entries; e += n_thr) {
+        const int blk = plan[(size_t)e * 3], slot = plan[(size_t)e * 3 + 1];
+        if (blk >= 0 && blk < nb_cap && slot >= 0 && slot < n_slots) slot_of[(size_t)(e / kb) * nb_cap + blk] = slot;
     }
 }
 
@@ -166,8 +210,11 @@ int offload_plan(const Shape& s, int n_slots, const int32_t* resident, const int
             const int sl = map[blk];
             if (sl >= 0 && sl < n_norm) used[sl] = 1;
         }
+        // ascending, -1 entries last (unsigned order); the selection kernel's
+        // lists already are, other callers' are sorted here
         sel.assign(S, S + kb);
-        std::sort(sel.begin(), sel.end());
+        const auto asc = [](int32_t x, int32_t y) { return (uint32_t)x < (uint32_t)y; };
+        if (!std::is_sorted(sel.begin(), sel.end(), asc)) std::sort(sel.begin(), sel.end(), asc);
         int np = 0, next_free = 0, rc = HSAB_OK;
         for (int blk : sel) {
             if (blk < 0 || blk >= s.nb_cap) continue;
@@ -204,29 +251,53 @@ int offload_plan(const Shape& s, int n_slots, const int32_t* resident, const int
 }
 
 // Enqueue a plan on copy stream cs, then record `done`.
-//  OFFLOAD_COPY_KERNEL: upload the plan, then gather_kernel pulls the
-//    blocks from the mapped pool and patches the slot table in one launch;
+//  OFFLOAD_COPY_KERNEL: gather_kernel pulls the blocks from the mapped pool
+//    and patches the slot table in one launch; with copy_list (coherent
+//    pinned, U*K_b pairs) the plan (then also coherent pinned) and the
+//    list the host fills here are read in place, else the plan is
+//    uploaded to plan_dev;
 //  OFFLOAD_COPY_DMA: contiguous runs of blocks into contiguous slots
 //    become one hipMemcpyAsync each (DMA engines), then the plan upload
 //    and the slot-table patch.
 // *n_copies: blocks gathered (kernel) or copies issued (DMA).
 hipError_t offload_copy(const Shape& s, int n_slots, const uint16_t* host_pool, uint16_t* cache,
                         const int32_t* plan, int32_t* plan_dev, int32_t* slot_of, hipStream_t cs,
-                        hipEvent_t done, int* n_copies, int mode) {
+                        hipEvent_t done, int* n_copies, int mode, int32_t* copy_list) {
     const int U = s.B * s.Hkv, kb = s.kb;
     const size_t blk_elems = (size_t)s.bs * (s.valias ? s.dk : s.dk + s.dv);
     int calls = 0;
     hipError_t e = hipSuccess;
     if (mode == OFFLOAD_COPY_KERNEL) {
-        for (int i = 0; i < U * kb; ++i) calls += plan[3 * i] >= 0 && plan[3 * i + 2] > 0;
+        const int n_entries = U * kb, waves = (n_entries + GATHER_EPW - 1) / GATHER_EPW;
+        const int n_wg = (waves + 3) / 4;
+        // a copy list (pool block, cache slot) lets the waves share the
+        // copies evenly; it holds at most 32 rounds of two per wave
+        int32_t* list = copy_list;
+        for (int i = 0; i < n_entries; ++i) {
+            const int blk = plan[3 * i], slot = plan[3 * i + 1];
+            if (blk < 0 || blk >= s.nb_cap || slot < 0 || slot >= n_slots || plan[3 * i + 2] <= 0) continue;
+            if (list) {
+                const int u = i / kb;
+                list[2 * calls] = u * s.nb_cap + plan[3 * i];
+                list[2 * calls + 1] = u * n_slots + plan[3 * i + 1];
+            }
+            ++calls;
+        }
+        if (calls > 2 * 32 * n_wg * 4) list = nullptr;
         const uint16_t* pool_dev = nullptr;
         e = hipHostGetDevicePointer((void**)&pool_dev, const_cast<uint16_t*>(host_pool), 0);
         if (e != hipSuccess) return e;
-        e = hipMemcpyAsync(plan_dev, plan, (size_t)U * kb * 3 * sizeof(int32_t), hipMemcpyHostToDevice, cs);
+        const int32_t* plan_src = plan_dev;
+        const int32_t* list_dev = nullptr;
+        if (copy_list) {   // the engine's plan and list: coherent pinned memory, read in place
+            e = hipHostGetDevicePointer((void**)&plan_src, const_cast<int32_t*>(plan), 0);
+            if (e == hipSuccess && list) e = hipHostGetDevicePointer((void**)&list_dev, list, 0);
+        } else {
+            e = hipMemcpyAsync(plan_dev, plan, (size_t)n_entries * 3 * sizeof(int32_t), hipMemcpyHostToDevice, cs);
+        }
         if (e != hipSuccess) return e;
-        const int n_entries = U * kb, chunks = (n_entries + GATHER_CHUNK - 1) / GATHER_CHUNK;
-        hipLaunchKernelGGL(gather_kernel, dim3(chunks < GATHER_WGS ? chunks : GATHER_WGS), dim3(256), 0, cs,
-                           plan_dev, pool_dev, cache, slot_of, kb, s.nb_cap, n_slots, (int)blk_elems, n_entries);
+        hipLaunchKernelGGL(gather_kernel, dim3(n_wg), dim3(256), 0, cs, plan_src, list_dev, calls, pool_dev, cache,
+                           slot_of, kb, s.nb_cap, n_slots, (int)blk_elems, n_entries);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     } else {
@@ -286,7 +357,8 @@ struct hsab_offload_engine {
     std::vector<int32_t> prev_sel, cur_sel;   // [U][K_b] S_b(t-1), S_b(t)
     std::vector<int32_t> none, slot_map, tail;
     int32_t* sel_h = nullptr;                 // pinned [U][K_b]
-    int32_t* plan_h[2] = {nullptr, nullptr};  // pinned [U][K_b][3]
+    int32_t* plan_h[2] = {nullptr, nullptr};  // pinned coherent [U][K_b][3]
+    int32_t* copy_h[2] = {nullptr, nullptr};  // pinned coherent [U*K_b][2]: the step's copies
     uint16_t* kv_h = nullptr;                 // pinned [U][d_k + d_v]: the new token's rows
     int32_t* sel_d[2] = {nullptr, nullptr};   // device [U][K_b]
     int32_t* plan_d[2] = {nullptr, nullptr};  // device [U][K_b][3]
@@ -304,6 +376,7 @@ void offload_destroy(hsab_offload_engine* e) {
     if (e->kv_h) (void)hipHostFree(e->kv_h);
     for (int i = 0; i < 2; ++i) {
         if (e->plan_h[i]) (void)hipHostFree(e->plan_h[i]);
+        if (e->copy_h[i]) (void)hipHostFree(e->copy_h[i]);
         if (e->sel_d[i]) (void)hipFree(e->sel_d[i]);
         if (e->plan_d[i]) (void)hipFree(e->plan_d[i]);
         if (e->ev_copy[i]) (void)hipEventDestroy(e->ev_copy[i]);
@@ -335,7 +408,12 @@ hipError_t offload_create(const Shape& s, int n_slots, int copy_mode, hsab_offlo
     ok(hipHostMalloc((void**)&e->sel_h, nsel * sizeof(int32_t), hipHostMallocDefault));
     ok(hipHostMalloc((void**)&e->kv_h, (size_t)e->U * (s.dk + s.dv) * sizeof(uint16_t), hipHostMallocDefault));
     for (int i = 0; i < 2; ++i) {
-        ok(hipHostMalloc((void**)&e->plan_h[i], nsel * 3 * sizeof(int32_t), hipHostMallocDefault));
+        // coherent: the gather kernel reads the plan in place while the host
+        // writes the other parity's
+        ok(hipHostMalloc((void**)&e->plan_h[i], nsel * 3 * sizeof(int32_t),
+                         hipHostMallocMapped | hipHostMallocCoherent));
+        ok(hipHostMalloc((void**)&e->copy_h[i], nsel * 2 * sizeof(int32_t),
+                         hipHostMallocMapped | hipHostMallocCoherent));
         ok(hipMalloc((void**)&e->sel_d[i], nsel * sizeof(int32_t)));
         ok(hipMalloc((void**)&e->plan_d[i], nsel * 3 * sizeof(int32_t)));
         ok(hipEventCreate(&e->ev_copy[i]));
@@ -469,7 +547,7 @@ hipError_t offload_step(hsab_offload_engine* e, const uint16_t* q, const uint16_
             return hipSuccess;
         }
         HSAB_TRY(offload_copy(s, e->n_slots, host_pool, cache, e->plan_h[1], e->plan_d[1], slot_of, xs,
-                              e->ev_copy[1], &calls, e->copy_mode));
+                              e->ev_copy[1], &calls, e->copy_mode, e->copy_h[1]));
         copies += calls;
         HSAB_TRY(hipEventRecord(tm[4], cs));
         HSAB_TRY(hipStreamWaitEvent(cs, e->ev_copy[1], 0));
@@ -487,7 +565,7 @@ hipError_t offload_step(hsab_offload_engine* e, const uint16_t* q, const uint16_
     }
     HSAB_TRY(hipEventRecord(tm[2], xs));
     HSAB_TRY(offload_copy(s, e->n_slots, host_pool, cache, e->plan_h[t & 1], e->plan_d[t & 1], slot_of, xs,
-                          e->ev_copy[t & 1], &calls, e->copy_mode));
+                          e->ev_copy[t & 1], &calls, e->copy_mode, e->copy_h[t & 1]));
     copies += calls;
     HSAB_TRY(hipEventRecord(tm[3], xs));
     const auto t2 = clk::now();
