@@ -59,11 +59,13 @@ hipError_t launch_block_score(const Shape& s, const uint16_t* q, uint16_t* meta,
 // With sel_keys and sel_cnt non-null (counters zero on entry, zero again on
 // exit) the token stage of each selection is spread over several
 // workgroups. Per-head selection runs U * G selections, each of one query
-// head (block lists [U][G][K_b], token lists [U][G][K_t]).
+// head (block lists [U][G][K_b], token lists [U][G][K_t]). blk_copy
+// (nullable): a second buffer that receives the same block lists (e.g.
+// host memory mapped into the GPU).
 hipError_t launch_select(const Shape& s, int mode, const uint16_t* q, const float* blk_score,
                          const uint16_t* klabel, const int32_t* label_ch, const int32_t* ctx_len,
                          int32_t* blk_idx, int32_t* tok_idx, float* tok_score, uint32_t* sel_keys,
-                         int32_t* sel_cnt, hipStream_t st);
+                         int32_t* sel_cnt, hipStream_t st, int32_t* blk_copy = nullptr);
 bool attend_supported(const Shape& s);
 // Per-head selection: the ascending union of the G token lists of each
 // unit ([U][G][K_t] -> [U][G*K_t], -1 padded) and, per entry, the bit mask
@@ -98,7 +100,7 @@ hipError_t launch_calibrate(const Shape& s, const uint16_t* q_samples, const uin
 constexpr int TIMING_RING = 32;
 hipError_t launch_append_slot(const Shape& s, int n_slots, const uint16_t* k_new, const uint16_t* v_new,
                               uint16_t* cache, uint16_t* meta, uint16_t* klabel, const int32_t* label_ch,
-                              const int32_t* ctx_len, hipStream_t st);
+                              const int32_t* ctx_len, hipStream_t st, uint16_t* pool_dev = nullptr);
 int offload_plan(const Shape& s, int n_slots, const int32_t* resident, const int32_t* selected,
                  const int32_t* tail, int32_t* slot_map, int32_t* plan, int64_t* delta_bytes);
 constexpr int OFFLOAD_COPY_KERNEL = HSAB_OFFLOAD_COPY_KERNEL;

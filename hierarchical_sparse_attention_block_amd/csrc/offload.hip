@@ -30,8 +30,8 @@ namespace {
 __global__ __launch_bounds__(256) void append_slot_kernel(
     const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new, uint16_t* __restrict__ cache,
     uint16_t* __restrict__ meta, uint16_t* __restrict__ klabel, const int32_t* __restrict__ label_ch,
-    const int32_t* __restrict__ ctx_len, int Hkv, int dk, int dv, int valias, int bs, int r, int max_ctx,
-    int nb_cap, int n_slots, int meta8, int lab8) {
+    const int32_t* __restrict__ ctx_len, uint16_t* __restrict__ pool, int Hkv, int dk, int dv, int valias, int bs,
+    int r, int max_ctx, int nb_cap, int n_slots, int meta8, int lab8) {
     const int unit = blockIdx.x, b = unit / Hkv, g = unit % Hkv;
     const int pos = ctx_len[b] - 1;
     if (pos < 0 || pos >= max_ctx) return;
@@ -41,14 +41,21 @@ __global__ __launch_bounds__(256) void append_slot_kernel(
     const uint16_t* kn = k_new + (size_t)unit * dk;
     uint16_t* slot = cache + ((size_t)unit * n_slots + (n_slots - 2 + (j & 1))) * slot_elems;
     uint8_t* M = meta_block(meta, (size_t)unit * nb_cap + j, dk, meta8);
+    // the same rows go to the pool block (pinned host memory through its
+    // device mapping) when pool is given
+    uint16_t* pb = pool ? pool + ((size_t)unit * nb_cap + j) * slot_elems : nullptr;
     for (int c = threadIdx.x; c < dk; c += blockDim.x) {
         const uint16_t kb = kn[c];
         slot[(size_t)off * dk + c] = kb;
+        if (pb) pb[(size_t)off * dk + c] = kb;
         meta_widen(M, dk, c, kb, first, meta8);
     }
     if (!valias) {
         const uint16_t* vn = v_new + (size_t)unit * dv;
-        for (int c = threadIdx.x; c < dv; c += blockDim.x) slot[(size_t)bs * dk + (size_t)off * dv + c] = vn[c];
+        for (int c = threadIdx.x; c < dv; c += blockDim.x) {
+            slot[(size_t)bs * dk + (size_t)off * dv + c] = vn[c];
+            if (pb) pb[(size_t)bs * dk + (size_t)off * dv + c] = vn[c];
+        }
     }
     const size_t lrow = ((size_t)unit * max_ctx + pos) * r;
     for (int c = threadIdx.x; c < r; c += blockDim.x)
@@ -175,10 +182,10 @@ __global__ __launch_bounds__(256) void gather_kernel(const int32_t* __restrict__
 
 hipError_t launch_append_slot(const Shape& s, int n_slots, const uint16_t* k_new, const uint16_t* v_new,
                               uint16_t* cache, uint16_t* meta, uint16_t* klabel, const int32_t* label_ch,
-                              const int32_t* ctx_len, hipStream_t st) {
+                              const int32_t* ctx_len, hipStream_t st, uint16_t* pool_dev) {
     hipLaunchKernelGGL(append_slot_kernel, dim3(s.B * s.Hkv), dim3(256), 0, st, k_new, v_new, cache, meta, klabel,
-                       label_ch, ctx_len, s.Hkv, s.dk, s.dv, s.valias, s.bs, s.r, s.max_ctx, s.nb_cap, n_slots,
-                       s.meta8, s.lab8);
+                       label_ch, ctx_len, pool_dev, s.Hkv, s.dk, s.dv, s.valias, s.bs, s.r, s.max_ctx, s.nb_cap,
+                       n_slots, s.meta8, s.lab8);
     return hipGetLastError();
 }
 
@@ -359,7 +366,6 @@ struct hsab_offload_engine {
     int32_t* sel_h = nullptr;                 // pinned [U][K_b]
     int32_t* plan_h[2] = {nullptr, nullptr};  // pinned coherent [U][K_b][3]
     int32_t* copy_h[2] = {nullptr, nullptr};  // pinned coherent [U*K_b][2]: the step's copies
-    uint16_t* kv_h = nullptr;                 // pinned [U][d_k + d_v]: the new token's rows
     int32_t* sel_d[2] = {nullptr, nullptr};   // device [U][K_b]
     int32_t* plan_d[2] = {nullptr, nullptr};  // device [U][K_b][3]
     hipEvent_t ev_sel = nullptr, ev_copy[2] = {nullptr, nullptr};
@@ -373,7 +379,6 @@ namespace hsab {
 void offload_destroy(hsab_offload_engine* e) {
     if (!e) return;
     if (e->sel_h) (void)hipHostFree(e->sel_h);
-    if (e->kv_h) (void)hipHostFree(e->kv_h);
     for (int i = 0; i < 2; ++i) {
         if (e->plan_h[i]) (void)hipHostFree(e->plan_h[i]);
         if (e->copy_h[i]) (void)hipHostFree(e->copy_h[i]);
@@ -405,8 +410,8 @@ hipError_t offload_create(const Shape& s, int n_slots, int copy_mode, hsab_offlo
     e->tail.assign((size_t)e->U * 2, -1);
     hipError_t r = hipSuccess;
     auto ok = [&](hipError_t x) { if (r == hipSuccess) r = x; };
-    ok(hipHostMalloc((void**)&e->sel_h, nsel * sizeof(int32_t), hipHostMallocDefault));
-    ok(hipHostMalloc((void**)&e->kv_h, (size_t)e->U * (s.dk + s.dv) * sizeof(uint16_t), hipHostMallocDefault));
+    // coherent: the selection kernel writes S_b(t) here through the mapping
+    ok(hipHostMalloc((void**)&e->sel_h, nsel * sizeof(int32_t), hipHostMallocMapped | hipHostMallocCoherent));
     for (int i = 0; i < 2; ++i) {
         // coherent: the gather kernel reads the plan in place while the host
         // writes the other parity's
@@ -500,16 +505,18 @@ hipError_t offload_step(hsab_offload_engine* e, const uint16_t* q, const uint16_
 
     // ---- compute stream, up to the token stage
     HSAB_TRY(hipEventRecord(tm[0], cs));
-    HSAB_TRY(launch_append_slot(s, e->n_slots, k_new, v_new, cache, meta, klabel, label_ch, ctx_len, cs));
-    HSAB_TRY(hipMemcpyAsync(e->kv_h, k_new, (size_t)U * s.dk * sizeof(uint16_t), hipMemcpyDeviceToHost, cs));
-    if (!s.valias)
-        HSAB_TRY(hipMemcpyAsync(e->kv_h + (size_t)U * s.dk, v_new, (size_t)U * s.dv * sizeof(uint16_t),
-                                hipMemcpyDeviceToHost, cs));
+    // the append also writes the new rows into the pool, and the block
+    // selection writes S_b(t) into mapped pinned memory as well: no copy
+    // engine round trip sits between the step's start and the host's plan
+    uint16_t* pool_dev = nullptr;
+    int32_t* sel_map = nullptr;
+    HSAB_TRY(hipHostGetDevicePointer((void**)&pool_dev, host_pool, 0));
+    HSAB_TRY(hipHostGetDevicePointer((void**)&sel_map, e->sel_h, 0));
+    HSAB_TRY(launch_append_slot(s, e->n_slots, k_new, v_new, cache, meta, klabel, label_ch, ctx_len, cs, pool_dev));
     HSAB_TRY(launch_block_score(s, q, meta, ctx_len, blk_score, nullptr, nullptr, nullptr, nullptr, nullptr,
                                 nullptr, sel_cnt, cs));
     HSAB_TRY(launch_select(s, 1, q, blk_score, nullptr, nullptr, ctx_len, sel_now, nullptr, nullptr, nullptr,
-                           nullptr, cs));
-    HSAB_TRY(hipMemcpyAsync(e->sel_h, sel_now, nsel * sizeof(int32_t), hipMemcpyDeviceToHost, cs));
+                           nullptr, cs, sel_map));
     HSAB_TRY(hipEventRecord(e->ev_sel, cs));
     HSAB_TRY(launch_select(s, 2, q, nullptr, klabel, label_ch, ctx_len, const_cast<int32_t*>(resident), tok_idx,
                            nullptr, sel_keys, sel_cnt, cs));
@@ -527,15 +534,6 @@ hipError_t offload_step(hsab_offload_engine* e, const uint16_t* q, const uint16_
     HSAB_TRY(hipEventSynchronize(e->ev_sel));
     const auto t1 = clk::now();
     std::memcpy(e->cur_sel.data(), e->sel_h, nsel * sizeof(int32_t));
-    for (int u = 0; u < U; ++u) {
-        const int b = u / s.Hkv, pos = e->n_ctx[b];   // the appended token
-        const int j = pos / s.bs, off = pos - j * s.bs;
-        uint16_t* blk = host_pool + ((size_t)u * s.nb_cap + j) * e->blk_elems;
-        std::memcpy(blk + (size_t)off * s.dk, e->kv_h + (size_t)u * s.dk, s.dk * sizeof(uint16_t));
-        if (!s.valias)
-            std::memcpy(blk + (size_t)s.bs * s.dk + (size_t)off * s.dv, e->kv_h + (size_t)U * s.dk + (size_t)u * s.dv,
-                        s.dv * sizeof(uint16_t));
-    }
     for (int b = 0; b < s.B; ++b) e->n_ctx[b] += 1;
     int64_t cold_bytes = 0, delta_bytes = 0;
     int copies = 0, calls = 0;

@@ -44,7 +44,8 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
     int mode, const uint16_t* __restrict__ q, const float* __restrict__ blk_score,
     const uint16_t* __restrict__ klabel, const int32_t* __restrict__ label_ch,
     const int32_t* __restrict__ ctx_len, int32_t* __restrict__ blk_idx, int32_t* __restrict__ tok_idx,
-    float* __restrict__ tok_score, uint32_t* __restrict__ gkeys, int32_t* __restrict__ cnt, int parts,
+    float* __restrict__ tok_score, uint32_t* __restrict__ gkeys, int32_t* __restrict__ cnt,
+    int32_t* __restrict__ blk_copy, int parts,
     int units, int heads, int Hkv, int G, int dk, int bs, int r, int kb, int kt, int max_ctx, int nb_cap,
     int bs_shift, int agg_sum, int sink, int local) {
     using Sel = TopK<SEL_WAVES, PT>;
@@ -129,18 +130,28 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
             bkey[j] = (j < pt_b && i < nb && i >= s1 && i < l0) ? f32_key(sraw[j]) : 0u;
         }
         int32_t* bo = blk_idx + (size_t)sel * kb;
+        int32_t* bc = blk_copy ? blk_copy + (size_t)sel * kb : nullptr;   // second copy of the list (nullable)
         const int keff = Sel::select(bkey, pt_b, kb - nforced, s_sel, [&](int pos, int i) {
             s_blk[s1 + pos] = i;
-            if (part == 0) bo[s1 + pos] = i;
+            if (part == 0) {
+                bo[s1 + pos] = i;
+                if (bc) bc[s1 + pos] = i;
+            }
         });
         for (int p = threadIdx.x; p < nforced; p += SEL_THREADS) {
             const int at = p < s1 ? p : keff + p, blk = p < s1 ? p : l0 + (p - s1);
             s_blk[at] = blk;
-            if (part == 0) bo[at] = blk;
+            if (part == 0) {
+                bo[at] = blk;
+                if (bc) bc[at] = blk;
+            }
         }
         for (int p = nforced + keff + threadIdx.x; p < kb; p += SEL_THREADS) {
             s_blk[p] = -1;
-            if (part == 0) bo[p] = -1;
+            if (part == 0) {
+                bo[p] = -1;
+                if (bc) bc[p] = -1;
+            }
         }
     } else {
         for (int p = threadIdx.x; p < kb; p += SEL_THREADS) s_blk[p] = blk_idx[(size_t)sel * kb + p];
@@ -275,10 +286,10 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
 template <int PT, int KK, bool L8>
 hipError_t launch_k(const Shape& s, dim3 grid, int mode, const uint16_t* q, const float* blk_score,
                     const uint16_t* klabel, const int32_t* label_ch, const int32_t* ctx_len, int32_t* blk_idx,
-                    int32_t* tok_idx, float* tok_score, uint32_t* gkeys, int32_t* cnt, int parts, int units, int shift,
-                    hipStream_t st) {
+                    int32_t* tok_idx, float* tok_score, uint32_t* gkeys, int32_t* cnt, int32_t* blk_copy, int parts,
+                    int units, int shift, hipStream_t st) {
     hipLaunchKernelGGL((select_kernel<PT, KK, L8>), grid, dim3(SEL_THREADS), 0, st, mode, q, blk_score, klabel,
-                       label_ch, ctx_len, blk_idx, tok_idx, tok_score, gkeys, cnt, parts, units, s.heads, s.Hkv, s.G,
+                       label_ch, ctx_len, blk_idx, tok_idx, tok_score, gkeys, cnt, blk_copy, parts, units, s.heads, s.Hkv, s.G,
                        s.dk, s.bs, s.r, s.kb, s.kt, s.max_ctx, s.nb_cap, shift, s.agg_sum, s.sink, s.local);
     return hipGetLastError();
 }
@@ -287,7 +298,7 @@ template <int PT>
 hipError_t launch_t(const Shape& s, int mode, const uint16_t* q, const float* blk_score,
                     const uint16_t* klabel, const int32_t* label_ch, const int32_t* ctx_len,
                     int32_t* blk_idx, int32_t* tok_idx, float* tok_score, uint32_t* gkeys, int32_t* cnt,
-                    hipStream_t st) {
+                    int32_t* blk_copy, hipStream_t st) {
     const int shift = (s.bs & (s.bs - 1)) ? -1 : __builtin_ctz(s.bs);
     const int units = s.B * s.Hkv * s.heads;   // selections
     // parts per selection: enough workgroups to cover the CUs, at least eight
@@ -300,13 +311,13 @@ hipError_t launch_t(const Shape& s, int mode, const uint16_t* q, const float* bl
     const dim3 grid(((units + 7) / 8) * 8 * parts);
     if (s.r >= 32)
         return s.lab8 ? launch_k<PT, 32, true>(s, grid, mode, q, blk_score, klabel, label_ch, ctx_len, blk_idx, tok_idx,
-                                               tok_score, gkeys, cnt, parts, units, shift, st)
+                                               tok_score, gkeys, cnt, blk_copy, parts, units, shift, st)
                       : launch_k<PT, 32, false>(s, grid, mode, q, blk_score, klabel, label_ch, ctx_len, blk_idx,
-                                                tok_idx, tok_score, gkeys, cnt, parts, units, shift, st);
+                                                tok_idx, tok_score, gkeys, cnt, blk_copy, parts, units, shift, st);
     return s.lab8 ? launch_k<PT, 16, true>(s, grid, mode, q, blk_score, klabel, label_ch, ctx_len, blk_idx, tok_idx,
-                                           tok_score, gkeys, cnt, parts, units, shift, st)
+                                           tok_score, gkeys, cnt, blk_copy, parts, units, shift, st)
                   : launch_k<PT, 16, false>(s, grid, mode, q, blk_score, klabel, label_ch, ctx_len, blk_idx, tok_idx,
-                                            tok_score, gkeys, cnt, parts, units, shift, st);
+                                            tok_score, gkeys, cnt, blk_copy, parts, units, shift, st);
 }
 
 }  // namespace
@@ -314,17 +325,17 @@ hipError_t launch_t(const Shape& s, int mode, const uint16_t* q, const float* bl
 hipError_t launch_select(const Shape& s, int mode, const uint16_t* q, const float* blk_score,
                          const uint16_t* klabel, const int32_t* label_ch, const int32_t* ctx_len,
                          int32_t* blk_idx, int32_t* tok_idx, float* tok_score, uint32_t* sel_keys,
-                         int32_t* sel_cnt, hipStream_t st) {
+                         int32_t* sel_cnt, hipStream_t st, int32_t* blk_copy) {
     int need = 1;
     if (mode & 1) need = (s.nb_cap + SEL_THREADS - 1) / SEL_THREADS;
     if (mode & 2) {
         const int t = (s.kb * s.bs + SEL_THREADS - 1) / SEL_THREADS;
         need = t > need ? t : need;
     }
-    if (need <= 1) return launch_t<1>(s, mode, q, blk_score, klabel, label_ch, ctx_len, blk_idx, tok_idx, tok_score, sel_keys, sel_cnt, st);
-    if (need <= 2) return launch_t<2>(s, mode, q, blk_score, klabel, label_ch, ctx_len, blk_idx, tok_idx, tok_score, sel_keys, sel_cnt, st);
-    if (need <= 4) return launch_t<4>(s, mode, q, blk_score, klabel, label_ch, ctx_len, blk_idx, tok_idx, tok_score, sel_keys, sel_cnt, st);
-    return launch_t<8>(s, mode, q, blk_score, klabel, label_ch, ctx_len, blk_idx, tok_idx, tok_score, sel_keys, sel_cnt, st);
+    if (need <= 1) return launch_t<1>(s, mode, q, blk_score, klabel, label_ch, ctx_len, blk_idx, tok_idx, tok_score, sel_keys, sel_cnt, blk_copy, st);
+    if (need <= 2) return launch_t<2>(s, mode, q, blk_score, klabel, label_ch, ctx_len, blk_idx, tok_idx, tok_score, sel_keys, sel_cnt, blk_copy, st);
+    if (need <= 4) return launch_t<4>(s, mode, q, blk_score, klabel, label_ch, ctx_len, blk_idx, tok_idx, tok_score, sel_keys, sel_cnt, blk_copy, st);
+    return launch_t<8>(s, mode, q, blk_score, klabel, label_ch, ctx_len, blk_idx, tok_idx, tok_score, sel_keys, sel_cnt, blk_copy, st);
 }
 
 }  // namespace hsab
