@@ -339,7 +339,8 @@ int hsab_offload_copy(const hsab_dims* dims, int32_t n_slots, const uint16_t* ho
  * hsab_offload_create and freed by hsab_offload_destroy; the caller owns
  * the pool, the block cache, metadata, label rows and outputs. Unlike the
  * rest of the library, hsab_offload_step waits on the host (for S_b(t),
- * about 16 KiB D2H) once per step. One engine serves one caller thread. */
+ * which the selection kernel writes into the engine's mapped pinned
+ * buffer) once per step. One engine serves one caller thread. */
 typedef struct hsab_offload_engine hsab_offload_engine;
 
 typedef struct hsab_offload_stats {
@@ -349,7 +350,7 @@ typedef struct hsab_offload_stats {
     int32_t delta_blocks;  /* blocks in the delta */
     int32_t n_copies;      /* blocks gathered (kernel copy) or copies issued (DMA copy) */
     float host_wait_ms;    /* host wait for S_b(t) */
-    float host_plan_ms;    /* pool write, planning and enqueue */
+    float host_plan_ms;    /* planning and enqueue of the copies */
 } hsab_offload_stats;
 
 /* n_slots >= 2*K_b + 2; copy_mode is HSAB_OFFLOAD_COPY_KERNEL or _DMA;
@@ -366,7 +367,9 @@ int hsab_offload_begin(hsab_offload_engine* engine, const int32_t* n_prefill, co
                        uint16_t* cache, int32_t* slot_of, hipStream_t stream);
 
 /* Decode step t [de 2.B; es 2.B]: appends k_new/v_new (device, written to
- * the tail slot, meta, klabel, and to host_pool by the host), selects
+ * the tail slot, meta, klabel, and by the same kernel to host_pool through
+ * its device mapping; host_pool must be pinned, hipHostMalloc memory),
+ * selects
  * S_b(t), runs the token stage and attention over R(t) = S_b(t-1) through
  * the block cache (R(0) = S_b(0) after a synchronous fill), and enqueues
  * the delta for step t+1 on copy_stream. ctx_len (device) and ctx_len_host
