@@ -98,10 +98,12 @@ __device__ __forceinline__ void copy_two_blocks(const uint4* src0, const uint4* 
     }
 }
 
-// One launch per step: every thread patches slot_of for one plan entry
-// (grid-stride), then the waves copy the blocks marked for copying from the
-// pinned host pool (mapped into the GPU's address space) into their cache
-// slots, two blocks in flight per wave. With a copy list (pairs of pool
+// The waves copy the blocks marked for copying from the pinned host pool
+// (mapped into the GPU's address space) into their cache slots, two blocks
+// in flight per wave; the slot table is patched by the next launch, once
+// every copy has landed (the step's attention may read slot_of meanwhile
+// and must find either a block's old slot, still intact, or a finished
+// copy). With a copy list (pairs of pool
 // block index and cache slot index, built by the host) wave v takes copies
 // 2v, 2v+1, then 2v + 2*waves, ... (balanced over the waves, the list
 // entries of all its rounds read in one load); without one, wave v takes
@@ -114,21 +116,12 @@ constexpr int GATHER_EPW = 32;
 __global__ __launch_bounds__(256) void gather_kernel(const int32_t* __restrict__ plan,
                                                      const int32_t* __restrict__ copy_list, int n_copies,
                                                      const uint16_t* __restrict__ pool, uint16_t* __restrict__ cache,
-                                                     int32_t* __restrict__ slot_of, int kb, int nb_cap, int n_slots,
-                                                     int blk_elems, int n_entries) {
+                                                     int kb, int nb_cap, int n_slots, int blk_elems, int n_entries) {
     const int lane = threadIdx.x & 63;
     const int wv = (blockIdx.x * blockDim.x + threadIdx.x) >> 6, n_waves = (gridDim.x * blockDim.x) >> 6;
     const int n16 = blk_elems / 8;   // 16-byte chunks per block
     const uint4* P4 = reinterpret_cast<const uint4*>(pool);
     uint4* C4 = reinterpret_cast<uint4*>(cache);
-    // this thread's first plan entry is requested now, with the copy list,
-    // and its slot written after the copies
-    const int tid = blockIdx.x * blockDim.x + threadIdx.x, n_thr = gridDim.x * blockDim.x;
-    int pblk = -1, pslot = -1;
-    if (tid < n_entries) {
-        pblk = plan[(size_t)tid * 3];
-        pslot = plan[(size_t)tid * 3 + 1];
-    }
     if (copy_list) {
         // copies of this wave, round k: list entries 2(v + k*waves) and the next
         int src = -1, dst = -1;
@@ -169,12 +162,6 @@ __global__ __launch_bounds__(256) void gather_kernel(const int32_t* __restrict__
             const size_t d1 = (size_t)u1 * n_slots + __builtin_amdgcn_readlane(slot, i1);
             copy_two_blocks(P4 + s0 * n16, P4 + s1 * n16, C4 + d0 * n16, C4 + d1 * n16, n16, lane);
         }
-    }
-    // slot table of every planned block
-    if (pblk >= 0 && pblk < nb_cap && pslot >= 0 && pslot < n_slots) slot_of[(size_t)(tid / kb) * nb_cap + pblk] = pslot;
-    for (int e = tid + n_thr; e < n_entries; e += n_thr) {
-        const int blk = plan[(size_t)e * 3], slot = plan[(size_t)e * 3 + 1];
-        if (blk >= 0 && blk < nb_cap && slot >= 0 && slot < n_slots) slot_of[(size_t)(e / kb) * nb_cap + blk] = slot;
     }
 }
 
@@ -258,8 +245,8 @@ int offload_plan(const Shape& s, int n_slots, const int32_t* resident, const int
 }
 
 // Enqueue a plan on copy stream cs, then record `done`.
-//  OFFLOAD_COPY_KERNEL: gather_kernel pulls the blocks from the mapped pool
-//    and patches the slot table in one launch; with copy_list (coherent
+//  OFFLOAD_COPY_KERNEL: gather_kernel pulls the blocks from the mapped pool,
+//    then slot_patch_kernel patches the slot table; with copy_list (coherent
 //    pinned, U*K_b pairs) the plan (then also coherent pinned) and the
 //    list the host fills here are read in place, else the plan is
 //    uploaded to plan_dev;
@@ -304,7 +291,10 @@ hipError_t offload_copy(const Shape& s, int n_slots, const uint16_t* host_pool, 
         }
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(gather_kernel, dim3(n_wg), dim3(256), 0, cs, plan_src, list_dev, calls, pool_dev, cache,
-                           slot_of, kb, s.nb_cap, n_slots, (int)blk_elems, n_entries);
+                           kb, s.nb_cap, n_slots, (int)blk_elems, n_entries);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(slot_patch_kernel, dim3(U), dim3(256), 0, cs, plan_src, slot_of, kb, s.nb_cap);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     } else {

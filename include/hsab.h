@@ -316,7 +316,8 @@ int hsab_offload_plan(const hsab_dims* dims, int32_t n_slots, const int32_t* res
 /* How the delta crosses the host link:
  *   HSAB_OFFLOAD_COPY_KERNEL  a GPU kernel reads the blocks from the pinned
  *       pool (hipHostMalloc memory, mapped into the GPU address space) and
- *       writes them to their slots, patching slot_of in the same launch;
+ *       writes them to their slots, then a second kernel patches slot_of
+ *       (a reader of slot_of finds a block's old slot or a finished copy);
  *   HSAB_OFFLOAD_COPY_DMA     the DMA engines copy each run of consecutive
  *       blocks into consecutive slots (one hipMemcpyAsync per run), then a
  *       kernel patches slot_of. */
