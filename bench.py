@@ -438,12 +438,18 @@ def offload_bench(args):
                 if t == 1:
                     torch.cuda.synchronize()
                     t_steady = time.perf_counter()
+                h0 = time.perf_counter()
                 stats.append(eng.step(q_d[t], kn_d[t], vn_d[t], pool, cache, meta, klabel, label, ctx_d[t],
                                       ctx_h[t], slot_of, tok, out, lse, ws, compute_stream=cs,
                                       copy_stream=xs).as_dict())
+                stats[-1]["host_call_ms"] = (time.perf_counter() - h0) * 1e3
             torch.cuda.synchronize()
             t_end = time.perf_counter()
             tim = [eng.timing(t) for t in range(steps)]
+            for t, x in enumerate(stats):   # planned on the GPU (kernel copies): read back now
+                x["delta_bytes"], x["cold_bytes"] = eng.delta(t)
+                if x["n_copies"] < 0:
+                    x["n_copies"] = x["delta_bytes"] // (H.block_elems(d) * 2)
             runs.append({"cold_s": t_steady - t_start, "steady_s": t_end - t_steady, "stats": stats, "tim": tim})
         eng.close()
         runs = runs[1:]
@@ -458,7 +464,8 @@ def offload_bench(args):
         hidden = 1.0 - waits.sum() / max(copy_ms[:-1].sum(), 1e-9)
         link_gbs = delta.sum() / max(copy_ms.sum() * 1e-3, 1e-12) / 1e9
         return ms_step, {
-            "copy_mode": "gather_kernel" if copy_mode == H.COPY_KERNEL else "dma_memcpy",
+            "copy_mode": {H.COPY_KERNEL: "gather_kernel", H.COPY_DMA: "dma_memcpy",
+                          H.COPY_KERNEL_GPU_PLAN: "gather_kernel_gpu_plan"}[copy_mode],
             "ms_per_step": round(ms_step, 6), "runs": len(runs),
             "cold_ms": round(best["cold_s"] * 1e3, 3), "cold_bytes": st[0]["cold_bytes"],
             "delta_bytes_per_step": delta.tolist(), "delta_bytes_mean": float(delta.mean()),
@@ -472,10 +479,12 @@ def offload_bench(args):
             "compute_ms_mean": round(float(np.mean([x["compute_ms"] for x in tim[1:]])), 4),
             "host_wait_ms_mean": round(float(np.mean([x["host_wait_ms"] for x in st[1:]])), 4),
             "host_plan_ms_mean": round(float(np.mean([x["host_plan_ms"] for x in st[1:]])), 4),
+            "host_call_ms_mean": round(float(np.mean([x["host_call_ms"] for x in st[1:]])), 4),
         }
 
     ms_step, off_k = timed_runs(H.COPY_KERNEL)
     _, off_d = timed_runs(H.COPY_DMA)
+    _, off_g = timed_runs(H.COPY_KERNEL_GPU_PLAN)
 
     def multilayer(n_layers):
         """n_layers layers stepped in turn each decode step on one compute
@@ -558,6 +567,7 @@ def offload_bench(args):
         "resident_ms_per_step": round(resident_ms, 6),
         "offload": off_k,
         "offload_dma": off_d,
+        "offload_gpu_plan": off_g,
         "multilayer": multi,
     }
     if not args.no_cpu:

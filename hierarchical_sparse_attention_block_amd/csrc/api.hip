@@ -307,7 +307,11 @@ int hsab_offload_create(const hsab_dims* dims, int32_t n_slots, int32_t copy_mod
     *engine = nullptr;
     const Shape s = make_shape(*dims);
     if (n_slots < 2 * s.kb + 2) return HSAB_EINVAL;
-    if (copy_mode != HSAB_OFFLOAD_COPY_KERNEL && copy_mode != HSAB_OFFLOAD_COPY_DMA) return HSAB_EINVAL;
+    if (copy_mode != HSAB_OFFLOAD_COPY_KERNEL && copy_mode != HSAB_OFFLOAD_COPY_DMA &&
+        copy_mode != HSAB_OFFLOAD_COPY_KERNEL_GPU_PLAN)
+        return HSAB_EINVAL;
+    if (copy_mode == HSAB_OFFLOAD_COPY_KERNEL_GPU_PLAN && 2 * ((n_slots - 2 + 31) / 32) + s.kb > 15360)
+        return HSAB_EINVAL;   // the device planner's LDS
     if (!attend_supported(s) || s.agg == AGG_HEAD) return HSAB_EUNSUPPORTED;   // blocks move per KV head
     return hip_status(offload_create(s, n_slots, copy_mode, engine));
 }
@@ -354,8 +358,17 @@ int hsab_offload_timing(hsab_offload_engine* engine, int64_t step, float* ms) {
 int hsab_offload_selection(const hsab_offload_engine* engine, int32_t* blk_idx_host) {
     if (!engine || !blk_idx_host || offload_steps(engine) < 1) return HSAB_EINVAL;
     const Shape& s = offload_shape(engine);
-    memcpy(blk_idx_host, offload_last_selection(engine), (size_t)s.B * s.Hkv * s.kb * sizeof(int32_t));
+    const int32_t* sel = offload_last_selection(const_cast<hsab_offload_engine*>(engine));
+    if (!sel) return HSAB_EHIP;
+    memcpy(blk_idx_host, sel, (size_t)s.B * s.Hkv * s.kb * sizeof(int32_t));
     return HSAB_OK;
+}
+
+int hsab_offload_step_delta(hsab_offload_engine* engine, int64_t step, int64_t* delta_bytes, int64_t* cold_bytes) {
+    if (!engine || !delta_bytes || !cold_bytes || step < 0 || step >= offload_steps(engine) ||
+        step < offload_steps(engine) - TIMING_RING)
+        return HSAB_EINVAL;
+    return hip_status(offload_step_delta(engine, step, delta_bytes, cold_bytes));
 }
 
 }  // extern "C"

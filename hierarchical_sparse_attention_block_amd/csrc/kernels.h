@@ -105,9 +105,21 @@ int offload_plan(const Shape& s, int n_slots, const int32_t* resident, const int
                  const int32_t* tail, int32_t* slot_map, int32_t* plan, int64_t* delta_bytes);
 constexpr int OFFLOAD_COPY_KERNEL = HSAB_OFFLOAD_COPY_KERNEL;
 constexpr int OFFLOAD_COPY_DMA = HSAB_OFFLOAD_COPY_DMA;
+constexpr int OFFLOAD_COPY_KERNEL_GPU_PLAN = HSAB_OFFLOAD_COPY_KERNEL_GPU_PLAN;
+// The offload engine's plan buffers in coherent pinned memory: the copy
+// lists ([U][K_b] pairs) and counts ([U]) the host fills, and the device
+// addresses of those, of the plan and of the pool.
+struct MappedPlan {
+    int32_t* list_h = nullptr;
+    int32_t* cnt_h = nullptr;
+    const int32_t* plan_dev = nullptr;
+    const int32_t* list_dev = nullptr;
+    const int32_t* cnt_dev = nullptr;
+    const uint16_t* pool_dev = nullptr;
+};
 hipError_t offload_copy(const Shape& s, int n_slots, const uint16_t* host_pool, uint16_t* cache,
                         const int32_t* plan, int32_t* plan_dev, int32_t* slot_of, hipStream_t cs,
-                        hipEvent_t done, int* n_copies, int mode, int32_t* copy_list);
+                        hipEvent_t done, int* n_copies, int mode, const MappedPlan* mp);
 hipError_t offload_create(const Shape& s, int n_slots, int copy_mode, hsab_offload_engine** out);
 void offload_destroy(hsab_offload_engine* e);
 hipError_t offload_begin(hsab_offload_engine* e, const int32_t* n_prefill, const uint16_t* host_pool,
@@ -119,7 +131,8 @@ hipError_t offload_step(hsab_offload_engine* e, const uint16_t* q, const uint16_
                         int32_t* slot_of, int32_t* tok_idx, float* out, float* lse, void* ws, hipStream_t cs,
                         hipStream_t xs, hsab_offload_stats* st, int* einval);
 hipError_t offload_timing(hsab_offload_engine* e, int64_t step, float* ms4);
-const int32_t* offload_last_selection(const hsab_offload_engine* e);
+const int32_t* offload_last_selection(hsab_offload_engine* e);
+hipError_t offload_step_delta(hsab_offload_engine* e, int64_t step, int64_t* delta_bytes, int64_t* cold_bytes);
 int64_t offload_steps(const hsab_offload_engine* e);
 const Shape& offload_shape(const hsab_offload_engine* e);
 

@@ -21,12 +21,12 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 HSAB_OK, HSAB_EINVAL, HSAB_EHIP, HSAB_EUNSUPPORTED = 0, -1, -2, -3
-COPY_KERNEL, COPY_DMA = 0, 1   # HSAB_OFFLOAD_COPY_*
+COPY_KERNEL, COPY_DMA, COPY_KERNEL_GPU_PLAN = 0, 1, 2   # HSAB_OFFLOAD_COPY_*
 EXPORTS = ("hsab_workspace_bytes", "hsab_status_string", "hsab_last_hip_error", "hsab_build_meta",
            "hsab_score_blocks", "hsab_select_blocks", "hsab_select_tokens", "hsab_sparse_attend",
            "hsab_decode_step", "hsab_offload_append", "hsab_offload_plan", "hsab_offload_copy", "hsab_offload_create",
            "hsab_offload_destroy", "hsab_offload_begin", "hsab_offload_step", "hsab_offload_timing",
-           "hsab_offload_selection", "hsab_dense_workspace_bytes", "hsab_dense_attend",
+           "hsab_offload_selection", "hsab_offload_step_delta", "hsab_dense_workspace_bytes", "hsab_dense_attend",
            "hsab_calibrate_labels")
 
 
@@ -102,6 +102,7 @@ _lib.hsab_offload_begin.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp]
 _lib.hsab_offload_step.argtypes = [_vp] * 16 + [_sz, _vp, _vp, ctypes.POINTER(OffloadStats)]
 _lib.hsab_offload_timing.argtypes = [_vp, ctypes.c_int64, _vp]
 _lib.hsab_offload_selection.argtypes = [_vp, _vp]
+_lib.hsab_offload_step_delta.argtypes = [_vp, ctypes.c_int64, _vp, _vp]
 for _f in EXPORTS[3:]:
     getattr(_lib, _f).restype = ctypes.c_int
 _lib.hsab_offload_destroy.restype = None
@@ -400,7 +401,7 @@ class OffloadEngine:
         _check("hsab_offload_step", _lib.hsab_offload_step(
             self._h, _buf("q", q, _u16, s["q"]), _buf("k_new", k_new, _u16, s["knew"]),
             _buf("v_new", v_new, _u16, s["vnew"], allow_none=bool(d.v_alias_k)),
-            _hbuf("host_pool", host_pool, _u16, U * d.nb_cap * block_elems(d), pinned=True),
+            self._pool(host_pool, U * d.nb_cap * block_elems(d)),
             _buf("cache", cache, _u16, U * self.n_slots * block_elems(d)), _meta(d, meta),
             _klabel(d, klabel), _buf("label_ch", label_ch, _i, s["label"]),
             _buf("ctx_len", ctx_len, _i, s["ctx"]), _hbuf("ctx_len_host", ctx_len_host, _i, d.batch),
@@ -408,6 +409,16 @@ class OffloadEngine:
             _buf("out", out, _f, s["out"]), _buf("lse", lse, _f, s["lse"]), wp, wn, _stream(compute_stream),
             _stream(copy_stream), ctypes.byref(st)))
         return st
+
+    def _pool(self, host_pool, numel):
+        """The pool's pointer; whether it is pinned is checked once per
+        tensor (the query goes to the HIP runtime), the rest every call."""
+        key = (host_pool.data_ptr(), host_pool.numel()) if isinstance(host_pool, torch.Tensor) else None
+        if key is not None and key == getattr(self, "_pool_ok", None):
+            return _hbuf("host_pool", host_pool, _u16, numel)
+        p = _hbuf("host_pool", host_pool, _u16, numel, pinned=True)
+        self._pool_ok = key
+        return p
 
     def timing(self, step):
         ms = (ctypes.c_float * 5)()
@@ -420,6 +431,14 @@ class OffloadEngine:
         outb = torch.empty(d.batch * d.n_kv_heads * d.k_blocks, dtype=torch.int32)
         _check("hsab_offload_selection", _lib.hsab_offload_selection(self._h, ctypes.c_void_p(outb.data_ptr())))
         return outb.view(d.batch, d.n_kv_heads, d.k_blocks)
+
+    def delta(self, step) -> tuple:
+        """(delta_bytes, cold_bytes) of a step among the last 32 (waits for
+        that step's copies when the GPU planned them)."""
+        db, cb = ctypes.c_int64(0), ctypes.c_int64(0)
+        _check("hsab_offload_step_delta", _lib.hsab_offload_step_delta(self._h, ctypes.c_int64(step),
+                                                                       ctypes.byref(db), ctypes.byref(cb)))
+        return int(db.value), int(cb.value)
 
 
 def dense_workspace_bytes(d: Dims) -> int:

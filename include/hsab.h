@@ -323,6 +323,10 @@ int hsab_offload_plan(const hsab_dims* dims, int32_t n_slots, const int32_t* res
  *       kernel patches slot_of. */
 #define HSAB_OFFLOAD_COPY_KERNEL 0
 #define HSAB_OFFLOAD_COPY_DMA    1
+/* Engine only: kernel copies whose plan the copy stream makes on the GPU
+ * (the same rules as hsab_offload_plan), so hsab_offload_step never waits
+ * on the host; the step's delta bytes come from hsab_offload_step_delta. */
+#define HSAB_OFFLOAD_COPY_KERNEL_GPU_PLAN 2
 
 /* Enqueue a plan on copy_stream: the block copies as copy_mode says, the
  * upload of the plan (plan must be pinned host memory; plan_dev is device
@@ -341,9 +345,15 @@ int hsab_offload_copy(const hsab_dims* dims, int32_t n_slots, const uint16_t* ho
  * the pool, the block cache, metadata, label rows and outputs. Unlike the
  * rest of the library, hsab_offload_step waits on the host (for S_b(t),
  * which the selection kernel writes into the engine's mapped pinned
- * buffer) once per step. One engine serves one caller thread. */
+ * buffer) once per step, except with HSAB_OFFLOAD_COPY_KERNEL_GPU_PLAN,
+ * where the copy stream plans the delta on the GPU (the same rules as
+ * hsab_offload_plan) and the host does not wait. One engine serves one
+ * caller thread. */
 typedef struct hsab_offload_engine hsab_offload_engine;
 
+/* With GPU planning the plan is made after the call returns:
+ * delta_bytes, cold_bytes, delta_blocks and n_copies are then -1, and
+ * hsab_offload_step_delta gives the bytes once the step's copies ran. */
 typedef struct hsab_offload_stats {
     int64_t step;          /* index of the step just enqueued (0 = cold start) */
     int64_t delta_bytes;   /* host-to-device bytes of the step's delta */
@@ -354,7 +364,9 @@ typedef struct hsab_offload_stats {
     float host_plan_ms;    /* planning and enqueue of the copies */
 } hsab_offload_stats;
 
-/* n_slots >= 2*K_b + 2; copy_mode is HSAB_OFFLOAD_COPY_KERNEL or _DMA;
+/* n_slots >= 2*K_b + 2; copy_mode is HSAB_OFFLOAD_COPY_KERNEL, _DMA or
+ * _KERNEL_GPU_PLAN (HSAB_EINVAL for the last when n_slots is beyond what
+ * the device planner holds in LDS: 2*ceil((n_slots-2)/32) + K_b > 15360);
  * HSAB_EHIP if an allocation fails. */
 int hsab_offload_create(const hsab_dims* dims, int32_t n_slots, int32_t copy_mode, hsab_offload_engine** engine);
 void hsab_offload_destroy(hsab_offload_engine* engine);
@@ -392,8 +404,15 @@ int hsab_offload_step(hsab_offload_engine* engine, const uint16_t* q, const uint
  * its attention. */
 int hsab_offload_timing(hsab_offload_engine* engine, int64_t step, float* ms);
 
-/* Host copy of the last step's S_b [B][Hkv][K_b] (ascending, -1 padded). */
+/* Host copy of the last step's S_b [B][Hkv][K_b] (ascending, -1 padded);
+ * waits for that step's block selection. */
 int hsab_offload_selection(const hsab_offload_engine* engine, int32_t* blk_idx_host);
+
+/* Delta bytes (and, for step 0, the cold-fill bytes; else 0) of a step
+ * among the last 32 enqueued, waiting for that step's copies when the GPU
+ * planned them. HSAB_EINVAL for a null pointer or a step outside that
+ * window; HSAB_EHIP if the wait fails. */
+int hsab_offload_step_delta(hsab_offload_engine* engine, int64_t step, int64_t* delta_bytes, int64_t* cold_bytes);
 
 #ifdef __cplusplus
 }

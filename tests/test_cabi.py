@@ -95,7 +95,7 @@ def test_null_pointers_rejected():
     q = ctypes.c_void_p(18)
     assert H.raw_call("hsab_offload_copy", ctypes.byref(d), 18, q, p, p, p, p, 0, None, None, None) == H.HSAB_EINVAL
     h = ctypes.c_void_p()
-    assert H.raw_call("hsab_offload_create", ctypes.byref(d), 18, 2, ctypes.byref(h)) == H.HSAB_EINVAL
+    assert H.raw_call("hsab_offload_create", ctypes.byref(d), 18, 3, ctypes.byref(h)) == H.HSAB_EINVAL
 
 
 def test_small_workspace_and_unsupported_shape():

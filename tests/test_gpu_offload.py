@@ -100,7 +100,10 @@ class _Layer:
 
     def collect(self, st):
         w, B, Hkv = self.w, self.w.batch, self.w.n_kv_heads
-        self.res.append({"sel": self.eng.selection().numpy().copy(), "stats": st.as_dict(),
+        stats = st.as_dict()
+        # with kernel copies the GPU plans the delta: its bytes once the step's copies ran
+        stats["delta_bytes"], stats["cold_bytes"] = self.eng.delta(stats["step"])
+        self.res.append({"sel": self.eng.selection().numpy().copy(), "stats": stats,
                          "tok": self.tok.cpu().numpy().reshape(B, Hkv, w.k_tokens),
                          "out": self.out.cpu().numpy().reshape(B, w.n_q_heads, w.d_v),
                          "lse": self.lse.cpu().numpy().reshape(B, w.n_q_heads)})
@@ -177,7 +180,7 @@ def _check_against_oracle(w, prefill, K, V, qs, res):
     return ties
 
 
-@pytest.mark.parametrize("copy_mode", [0, 1], ids=["gather_kernel", "dma"])
+@pytest.mark.parametrize("copy_mode", [0, 1, 2], ids=["gather_kernel", "dma", "gather_kernel_gpu_plan"])
 def test_offload_gqa_matches_lagged_oracle(copy_mode):
     w = W.WORKLOADS["tiny4k"].replace(name="offload_gqa", batch=2, n_q_heads=8, n_kv_heads=2, k_blocks=8,
                                       k_tokens=64, ctx=1024, max_ctx=1024, scaled_keys=True, n_planted=0,
@@ -199,7 +202,8 @@ def test_offload_gqa_fp8_metadata():
     _check_against_oracle(w, np.array(prefill), K, V, qs, res)
 
 
-def test_offload_layers_interleaved():
+@pytest.mark.parametrize("copy_mode", [0, 2], ids=["host_plan", "gpu_plan"])
+def test_offload_layers_interleaved(copy_mode):
     """Three layers (own pools, caches, engines; different keys and queries)
     stepped in turn on one compute and one copy stream: every layer still
     matches the lagged oracle, step by step."""
@@ -207,7 +211,8 @@ def test_offload_layers_interleaved():
                                          k_tokens=64, ctx=1024, max_ctx=1024, scaled_keys=True, n_planted=0)
     prefill, steps = [300, 511], 6
     xs = torch.cuda.Stream()
-    layers = [_Layer(base.replace(seed=40 + l), prefill, steps, copy_stream=xs) for l in range(3)]
+    layers = [_Layer(base.replace(seed=40 + l), prefill, steps, copy_mode=copy_mode, copy_stream=xs)
+              for l in range(3)]
     for t in range(steps):
         sts = [layer.step(t) for layer in layers]
         torch.cuda.synchronize()
@@ -240,9 +245,10 @@ def test_offload_gqa_without_oracle_ties_equals_oracle_run():
         assert np.max(np.abs(ref[t]["out"] - res[t]["out"][0])) <= OUT_ATOL
 
 
-def test_offload_mla_latent_blocks():
+@pytest.mark.parametrize("copy_mode", [0, 2], ids=["host_plan", "gpu_plan"])
+def test_offload_mla_latent_blocks(copy_mode):
     w = W.WORKLOADS["mla64k"].replace(name="offload_mla", batch=1, k_blocks=4, k_tokens=64, ctx=700,
                                       max_ctx=700, seed=23)
     prefill = [640]               # 640 = 20 blocks of 32: the first decode token opens block 20
-    K, V, qs, res = _run_offload(w, prefill, steps=6, copy_mode=0)
+    K, V, qs, res = _run_offload(w, prefill, steps=6, copy_mode=copy_mode)
     _check_against_oracle(w, np.array(prefill), K, V, qs, res)
