@@ -427,7 +427,12 @@ def offload_bench(args):
     def timed_runs(copy_mode):
         eng = H.OffloadEngine(d, n_slots, copy_mode)
         runs = []
-        for run in range(args.offload_runs + 1):   # run 0 warms up
+        # run 0 warms up; the timed runs record no GPU timestamps (each
+        # timed event is a marker the GPU processes, several us per step);
+        # one more run with timestamps gives the copy / wait breakdown
+        for run in range(args.offload_runs + 2):
+            instrumented = run == args.offload_runs + 1
+            eng.set_timing(instrumented)
             meta.copy_(meta0)
             klabel.copy_(klabel0)
             torch.cuda.synchronize()
@@ -445,17 +450,20 @@ def offload_bench(args):
                 stats[-1]["host_call_ms"] = (time.perf_counter() - h0) * 1e3
             torch.cuda.synchronize()
             t_end = time.perf_counter()
-            tim = [eng.timing(t) for t in range(steps)]
             for t, x in enumerate(stats):   # planned on the GPU (kernel copies): read back now
                 x["delta_bytes"], x["cold_bytes"] = eng.delta(t)
                 if x["n_copies"] < 0:
                     x["n_copies"] = x["delta_bytes"] // (H.block_elems(d) * 2)
-            runs.append({"cold_s": t_steady - t_start, "steady_s": t_end - t_steady, "stats": stats, "tim": tim})
+            if instrumented:
+                tim = [eng.timing(t) for t in range(steps)]
+                timed_ms = (t_end - t_steady) * 1e3 / (steps - 1)
+            else:
+                runs.append({"cold_s": t_steady - t_start, "steady_s": t_end - t_steady, "stats": stats})
         eng.close()
         runs = runs[1:]
         best = min(runs, key=lambda r: r["steady_s"])
         ms_step = best["steady_s"] * 1e3 / (steps - 1)
-        st, tim = best["stats"], best["tim"]
+        st = best["stats"]
         delta = np.array([x["delta_bytes"] for x in st[1:]], np.float64)
         copy_ms = np.array([x["copy_ms"] for x in tim[1:]], np.float64)
         # the compute stream of step t+1 waits for step t's copies; what it
@@ -467,6 +475,7 @@ def offload_bench(args):
             "copy_mode": {H.COPY_KERNEL: "gather_kernel", H.COPY_DMA: "dma_memcpy",
                           H.COPY_KERNEL_GPU_PLAN: "gather_kernel_gpu_plan"}[copy_mode],
             "ms_per_step": round(ms_step, 6), "runs": len(runs),
+            "ms_per_step_with_timestamps": round(timed_ms, 6),
             "cold_ms": round(best["cold_s"] * 1e3, 3), "cold_bytes": st[0]["cold_bytes"],
             "delta_bytes_per_step": delta.tolist(), "delta_bytes_mean": float(delta.mean()),
             "full_set_bytes_per_step": full_bytes,
@@ -477,6 +486,7 @@ def offload_bench(args):
             "link": {"achieved": round(link_gbs, 2), "peak": PCIE_PEAK_GBS, "unit": "GB/s",
                      "frac": round(link_gbs / PCIE_PEAK_GBS, 4)},
             "compute_ms_mean": round(float(np.mean([x["compute_ms"] for x in tim[1:]])), 4),
+            "breakdown_from": "one extra run with per-step GPU timestamps (copy, wait, compute, link)",
             "host_wait_ms_mean": round(float(np.mean([x["host_wait_ms"] for x in st[1:]])), 4),
             "host_plan_ms_mean": round(float(np.mean([x["host_plan_ms"] for x in st[1:]])), 4),
             "host_call_ms_mean": round(float(np.mean([x["host_call_ms"] for x in st[1:]])), 4),
@@ -502,9 +512,11 @@ def offload_bench(args):
                       "cache": torch.zeros_like(cache), "slot_of": torch.full_like(slot_of, -1),
                       "tok": torch.empty_like(tok), "out": torch.empty_like(out), "lse": torch.empty_like(lse),
                       "ws": H.alloc_workspace(d), "eng": H.OffloadEngine(d, n_slots, H.COPY_KERNEL)})
-        best = None
-        for run in range(args.offload_runs + 1):
+        best, tim = None, None
+        for run in range(args.offload_runs + 2):   # as timed_runs: the last run records timestamps
+            instrumented = run == args.offload_runs + 1
             for x in L:
+                x["eng"].set_timing(instrumented)
                 x["meta"].copy_(meta0)
                 x["klabel"].copy_(klabel0)
             torch.cuda.synchronize()
@@ -521,12 +533,13 @@ def offload_bench(args):
                                   compute_stream=cs, copy_stream=xs)
             torch.cuda.synchronize()
             steady = time.perf_counter() - t_steady
-            tim = [[x["eng"].timing(t) for t in range(steps)] for x in L]
-            if run > 0 and (best is None or steady < best[0]):
-                best = (steady, tim)
+            if instrumented:
+                tim = [[x["eng"].timing(t) for t in range(steps)] for x in L]
+            elif run > 0 and (best is None or steady < best):
+                best = steady
         for x in L:
             x["eng"].close()
-        steady, tim = best
+        steady = best
         ms = steady * 1e3 / (steps - 1)
         copy_ms = sum(float(np.sum([x["copy_ms"] for x in tl[1:-1]])) for tl in tim)
         waits = sum(float(np.sum([x["copy_wait_ms"] for x in tl[2:]])) for tl in tim)

@@ -349,8 +349,15 @@ int hsab_offload_step(hsab_offload_engine* engine, const uint16_t* q, const uint
     return rc ? rc : (einval ? HSAB_EINVAL : HSAB_OK);
 }
 
+int hsab_offload_set_timing(hsab_offload_engine* engine, int32_t enable) {
+    if (!engine) return HSAB_EINVAL;
+    offload_set_timing(engine, enable != 0);
+    return HSAB_OK;
+}
+
 int hsab_offload_timing(hsab_offload_engine* engine, int64_t step, float* ms) {
-    if (!engine || !ms || step < 0 || step >= offload_steps(engine) || step < offload_steps(engine) - TIMING_RING)
+    if (!engine || !ms || step < 0 || step >= offload_steps(engine) || step < offload_steps(engine) - TIMING_RING ||
+        !offload_step_timed(engine, step))
         return HSAB_EINVAL;
     return hip_status(offload_timing(engine, step, ms));
 }

@@ -131,6 +131,8 @@ hipError_t offload_step(hsab_offload_engine* e, const uint16_t* q, const uint16_
                         int32_t* slot_of, int32_t* tok_idx, float* out, float* lse, void* ws, hipStream_t cs,
                         hipStream_t xs, hsab_offload_stats* st, int* einval);
 hipError_t offload_timing(hsab_offload_engine* e, int64_t step, float* ms4);
+void offload_set_timing(hsab_offload_engine* e, bool on);
+bool offload_step_timed(const hsab_offload_engine* e, int64_t step);
 const int32_t* offload_last_selection(hsab_offload_engine* e);
 hipError_t offload_step_delta(hsab_offload_engine* e, int64_t step, int64_t* delta_bytes, int64_t* cold_bytes);
 int64_t offload_steps(const hsab_offload_engine* e);

@@ -546,9 +546,15 @@ struct hsab_offload_engine {
     int32_t* rec_h = nullptr;                 // pinned coherent [TIMING_RING][2][U]
     int64_t ring_delta[hsab::TIMING_RING] = {}, ring_cold[hsab::TIMING_RING] = {};   // host-planned steps
     hipEvent_t ev_sel = nullptr, ev_copy[2] = {nullptr, nullptr};
-    // per step % TIMING_RING: compute begin, compute end, copy begin, copy
-    // end, and the compute stream before and after its wait for the copies
+    // per step % TIMING_RING, recorded only while timing is on (each timed
+    // record is a marker the GPU processes, ~1-3 us per step and record):
+    // compute begin, compute end, copy begin, copy end, and the compute
+    // stream before and after its wait for the copies
     hipEvent_t tm[hsab::TIMING_RING][6] = {};
+    bool timing = false;
+    bool ring_timed[hsab::TIMING_RING] = {};
+    // per step % TIMING_RING, GPU planning only: the step's copies are done
+    hipEvent_t done[hsab::TIMING_RING] = {};
 };
 
 namespace hsab {
@@ -573,6 +579,8 @@ void offload_destroy(hsab_offload_engine* e) {
     for (auto& row : e->tm)
         for (auto& ev : row)
             if (ev) (void)hipEventDestroy(ev);
+    for (auto& ev : e->done)
+        if (ev) (void)hipEventDestroy(ev);
     delete e;
 }
 
@@ -616,7 +624,7 @@ hipError_t offload_create(const Shape& s, int n_slots, int copy_mode, hsab_offlo
         ok(hipMalloc((void**)&e->plan_d[i], nsel * 3 * sizeof(int32_t)));
         ok(hipMalloc((void**)&e->list_d[i], nsel * 2 * sizeof(int32_t)));
         ok(hipMalloc((void**)&e->cnt_d[i], (size_t)e->U * sizeof(int32_t)));
-        ok(hipEventCreate(&e->ev_copy[i]));
+        ok(hipEventCreateWithFlags(&e->ev_copy[i], hipEventDisableTiming));
     }
     ok(hipEventCreateWithFlags(&e->ev_sel, hipEventDisableTiming));
     ok(hipMalloc((void**)&e->map_d, (size_t)e->U * s.nb_cap * sizeof(int32_t)));
@@ -626,6 +634,7 @@ hipError_t offload_create(const Shape& s, int n_slots, int copy_mode, hsab_offlo
 
     for (auto& row : e->tm)
         for (auto& ev : row) ok(hipEventCreate(&ev));
+    for (auto& ev : e->done) ok(hipEventCreateWithFlags(&ev, hipEventDisableTiming));
     if (r != hipSuccess) {
         offload_destroy(e);
         return r;
@@ -733,6 +742,9 @@ hipError_t offload_step(hsab_offload_engine* e, const uint16_t* q, const uint16_
     int32_t* sel_cnt = reinterpret_cast<int32_t*>(w + L.sel_cnt);
     const int ring = (int)(e->step % TIMING_RING);
     hipEvent_t* tm = e->tm[ring];
+    const bool timed = e->timing;
+    e->ring_timed[ring] = timed;
+    auto mark = [&](int i, hipStream_t s) { return timed ? hipEventRecord(tm[i], s) : hipSuccess; };
     int32_t* sel_now = e->sel_d[t & 1];
     const int32_t* resident = e->step == 0 ? sel_now : e->sel_d[(t - 1) & 1];
 
@@ -746,7 +758,7 @@ hipError_t offload_step(hsab_offload_engine* e, const uint16_t* q, const uint16_
     }
     uint16_t* pool_dev = e->pool_dev;
     int32_t* sel_map = e->sel_map;
-    HSAB_TRY(hipEventRecord(tm[0], cs));
+    HSAB_TRY(mark(0, cs));
     HSAB_TRY(launch_append_slot(s, e->n_slots, k_new, v_new, cache, meta, klabel, label_ch, ctx_len, cs, pool_dev));
     HSAB_TRY(launch_block_score(s, q, meta, ctx_len, blk_score, nullptr, nullptr, nullptr, nullptr, nullptr,
                                 nullptr, sel_cnt, cs));
@@ -756,14 +768,17 @@ hipError_t offload_step(hsab_offload_engine* e, const uint16_t* q, const uint16_
     HSAB_TRY(launch_select(s, 2, q, nullptr, klabel, label_ch, ctx_len, const_cast<int32_t*>(resident), tok_idx,
                            nullptr, sel_keys, sel_cnt, cs));
     auto attend_after = [&](hipEvent_t copies) -> hipError_t {
-        HSAB_TRY(hipEventRecord(tm[4], cs));
+        HSAB_TRY(mark(4, cs));
         HSAB_TRY(hipStreamWaitEvent(cs, copies, 0));
-        HSAB_TRY(hipEventRecord(tm[5], cs));
+        HSAB_TRY(mark(5, cs));
         HSAB_TRY(launch_attend(s, q, cache, cache, tok_idx, nullptr, s.kt, slot_of, e->n_slots, part_ml, part_acc,
                                out, lse, cs));
-        return hipEventRecord(tm[1], cs);
+        return mark(1, cs);
     };
-    if (e->step > 0) HSAB_TRY(attend_after(e->ev_copy[(t - 1) & 1]));
+    if (e->step > 0) {   // the previous step's copies: its done event (GPU planning) or its parity's copy event
+        const int prev_ring = (int)((e->step - 1) % TIMING_RING);
+        HSAB_TRY(attend_after(e->gpu_plan ? e->done[prev_ring] : e->ev_copy[(t - 1) & 1]));
+    }
 
     int64_t cold_bytes = 0, delta_bytes = 0;
     int copies = 0, calls = 0;
@@ -777,10 +792,10 @@ hipError_t offload_step(hsab_offload_engine* e, const uint16_t* q, const uint16_
             HSAB_TRY(hipEventRecord(e->ev_copy[1], xs));
             HSAB_TRY(attend_after(e->ev_copy[1]));
         }
-        HSAB_TRY(hipEventRecord(tm[2], xs));
+        HSAB_TRY(mark(2, xs));
         HSAB_TRY(gpu_plan_copy(e, t & 1, resident, sel_now, ctx_len, 1, pool_dev, cache, slot_of, rec, xs));
-        HSAB_TRY(hipEventRecord(tm[3], xs));
-        HSAB_TRY(hipEventRecord(e->ev_copy[t & 1], xs));
+        HSAB_TRY(mark(3, xs));
+        HSAB_TRY(hipEventRecord(e->done[ring], xs));
         for (int b = 0; b < s.B; ++b) e->n_ctx[b] += 1;
         e->ring_delta[ring] = e->ring_cold[ring] = -1;   // known once the copy stream gets there
         delta_bytes = cold_bytes = -1;
@@ -812,11 +827,11 @@ hipError_t offload_step(hsab_offload_engine* e, const uint16_t* q, const uint16_
             *einval = 1;
             return hipSuccess;
         }
-        HSAB_TRY(hipEventRecord(tm[2], xs));
+        HSAB_TRY(mark(2, xs));
         HSAB_TRY(offload_copy(s, e->n_slots, host_pool, cache, e->plan_h[t & 1], e->plan_d[t & 1], slot_of, xs,
                               e->ev_copy[t & 1], &calls, e->copy_mode, &e->mp[t & 1]));
         copies += calls;
-        HSAB_TRY(hipEventRecord(tm[3], xs));
+        HSAB_TRY(mark(3, xs));
         e->prev_sel.swap(e->cur_sel);
         e->ring_delta[ring] = delta_bytes;
         e->ring_cold[ring] = cold_bytes;
@@ -842,7 +857,7 @@ hipError_t offload_step(hsab_offload_engine* e, const uint16_t* q, const uint16_
 hipError_t offload_step_delta(hsab_offload_engine* e, int64_t step, int64_t* delta_bytes, int64_t* cold_bytes) {
     const int ring = (int)(step % TIMING_RING);
     if (e->ring_delta[ring] < 0) {
-        HSAB_TRY(hipEventSynchronize(e->tm[ring][3]));
+        HSAB_TRY(hipEventSynchronize(e->done[ring]));
         const int32_t* rec = e->rec_h + (size_t)ring * 2 * e->U;
         int64_t d = 0, c = 0;
         for (int u = 0; u < e->U; ++u) {
@@ -858,8 +873,12 @@ hipError_t offload_step_delta(hsab_offload_engine* e, int64_t step, int64_t* del
     return hipSuccess;
 }
 
-// GPU times of a finished step (within the last four), see
-// hsab_offload_timing. Waits for that step's events.
+// Timestamps for the steps enqueued from now on (off by default).
+void offload_set_timing(hsab_offload_engine* e, bool on) { e->timing = on; }
+bool offload_step_timed(const hsab_offload_engine* e, int64_t step) { return e->ring_timed[step % TIMING_RING]; }
+
+// GPU times of a finished step enqueued with timing on (within the last
+// TIMING_RING), see hsab_offload_timing. Waits for that step's events.
 hipError_t offload_timing(hsab_offload_engine* e, int64_t step, float* ms) {
     hipEvent_t* tm = e->tm[step % TIMING_RING];
     HSAB_TRY(hipEventSynchronize(tm[3]));

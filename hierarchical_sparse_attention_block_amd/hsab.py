@@ -26,7 +26,7 @@ EXPORTS = ("hsab_workspace_bytes", "hsab_status_string", "hsab_last_hip_error", 
            "hsab_score_blocks", "hsab_select_blocks", "hsab_select_tokens", "hsab_sparse_attend",
            "hsab_decode_step", "hsab_offload_append", "hsab_offload_plan", "hsab_offload_copy", "hsab_offload_create",
            "hsab_offload_destroy", "hsab_offload_begin", "hsab_offload_step", "hsab_offload_timing",
-           "hsab_offload_selection", "hsab_offload_step_delta", "hsab_dense_workspace_bytes", "hsab_dense_attend",
+           "hsab_offload_set_timing", "hsab_offload_selection", "hsab_offload_step_delta", "hsab_dense_workspace_bytes", "hsab_dense_attend",
            "hsab_calibrate_labels")
 
 
@@ -101,6 +101,7 @@ _lib.hsab_offload_destroy.argtypes = [_vp]
 _lib.hsab_offload_begin.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp]
 _lib.hsab_offload_step.argtypes = [_vp] * 16 + [_sz, _vp, _vp, ctypes.POINTER(OffloadStats)]
 _lib.hsab_offload_timing.argtypes = [_vp, ctypes.c_int64, _vp]
+_lib.hsab_offload_set_timing.argtypes = [_vp, ctypes.c_int32]
 _lib.hsab_offload_selection.argtypes = [_vp, _vp]
 _lib.hsab_offload_step_delta.argtypes = [_vp, ctypes.c_int64, _vp, _vp]
 for _f in EXPORTS[3:]:
@@ -419,6 +420,10 @@ class OffloadEngine:
         p = _hbuf("host_pool", host_pool, _u16, numel, pinned=True)
         self._pool_ok = key
         return p
+
+    def set_timing(self, enable: bool):
+        """Record per-step GPU timestamps (for timing()) from the next step on."""
+        _check("hsab_offload_set_timing", _lib.hsab_offload_set_timing(self._h, int(bool(enable))))
 
     def timing(self, step):
         ms = (ctypes.c_float * 5)()

@@ -396,12 +396,19 @@ int hsab_offload_step(hsab_offload_engine* engine, const uint16_t* q, const uint
                       void* ws, size_t ws_bytes, hipStream_t compute_stream, hipStream_t copy_stream,
                       hsab_offload_stats* stats);
 
-/* GPU times (ms) of a step among the last 32, waiting for them (ms has
- * 5 entries): ms[0] compute stream span of the step, ms[1] span of the
- * step's copies on the copy stream, ms[2] and ms[3] their start and end
- * relative to the step's compute start, ms[4] how long the compute stream
- * waited for the previous step's copies (the cold fill at step 0) before
- * its attention. */
+/* Per-step GPU timestamps for hsab_offload_timing, for the steps enqueued
+ * after this call while enable is nonzero. Off by default: the six timed
+ * event records of a step are markers the GPU processes in stream order,
+ * and cost the step several microseconds. HSAB_EINVAL for a null engine. */
+int hsab_offload_set_timing(hsab_offload_engine* engine, int32_t enable);
+
+/* GPU times (ms) of a step among the last 32 that was enqueued with timing
+ * on, waiting for them (ms has 5 entries): ms[0] compute stream span of the
+ * step, ms[1] span of the step's copies on the copy stream, ms[2] and ms[3]
+ * their start and end relative to the step's compute start, ms[4] how long
+ * the compute stream waited for the previous step's copies (the cold fill
+ * at step 0) before its attention. HSAB_EINVAL for a step outside that
+ * window or enqueued without timing. */
 int hsab_offload_timing(hsab_offload_engine* engine, int64_t step, float* ms);
 
 /* Host copy of the last step's S_b [B][Hkv][K_b] (ascending, -1 padded);

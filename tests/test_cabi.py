@@ -89,6 +89,7 @@ def test_null_pointers_rejected():
     assert H.raw_call("hsab_offload_step", n, *([p] * 15), 1 << 20, None, None, None) == H.HSAB_EINVAL
     assert H.raw_call("hsab_offload_begin", n, p, p, p, p, None) == H.HSAB_EINVAL
     assert H.raw_call("hsab_offload_timing", n, 0, p) == H.HSAB_EINVAL
+    assert H.raw_call("hsab_offload_set_timing", n, 1) == H.HSAB_EINVAL
     assert H.raw_call("hsab_offload_selection", n, p) == H.HSAB_EINVAL
     # unknown copy mode, misaligned pool
     assert H.raw_call("hsab_offload_copy", ctypes.byref(d), 18, p, p, p, p, p, 7, None, None, None) == H.HSAB_EINVAL

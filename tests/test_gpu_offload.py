@@ -14,6 +14,7 @@ import torch
 
 import oracle as O
 from hierarchical_sparse_attention_block_amd import workloads as W
+from hierarchical_sparse_attention_block_amd import hsab as H
 from hsab_testlib import check_index_set, dims_of, dev16, OUT_ATOL, LSE_RTOL
 
 pytestmark = pytest.mark.gpu
@@ -189,6 +190,34 @@ def test_offload_gqa_matches_lagged_oracle(copy_mode):
     K, V, qs, res = _run_offload(w, prefill, steps=12, copy_mode=copy_mode)
     _check_against_oracle(w, np.array(prefill), K, V, qs, res)
     assert sum(r["stats"]["delta_bytes"] for r in res[1:]) > 0, "the queries drift, so some blocks move"
+
+
+@pytest.mark.parametrize("copy_mode", [0, 2], ids=["host_plan", "gpu_plan"])
+def test_offload_timing_switch(copy_mode):
+    """Per-step GPU timestamps only for the steps enqueued with timing on;
+    the results stay those of the lagged oracle either way."""
+    w = W.WORKLOADS["tiny4k"].replace(name="offload_timing", batch=2, n_q_heads=8, n_kv_heads=2, k_blocks=8,
+                                      k_tokens=64, ctx=1024, max_ctx=1024, scaled_keys=True, n_planted=0,
+                                      seed=23)
+    prefill = [300, 700]
+    steps, on = 8, (2, 3, 5)
+    layer = _Layer(w, prefill, steps, None, copy_mode)
+    for t in range(steps):
+        layer.eng.set_timing(t in on)
+        st = layer.step(t)
+        torch.cuda.synchronize()
+        layer.collect(st)
+    for t in range(steps):
+        if t in on:
+            tm = layer.eng.timing(t)
+            assert tm["compute_ms"] > 0 and tm["copy_ms"] > 0, tm
+            assert tm["copy_end_ms"] >= tm["copy_start_ms"] and tm["copy_wait_ms"] >= 0, tm
+        else:
+            with pytest.raises(H.HsabError) as e:
+                layer.eng.timing(t)
+            assert e.value.status == H.HSAB_EINVAL
+    K, V, qs, res = layer.finish()
+    _check_against_oracle(w, np.array(prefill), K, V, qs, res)
 
 
 def test_offload_gqa_fp8_metadata():
