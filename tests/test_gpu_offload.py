@@ -193,6 +193,20 @@ def test_offload_gqa_matches_lagged_oracle(copy_mode):
 
 
 @pytest.mark.parametrize("copy_mode", [0, 2], ids=["host_plan", "gpu_plan"])
+def test_offload_short_contexts(copy_mode):
+    """Contexts of fewer blocks than K_b: S_b(t) is padded with -1, a row
+    starts inside its first block, one on a block boundary, and the tail
+    moves into a new block during the run."""
+    w = W.WORKLOADS["tiny4k"].replace(name="offload_short", batch=3, n_q_heads=8, n_kv_heads=2, k_blocks=8,
+                                      k_tokens=64, ctx=1024, max_ctx=1024, scaled_keys=True, n_planted=0,
+                                      seed=25)
+    prefill = [5, 16, 120]         # under one block, exactly one block, 7.5 blocks
+    K, V, qs, res = _run_offload(w, prefill, steps=12, copy_mode=copy_mode)
+    _check_against_oracle(w, np.array(prefill), K, V, qs, res)
+    assert (res[0]["sel"].reshape(3, 2, 8)[0] == -1).any(), "the first row selects fewer than K_b blocks"
+
+
+@pytest.mark.parametrize("copy_mode", [0, 2], ids=["host_plan", "gpu_plan"])
 def test_offload_timing_switch(copy_mode):
     """Per-step GPU timestamps only for the steps enqueued with timing on;
     the results stay those of the lagged oracle either way."""
