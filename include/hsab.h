@@ -339,8 +339,9 @@ int hsab_offload_copy(const hsab_dims* dims, int32_t n_slots, const uint16_t* ho
                       hipStream_t copy_stream, hipEvent_t done, int32_t* n_copies);
 
 /* Offload engine object: the lagged schedule above driven step by step.
- * It owns only small buffers (pinned copies of S_b and of the plan, the new
- * token's rows, two index buffers on the GPU) and events, allocated by
+ * It owns only small buffers (in coherent pinned memory S_b, the plans,
+ * copy lists and per-step copy counts; on the GPU the selections, plans,
+ * copy lists and slot map of the device planner) and events, allocated by
  * hsab_offload_create and freed by hsab_offload_destroy; the caller owns
  * the pool, the block cache, metadata, label rows and outputs. Unlike the
  * rest of the library, hsab_offload_step waits on the host (for S_b(t),
@@ -367,7 +368,9 @@ typedef struct hsab_offload_stats {
 /* n_slots >= 2*K_b + 2; copy_mode is HSAB_OFFLOAD_COPY_KERNEL, _DMA or
  * _KERNEL_GPU_PLAN (HSAB_EINVAL for the last when n_slots is beyond what
  * the device planner holds in LDS: 2*ceil((n_slots-2)/32) + K_b > 15360);
- * HSAB_EHIP if an allocation fails. */
+ * HSAB_EUNSUPPORTED for per-query-head selection (HSAB_AGG_HEAD: blocks
+ * move per KV head) and for shapes the attention does not take; HSAB_EHIP
+ * if an allocation fails. */
 int hsab_offload_create(const hsab_dims* dims, int32_t n_slots, int32_t copy_mode, hsab_offload_engine** engine);
 void hsab_offload_destroy(hsab_offload_engine* engine);
 
@@ -382,8 +385,7 @@ int hsab_offload_begin(hsab_offload_engine* engine, const int32_t* n_prefill, co
 /* Decode step t [de 2.B; es 2.B]: appends k_new/v_new (device, written to
  * the tail slot, meta, klabel, and by the same kernel to host_pool through
  * its device mapping; host_pool must be pinned, hipHostMalloc memory),
- * selects
- * S_b(t), runs the token stage and attention over R(t) = S_b(t-1) through
+ * selects S_b(t), runs the token stage and attention over R(t) = S_b(t-1) through
  * the block cache (R(0) = S_b(0) after a synchronous fill), and enqueues
  * the delta for step t+1 on copy_stream. ctx_len (device) and ctx_len_host
  * hold the same lengths, one more than at the previous step. tok_idx, out
