@@ -21,9 +21,12 @@ namespace {
 constexpr int UNION_THREADS = 1024;
 constexpr int UNION_LDS_WORDS = 15360;   // 60 KiB of head bitmaps per window
 
+// G: heads per group (compile time: a word's G head words are held in
+// registers while its bits are emitted, so the per-entry work is ALU only)
+template <int G>
 __global__ __launch_bounds__(UNION_THREADS) void union_kernel(const int32_t* __restrict__ tok_idx,
                                                               int32_t* __restrict__ union_idx,
-                                                              uint32_t* __restrict__ union_mask, int G, int kt,
+                                                              uint32_t* __restrict__ union_mask, int kt,
                                                               int max_ctx, int wph) {
     __shared__ uint32_t bits[UNION_LDS_WORDS];   // [G][wph]
     __shared__ uint32_t s_wsum[UNION_THREADS / 64];
@@ -51,6 +54,7 @@ __global__ __launch_bounds__(UNION_THREADS) void union_kernel(const int32_t* __r
         uint32_t cnt = 0;
         for (int k = k0; k < k1; ++k) {
             uint32_t u = 0;
+#pragma unroll
             for (int h = 0; h < G; ++h) u |= bits[h * wph + k];
             cnt += __popc(u);
         }
@@ -65,13 +69,18 @@ __global__ __launch_bounds__(UNION_THREADS) void union_kernel(const int32_t* __r
         }
         int at = base + (int)(before + incl - cnt);
         for (int k = k0; k < k1; ++k) {
-            uint32_t u = 0;
-            for (int h = 0; h < G; ++h) u |= bits[h * wph + k];
+            uint32_t hw[G], u = 0;
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                hw[h] = bits[h * wph + k];
+                u |= hw[h];
+            }
             while (u) {
                 const int bit = __ffs(u) - 1;
                 u &= u - 1;
                 uint32_t m = 0;
-                for (int h = 0; h < G; ++h) m |= ((bits[h * wph + k] >> bit) & 1u) << h;
+#pragma unroll
+                for (int h = 0; h < G; ++h) m |= ((hw[h] >> bit) & 1u) << h;
                 U[at] = w0 + k * 32 + bit;
                 M[at] = m;
                 ++at;
@@ -93,8 +102,18 @@ hipError_t launch_union(const Shape& s, const int32_t* tok_idx, int32_t* union_i
     const int words = (s.max_ctx + 31) / 32;
     const int cap = UNION_LDS_WORDS / s.G;
     const int wph = words < cap ? words : cap;
-    hipLaunchKernelGGL(union_kernel, dim3(s.B * s.Hkv), dim3(UNION_THREADS), 0, st, tok_idx, union_idx, union_mask,
-                       s.G, s.kt, s.max_ctx, wph);
+    const dim3 grid(s.B * s.Hkv), block(UNION_THREADS);
+    switch (s.G) {   // the group sizes the masked attention takes
+        case 1: hipLaunchKernelGGL(union_kernel<1>, grid, block, 0, st, tok_idx, union_idx, union_mask, s.kt,
+                                   s.max_ctx, wph); break;
+        case 2: hipLaunchKernelGGL(union_kernel<2>, grid, block, 0, st, tok_idx, union_idx, union_mask, s.kt,
+                                   s.max_ctx, wph); break;
+        case 4: hipLaunchKernelGGL(union_kernel<4>, grid, block, 0, st, tok_idx, union_idx, union_mask, s.kt,
+                                   s.max_ctx, wph); break;
+        case 8: hipLaunchKernelGGL(union_kernel<8>, grid, block, 0, st, tok_idx, union_idx, union_mask, s.kt,
+                                   s.max_ctx, wph); break;
+        default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 
