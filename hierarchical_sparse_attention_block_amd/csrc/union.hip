@@ -7,10 +7,14 @@
 // One 1024-thread workgroup per unit. The heads' lists are ascending token
 // positions (-1 padded); a window of positions gets one LDS bit set per
 // head (bit t of head h: head h kept token t), the words of the window are
-// OR-ed over the heads, counted and prefix-summed over the workgroup, and
-// every set bit becomes one union entry (its position, and the bits of the
-// heads that hold it as the mask). Windows cover max_ctx in turn, so the
-// union comes out ascending; the LDS per window is fixed (64 KiB).
+// OR-ed over the heads, counted and prefix-summed over the workgroup into
+// per-word entry offsets, and every set bit becomes one union entry (its
+// position, and the bits of the heads that hold it as the mask). Entries
+// are emitted by entry, not by word: thread e finds the word holding entry
+// e by binary search over the offsets and writes slot e, so the stores are
+// coalesced and the dense words (the kept tokens cluster in kept blocks)
+// are not left to a few lanes. Windows cover max_ctx in turn, so the union
+// comes out ascending; the LDS per window is fixed (60 KiB).
 #include "common.h"
 #include "kernels.h"
 
@@ -19,16 +23,16 @@ namespace hsab {
 namespace {
 
 constexpr int UNION_THREADS = 1024;
-constexpr int UNION_LDS_WORDS = 15360;   // 60 KiB of head bitmaps per window
+constexpr int UNION_LDS_WORDS = 15360;   // 60 KiB per window: head bitmaps [G][wph], word offsets [wph]
 
-// G: heads per group (compile time: a word's G head words are held in
-// registers while its bits are emitted, so the per-entry work is ALU only)
+// G: heads per group (compile time); (G + 1) * wph <= UNION_LDS_WORDS.
 template <int G>
 __global__ __launch_bounds__(UNION_THREADS) void union_kernel(const int32_t* __restrict__ tok_idx,
                                                               int32_t* __restrict__ union_idx,
                                                               uint32_t* __restrict__ union_mask, int kt,
                                                               int max_ctx, int wph) {
-    __shared__ uint32_t bits[UNION_LDS_WORDS];   // [G][wph]
+    __shared__ uint32_t bits[UNION_LDS_WORDS];   // [G][wph] head bitmaps, then [wph] word offsets
+    uint32_t* off = bits + G * wph;
     __shared__ uint32_t s_wsum[UNION_THREADS / 64];
     const int unit = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int E = G * kt;
@@ -67,24 +71,37 @@ __global__ __launch_bounds__(UNION_THREADS) void union_kernel(const int32_t* __r
             before += i < w ? x : 0u;
             total += x;
         }
-        int at = base + (int)(before + incl - cnt);
+        // entries before each of this thread's words
+        uint32_t run = before + incl - cnt;
         for (int k = k0; k < k1; ++k) {
+            off[k] = run;
+            uint32_t u = 0;
+#pragma unroll
+            for (int h = 0; h < G; ++h) u |= bits[h * wph + k];
+            run += __popc(u);
+        }
+        __syncthreads();
+        for (int e = tid; e < (int)total; e += UNION_THREADS) {
+            // the last word whose offset is <= e holds entry e (words past
+            // it start later; an empty word shares the next one's offset)
+            int lo = 0, hi = wph - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (off[mid] <= (uint32_t)e) lo = mid; else hi = mid - 1;
+            }
             uint32_t hw[G], u = 0;
 #pragma unroll
             for (int h = 0; h < G; ++h) {
-                hw[h] = bits[h * wph + k];
+                hw[h] = bits[h * wph + lo];
                 u |= hw[h];
             }
-            while (u) {
-                const int bit = __ffs(u) - 1;
-                u &= u - 1;
-                uint32_t m = 0;
+            for (uint32_t r = (uint32_t)e - off[lo]; r > 0; --r) u &= u - 1;   // drop the lower entries
+            const int bit = __ffs(u) - 1;
+            uint32_t m = 0;
 #pragma unroll
-                for (int h = 0; h < G; ++h) m |= ((hw[h] >> bit) & 1u) << h;
-                U[at] = w0 + k * 32 + bit;
-                M[at] = m;
-                ++at;
-            }
+            for (int h = 0; h < G; ++h) m |= ((hw[h] >> bit) & 1u) << h;
+            U[base + e] = w0 + lo * 32 + bit;
+            M[base + e] = m;
         }
         base += (int)total;
         __syncthreads();   // the next window reuses bits and s_wsum
@@ -100,7 +117,7 @@ __global__ __launch_bounds__(UNION_THREADS) void union_kernel(const int32_t* __r
 hipError_t launch_union(const Shape& s, const int32_t* tok_idx, int32_t* union_idx, uint32_t* union_mask,
                         hipStream_t st) {
     const int words = (s.max_ctx + 31) / 32;
-    const int cap = UNION_LDS_WORDS / s.G;
+    const int cap = UNION_LDS_WORDS / (s.G + 1);
     const int wph = words < cap ? words : cap;
     const dim3 grid(s.B * s.Hkv), block(UNION_THREADS);
     switch (s.G) {   // the group sizes the masked attention takes
