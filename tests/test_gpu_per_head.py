@@ -131,7 +131,15 @@ def test_per_head_attention_over_crafted_lists(G, max_ctx, seed):
     from hierarchical_sparse_attention_block_amd import hsab as H
     dm = H.dims(B, Hq, Hkv, d, d, False, 32, 16, 8, kt, max_ctx, 1 / math.sqrt(d), group_agg=H.AGG_HEAD)
     tok = np.full((B, Hq, kt), -1, np.int32)
-    shared = np.sort(rng.choice(max_ctx, kt, replace=False))
+    # the shared list holds the positions around the union kernel's window
+    # edges (windows of (15360 // (G + 1)) * 32 positions: 60 KiB of LDS
+    # for G head bitmaps and one offset per word) and the context's ends
+    span = (15360 // (G + 1)) * 32
+    edges = {p for p in (0, 31, 32, span - 1, span, span + 1, 2 * span - 1, 2 * span, max_ctx - 2, max_ctx - 1)
+             if 0 <= p < max_ctx}
+    rest = np.setdiff1d(np.arange(max_ctx), np.array(sorted(edges)))
+    shared = np.sort(np.concatenate([np.array(sorted(edges)),
+                                     rng.choice(rest, kt - len(edges), replace=False)])).astype(np.int64)
     for b in range(B):
         for a in range(Hq):
             kind = (a + b) % 4
