@@ -98,7 +98,7 @@ __all__ = [
     "bf16_to_f64", "n_blocks", "block_meta", "append_meta", "quest_bound",
     "quest_bound_gemm", "block_scores", "topk_stable", "candidate_tokens",
     "label_scores", "attend", "select_tokens_unit", "decode_unit", "select_blocks",
-    "e4m3_grid", "e4m3_round", "e4m3_round_nearest", "block_meta_e4m3", "calibrate_labels",
+    "e4m3_grid", "e4m3_round", "e4m3_round_nearest", "block_meta_e4m3", "label_importance", "calibrate_labels",
     "decode_unit_heads", "token_union", "decode_all", "offload_delta", "offload_held", "offload_schedule", "offload_run",
 ]
 
@@ -277,13 +277,18 @@ def label_scores(q: np.ndarray, K_rows: np.ndarray, label_ch: np.ndarray, agg: s
     return s.sum(axis=0) if agg == "sum" else s.max(axis=0)
 
 
+def label_importance(q_samples: np.ndarray, k_samples: np.ndarray) -> np.ndarray:
+    """Channel importance of one KV head from sampled activations: for each
+    channel c the sum over samples s and the group's query heads h of
+    |q[s,h,c] * k[s,c]|. q_samples [S, G, d], k_samples [S, d] float64;
+    returns [d]."""
+    return np.abs(q_samples * k_samples[:, None, :]).sum(axis=(0, 1))
+
+
 def calibrate_labels(q_samples: np.ndarray, k_samples: np.ndarray, r: int) -> np.ndarray:
-    """Label channels of one KV head from sampled activations: channel
-    importance = sum over samples s and the group's query heads h of
-    |q[s,h,c] * k[s,c]|; the r most important channels, ties to the lower
-    channel, ascending. q_samples [S, G, d], k_samples [S, d] float64."""
-    imp = np.abs(q_samples * k_samples[:, None, :]).sum(axis=(0, 1))
-    return topk_stable(imp, r)
+    """Label channels of one KV head: the r channels of largest
+    ``label_importance``, ties to the lower channel, ascending."""
+    return topk_stable(label_importance(q_samples, k_samples), r)
 
 
 # ------------------------------------------------------ step 6: attention

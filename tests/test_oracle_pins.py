@@ -44,6 +44,27 @@ def _rand_unit(seed, G, d, n, dv=None, scale=1.0):
     return q, K, V
 
 
+# ------------------------------------------------------------------ bf16 input
+def test_bf16_to_f64_matches_torch_on_every_pattern():
+    """The oracle's bf16 decoder against torch's own bfloat16 type on all
+    65,536 bit patterns: every finite value, both zeros (with their signs)
+    and both infinities equal torch's widening; NaN patterns decode to NaN."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    with np.errstate(invalid="ignore"):        # NaN patterns pass through the fp32 widening
+        got = O.bf16_to_f64(bits)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert nan.sum() == 2 * 127                      # exponent all ones, mantissa nonzero
+    np.testing.assert_array_equal(np.isnan(got), nan)
+    np.testing.assert_array_equal(got[~nan], ref[~nan])
+    np.testing.assert_array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+    # landmarks of the format: 1.0, -2.0, the largest finite value, the
+    # smallest normal and subnormal numbers
+    for b, v in [(0x3F80, 1.0), (0xC000, -2.0), (0x7F7F, (2 - 2 ** -7) * 2.0 ** 127),
+                 (0x0080, 2.0 ** -126), (0x0001, 2.0 ** -133), (0x7F80, np.inf)]:
+        assert O.bf16_to_f64(np.array([b], np.uint16))[0] == v
+
+
 # ------------------------------------------------------------ golden examples
 def test_worked_example_every_stage():
     g = _read_golden("worked_example.txt")
@@ -238,6 +259,28 @@ def test_decode_all_maps_query_heads_to_kv_heads():
         np.testing.assert_allclose(got, ref.numpy(), rtol=0, atol=1e-12)
 
 
+def test_decode_all_aliased_values_equal_sdpa():
+    """Absorbed latent layout: values are the first d_v dims of each key row
+    (decode_all given the int d_v instead of a V array). With every token
+    kept the result is SDPA with V = K[:, :d_v], per batch row, for every
+    query head of the one latent KV head."""
+    B, Hq, d, dv, n = 2, 4, 24, 16, 19
+    rng = np.random.default_rng(12)
+    qb = W.f32_to_bf16_bits(rng.standard_normal((B, Hq, d)).astype(np.float32))
+    Kb = W.f32_to_bf16_bits(rng.standard_normal((B, 1, 32, d)).astype(np.float32))
+    ctx = np.array([n, 7])
+    res = O.decode_all(qb, Kb, dv, ctx, 1, 4, 100, np.arange(4)[None, :], 100, 0.2)
+    q = torch.tensor(O.bf16_to_f64(qb))
+    K = torch.tensor(O.bf16_to_f64(Kb))
+    for b in range(B):
+        m = int(ctx[b])
+        k = K[b, 0, :m]
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            q[b][:, None], k[None].expand(Hq, -1, -1), k[None, :, :dv].expand(Hq, -1, -1), scale=0.2)[:, 0]
+        assert res[(b, 0)]["out"].shape == (Hq, dv)
+        np.testing.assert_allclose(res[(b, 0)]["out"], ref.numpy(), rtol=0, atol=1e-12)
+
+
 def test_lse_merges_disjoint_token_sets():
     """lse is the true log-partition: attention over A u B equals the
     lse-weighted merge of attention over A and over B."""
@@ -332,6 +375,35 @@ def test_offload_run_attends_over_previous_selection():
         assert r["delta_bytes"] == len(r["delta"]) * bs * 2 * d * 2
         # every transferred block was selected at this step
         assert set(r["delta"]) <= set(r["sel"])
+
+
+def test_offload_run_bytes_on_forced_selections():
+    """offload_run end to end on a unit whose block selections are forced:
+    block j (block 4) holds keys A*e_j, so the bound of block j for a 0/1
+    query is A where the query has a one at channel j and 0 elsewhere, and
+    top-K_b with K_b = the query's weight keeps exactly those blocks. The
+    selections are the hand-worked schedule above ({0,1,2}, {1,2}, {0,2},
+    {1,3}; prefill 9, contexts 10..13), so the transfers are counted by
+    hand: cold fill blocks {0,1}, then 0, 0, 1 and 1 blocks. A block is
+    4 tokens of d_k + d_v = 8 + 8 bf16 values: 4 * 16 * 2 = 128 bytes
+    (64 with values aliased to the keys)."""
+    d, bs, A = 8, 4, 5.0
+    K = np.zeros((16, d))
+    for j in range(4):
+        K[4 * j:4 * j + 4, j] = A
+    V = _bf16(np.random.default_rng(3).standard_normal((16, d)))
+    want = [[0, 1, 2], [1, 2], [0, 2], [1, 3]]
+    steps = []
+    for t, sel in enumerate(want):
+        q = np.zeros((2, d))
+        q[0, sel] = 1.0
+        steps.append((q, K, V, 10 + t, len(sel), np.arange(4), 8, 0.5))
+    for alias, per_block in [(False, 128), (True, 64)]:
+        res = O.offload_run(steps, bs, d, d, v_alias=alias)
+        assert [list(r["sel"]) for r in res] == want
+        assert res[0]["cold_bytes"] == 2 * per_block
+        assert [r["delta_bytes"] for r in res] == [0, 0, per_block, per_block]
+        assert [r["cold_bytes"] for r in res[1:]] == [0, 0, 0]
 
 
 # ------------------------------------------- quantised metadata (fp8 e4m3)
