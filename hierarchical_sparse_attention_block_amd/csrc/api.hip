@@ -91,19 +91,19 @@ static int hip_status(hipError_t e) {
 // are merged into their union (with head masks) in the workspace first
 // (with one head per group the list is already its own union).
 static int attend_step(const Shape& s, const uint16_t* q, const uint16_t* K, const uint16_t* V,
-                       const int32_t* tok_idx, const int32_t* slot_of, int n_slots, char* w, const WsLayout& L,
-                       float* out, float* lse, hipStream_t stream) {
+                       const int32_t* tok_idx, const int32_t* ctx_len, const int32_t* slot_of, int n_slots, char* w,
+                       const WsLayout& L, float* out, float* lse, hipStream_t stream) {
     const int32_t* list = tok_idx;
     const uint32_t* mask = nullptr;
     if (s.heads > 1) {
         int32_t* uidx = reinterpret_cast<int32_t*>(w + L.union_idx);
         uint32_t* umask = reinterpret_cast<uint32_t*>(w + L.union_mask);
-        const int rc = hip_status(launch_union(s, tok_idx, uidx, umask, stream));
+        const int rc = hip_status(launch_union(s, tok_idx, ctx_len, uidx, umask, stream));
         if (rc) return rc;
         list = uidx;
         mask = umask;
     }
-    return hip_status(launch_attend(s, q, K, V, list, mask, attn_list_len(s), slot_of, n_slots,
+    return hip_status(launch_attend(s, q, K, V, list, mask, attn_list_len(s), ctx_len, slot_of, n_slots,
                                     reinterpret_cast<float*>(w + L.part_ml),
                                     reinterpret_cast<float*>(w + L.part_acc), out, lse, stream));
 }
@@ -186,18 +186,17 @@ int hsab_sparse_attend(const hsab_dims* dims, const uint16_t* q, const uint16_t*
                        const uint16_t* V, const int32_t* tok_idx, const int32_t* ctx_len,
                        const int32_t* slot_of, int32_t n_slots, float* out, float* lse, void* ws,
                        size_t ws_bytes, hipStream_t stream) {
-    (void)ctx_len;
     int rc = check_dims(dims);
     if (rc) return rc;
     const Shape s = make_shape(*dims);
-    if (!q || !K || !tok_idx || !out || !lse) return HSAB_EINVAL;
+    if (!q || !K || !tok_idx || !ctx_len || !out || !lse) return HSAB_EINVAL;
     if (!s.valias && !V && !slot_of) return HSAB_EINVAL;   // a block cache carries its values
     if (slot_of && n_slots < 1) return HSAB_EINVAL;
     const WsLayout L = ws_layout(s);
     if (!ws || ws_bytes < L.total) return HSAB_EINVAL;
     if (!attend_supported(s)) return HSAB_EUNSUPPORTED;
     char* w = static_cast<char*>(ws);
-    return attend_step(s, q, K, s.valias ? K : V, tok_idx, slot_of, n_slots, w, L, out, lse, stream);
+    return attend_step(s, q, K, s.valias ? K : V, tok_idx, ctx_len, slot_of, n_slots, w, L, out, lse, stream);
 }
 
 int hsab_decode_step(const hsab_dims* dims, const uint16_t* q, const uint16_t* k_new,
@@ -227,7 +226,7 @@ int hsab_decode_step(const hsab_dims* dims, const uint16_t* q, const uint16_t* k
     rc = hip_status(launch_select(s, 3, q, scores, klabel, label_ch, ctx_len, blk_idx, tok_idx, nullptr,
                                   sel_keys, sel_cnt, stream));
     if (rc) return rc;
-    return attend_step(s, q, K, s.valias ? K : V, tok_idx, nullptr, 0, w, L, out, lse, stream);
+    return attend_step(s, q, K, s.valias ? K : V, tok_idx, ctx_len, nullptr, 0, w, L, out, lse, stream);
 }
 
 int hsab_calibrate_labels(const hsab_dims* dims, const uint16_t* q_samples, const uint16_t* k_samples,
@@ -366,6 +365,17 @@ int hsab_offload_selection(const hsab_offload_engine* engine, int32_t* blk_idx_h
     if (!engine || !blk_idx_host || offload_steps(engine) < 1) return HSAB_EINVAL;
     const Shape& s = offload_shape(engine);
     const int32_t* sel = offload_last_selection(const_cast<hsab_offload_engine*>(engine));
+    if (!sel) return HSAB_EHIP;
+    memcpy(blk_idx_host, sel, (size_t)s.B * s.Hkv * s.kb * sizeof(int32_t));
+    return HSAB_OK;
+}
+
+int hsab_offload_step_selection(hsab_offload_engine* engine, int64_t step, int32_t* blk_idx_host) {
+    if (!engine || !blk_idx_host || step < 0 || step >= offload_steps(engine) ||
+        step < offload_steps(engine) - TIMING_RING)
+        return HSAB_EINVAL;
+    const Shape& s = offload_shape(engine);
+    const int32_t* sel = offload_step_selection(engine, step);
     if (!sel) return HSAB_EHIP;
     memcpy(blk_idx_host, sel, (size_t)s.B * s.Hkv * s.kb * sizeof(int32_t));
     return HSAB_OK;

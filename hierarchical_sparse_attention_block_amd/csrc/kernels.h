@@ -70,13 +70,14 @@ bool attend_supported(const Shape& s);
 // Per-head selection: the ascending union of the G token lists of each
 // unit ([U][G][K_t] -> [U][G*K_t], -1 padded) and, per entry, the bit mask
 // of the heads that selected it.
-hipError_t launch_union(const Shape& s, const int32_t* tok_idx, int32_t* union_idx, uint32_t* union_mask,
-                        hipStream_t st);
+hipError_t launch_union(const Shape& s, const int32_t* tok_idx, const int32_t* ctx_len, int32_t* union_idx,
+                        uint32_t* union_mask, hipStream_t st);
 // Split attention over the kept tokens, then the merge of the partials.
 // tok_idx: [U][list_len]; tok_mask (nullable): per entry the query heads
-// of the group that attend it (all when null).
+// of the group that attend it (all when null); entries at or past
+// ctx_len[b] are skipped.
 hipError_t launch_attend(const Shape& s, const uint16_t* q, const uint16_t* K, const uint16_t* V,
-                         const int32_t* tok_idx, const uint32_t* tok_mask, int list_len,
+                         const int32_t* tok_idx, const uint32_t* tok_mask, int list_len, const int32_t* ctx_len,
                          const int32_t* slot_of, int n_slots, float* part_ml, float* part_acc, float* out,
                          float* lse, hipStream_t st);
 
@@ -100,7 +101,8 @@ hipError_t launch_calibrate(const Shape& s, const uint16_t* q_samples, const uin
 constexpr int TIMING_RING = 32;
 hipError_t launch_append_slot(const Shape& s, int n_slots, const uint16_t* k_new, const uint16_t* v_new,
                               uint16_t* cache, uint16_t* meta, uint16_t* klabel, const int32_t* label_ch,
-                              const int32_t* ctx_len, hipStream_t st, uint16_t* pool_dev = nullptr);
+                              const int32_t* ctx_len, hipStream_t st, uint16_t* pool_dev = nullptr,
+                              int32_t* ctx_copy = nullptr);
 int offload_plan(const Shape& s, int n_slots, const int32_t* resident, const int32_t* selected,
                  const int32_t* tail, int32_t* slot_map, int32_t* plan, int64_t* delta_bytes);
 constexpr int OFFLOAD_COPY_KERNEL = HSAB_OFFLOAD_COPY_KERNEL;
@@ -134,6 +136,7 @@ hipError_t offload_timing(hsab_offload_engine* e, int64_t step, float* ms4);
 void offload_set_timing(hsab_offload_engine* e, bool on);
 bool offload_step_timed(const hsab_offload_engine* e, int64_t step);
 const int32_t* offload_last_selection(hsab_offload_engine* e);
+const int32_t* offload_step_selection(hsab_offload_engine* e, int64_t step);
 hipError_t offload_step_delta(hsab_offload_engine* e, int64_t step, int64_t* delta_bytes, int64_t* cold_bytes);
 int64_t offload_steps(const hsab_offload_engine* e);
 const Shape& offload_shape(const hsab_offload_engine* e);

@@ -26,14 +26,17 @@ namespace {
 
 // grid: (B*Hkv), one workgroup per unit. Appends the token at position
 // ctx_len[b]-1 into the tail slot of its block, widens that block's
-// max/min and writes its label row.
+// max/min and writes its label row. ctx_copy (nullable) receives ctx_len:
+// the copy stream's planner reads that snapshot, never the caller's
+// buffer, which the caller may change once the compute stream is past it.
 __global__ __launch_bounds__(256) void append_slot_kernel(
     const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new, uint16_t* __restrict__ cache,
     uint16_t* __restrict__ meta, uint16_t* __restrict__ klabel, const int32_t* __restrict__ label_ch,
-    const int32_t* __restrict__ ctx_len, uint16_t* __restrict__ pool, int Hkv, int dk, int dv, int valias, int bs,
-    int r, int max_ctx, int nb_cap, int n_slots, int meta8, int lab8) {
+    const int32_t* __restrict__ ctx_len, uint16_t* __restrict__ pool, int32_t* __restrict__ ctx_copy, int Hkv,
+    int dk, int dv, int valias, int bs, int r, int max_ctx, int nb_cap, int n_slots, int meta8, int lab8) {
     const int unit = blockIdx.x, b = unit / Hkv, g = unit % Hkv;
     const int pos = ctx_len[b] - 1;
+    if (ctx_copy && g == 0 && threadIdx.x == 0) ctx_copy[b] = pos + 1;
     if (pos < 0 || pos >= max_ctx) return;
     const int j = pos / bs, off = pos - j * bs;
     const bool first = off == 0;
@@ -336,10 +339,10 @@ __global__ __launch_bounds__(256) void gather_kernel(const int32_t* __restrict__
 
 hipError_t launch_append_slot(const Shape& s, int n_slots, const uint16_t* k_new, const uint16_t* v_new,
                               uint16_t* cache, uint16_t* meta, uint16_t* klabel, const int32_t* label_ch,
-                              const int32_t* ctx_len, hipStream_t st, uint16_t* pool_dev) {
+                              const int32_t* ctx_len, hipStream_t st, uint16_t* pool_dev, int32_t* ctx_copy) {
     hipLaunchKernelGGL(append_slot_kernel, dim3(s.B * s.Hkv), dim3(256), 0, st, k_new, v_new, cache, meta, klabel,
-                       label_ch, ctx_len, pool_dev, s.Hkv, s.dk, s.dv, s.valias, s.bs, s.r, s.max_ctx, s.nb_cap,
-                       n_slots, s.meta8, s.lab8);
+                       label_ch, ctx_len, pool_dev, ctx_copy, s.Hkv, s.dk, s.dv, s.valias, s.bs, s.r, s.max_ctx,
+                       s.nb_cap, n_slots, s.meta8, s.lab8);
     return hipGetLastError();
 }
 
@@ -525,15 +528,22 @@ struct hsab_offload_engine {
     std::vector<int32_t> n_ctx, jp;           // [B] tokens so far, last prefill block
     std::vector<int32_t> prev_sel, cur_sel;   // [U][K_b] S_b(t-1), S_b(t)
     std::vector<int32_t> none, slot_map, tail;
-    int32_t* sel_h = nullptr;                 // pinned [U][K_b]
-    int32_t* sel_map = nullptr;               // sel_h's device address
+    // pinned coherent [TIMING_RING][U][K_b]: S_b of each of the last steps,
+    // written by the selection kernel through the mapping (sel_map)
+    int32_t* sel_h = nullptr;
+    int32_t* sel_map = nullptr;
     const uint16_t* pool_h = nullptr;         // the last pool seen, and its device address
     uint16_t* pool_dev = nullptr;
     int32_t* plan_h[2] = {nullptr, nullptr};  // pinned coherent [U][K_b][3]
     int32_t* list_h[2] = {nullptr, nullptr};  // pinned coherent [U][K_b][2]: host-planned copy lists
     int32_t* cnt_h[2] = {nullptr, nullptr};   // pinned coherent [U]
     hsab::MappedPlan mp[2];                   // the above with their device addresses
-    int32_t* sel_d[2] = {nullptr, nullptr};   // device [U][K_b]
+    // device [U][K_b] selections, a ring of three: step t writes sel_d[t % 3]
+    // while the copy stream may still plan step t-1 from sel_d[(t-2) % 3]
+    // (its R) and sel_d[(t-1) % 3]; step t's attention waits for step t-1's
+    // copies, so step t+1 reuses sel_d[(t-2) % 3] only after that plan ran
+    int32_t* sel_d[3] = {nullptr, nullptr, nullptr};
+    int32_t* ctx_d[2] = {nullptr, nullptr};   // device [B]: ctx_len of the step's parity, for the planner
     int32_t* plan_d[2] = {nullptr, nullptr};  // device [U][K_b][3]
     // planning on the GPU (kernel copies): the slot map, the last prefill
     // block per sequence, per-unit copy lists and counts, and per step the
@@ -565,11 +575,13 @@ void offload_destroy(hsab_offload_engine* e) {
     if (e->rec_h) (void)hipHostFree(e->rec_h);
     if (e->map_d) (void)hipFree(e->map_d);
     if (e->jp_d) (void)hipFree(e->jp_d);
+    for (int i = 0; i < 3; ++i)
+        if (e->sel_d[i]) (void)hipFree(e->sel_d[i]);
     for (int i = 0; i < 2; ++i) {
+        if (e->ctx_d[i]) (void)hipFree(e->ctx_d[i]);
         if (e->plan_h[i]) (void)hipHostFree(e->plan_h[i]);
         if (e->list_h[i]) (void)hipHostFree(e->list_h[i]);
         if (e->cnt_h[i]) (void)hipHostFree(e->cnt_h[i]);
-        if (e->sel_d[i]) (void)hipFree(e->sel_d[i]);
         if (e->plan_d[i]) (void)hipFree(e->plan_d[i]);
         if (e->list_d[i]) (void)hipFree(e->list_d[i]);
         if (e->cnt_d[i]) (void)hipFree(e->cnt_d[i]);
@@ -603,8 +615,10 @@ hipError_t offload_create(const Shape& s, int n_slots, int copy_mode, hsab_offlo
     hipError_t r = hipSuccess;
     auto ok = [&](hipError_t x) { if (r == hipSuccess) r = x; };
     // coherent: the selection kernel writes S_b(t) here through the mapping
-    ok(hipHostMalloc((void**)&e->sel_h, nsel * sizeof(int32_t), hipHostMallocMapped | hipHostMallocCoherent));
+    ok(hipHostMalloc((void**)&e->sel_h, (size_t)TIMING_RING * nsel * sizeof(int32_t),
+                     hipHostMallocMapped | hipHostMallocCoherent));
     if (r == hipSuccess) ok(hipHostGetDevicePointer((void**)&e->sel_map, e->sel_h, 0));
+    for (int i = 0; i < 3; ++i) ok(hipMalloc((void**)&e->sel_d[i], nsel * sizeof(int32_t)));
     for (int i = 0; i < 2; ++i) {
         // coherent: the gather kernel reads the plan in place while the host
         // writes the other parity's
@@ -620,7 +634,7 @@ hipError_t offload_create(const Shape& s, int n_slots, int copy_mode, hsab_offlo
         ok(hipHostGetDevicePointer((void**)&m.plan_dev, e->plan_h[i], 0));
         ok(hipHostGetDevicePointer((void**)&m.list_dev, e->list_h[i], 0));
         ok(hipHostGetDevicePointer((void**)&m.cnt_dev, e->cnt_h[i], 0));
-        ok(hipMalloc((void**)&e->sel_d[i], nsel * sizeof(int32_t)));
+        ok(hipMalloc((void**)&e->ctx_d[i], (size_t)s.B * sizeof(int32_t)));
         ok(hipMalloc((void**)&e->plan_d[i], nsel * 3 * sizeof(int32_t)));
         ok(hipMalloc((void**)&e->list_d[i], nsel * 2 * sizeof(int32_t)));
         ok(hipMalloc((void**)&e->cnt_d[i], (size_t)e->U * sizeof(int32_t)));
@@ -745,8 +759,9 @@ hipError_t offload_step(hsab_offload_engine* e, const uint16_t* q, const uint16_
     const bool timed = e->timing;
     e->ring_timed[ring] = timed;
     auto mark = [&](int i, hipStream_t s) { return timed ? hipEventRecord(tm[i], s) : hipSuccess; };
-    int32_t* sel_now = e->sel_d[t & 1];
-    const int32_t* resident = e->step == 0 ? sel_now : e->sel_d[(t - 1) & 1];
+    int32_t* sel_now = e->sel_d[e->step % 3];
+    const int32_t* resident = e->step == 0 ? sel_now : e->sel_d[(e->step - 1) % 3];
+    int32_t* ctx_snap = e->ctx_d[t & 1];
 
     // ---- compute stream, up to the token stage. The append also writes the
     // new rows into the pool, and the block selection writes S_b(t) into
@@ -757,9 +772,10 @@ hipError_t offload_step(hsab_offload_engine* e, const uint16_t* q, const uint16_
         e->mp[0].pool_dev = e->mp[1].pool_dev = e->pool_dev;
     }
     uint16_t* pool_dev = e->pool_dev;
-    int32_t* sel_map = e->sel_map;
+    int32_t* sel_map = e->sel_map + (size_t)ring * nsel;
     HSAB_TRY(mark(0, cs));
-    HSAB_TRY(launch_append_slot(s, e->n_slots, k_new, v_new, cache, meta, klabel, label_ch, ctx_len, cs, pool_dev));
+    HSAB_TRY(launch_append_slot(s, e->n_slots, k_new, v_new, cache, meta, klabel, label_ch, ctx_len, cs, pool_dev,
+                                ctx_snap));
     HSAB_TRY(launch_block_score(s, q, meta, ctx_len, blk_score, nullptr, nullptr, nullptr, nullptr, nullptr,
                                 nullptr, sel_cnt, cs));
     HSAB_TRY(launch_select(s, 1, q, blk_score, nullptr, nullptr, ctx_len, sel_now, nullptr, nullptr, nullptr,
@@ -771,7 +787,7 @@ hipError_t offload_step(hsab_offload_engine* e, const uint16_t* q, const uint16_
         HSAB_TRY(mark(4, cs));
         HSAB_TRY(hipStreamWaitEvent(cs, copies, 0));
         HSAB_TRY(mark(5, cs));
-        HSAB_TRY(launch_attend(s, q, cache, cache, tok_idx, nullptr, s.kt, slot_of, e->n_slots, part_ml, part_acc,
+        HSAB_TRY(launch_attend(s, q, cache, cache, tok_idx, nullptr, s.kt, ctx_len, slot_of, e->n_slots, part_ml, part_acc,
                                out, lse, cs));
         return mark(1, cs);
     };
@@ -788,12 +804,12 @@ hipError_t offload_step(hsab_offload_engine* e, const uint16_t* q, const uint16_
         int32_t* rec = e->rec_h + (size_t)ring * 2 * U;
         HSAB_TRY(hipStreamWaitEvent(xs, e->ev_sel, 0));
         if (e->step == 0) {   // cold start: S_b(0) is also R(0)
-            HSAB_TRY(gpu_plan_copy(e, 1, nullptr, sel_now, ctx_len, 0, pool_dev, cache, slot_of, rec + U, xs));
+            HSAB_TRY(gpu_plan_copy(e, 1, nullptr, sel_now, ctx_snap, 0, pool_dev, cache, slot_of, rec + U, xs));
             HSAB_TRY(hipEventRecord(e->ev_copy[1], xs));
             HSAB_TRY(attend_after(e->ev_copy[1]));
         }
         HSAB_TRY(mark(2, xs));
-        HSAB_TRY(gpu_plan_copy(e, t & 1, resident, sel_now, ctx_len, 1, pool_dev, cache, slot_of, rec, xs));
+        HSAB_TRY(gpu_plan_copy(e, t & 1, resident, sel_now, ctx_snap, 1, pool_dev, cache, slot_of, rec, xs));
         HSAB_TRY(mark(3, xs));
         HSAB_TRY(hipEventRecord(e->done[ring], xs));
         for (int b = 0; b < s.B; ++b) e->n_ctx[b] += 1;
@@ -806,7 +822,7 @@ hipError_t offload_step(hsab_offload_engine* e, const uint16_t* q, const uint16_
         t0 = clk::now();
         HSAB_TRY(hipEventSynchronize(e->ev_sel));
         t1 = clk::now();
-        std::memcpy(e->cur_sel.data(), e->sel_h, nsel * sizeof(int32_t));
+        std::memcpy(e->cur_sel.data(), e->sel_h + (size_t)ring * nsel, nsel * sizeof(int32_t));
         for (int b = 0; b < s.B; ++b) e->n_ctx[b] += 1;
         if (e->step == 0) {   // cold start: fill S_b(0) synchronously
             for (int u = 0; u < U; ++u) tail_blocks(e->n_ctx[u / s.Hkv], e->jp[u / s.Hkv], s.bs, &e->tail[2 * u]);
@@ -896,7 +912,16 @@ hipError_t offload_timing(hsab_offload_engine* e, int64_t step, float* ms) {
 const int32_t* offload_last_selection(hsab_offload_engine* e) {
     if (!e->gpu_plan) return e->prev_sel.data();
     if (hipEventSynchronize(e->ev_sel) != hipSuccess) return nullptr;
-    return e->sel_h;
+    return e->sel_h + (size_t)((e->step - 1) % TIMING_RING) * e->U * e->s.kb;
+}
+
+// S_b of a step among the last TIMING_RING. With host planning the host
+// waited for it when the step was enqueued; with GPU planning the step's
+// copies (planned from it) are waited for.
+const int32_t* offload_step_selection(hsab_offload_engine* e, int64_t step) {
+    const int ring = (int)(step % TIMING_RING);
+    if (e->gpu_plan && hipEventSynchronize(e->done[ring]) != hipSuccess) return nullptr;
+    return e->sel_h + (size_t)ring * e->U * e->s.kb;
 }
 int64_t offload_steps(const hsab_offload_engine* e) { return e->step; }
 const Shape& offload_shape(const hsab_offload_engine* e) { return e->s; }

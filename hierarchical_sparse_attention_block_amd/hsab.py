@@ -26,7 +26,8 @@ EXPORTS = ("hsab_workspace_bytes", "hsab_status_string", "hsab_last_hip_error", 
            "hsab_score_blocks", "hsab_select_blocks", "hsab_select_tokens", "hsab_sparse_attend",
            "hsab_decode_step", "hsab_offload_append", "hsab_offload_plan", "hsab_offload_copy", "hsab_offload_create",
            "hsab_offload_destroy", "hsab_offload_begin", "hsab_offload_step", "hsab_offload_timing",
-           "hsab_offload_set_timing", "hsab_offload_selection", "hsab_offload_step_delta", "hsab_dense_workspace_bytes", "hsab_dense_attend",
+           "hsab_offload_set_timing", "hsab_offload_selection", "hsab_offload_step_selection", "hsab_offload_step_delta",
+           "hsab_dense_workspace_bytes", "hsab_dense_attend",
            "hsab_calibrate_labels")
 
 
@@ -103,6 +104,7 @@ _lib.hsab_offload_step.argtypes = [_vp] * 16 + [_sz, _vp, _vp, ctypes.POINTER(Of
 _lib.hsab_offload_timing.argtypes = [_vp, ctypes.c_int64, _vp]
 _lib.hsab_offload_set_timing.argtypes = [_vp, ctypes.c_int32]
 _lib.hsab_offload_selection.argtypes = [_vp, _vp]
+_lib.hsab_offload_step_selection.argtypes = [_vp, ctypes.c_int64, _vp]
 _lib.hsab_offload_step_delta.argtypes = [_vp, ctypes.c_int64, _vp, _vp]
 for _f in EXPORTS[3:]:
     getattr(_lib, _f).restype = ctypes.c_int
@@ -435,6 +437,14 @@ class OffloadEngine:
         d = self.d
         outb = torch.empty(d.batch * d.n_kv_heads * d.k_blocks, dtype=torch.int32)
         _check("hsab_offload_selection", _lib.hsab_offload_selection(self._h, ctypes.c_void_p(outb.data_ptr())))
+        return outb.view(d.batch, d.n_kv_heads, d.k_blocks)
+
+    def step_selection(self, step) -> torch.Tensor:
+        """S_b [B][Hkv][K_b] of a step among the last 32 (waits for it)."""
+        d = self.d
+        outb = torch.empty(d.batch * d.n_kv_heads * d.k_blocks, dtype=torch.int32)
+        _check("hsab_offload_step_selection", _lib.hsab_offload_step_selection(
+            self._h, ctypes.c_int64(step), ctypes.c_void_p(outb.data_ptr())))
         return outb.view(d.batch, d.n_kv_heads, d.k_blocks)
 
     def delta(self, step) -> tuple:

@@ -213,7 +213,8 @@ int hsab_select_tokens(const hsab_dims* dims, const uint16_t* q, const uint16_t*
 /* Exact attention over the kept tokens [es 2.A item 2, final attention]:
  *   out[b][h] = sum_t softmax_t(sm_scale * q_h . K_t) V_t,  t in tok_idx[b][h/G]
  * computed as split partials (max, sum, weighted values) merged by
- * log-sum-exp. -1 entries of tok_idx are skipped.
+ * log-sum-exp. -1 entries of tok_idx, and entries at or past ctx_len[b],
+ * are skipped (a list with no entry left gives out 0 and lse -inf).
  * slot_of == NULL: K and V are the dense caches above. Otherwise K is the
  * offload engine's block cache [B][Hkv][n_slots][slot] (a slot is block
  * key rows of d_k followed, unless v_alias_k, by block value rows of d_v),
@@ -388,9 +389,15 @@ int hsab_offload_begin(hsab_offload_engine* engine, const int32_t* n_prefill, co
  * selects S_b(t), runs the token stage and attention over R(t) = S_b(t-1) through
  * the block cache (R(0) = S_b(0) after a synchronous fill), and enqueues
  * the delta for step t+1 on copy_stream. ctx_len (device) and ctx_len_host
- * hold the same lengths, one more than at the previous step. tok_idx, out
+ * hold the same lengths, one more than at the previous step; only work on
+ * compute_stream reads ctx_len (the copy stream plans from a copy the step
+ * takes), so the caller may update it in place by work it enqueues on
+ * compute_stream after this call. The step's inputs (q, k_new, v_new) are
+ * read by compute_stream only. tok_idx, out
  * and lse are as for hsab_decode_step; ws is a workspace of
- * hsab_workspace_bytes. stats is nullable. */
+ * hsab_workspace_bytes. stats is nullable. Steps may be enqueued
+ * back to back without synchronising in between: each step's attention
+ * waits on the GPU for the previous step's copies. */
 int hsab_offload_step(hsab_offload_engine* engine, const uint16_t* q, const uint16_t* k_new,
                       const uint16_t* v_new, uint16_t* host_pool, uint16_t* cache, uint16_t* meta,
                       uint16_t* klabel, const int32_t* label_ch, const int32_t* ctx_len,
@@ -416,6 +423,14 @@ int hsab_offload_timing(hsab_offload_engine* engine, int64_t step, float* ms);
 /* Host copy of the last step's S_b [B][Hkv][K_b] (ascending, -1 padded);
  * waits for that step's block selection. */
 int hsab_offload_selection(const hsab_offload_engine* engine, int32_t* blk_idx_host);
+
+/* Host copy of S_b [B][Hkv][K_b] of a step among the last 32 enqueued
+ * (ascending, -1 padded), waiting for that step's selection (with GPU
+ * planning, for that step's copies). Lets a caller that enqueues several
+ * steps without synchronising read every step's selection afterwards.
+ * HSAB_EINVAL for a null pointer or a step outside that window; HSAB_EHIP
+ * if the wait fails. */
+int hsab_offload_step_selection(hsab_offload_engine* engine, int64_t step, int32_t* blk_idx_host);
 
 /* Delta bytes (and, for step 0, the cold-fill bytes; else 0) of a step
  * among the last 32 enqueued, waiting for that step's copies when the GPU

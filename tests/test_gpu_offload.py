@@ -8,6 +8,8 @@ Per step and unit: S_b(t) under the near-tie rule; the token stage over the
 GPU's R(t); attention within 2e-3; the delta bytes exactly as the oracle's
 schedule gives for the GPU's S_b sequence.
 """
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import pytest
 import torch
@@ -20,12 +22,43 @@ from hsab_testlib import check_index_set, dims_of, dev16, OUT_ATOL, LSE_RTOL
 pytestmark = pytest.mark.gpu
 
 
+def _host_run(w, prefill, steps, threads=16):
+    """Seeded host arrays of a run: the dense K/V (prefill rows plus one new
+    token per row per step), the drifting queries and the new tokens."""
+    B, Hkv = w.batch, w.n_kv_heads
+    q0 = W.queries(w)
+    n_all = int(max(prefill)) + steps
+    K = np.zeros((B, Hkv, w.max_ctx, w.d_k), np.uint16)
+    V = None if w.v_alias_k else np.zeros((B, Hkv, w.max_ctx, w.d_v), np.uint16)
+
+    def fill(u):
+        b, g = divmod(u, Hkv)
+        kb, vb = W.unit_kv(w, b, g, q0, n_all)
+        K[b, g, : prefill[b]] = kb[: prefill[b]]
+        if V is not None:
+            V[b, g, : prefill[b]] = vb[: prefill[b]]
+
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        list(ex.map(fill, range(B * Hkv)))
+    news = [W.new_token(w, t) for t in range(steps)]
+    for t, (kn, vn) in enumerate(news):
+        for b in range(B):
+            K[b, :, prefill[b] + t] = kn[b]
+            if V is not None:
+                V[b, :, prefill[b] + t] = vn[b]
+    qs = [q0]
+    for t in range(1, steps):
+        qs.append(W.f32_to_bf16_bits(W.drift_queries(W.bf16_bits_to_f32(qs[-1]), w, t)))
+    return K, V, qs, news
+
+
 class _Layer:
     """One attention layer of an offload run: its host pool, GPU state and
     engine. step(t) enqueues decode step t without waiting; collect(t)
-    reads its results after the caller synchronised."""
+    reads its results after the caller synchronised; run_pipelined()
+    enqueues every step back to back and reads them all at the end."""
 
-    def __init__(self, w, prefill, steps, n_slots=None, copy_mode=0, copy_stream=None):
+    def __init__(self, w, prefill, steps, n_slots=None, copy_mode=0, copy_stream=None, host=None):
         from hierarchical_sparse_attention_block_amd import hsab as H
         self.w, self.H = w, H
         d = dims_of(w)
@@ -36,49 +69,34 @@ class _Layer:
         assert prefill.max() + steps <= w.max_ctx
         print(f"offload run {w.name} B={B} Hkv={Hkv} G={G} d_k={w.d_k} prefill={prefill.tolist()} steps={steps} "
               f"copy_mode={copy_mode}", flush=True)
-
-        # host cache: prefill rows plus one new token per step
-        q0 = W.queries(w)
-        n_all = int(prefill.max()) + steps
-        K = np.zeros((B, Hkv, w.max_ctx, w.d_k), np.uint16)
-        V = None if w.v_alias_k else np.zeros((B, Hkv, w.max_ctx, w.d_v), np.uint16)
-        for b in range(B):
-            for g in range(Hkv):
-                kb, vb = W.unit_kv(w, b, g, q0, n_all)
-                K[b, g, : prefill[b]] = kb[: prefill[b]]
-                if V is not None:
-                    V[b, g, : prefill[b]] = vb[: prefill[b]]
-        news = [W.new_token(w, t) for t in range(steps)]
-        for t, (kn, vn) in enumerate(news):
-            for b in range(B):
-                K[b, :, prefill[b] + t] = kn[b]
-                if V is not None:
-                    V[b, :, prefill[b] + t] = vn[b]
-        qs = [q0]
-        for t in range(1, steps):
-            qs.append(W.f32_to_bf16_bits(W.drift_queries(W.bf16_bits_to_f32(qs[-1]), w, t)))
+        K, V, qs, news = host if host is not None else _host_run(w, prefill, steps)
 
         # pinned pool [U][nb_cap][block keys | block values], prefill rows only
         be = H.block_elems(d)
         pool = torch.zeros(U * nb_cap * be, dtype=torch.int16, pin_memory=True)
         pv = pool.numpy().view(np.uint16).reshape(U, nb_cap, be)
+        kw, vw = bs * w.d_k, bs * w.d_v
         for b in range(B):
+            n = int(prefill[b])
+            nf, rem = divmod(n, bs)
             for g in range(Hkv):
                 u = b * Hkv + g
-                for p in range(prefill[b]):
-                    j, off = divmod(p, bs)
-                    pv[u, j, off * w.d_k:(off + 1) * w.d_k] = K[b, g, p]
-                    if V is not None:
-                        pv[u, j, bs * w.d_k + off * w.d_v: bs * w.d_k + (off + 1) * w.d_v] = V[b, g, p]
+                pv[u, :nf, :kw] = K[b, g, :nf * bs].reshape(nf, kw)
+                pv[u, nf, :rem * w.d_k] = K[b, g, nf * bs:n].reshape(-1)
+                if V is not None:
+                    pv[u, :nf, kw:kw + vw] = V[b, g, :nf * bs].reshape(nf, vw)
+                    pv[u, nf, kw:kw + rem * w.d_v] = V[b, g, nf * bs:n].reshape(-1)
 
         # GPU side: metadata and label rows of the prefill, block cache, outputs
-        Kpre = K.copy()
+        Kpre = torch.from_numpy(K.view(np.int16)).cuda()
         for b in range(B):
             Kpre[b, :, prefill[b]:] = 0
         self.meta = H.alloc_meta(d)
         self.klabel = H.alloc_klabel(d)
         self.label = torch.from_numpy(W.label_channels(w)).cuda()
-        H.build_meta(d, dev16(Kpre), torch.from_numpy(prefill).cuda(), self.label, self.meta, self.klabel)
+        H.build_meta(d, Kpre, torch.from_numpy(prefill).cuda(), self.label, self.meta, self.klabel)
+        torch.cuda.synchronize()
+        del Kpre
         self.cache = torch.zeros(U * n_slots * be, dtype=torch.int16, device="cuda")
         self.slot_of = torch.full((U * nb_cap,), -1, dtype=torch.int32, device="cuda")
         self.tok = torch.full((U * w.k_tokens,), -7, dtype=torch.int32, device="cuda")
@@ -109,6 +127,39 @@ class _Layer:
                          "out": self.out.cpu().numpy().reshape(B, w.n_q_heads, w.d_v),
                          "lse": self.lse.cpu().numpy().reshape(B, w.n_q_heads)})
 
+    def run_pipelined(self):
+        """Every step enqueued back to back with no host synchronisation:
+        each step's inputs and outputs in buffers of their own, and the
+        device ctx_len advanced in place by a kernel the caller enqueues on
+        the compute stream after each step (the copy stream must not read
+        it). Results are read once, after one synchronisation."""
+        w, B, Hkv = self.w, self.w.batch, self.w.n_kv_heads
+        V = self.V
+        ins = [(dev16(self.qs[t]), dev16(self.news[t][0]), None if V is None else dev16(self.news[t][1]))
+               for t in range(self.steps)]
+        outs = [(torch.full_like(self.tok, -7), torch.full_like(self.out, float("nan")),
+                 torch.full_like(self.lse, float("nan"))) for _ in range(self.steps)]
+        ctx_dev = torch.from_numpy(self.prefill + 1).cuda()
+        torch.cuda.synchronize()
+        sts = []
+        for t in range(self.steps):
+            ctx_h = torch.from_numpy(self.prefill + t + 1)
+            q, kn, vn = ins[t]
+            tok, out, lse = outs[t]
+            sts.append(self.eng.step(q, kn, vn, self.pool, self.cache, self.meta, self.klabel, self.label, ctx_dev,
+                                     ctx_h, self.slot_of, tok, out, lse, self.ws, copy_stream=self.copy_stream))
+            ctx_dev.add_(1)   # the next step's lengths, ordered after this step on the compute stream
+        torch.cuda.synchronize()
+        self.copy_stream.synchronize()
+        for t in range(self.steps):
+            stats = sts[t].as_dict()
+            stats["delta_bytes"], stats["cold_bytes"] = self.eng.delta(t)
+            tok, out, lse = outs[t]
+            self.res.append({"sel": self.eng.step_selection(t).numpy().copy(), "stats": stats,
+                             "tok": tok.cpu().numpy().reshape(B, Hkv, w.k_tokens),
+                             "out": out.cpu().numpy().reshape(B, w.n_q_heads, w.d_v),
+                             "lse": lse.cpu().numpy().reshape(B, w.n_q_heads)})
+
     def finish(self):
         self.eng.close()
         w, bs = self.w, self.w.block
@@ -123,16 +174,22 @@ class _Layer:
         return self.K, self.V, self.qs, self.res
 
 
-def _run_offload(w, prefill, steps, n_slots=None, copy_mode=0):
-    layer = _Layer(w, prefill, steps, n_slots, copy_mode)
-    for t in range(steps):
-        st = layer.step(t)
-        torch.cuda.synchronize()
-        layer.collect(st)
+def _run_offload(w, prefill, steps, n_slots=None, copy_mode=0, pipelined=False, host=None):
+    layer = _Layer(w, prefill, steps, n_slots, copy_mode, host=host)
+    if pipelined:
+        layer.run_pipelined()
+    else:
+        for t in range(steps):
+            st = layer.step(t)
+            torch.cuda.synchronize()
+            layer.collect(st)
     return layer.finish()
 
 
 def _check_against_oracle(w, prefill, K, V, qs, res):
+    """Every unit at every step under the parity rules. The oracle's block
+    metadata is built once at the first step's length and then advanced by
+    its incremental append (equal to a rebuild: pinned on the CPU)."""
     B, Hkv, G, bs = w.batch, w.n_kv_heads, w.group, w.block
     label = W.label_channels(w)
     row_bytes = (w.d_k if w.v_alias_k else w.d_k + w.d_v) * 2
@@ -142,14 +199,22 @@ def _check_against_oracle(w, prefill, K, V, qs, res):
     cold_total = 0
     for b in range(B):
         for g in range(Hkv):
-            Kf = O.bf16_to_f64(K[b, g])
-            Vf = Kf[:, : w.d_v] if w.v_alias_k else O.bf16_to_f64(V[b, g])
+            n_all = int(prefill[b]) + steps
+            Kf = O.bf16_to_f64(K[b, g, :n_all])
+            Vf = Kf[:, : w.d_v] if w.v_alias_k else O.bf16_to_f64(V[b, g, :n_all])
             sels, ns = [], []
+            kmax = kmin = None
             for t in range(steps):
                 n = int(prefill[b]) + t + 1
                 q = O.bf16_to_f64(qs[t][b, g * G:(g + 1) * G])
-                kmax, kmin = (O.block_meta_e4m3 if w.meta_fp8 else O.block_meta)(Kf, n, bs)
-                s_blk = O.block_scores(q, kmax, kmin)
+                if kmax is None:
+                    kmax, kmin = O.block_meta(Kf, n, bs)
+                else:
+                    kmax, kmin = O.append_meta(kmax, kmin, Kf[n - 1], n - 1, bs)
+                if w.meta_fp8:
+                    s_blk = O.block_scores(q, O.e4m3_round(kmax, True), O.e4m3_round(kmin, False))
+                else:
+                    s_blk = O.block_scores(q, kmax, kmin)
                 sel, tie = check_index_set(s_blk, res[t]["sel"][b, g], w.k_blocks, f"S_b step {t} unit ({b},{g})")
                 ties += tie
                 resident = sel if t == 0 else sels[-1]
@@ -295,3 +360,47 @@ def test_offload_mla_latent_blocks(copy_mode):
     prefill = [640]               # 640 = 20 blocks of 32: the first decode token opens block 20
     K, V, qs, res = _run_offload(w, prefill, steps=6, copy_mode=copy_mode)
     _check_against_oracle(w, np.array(prefill), K, V, qs, res)
+
+
+@pytest.mark.parametrize("copy_mode", [0, 1, 2], ids=["host_plan", "dma", "gpu_plan"])
+def test_offload_pipelined_steps(copy_mode):
+    """Every step enqueued back to back, no host synchronisation between
+    them, the caller's device ctx_len advanced in place on the compute
+    stream after each step: every step (S_b(t) read back afterwards) still
+    matches the lagged oracle, delta bytes exactly."""
+    w = W.WORKLOADS["tiny4k"].replace(name="offload_pipe", batch=2, n_q_heads=8, n_kv_heads=2, k_blocks=8,
+                                      k_tokens=64, ctx=1024, max_ctx=1024, scaled_keys=True, n_planted=0,
+                                      seed=26)
+    prefill = [318, 700]
+    K, V, qs, res = _run_offload(w, prefill, steps=14, copy_mode=copy_mode, pipelined=True)
+    _check_against_oracle(w, np.array(prefill), K, V, qs, res)
+    assert sum(r["stats"]["delta_bytes"] for r in res[1:]) > 0, "the queries drift, so some blocks move"
+
+
+_FULL = {}
+
+
+def _offload96k_host():
+    """Host arrays of the full multi-step offload run, built once per module."""
+    if "host" not in _FULL:
+        w = W.WORKLOADS["offload96k"]
+        prefill = W.offload_prefill(w)
+        _FULL["host"] = (w, prefill, _host_run(w, prefill, W.OFFLOAD_STEPS))
+    return _FULL["host"]
+
+
+@pytest.mark.parametrize("copy_mode,pipelined", [(0, False), (2, True)], ids=["host_plan", "gpu_plan_pipelined"])
+def test_offload96k_full_scale(copy_mode, pipelined):
+    """The full multi-step offload run: B = 4, 32/8 heads, d = 128, prefill
+    lengths drawn in 8k-96k, K_b = 128, K_t = 512, 16 drifting steps
+    (about 500 blocks of 8 KiB cross the link per step, the device
+    planner's slot bitmap spans 8 words). Every unit's S_b(t) at every step
+    under the near-tie rule, the token stage over the GPU's R(t),
+    attention, and the delta bytes of every step exactly."""
+    w, prefill, host = _offload96k_host()
+    K, V, qs, res = _run_offload(w, prefill, W.OFFLOAD_STEPS, copy_mode=copy_mode, pipelined=pipelined, host=host)
+    ties = _check_against_oracle(w, np.array(prefill), K, V, qs, res)
+    moved = [r["stats"]["delta_bytes"] for r in res[1:]]
+    print(f"offload96k copy_mode={copy_mode}: cold {res[0]['stats']['cold_bytes']} B, delta per step {moved}, "
+          f"near ties {ties}", flush=True)
+    assert min(moved) > 0
