@@ -26,28 +26,13 @@ namespace hsab {
 
 namespace {
 
-// Row index (in rows of d_k elements from the K base) of token t of unit,
-// or -1. Dense caches: unit*max_ctx + t. Block cache: slot s of the unit
-// spans slot_rows rows (key rows first, then value rows), found through
-// slot_of.
-__device__ __forceinline__ long row_of(int t, int unit, int bs, int max_ctx, int nb_cap,
-                                       const int32_t* __restrict__ slot_of, int n_slots, int slot_rows) {
-    if (t < 0) return -1;
-    if (!slot_of) return (t < max_ctx) ? (long)unit * max_ctx + t : -1;
-    const int blk = t / bs;
-    if (blk >= nb_cap) return -1;
-    const int slot = slot_of[(size_t)unit * nb_cap + blk];
-    if (slot < 0 || slot >= n_slots) return -1;
-    return ((long)unit * n_slots + slot) * slot_rows + (t - blk * bs);
-}
-
 // MASKED: the token list is the union of the heads' own token sets (per-head
 // selection) and tok_mask gives, per entry, the heads that attend it.
 template <int D, int G, bool MASKED>
 __global__ __launch_bounds__(256) void attend_gqa_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const int32_t* __restrict__ tok_idx, const uint32_t* __restrict__ tok_mask,
-    const int32_t* __restrict__ slot_of, int n_slots,
+    const int32_t* __restrict__ ctx_len, const int32_t* __restrict__ slot_of, int n_slots,
     float* __restrict__ part_ml, float* __restrict__ part_acc, int Hkv, int bs, int kt,
     int max_ctx, int nb_cap, int n_splits, int units, float scale2, int slot_rows) {
     constexpr int LPT = D / 8;                         // lanes per token (8 channels each)
@@ -65,6 +50,9 @@ __global__ __launch_bounds__(256) void attend_gqa_kernel(
     const int b = unit / Hkv, g = unit % Hkv;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int cc = lane % LPT, ts = lane / LPT;
+    // entries at or past the context length are skipped
+    int n = ctx_len[b];
+    n = n < 0 ? 0 : (n > max_ctx ? max_ctx : n);
 
     float qf[G][8];
 #pragma unroll
@@ -90,7 +78,7 @@ __global__ __launch_bounds__(256) void attend_gqa_kernel(
         const int ti = split * ATT_TOK_PER_SPLIT + wave * TPW + it * TPI + ts;
         const int tc = ti < kt ? ti : kt - 1;
         const int t = tl[tc];
-        tv[it] = ti < kt ? t : -1;
+        tv[it] = ti < kt && t < n ? t : -1;
         mk[it] = MASKED ? tok_mask[(size_t)unit * kt + tc] : ~0u;
     }
     if (slot_of) {
@@ -108,8 +96,7 @@ __global__ __launch_bounds__(256) void attend_gqa_kernel(
         }
     } else {
 #pragma unroll
-        for (int it = 0; it < IT; ++it)
-            rows[it] = (tv[it] >= 0 && tv[it] < max_ctx) ? (long)unit * max_ctx + tv[it] : -1;
+        for (int it = 0; it < IT; ++it) rows[it] = tv[it] >= 0 ? (long)unit * max_ctx + tv[it] : -1;
     }
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
@@ -219,7 +206,7 @@ __global__ __launch_bounds__(256) void attend_gqa_kernel(
 template <int DKMAX>
 __global__ __launch_bounds__(256, 1) void attend_mla_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ K, const int32_t* __restrict__ tok_idx,
-    const int32_t* __restrict__ slot_of, int n_slots, float* __restrict__ part_ml,
+    const int32_t* __restrict__ ctx_len, const int32_t* __restrict__ slot_of, int n_slots, float* __restrict__ part_ml,
     float* __restrict__ part_acc, int Hkv, int dk, int dv, int bs, int kt, int max_ctx, int nb_cap,
     int n_splits, int units, float scale2, int slot_rows, int rounds, int vsplit) {
     constexpr int T = 32;                  // tokens per round
@@ -249,7 +236,9 @@ __global__ __launch_bounds__(256, 1) void attend_mla_kernel(
     // complete in order, so the rows wait for no fragment)
     const int ti = split * TS + tid;
     const int t_raw = tok_idx[(size_t)unit * kt + (ti < kt ? ti : kt - 1)];   // unconditional load
-    const int t = tid < TS && ti < kt ? t_raw : -1;
+    int n = ctx_len[unit / Hkv];   // entries at or past the context length are skipped
+    n = n < 0 ? 0 : (n > max_ctx ? max_ctx : n);
+    const int t = tid < TS && ti < kt && t_raw < n ? t_raw : -1;
     // query fragments of head nt*16 + c16 (B operand, zero past d_k)
     uint4 qb[KSMAX];
     {
@@ -263,7 +252,7 @@ __global__ __launch_bounds__(256, 1) void attend_mla_kernel(
         long row = -1;
         if (tid < TS) {
             if (!slot_of) {
-                row = (t >= 0 && t < max_ctx) ? (long)unit * max_ctx + t : -1;
+                row = t >= 0 ? (long)unit * max_ctx + t : -1;
             } else if (t >= 0) {
                 const int blk = t / bs;
                 const int sl_ = blk < nb_cap ? slot_of[(size_t)unit * nb_cap + blk] : -1;
@@ -446,30 +435,30 @@ __global__ __launch_bounds__(256) void combine_kernel(
 
 template <int D, int G>
 hipError_t launch_gqa(const Shape& s, const uint16_t* q, const uint16_t* K, const uint16_t* V,
-                      const int32_t* tok_idx, const uint32_t* tok_mask, int list_len, int ns,
+                      const int32_t* tok_idx, const uint32_t* tok_mask, int list_len, int ns, const int32_t* ctx_len,
                       const int32_t* slot_of, int n_slots, float* part_ml, float* part_acc, hipStream_t st) {
     const int units = s.B * s.Hkv;
     const dim3 grid(((units + 7) / 8) * 8 * ns);
     if (tok_mask)
         hipLaunchKernelGGL((attend_gqa_kernel<D, G, true>), grid, dim3(256), 0, st, q, K, V, tok_idx, tok_mask,
-                           slot_of, n_slots, part_ml, part_acc, s.Hkv, s.bs, list_len, s.max_ctx, s.nb_cap, ns,
-                           units, s.sm_scale * LOG2E, 2 * s.bs);
+                           ctx_len, slot_of, n_slots, part_ml, part_acc, s.Hkv, s.bs, list_len, s.max_ctx, s.nb_cap,
+                           ns, units, s.sm_scale * LOG2E, 2 * s.bs);
     else
         hipLaunchKernelGGL((attend_gqa_kernel<D, G, false>), grid, dim3(256), 0, st, q, K, V, tok_idx, tok_mask,
-                           slot_of, n_slots, part_ml, part_acc, s.Hkv, s.bs, list_len, s.max_ctx, s.nb_cap, ns,
-                           units, s.sm_scale * LOG2E, 2 * s.bs);
+                           ctx_len, slot_of, n_slots, part_ml, part_acc, s.Hkv, s.bs, list_len, s.max_ctx, s.nb_cap,
+                           ns, units, s.sm_scale * LOG2E, 2 * s.bs);
     return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_gqa_d(const Shape& s, const uint16_t* q, const uint16_t* K, const uint16_t* V,
-                        const int32_t* tok_idx, const uint32_t* tok_mask, int list_len, int ns,
+                        const int32_t* tok_idx, const uint32_t* tok_mask, int list_len, int ns, const int32_t* ctx_len,
                         const int32_t* slot_of, int n_slots, float* part_ml, float* part_acc, hipStream_t st) {
     switch (s.G) {
-        case 1: return launch_gqa<D, 1>(s, q, K, V, tok_idx, tok_mask, list_len, ns, slot_of, n_slots, part_ml, part_acc, st);
-        case 2: return launch_gqa<D, 2>(s, q, K, V, tok_idx, tok_mask, list_len, ns, slot_of, n_slots, part_ml, part_acc, st);
-        case 4: return launch_gqa<D, 4>(s, q, K, V, tok_idx, tok_mask, list_len, ns, slot_of, n_slots, part_ml, part_acc, st);
-        case 8: return launch_gqa<D, 8>(s, q, K, V, tok_idx, tok_mask, list_len, ns, slot_of, n_slots, part_ml, part_acc, st);
+        case 1: return launch_gqa<D, 1>(s, q, K, V, tok_idx, tok_mask, list_len, ns, ctx_len, slot_of, n_slots, part_ml, part_acc, st);
+        case 2: return launch_gqa<D, 2>(s, q, K, V, tok_idx, tok_mask, list_len, ns, ctx_len, slot_of, n_slots, part_ml, part_acc, st);
+        case 4: return launch_gqa<D, 4>(s, q, K, V, tok_idx, tok_mask, list_len, ns, ctx_len, slot_of, n_slots, part_ml, part_acc, st);
+        case 8: return launch_gqa<D, 8>(s, q, K, V, tok_idx, tok_mask, list_len, ns, ctx_len, slot_of, n_slots, part_ml, part_acc, st);
         default: return hipErrorInvalidValue;
     }
 }
@@ -494,7 +483,7 @@ bool attend_supported(const Shape& s) {
 }
 
 hipError_t launch_attend(const Shape& s, const uint16_t* q, const uint16_t* K, const uint16_t* V,
-                         const int32_t* tok_idx, const uint32_t* tok_mask, int list_len,
+                         const int32_t* tok_idx, const uint32_t* tok_mask, int list_len, const int32_t* ctx_len,
                          const int32_t* slot_of, int n_slots, float* part_ml, float* part_acc, float* out,
                          float* lse, hipStream_t st) {
     if (!attend_supported(s)) return hipErrorInvalidValue;
@@ -509,19 +498,19 @@ hipError_t launch_attend(const Shape& s, const uint16_t* q, const uint16_t* K, c
         const int vs = (long)units * ns < 256 && s.dv >= 128 ? 2 : 1;
         const dim3 grid(((units + 7) / 8) * 8 * ns * vs);
         if (s.dk <= 576)
-            hipLaunchKernelGGL(attend_mla_kernel<576>, grid, dim3(256), 0, st, q, K, tok_idx, slot_of, n_slots,
+            hipLaunchKernelGGL(attend_mla_kernel<576>, grid, dim3(256), 0, st, q, K, tok_idx, ctx_len, slot_of, n_slots,
                                part_ml, part_acc, s.Hkv, s.dk, s.dv, s.bs, s.kt, s.max_ctx, s.nb_cap, ns, units,
                                s.sm_scale * LOG2E, s.bs, MLA_TOK_PER_SPLIT / 32, vs);
         else
-            hipLaunchKernelGGL(attend_mla_kernel<1024>, grid, dim3(256), 0, st, q, K, tok_idx, slot_of, n_slots,
+            hipLaunchKernelGGL(attend_mla_kernel<1024>, grid, dim3(256), 0, st, q, K, tok_idx, ctx_len, slot_of, n_slots,
                                part_ml, part_acc, s.Hkv, s.dk, s.dv, s.bs, s.kt, s.max_ctx, s.nb_cap, ns, units,
                                s.sm_scale * LOG2E, s.bs, MLA_TOK_PER_SPLIT / 32, vs);
         e = hipGetLastError();
     } else {
         switch (s.dk) {
-            case 64: e = launch_gqa_d<64>(s, q, K, V, tok_idx, tok_mask, list_len, ns, slot_of, n_slots, part_ml, part_acc, st); break;
-            case 128: e = launch_gqa_d<128>(s, q, K, V, tok_idx, tok_mask, list_len, ns, slot_of, n_slots, part_ml, part_acc, st); break;
-            case 256: e = launch_gqa_d<256>(s, q, K, V, tok_idx, tok_mask, list_len, ns, slot_of, n_slots, part_ml, part_acc, st); break;
+            case 64: e = launch_gqa_d<64>(s, q, K, V, tok_idx, tok_mask, list_len, ns, ctx_len, slot_of, n_slots, part_ml, part_acc, st); break;
+            case 128: e = launch_gqa_d<128>(s, q, K, V, tok_idx, tok_mask, list_len, ns, ctx_len, slot_of, n_slots, part_ml, part_acc, st); break;
+            case 256: e = launch_gqa_d<256>(s, q, K, V, tok_idx, tok_mask, list_len, ns, ctx_len, slot_of, n_slots, part_ml, part_acc, st); break;
             default: return hipErrorInvalidValue;
         }
     }

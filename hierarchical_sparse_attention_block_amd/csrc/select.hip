@@ -21,9 +21,10 @@
 // misses one CU keeps in flight, so with few units each unit gets `parts`
 // workgroups (on one XCD). Every part selects the blocks itself (part 0
 // writes them), scores its share of the candidate tiles and publishes the
-// keys with agent-scope stores; after its stores have completed, each part
-// bumps the unit's arrival counter, and the part that arrives last reads
-// all keys back (agent-scope loads), runs top-K_t and resets the counter.
+// keys with agent-scope stores; each part then bumps the unit's arrival
+// counter with an agent-scope acquire-release read-modify-write, and the
+// part that arrives last reads all keys back (agent-scope loads), runs
+// top-K_t and resets the counter.
 #include <type_traits>
 #include "common.h"
 #include "kernels.h"
@@ -248,11 +249,15 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
         }
     }
     if (parts > 1) {
-        // this part's key stores are complete before the arrival is counted
-        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+        // The barrier orders every wave's key stores before thread 0's
+        // arrival; the arrival releases them at agent scope and, in the part
+        // that arrives last, acquires the other parts' (every arrival is a
+        // read-modify-write of the one counter, so the last one reads a value
+        // that every earlier release wrote into); the second barrier passes
+        // that acquire on to the waves that read the keys.
         __syncthreads();
         if (threadIdx.x == 0)
-            s_last = __hip_atomic_fetch_add(&cnt[sel], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == parts - 1;
+            s_last = __hip_atomic_fetch_add(&cnt[sel], 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) == parts - 1;
         __syncthreads();
         if (!s_last) return;
     } else {

@@ -13,8 +13,12 @@
 // are emitted by entry, not by word: thread e finds the word holding entry
 // e by binary search over the offsets and writes slot e, so the stores are
 // coalesced and the dense words (the kept tokens cluster in kept blocks)
-// are not left to a few lanes. Windows cover max_ctx in turn, so the union
-// comes out ascending; the LDS per window is fixed (60 KiB).
+// are not left to a few lanes. Each window starts at the smallest listed
+// position past the previous window (the first at the smallest of all), so
+// windows holding no entry are never visited and the union comes out
+// ascending; positions at or past the unit's context length are dropped.
+// The LDS per window is fixed (60 KiB).
+#include <climits>
 #include "common.h"
 #include "kernels.h"
 
@@ -28,28 +32,45 @@ constexpr int UNION_LDS_WORDS = 15360;   // 60 KiB per window: head bitmaps [G][
 // G: heads per group (compile time); (G + 1) * wph <= UNION_LDS_WORDS.
 template <int G>
 __global__ __launch_bounds__(UNION_THREADS) void union_kernel(const int32_t* __restrict__ tok_idx,
+                                                              const int32_t* __restrict__ ctx_len,
                                                               int32_t* __restrict__ union_idx,
-                                                              uint32_t* __restrict__ union_mask, int kt,
+                                                              uint32_t* __restrict__ union_mask, int Hkv, int kt,
                                                               int max_ctx, int wph) {
     __shared__ uint32_t bits[UNION_LDS_WORDS];   // [G][wph] head bitmaps, then [wph] word offsets
     uint32_t* off = bits + G * wph;
     __shared__ uint32_t s_wsum[UNION_THREADS / 64];
+    __shared__ int s_next;                        // smallest listed position past the window
     const int unit = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int E = G * kt;
     const int32_t* L = tok_idx + (size_t)unit * E;
     int32_t* U = union_idx + (size_t)unit * E;
     uint32_t* M = union_mask + (size_t)unit * E;
+    int n = ctx_len[unit / Hkv];
+    n = n < 0 ? 0 : (n > max_ctx ? max_ctx : n);
     const int span = wph * 32;                        // positions per window
     const int per = (wph + UNION_THREADS - 1) / UNION_THREADS;   // words per thread
     int base = 0;                                     // entries written so far
-    for (int w0 = 0; w0 < max_ctx; w0 += span) {
+    if (tid == 0) s_next = INT_MAX;
+    __syncthreads();
+    for (int e = tid; e < E; e += UNION_THREADS) {
+        const int t = L[e];
+        if (t >= 0 && t < n) atomicMin(&s_next, t);
+    }
+    __syncthreads();
+    int w0 = s_next;                                  // INT_MAX: no entry at all
+    while (w0 < n) {
+        __syncthreads();                              // every thread has read s_next
+        if (tid == 0) s_next = INT_MAX;
         for (int i = tid; i < G * wph; i += UNION_THREADS) bits[i] = 0u;
         __syncthreads();
+        const int w1 = n - w0 > span ? w0 + span : n;  // this window: positions [w0, w1)
         for (int e = tid; e < E; e += UNION_THREADS) {
             const int t = L[e];
-            if (t >= w0 && t < w0 + span && t < max_ctx) {
+            if (t >= w0 && t < w1) {
                 const int h = e / kt, o = t - w0;
                 atomicOr(&bits[h * wph + (o >> 5)], 1u << (o & 31));
+            } else if (t >= w1 && t < n) {
+                atomicMin(&s_next, t);
             }
         }
         __syncthreads();
@@ -105,6 +126,7 @@ __global__ __launch_bounds__(UNION_THREADS) void union_kernel(const int32_t* __r
         }
         base += (int)total;
         __syncthreads();   // the next window reuses bits and s_wsum
+        w0 = s_next;
     }
     for (int e = base + tid; e < E; e += UNION_THREADS) {
         U[e] = -1;
@@ -114,21 +136,21 @@ __global__ __launch_bounds__(UNION_THREADS) void union_kernel(const int32_t* __r
 
 }  // namespace
 
-hipError_t launch_union(const Shape& s, const int32_t* tok_idx, int32_t* union_idx, uint32_t* union_mask,
-                        hipStream_t st) {
+hipError_t launch_union(const Shape& s, const int32_t* tok_idx, const int32_t* ctx_len, int32_t* union_idx,
+                        uint32_t* union_mask, hipStream_t st) {
     const int words = (s.max_ctx + 31) / 32;
     const int cap = UNION_LDS_WORDS / (s.G + 1);
     const int wph = words < cap ? words : cap;
     const dim3 grid(s.B * s.Hkv), block(UNION_THREADS);
     switch (s.G) {   // the group sizes the masked attention takes
-        case 1: hipLaunchKernelGGL(union_kernel<1>, grid, block, 0, st, tok_idx, union_idx, union_mask, s.kt,
-                                   s.max_ctx, wph); break;
-        case 2: hipLaunchKernelGGL(union_kernel<2>, grid, block, 0, st, tok_idx, union_idx, union_mask, s.kt,
-                                   s.max_ctx, wph); break;
-        case 4: hipLaunchKernelGGL(union_kernel<4>, grid, block, 0, st, tok_idx, union_idx, union_mask, s.kt,
-                                   s.max_ctx, wph); break;
-        case 8: hipLaunchKernelGGL(union_kernel<8>, grid, block, 0, st, tok_idx, union_idx, union_mask, s.kt,
-                                   s.max_ctx, wph); break;
+        case 1: hipLaunchKernelGGL(union_kernel<1>, grid, block, 0, st, tok_idx, ctx_len, union_idx, union_mask,
+                                   s.Hkv, s.kt, s.max_ctx, wph); break;
+        case 2: hipLaunchKernelGGL(union_kernel<2>, grid, block, 0, st, tok_idx, ctx_len, union_idx, union_mask,
+                                   s.Hkv, s.kt, s.max_ctx, wph); break;
+        case 4: hipLaunchKernelGGL(union_kernel<4>, grid, block, 0, st, tok_idx, ctx_len, union_idx, union_mask,
+                                   s.Hkv, s.kt, s.max_ctx, wph); break;
+        case 8: hipLaunchKernelGGL(union_kernel<8>, grid, block, 0, st, tok_idx, ctx_len, union_idx, union_mask,
+                                   s.Hkv, s.kt, s.max_ctx, wph); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

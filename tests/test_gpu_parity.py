@@ -53,12 +53,17 @@ def _check_all_units(w, h, r, units=None):
 
 
 # --------------------------------------------------------------- metadata
-@pytest.mark.parametrize("dk,bs,r", [(128, 16, 16), (64, 8, 32), (576, 32, 32)])
-def test_build_meta_and_append_exact(dk, bs, r):
+# (576, 32, 32, 32, 1): the absorbed latent layer (32 query heads on one
+# 576-dim latent), whose append runs in the split-row block-score kernel;
+# (576, 32, 32, 4, 2) is a latent shape no attention kernel takes, so the
+# step must refuse it before appending
+@pytest.mark.parametrize("dk,bs,r,Hq,Hkv", [(128, 16, 16, 4, 2), (64, 8, 32, 4, 2), (576, 32, 32, 32, 1),
+                                           (576, 32, 32, 4, 2)])
+def test_build_meta_and_append_exact(dk, bs, r, Hq, Hkv):
     w = _wl(d_k=dk, d_v=dk if dk != 576 else 512, v_alias_k=dk == 576, block=bs, r=r,
-            n_q_heads=4, n_kv_heads=2, max_ctx=700, ctx=700, n_planted=0)
+            n_q_heads=Hq, n_kv_heads=Hkv, max_ctx=700, ctx=700, n_planted=0)
     ctx = np.array([700, 333], np.int32)
-    say(f"[build_meta+append] dk={dk} bs={bs} r={r} ctx={ctx}")
+    say(f"[build_meta+append] dk={dk} bs={bs} r={r} heads={Hq}/{Hkv} ctx={ctx}")
     h = T.host_inputs(w, ctx_len=ctx)
     dev = T.Device(w, h)
     dev.prefill_meta()
@@ -75,22 +80,27 @@ def test_build_meta_and_append_exact(dk, bs, r):
             np.testing.assert_array_equal(O.bf16_to_f64(meta[b, g, :nb, 0]), kmax)
             np.testing.assert_array_equal(O.bf16_to_f64(meta[b, g, :nb, 1]), kmin)
             np.testing.assert_array_equal(klab[b, g, :n], h["K"][b, g, :n][:, h["label"][g]])
-    # the append of decode_step (attention is not needed for this check)
+    # the append of decode_step
     H = dev.H
-    if not w.v_alias_k:
-        dev.decode_step()
-    else:
+    if w.v_alias_k and w.group != 32:
         with pytest.raises(H.HsabError):
             dev.decode_step()
         return
+    dev.decode_step()
     torch.cuda.synchronize()
     meta = T.host16(dev.meta).reshape(w.batch, w.n_kv_heads, d.nb_cap, 2, w.d_k)
     Kd = T.host16(dev.K).reshape(h["K"].shape)
-    Ka, _ = T.appended_cache(w, h)
+    klab = T.host16(dev.klabel).reshape(w.batch, w.n_kv_heads, w.max_ctx, w.r)
+    Ka, Va = T.appended_cache(w, h)
+    if Va is not None:
+        Vd = T.host16(dev.V).reshape(h["V"].shape)
     for b in range(w.batch):
         n = int(ctx[b])
         np.testing.assert_array_equal(Kd[b, :, :n], Ka[b, :, :n])
+        if Va is not None:
+            np.testing.assert_array_equal(Vd[b, :, :n], Va[b, :, :n])
         for g in range(w.n_kv_heads):
+            np.testing.assert_array_equal(klab[b, g, :n], Ka[b, g, :n][:, h["label"][g]])
             kmax, kmin = O.block_meta(O.bf16_to_f64(Ka[b, g, :n]), n, bs)
             kmax0, kmin0 = O.block_meta(O.bf16_to_f64(Ka[b, g, :n - 1]), n - 1, bs) if n > 1 else (None, None)
             if kmax0 is not None:
@@ -279,8 +289,15 @@ def test_select_blocks_tokens_attend_match_decode_step():
                 assert np.all(seg[len(toks):] == -np.inf)
 
 
-def test_sparse_attend_skips_padding_and_handles_empty():
-    w = _wl(batch=1, n_q_heads=4, n_kv_heads=1, max_ctx=256, ctx=256, k_tokens=70, n_planted=0)
+@pytest.mark.parametrize("latent", [False, True], ids=["gqa", "latent"])
+def test_sparse_attend_skips_padding_and_handles_empty(latent):
+    """hsab_sparse_attend on a given list: -1 padding skipped; entries at
+    or past ctx_len skipped; an all-empty list gives out 0, lse -inf."""
+    if latent:
+        w = _wl(batch=1, n_q_heads=32, n_kv_heads=1, d_k=576, d_v=512, v_alias_k=True, block=32, r=32,
+                max_ctx=256, ctx=256, k_tokens=70, n_planted=0)
+    else:
+        w = _wl(batch=1, n_q_heads=4, n_kv_heads=1, max_ctx=256, ctx=256, k_tokens=70, n_planted=0)
     h = T.host_inputs(w)
     dev = T.Device(w, h)
     sel = np.sort(np.random.default_rng(5).choice(255, size=33, replace=False)).astype(np.int32)
@@ -288,15 +305,18 @@ def test_sparse_attend_skips_padding_and_handles_empty():
     tok[:33] = sel
     out = torch.empty_like(dev.out)
     lse = torch.empty_like(dev.lse)
-    say("[sparse_attend] 33 of 70 slots used")
-    dev.H.sparse_attend(dev.d, dev.q, dev.K, dev.V, torch.from_numpy(tok).cuda(), dev.ctx, out, lse, dev.ws)
-    torch.cuda.synchronize()
     q = O.bf16_to_f64(h["q"][0])
     K = O.bf16_to_f64(h["K"][0, 0])
-    V = O.bf16_to_f64(h["V"][0, 0])
-    o, l = O.attend(q, K[sel], V[sel], w.sm_scale)
-    assert np.max(np.abs(out.cpu().numpy().reshape(4, -1) - o)) <= T.OUT_ATOL
-    np.testing.assert_allclose(lse.cpu().numpy(), l, rtol=T.LSE_RTOL)
+    V = K[:, : w.d_v] if latent else O.bf16_to_f64(h["V"][0, 0])
+    for n in (256, 150):
+        say(f"[sparse_attend] 33 of 70 slots used, ctx_len {n}")
+        dev.H.sparse_attend(dev.d, dev.q, dev.K, dev.V, torch.from_numpy(tok).cuda(),
+                            torch.full((1,), n, dtype=torch.int32, device="cuda"), out, lse, dev.ws)
+        torch.cuda.synchronize()
+        keep = sel[sel < n]
+        o, l = O.attend(q, K[keep], V[keep], w.sm_scale)
+        assert np.max(np.abs(out.cpu().numpy().reshape(w.n_q_heads, -1) - o)) <= T.OUT_ATOL
+        np.testing.assert_allclose(lse.cpu().numpy(), l, rtol=T.LSE_RTOL)
     # all slots empty: out 0, lse -inf
     dev.H.sparse_attend(dev.d, dev.q, dev.K, dev.V, torch.full((w.k_tokens,), -1, dtype=torch.int32,
                         device="cuda"), dev.ctx, out, lse, dev.ws)
@@ -347,8 +367,29 @@ def test_gqa48k_full_size_sampled_units():
             assert set(pos) <= set(r["tok"][b, g]), f"planted token missed in ({b},{g})"
             assert np.all(np.diff(r["blk"][b, g]) > 0) and np.all(np.diff(r["tok"][b, g]) > 0)
     assert np.all(np.isfinite(r["out"])) and np.all(np.isfinite(r["lse"]))
-    st = _check_all_units(w, h, r, units=[(0, 0), (3, 5), (7, 7)])
+    # one unit of every batch row and of every KV head, plus one more
+    st = _check_all_units(w, h, r, units=[(b, b) for b in range(8)] + [(3, 5)])
     say("gqa48k sampled", st)
+
+
+def test_gqa96k_full_size_sampled_units():
+    """The 96k GQA layer (B = 16, 32/8 heads, 98,304 tokens, K_b = 256,
+    K_t = 1024) in the benchmark's launch configuration: 6,144 blocks and
+    4,096 candidates per unit, 16 attention splits. Every unit is checked
+    for structure and planted-key recall; one unit of every batch row and
+    of every KV head (16 units) against the oracle."""
+    w = W.WORKLOADS["gqa96k"]
+    w, h, dev, r = _run_decode(w)
+    for b in range(w.batch):
+        for g in range(w.n_kv_heads):
+            pos, _ = W.planted_positions(w, b, g)
+            assert set(pos // w.block) <= set(r["blk"][b, g]), f"planted block missed in ({b},{g})"
+            assert set(pos) <= set(r["tok"][b, g]), f"planted token missed in ({b},{g})"
+            assert np.all(np.diff(r["blk"][b, g]) > 0) and np.all(np.diff(r["tok"][b, g]) > 0)
+            assert r["blk"][b, g, -1] < w.ctx // w.block and r["tok"][b, g, -1] < w.ctx
+    assert np.all(np.isfinite(r["out"])) and np.all(np.isfinite(r["lse"]))
+    st = _check_all_units(w, h, r, units=[(b, b % 8) for b in range(16)])
+    say("gqa96k sampled", st)
 
 
 def test_mha48k_full_size_sampled_units():
@@ -363,7 +404,7 @@ def test_mha48k_full_size_sampled_units():
             assert set(pos // w.block) <= set(r["blk"][b, g]), f"planted block missed in ({b},{g})"
             assert set(pos) <= set(r["tok"][b, g]), f"planted token missed in ({b},{g})"
     assert np.all(np.isfinite(r["out"])) and np.all(np.isfinite(r["lse"]))
-    st = _check_all_units(w, h, r, units=[(0, 0), (1, 17), (1, 31)])
+    st = _check_all_units(w, h, r, units=[(b, g) for g in range(0, 32, 4) for b in ((g // 4) % 2,)] + [(1, 31)])
     say("mha48k sampled", st)
 
 
@@ -414,5 +455,5 @@ def test_mla64k_full_size_sampled_units():
     assert np.all(np.isfinite(r["out"])) and np.all(np.isfinite(r["lse"]))
     for b in range(w.batch):
         assert np.all(np.diff(r["blk"][b, 0]) > 0) and np.all(np.diff(r["tok"][b, 0]) > 0)
-    st = _check_all_units(w, h, r, units=[(0, 0), (5, 0)])
-    say("mla64k sampled", st)
+    st = _check_all_units(w, h, r)   # all eight batch rows
+    say("mla64k all units", st)

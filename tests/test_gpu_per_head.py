@@ -115,12 +115,15 @@ def test_per_head_stage_entry_points():
                                      r["tok"][b, a], r["out"][b, a:a + 1], r["lse"][b, a:a + 1], head=hh)
 
 
-@pytest.mark.parametrize("G,max_ctx,seed", [(4, 3000, 1), (8, 140000, 2), (2, 70000, 3), (1, 500, 4)])
+@pytest.mark.parametrize("G,max_ctx,seed", [(4, 3000, 1), (8, 140000, 2), (2, 200000, 3), (4, 140000, 5),
+                                            (1, 500, 4)])
 def test_per_head_attention_over_crafted_lists(G, max_ctx, seed):
     """hsab_sparse_attend with given per-head lists: overlapping, identical,
     disjoint and empty (all -1) lists, positions spread over several union
-    windows (G = 8 at 140k positions needs three), against the oracle's
-    attention over each head's own tokens."""
+    windows (G = 8 at 140k positions needs three, G = 2 at 200k and G = 4
+    at 140k two), against the oracle's attention over each head's own
+    tokens. The second batch row's context is a third shorter than the
+    capacity: its entries at or past that length are skipped."""
     rng = np.random.default_rng(seed)
     B, Hkv, d, kt = 2, 2, 64, 96
     Hq = G * Hkv
@@ -157,15 +160,16 @@ def test_per_head_attention_over_crafted_lists(G, max_ctx, seed):
     out = torch.full((B * Hq * d,), float("nan"), device="cuda")
     lse = torch.full((B * Hq,), float("nan"), device="cuda")
     ws = H.alloc_workspace(dm)
+    ctx = np.array([max_ctx, max_ctx - max_ctx // 3], np.int32)
     H.sparse_attend(dm, T.dev16(q), T.dev16(K), T.dev16(V), torch.from_numpy(tok.ravel()).cuda(),
-                    torch.full((B,), max_ctx, dtype=torch.int32, device="cuda"), out, lse, ws)
+                    torch.from_numpy(ctx).cuda(), out, lse, ws)
     torch.cuda.synchronize()
     out = out.cpu().numpy().reshape(B, Hq, d)
     lse = lse.cpu().numpy().reshape(B, Hq)
     for b in range(B):
         for a in range(Hq):
             g = a // G
-            lst = tok[b, a][tok[b, a] >= 0]
+            lst = tok[b, a][(tok[b, a] >= 0) & (tok[b, a] < ctx[b])]
             qa = O.bf16_to_f64(q[b, a:a + 1])
             o, l = O.attend(qa, O.bf16_to_f64(K[b, g, lst]), O.bf16_to_f64(V[b, g, lst]), 1 / math.sqrt(d))
             if len(lst) == 0:
