@@ -238,6 +238,8 @@ def _check_against_oracle(w, prefill, K, V, qs, res):
                 ns.append(n)
             cold, deltas = O.offload_schedule(sels, ns, int(prefill[b]), bs)
             cold_total += len(cold) * bs * row_bytes
+            if w.units > 8:
+                print(f"  unit ({b},{g}) checked over {steps} steps", flush=True)
             delta_total += np.array([len(x) * bs * row_bytes for x in deltas], np.int64)
     got = np.array([r["stats"]["delta_bytes"] for r in res], np.int64)
     assert np.array_equal(got, delta_total), f"delta bytes {got.tolist()} != {delta_total.tolist()}"

@@ -46,6 +46,8 @@ def _check_all_units(w, h, r, units=None):
     todo = units or [(b, g) for b in range(w.batch) for g in range(w.n_kv_heads)]
     for b, g in todo:
         G = w.group
+        if w.ctx > 16384:
+            say(f"  oracle check of unit ({b},{g})")
         stats.append(T.oracle_unit_vs_gpu(
             w, h["q"], K, V, h["ctx"], h["label"], b, g, r["blk"][b, g], r["tok"][b, g],
             r["out"][b, g * G:(g + 1) * G], r["lse"][b, g * G:(g + 1) * G]))
