@@ -89,31 +89,31 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
     const int nb = (n + bs - 1) / bs;
     const uint16_t* qg = q + ((size_t)unit * G + hsel) * dk;
 
-    // label-channel A fragments (independent of the block selection)
+    // label-channel A fragments (independent of the block selection): entry
+    // e = threadIdx.x of the table (at most MT * KSr * 64 <= 2 * 8 * 64 of
+    // them, one per thread) has its channel indices and then its query
+    // values requested here; they are stored to LDS after the block stage,
+    // so their two dependent round trips overlap it
     const int MT = (Ge + 15) / 16;
     const int KSr = r / KK;               // matrix steps per label row
     constexpr int CPL = KK / 4;           // channels per lane per step
     constexpr int SMAX = MAX_R / KK;      // step stride of the fragment table
-    if (mode & 2) {
-        const int32_t* lab = label_ch + g * r;
-        for (int e = threadIdx.x; e < MT * KSr * 64; e += SEL_THREADS) {
-            const int l = e & 63, s = (e >> 6) % KSr, mt = e / (64 * KSr);
-            const int m = mt * 16 + (l & 15);
-            const int c0 = s * KK + (l >> 4) * CPL;
-            uint32_t x[CPL / 2];
+    const int n_frag = (mode & 2) ? MT * KSr * 64 : 0;
+    uint32_t xq[CPL / 2];
 #pragma unroll
-            for (int j = 0; j < CPL / 2; ++j) x[j] = 0u;
-            if (m < Ge) {
-                const uint16_t* qh = qg + (size_t)m * dk;
+    for (int j = 0; j < CPL / 2; ++j) xq[j] = 0u;
+    {
+        const int e = threadIdx.x;
+        const int l = e & 63, s = (e >> 6) % KSr, mt = e / (64 * KSr);
+        const int m = mt * 16 + (l & 15);
+        if (e < n_frag && m < Ge) {
+            const int32_t* lab = label_ch + g * r + s * KK + (l >> 4) * CPL;
+            const uint16_t* qh = qg + (size_t)m * dk;
+            int ch[CPL];
 #pragma unroll
-                for (int j = 0; j < CPL / 2; ++j)
-                    x[j] = (uint32_t)qh[clamp_ch(lab[c0 + 2 * j], dk)] |
-                           ((uint32_t)qh[clamp_ch(lab[c0 + 2 * j + 1], dk)] << 16);
-            }
-            if constexpr (KK == 32)
-                s_qa4[(mt * SMAX + s) * 64 + l] = make_uint4(x[0], x[1], x[2], x[3]);
-            else
-                s_qa[(mt * SMAX + s) * 64 + l] = make_uint2(x[0], x[1]);
+            for (int j = 0; j < CPL; ++j) ch[j] = clamp_ch(lab[j], dk);
+#pragma unroll
+            for (int j = 0; j < CPL / 2; ++j) xq[j] = (uint32_t)qh[ch[2 * j]] | ((uint32_t)qh[ch[2 * j + 1]] << 16);
         }
     }
 
@@ -158,6 +158,13 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
         for (int p = threadIdx.x; p < kb; p += SEL_THREADS) s_blk[p] = blk_idx[(size_t)sel * kb + p];
     }
     if (!(mode & 2)) return;
+    if (threadIdx.x < n_frag) {
+        const int e = threadIdx.x, l = e & 63, s = (e >> 6) % KSr, mt = e / (64 * KSr);
+        if constexpr (KK == 32)
+            s_qa4[(mt * SMAX + s) * 64 + l] = make_uint4(xq[0], xq[1], xq[2], xq[3]);
+        else
+            s_qa[(mt * SMAX + s) * 64 + l] = make_uint2(xq[0], xq[1]);
+    }
     __syncthreads();   // s_blk, s_qa and the selector's scratch settled
 
     // -------------------------------------------------- token label scores
