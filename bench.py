@@ -38,6 +38,7 @@ from hierarchical_sparse_attention_block_amd import workloads as W  # noqa: E402
 
 METRIC = "sparse-attn decode queries/s (batch×heads) at 48k/96k ctx; % HBM roofline"
 HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
 COUNTERS = os.path.join(ROOT, "profiles", "block_score_{wl}_counters.json")
 SCORE_SOURCES = ["hierarchical_sparse_attention_block_amd/csrc/score.hip",
                  "hierarchical_sparse_attention_block_amd/csrc/common.h"]
@@ -315,17 +316,47 @@ def decode(d, base, rep, stream):
                   base["label"], base["ctx"], rep.blk, rep.tok, rep.out, rep.lse, rep.ws, stream=stream)
 
 
-def cpu_baseline(w, host, budget_s=10.0, n_units=4):
-    """The CPU oracle on a bounded sample of the same step: the first
-    n_units (batch, KV head) units, converted to fp64 and with metadata
-    prebuilt outside the timed region, decoded repeatedly until about
-    budget_s seconds of oracle work. One thread (BLAS pinned to 1)."""
+_CPU_JOB = None   # (workload, prepared units) shared with forked workers
+
+
+def _cpu_decode_loop(k, n_workers, budget_s):
+    """Oracle decodes of units k, k + n_workers, ... of the prepared sample,
+    one BLAS thread, for about budget_s seconds. Returns (units, seconds)."""
     import oracle as O
     from threadpoolctl import threadpool_limits
+    w, units = _CPU_JOB
+    done, spent, i = 0, 0.0, k
+    with threadpool_limits(limits=1):
+        while spent < budget_s:
+            q, K, V, meta, lab = units[i % len(units)]
+            t0 = time.perf_counter()
+            O.decode_unit(q, K, V, w.ctx, w.block, w.k_blocks, lab, w.k_tokens, w.sm_scale, meta=meta)
+            spent += time.perf_counter() - t0
+            done += 1
+            i += n_workers
+    return done, spent
 
+
+def _cpu_worker(a):
+    return _cpu_decode_loop(*a)
+
+
+def cpu_baseline(w, host, budget_s=10.0, max_workers=16):
+    """The CPU oracle on a bounded sample of the same step: the first units
+    of the batch, converted to fp64 with metadata prebuilt outside the
+    timed region, decoded repeatedly for about budget_s seconds, once on one
+    core and once on every core this process may use (at most max_workers
+    worker processes, one BLAS thread each, each cycling over its own units;
+    rate = all queries decoded / wall time)."""
+    import multiprocessing as mp
+    import oracle as O
+    global _CPU_JOB
+    cpus = os.cpu_count()
+    avail = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else cpus
+    n_workers = max(1, min(avail, max_workers))
     G, n = w.group, w.ctx
     units = []
-    for u in range(min(n_units, w.units)):
+    for u in range(min(max(4, n_workers), w.units)):
         b, g = divmod(u, w.n_kv_heads)
         Kb = host["K"][b, g, :n].copy()
         Kb[n - 1] = host["k_new"][b, g]
@@ -339,30 +370,36 @@ def cpu_baseline(w, host, budget_s=10.0, n_units=4):
         q = O.bf16_to_f64(host["q"][b, g * G:(g + 1) * G])
         meta_fn = O.block_meta_e4m3 if w.meta_fp8 else O.block_meta
         units.append((q, K, V, meta_fn(K, n, w.block), host["label"][g]))
-    done, spent = 0, 0.0
-    with threadpool_limits(limits=1):
-        while spent < budget_s:
-            q, K, V, meta, lab = units[done % len(units)]
-            t0 = time.perf_counter()
-            O.decode_unit(q, K, V, n, w.block, w.k_blocks, lab, w.k_tokens, w.sm_scale, meta=meta)
-            spent += time.perf_counter() - t0
-            done += 1
-    return {"value": done * G / spent, "unit": "queries/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} unit decodes cycling over the first {len(units)} (batch, KV head) units of "
-                      f"the {w.name} step ({done * G} queries), fp64 NumPy, metadata prebuilt, {spent:.1f}s"}
+    _CPU_JOB = (w, units)
+    done1, spent1 = _cpu_decode_loop(0, 1, budget_s)
+    t0 = time.perf_counter()
+    with mp.get_context("fork").Pool(n_workers) as pool:
+        parts = pool.map(_cpu_worker, [(k, n_workers, budget_s) for k in range(n_workers)])
+    wall = time.perf_counter() - t0
+    done_all = sum(p[0] for p in parts)
+    _CPU_JOB = None
+    return {"value": round(done_all * G / wall, 2), "unit": "queries/s", "cores": n_workers, "kind": "oracle",
+            "os_cpu_count": cpus, "cores_available": avail,
+            "single_core": {"value": round(done1 * G / spent1, 2), "cores": 1,
+                            "sample": f"{done1} unit decodes cycling over the first {len(units)} units, {spent1:.1f}s"},
+            "sample": f"{done_all} unit decodes by {n_workers} worker processes (one BLAS thread each) over the first "
+                      f"{len(units)} (batch, KV head) units of the {w.name} step ({done_all * G} queries), fp64 "
+                      f"NumPy, metadata prebuilt, {wall:.1f}s wall"}
 
 
 PCIE_PEAK_GBS = 64.0   # PCIe 5.0 x16, one direction
 
 
-def offload_bench(args):
+def offload_bench(args, lite=False):
     """The multi-step offload run: 16 decode steps with drifting queries;
     the full cache sits in a pinned host pool, the GPU holds metadata,
     label rows and a block cache. One JSON line with the step rate over
     the steady steps (1..15), the delta bytes per step, the copy time and
     how much of it the compute stream did not wait for (overlap), next to
-    the same 16 steps on an HBM-resident cache."""
-    w = W.WORKLOADS[args.workload]
+    the same 16 steps on an HBM-resident cache. lite: host and GPU
+    planning only (no runtime-copy mode, no multi-layer loop, no CPU
+    baseline), returned instead of printed."""
+    w = W.WORKLOADS["offload96k"]
     if args.meta == "fp8":
         w = dataclasses.replace(w, meta_fp8=True)
     steps = W.OFFLOAD_STEPS
@@ -493,7 +530,7 @@ def offload_bench(args):
         }
 
     ms_step, off_k = timed_runs(H.COPY_KERNEL)
-    _, off_d = timed_runs(H.COPY_DMA)
+    off_d = None if lite else timed_runs(H.COPY_DMA)[1]
     _, off_g = timed_runs(H.COPY_KERNEL_GPU_PLAN)
 
     def multilayer(n_layers):
@@ -548,9 +585,10 @@ def offload_bench(args):
                 "copy_ms_per_layer_step": round(copy_ms / (n_layers * (steps - 2)), 4),
                 "overlap_hidden_frac": round(1.0 - waits / max(copy_ms, 1e-9), 4)}
 
-    multi = multilayer(4)
-    log(f"[bench] 4 layers: {multi['ms_per_step'] * 1e3:.1f} us/step, {multi['ms_per_layer'] * 1e3:.1f} us/layer, "
-        f"{100 * multi['overlap_hidden_frac']:.0f}% of copies hidden")
+    multi = None if lite else multilayer(4)
+    if multi:
+        log(f"[bench] 4 layers: {multi['ms_per_step'] * 1e3:.1f} us/step, {multi['ms_per_layer'] * 1e3:.1f} "
+            f"us/layer, {100 * multi['overlap_hidden_frac']:.0f}% of copies hidden")
 
     # the same 16 steps on an HBM-resident cache (no offload), for reference
     meta.copy_(meta0)
@@ -583,10 +621,32 @@ def offload_bench(args):
         "offload_gpu_plan": off_g,
         "multilayer": multi,
     }
+    if lite:
+        return res
     if not args.no_cpu:
         log("[bench] timing the CPU oracle on a bounded sample")
         res["cpu_baseline"] = offload_cpu_baseline(w, prefill, qs, news, Kv, Vv)
     print(json.dumps(res), flush=True)
+
+
+def offload_summary(args):
+    """The offload run's figures for the default bench line: step time and
+    rate with host and with GPU planning, delta bytes per step, link rate
+    and the share of the copy time hidden behind compute."""
+    r = offload_bench(args, lite=True)
+    out = {"workload": "offload96k", "prefill": r["config"]["prefill"], "steps": W.OFFLOAD_STEPS,
+           "resident_ms_per_step": r["resident_ms_per_step"]}
+    for key, src in (("host_plan", r["offload"]), ("gpu_plan", r["offload_gpu_plan"])):
+        out[key] = {"ms_per_step": src["ms_per_step"],
+                    "queries_per_s": round(r["config"]["batch"] * r["config"]["q_heads"]
+                                           / (src["ms_per_step"] * 1e-3), 1),
+                    "delta_bytes_mean": src["delta_bytes_mean"], "delta_frac_of_full": src["delta_frac_of_full"],
+                    "link_gbs": src["link"]["achieved"], "link_frac": src["link"]["frac"],
+                    "overlap_hidden_frac": src["overlap_hidden_frac"], "copy_ms_mean": src["copy_ms_mean"],
+                    "host_call_ms_mean": src["host_call_ms_mean"]}
+    log(f"[bench] offload: host plan {out['host_plan']['ms_per_step'] * 1e3:.1f} us/step, GPU plan "
+        f"{out['gpu_plan']['ms_per_step'] * 1e3:.1f} us/step, resident {out['resident_ms_per_step'] * 1e3:.1f}")
+    return out
 
 
 def offload_cpu_baseline(w, prefill, qs, news, Kv, Vv, budget_s=10.0):
@@ -616,6 +676,109 @@ def offload_cpu_baseline(w, prefill, qs, news, Kv, Vv, budget_s=10.0):
                       f"({done * steps * G} queries), fp64 NumPy, {spent:.1f}s"}
 
 
+def layer_leg(w, args, full):
+    """Stage workload w, time its decode step (grouped graph replay and one
+    graph launch per step) and its block-score launches; full: also the
+    dense reference, the fp8 and the selection-variant legs. Returns the
+    result dict and the host arrays (for the CPU baseline)."""
+    d, base, host = stage(w, args.threads)
+    sb = step_bytes(w)
+    R = args.replicas or max(4, math.ceil(768e6 / sb["total"]))
+    reps = [Replica(d, base)]
+    for _ in range(R - 1):
+        reps.append(Replica(d, base, clone_from={"K": reps[0].K, "V": reps[0].V, "meta": reps[0].meta,
+                                                 "klabel": reps[0].klabel}))
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+
+    # the timed loop replays graphs of `group` consecutive steps (the way a
+    # model captures the layers of one token step in one graph); one graph
+    # launch per step is timed too and reported beside it
+    group = graph_group(args.steps) if not args.no_graph else 1
+    step_fns = [(lambda r=r: decode(d, base, r, stream)) for r in reps]
+    ms_step = time_replays(step_fns, stream, args.warmup, args.steps, not args.no_graph, group)
+    ms_step_single = time_replays(step_fns, stream, args.warmup, args.steps, True, 1) if not args.no_graph else None
+    log(f"[bench] {w.name}: {args.steps} steps: {ms_step * 1e3:.1f} us/step (events)")
+
+    # dominant kernel alone: a graph of back-to-back block-score launches
+    us_score = time_score_launches(d, base, [r.meta for r in reps], reps, stream, args.steps)
+    kb = score_kernel_bytes(w)
+    achieved = kb / (us_score * 1e-6) / 1e9
+
+    traffic = None
+    cpath = COUNTERS.format(wl=w.name + ("_fp8" if w.meta_fp8 else ""))
+    if os.path.exists(cpath):
+        c = json.load(open(cpath))
+        if c.get("source_hash") == source_hash(SCORE_SOURCES):
+            traffic = c.get("bytes_per_launch")
+
+    queries = w.batch * w.n_q_heads
+    res = {
+        "value": round(queries / (ms_step * 1e-3), 1), "ms_per_step": round(ms_step, 6),
+        "config": {"workload": w.name, "batch": w.batch, "q_heads": w.n_q_heads, "kv_heads": w.n_kv_heads,
+                   "d_k": w.d_k, "d_v": w.d_v, "ctx": w.ctx, "block": w.block, "k_blocks": w.k_blocks,
+                   "r": w.r, "k_tokens": w.k_tokens, "meta": "fp8_e4m3_outward" if w.meta_fp8 else "bf16",
+                   "cache_replicas": R, "hip_graph": not args.no_graph, "steps_per_graph": group,
+                   "parallelism": "none (1 GPU)"},
+        "ms_per_step_one_graph_per_step": None if ms_step_single is None else round(ms_step_single, 6),
+        "hbm_frac_step": round(sb["total"] / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "step_bytes": sb["total"],
+        "roofline": {"kernel": "block_score", "bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "algorithmic_bytes": kb, "us_per_launch": round(us_score, 3)},
+    }
+    if w.group > 1:
+        # the block score as a matrix product on the matrix cores: G heads x
+        # 2 d_k stacked channels per block, 2 flops per multiply-add
+        flops = 2 * w.group * 2 * w.d_k * w.units * (-(-w.ctx // w.block))
+        tf = flops / (us_score * 1e-6) / 1e12
+        res["score_gemm"] = {"flops_per_launch": flops, "achieved_tflops": round(tf, 2),
+                             "peak_tflops_bf16_dense": MFMA_PEAK_TFLOPS,
+                             "frac_of_mfma_peak": round(tf / MFMA_PEAK_TFLOPS, 4),
+                             "flop_per_byte": round(flops / kb, 2)}
+    if full:
+        # full attention over every token on the same caches: the operator the
+        # sparse step replaces (the pages report the sparse speedup over it)
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        dws = H.dense_workspace_bytes(d)
+        if dws:
+            dout = torch.empty(w.batch * w.n_q_heads * w.d_v, device="cuda")
+            dlse = torch.empty(w.batch * w.n_q_heads, device="cuda")
+            dwsb = torch.empty(dws, dtype=torch.uint8, device="cuda")
+            gd = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(stream):
+                H.dense_attend(d, base["q"], reps[0].K, reps[0].V, base["ctx"], dout, dlse, dwsb, stream=stream)
+            torch.cuda.synchronize()
+            with torch.cuda.graph(gd, stream=stream):
+                for r in reps:
+                    H.dense_attend(d, base["q"], r.K, r.V, base["ctx"], dout, dlse, dwsb, stream=stream)
+            with torch.cuda.stream(stream):
+                gd.replay()
+            torch.cuda.synchronize()
+            n_rep = max(1, args.steps // (4 * R))
+            with torch.cuda.stream(stream):
+                ev0.record(stream)
+                for _ in range(n_rep):
+                    gd.replay()
+                ev1.record(stream)
+            torch.cuda.synchronize()
+            ms_dense = ev0.elapsed_time(ev1) / (n_rep * R)
+            dbytes = w.units * w.ctx * (w.d_k + (0 if w.v_alias_k else w.d_v)) * 2
+            res["dense_reference"] = {"ms_per_call": round(ms_dense, 6), "kv_bytes": dbytes,
+                                      "achieved_gbs": round(dbytes / (ms_dense * 1e-3) / 1e9, 1),
+                                      "speedup_sparse_step_vs_dense": round(ms_dense / ms_step, 3)}
+            log(f"[bench] dense attention {ms_dense * 1e3:.1f} us/call, sparse step {ms_step * 1e3:.1f} us "
+                f"({ms_dense / ms_step:.2f}x)")
+        if not w.meta_fp8 and not args.no_fp8_leg and w.d_k % 32 == 0:
+            res["meta_fp8"] = fp8_meta_leg(w, base, reps, stream, args, ms_step)
+        if not args.no_fp8_leg:
+            res["variants"] = variants_leg(w, base, reps, stream, args, ms_step)
+    del reps, base
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res, host
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -630,6 +793,8 @@ def main():
                     help="block metadata format of the timed step (fp8: e4m3, rounded outward)")
     ap.add_argument("--no-fp8-leg", action="store_true",
                     help="skip the extra timings (fp8 metadata, selection variants, calibration)")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the 96k, latent and offload legs of the default run")
     ap.add_argument("--offload-runs", type=int, default=3, help="timed 16-step runs of the offload workload")
     ap.add_argument("--score-only", type=int, default=0,
                     help="only launch the block-score kernel this many times (for counter runs)")
@@ -647,6 +812,36 @@ def main():
     if w.name == "offload96k":
         offload_bench(args)
         return
+    if args.score_only:
+        score_only(w, args)
+        return
+
+    leg, host = layer_leg(w, args, full=True)
+    res = {"metric": METRIC, "value": leg.pop("value"), "unit": "queries/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": leg.pop("ms_per_step"), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic"}
+    res.update(leg)
+    if args.workload == "gqa48k" and args.meta == "bf16" and not args.no_extra:
+        # the other layers the metric is quoted on, measured in the same run
+        for key, name in (("ctx96k", "gqa96k"), ("mla64k", "mla64k")):
+            sub, _ = layer_leg(W.WORKLOADS[name], args, full=False)
+            sub["queries_per_s"] = sub.pop("value")
+            res[key] = sub
+        mpath = os.path.join(ROOT, "profiles", "block_score_mla64k_mfma_counters.json")
+        if os.path.exists(mpath):
+            c = json.load(open(mpath))
+            if c.get("source_hash") == source_hash(SCORE_SOURCES):
+                res["mla64k"]["score_gemm"]["mfma_busy_frac_counters"] = c.get("mfma_busy_frac")
+        res["offload"] = offload_summary(args)
+    if not args.no_cpu:
+        log("[bench] timing the CPU oracle on a bounded sample")
+        res["cpu_baseline"] = cpu_baseline(w, host)
+    print(json.dumps(res), flush=True)
+
+
+def score_only(w, args):
+    """Block-score launches alone (for counter runs), then a plain copy of
+    known size as the last kernel, for calibrating the counters."""
     d, base, host = stage(w, args.threads)
     sb = step_bytes(w)
     R = args.replicas or max(4, math.ceil(768e6 / sb["total"]))
@@ -656,106 +851,18 @@ def main():
                                                  "klabel": reps[0].klabel}))
     torch.cuda.synchronize()
     stream = torch.cuda.Stream()
-
-    if args.score_only:
-        with torch.cuda.stream(stream):
-            for i in range(args.score_only):
-                r = reps[i % R]
-                H.score_blocks(d, base["q"], r.meta, base["ctx_prefill"], r.score, stream=stream)
-            # plain copy of known size for counter calibration: 1 GiB of
-            # initialized data, the last kernel this mode launches
-            a = torch.ones(256 << 20, dtype=torch.float32, device="cuda")
-            b = torch.empty_like(a)
-            torch.cuda.synchronize()
-            b.copy_(a)
+    with torch.cuda.stream(stream):
+        for i in range(args.score_only):
+            r = reps[i % R]
+            H.score_blocks(d, base["q"], r.meta, base["ctx_prefill"], r.score, stream=stream)
+        # plain copy of known size for counter calibration: 1 GiB of
+        # initialized data, the last kernel this mode launches
+        a = torch.ones(256 << 20, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
         torch.cuda.synchronize()
-        log(f"[bench] score-only: {args.score_only} launches, then a copy of {a.numel() * 4} bytes")
-        return
-
-    # the timed loop replays graphs of `group` consecutive steps (the way a
-    # model captures the layers of one token step in one graph); one graph
-    # launch per step is timed too and reported beside it
-    group = graph_group(args.steps) if not args.no_graph else 1
-    step_fns = [(lambda r=r: decode(d, base, r, stream)) for r in reps]
-    ms_step = time_replays(step_fns, stream, args.warmup, args.steps, not args.no_graph, group)
-    ms_step_single = time_replays(step_fns, stream, args.warmup, args.steps, True, 1) if not args.no_graph else None
-    log(f"[bench] {args.steps} steps: {ms_step * 1e3:.1f} us/step (events)")
-
-    # dominant kernel alone: a graph of back-to-back block-score launches
-    us_score = time_score_launches(d, base, [r.meta for r in reps], reps, stream, args.steps)
-    kb = score_kernel_bytes(w)
-    achieved = kb / (us_score * 1e-6) / 1e9
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-
-    traffic = None
-    cpath = COUNTERS.format(wl=w.name + ("_fp8" if w.meta_fp8 else ""))
-    if os.path.exists(cpath):
-        c = json.load(open(cpath))
-        if c.get("source_hash") == source_hash(SCORE_SOURCES):
-            traffic = c.get("bytes_per_launch")
-
-    # full attention over every token on the same caches: the operator the
-    # sparse step replaces (the pages report the sparse speedup over it)
-    dense = None
-    dws = H.dense_workspace_bytes(d)
-    if dws:
-        dout = torch.empty(w.batch * w.n_q_heads * w.d_v, device="cuda")
-        dlse = torch.empty(w.batch * w.n_q_heads, device="cuda")
-        dwsb = torch.empty(dws, dtype=torch.uint8, device="cuda")
-        gd = torch.cuda.CUDAGraph()
-        with torch.cuda.stream(stream):
-            H.dense_attend(d, base["q"], reps[0].K, reps[0].V, base["ctx"], dout, dlse, dwsb, stream=stream)
-        torch.cuda.synchronize()
-        with torch.cuda.graph(gd, stream=stream):
-            for r in reps:
-                H.dense_attend(d, base["q"], r.K, r.V, base["ctx"], dout, dlse, dwsb, stream=stream)
-        with torch.cuda.stream(stream):
-            gd.replay()
-        torch.cuda.synchronize()
-        n_rep = max(1, args.steps // (4 * R))
-        with torch.cuda.stream(stream):
-            ev0.record(stream)
-            for _ in range(n_rep):
-                gd.replay()
-            ev1.record(stream)
-        torch.cuda.synchronize()
-        ms_dense = ev0.elapsed_time(ev1) / (n_rep * R)
-        dbytes = w.units * w.ctx * (w.d_k + (0 if w.v_alias_k else w.d_v)) * 2
-        dense = {"ms_per_call": round(ms_dense, 6), "kv_bytes": dbytes,
-                 "achieved_gbs": round(dbytes / (ms_dense * 1e-3) / 1e9, 1),
-                 "speedup_sparse_step_vs_dense": round(ms_dense / ms_step, 3)}
-        log(f"[bench] dense attention {ms_dense * 1e3:.1f} us/call, sparse step {ms_step * 1e3:.1f} us "
-            f"({ms_dense / ms_step:.2f}x)")
-
-    queries = w.batch * w.n_q_heads
-    value = queries / (ms_step * 1e-3)
-    res = {
-        "metric": METRIC, "value": round(value, 1), "unit": "queries/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 6),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": w.name, "batch": w.batch, "q_heads": w.n_q_heads, "kv_heads": w.n_kv_heads,
-                   "d_k": w.d_k, "d_v": w.d_v, "ctx": w.ctx, "block": w.block, "k_blocks": w.k_blocks,
-                   "r": w.r, "k_tokens": w.k_tokens, "meta": "fp8_e4m3_outward" if w.meta_fp8 else "bf16",
-                   "cache_replicas": R, "hip_graph": not args.no_graph, "steps_per_graph": group,
-                   "parallelism": "none (1 GPU)"},
-        "ms_per_step_one_graph_per_step": None if ms_step_single is None else round(ms_step_single, 6),
-        "hbm_frac_step": round(sb["total"] / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-        "step_bytes": sb["total"],
-        "roofline": {"kernel": "block_score", "bound": "hbm", "achieved": round(achieved, 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "algorithmic_bytes": kb, "us_per_launch": round(us_score, 3)},
-    }
-    if dense is not None:
-        res["dense_reference"] = dense
-    if not w.meta_fp8 and not args.no_fp8_leg and w.d_k % 32 == 0:
-        res["meta_fp8"] = fp8_meta_leg(w, base, reps, stream, args, ms_step)
-    if not args.no_fp8_leg:
-        res["variants"] = variants_leg(w, base, reps, stream, args, ms_step)
-    if not args.no_cpu:
-        log("[bench] timing the CPU oracle on a bounded sample")
-        res["cpu_baseline"] = cpu_baseline(w, host)
-    print(json.dumps(res), flush=True)
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"[bench] score-only: {args.score_only} launches, then a copy of {a.numel() * 4} bytes")
 
 
 if __name__ == "__main__":
