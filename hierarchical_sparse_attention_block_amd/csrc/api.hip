@@ -5,6 +5,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "kernels.h"
 
 namespace hsab {
@@ -108,6 +110,60 @@ static int attend_step(const Shape& s, const uint16_t* q, const uint16_t* K, con
                                     reinterpret_cast<float*>(w + L.part_acc), out, lse, stream));
 }
 
+static int decode_step_ws(const hsab_dims* dims, const uint16_t* q, const uint16_t* k_new,
+                          const uint16_t* v_new, uint16_t* K, uint16_t* V, uint16_t* meta,
+                          uint16_t* klabel, const int32_t* label_ch, const int32_t* ctx_len,
+                          int32_t* blk_idx, int32_t* tok_idx, float* out, float* lse, void* ws,
+                          size_t ws_bytes, hipStream_t stream) {
+    int rc = check_dims(dims);
+    if (rc) return rc;
+    const Shape s = make_shape(*dims);
+    if (!q || !k_new || !K || !meta || !klabel || !label_ch || !ctx_len || !blk_idx || !tok_idx ||
+        !out || !lse)
+        return HSAB_EINVAL;
+    if (!s.valias && (!V || !v_new)) return HSAB_EINVAL;
+    const WsLayout L = ws_layout(s);
+    if (!ws || ws_bytes < L.total) return HSAB_EINVAL;
+    if (!attend_supported(s)) return HSAB_EUNSUPPORTED;
+    char* w = static_cast<char*>(ws);
+    float* scores = reinterpret_cast<float*>(w + L.blk_score);
+    uint32_t* sel_keys = reinterpret_cast<uint32_t*>(w + L.sel_keys);
+    int32_t* sel_cnt = reinterpret_cast<int32_t*>(w + L.sel_cnt);
+    // 1) append + block scores (and zeroed selection counters); 2) top-K_b,
+    // label scores, top-K_t; 3) split attention and the merge of its partials
+    rc = hip_status(launch_block_score(s, q, meta, ctx_len, scores, k_new, v_new, K, V, klabel, label_ch,
+                                       sel_cnt, stream));
+    if (rc) return rc;
+    rc = hip_status(launch_select(s, 3, q, scores, klabel, label_ch, ctx_len, blk_idx, tok_idx, nullptr,
+                                  sel_keys, sel_cnt, stream));
+    if (rc) return rc;
+    return attend_step(s, q, K, s.valias ? K : V, tok_idx, ctx_len, nullptr, 0, w, L, out, lse, stream);
+}
+
+// The allocation-free step's workspace: one fixed array per GPU, held from
+// the library's first use on that GPU until the process ends. Host code
+// never passes `scratch` itself (its host-side name is no device address);
+// it passes the address hipGetSymbolAddress gives for the current device.
+static __device__ __align__(256) unsigned char scratch[HSAB_SCRATCH_BYTES];
+constexpr int SCRATCH_DEVICES = 64;
+static void* g_scratch_ptr[SCRATCH_DEVICES];
+static hipError_t g_scratch_err[SCRATCH_DEVICES];
+static std::once_flag g_scratch_once[SCRATCH_DEVICES];
+
+// Device address of the current device's scratch array, looked up once per
+// device (with that device current).
+static hipError_t scratch_address(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= SCRATCH_DEVICES) return hipErrorInvalidDevice;
+    std::call_once(g_scratch_once[dev], [dev] {
+        g_scratch_err[dev] = hipGetSymbolAddress(&g_scratch_ptr[dev], HIP_SYMBOL(scratch));
+    });
+    if (g_scratch_err[dev] != hipSuccess) return g_scratch_err[dev];
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
 }  // namespace hsab
 
 using namespace hsab;
@@ -125,6 +181,7 @@ const char* hsab_status_string(int status) {
         case HSAB_EINVAL: return "invalid argument";
         case HSAB_EHIP: return "HIP launch or runtime error";
         case HSAB_EUNSUPPORTED: return "shape not supported by the available kernels";
+        case HSAB_ESCRATCH: return "workspace larger than the static scratch of hsab_decode_step_noalloc";
         default: return "unknown status";
     }
 }
@@ -199,34 +256,32 @@ int hsab_sparse_attend(const hsab_dims* dims, const uint16_t* q, const uint16_t*
     return attend_step(s, q, K, s.valias ? K : V, tok_idx, ctx_len, slot_of, n_slots, w, L, out, lse, stream);
 }
 
+
 int hsab_decode_step(const hsab_dims* dims, const uint16_t* q, const uint16_t* k_new,
                      const uint16_t* v_new, uint16_t* K, uint16_t* V, uint16_t* meta,
                      uint16_t* klabel, const int32_t* label_ch, const int32_t* ctx_len,
                      int32_t* blk_idx, int32_t* tok_idx, float* out, float* lse, void* ws,
                      size_t ws_bytes, hipStream_t stream) {
+    return decode_step_ws(dims, q, k_new, v_new, K, V, meta, klabel, label_ch, ctx_len, blk_idx, tok_idx, out,
+                          lse, ws, ws_bytes, stream);
+}
+
+int hsab_decode_step_noalloc(const hsab_dims* dims, const uint16_t* q, const uint16_t* k_new,
+                             const uint16_t* v_new, uint16_t* K, uint16_t* V, uint16_t* meta,
+                             uint16_t* klabel, const int32_t* label_ch, const int32_t* ctx_len,
+                             int32_t* blk_idx, int32_t* tok_idx, float* out, float* lse, hipStream_t stream) {
     int rc = check_dims(dims);
     if (rc) return rc;
-    const Shape s = make_shape(*dims);
-    if (!q || !k_new || !K || !meta || !klabel || !label_ch || !ctx_len || !blk_idx || !tok_idx ||
-        !out || !lse)
-        return HSAB_EINVAL;
-    if (!s.valias && (!V || !v_new)) return HSAB_EINVAL;
-    const WsLayout L = ws_layout(s);
-    if (!ws || ws_bytes < L.total) return HSAB_EINVAL;
-    if (!attend_supported(s)) return HSAB_EUNSUPPORTED;
-    char* w = static_cast<char*>(ws);
-    float* scores = reinterpret_cast<float*>(w + L.blk_score);
-    uint32_t* sel_keys = reinterpret_cast<uint32_t*>(w + L.sel_keys);
-    int32_t* sel_cnt = reinterpret_cast<int32_t*>(w + L.sel_cnt);
-    // 1) append + block scores (and zeroed selection counters); 2) top-K_b,
-    // label scores, top-K_t; 3) split attention and the merge of its partials
-    rc = hip_status(launch_block_score(s, q, meta, ctx_len, scores, k_new, v_new, K, V, klabel, label_ch,
-                                       sel_cnt, stream));
+    const size_t need = ws_layout(make_shape(*dims)).total;
+    if (need > HSAB_SCRATCH_BYTES) return HSAB_ESCRATCH;
+    void* ws = nullptr;
+    rc = hip_status(scratch_address(&ws));
     if (rc) return rc;
-    rc = hip_status(launch_select(s, 3, q, scores, klabel, label_ch, ctx_len, blk_idx, tok_idx, nullptr,
-                                  sel_keys, sel_cnt, stream));
-    if (rc) return rc;
-    return attend_step(s, q, K, s.valias ? K : V, tok_idx, ctx_len, nullptr, 0, w, L, out, lse, stream);
+    // the workspace needs no clearing: the selection counters in it are set
+    // to zero by the step's first kernel, everything else is written before
+    // it is read
+    return decode_step_ws(dims, q, k_new, v_new, K, V, meta, klabel, label_ch, ctx_len, blk_idx, tok_idx, out,
+                          lse, ws, HSAB_SCRATCH_BYTES, stream);
 }
 
 int hsab_calibrate_labels(const hsab_dims* dims, const uint16_t* q_samples, const uint16_t* k_samples,

@@ -20,11 +20,12 @@ if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run `python -m hierarchical_sparse_attention_block_amd.build`")
 _lib = ctypes.CDLL(LIB_PATH)
 
-HSAB_OK, HSAB_EINVAL, HSAB_EHIP, HSAB_EUNSUPPORTED = 0, -1, -2, -3
+HSAB_OK, HSAB_EINVAL, HSAB_EHIP, HSAB_EUNSUPPORTED, HSAB_ESCRATCH = 0, -1, -2, -3, -4
+SCRATCH_BYTES = 16 << 20   # HSAB_SCRATCH_BYTES: the static workspace of decode_step_noalloc
 COPY_KERNEL, COPY_DMA, COPY_KERNEL_GPU_PLAN = 0, 1, 2   # HSAB_OFFLOAD_COPY_*
 EXPORTS = ("hsab_workspace_bytes", "hsab_status_string", "hsab_last_hip_error", "hsab_build_meta",
            "hsab_score_blocks", "hsab_select_blocks", "hsab_select_tokens", "hsab_sparse_attend",
-           "hsab_decode_step", "hsab_offload_append", "hsab_offload_plan", "hsab_offload_copy", "hsab_offload_create",
+           "hsab_decode_step", "hsab_decode_step_noalloc", "hsab_offload_append", "hsab_offload_plan", "hsab_offload_copy", "hsab_offload_create",
            "hsab_offload_destroy", "hsab_offload_begin", "hsab_offload_step", "hsab_offload_timing",
            "hsab_offload_set_timing", "hsab_offload_selection", "hsab_offload_step_selection", "hsab_offload_step_delta",
            "hsab_dense_workspace_bytes", "hsab_dense_attend",
@@ -80,6 +81,8 @@ _lib.hsab_select_tokens.argtypes = [_D, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, 
 _lib.hsab_sparse_attend.argtypes = [_D, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _sz, _vp]
 _lib.hsab_decode_step.argtypes = [_D, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                   _vp, _sz, _vp]
+_lib.hsab_decode_step_noalloc.argtypes = [_D, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                          _vp, _vp]
 _lib.hsab_offload_append.argtypes = [_D, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
 _lib.hsab_offload_plan.argtypes = [_D, _i32, _vp, _vp, _vp, _vp, _vp, _vp]
 _lib.hsab_offload_copy.argtypes = [_D, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp]
@@ -308,6 +311,23 @@ def decode_step(d: Dims, q, k_new, v_new, K, V, meta, klabel, label_ch, ctx_len,
         _buf("ctx_len", ctx_len, _i, s["ctx"]), _buf("blk_idx", blk_idx, _i, s["blk"]),
         _buf("tok_idx", tok_idx, _i, s["tok"]), _buf("out", out, _f, s["out"]),
         _buf("lse", lse, _f, s["lse"]), wp, wn, _stream(stream)))
+
+
+def decode_step_noalloc(d: Dims, q, k_new, v_new, K, V, meta, klabel, label_ch, ctx_len, blk_idx, tok_idx,
+                        out, lse, stream=None):
+    """decode_step on the library's static per-GPU workspace (no workspace
+    argument; raises with HSAB_ESCRATCH when the shape needs more than
+    SCRATCH_BYTES)."""
+    s = _sizes(d)
+    alias = bool(d.v_alias_k)
+    _check("hsab_decode_step_noalloc", _lib.hsab_decode_step_noalloc(
+        ctypes.byref(d), _buf("q", q, _u16, s["q"]), _buf("k_new", k_new, _u16, s["knew"]),
+        _buf("v_new", v_new, _u16, s["vnew"], allow_none=alias), _buf("K", K, _u16, s["K"]),
+        _buf("V", V, _u16, s["V"], allow_none=alias), _meta(d, meta),
+        _klabel(d, klabel), _buf("label_ch", label_ch, _i, s["label"]),
+        _buf("ctx_len", ctx_len, _i, s["ctx"]), _buf("blk_idx", blk_idx, _i, s["blk"]),
+        _buf("tok_idx", tok_idx, _i, s["tok"]), _buf("out", out, _f, s["out"]),
+        _buf("lse", lse, _f, s["lse"]), _stream(stream)))
 
 
 def block_elems(d: Dims) -> int:

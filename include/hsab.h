@@ -88,6 +88,7 @@ extern "C" {
 #define HSAB_EINVAL       -1   /* bad argument: null pointer, shape, budget, workspace too small */
 #define HSAB_EHIP         -2   /* a HIP launch or runtime call failed */
 #define HSAB_EUNSUPPORTED -3   /* valid shape with no kernel instantiation (see limits below) */
+#define HSAB_ESCRATCH     -4   /* hsab_decode_step_noalloc: workspace beyond HSAB_SCRATCH_BYTES */
 
 /* Shape and budget of one decode layer.
  * Limits: 1 <= G <= 32; d_k % 16 == 0, 16 <= d_k <= 1024 (d_k % 32 == 0
@@ -237,6 +238,24 @@ int hsab_decode_step(const hsab_dims* dims, const uint16_t* q, const uint16_t* k
                      uint16_t* klabel, const int32_t* label_ch, const int32_t* ctx_len,
                      int32_t* blk_idx, int32_t* tok_idx, float* out, float* lse,
                      void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* hsab_decode_step without a workspace argument, for callers that cannot
+ * allocate device memory (code under graph capture, serving loops or
+ * harnesses that forbid allocation): the same kernels run on a static
+ * array of HSAB_SCRATCH_BYTES held by the library on each GPU it runs on
+ * (from its first use there until the process ends). The array of the
+ * calling thread's current device is used, so `stream` must belong to that
+ * device. Nothing is allocated or freed. Returns HSAB_ESCRATCH, before any
+ * launch, when hsab_workspace_bytes(dims) > HSAB_SCRATCH_BYTES (every
+ * workload of this library's benchmarks fits; per-query-head selection at
+ * 96k context does not); otherwise as hsab_decode_step. All calls on one
+ * GPU share its array: calls that overlap in time on one GPU (concurrent
+ * streams, or several threads) race and give undefined results. */
+#define HSAB_SCRATCH_BYTES ((size_t)16 << 20)
+int hsab_decode_step_noalloc(const hsab_dims* dims, const uint16_t* q, const uint16_t* k_new,
+                             const uint16_t* v_new, uint16_t* K, uint16_t* V, uint16_t* meta,
+                             uint16_t* klabel, const int32_t* label_ch, const int32_t* ctx_len,
+                             int32_t* blk_idx, int32_t* tok_idx, float* out, float* lse, hipStream_t stream);
 
 /* ------------------------------------------------- label-channel calibration
  * The offline step that chooses the label channels the fine stage scores

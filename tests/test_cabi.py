@@ -122,3 +122,17 @@ def test_status_strings():
         assert H.status_string(s) not in ("ok", "unknown status")
     assert H.status_string(12345) == "unknown status"
     assert H.raw_call("hsab_last_hip_error") == 0
+
+
+def test_noalloc_refuses_oversize_before_any_gpu_call():
+    """hsab_decode_step_noalloc checks the workspace a shape needs against
+    its static scratch before touching a GPU: per-head selection at 96k
+    needs more and is refused with HSAB_ESCRATCH."""
+    from hierarchical_sparse_attention_block_amd import workloads as W
+    from tests.hsab_testlib import dims_of
+    d = dims_of(W.WORKLOADS["gqa96k"].replace(per_head=True))
+    assert H.workspace_bytes(d) > H.SCRATCH_BYTES
+    p = ctypes.c_void_p(16)
+    assert H.raw_call("hsab_decode_step_noalloc", ctypes.byref(d), p, p, p, p, p, p, p, p, p, p, p, p, p,
+                      None) == H.HSAB_ESCRATCH
+    assert b"static scratch" in H._lib.hsab_status_string(H.HSAB_ESCRATCH)
