@@ -131,8 +131,9 @@ static int decode_step_ws(const hsab_dims* dims, const uint16_t* q, const uint16
     int32_t* sel_cnt = reinterpret_cast<int32_t*>(w + L.sel_cnt);
     // 1) append + block scores (and zeroed selection counters); 2) top-K_b,
     // label scores, top-K_t; 3) split attention and the merge of its partials
-    rc = hip_status(launch_block_score(s, q, meta, ctx_len, scores, k_new, v_new, K, V, klabel, label_ch,
-                                       sel_cnt, stream));
+    const Handoff ho{sel_cnt, sel_keys, s.kb * s.bs};
+    rc = hip_status(launch_block_score(s, q, meta, ctx_len, scores, k_new, v_new, K, V, klabel, label_ch, &ho,
+                                       stream));
     if (rc) return rc;
     rc = hip_status(launch_select(s, 3, q, scores, klabel, label_ch, ctx_len, blk_idx, tok_idx, nullptr,
                                   sel_keys, sel_cnt, stream));

@@ -47,18 +47,30 @@ WsLayout ws_layout(const Shape& s);
 hipError_t launch_build_meta(const Shape& s, const uint16_t* K, const int32_t* ctx_len,
                              const int32_t* label_ch, uint16_t* meta, uint16_t* klabel,
                              hipStream_t st);
+// A split token selection's shared state in the workspace: one arrival
+// counter per selection ([U * heads]) and the candidate keys the parts
+// publish ([U * heads][K_b * block]). The block-score launch of the same
+// step sets every counter to zero and every key to KEY_PENDING, a value no
+// key takes (0 marks an empty candidate; f32_key maps every number to
+// 0x007fffff or more), so the part that arrives last can tell a key not yet
+// visible to it from a stored one.
+struct Handoff {
+    int32_t* cnt;
+    uint32_t* keys;
+    int keys_per_sel;
+};
+constexpr uint32_t KEY_PENDING = 1u;
 // Block scores ([U][nb_cap], or [U][G][nb_cap] with per-head selection);
-// with k_new non-null the decode-step append runs first. sel_cnt
-// (nullable): the arrival counters ([U * heads]) of a following split
-// token selection, set to zero here.
+// with k_new non-null the decode-step append runs first. ho (nullable): the
+// shared state of a following split token selection, reset here.
 hipError_t launch_block_score(const Shape& s, const uint16_t* q, uint16_t* meta, const int32_t* ctx_len,
                               float* score, const uint16_t* k_new, const uint16_t* v_new, uint16_t* K,
-                              uint16_t* V, uint16_t* klabel, const int32_t* label_ch, int32_t* sel_cnt,
+                              uint16_t* V, uint16_t* klabel, const int32_t* label_ch, const Handoff* ho,
                               hipStream_t st);
 // mode bit 1: select blocks from block scores; bit 2: score + select tokens.
-// With sel_keys and sel_cnt non-null (counters zero on entry, zero again on
-// exit) the token stage of each selection is spread over several
-// workgroups. Per-head selection runs U * G selections, each of one query
+// With sel_keys and sel_cnt non-null (counters zero and keys KEY_PENDING on
+// entry: the block-score launch of the step resets them, see Handoff) the
+// token stage of each selection is spread over several workgroups. Per-head selection runs U * G selections, each of one query
 // head (block lists [U][G][K_b], token lists [U][G][K_t]). blk_copy
 // (nullable): a second buffer that receives the same block lists (e.g.
 // host memory mapped into the GPU).

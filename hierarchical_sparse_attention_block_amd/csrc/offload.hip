@@ -776,8 +776,9 @@ hipError_t offload_step(hsab_offload_engine* e, const uint16_t* q, const uint16_
     HSAB_TRY(mark(0, cs));
     HSAB_TRY(launch_append_slot(s, e->n_slots, k_new, v_new, cache, meta, klabel, label_ch, ctx_len, cs, pool_dev,
                                 ctx_snap));
+    const Handoff ho{sel_cnt, sel_keys, s.kb * s.bs};
     HSAB_TRY(launch_block_score(s, q, meta, ctx_len, blk_score, nullptr, nullptr, nullptr, nullptr, nullptr,
-                                nullptr, sel_cnt, cs));
+                                nullptr, &ho, cs));
     HSAB_TRY(launch_select(s, 1, q, blk_score, nullptr, nullptr, ctx_len, sel_now, nullptr, nullptr, nullptr,
                            nullptr, cs, sel_map));
     HSAB_TRY(hipEventRecord(e->ev_sel, cs));

@@ -61,7 +61,7 @@ __global__ __launch_bounds__(256) void block_score_kernel(
     const uint16_t* __restrict__ q, uint16_t* __restrict__ meta,
     const int32_t* __restrict__ ctx_len, float* __restrict__ score,
     int Hkv, int G, int dk, int bs, int max_ctx, int nb_cap, int tiles_per_wave, Append ap,
-    int32_t* __restrict__ sel_cnt, int agg) {
+    Handoff ho, int agg) {
     __shared__ f32x4_t red[KSPLIT > 1 ? SPLIT_TILES * KSPLIT * MT * 64 : 1];
 
     const int unit = blockIdx.y, b = unit / Hkv, g = unit % Hkv;
@@ -81,11 +81,17 @@ __global__ __launch_bounds__(256) void block_score_kernel(
     constexpr bool SEP = KSPLIT == 1;
     const bool app_wg = SEP && ap.k_new && blockIdx.x == gridDim.x - 1;
     const int tail_j0 = SEP && ap.k_new ? ((nb - 1) & ~15) : -1;
-    // arrival counters of the split token selection: one per unit, or one
-    // per query head with per-head selection
+    // shared state of the split token selection that follows in the step:
+    // arrival counters (one per unit, or one per query head with per-head
+    // selection) to zero, the unit's candidate keys to KEY_PENDING, spread
+    // over the unit's workgroups
     const int heads = agg == AGG_HEAD ? G : 1;
-    if (sel_cnt && blockIdx.x == 0 && threadIdx.x < heads)
-        __hip_atomic_store(&sel_cnt[unit * heads + threadIdx.x], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (ho.cnt) {
+        if (blockIdx.x == 0 && threadIdx.x < heads) ho.cnt[unit * heads + threadIdx.x] = 0;
+        const int nk = heads * ho.keys_per_sel;
+        uint32_t* ku = ho.keys + (size_t)unit * nk;
+        for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < nk; i += gridDim.x * blockDim.x) ku[i] = KEY_PENDING;
+    }
     if (!app_wg && j_wg >= nb) return;
 
     if (app_wg || (!SEP && ap.k_new && nb - 1 < j_wg + per_wg)) {
@@ -275,7 +281,7 @@ __global__ __launch_bounds__(256) void block_score_kernel(
 
 template <int MT, int KSW, int KSPLIT, bool F8>
 hipError_t launch_t(const Shape& s, const uint16_t* q, uint16_t* meta, const int32_t* ctx_len,
-                    float* score, const Append& ap, int32_t* sel_cnt, hipStream_t st) {
+                    float* score, const Append& ap, const Handoff& ho, hipStream_t st) {
     constexpr int TILES_WG = SCORE_WAVES / KSPLIT;
     const long tiles = (long)((s.nb_cap + 15) / 16) * s.B * s.Hkv;
     // aim for ~2048 workgroups (8 per CU) before giving a wave more tiles;
@@ -287,41 +293,42 @@ hipError_t launch_t(const Shape& s, const uint16_t* q, uint16_t* meta, const int
     const int per_wg = TILES_WG * tpw * 16;
     dim3 grid((s.nb_cap + per_wg - 1) / per_wg + (KSPLIT == 1 && ap.k_new ? 1 : 0), s.B * s.Hkv);
     hipLaunchKernelGGL((block_score_kernel<MT, KSW, KSPLIT, F8>), grid, dim3(64 * SCORE_WAVES), 0, st, q, meta,
-                       ctx_len, score, s.Hkv, s.G, s.dk, s.bs, s.max_ctx, s.nb_cap, tpw, ap, sel_cnt, s.agg);
+                       ctx_len, score, s.Hkv, s.G, s.dk, s.bs, s.max_ctx, s.nb_cap, tpw, ap, ho, s.agg);
     return hipGetLastError();
 }
 
 template <int MT>
 hipError_t launch_mt(const Shape& s, const uint16_t* q, uint16_t* meta, const int32_t* ctx_len, float* score,
-                     const Append& ap, int32_t* sel_cnt, hipStream_t st) {
+                     const Append& ap, const Handoff& ho, hipStream_t st) {
     if (s.meta8) {   // e4m3 rows: d_k / 32 loads of 64 channels, two matrix steps each
         const int kl = s.dk / 32;
-        if (kl <= 2) return launch_t<MT, 2, 1, true>(s, q, meta, ctx_len, score, ap, sel_cnt, st);
-        if (kl <= 4) return launch_t<MT, 4, 1, true>(s, q, meta, ctx_len, score, ap, sel_cnt, st);
-        if (kl <= 8) return launch_t<MT, 8, 1, true>(s, q, meta, ctx_len, score, ap, sel_cnt, st);
-        if (kl <= 16) return launch_t<MT, 4, 4, true>(s, q, meta, ctx_len, score, ap, sel_cnt, st);
-        if (kl <= 20) return launch_t<MT, 5, 4, true>(s, q, meta, ctx_len, score, ap, sel_cnt, st);
-        return launch_t<MT, 8, 4, true>(s, q, meta, ctx_len, score, ap, sel_cnt, st);   // d_k <= 1024
+        if (kl <= 2) return launch_t<MT, 2, 1, true>(s, q, meta, ctx_len, score, ap, ho, st);
+        if (kl <= 4) return launch_t<MT, 4, 1, true>(s, q, meta, ctx_len, score, ap, ho, st);
+        if (kl <= 8) return launch_t<MT, 8, 1, true>(s, q, meta, ctx_len, score, ap, ho, st);
+        if (kl <= 16) return launch_t<MT, 4, 4, true>(s, q, meta, ctx_len, score, ap, ho, st);
+        if (kl <= 20) return launch_t<MT, 5, 4, true>(s, q, meta, ctx_len, score, ap, ho, st);
+        return launch_t<MT, 8, 4, true>(s, q, meta, ctx_len, score, ap, ho, st);   // d_k <= 1024
     }
     const int ks = s.dk / 16;
-    if (ks <= 4) return launch_t<MT, 4, 1, false>(s, q, meta, ctx_len, score, ap, sel_cnt, st);
-    if (ks <= 8) return launch_t<MT, 8, 1, false>(s, q, meta, ctx_len, score, ap, sel_cnt, st);
-    if (ks <= 16) return launch_t<MT, 16, 1, false>(s, q, meta, ctx_len, score, ap, sel_cnt, st);
-    if (ks <= 32) return launch_t<MT, 8, 4, false>(s, q, meta, ctx_len, score, ap, sel_cnt, st);
-    if (ks <= 36) return launch_t<MT, 9, 4, false>(s, q, meta, ctx_len, score, ap, sel_cnt, st);    // 576-dim latent keys
-    if (ks <= 40) return launch_t<MT, 10, 4, false>(s, q, meta, ctx_len, score, ap, sel_cnt, st);
-    return launch_t<MT, 16, 4, false>(s, q, meta, ctx_len, score, ap, sel_cnt, st);   // d_k <= 1024: <= 64 steps
+    if (ks <= 4) return launch_t<MT, 4, 1, false>(s, q, meta, ctx_len, score, ap, ho, st);
+    if (ks <= 8) return launch_t<MT, 8, 1, false>(s, q, meta, ctx_len, score, ap, ho, st);
+    if (ks <= 16) return launch_t<MT, 16, 1, false>(s, q, meta, ctx_len, score, ap, ho, st);
+    if (ks <= 32) return launch_t<MT, 8, 4, false>(s, q, meta, ctx_len, score, ap, ho, st);
+    if (ks <= 36) return launch_t<MT, 9, 4, false>(s, q, meta, ctx_len, score, ap, ho, st);    // 576-dim latent keys
+    if (ks <= 40) return launch_t<MT, 10, 4, false>(s, q, meta, ctx_len, score, ap, ho, st);
+    return launch_t<MT, 16, 4, false>(s, q, meta, ctx_len, score, ap, ho, st);   // d_k <= 1024: <= 64 steps
 }
 
 }  // namespace
 
 hipError_t launch_block_score(const Shape& s, const uint16_t* q, uint16_t* meta, const int32_t* ctx_len,
                               float* score, const uint16_t* k_new, const uint16_t* v_new, uint16_t* K,
-                              uint16_t* V, uint16_t* klabel, const int32_t* label_ch, int32_t* sel_cnt,
+                              uint16_t* V, uint16_t* klabel, const int32_t* label_ch, const Handoff* ho,
                               hipStream_t st) {
     const Append ap{k_new, v_new, K, s.valias ? nullptr : V, klabel, label_ch, s.dv, s.r, s.lab8};
-    return s.G <= 16 ? launch_mt<1>(s, q, meta, ctx_len, score, ap, sel_cnt, st)
-                     : launch_mt<2>(s, q, meta, ctx_len, score, ap, sel_cnt, st);
+    const Handoff h = ho ? *ho : Handoff{nullptr, nullptr, 0};
+    return s.G <= 16 ? launch_mt<1>(s, q, meta, ctx_len, score, ap, h, st)
+                     : launch_mt<2>(s, q, meta, ctx_len, score, ap, h, st);
 }
 
 }  // namespace hsab

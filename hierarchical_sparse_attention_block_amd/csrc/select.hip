@@ -21,10 +21,15 @@
 // misses one CU keeps in flight, so with few units each unit gets `parts`
 // workgroups (on one XCD). Every part selects the blocks itself (part 0
 // writes them), scores its share of the candidate tiles and publishes the
-// keys with agent-scope stores; each part then bumps the unit's arrival
-// counter with an agent-scope acquire-release read-modify-write, and the
-// part that arrives last reads all keys back (agent-scope loads), runs
-// top-K_t and resets the counter.
+// keys with agent-scope atomic stores, then counts its arrival with an
+// agent-scope read-modify-write of the unit's counter; the part that
+// arrives last reads every key back with agent-scope atomic loads and runs
+// top-K_t. No ordering between different addresses is needed: the
+// block-score launch earlier in the step set every key to KEY_PENDING (that
+// launch completes before this one starts), each key is stored once per
+// step, so a load of it returns either KEY_PENDING or this step's key; the
+// last part loads a key again while it reads KEY_PENDING (every part has
+// stored its keys before arriving, so each such loop ends).
 #include <type_traits>
 #include "common.h"
 #include "kernels.h"
@@ -256,15 +261,10 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
         }
     }
     if (parts > 1) {
-        // The barrier orders every wave's key stores before thread 0's
-        // arrival; the arrival releases them at agent scope and, in the part
-        // that arrives last, acquires the other parts' (every arrival is a
-        // read-modify-write of the one counter, so the last one reads a value
-        // that every earlier release wrote into); the second barrier passes
-        // that acquire on to the waves that read the keys.
+        // the barrier puts the arrival after every wave's key stores
         __syncthreads();
         if (threadIdx.x == 0)
-            s_last = __hip_atomic_fetch_add(&cnt[sel], 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) == parts - 1;
+            s_last = __hip_atomic_fetch_add(&cnt[sel], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == parts - 1;
         __syncthreads();
         if (!s_last) return;
     } else {
@@ -285,14 +285,32 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
         else
             key[j] = in ? s_key[i] : 0u;
     }
+    if (parts > 1) {
+        // another part's key not yet visible here: load it again (the bound
+        // only guards against a key that is never stored, which the tiling
+        // rules out: the parts' tile ranges cover every candidate)
+        for (int spin = 0; spin < (1 << 22); ++spin) {
+            bool pending = false;
+#pragma unroll
+            for (int j = 0; j < PT; ++j) {
+                if (key[j] == KEY_PENDING) {
+                    const int i = (w * pt + j) * 64 + lane;
+                    key[j] = __hip_atomic_load(&gkeys[(size_t)sel * ncand + i], __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+                    pending |= key[j] == KEY_PENDING;
+                }
+            }
+            if (!pending) break;
+        }
+#pragma unroll
+        for (int j = 0; j < PT; ++j) key[j] = key[j] == KEY_PENDING ? 0u : key[j];
+    }
     int32_t* to = tok_idx + (size_t)sel * kt;
     const int keff_t = Sel::select(key, pt, kt, s_sel, [&](int p, int i) {
         const int slot = slot_of(i);
         to[p] = s_blk[slot] * bs + (i - slot * bs);
     });
     for (int p = keff_t + threadIdx.x; p < kt; p += SEL_THREADS) to[p] = -1;
-    if (parts > 1 && threadIdx.x == 0)   // ready for the next call
-        __hip_atomic_store(&cnt[sel], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int PT, int KK, bool L8>
