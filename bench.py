@@ -736,6 +736,14 @@ def layer_leg(w, args, full):
                              "peak_tflops_bf16_dense": MFMA_PEAK_TFLOPS,
                              "frac_of_mfma_peak": round(tf / MFMA_PEAK_TFLOPS, 4),
                              "flop_per_byte": round(flops / kb, 2)}
+        # matrix-core busy share from the committed rocprofv3 counters of this
+        # kernel (reported while the hash of its sources matches)
+        mpath = os.path.join(ROOT, "profiles", f"block_score_{w.name}_mfma_counters.json")
+        if not w.meta_fp8 and os.path.exists(mpath):
+            c = json.load(open(mpath))
+            if c.get("source_hash") == source_hash(SCORE_SOURCES):
+                res["score_gemm"]["mfma_busy_frac_counters"] = round(c["mfma_busy_frac"], 4)
+                res["score_gemm"]["mfma_flops_executed_per_launch"] = int(c["mfma_flops_executed"])
     if full:
         # full attention over every token on the same caches: the operator the
         # sparse step replaces (the pages report the sparse speedup over it)
@@ -827,11 +835,6 @@ def main():
             sub, _ = layer_leg(W.WORKLOADS[name], args, full=False)
             sub["queries_per_s"] = sub.pop("value")
             res[key] = sub
-        mpath = os.path.join(ROOT, "profiles", "block_score_mla64k_mfma_counters.json")
-        if os.path.exists(mpath):
-            c = json.load(open(mpath))
-            if c.get("source_hash") == source_hash(SCORE_SOURCES):
-                res["mla64k"]["score_gemm"]["mfma_busy_frac_counters"] = c.get("mfma_busy_frac")
         res["offload"] = offload_summary(args)
     if not args.no_cpu:
         log("[bench] timing the CPU oracle on a bounded sample")
