@@ -20,15 +20,12 @@ __device__ __forceinline__ float bf16_f32(uint32_t bits16) { return __uint_as_fl
 __device__ __forceinline__ float lo_f32(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_f32(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// Keep the bf16 lanes of w whose sign bit is clear (q+) or set (q-); the
-// other lanes become +0. Exact: the kept values are unchanged.
-__device__ __forceinline__ uint32_t bf16x2_pos(uint32_t w) {
-    uint32_t m = ((w & 0x80008000u) >> 15) * 0xffffu;   // 0xffff per negative lane
-    return w & ~m;
-}
-__device__ __forceinline__ uint32_t bf16x2_neg(uint32_t w) {
-    uint32_t m = ((w & 0x80008000u) >> 15) * 0xffffu;
-    return w & m;
+// Sign split of a packed bf16 pair: with flip = 0 the lanes whose sign bit
+// is set are kept (q-), with flip = ~0 the others (q+); the rest become +0,
+// and keep = 0 clears both. Exact: kept values are unchanged.
+__device__ __forceinline__ uint32_t bf16x2_split(uint32_t w, uint32_t flip, uint32_t keep) {
+    const uint32_t neg = ((w & 0x80008000u) >> 15) * 0xffffu;   // 0xffff per negative lane
+    return w & (neg ^ flip) & keep;
 }
 
 // Order-preserving map of fp32 onto uint32 (a > b  <=>  key(a) > key(b) for

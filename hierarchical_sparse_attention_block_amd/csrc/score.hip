@@ -174,7 +174,13 @@ __global__ __launch_bounds__(256) void block_score_kernel(
     if constexpr (KSPLIT > 1) {
 #pragma unroll
         for (int d = 1; d < NBUF; ++d) load_tile(d, tl[d]);
+        // every load stays ahead of the first wait, so the waits count the
+        // loads down in issue order (fragments, then tile 0, 1, ...); left
+        // to itself the scheduler moves loads behind earlier tiles' products
+        __builtin_amdgcn_sched_barrier(0);
     }
+    // sign split without branches: a branch here lets the compiler sink a
+    // fragment load into it, behind the rows, and wait for every load there
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
         const bool head = mt * 16 + (lane & 15) < G;
@@ -182,9 +188,10 @@ __global__ __launch_bounds__(256) void block_score_kernel(
         for (int u = 0; u < KSW * LS; ++u) {
             const uint4 r = af[mt][u];
             const bool lower = chunk(s_lo + u / LS, u % LS) >= CH;
-            af[mt][u] = !head || s_lo + u / LS >= s_hi ? make_uint4(0u, 0u, 0u, 0u)
-                        : lower ? make_uint4(bf16x2_neg(r.x), bf16x2_neg(r.y), bf16x2_neg(r.z), bf16x2_neg(r.w))
-                                : make_uint4(bf16x2_pos(r.x), bf16x2_pos(r.y), bf16x2_pos(r.z), bf16x2_pos(r.w));
+            const uint32_t keep = head && s_lo + u / LS < s_hi ? ~0u : 0u;
+            const uint32_t flip = (lower ? 0u : ~0u) & keep;   // q- keeps the negative halves, q+ the rest
+            af[mt][u] = make_uint4(bf16x2_split(r.x, flip, keep), bf16x2_split(r.y, flip, keep),
+                                   bf16x2_split(r.z, flip, keep), bf16x2_split(r.w, flip, keep));
         }
     }
 
