@@ -20,12 +20,16 @@ __device__ __forceinline__ float bf16_f32(uint32_t bits16) { return __uint_as_fl
 __device__ __forceinline__ float lo_f32(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_f32(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// Sign split of a packed bf16 pair: with flip = 0 the lanes whose sign bit
-// is set are kept (q-), with flip = ~0 the others (q+); the rest become +0,
-// and keep = 0 clears both. Exact: kept values are unchanged.
-__device__ __forceinline__ uint32_t bf16x2_split(uint32_t w, uint32_t flip, uint32_t keep) {
-    const uint32_t neg = ((w & 0x80008000u) >> 15) * 0xffffu;   // 0xffff per negative lane
-    return w & (neg ^ flip) & keep;
+// Sign split of a packed bf16 pair. As signed 16-bit integers the halves
+// whose sign bit is clear are exactly the non-negative ones, so a packed
+// integer max with 0 leaves q+ (the others become +0), and w ^ q+ leaves
+// q- (the halves with the sign bit set). neg = ~0 selects q-, 0 selects q+.
+// Exact: kept values are unchanged.
+typedef short s16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16x2_split(uint32_t w, uint32_t neg) {
+    const s16x2_t h = __builtin_bit_cast(s16x2_t, w);
+    const uint32_t pos = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(h, s16x2_t{0, 0}));
+    return pos ^ (w & neg);
 }
 
 // Order-preserving map of fp32 onto uint32 (a > b  <=>  key(a) > key(b) for

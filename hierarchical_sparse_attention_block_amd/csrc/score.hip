@@ -11,7 +11,8 @@
 // or, with per-head selection, every head's own bound).
 //
 // Mapping onto v_mfma_f32_16x16x32_bf16: A = [q+ | q-] (16 head rows per
-// tile, padded with zeros), B = metadata rows (16 blocks per tile), K = the
+// tile; rows past the group repeat head 0 and are never read back), B =
+// metadata rows (16 blocks per tile), K = the
 // 2*d_k stacked channels in steps of 32. Lane l supplies block (l % 16) and
 // the 8-channel chunk 4*s + l/16 of step s, i.e. one 16-byte load per step;
 // the 16 lanes of a chunk read 16 different 64-byte row segments, and four
@@ -167,32 +168,45 @@ __global__ __launch_bounds__(256) void block_score_kernel(
 #pragma unroll
         for (int u = 0; u < KSW; ++u) dst[u] = ldg16(row + (s_lo + u < s_hi ? s_lo + u : s_hi - 1) * 64);
     };
-    // split-row workgroups take SPLIT_TILES tiles, all requested at once
+    // split-row workgroups take SPLIT_TILES tiles, all requested at once:
+    // tile 0 first, then the sign split of the fragments (it runs while
+    // tile 0's rows are in flight), then the other tiles. The scheduling
+    // barriers pin that order and keep every load ahead of the first row
+    // wait, so the waits count the loads down in issue order; left to
+    // itself the scheduler moves loads behind earlier tiles' products. A
+    // wave cannot issue past a full memory queue, so whatever follows the
+    // last load waits for the queue to drain.
     constexpr int NBUF = KSPLIT > 1 ? SPLIT_TILES : 1;
     uint4 tl[NBUF][KSW];
     load_tile(0, tl[0]);
-    if constexpr (KSPLIT > 1) {
-#pragma unroll
-        for (int d = 1; d < NBUF; ++d) load_tile(d, tl[d]);
-        // every load stays ahead of the first wait, so the waits count the
-        // loads down in issue order (fragments, then tile 0, 1, ...); left
-        // to itself the scheduler moves loads behind earlier tiles' products
-        __builtin_amdgcn_sched_barrier(0);
-    }
-    // sign split without branches: a branch here lets the compiler sink a
-    // fragment load into it, behind the rows, and wait for every load there
+    if constexpr (KSPLIT > 1) __builtin_amdgcn_sched_barrier(0);
+    // sign split without branches (a branch here lets the compiler sink a
+    // fragment load into it, behind the rows). Rows of heads >= G are never
+    // read back, so they need no clearing; steps past this wave's range
+    // re-read its last step and are cleared below, as the matrix
+    // instructions run for every step.
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-        const bool head = mt * 16 + (lane & 15) < G;
 #pragma unroll
         for (int u = 0; u < KSW * LS; ++u) {
             const uint4 r = af[mt][u];
-            const bool lower = chunk(s_lo + u / LS, u % LS) >= CH;
-            const uint32_t keep = head && s_lo + u / LS < s_hi ? ~0u : 0u;
-            const uint32_t flip = (lower ? 0u : ~0u) & keep;   // q- keeps the negative halves, q+ the rest
-            af[mt][u] = make_uint4(bf16x2_split(r.x, flip, keep), bf16x2_split(r.y, flip, keep),
-                                   bf16x2_split(r.z, flip, keep), bf16x2_split(r.w, flip, keep));
+            const uint32_t neg = chunk(s_lo + u / LS, u % LS) >= CH ? ~0u : 0u;
+            af[mt][u] = make_uint4(bf16x2_split(r.x, neg), bf16x2_split(r.y, neg), bf16x2_split(r.z, neg),
+                                   bf16x2_split(r.w, neg));
         }
+    }
+    if (s_hi - s_lo < KSW) {   // uniform: this wave has fewer steps than loads
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int u = 0; u < KSW * LS; ++u)
+                if (s_lo + u / LS >= s_hi) af[mt][u] = make_uint4(0u, 0u, 0u, 0u);
+    }
+    if constexpr (KSPLIT > 1) {
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int d = 1; d < NBUF; ++d) load_tile(d, tl[d]);
+        __builtin_amdgcn_sched_barrier(0);
     }
 
     // partial bound tile of this wave's steps
@@ -235,16 +249,23 @@ __global__ __launch_bounds__(256) void block_score_kernel(
             }
             return;
         }
-        const bool agg_sum = agg == AGG_SUM;
-        float v = agg_sum ? 0.f : -INFINITY;
+        // group maximum and sum side by side, without branches; heads past
+        // G are left out by selects
+        float vs = 0.f, vm = -INFINITY;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (mt * 16 + (lane >> 4) * 4 + i < G) v = agg_sum ? v + tot[mt][i] : fmaxf(v, tot[mt][i]);
+            for (int i = 0; i < 4; ++i) {
+                const bool ok = mt * 16 + (lane >> 4) * 4 + i < G;
+                const float x = tot[mt][i];
+                vs = ok ? vs + x : vs;
+                vm = ok ? fmaxf(vm, x) : vm;
+            }
         if (G > 4) {   // heads 4.. sit in the other 16-lane rows
-            v = agg_sum ? sum_xor32(sum_xor16(v)) : max_xor32(max_xor16(v));
+            vs = sum_xor32(sum_xor16(vs));
+            vm = max_xor32(max_xor16(vm));
         }
+        const float v = agg == AGG_SUM ? vs : vm;
         const int j0 = tile_j0(t), jl = j0 + (lane & 15);
         if (lane < 16 && jl < nb && (app_wg || j0 != tail_j0)) Su[jl] = v;
     };
