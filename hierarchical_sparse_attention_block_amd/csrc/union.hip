@@ -14,9 +14,10 @@
 // e by binary search over the offsets and writes slot e, so the stores are
 // coalesced and the dense words (the kept tokens cluster in kept blocks)
 // are not left to a few lanes. Each window starts at the smallest listed
-// position past the previous window (the first at the smallest of all), so
-// windows holding no entry are never visited and the union comes out
-// ascending; positions at or past the unit's context length are dropped.
+// position past the previous window (the first at the smallest of all, or
+// at 0 when one window covers the context), so windows holding no entry
+// are never visited and the union comes out ascending; positions at or
+// past the unit's context length are dropped.
 // The LDS per window is fixed (60 KiB).
 #include <climits>
 #include "common.h"
@@ -50,29 +51,40 @@ __global__ __launch_bounds__(UNION_THREADS) void union_kernel(const int32_t* __r
     const int span = wph * 32;                        // positions per window
     const int per = (wph + UNION_THREADS - 1) / UNION_THREADS;   // words per thread
     int base = 0;                                     // entries written so far
-    if (tid == 0) s_next = INT_MAX;
-    __syncthreads();
-    for (int e = tid; e < E; e += UNION_THREADS) {
-        const int t = L[e];
-        if (t >= 0 && t < n) atomicMin(&s_next, t);
+    int w0 = 0;   // one window from 0 covers a context no longer than a window
+    if (n > span) {
+        if (tid == 0) s_next = INT_MAX;
+        __syncthreads();
+        // the smallest listed position: a minimum per thread, then per wave
+        // (same-address LDS atomics serialise, one per wave is cheap)
+        uint32_t lmin = INT_MAX;
+        for (int e = tid; e < E; e += UNION_THREADS) {
+            const int t = L[e];
+            if (t >= 0 && t < n) lmin = (uint32_t)t < lmin ? (uint32_t)t : lmin;
+        }
+        lmin = wave_minmax<false>(lmin);
+        if (lane == 0 && lmin != (uint32_t)INT_MAX) atomicMin(&s_next, (int)lmin);
+        __syncthreads();
+        w0 = s_next;   // INT_MAX: no entry at all
     }
-    __syncthreads();
-    int w0 = s_next;                                  // INT_MAX: no entry at all
     while (w0 < n) {
         __syncthreads();                              // every thread has read s_next
         if (tid == 0) s_next = INT_MAX;
         for (int i = tid; i < G * wph; i += UNION_THREADS) bits[i] = 0u;
         __syncthreads();
         const int w1 = n - w0 > span ? w0 + span : n;  // this window: positions [w0, w1)
+        uint32_t nmin = INT_MAX;   // smallest listed position past this window
         for (int e = tid; e < E; e += UNION_THREADS) {
             const int t = L[e];
             if (t >= w0 && t < w1) {
                 const int h = e / kt, o = t - w0;
                 atomicOr(&bits[h * wph + (o >> 5)], 1u << (o & 31));
             } else if (t >= w1 && t < n) {
-                atomicMin(&s_next, t);
+                nmin = (uint32_t)t < nmin ? (uint32_t)t : nmin;
             }
         }
+        nmin = wave_minmax<false>(nmin);
+        if (lane == 0 && nmin != (uint32_t)INT_MAX) atomicMin(&s_next, (int)nmin);
         __syncthreads();
         // this thread's words: [k0, k1) of the window
         const int k0 = tid * per, k1 = min(k0 + per, wph);
