@@ -21,10 +21,11 @@
 // misses one CU keeps in flight, so with few units each unit gets `parts`
 // workgroups (on one XCD). Every part selects the blocks itself (part 0
 // writes them), scores its share of the candidate tiles and publishes the
-// keys with agent-scope atomic stores, then counts its arrival with an
-// agent-scope read-modify-write of the unit's counter; the part that
-// arrives last reads every key back with agent-scope atomic loads and runs
-// top-K_t. No ordering between different addresses is needed: the
+// keys with agent-scope atomic stores, requests every key back with
+// agent-scope atomic loads and counts its arrival with an agent-scope
+// read-modify-write of the unit's counter (the loads overlap that round
+// trip); the part that arrives last keeps the keys and runs top-K_t, the
+// others drop them. No ordering between different addresses is needed: the
 // block-score launch earlier in the step set every key to KEY_PENDING (that
 // launch completes before this one starts), each key is stored once per
 // step, so a load of it returns either KEY_PENDING or this step's key; the
@@ -260,30 +261,34 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
             }
         }
     }
+    // ----------------------------------------------------------- top-K_t
+    const int pt = (ncand + SEL_THREADS - 1) / SEL_THREADS;
+    uint32_t key[PT];
     if (parts > 1) {
-        // the barrier puts the arrival after every wave's key stores
+        // the barrier puts the arrival after every wave's key stores. Every
+        // part requests the keys before it arrives, so the loads overlap the
+        // arrival's round trip (a part that does not arrive last drops
+        // them); a key whose part has not stored it yet reads KEY_PENDING
+        // and is loaded again below
         __syncthreads();
+#pragma unroll
+        for (int j = 0; j < PT; ++j) {
+            const int i = (w * pt + j) * 64 + lane;
+            key[j] = j < pt && i < ncand ? __hip_atomic_load(&gkeys[(size_t)sel * ncand + i], __ATOMIC_RELAXED,
+                                                             __HIP_MEMORY_SCOPE_AGENT)
+                                         : 0u;
+        }
         if (threadIdx.x == 0)
             s_last = __hip_atomic_fetch_add(&cnt[sel], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == parts - 1;
         __syncthreads();
         if (!s_last) return;
     } else {
         __syncthreads();
-    }
-
-    // ----------------------------------------------------------- top-K_t
-    const int pt = (ncand + SEL_THREADS - 1) / SEL_THREADS;
-    uint32_t key[PT];
 #pragma unroll
-    for (int j = 0; j < PT; ++j) {
-        const int i = (w * pt + j) * 64 + lane;
-        const bool in = j < pt && i < ncand;
-        if (parts > 1)
-            key[j] = in ? __hip_atomic_load(&gkeys[(size_t)sel * ncand + i], __ATOMIC_RELAXED,
-                                            __HIP_MEMORY_SCOPE_AGENT)
-                        : 0u;
-        else
-            key[j] = in ? s_key[i] : 0u;
+        for (int j = 0; j < PT; ++j) {
+            const int i = (w * pt + j) * 64 + lane;
+            key[j] = j < pt && i < ncand ? s_key[i] : 0u;
+        }
     }
     if (parts > 1) {
         // another part's key not yet visible here: load it again (the bound
