@@ -135,13 +135,16 @@ def graph_group(steps, cap=16):
     return max(g for g in range(1, min(cap, steps) + 1) if steps % g == 0)
 
 
-def time_replays(fns, stream, warmup, steps, graphs=True, group=1):
+def time_replays(fns, stream, warmup, steps, graphs=True, group=1, spread=False):
     """Average ms per call of fns[i % len(fns)] over `steps` calls (after an
     eager warmup call of every fn and about `warmup` untimed calls). With
     graphs, calls are captured as HIP graphs of `group` consecutive calls
     each (len(fns) graphs, graph k holding calls k*group .. k*group+group-1,
     so replaying them in turn continues the rotation over fns) and
-    steps / group graphs are replayed; group must divide steps."""
+    steps / group graphs are replayed; group must divide steps. spread
+    (graphs only): also return the median, p10 and p90 of ms per call from
+    a second pass that brackets every replay with its own events (after the
+    timed region, which holds no events between its replays)."""
     assert steps % group == 0
     with torch.cuda.stream(stream):
         for f in fns:
@@ -172,7 +175,69 @@ def time_replays(fns, stream, warmup, steps, graphs=True, group=1):
             call(i)
         ev1.record(stream)
     torch.cuda.synchronize()
-    return ev0.elapsed_time(ev1) / steps
+    avg = ev0.elapsed_time(ev1) / steps
+    if not (spread and graphs):
+        return avg
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
+    with torch.cuda.stream(stream):
+        for i in range(calls):
+            evs[i][0].record(stream)
+            call(i)
+            evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    per = np.array([a.elapsed_time(b) / group for a, b in evs])
+    return avg, {"median_ms": round(float(np.median(per)), 6), "p10_ms": round(float(np.percentile(per, 10)), 6),
+                 "p90_ms": round(float(np.percentile(per, 90)), 6), "samples": int(calls), "steps_per_sample": group}
+
+
+_COPY_GBS = []
+
+
+def copy_reference():
+    """measured_copy_gbs(), measured once per process."""
+    if not _COPY_GBS:
+        _COPY_GBS.append(measured_copy_gbs())
+        log(f"[bench] device copy: {_COPY_GBS[0]:.0f} GB/s (read + write)")
+    return _COPY_GBS[0]
+
+
+def measured_h2d_gbs(pinned, n_bytes=256 << 20, reps=4):
+    """Rate of one large host-to-device copy from pinned host memory (best
+    of reps after one untimed copy): the measured link reference beside the
+    PCIe peak."""
+    src = pinned.view(torch.uint8)[:n_bytes]
+    dst = torch.empty(n_bytes, dtype=torch.uint8, device="cuda")
+    best = float("inf")
+    for i in range(reps + 1):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src, non_blocking=True)
+        e1.record()
+        torch.cuda.synchronize()
+        if i:
+            best = min(best, e0.elapsed_time(e1))
+    del dst
+    return n_bytes / (best * 1e-3) / 1e9
+
+
+def measured_copy_gbs(n_bytes=1 << 30, reps=5):
+    """Device-to-device copy rate of this GPU (bytes read plus bytes
+    written per second, best of reps after one untimed copy): the measured
+    stream-copy reference beside the published HBM peak."""
+    a = torch.ones(n_bytes // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    best = float("inf")
+    for i in range(reps + 1):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        b.copy_(a)
+        e1.record()
+        torch.cuda.synchronize()
+        if i:
+            best = min(best, e0.elapsed_time(e1))
+    del a, b
+    torch.cuda.empty_cache()
+    return 2 * n_bytes / (best * 1e-3) / 1e9
 
 
 def time_score_launches(d, base, metas, reps, stream, steps):
@@ -450,6 +515,8 @@ def offload_bench(args, lite=False):
     torch.cuda.synchronize()
     log(f"[bench] offload run: prefill {prefill.tolist()}, pool {pool.numel() * 2 / 1e9:.2f} GB pinned, "
         f"staged in {time.time() - t0:.1f}s")
+    h2d_gbs = measured_h2d_gbs(pool)
+    log(f"[bench] pinned host-to-device copy of 256 MiB: {h2d_gbs:.1f} GB/s")
 
     meta, klabel = meta0.clone(), klabel0.clone()
     cache = torch.zeros(U * n_slots * be, dtype=torch.int16, device="cuda")
@@ -521,7 +588,8 @@ def offload_bench(args, lite=False):
             "copy_ms_mean": round(float(copy_ms.mean()), 4), "copy_wait_ms_mean": round(float(waits.mean()), 4),
             "overlap_hidden_frac": round(float(hidden), 4),
             "link": {"achieved": round(link_gbs, 2), "peak": PCIE_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(link_gbs / PCIE_PEAK_GBS, 4)},
+                     "frac": round(link_gbs / PCIE_PEAK_GBS, 4), "measured_h2d_gbs": round(h2d_gbs, 2),
+                     "frac_of_measured_h2d": round(link_gbs / h2d_gbs, 4)},
             "compute_ms_mean": round(float(np.mean([x["compute_ms"] for x in tim[1:]])), 4),
             "breakdown_from": "one extra run with per-step GPU timestamps (copy, wait, compute, link)",
             "host_wait_ms_mean": round(float(np.mean([x["host_wait_ms"] for x in st[1:]])), 4),
@@ -605,6 +673,13 @@ def offload_bench(args, lite=False):
         evs[1].record(cs)
     torch.cuda.synchronize()
     resident_ms = evs[0].elapsed_time(evs[1]) / (steps - 1)
+    # overlap of the copies with compute: (t_compute + t_copy - t_step) /
+    # min(t_compute, t_copy), with the resident step as t_compute (1: fully
+    # overlapped, 0: in series)
+    for o in (off_k, off_d, off_g):
+        if o:
+            tc, tx = resident_ms, o["copy_ms_mean"]
+            o["overlap_ratio"] = round((tc + tx - o["ms_per_step"]) / max(min(tc, tx), 1e-9), 4)
 
     queries = B * w.n_q_heads
     res = {
@@ -642,7 +717,9 @@ def offload_summary(args):
                                            / (src["ms_per_step"] * 1e-3), 1),
                     "delta_bytes_mean": src["delta_bytes_mean"], "delta_frac_of_full": src["delta_frac_of_full"],
                     "link_gbs": src["link"]["achieved"], "link_frac": src["link"]["frac"],
-                    "overlap_hidden_frac": src["overlap_hidden_frac"], "copy_ms_mean": src["copy_ms_mean"],
+                    "measured_h2d_gbs": src["link"]["measured_h2d_gbs"],
+                    "overlap_hidden_frac": src["overlap_hidden_frac"], "overlap_ratio": src["overlap_ratio"],
+                    "copy_ms_mean": src["copy_ms_mean"],
                     "host_call_ms_mean": src["host_call_ms_mean"]}
     log(f"[bench] offload: host plan {out['host_plan']['ms_per_step'] * 1e3:.1f} us/step, GPU plan "
         f"{out['gpu_plan']['ms_per_step'] * 1e3:.1f} us/step, resident {out['resident_ms_per_step'] * 1e3:.1f}")
@@ -696,12 +773,15 @@ def layer_leg(w, args, full):
     # launch per step is timed too and reported beside it
     group = graph_group(args.steps) if not args.no_graph else 1
     step_fns = [(lambda r=r: decode(d, base, r, stream)) for r in reps]
-    ms_step = time_replays(step_fns, stream, args.warmup, args.steps, not args.no_graph, group)
+    ms_step = time_replays(step_fns, stream, args.warmup, args.steps, not args.no_graph, group,
+                           spread=not args.no_graph)
+    ms_step, spread = ms_step if isinstance(ms_step, tuple) else (ms_step, None)
     ms_step_single = time_replays(step_fns, stream, args.warmup, args.steps, True, 1) if not args.no_graph else None
     log(f"[bench] {w.name}: {args.steps} steps: {ms_step * 1e3:.1f} us/step (events)")
 
     # dominant kernel alone: a graph of back-to-back block-score launches
     us_score = time_score_launches(d, base, [r.meta for r in reps], reps, stream, args.steps)
+    copy_gbs = copy_reference()
     kb = score_kernel_bytes(w)
     achieved = kb / (us_score * 1e-6) / 1e9
 
@@ -723,9 +803,11 @@ def layer_leg(w, args, full):
         "ms_per_step_one_graph_per_step": None if ms_step_single is None else round(ms_step_single, 6),
         "hbm_frac_step": round(sb["total"] / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "step_bytes": sb["total"],
+        "step_ms_spread": spread,
         "roofline": {"kernel": "block_score", "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "algorithmic_bytes": kb, "us_per_launch": round(us_score, 3)},
+                     "traffic": traffic, "algorithmic_bytes": kb, "us_per_launch": round(us_score, 3),
+                     "measured_copy_gbs": round(copy_gbs, 1), "frac_of_measured_copy": round(achieved / copy_gbs, 4)},
     }
     if w.group > 1:
         # the block score as a matrix product on the matrix cores: G heads x
