@@ -26,6 +26,11 @@ from hierarchical_sparse_attention_block_amd import workloads as W
 REL_GAP = 1e-4
 OUT_ATOL = 2e-3
 LSE_RTOL = 1e-4
+# lse = logsumexp(z) has condition number <= 1 in the logits (its gradient
+# is the softmax), so its error is at most the largest fp32 logit error; near
+# lse = 0 the max and the log-sum cancel and a relative bound alone cannot be
+# met in fp32, hence an absolute floor of the same size
+LSE_ATOL = 1e-4
 
 
 def dims_of(w: W.Workload):
@@ -213,7 +218,7 @@ def oracle_unit_vs_gpu(w, q_bits, K_bits, V_bits, ctx, label, b, g, gpu_blk, gpu
     out, lse = O.attend(q, K[tok], V[tok], w.sm_scale)
     err = np.max(np.abs(out - gpu_out))
     assert err <= OUT_ATOL, f"unit ({b},{g}): out max-abs {err:.3g} > {OUT_ATOL}"
-    np.testing.assert_allclose(gpu_lse, lse, rtol=LSE_RTOL, err_msg=f"unit ({b},{g}) lse")
+    np.testing.assert_allclose(gpu_lse, lse, rtol=LSE_RTOL, atol=LSE_ATOL, err_msg=f"unit ({b},{g}) lse")
     return {"tie_blocks": tie_b, "tie_tokens": tie_t, "max_abs": float(err)}
 
 

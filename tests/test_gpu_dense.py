@@ -45,7 +45,7 @@ def _run(w, ctx):
             o, l = O.attend(qq, Kf, Vf, w.sm_scale)
             err = np.max(np.abs(o - out[b, g * G:(g + 1) * G]))
             assert err <= T.OUT_ATOL, f"unit ({b},{g}) n={n}: max-abs {err:.3g}"
-            np.testing.assert_allclose(lse[b, g * G:(g + 1) * G], l, rtol=T.LSE_RTOL)
+            np.testing.assert_allclose(lse[b, g * G:(g + 1) * G], l, rtol=T.LSE_RTOL, atol=T.LSE_ATOL)
     return out, lse
 
 

@@ -318,7 +318,7 @@ def test_sparse_attend_skips_padding_and_handles_empty(latent):
         keep = sel[sel < n]
         o, l = O.attend(q, K[keep], V[keep], w.sm_scale)
         assert np.max(np.abs(out.cpu().numpy().reshape(w.n_q_heads, -1) - o)) <= T.OUT_ATOL
-        np.testing.assert_allclose(lse.cpu().numpy(), l, rtol=T.LSE_RTOL)
+        np.testing.assert_allclose(lse.cpu().numpy(), l, rtol=T.LSE_RTOL, atol=T.LSE_ATOL)
     # all slots empty: out 0, lse -inf
     dev.H.sparse_attend(dev.d, dev.q, dev.K, dev.V, torch.full((w.k_tokens,), -1, dtype=torch.int32,
                         device="cuda"), dev.ctx, out, lse, dev.ws)
