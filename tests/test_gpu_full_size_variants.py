@@ -96,3 +96,24 @@ def test_gqa48k_per_head_selection_full_size():
     for i, (b, g) in enumerate(SAMPLED[:4]):
         st += _oracle_units(w, h, r, [(b, g)], head=i % G)
     say("gqa48k per-head sampled", st)
+
+
+def test_gqa96k_fp8_metadata_full_size():
+    """The 96k layer with e4m3 metadata (the benchmark's fp8 leg at 96k):
+    6,144 blocks and 4,096 candidates per unit; one unit of every batch row
+    and every KV head against the oracle."""
+    w = dataclasses.replace(W.WORKLOADS["gqa96k"], meta_fp8=True)
+    h, r = _decode(w)
+    _structure(w, r["blk"].reshape(-1, w.k_blocks), r["tok"].reshape(-1, w.k_tokens))
+    assert np.all(np.isfinite(r["out"])) and np.all(np.isfinite(r["lse"]))
+    say("gqa96k fp8 sampled", _oracle_units(w, h, r, [(b, b % 8) for b in range(16)]))
+
+
+def test_mla64k_fp8_metadata_full_size():
+    """The latent layer with e4m3 metadata (split-row block score widening
+    e4m3 rows), all eight units against the oracle."""
+    w = dataclasses.replace(W.WORKLOADS["mla64k"], meta_fp8=True)
+    h, r = _decode(w)
+    _structure(w, r["blk"].reshape(-1, w.k_blocks), r["tok"].reshape(-1, w.k_tokens))
+    assert np.all(np.isfinite(r["out"])) and np.all(np.isfinite(r["lse"]))
+    say("mla64k fp8 all units", _oracle_units(w, h, r, [(b, 0) for b in range(w.batch)]))
