@@ -33,8 +33,17 @@ Shape make_shape(const hsab_dims& d) {
 
 int attn_list_len(const Shape& s) { return s.kt * s.heads; }
 
+int attn_tok_per_split(const Shape& s) {
+    if (s.valias) return MLA_TOK_PER_SPLIT;
+    // GQA: 64-token splits while they fit one round of resident workgroups;
+    // beyond that, 128-token splits (for d <= 128) halve the workgroups
+    // instead of running a second round
+    const long wgs = (long)s.B * s.Hkv * ((attn_list_len(s) + ATT_TOK_PER_SPLIT - 1) / ATT_TOK_PER_SPLIT);
+    return wgs > ATT_ROUND_WGS && s.dk <= 128 ? ATT_TOK_PER_SPLIT_LONG : ATT_TOK_PER_SPLIT;
+}
+
 int attn_splits(const Shape& s) {
-    const int tps = s.valias ? MLA_TOK_PER_SPLIT : ATT_TOK_PER_SPLIT;
+    const int tps = attn_tok_per_split(s);
     return (attn_list_len(s) + tps - 1) / tps;
 }
 

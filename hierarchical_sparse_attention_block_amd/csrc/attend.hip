@@ -28,7 +28,7 @@ namespace {
 
 // MASKED: the token list is the union of the heads' own token sets (per-head
 // selection) and tok_mask gives, per entry, the heads that attend it.
-template <int D, int G, bool MASKED>
+template <int D, int G, bool MASKED, int TPS>
 __global__ __launch_bounds__(256) void attend_gqa_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const int32_t* __restrict__ tok_idx, const uint32_t* __restrict__ tok_mask,
@@ -37,7 +37,7 @@ __global__ __launch_bounds__(256) void attend_gqa_kernel(
     int max_ctx, int nb_cap, int n_splits, int units, float scale2, int slot_rows) {
     constexpr int LPT = D / 8;                         // lanes per token (8 channels each)
     constexpr int TPI = 64 / LPT;                      // tokens per wave load = lane groups per wave
-    constexpr int TPW = ATT_TOK_PER_SPLIT / 4;         // tokens per wave
+    constexpr int TPW = TPS / 4;                       // tokens per wave
     constexpr int IT = TPW / TPI;                      // tokens per lane group
     constexpr int NP = 4 * TPI;                        // partial softmax states per workgroup
     static_assert(IT >= 1 && TPW % TPI == 0, "bad D");
@@ -75,7 +75,7 @@ __global__ __launch_bounds__(256) void attend_gqa_kernel(
     uint32_t mk[IT];   // heads that attend the entry
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
-        const int ti = split * ATT_TOK_PER_SPLIT + wave * TPW + it * TPI + ts;
+        const int ti = split * TPS + wave * TPW + it * TPI + ts;
         const int tc = ti < kt ? ti : kt - 1;
         const int t = tl[tc];
         tv[it] = ti < kt && t < n ? t : -1;
@@ -433,21 +433,35 @@ __global__ __launch_bounds__(256) void combine_kernel(
     if (threadIdx.x == 0) lse[bh] = L > 0.f ? (M + log2f(L)) * LN2 : -INFINITY;
 }
 
+template <int D, int G, int TPS>
+hipError_t launch_gqa_tps(const Shape& s, const uint16_t* q, const uint16_t* K, const uint16_t* V,
+                          const int32_t* tok_idx, const uint32_t* tok_mask, int list_len, int ns,
+                          const int32_t* ctx_len, const int32_t* slot_of, int n_slots, float* part_ml,
+                          float* part_acc, hipStream_t st) {
+    const int units = s.B * s.Hkv;
+    const dim3 grid(((units + 7) / 8) * 8 * ns);
+    if (tok_mask)
+        hipLaunchKernelGGL((attend_gqa_kernel<D, G, true, TPS>), grid, dim3(256), 0, st, q, K, V, tok_idx, tok_mask,
+                           ctx_len, slot_of, n_slots, part_ml, part_acc, s.Hkv, s.bs, list_len, s.max_ctx, s.nb_cap,
+                           ns, units, s.sm_scale * LOG2E, 2 * s.bs);
+    else
+        hipLaunchKernelGGL((attend_gqa_kernel<D, G, false, TPS>), grid, dim3(256), 0, st, q, K, V, tok_idx, tok_mask,
+                           ctx_len, slot_of, n_slots, part_ml, part_acc, s.Hkv, s.bs, list_len, s.max_ctx, s.nb_cap,
+                           ns, units, s.sm_scale * LOG2E, 2 * s.bs);
+    return hipGetLastError();
+}
+
 template <int D, int G>
 hipError_t launch_gqa(const Shape& s, const uint16_t* q, const uint16_t* K, const uint16_t* V,
                       const int32_t* tok_idx, const uint32_t* tok_mask, int list_len, int ns, const int32_t* ctx_len,
                       const int32_t* slot_of, int n_slots, float* part_ml, float* part_acc, hipStream_t st) {
-    const int units = s.B * s.Hkv;
-    const dim3 grid(((units + 7) / 8) * 8 * ns);
-    if (tok_mask)
-        hipLaunchKernelGGL((attend_gqa_kernel<D, G, true>), grid, dim3(256), 0, st, q, K, V, tok_idx, tok_mask,
-                           ctx_len, slot_of, n_slots, part_ml, part_acc, s.Hkv, s.bs, list_len, s.max_ctx, s.nb_cap,
-                           ns, units, s.sm_scale * LOG2E, 2 * s.bs);
-    else
-        hipLaunchKernelGGL((attend_gqa_kernel<D, G, false>), grid, dim3(256), 0, st, q, K, V, tok_idx, tok_mask,
-                           ctx_len, slot_of, n_slots, part_ml, part_acc, s.Hkv, s.bs, list_len, s.max_ctx, s.nb_cap,
-                           ns, units, s.sm_scale * LOG2E, 2 * s.bs);
-    return hipGetLastError();
+    if constexpr (D <= 128) {
+        if (attn_tok_per_split(s) == ATT_TOK_PER_SPLIT_LONG)
+            return launch_gqa_tps<D, G, ATT_TOK_PER_SPLIT_LONG>(s, q, K, V, tok_idx, tok_mask, list_len, ns, ctx_len,
+                                                                slot_of, n_slots, part_ml, part_acc, st);
+    }
+    return launch_gqa_tps<D, G, ATT_TOK_PER_SPLIT>(s, q, K, V, tok_idx, tok_mask, list_len, ns, ctx_len, slot_of,
+                                                   n_slots, part_ml, part_acc, st);
 }
 
 template <int D>
@@ -488,7 +502,7 @@ hipError_t launch_attend(const Shape& s, const uint16_t* q, const uint16_t* K, c
                          float* lse, hipStream_t st) {
     if (!attend_supported(s)) return hipErrorInvalidValue;
     if (slot_of && !s.valias) V = K + (size_t)s.bs * s.dk;   // value rows follow the key rows in a slot
-    const int tps = mla_shape(s) ? MLA_TOK_PER_SPLIT : ATT_TOK_PER_SPLIT;
+    const int tps = mla_shape(s) ? MLA_TOK_PER_SPLIT : attn_tok_per_split(s);
     const int ns = (list_len + tps - 1) / tps;
     hipError_t e = hipSuccess;
     if (mla_shape(s)) {

@@ -14,6 +14,8 @@ constexpr int MAX_KB = 2048;         // K_b
 constexpr int MAX_G = 32;            // query heads per KV head
 constexpr int MAX_R = 128;           // label channels
 constexpr int ATT_TOK_PER_SPLIT = 64;    // tokens per attention workgroup (GQA path)
+constexpr int ATT_TOK_PER_SPLIT_LONG = 128;   // GQA path when 64-token splits need more than one round
+constexpr int ATT_ROUND_WGS = 1024;      // GQA attention workgroups resident at once (four per CU)
 constexpr int MLA_TOK_PER_SPLIT = 64;    // tokens per attention workgroup (MLA path)
 
 // group score modes (dims.group_agg)
@@ -34,6 +36,8 @@ struct Shape {
 
 Shape make_shape(const hsab_dims& d);
 int attn_splits(const Shape& s);
+// list entries per attention workgroup (one split)
+int attn_tok_per_split(const Shape& s);
 // entries of a unit's attention token list: K_t, or G * K_t (the union of
 // the heads' token sets) with per-head selection
 int attn_list_len(const Shape& s);
