@@ -59,6 +59,35 @@ def test_workspace_layout():
         H.workspace_bytes(_dims(n_q_heads=2))
 
 
+def test_workspace_splits_follow_the_resident_round():
+    """64-token attention splits while units x splits fit one round of 1,024
+    resident workgroups; 128-token splits beyond it for d <= 128; 64 for
+    wider heads. The split count sizes the two partial arrays."""
+    al = lambda x: (x + 255) // 256 * 256
+
+    def partials(d, splits):
+        Hq = d.batch * d.n_q_heads
+        return al(Hq * splits * 2 * 4) + al(Hq * splits * d.d_v * 4)
+
+    def ws_without_partials(d):
+        U = d.batch * d.n_kv_heads
+        return al(U * d.nb_cap * 4) + al(U * d.k_blocks * d.block * 4) + al(U * 4)
+
+    # 128 units x 16 splits of 64 = 2,048 workgroups: 8 splits of 128
+    d = _dims(batch=16, n_q_heads=32, n_kv_heads=8, k_blocks=256, k_tokens=1024, max_ctx=98304)
+    assert H.workspace_bytes(d) == ws_without_partials(d) + partials(d, 8)
+    # 64 units x 8 splits = 512 workgroups: 64-token splits
+    d = _dims(batch=8, n_q_heads=32, n_kv_heads=8, k_blocks=128, k_tokens=512, max_ctx=49152)
+    assert H.workspace_bytes(d) == ws_without_partials(d) + partials(d, 8)
+    # exactly 1,024 workgroups still fit the round
+    d = _dims(batch=16, n_q_heads=32, n_kv_heads=8, k_blocks=128, k_tokens=512, max_ctx=49152)
+    assert H.workspace_bytes(d) == ws_without_partials(d) + partials(d, 8)
+    # d = 256 keeps 64-token splits
+    d = _dims(batch=16, n_q_heads=32, n_kv_heads=8, d_k=256, d_v=256, k_blocks=256, k_tokens=1024,
+              max_ctx=98304)
+    assert H.workspace_bytes(d) == ws_without_partials(d) + partials(d, 16)
+
+
 @pytest.mark.parametrize("bad", [
     dict(batch=0), dict(n_q_heads=7), dict(n_q_heads=128, n_kv_heads=2), dict(d_k=100), dict(d_k=2048),
     dict(d_v=12), dict(r=24), dict(r=256), dict(k_blocks=0), dict(k_blocks=4096), dict(k_blocks=1024, block=16),
