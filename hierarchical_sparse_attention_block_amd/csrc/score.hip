@@ -95,7 +95,7 @@ __global__ __launch_bounds__(256) void block_score_kernel(
     }
     if (!app_wg && j_wg >= nb) return;
 
-    if (app_wg || (!SEP && ap.k_new && nb - 1 < j_wg + per_wg)) {
+    if (app_wg) {
         const int pos = n - 1, jt = pos / bs;
         const bool first = (pos % bs) == 0;
         const uint16_t* kn = ap.k_new + (size_t)unit * dk;
@@ -115,6 +115,44 @@ __global__ __launch_bounds__(256) void block_score_kernel(
         for (int c = threadIdx.x; c < ap.r; c += blockDim.x)
             label_put(ap.klabel, lrow + c, kn[clamp_ch(ap.label_ch[g * ap.r + c], dk)], ap.lab8);
         __syncthreads();   // the tail block's new bounds are read below
+    }
+
+    // Split-row append: the workgroup owning the tail block requests the
+    // tail block's current bounds, the new key (and value) and the label
+    // channels before its A fragments and tile rows, widens the bounds in
+    // LDS once those arrive (its rows still in flight), publishes the
+    // widened row, the key, value and label rows, and multiplies its copy
+    // of the tail block's rows from LDS; no tile row waits for the append.
+    constexpr int RV = KSPLIT > 1 ? 256 : 1;    // 16-byte words of the longest metadata row (2 x 1024 bf16)
+    __shared__ uint4 s_tail[RV];
+    __shared__ uint16_t s_kn[KSPLIT > 1 ? 1024 : 1];
+    const bool app_split = KSPLIT > 1 && ap.k_new && nb - 1 < j_wg + per_wg;
+    const int jt = (n - 1) / bs;                 // the tail block
+    const int row_vec = 2 * dk * (F8 ? 1 : 2) / 16;
+    uint4 orow = make_uint4(0u, 0u, 0u, 0u);
+    uint16_t kv[4] = {0, 0, 0, 0}, vv[4] = {0, 0, 0, 0};
+    int lab = 0;
+    if constexpr (KSPLIT > 1) {
+        if (app_split) {   // every load unconditional (clamped), so the wait counts stay exact
+            const int tid = threadIdx.x;
+            const uint8_t* Mo = meta_block(meta, (size_t)unit * nb_cap + jt, dk, F8);
+            orow = ldg16(Mo + (size_t)(tid < row_vec ? tid : row_vec - 1) * 16);
+            const uint16_t* kn = ap.k_new + (size_t)unit * dk;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int c = tid + 256 * i;
+                kv[i] = kn[c < dk ? c : dk - 1];
+            }
+            const uint16_t* vn = ap.V ? ap.v_new + (size_t)unit * ap.dv : kn;
+            const int vlim = ap.V ? ap.dv : dk;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int c = tid + 256 * i;
+                vv[i] = vn[c < vlim ? c : vlim - 1];
+            }
+            lab = ap.label_ch[g * ap.r + (tid < ap.r ? tid : ap.r - 1)];
+        }
+        __builtin_amdgcn_sched_barrier(0);
     }
 
     // row loads of 64 bytes per 16 lanes over the 2*dk stacked channels:
@@ -208,21 +246,66 @@ __global__ __launch_bounds__(256) void block_score_kernel(
         for (int d = 1; d < NBUF; ++d) load_tile(d, tl[d]);
         __builtin_amdgcn_sched_barrier(0);
     }
+    int tail_tile = -1;   // split-row append: this workgroup's tile holding the tail block
+    if constexpr (KSPLIT > 1) {
+        if (app_split) {
+            const int tid = threadIdx.x, pos = n - 1;
+            const bool first = (pos % bs) == 0;
+            if (tid < row_vec) s_tail[tid] = orow;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (tid + 256 * i < dk) s_kn[tid + 256 * i] = kv[i];
+            __syncthreads();
+            uint16_t* Krow = ap.K + ((size_t)unit * max_ctx + pos) * dk;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int c = tid + 256 * i;
+                if (c < dk) {
+                    meta_widen(reinterpret_cast<uint8_t*>(s_tail), dk, c, kv[i], first, F8);
+                    Krow[c] = kv[i];
+                }
+            }
+            if (ap.V) {
+                uint16_t* Vrow = ap.V + ((size_t)unit * max_ctx + pos) * ap.dv;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (tid + 256 * i < ap.dv) Vrow[tid + 256 * i] = vv[i];
+                const uint16_t* vn = ap.v_new + (size_t)unit * ap.dv;
+                for (int c = tid + 1024; c < ap.dv; c += 256) Vrow[c] = vn[c];   // values past 1024
+            }
+            __syncthreads();
+            uint8_t* Mt = meta_block(meta, (size_t)unit * nb_cap + jt, dk, F8);
+            if (tid < row_vec) *reinterpret_cast<uint4*>(Mt + (size_t)tid * 16) = s_tail[tid];
+            if (tid < ap.r)
+                label_put(ap.klabel, ((size_t)unit * max_ctx + pos) * ap.r + tid, s_kn[clamp_ch(lab, dk)], ap.lab8);
+            tail_tile = (jt - j_wg) / 16;
+        }
+    }
 
     // partial bound tile of this wave's steps
-    auto mul_tile = [&](const uint4 (&rows)[KSW], f32x4_t (&tot)[MT]) {
+    // take: this lane holds the tail block of a split-row append, whose
+    // widened rows are read from LDS instead of the rows loaded before
+    auto mul_tile = [&](const uint4 (&rows)[KSW], f32x4_t (&tot)[MT], bool take = false) {
         // two accumulators per head tile shorten the dependent MFMA chain
         f32x4_t acc[MT][2];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) acc[mt][0] = acc[mt][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int u = 0; u < KSW; ++u) {
+            uint4 rw = rows[u];
+            if constexpr (KSPLIT > 1) {
+                const int st = s_lo + u < s_hi ? s_lo + u : s_hi - 1;
+                const uint4 pv = s_tail[st * 4 + (lane >> 4)];
+                // per component: a select of the whole vector goes through memory
+                rw.x = take ? pv.x : rw.x;
+                rw.y = take ? pv.y : rw.y;
+                rw.z = take ? pv.z : rw.z;
+                rw.w = take ? pv.w : rw.w;
+            }
 #pragma unroll
             for (int w = 0; w < LS; ++w) {
                 // e4m3 bytes 8w..8w+7 of the load widened to bf16 (exact)
-                const uint4 bv = F8 ? f8x8_bf16(w == 0 ? make_uint2(rows[u].x, rows[u].y)
-                                                       : make_uint2(rows[u].z, rows[u].w))
-                                    : rows[u];
+                const uint4 bv = F8 ? f8x8_bf16(w == 0 ? make_uint2(rw.x, rw.y) : make_uint2(rw.z, rw.w)) : rw;
                 const int k = u * LS + w;
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt)
@@ -276,7 +359,7 @@ __global__ __launch_bounds__(256) void block_score_kernel(
 #pragma unroll
         for (int d = 0; d < NBUF; ++d) {
             f32x4_t tot[MT];
-            mul_tile(tl[d], tot);
+            mul_tile(tl[d], tot, d == tail_tile && tile_j0(d) + (lane & 15) == jt);
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) red[((d * KSPLIT + wave) * MT + mt) * 64 + lane] = tot[mt];
         }
