@@ -395,11 +395,16 @@ hipError_t launch_t(const Shape& s, const uint16_t* q, uint16_t* meta, const int
                     float* score, const Append& ap, const Handoff& ho, hipStream_t st) {
     constexpr int TILES_WG = SCORE_WAVES / KSPLIT;
     const long tiles = (long)((s.nb_cap + 15) / 16) * s.B * s.Hkv;
-    // aim for ~2048 workgroups (8 per CU) before giving a wave more tiles;
-    // split-row workgroups take SPLIT_TILES tiles each, all in flight at once
+    // bf16 rows: one tile per wave, so short workgroups keep every CU fed
+    // to the end of the launch (against ~2048 workgroups with 2-6 tiles per
+    // wave: gqa48k step 52.8 -> 52.0 us, gqa96k 133.8 -> 125.2 us); e4m3
+    // rows carry half the bytes per tile and keep ~2048 workgroups (one tile
+    // per wave there: 44.7 -> 46.7 and 96.9 -> 101.3 us); split-row
+    // workgroups take SPLIT_TILES tiles each, all in flight at once
     const long target = 2048;
     int tpw = (int)((tiles / TILES_WG + target - 1) / target);
     tpw = tpw < 1 ? 1 : (tpw > 8 ? 8 : tpw);
+    if (!F8) tpw = 1;
     if (KSPLIT > 1) tpw = SPLIT_TILES;
     const int per_wg = TILES_WG * tpw * 16;
     dim3 grid((s.nb_cap + per_wg - 1) / per_wg + (KSPLIT == 1 && ap.k_new ? 1 : 0), s.B * s.Hkv);
