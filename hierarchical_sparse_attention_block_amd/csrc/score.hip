@@ -394,18 +394,14 @@ template <int MT, int KSW, int KSPLIT, bool F8>
 hipError_t launch_t(const Shape& s, const uint16_t* q, uint16_t* meta, const int32_t* ctx_len,
                     float* score, const Append& ap, const Handoff& ho, hipStream_t st) {
     constexpr int TILES_WG = SCORE_WAVES / KSPLIT;
-    const long tiles = (long)((s.nb_cap + 15) / 16) * s.B * s.Hkv;
-    // bf16 rows: one tile per wave, so short workgroups keep every CU fed
-    // to the end of the launch (against ~2048 workgroups with 2-6 tiles per
-    // wave: gqa48k step 52.8 -> 52.0 us, gqa96k 133.8 -> 125.2 us); e4m3
-    // rows carry half the bytes per tile and keep ~2048 workgroups (one tile
-    // per wave there: 44.7 -> 46.7 and 96.9 -> 101.3 us); split-row
-    // workgroups take SPLIT_TILES tiles each, all in flight at once
-    const long target = 2048;
-    int tpw = (int)((tiles / TILES_WG + target - 1) / target);
-    tpw = tpw < 1 ? 1 : (tpw > 8 ? 8 : tpw);
-    if (!F8) tpw = 1;
-    if (KSPLIT > 1) tpw = SPLIT_TILES;
+    // Tiles per wave, chosen by timing the step: bf16 rows take one, so the
+    // grid is many short workgroups that keep every CU fed to the end of the
+    // launch (against ~2048 workgroups of 2-6 tiles per wave: gqa48k step
+    // 52.8 -> 52.0 us, gqa96k 133.8 -> 125.2 us); e4m3 rows carry half the
+    // bytes per tile and take two (one: gqa48k 44.7 -> 46.7 us; ~2048
+    // workgroups: gqa96k 95.1 -> 97.5 us); split-row workgroups take
+    // SPLIT_TILES tiles each, all in flight at once
+    const int tpw = KSPLIT > 1 ? SPLIT_TILES : (F8 ? 2 : 1);
     const int per_wg = TILES_WG * tpw * 16;
     dim3 grid((s.nb_cap + per_wg - 1) / per_wg + (KSPLIT == 1 && ap.k_new ? 1 : 0), s.B * s.Hkv);
     hipLaunchKernelGGL((block_score_kernel<MT, KSW, KSPLIT, F8>), grid, dim3(64 * SCORE_WAVES), 0, st, q, meta,
