@@ -3,9 +3,10 @@
 // selected tokens only), split over workgroups and merged by log-sum-exp.
 //
 // GQA path (d_k == d_v == D, G query heads per KV head): one workgroup of
-// four waves takes 64 consecutive entries of the unit's token list; D/8
-// lanes share a token (8 channels = 16 bytes each), so one wave load
-// gathers 64/(D/8) whole key rows. Logits are fp32 (bf16 products are
+// four waves takes 64 consecutive entries of the unit's token list (128
+// for D <= 128 when 64-entry splits would need more workgroups than one
+// resident round holds); D/8 lanes share a token (8 channels = 16 bytes
+// each), so one wave load gathers 64/(D/8) whole key rows. Logits are fp32 (bf16 products are
 // exact in fp32), kept in base-2 units (q pre-scaled by sm_scale*log2 e).
 // Each wave keeps (max, sum, weighted values) per head; the workgroup
 // merges its four waves and writes one partial per head; the combine
