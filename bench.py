@@ -40,8 +40,12 @@ METRIC = "sparse-attn decode queries/s (batch×heads) at 48k/96k ctx; % HBM roof
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
 COUNTERS = os.path.join(ROOT, "profiles", "block_score_{wl}_counters.json")
+# what the block-score kernel is built from: its sources and the build
+# options (per-source compiler flags), so counters taken on another build
+# are not reported
 SCORE_SOURCES = ["hierarchical_sparse_attention_block_amd/csrc/score.hip",
-                 "hierarchical_sparse_attention_block_amd/csrc/common.h"]
+                 "hierarchical_sparse_attention_block_amd/csrc/common.h",
+                 "hierarchical_sparse_attention_block_amd/build.py"]
 
 
 def log(*a):

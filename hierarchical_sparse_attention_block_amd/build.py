@@ -27,11 +27,16 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I" + os.path.join(ROOT, "include"),
 ]
+# Per-source options. The block-score kernels keep their accumulators in
+# ordinary VGPRs: left to choose, the compiler puts them in AGPRs, and the
+# AGPR block, allocated apart from the VGPRs, costs the separate-column
+# kernels one wave per SIMD.
+SOURCE_FLAGS = {"score.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "'-packed-fp32-ops' is not a recognized feature for this target (ignoring feature)"
     err = "\n".join(l for l in r.stderr.splitlines() if noise not in l)
