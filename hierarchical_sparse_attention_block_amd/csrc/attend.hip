@@ -6,8 +6,14 @@
 // four waves takes 64 consecutive entries of the unit's token list (128
 // for D <= 128 when 64-entry splits would need more workgroups than one
 // resident round holds); D/8 lanes share a token (8 channels = 16 bytes
-// each), so one wave load gathers 64/(D/8) whole key rows. Logits are fp32 (bf16 products are
-// exact in fp32), kept in base-2 units (q pre-scaled by sm_scale*log2 e).
+// each), so one wave load gathers 64/(D/8) whole key rows. Logits are
+// v_dot2_f32_bf16 sums of the packed bf16 pairs (fp32 accumulation),
+// added over the token's lane group and then scaled by sm_scale*log2 e
+// (base-2 units). Rows are addressed from the unit's first row by 32-bit
+// byte offsets, one register per entry for its key and value loads. With
+// 128 entries per workgroup each lane keeps 8 key and 8 value rows in
+// flight; at G <= 4 the kernel is held to 128 registers so that four
+// workgroups share a CU and one resident round takes the whole grid.
 // Each wave keeps (max, sum, weighted values) per head; the workgroup
 // merges its four waves and writes one partial per head; the combine
 // kernel merges the partials of all splits.
@@ -30,7 +36,8 @@ namespace {
 // MASKED: the token list is the union of the heads' own token sets (per-head
 // selection) and tok_mask gives, per entry, the heads that attend it.
 template <int D, int G, bool MASKED, int TPS>
-__global__ __launch_bounds__(256) void attend_gqa_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TPS == 128 && G <= 4 ? 4 : 1)))
+void attend_gqa_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const int32_t* __restrict__ tok_idx, const uint32_t* __restrict__ tok_mask,
     const int32_t* __restrict__ ctx_len, const int32_t* __restrict__ slot_of, int n_slots,
@@ -55,33 +62,35 @@ __global__ __launch_bounds__(256) void attend_gqa_kernel(
     int n = ctx_len[b];
     n = n < 0 ? 0 : (n > max_ctx ? max_ctx : n);
 
-    float qf[G][8];
+    uint4 qp[G];   // this lane's 8 query channels of each head, bf16 pairs
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-        const uint4 v = ldg16(q + ((size_t)(b * Hkv + g) * G + h) * D + cc * 8);
-        widen8(v, qf[h]);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qf[h][e] *= scale2;
-    }
+    for (int h = 0; h < G; ++h) qp[h] = ldg16(q + ((size_t)(b * Hkv + g) * G + h) * D + cc * 8);
 
     // Three dependent rounds, each with all its loads in flight: token
     // positions, block slots (block cache only), then the K and V rows.
-    // Loads are unconditional (invalid entries read row 0 and are masked)
+    // Loads are unconditional (invalid entries read the unit's row 0 and are masked)
     // so no round waits on a previous one's stragglers.
     uint4 kr[IT], vr[IT];
     bool ok[IT];
-    long rows[IT];
     const int32_t* tl = tok_idx + (size_t)unit * kt;
     int tv[IT];
     uint32_t mk[IT];   // heads that attend the entry
+    // all heads, as a value the compiler cannot see through: with a
+    // constant here the unmasked kernel schedules differently and spills
+    // under the 128-register limit (the masked one does not)
+    uint32_t all_heads = ~0u;
+    asm volatile("" : "+s"(all_heads));
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
         const int ti = split * TPS + wave * TPW + it * TPI + ts;
         const int tc = ti < kt ? ti : kt - 1;
         const int t = tl[tc];
         tv[it] = ti < kt && t < n ? t : -1;
-        mk[it] = MASKED ? tok_mask[(size_t)unit * kt + tc] : ~0u;
+        mk[it] = MASKED ? tok_mask[(size_t)unit * kt + tc] : all_heads;
     }
+    // rows are addressed within the unit (a uniform base and a 32-bit
+    // byte offset per lane, one register shared by the key and value loads)
+    int rin[IT];   // row of the entry inside the unit's rows, -1: none
     if (slot_of) {
         int sl[IT];
 #pragma unroll
@@ -93,18 +102,21 @@ __global__ __launch_bounds__(256) void attend_gqa_kernel(
         for (int it = 0; it < IT; ++it) {
             const int t = tv[it], blk = t >= 0 ? t / bs : 0;
             const bool v = t >= 0 && blk < nb_cap && sl[it] >= 0 && sl[it] < n_slots;
-            rows[it] = v ? ((long)unit * n_slots + sl[it]) * slot_rows + (t - blk * bs) : -1;
+            rin[it] = v ? sl[it] * slot_rows + (t - blk * bs) : -1;
         }
     } else {
 #pragma unroll
-        for (int it = 0; it < IT; ++it) rows[it] = tv[it] >= 0 ? (long)unit * max_ctx + tv[it] : -1;
+        for (int it = 0; it < IT; ++it) rin[it] = tv[it];
     }
+    const size_t urows = slot_of ? (size_t)unit * n_slots * slot_rows : (size_t)unit * max_ctx;
+    const char* Ku = reinterpret_cast<const char*>(K + urows * D);
+    const char* Vu = reinterpret_cast<const char*>(V + urows * D);
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
-        ok[it] = rows[it] >= 0;
-        const long r = ok[it] ? rows[it] : 0;
-        kr[it] = ldg16(K + r * D + cc * 8);
-        vr[it] = ldg16(V + r * D + cc * 8);
+        ok[it] = rin[it] >= 0;
+        const uint32_t off = (uint32_t)(ok[it] ? rin[it] : 0) * (uint32_t)(D * 2) + (uint32_t)(cc * 16);
+        kr[it] = ldg16(Ku + off);
+        vr[it] = ldg16(Vu + off);
     }
     // keep the value loads here, in flight with the key loads; left alone
     // the scheduler sinks them to their use after the logits
@@ -114,46 +126,53 @@ __global__ __launch_bounds__(256) void attend_gqa_kernel(
     float z[IT][G];
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
-        float kf[8];
-        widen8(kr[it], kf);
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-            float p = 0.f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) p = fmaf(qf[h][e], kf[e], p);
-            p = group_sum<LPT>(p);
-            z[it][h] = ok[it] && ((mk[it] >> h) & 1u) ? p : -INFINITY;
+            const uint4 k = kr[it], qv = qp[h];
+            const float p = dot2_bf16(qv.w, k.w, dot2_bf16(qv.z, k.z, dot2_bf16(qv.y, k.y, dot2_bf16(qv.x, k.x, 0.f))));
+            const float zl = group_sum<LPT>(p) * scale2;
+            z[it][h] = ok[it] && ((mk[it] >> h) & 1u) ? zl : -INFINITY;
         }
     }
 
     // softmax state of this lane group's IT tokens; the groups of the
     // workgroup are merged once through LDS, no cross-group shuffles
     const int slot = wave * TPI + ts;
+    float m[G], l[G], acc[G][8];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-        float m = z[0][h];
+        m[h] = z[0][h];
 #pragma unroll
-        for (int it = 1; it < IT; ++it) m = fmaxf(m, z[it][h]);
-        float l = 0.f, acc[8];
+        for (int it = 1; it < IT; ++it) m[h] = fmaxf(m[h], z[it][h]);
+        l[h] = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-        if (m != -INFINITY) {
+        for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+    }
+    // tokens outermost, so each value row is widened once for all heads
+    // (heads outermost, the widened rows of every token stay live across
+    // the head loop and cost a wave per SIMD at G = 4, 128 entries)
 #pragma unroll
-            for (int it = 0; it < IT; ++it) {
-                float vf[8];
-                widen8(vr[it], vf);
-                const float p = ok[it] ? exp2f(z[it][h] - m) : 0.f;
-                l += p;
+    for (int it = 0; it < IT; ++it) {
+        float vf[8];
+        widen8(vr[it], vf);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) acc[e] = fmaf(p, vf[e], acc[e]);
-            }
+        for (int h = 0; h < G; ++h) {
+            // -inf logits (an absent token, or a head that does not attend
+            // it) weigh 0; a finite logit implies a finite head maximum
+            const float p = z[it][h] == -INFINITY ? 0.f : exp2f(z[it][h] - m[h]);
+            l[h] += p;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(p, vf[e], acc[h][e]);
         }
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
         float4* dst = reinterpret_cast<float4*>(&s_acc[slot][h][cc * 8]);
-        dst[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-        dst[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+        dst[0] = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
+        dst[1] = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
         if (cc == 0) {
-            s_m[slot][h] = m;
-            s_l[slot][h] = l;
+            s_m[slot][h] = m[h];
+            s_l[slot][h] = l[h];
         }
     }
     __syncthreads();
@@ -440,6 +459,10 @@ hipError_t launch_gqa_tps(const Shape& s, const uint16_t* q, const uint16_t* K, 
                           const int32_t* ctx_len, const int32_t* slot_of, int n_slots, float* part_ml,
                           float* part_acc, hipStream_t st) {
     const int units = s.B * s.Hkv;
+    // a unit's rows are addressed by 32-bit byte offsets (always within
+    // range under the shape limits: nb_cap <= 8192, d_k <= 256 here)
+    const size_t unit_rows = slot_of ? (size_t)n_slots * 2 * s.bs : (size_t)s.max_ctx;
+    if (unit_rows * D * 2 > 0xffffffffull) return hipErrorInvalidValue;
     const dim3 grid(((units + 7) / 8) * 8 * ns);
     if (tok_mask)
         hipLaunchKernelGGL((attend_gqa_kernel<D, G, true, TPS>), grid, dim3(256), 0, st, q, K, V, tok_idx, tok_mask,
