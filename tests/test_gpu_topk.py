@@ -111,3 +111,20 @@ def test_random_normal_many_sizes():
 
 def test_group_max_of_identical_heads():
     _check(rng.standard_normal(3072), 128, G=4)
+
+
+@pytest.mark.parametrize("m", [2, 5, 33, 64, 65, 200])
+def test_small_pivot_bin_cut_inside_a_tie(m):
+    """A tie group of m equal scores at scattered entries (so it spans many
+    waves of the selecting workgroup) in a sparse part of the range, with the
+    cut falling inside it: its histogram bin is the pivot bin, ranked by
+    every wave when it holds at most 64 entries and by each entry's own lane
+    otherwise."""
+    n = 3072
+    s = rng.standard_normal(n)
+    s = np.where(np.abs(s - 3.0) < 0.05, s + 0.2, s)      # keep the tie's neighbourhood empty
+    pos = rng.choice(n, m, replace=False)
+    s[pos] = 3.0
+    above = int(np.sum(O.bf16_to_f64(W.f32_to_bf16_bits(s.astype(np.float32))) > 3.0))
+    for cut in sorted({1, m // 2, m - 1}):
+        _check(s, above + cut)
