@@ -24,8 +24,11 @@
 // queries staged in LDS, with an online softmax across the rounds.
 //
 // Workgroup numbering: the dispatcher hands consecutive workgroups to the
-// eight XCDs in turn, so workgroup L runs on XCD L % 8. All splits of a unit
-// are given the same L % 8, which keeps a unit's rows and partials in one L2.
+// eight XCDs in turn, so workgroup L runs on XCD L % 8 (measured on MI355X:
+// every workgroup of 1-D and 2-D grids of 1,024 to 6,272 workgroups read
+// L % 8 from its XCC_ID hardware register). All splits of a unit are given
+// the same L % 8, which keeps a unit's rows and partials in one L2. The key
+// and value rows are loaded non-temporally: a step reads each one once.
 #include "common.h"
 #include "kernels.h"
 
@@ -115,8 +118,8 @@ void attend_gqa_kernel(
     for (int it = 0; it < IT; ++it) {
         ok[it] = rin[it] >= 0;
         const uint32_t off = (uint32_t)(ok[it] ? rin[it] : 0) * (uint32_t)(D * 2) + (uint32_t)(cc * 16);
-        kr[it] = ldg16(Ku + off);
-        vr[it] = ldg16(Vu + off);
+        kr[it] = ldg16_nt(Ku + off);
+        vr[it] = ldg16_nt(Vu + off);
     }
     // keep the value loads here, in flight with the key loads; left alone
     // the scheduler sinks them to their use after the logits

@@ -50,6 +50,21 @@ __device__ __forceinline__ int clamp_ch(int c, int dk) { return c < 0 ? 0 : (c >
 __device__ __forceinline__ uint4 ldg16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ uint2 ldg8(const void* p) { return *reinterpret_cast<const uint2*>(p); }
 __device__ __forceinline__ uint32_t ldg4(const void* p) { return *reinterpret_cast<const uint32_t*>(p); }
+// Non-temporal forms, for rows a step reads once (the nontemporal hint on
+// the load: the line is not kept in the caches for reuse).
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint4 ldg16_nt(const void* p) {
+    const u32x4v v = __builtin_nontemporal_load(reinterpret_cast<const u32x4v*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 ldg8_nt(const void* p) {
+    const u32x2v v = __builtin_nontemporal_load(reinterpret_cast<const u32x2v*>(p));
+    return make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ uint32_t ldg4_nt(const void* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+}
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
