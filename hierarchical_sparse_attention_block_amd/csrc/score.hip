@@ -201,10 +201,15 @@ __global__ __launch_bounds__(256) void block_score_kernel(
             }
         }
     }
+    // split-row (latent) rows are loaded non-temporally: the stream then
+    // leaves the caches to the selection and attention that follow it
     auto load_tile = [&](int t, uint4 (&dst)[KSW]) {
         const uint8_t* row = tile_row(t < tiles_per_wave ? t : tiles_per_wave - 1);
 #pragma unroll
-        for (int u = 0; u < KSW; ++u) dst[u] = ldg16(row + (s_lo + u < s_hi ? s_lo + u : s_hi - 1) * 64);
+        for (int u = 0; u < KSW; ++u) {
+            const uint8_t* p = row + (s_lo + u < s_hi ? s_lo + u : s_hi - 1) * 64;
+            dst[u] = KSPLIT > 1 ? ldg16_nt(p) : ldg16(p);
+        }
     };
     // split-row workgroups take SPLIT_TILES tiles, all requested at once:
     // tile 0 first, then the sign split of the fragments (it runs while
