@@ -21,7 +21,8 @@
 // MLA path (values are the first d_v dims of the d_k-dim latent key rows,
 // 32 query heads on one KV head): a workgroup takes rounds of 32 kept
 // tokens; logits and P.V run on v_mfma_f32_16x16x32_bf16 from key rows and
-// queries staged in LDS, with an online softmax across the rounds.
+// queries staged in LDS, with an online softmax across the rounds; the
+// rows are loaded non-temporally, as in the GQA path.
 //
 // Workgroup numbering: the dispatcher hands consecutive workgroups to the
 // eight XCDs in turn, so workgroup L runs on XCD L % 8 (measured on MI355X:
@@ -309,7 +310,7 @@ __global__ __launch_bounds__(256, 1) void attend_mla_kernel(
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const long row = s_row[rd * T + rsel[i]];
-            v[i] = row >= 0 ? ldg16(K + row * dk + coff[i]) : make_uint4(0u, 0u, 0u, 0u);
+            v[i] = row >= 0 ? ldg16_nt(K + row * dk + coff[i]) : make_uint4(0u, 0u, 0u, 0u);
         }
     };
     uint4 v[PER];

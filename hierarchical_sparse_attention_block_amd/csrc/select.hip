@@ -14,7 +14,8 @@
 // l % 16, channels 4*(l/16)..+3, an 8-byte load); with 32 or more it is
 // v_mfma_f32_16x16x32_bf16 (channels 32*s + 8*(l/16)..+7, a 16-byte load),
 // which halves the load round trips of long label rows. Each wave issues
-// eight label-row loads before its MFMAs. Selection keeps all scores in
+// eight label-row loads (non-temporal: a step reads each row once) before
+// its MFMAs. Selection keeps all scores in
 // registers and LDS (TopK in topk.h).
 //
 // Split token stage: the label-row gather of one unit is bound by how many
@@ -201,14 +202,14 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
             if constexpr (L8) {
                 const uint8_t* src = reinterpret_cast<const uint8_t*>(klabel) + e;
                 if constexpr (KK == 32)
-                    bf[u] = ldg8(src);
+                    bf[u] = ldg8_nt(src);
                 else
-                    bf[u] = ldg4(src);
+                    bf[u] = ldg4_nt(src);
             } else {
                 if constexpr (KK == 32)
-                    bf[u] = ldg16(klabel + e);
+                    bf[u] = ldg16_nt(klabel + e);
                 else
-                    bf[u] = ldg8(klabel + e);
+                    bf[u] = ldg8_nt(klabel + e);
             }
         }
         f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
