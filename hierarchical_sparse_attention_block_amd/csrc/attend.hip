@@ -88,7 +88,7 @@ void attend_gqa_kernel(
     for (int it = 0; it < IT; ++it) {
         const int ti = split * TPS + wave * TPW + it * TPI + ts;
         const int tc = ti < kt ? ti : kt - 1;
-        const int t = tl[tc];
+        const int t = (int)ldg4_nt(tl + tc);
         tv[it] = ti < kt && t < n ? t : -1;
         mk[it] = MASKED ? tok_mask[(size_t)unit * kt + tc] : all_heads;
     }
@@ -259,7 +259,7 @@ __global__ __launch_bounds__(256, 1) void attend_mla_kernel(
     // the token list is requested before the query fragments (loads
     // complete in order, so the rows wait for no fragment)
     const int ti = split * TS + tid;
-    const int t_raw = tok_idx[(size_t)unit * kt + (ti < kt ? ti : kt - 1)];   // unconditional load
+    const int t_raw = (int)ldg4_nt(tok_idx + (size_t)unit * kt + (ti < kt ? ti : kt - 1));   // unconditional load
     int n = ctx_len[unit / Hkv];   // entries at or past the context length are skipped
     n = n < 0 ? 0 : (n > max_ctx ? max_ctx : n);
     const int t = tid < TS && ti < kt && t_raw < n ? t_raw : -1;
@@ -427,9 +427,9 @@ __global__ __launch_bounds__(256) void combine_kernel(
 #pragma unroll
         for (int j = 0; j < CH; ++j) {
             const int sj = s0 + j < n_splits ? s0 + j : n_splits - 1;
-            mlv[j] = *reinterpret_cast<const float2*>(ml + 2 * sj);
-            a0[j] = c0 < dv ? pa[(size_t)sj * dv + c0] : 0.f;
-            a1[j] = c1 < dv ? pa[(size_t)sj * dv + c1] : 0.f;
+            { const uint2 t2 = ldg8_nt(ml + 2 * sj); mlv[j] = make_float2(__uint_as_float(t2.x), __uint_as_float(t2.y)); }
+            a0[j] = c0 < dv ? __uint_as_float(ldg4_nt(pa + (size_t)sj * dv + c0)) : 0.f;
+            a1[j] = c1 < dv ? __uint_as_float(ldg4_nt(pa + (size_t)sj * dv + c1)) : 0.f;
         }
         float Mc = M;
 #pragma unroll

@@ -88,7 +88,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
 #pragma unroll
         for (int j = 0; j < PT; ++j) {
             const int i = (w * pt_b + j) * 64 + lane;
-            sraw[j] = (j < pt_b && i < nb_cap) ? S[i] : 0.f;
+            sraw[j] = (j < pt_b && i < nb_cap) ? __uint_as_float(ldg4_nt(S + i)) : 0.f;
         }
     }
     int n = ctx_len[b];
