@@ -370,7 +370,9 @@ hipError_t launch_select(const Shape& s, int mode, const uint16_t* q, const floa
     }
     if (need <= 1) return launch_t<1>(s, mode, q, blk_score, klabel, label_ch, ctx_len, blk_idx, tok_idx, tok_score, sel_keys, sel_cnt, blk_copy, st);
     if (need <= 2) return launch_t<2>(s, mode, q, blk_score, klabel, label_ch, ctx_len, blk_idx, tok_idx, tok_score, sel_keys, sel_cnt, blk_copy, st);
+    if (need <= 3) return launch_t<3>(s, mode, q, blk_score, klabel, label_ch, ctx_len, blk_idx, tok_idx, tok_score, sel_keys, sel_cnt, blk_copy, st);
     if (need <= 4) return launch_t<4>(s, mode, q, blk_score, klabel, label_ch, ctx_len, blk_idx, tok_idx, tok_score, sel_keys, sel_cnt, blk_copy, st);
+    if (need <= 6) return launch_t<6>(s, mode, q, blk_score, klabel, label_ch, ctx_len, blk_idx, tok_idx, tok_score, sel_keys, sel_cnt, blk_copy, st);
     return launch_t<8>(s, mode, q, blk_score, klabel, label_ch, ctx_len, blk_idx, tok_idx, tok_score, sel_keys, sel_cnt, blk_copy, st);
 }
 
