@@ -47,7 +47,7 @@ constexpr int SEL_THREADS = SEL_WAVES * 64;
 // KK: channels per matrix step (16, or 32 when r >= 32); L8: label rows in
 // e4m3 bytes (half the bytes per load), widened exactly to bf16 at the
 // matrix step so the loads stay back to back
-template <int PT, int KK, bool L8>
+template <int PTB, int PTT, int KK, bool L8>
 __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
     int mode, const uint16_t* __restrict__ q, const float* __restrict__ blk_score,
     const uint16_t* __restrict__ klabel, const int32_t* __restrict__ label_ch,
@@ -56,7 +56,9 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
     int32_t* __restrict__ blk_copy, int parts,
     int units, int heads, int Hkv, int G, int dk, int bs, int r, int kb, int kt, int max_ctx, int nb_cap,
     int bs_shift, int agg_sum, int sink, int local) {
-    using Sel = TopK<SEL_WAVES, PT>;
+    // PTB / PTT: key slots per thread of the block / token top-k
+    using SelB = TopK<SEL_WAVES, PTB>;
+    using SelT = TopK<SEL_WAVES, PTT>;
     // candidate i sits in slot i / bs of the block list (a shift when bs is a power of two)
     auto slot_of = [&](int i) { return bs_shift >= 0 ? (i >> bs_shift) : i / bs; };
     __shared__ uint32_t s_key[MAX_CAND];
@@ -65,7 +67,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
     // uint4 for KK = 32 (same bytes)
     __shared__ uint4 s_qa4[2 * (MAX_R / 32) * 64];
     uint2* s_qa = reinterpret_cast<uint2*>(s_qa4);
-    __shared__ typename Sel::Smem s_sel;
+    __shared__ TopKSmem<SEL_WAVES> s_sel;
     __shared__ int s_last;
 
     // selection sel (of `units`) belongs to KV unit sel / heads and, with
@@ -82,11 +84,11 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
     // as ctx_len and masked once n is known; the entry layout of the block
     // selection uses the capacity's slot count
     const int pt_b = (nb_cap + SEL_THREADS - 1) / SEL_THREADS;
-    float sraw[PT];
+    float sraw[PTB];
     if (mode & 1) {
         const float* S = blk_score + (size_t)sel * nb_cap;
 #pragma unroll
-        for (int j = 0; j < PT; ++j) {
+        for (int j = 0; j < PTB; ++j) {
             const int i = (w * pt_b + j) * 64 + lane;
             sraw[j] = (j < pt_b && i < nb_cap) ? __uint_as_float(ldg4_nt(S + i)) : 0.f;
         }
@@ -131,15 +133,15 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
         const int s1 = sink < nb ? sink : nb;
         const int l0 = nb - local > s1 ? nb - local : s1;
         const int nforced = s1 + (nb - l0);
-        uint32_t bkey[PT];
+        uint32_t bkey[PTB];
 #pragma unroll
-        for (int j = 0; j < PT; ++j) {
+        for (int j = 0; j < PTB; ++j) {
             const int i = (w * pt_b + j) * 64 + lane;
             bkey[j] = (j < pt_b && i < nb && i >= s1 && i < l0) ? f32_key(sraw[j]) : 0u;
         }
         int32_t* bo = blk_idx + (size_t)sel * kb;
         int32_t* bc = blk_copy ? blk_copy + (size_t)sel * kb : nullptr;   // second copy of the list (nullable)
-        const int keff = Sel::select(bkey, pt_b, kb - nforced, s_sel, [&](int pos, int i) {
+        const int keff = SelB::select(bkey, pt_b, kb - nforced, s_sel, [&](int pos, int i) {
             s_blk[s1 + pos] = i;
             if (part == 0) {
                 bo[s1 + pos] = i;
@@ -264,7 +266,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
     }
     // ----------------------------------------------------------- top-K_t
     const int pt = (ncand + SEL_THREADS - 1) / SEL_THREADS;
-    uint32_t key[PT];
+    uint32_t key[PTT];
     if (parts > 1) {
         // the barrier puts the arrival after every wave's key stores. Every
         // part requests the keys before it arrives, so the loads overlap the
@@ -273,7 +275,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
         // and is loaded again below
         __syncthreads();
 #pragma unroll
-        for (int j = 0; j < PT; ++j) {
+        for (int j = 0; j < PTT; ++j) {
             const int i = (w * pt + j) * 64 + lane;
             key[j] = j < pt && i < ncand ? __hip_atomic_load(&gkeys[(size_t)sel * ncand + i], __ATOMIC_RELAXED,
                                                              __HIP_MEMORY_SCOPE_AGENT)
@@ -286,7 +288,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
     } else {
         __syncthreads();
 #pragma unroll
-        for (int j = 0; j < PT; ++j) {
+        for (int j = 0; j < PTT; ++j) {
             const int i = (w * pt + j) * 64 + lane;
             key[j] = j < pt && i < ncand ? s_key[i] : 0u;
         }
@@ -298,7 +300,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
         for (int spin = 0; spin < (1 << 22); ++spin) {
             bool pending = false;
 #pragma unroll
-            for (int j = 0; j < PT; ++j) {
+            for (int j = 0; j < PTT; ++j) {
                 if (key[j] == KEY_PENDING) {
                     const int i = (w * pt + j) * 64 + lane;
                     key[j] = __hip_atomic_load(&gkeys[(size_t)sel * ncand + i], __ATOMIC_RELAXED,
@@ -309,28 +311,28 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
             if (!pending) break;
         }
 #pragma unroll
-        for (int j = 0; j < PT; ++j) key[j] = key[j] == KEY_PENDING ? 0u : key[j];
+        for (int j = 0; j < PTT; ++j) key[j] = key[j] == KEY_PENDING ? 0u : key[j];
     }
     int32_t* to = tok_idx + (size_t)sel * kt;
-    const int keff_t = Sel::select(key, pt, kt, s_sel, [&](int p, int i) {
+    const int keff_t = SelT::select(key, pt, kt, s_sel, [&](int p, int i) {
         const int slot = slot_of(i);
         to[p] = s_blk[slot] * bs + (i - slot * bs);
     });
     for (int p = keff_t + threadIdx.x; p < kt; p += SEL_THREADS) to[p] = -1;
 }
 
-template <int PT, int KK, bool L8>
+template <int PTB, int PTT, int KK, bool L8>
 hipError_t launch_k(const Shape& s, dim3 grid, int mode, const uint16_t* q, const float* blk_score,
                     const uint16_t* klabel, const int32_t* label_ch, const int32_t* ctx_len, int32_t* blk_idx,
                     int32_t* tok_idx, float* tok_score, uint32_t* gkeys, int32_t* cnt, int32_t* blk_copy, int parts,
                     int units, int shift, hipStream_t st) {
-    hipLaunchKernelGGL((select_kernel<PT, KK, L8>), grid, dim3(SEL_THREADS), 0, st, mode, q, blk_score, klabel,
+    hipLaunchKernelGGL((select_kernel<PTB, PTT, KK, L8>), grid, dim3(SEL_THREADS), 0, st, mode, q, blk_score, klabel,
                        label_ch, ctx_len, blk_idx, tok_idx, tok_score, gkeys, cnt, blk_copy, parts, units, s.heads, s.Hkv, s.G,
                        s.dk, s.bs, s.r, s.kb, s.kt, s.max_ctx, s.nb_cap, shift, s.agg_sum, s.sink, s.local);
     return hipGetLastError();
 }
 
-template <int PT>
+template <int PTB, int PTT>
 hipError_t launch_t(const Shape& s, int mode, const uint16_t* q, const float* blk_score,
                     const uint16_t* klabel, const int32_t* label_ch, const int32_t* ctx_len,
                     int32_t* blk_idx, int32_t* tok_idx, float* tok_score, uint32_t* gkeys, int32_t* cnt,
@@ -346,13 +348,13 @@ hipError_t launch_t(const Shape& s, int mode, const uint16_t* q, const float* bl
     }
     const dim3 grid(((units + 7) / 8) * 8 * parts);
     if (s.r >= 32)
-        return s.lab8 ? launch_k<PT, 32, true>(s, grid, mode, q, blk_score, klabel, label_ch, ctx_len, blk_idx, tok_idx,
+        return s.lab8 ? launch_k<PTB, PTT, 32, true>(s, grid, mode, q, blk_score, klabel, label_ch, ctx_len, blk_idx, tok_idx,
                                                tok_score, gkeys, cnt, blk_copy, parts, units, shift, st)
-                      : launch_k<PT, 32, false>(s, grid, mode, q, blk_score, klabel, label_ch, ctx_len, blk_idx,
+                      : launch_k<PTB, PTT, 32, false>(s, grid, mode, q, blk_score, klabel, label_ch, ctx_len, blk_idx,
                                                 tok_idx, tok_score, gkeys, cnt, blk_copy, parts, units, shift, st);
-    return s.lab8 ? launch_k<PT, 16, true>(s, grid, mode, q, blk_score, klabel, label_ch, ctx_len, blk_idx, tok_idx,
+    return s.lab8 ? launch_k<PTB, PTT, 16, true>(s, grid, mode, q, blk_score, klabel, label_ch, ctx_len, blk_idx, tok_idx,
                                            tok_score, gkeys, cnt, blk_copy, parts, units, shift, st)
-                  : launch_k<PT, 16, false>(s, grid, mode, q, blk_score, klabel, label_ch, ctx_len, blk_idx, tok_idx,
+                  : launch_k<PTB, PTT, 16, false>(s, grid, mode, q, blk_score, klabel, label_ch, ctx_len, blk_idx, tok_idx,
                                             tok_score, gkeys, cnt, blk_copy, parts, units, shift, st);
 }
 
@@ -362,18 +364,28 @@ hipError_t launch_select(const Shape& s, int mode, const uint16_t* q, const floa
                          const uint16_t* klabel, const int32_t* label_ch, const int32_t* ctx_len,
                          int32_t* blk_idx, int32_t* tok_idx, float* tok_score, uint32_t* sel_keys,
                          int32_t* sel_cnt, hipStream_t st, int32_t* blk_copy) {
-    int need = 1;
-    if (mode & 1) need = (s.nb_cap + SEL_THREADS - 1) / SEL_THREADS;
-    if (mode & 2) {
-        const int t = (s.kb * s.bs + SEL_THREADS - 1) / SEL_THREADS;
-        need = t > need ? t : need;
-    }
-    if (need <= 1) return launch_t<1>(s, mode, q, blk_score, klabel, label_ch, ctx_len, blk_idx, tok_idx, tok_score, sel_keys, sel_cnt, blk_copy, st);
-    if (need <= 2) return launch_t<2>(s, mode, q, blk_score, klabel, label_ch, ctx_len, blk_idx, tok_idx, tok_score, sel_keys, sel_cnt, blk_copy, st);
-    if (need <= 3) return launch_t<3>(s, mode, q, blk_score, klabel, label_ch, ctx_len, blk_idx, tok_idx, tok_score, sel_keys, sel_cnt, blk_copy, st);
-    if (need <= 4) return launch_t<4>(s, mode, q, blk_score, klabel, label_ch, ctx_len, blk_idx, tok_idx, tok_score, sel_keys, sel_cnt, blk_copy, st);
-    if (need <= 6) return launch_t<6>(s, mode, q, blk_score, klabel, label_ch, ctx_len, blk_idx, tok_idx, tok_score, sel_keys, sel_cnt, blk_copy, st);
-    return launch_t<8>(s, mode, q, blk_score, klabel, label_ch, ctx_len, blk_idx, tok_idx, tok_score, sel_keys, sel_cnt, blk_copy, st);
+    // key slots per thread of each top-k: the block scores (capacity) and
+    // the candidate tokens over the workgroup's threads; the pairs of the
+    // benchmark layers have their own instances (48k and 96k GQA, the
+    // latent layer, the offload capacity), other shapes round the larger
+    // count up to 1, 2, 3, 4, 6 or 8 for both
+    const int nb_need = (mode & 1) ? (s.nb_cap + SEL_THREADS - 1) / SEL_THREADS : 1;
+    const int nt_need = (mode & 2) ? (s.kb * s.bs + SEL_THREADS - 1) / SEL_THREADS : 1;
+#define HSAB_SEL_LAUNCH(B_, T_) \
+    return launch_t<B_, T_>(s, mode, q, blk_score, klabel, label_ch, ctx_len, blk_idx, tok_idx, tok_score, sel_keys, \
+                            sel_cnt, blk_copy, st)
+    if (nb_need == 3 && nt_need <= 2) HSAB_SEL_LAUNCH(3, 2);
+    if (nb_need == 6 && nt_need <= 2) HSAB_SEL_LAUNCH(6, 2);
+    if (nb_need == 6 && nt_need <= 4) HSAB_SEL_LAUNCH(6, 4);
+    if (nb_need <= 2 && nt_need > 2 && nt_need <= 4) HSAB_SEL_LAUNCH(2, 4);
+    const int need = nb_need > nt_need ? nb_need : nt_need;
+    if (need <= 1) HSAB_SEL_LAUNCH(1, 1);
+    if (need <= 2) HSAB_SEL_LAUNCH(2, 2);
+    if (need <= 3) HSAB_SEL_LAUNCH(3, 3);
+    if (need <= 4) HSAB_SEL_LAUNCH(4, 4);
+    if (need <= 6) HSAB_SEL_LAUNCH(6, 6);
+    HSAB_SEL_LAUNCH(8, 8);
+#undef HSAB_SEL_LAUNCH
 }
 
 }  // namespace hsab

@@ -24,6 +24,17 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) { return wave_sca
 // bin holds more than CMAX entries (or the value range is not a finite
 // positive fp32 number) the k-th largest key is found instead by bit-serial
 // refinement over all keys, two bits per round.
+// Scratch of a top-k selection by NW waves (independent of the keys per
+// thread, so selections of different sizes can share it).
+template <int NW>
+struct TopKSmem {
+    static constexpr int NBIN = 2048, CMAX = 1024;
+    uint32_t hist[NBIN];
+    uint32_t ckey[CMAX];
+    int32_t cidx[CMAX];
+    uint32_t red[15 * NW + 4];
+};
+
 template <int NW, int PT>
 struct TopK {
     static constexpr int NT = NW * 64;
@@ -35,12 +46,8 @@ struct TopK {
     // red: [0,8NW) round counts (two parity slots of 4NW), [8NW,10NW)
     // fallback tie counts, [10NW,11NW) compaction counts, [11NW,12NW) wave
     // bin totals, [12NW,15NW) wave min/max/count, then the candidate count.
-    struct Smem {
-        uint32_t hist[NBIN];
-        uint32_t ckey[CMAX];
-        int32_t cidx[CMAX];
-        uint32_t red[15 * NW + 4];
-    };
+    using Smem = TopKSmem<NW>;
+    static_assert(Smem::NBIN == NBIN && Smem::CMAX == CMAX, "scratch layout");
 
     template <typename Emit>
     __device__ static int select(const uint32_t (&key)[PT], int pt, int k, Smem& sm, Emit emit) {
