@@ -227,12 +227,16 @@ void attend_gqa_kernel(
 //    (within each 16-lane group, lane i receives element i % 4 of the 8
 //    bytes that lane 4j + i / 4 addressed). P enters as two bf16 terms
 //    (hi + lo) so the weights keep ~16 mantissa bits; V is exact in bf16.
-template <int DKMAX>
+// DKC, DVC: d_k and d_v fixed at compile time (0: taken from the arguments),
+// which turns the row-chunk divisions into multiplications
+template <int DKMAX, int DKC, int DVC>
 __global__ __launch_bounds__(256, 1) void attend_mla_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ K, const int32_t* __restrict__ tok_idx,
     const int32_t* __restrict__ ctx_len, const int32_t* __restrict__ slot_of, int n_slots, float* __restrict__ part_ml,
-    float* __restrict__ part_acc, int Hkv, int dk, int dv, int bs, int kt, int max_ctx, int nb_cap,
+    float* __restrict__ part_acc, int Hkv, int dk_arg, int dv_arg, int bs, int kt, int max_ctx, int nb_cap,
     int n_splits, int units, float scale2, int slot_rows, int rounds, int vsplit) {
+    static_assert(DKC == 0 || (DKC <= DKMAX && DKC % 32 == 0), "d_k");
+    const int dk = DKC ? DKC : dk_arg, dv = DVC ? DVC : dv_arg;
     constexpr int T = 32;                  // tokens per round
     constexpr int H = 32;                  // query heads per KV head
     constexpr int KSMAX = DKMAX / 32;      // logit steps
@@ -539,12 +543,16 @@ hipError_t launch_attend(const Shape& s, const uint16_t* q, const uint16_t* K, c
         // alone would leave CUs idle
         const int vs = (long)units * ns < 256 && s.dv >= 128 ? 2 : 1;
         const dim3 grid(((units + 7) / 8) * 8 * ns * vs);
-        if (s.dk <= 576)
-            hipLaunchKernelGGL(attend_mla_kernel<576>, grid, dim3(256), 0, st, q, K, tok_idx, ctx_len, slot_of, n_slots,
+        if (s.dk == 576 && s.dv == 512)   // the 512 + 64 latent layout
+            hipLaunchKernelGGL((attend_mla_kernel<576, 576, 512>), grid, dim3(256), 0, st, q, K, tok_idx, ctx_len,
+                               slot_of, n_slots, part_ml, part_acc, s.Hkv, s.dk, s.dv, s.bs, s.kt, s.max_ctx, s.nb_cap,
+                               ns, units, s.sm_scale * LOG2E, s.bs, MLA_TOK_PER_SPLIT / 32, vs);
+        else if (s.dk <= 576)
+            hipLaunchKernelGGL((attend_mla_kernel<576, 0, 0>), grid, dim3(256), 0, st, q, K, tok_idx, ctx_len, slot_of, n_slots,
                                part_ml, part_acc, s.Hkv, s.dk, s.dv, s.bs, s.kt, s.max_ctx, s.nb_cap, ns, units,
                                s.sm_scale * LOG2E, s.bs, MLA_TOK_PER_SPLIT / 32, vs);
         else
-            hipLaunchKernelGGL(attend_mla_kernel<1024>, grid, dim3(256), 0, st, q, K, tok_idx, ctx_len, slot_of, n_slots,
+            hipLaunchKernelGGL((attend_mla_kernel<1024, 0, 0>), grid, dim3(256), 0, st, q, K, tok_idx, ctx_len, slot_of, n_slots,
                                part_ml, part_acc, s.Hkv, s.dk, s.dv, s.bs, s.kt, s.max_ctx, s.nb_cap, ns, units,
                                s.sm_scale * LOG2E, s.bs, MLA_TOK_PER_SPLIT / 32, vs);
         e = hipGetLastError();
