@@ -47,7 +47,7 @@ constexpr int SEL_THREADS = SEL_WAVES * 64;
 // KK: channels per matrix step (16, or 32 when r >= 32); L8: label rows in
 // e4m3 bytes (half the bytes per load), widened exactly to bf16 at the
 // matrix step so the loads stay back to back
-template <int PTB, int PTT, int KK, bool L8>
+template <int PTB, int PTT, int KK, bool L8, bool KS1>
 __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
     int mode, const uint16_t* __restrict__ q, const float* __restrict__ blk_score,
     const uint16_t* __restrict__ klabel, const int32_t* __restrict__ label_ch,
@@ -90,7 +90,9 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
 #pragma unroll
         for (int j = 0; j < PTB; ++j) {
             const int i = (w * pt_b + j) * 64 + lane;
-            sraw[j] = (j < pt_b && i < nb_cap) ? __uint_as_float(ldg4_nt(S + i)) : 0.f;
+            // unconditional (clamped) load, masked afterwards
+            const float v = __uint_as_float(ldg4_nt(S + (i < nb_cap ? i : nb_cap - 1)));
+            sraw[j] = (j < pt_b && i < nb_cap) ? v : 0.f;
         }
     }
     int n = ctx_len[b];
@@ -104,7 +106,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
     // values requested here; they are stored to LDS after the block stage,
     // so their two dependent round trips overlap it
     const int MT = (Ge + 15) / 16;
-    const int KSr = r / KK;               // matrix steps per label row
+    const int KSr = KS1 ? 1 : r / KK;     // matrix steps per label row (KS1: r == KK)
     constexpr int CPL = KK / 4;           // channels per lane per step
     constexpr int SMAX = MAX_R / KK;      // step stride of the fragment table
     const int n_frag = (mode & 2) ? MT * KSr * 64 : 0;
@@ -321,12 +323,12 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
     for (int p = keff_t + threadIdx.x; p < kt; p += SEL_THREADS) to[p] = -1;
 }
 
-template <int PTB, int PTT, int KK, bool L8>
+template <int PTB, int PTT, int KK, bool L8, bool KS1>
 hipError_t launch_k(const Shape& s, dim3 grid, int mode, const uint16_t* q, const float* blk_score,
                     const uint16_t* klabel, const int32_t* label_ch, const int32_t* ctx_len, int32_t* blk_idx,
                     int32_t* tok_idx, float* tok_score, uint32_t* gkeys, int32_t* cnt, int32_t* blk_copy, int parts,
                     int units, int shift, hipStream_t st) {
-    hipLaunchKernelGGL((select_kernel<PTB, PTT, KK, L8>), grid, dim3(SEL_THREADS), 0, st, mode, q, blk_score, klabel,
+    hipLaunchKernelGGL((select_kernel<PTB, PTT, KK, L8, KS1>), grid, dim3(SEL_THREADS), 0, st, mode, q, blk_score, klabel,
                        label_ch, ctx_len, blk_idx, tok_idx, tok_score, gkeys, cnt, blk_copy, parts, units, s.heads, s.Hkv, s.G,
                        s.dk, s.bs, s.r, s.kb, s.kt, s.max_ctx, s.nb_cap, shift, s.agg_sum, s.sink, s.local);
     return hipGetLastError();
@@ -347,15 +349,19 @@ hipError_t launch_t(const Shape& s, int mode, const uint16_t* q, const float* bl
         while (parts < 32 && (long)parts * 2 * units <= 256 && parts * 2 * 8 <= n_tiles) parts *= 2;
     }
     const dim3 grid(((units + 7) / 8) * 8 * parts);
-    if (s.r >= 32)
-        return s.lab8 ? launch_k<PTB, PTT, 32, true>(s, grid, mode, q, blk_score, klabel, label_ch, ctx_len, blk_idx, tok_idx,
-                                               tok_score, gkeys, cnt, blk_copy, parts, units, shift, st)
-                      : launch_k<PTB, PTT, 32, false>(s, grid, mode, q, blk_score, klabel, label_ch, ctx_len, blk_idx,
-                                                tok_idx, tok_score, gkeys, cnt, blk_copy, parts, units, shift, st);
-    return s.lab8 ? launch_k<PTB, PTT, 16, true>(s, grid, mode, q, blk_score, klabel, label_ch, ctx_len, blk_idx, tok_idx,
-                                           tok_score, gkeys, cnt, blk_copy, parts, units, shift, st)
-                  : launch_k<PTB, PTT, 16, false>(s, grid, mode, q, blk_score, klabel, label_ch, ctx_len, blk_idx, tok_idx,
-                                            tok_score, gkeys, cnt, blk_copy, parts, units, shift, st);
+#define HSAB_SEL_K(KK_, L8_, KS1_) \
+    return launch_k<PTB, PTT, KK_, L8_, KS1_>(s, grid, mode, q, blk_score, klabel, label_ch, ctx_len, blk_idx, \
+                                             tok_idx, tok_score, gkeys, cnt, blk_copy, parts, units, shift, st)
+    // the benchmark layers' pairs also have instances for label rows of one
+    // matrix step (r == 16 or r == 32)
+    if constexpr (PTB != PTT) {
+        if (s.r == 32) { if (s.lab8) HSAB_SEL_K(32, true, true); HSAB_SEL_K(32, false, true); }
+        if (s.r == 16) { if (s.lab8) HSAB_SEL_K(16, true, true); HSAB_SEL_K(16, false, true); }
+    }
+    if (s.r >= 32) { if (s.lab8) HSAB_SEL_K(32, true, false); HSAB_SEL_K(32, false, false); }
+    if (s.lab8) HSAB_SEL_K(16, true, false);
+    HSAB_SEL_K(16, false, false);
+#undef HSAB_SEL_K
 }
 
 }  // namespace
