@@ -47,7 +47,9 @@ constexpr int SEL_THREADS = SEL_WAVES * 64;
 // KK: channels per matrix step (16, or 32 when r >= 32); L8: label rows in
 // e4m3 bytes (half the bytes per load), widened exactly to bf16 at the
 // matrix step so the loads stay back to back
-template <int PTB, int PTT, int KK, bool L8, bool KS1>
+// SPEC: 0 generic; 1 label rows of one matrix step (r == KK); 2 as 1, and
+// the block scores and candidates fill exactly PTB and PTT slots per thread
+template <int PTB, int PTT, int KK, bool L8, int SPEC>
 __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
     int mode, const uint16_t* __restrict__ q, const float* __restrict__ blk_score,
     const uint16_t* __restrict__ klabel, const int32_t* __restrict__ label_ch,
@@ -83,7 +85,8 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
     // block scores are loaded over the whole capacity in the same round trip
     // as ctx_len and masked once n is known; the entry layout of the block
     // selection uses the capacity's slot count
-    const int pt_b = (nb_cap + SEL_THREADS - 1) / SEL_THREADS;
+    constexpr bool KS1 = SPEC >= 1, EXACT = SPEC == 2;
+    const int pt_b = EXACT ? PTB : (nb_cap + SEL_THREADS - 1) / SEL_THREADS;
     float sraw[PTB];
     if (mode & 1) {
         const float* S = blk_score + (size_t)sel * nb_cap;
@@ -267,7 +270,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
         }
     }
     // ----------------------------------------------------------- top-K_t
-    const int pt = (ncand + SEL_THREADS - 1) / SEL_THREADS;
+    const int pt = EXACT ? PTT : (ncand + SEL_THREADS - 1) / SEL_THREADS;
     uint32_t key[PTT];
     if (parts > 1) {
         // the barrier puts the arrival after every wave's key stores. Every
@@ -323,12 +326,12 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
     for (int p = keff_t + threadIdx.x; p < kt; p += SEL_THREADS) to[p] = -1;
 }
 
-template <int PTB, int PTT, int KK, bool L8, bool KS1>
+template <int PTB, int PTT, int KK, bool L8, int SPEC>
 hipError_t launch_k(const Shape& s, dim3 grid, int mode, const uint16_t* q, const float* blk_score,
                     const uint16_t* klabel, const int32_t* label_ch, const int32_t* ctx_len, int32_t* blk_idx,
                     int32_t* tok_idx, float* tok_score, uint32_t* gkeys, int32_t* cnt, int32_t* blk_copy, int parts,
                     int units, int shift, hipStream_t st) {
-    hipLaunchKernelGGL((select_kernel<PTB, PTT, KK, L8, KS1>), grid, dim3(SEL_THREADS), 0, st, mode, q, blk_score, klabel,
+    hipLaunchKernelGGL((select_kernel<PTB, PTT, KK, L8, SPEC>), grid, dim3(SEL_THREADS), 0, st, mode, q, blk_score, klabel,
                        label_ch, ctx_len, blk_idx, tok_idx, tok_score, gkeys, cnt, blk_copy, parts, units, s.heads, s.Hkv, s.G,
                        s.dk, s.bs, s.r, s.kb, s.kt, s.max_ctx, s.nb_cap, shift, s.agg_sum, s.sink, s.local);
     return hipGetLastError();
@@ -349,18 +352,29 @@ hipError_t launch_t(const Shape& s, int mode, const uint16_t* q, const float* bl
         while (parts < 32 && (long)parts * 2 * units <= 256 && parts * 2 * 8 <= n_tiles) parts *= 2;
     }
     const dim3 grid(((units + 7) / 8) * 8 * parts);
-#define HSAB_SEL_K(KK_, L8_, KS1_) \
-    return launch_k<PTB, PTT, KK_, L8_, KS1_>(s, grid, mode, q, blk_score, klabel, label_ch, ctx_len, blk_idx, \
+#define HSAB_SEL_K(KK_, L8_, SPEC_) \
+    return launch_k<PTB, PTT, KK_, L8_, SPEC_>(s, grid, mode, q, blk_score, klabel, label_ch, ctx_len, blk_idx, \
                                              tok_idx, tok_score, gkeys, cnt, blk_copy, parts, units, shift, st)
     // the benchmark layers' pairs also have instances for label rows of one
     // matrix step (r == 16 or r == 32)
+    // (and, when the slot counts are exact, with them fixed)
     if constexpr (PTB != PTT) {
-        if (s.r == 32) { if (s.lab8) HSAB_SEL_K(32, true, true); HSAB_SEL_K(32, false, true); }
-        if (s.r == 16) { if (s.lab8) HSAB_SEL_K(16, true, true); HSAB_SEL_K(16, false, true); }
+        const bool ex = (!(mode & 1) || (s.nb_cap + SEL_THREADS - 1) / SEL_THREADS == PTB) &&
+                        (!(mode & 2) || (s.kb * s.bs + SEL_THREADS - 1) / SEL_THREADS == PTT);
+        if (s.r == 32) {
+            if (ex) { if (s.lab8) HSAB_SEL_K(32, true, 2); HSAB_SEL_K(32, false, 2); }
+            if (s.lab8) HSAB_SEL_K(32, true, 1);
+            HSAB_SEL_K(32, false, 1);
+        }
+        if (s.r == 16) {
+            if (ex) { if (s.lab8) HSAB_SEL_K(16, true, 2); HSAB_SEL_K(16, false, 2); }
+            if (s.lab8) HSAB_SEL_K(16, true, 1);
+            HSAB_SEL_K(16, false, 1);
+        }
     }
-    if (s.r >= 32) { if (s.lab8) HSAB_SEL_K(32, true, false); HSAB_SEL_K(32, false, false); }
-    if (s.lab8) HSAB_SEL_K(16, true, false);
-    HSAB_SEL_K(16, false, false);
+    if (s.r >= 32) { if (s.lab8) HSAB_SEL_K(32, true, 0); HSAB_SEL_K(32, false, 0); }
+    if (s.lab8) HSAB_SEL_K(16, true, 0);
+    HSAB_SEL_K(16, false, 0);
 #undef HSAB_SEL_K
 }
 
