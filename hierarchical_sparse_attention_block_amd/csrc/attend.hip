@@ -229,14 +229,19 @@ void attend_gqa_kernel(
 //    (hi + lo) so the weights keep ~16 mantissa bits; V is exact in bf16.
 // DKC, DVC: d_k and d_v fixed at compile time (0: taken from the arguments),
 // which turns the row-chunk divisions into multiplications
-template <int DKMAX, int DKC, int DVC>
+template <int DKMAX, int DKC, int DVC, int VS>
 __global__ __launch_bounds__(256, 1) void attend_mla_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ K, const int32_t* __restrict__ tok_idx,
     const int32_t* __restrict__ ctx_len, const int32_t* __restrict__ slot_of, int n_slots, float* __restrict__ part_ml,
     float* __restrict__ part_acc, int Hkv, int dk_arg, int dv_arg, int bs, int kt, int max_ctx, int nb_cap,
-    int n_splits, int units, float scale2, int slot_rows, int rounds, int vsplit) {
+    int n_splits, int units, float scale2, int slot_rows, int rounds_arg, int vsplit_arg) {
     static_assert(DKC == 0 || (DKC <= DKMAX && DKC % 32 == 0), "d_k");
     const int dk = DKC ? DKC : dk_arg, dv = DVC ? DVC : dv_arg;
+    // VS: workgroups per split fixed at compile time (0: from the argument);
+    // the rounds per split are always MLA_TOK_PER_SPLIT / 32
+    const int vsplit = VS ? VS : vsplit_arg;
+    constexpr int rounds = MLA_TOK_PER_SPLIT / 32;
+    (void)rounds_arg;
     constexpr int T = 32;                  // tokens per round
     constexpr int H = 32;                  // query heads per KV head
     constexpr int KSMAX = DKMAX / 32;      // logit steps
@@ -543,16 +548,20 @@ hipError_t launch_attend(const Shape& s, const uint16_t* q, const uint16_t* K, c
         // alone would leave CUs idle
         const int vs = (long)units * ns < 256 && s.dv >= 128 ? 2 : 1;
         const dim3 grid(((units + 7) / 8) * 8 * ns * vs);
-        if (s.dk == 576 && s.dv == 512)   // the 512 + 64 latent layout
-            hipLaunchKernelGGL((attend_mla_kernel<576, 576, 512>), grid, dim3(256), 0, st, q, K, tok_idx, ctx_len,
+        if (s.dk == 576 && s.dv == 512 && vs == 2)   // the 512 + 64 latent layout
+            hipLaunchKernelGGL((attend_mla_kernel<576, 576, 512, 2>), grid, dim3(256), 0, st, q, K, tok_idx, ctx_len,
+                               slot_of, n_slots, part_ml, part_acc, s.Hkv, s.dk, s.dv, s.bs, s.kt, s.max_ctx, s.nb_cap,
+                               ns, units, s.sm_scale * LOG2E, s.bs, MLA_TOK_PER_SPLIT / 32, vs);
+        else if (s.dk == 576 && s.dv == 512)
+            hipLaunchKernelGGL((attend_mla_kernel<576, 576, 512, 0>), grid, dim3(256), 0, st, q, K, tok_idx, ctx_len,
                                slot_of, n_slots, part_ml, part_acc, s.Hkv, s.dk, s.dv, s.bs, s.kt, s.max_ctx, s.nb_cap,
                                ns, units, s.sm_scale * LOG2E, s.bs, MLA_TOK_PER_SPLIT / 32, vs);
         else if (s.dk <= 576)
-            hipLaunchKernelGGL((attend_mla_kernel<576, 0, 0>), grid, dim3(256), 0, st, q, K, tok_idx, ctx_len, slot_of, n_slots,
+            hipLaunchKernelGGL((attend_mla_kernel<576, 0, 0, 0>), grid, dim3(256), 0, st, q, K, tok_idx, ctx_len, slot_of, n_slots,
                                part_ml, part_acc, s.Hkv, s.dk, s.dv, s.bs, s.kt, s.max_ctx, s.nb_cap, ns, units,
                                s.sm_scale * LOG2E, s.bs, MLA_TOK_PER_SPLIT / 32, vs);
         else
-            hipLaunchKernelGGL((attend_mla_kernel<1024, 0, 0>), grid, dim3(256), 0, st, q, K, tok_idx, ctx_len, slot_of, n_slots,
+            hipLaunchKernelGGL((attend_mla_kernel<1024, 0, 0, 0>), grid, dim3(256), 0, st, q, K, tok_idx, ctx_len, slot_of, n_slots,
                                part_ml, part_acc, s.Hkv, s.dk, s.dv, s.bs, s.kt, s.max_ctx, s.nb_cap, ns, units,
                                s.sm_scale * LOG2E, s.bs, MLA_TOK_PER_SPLIT / 32, vs);
         e = hipGetLastError();
