@@ -421,9 +421,13 @@ __global__ __launch_bounds__(256, 1) void attend_mla_kernel(
 // grid: (B*Hq). Merges the split partials of one query head. The (max,
 // sum) pairs and the accumulator rows of a chunk of eight splits are all
 // loaded before any arithmetic, so a chunk costs one memory round trip.
+// DVC, NSC: d_v and the split count fixed at compile time (0: from the
+// arguments)
+template <int DVC, int NSC>
 __global__ __launch_bounds__(256) void combine_kernel(
     const float* __restrict__ part_ml, const float* __restrict__ part_acc, float* __restrict__ out,
-    float* __restrict__ lse, int dv, int n_splits) {
+    float* __restrict__ lse, int dv_arg, int n_splits_arg) {
+    const int dv = DVC ? DVC : dv_arg, n_splits = NSC ? NSC : n_splits_arg;
     constexpr int CH = 8;
     const size_t bh = blockIdx.x;
     const float* ml = part_ml + bh * n_splits * 2;
@@ -522,7 +526,18 @@ bool mla_shape(const Shape& s) {
 
 hipError_t launch_combine(const Shape& s, const float* part_ml, const float* part_acc, float* out, float* lse,
                           int n_splits, hipStream_t st) {
-    hipLaunchKernelGGL(combine_kernel, dim3(s.B * s.Hq), dim3(s.dv < 256 ? 128 : 256), 0, st, part_ml, part_acc,
+    // the benchmark layers' merges: 8 splits of 128 values, 16 of 512
+    if (s.dv == 128 && n_splits == 8) {
+        hipLaunchKernelGGL((combine_kernel<128, 8>), dim3(s.B * s.Hq), dim3(128), 0, st, part_ml, part_acc, out, lse,
+                           s.dv, n_splits);
+        return hipGetLastError();
+    }
+    if (s.dv == 512 && n_splits == 16) {
+        hipLaunchKernelGGL((combine_kernel<512, 16>), dim3(s.B * s.Hq), dim3(256), 0, st, part_ml, part_acc, out, lse,
+                           s.dv, n_splits);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL((combine_kernel<0, 0>), dim3(s.B * s.Hq), dim3(s.dv < 256 ? 128 : 256), 0, st, part_ml, part_acc,
                        out, lse, s.dv, n_splits);
     return hipGetLastError();
 }
@@ -574,9 +589,7 @@ hipError_t launch_attend(const Shape& s, const uint16_t* q, const uint16_t* K, c
         }
     }
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(combine_kernel, dim3(s.B * s.Hq), dim3(s.dv < 256 ? 128 : 256), 0, st, part_ml,
-                       part_acc, out, lse, s.dv, ns);
-    return hipGetLastError();
+    return launch_combine(s, part_ml, part_acc, out, lse, ns, st);
 }
 
 }  // namespace hsab
