@@ -48,15 +48,16 @@ constexpr int SEL_THREADS = SEL_WAVES * 64;
 // e4m3 bytes (half the bytes per load), widened exactly to bf16 at the
 // matrix step so the loads stay back to back
 // SPEC: 0 generic; 1 label rows of one matrix step (r == KK); 2 as 1, and
-// the block scores and candidates fill exactly PTB and PTT slots per thread
-template <int PTB, int PTT, int KK, bool L8, int SPEC>
+// the block scores and candidates fill exactly PTB and PTT slots per
+// thread. GC: the group size fixed at compile time (0: from the argument).
+template <int PTB, int PTT, int KK, bool L8, int SPEC, int GC>
 __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
     int mode, const uint16_t* __restrict__ q, const float* __restrict__ blk_score,
     const uint16_t* __restrict__ klabel, const int32_t* __restrict__ label_ch,
     const int32_t* __restrict__ ctx_len, int32_t* __restrict__ blk_idx, int32_t* __restrict__ tok_idx,
     float* __restrict__ tok_score, uint32_t* __restrict__ gkeys, int32_t* __restrict__ cnt,
     int32_t* __restrict__ blk_copy, int parts,
-    int units, int heads, int Hkv, int G, int dk, int bs, int r, int kb, int kt, int max_ctx, int nb_cap,
+    int units, int heads, int Hkv, int G_arg, int dk, int bs, int r, int kb, int kt, int max_ctx, int nb_cap,
     int bs_shift, int agg_sum, int sink, int local) {
     // PTB / PTT: key slots per thread of the block / token top-k
     using SelB = TopK<SEL_WAVES, PTB>;
@@ -80,6 +81,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
     if (sel >= units) return;
     const int unit = sel / heads, hsel = sel - unit * heads;
     const int b = unit / Hkv, g = unit % Hkv;
+    const int G = GC ? GC : G_arg;
     const int Ge = heads > 1 ? 1 : G;   // query heads scored together
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     // block scores are loaded over the whole capacity in the same round trip
@@ -326,12 +328,12 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
     for (int p = keff_t + threadIdx.x; p < kt; p += SEL_THREADS) to[p] = -1;
 }
 
-template <int PTB, int PTT, int KK, bool L8, int SPEC>
+template <int PTB, int PTT, int KK, bool L8, int SPEC, int GC>
 hipError_t launch_k(const Shape& s, dim3 grid, int mode, const uint16_t* q, const float* blk_score,
                     const uint16_t* klabel, const int32_t* label_ch, const int32_t* ctx_len, int32_t* blk_idx,
                     int32_t* tok_idx, float* tok_score, uint32_t* gkeys, int32_t* cnt, int32_t* blk_copy, int parts,
                     int units, int shift, hipStream_t st) {
-    hipLaunchKernelGGL((select_kernel<PTB, PTT, KK, L8, SPEC>), grid, dim3(SEL_THREADS), 0, st, mode, q, blk_score, klabel,
+    hipLaunchKernelGGL((select_kernel<PTB, PTT, KK, L8, SPEC, GC>), grid, dim3(SEL_THREADS), 0, st, mode, q, blk_score, klabel,
                        label_ch, ctx_len, blk_idx, tok_idx, tok_score, gkeys, cnt, blk_copy, parts, units, s.heads, s.Hkv, s.G,
                        s.dk, s.bs, s.r, s.kb, s.kt, s.max_ctx, s.nb_cap, shift, s.agg_sum, s.sink, s.local);
     return hipGetLastError();
@@ -352,29 +354,31 @@ hipError_t launch_t(const Shape& s, int mode, const uint16_t* q, const float* bl
         while (parts < 32 && (long)parts * 2 * units <= 256 && parts * 2 * 8 <= n_tiles) parts *= 2;
     }
     const dim3 grid(((units + 7) / 8) * 8 * parts);
-#define HSAB_SEL_K(KK_, L8_, SPEC_) \
-    return launch_k<PTB, PTT, KK_, L8_, SPEC_>(s, grid, mode, q, blk_score, klabel, label_ch, ctx_len, blk_idx, \
+#define HSAB_SEL_K(KK_, L8_, SPEC_, GC_) \
+    return launch_k<PTB, PTT, KK_, L8_, SPEC_, GC_>(s, grid, mode, q, blk_score, klabel, label_ch, ctx_len, blk_idx, \
                                              tok_idx, tok_score, gkeys, cnt, blk_copy, parts, units, shift, st)
     // the benchmark layers' pairs also have instances for label rows of one
     // matrix step (r == 16 or r == 32)
-    // (and, when the slot counts are exact, with them fixed)
+    // (and, when the slot counts are exact and the group is the layer's,
+    // 32 query heads on the latent pair, 4 on the others, with both fixed)
     if constexpr (PTB != PTT) {
-        const bool ex = (!(mode & 1) || (s.nb_cap + SEL_THREADS - 1) / SEL_THREADS == PTB) &&
+        constexpr int GP = PTB == 2 && PTT == 4 ? 32 : 4;
+        const bool ex = s.G == GP && (!(mode & 1) || (s.nb_cap + SEL_THREADS - 1) / SEL_THREADS == PTB) &&
                         (!(mode & 2) || (s.kb * s.bs + SEL_THREADS - 1) / SEL_THREADS == PTT);
         if (s.r == 32) {
-            if (ex) { if (s.lab8) HSAB_SEL_K(32, true, 2); HSAB_SEL_K(32, false, 2); }
-            if (s.lab8) HSAB_SEL_K(32, true, 1);
-            HSAB_SEL_K(32, false, 1);
+            if (ex) { if (s.lab8) HSAB_SEL_K(32, true, 2, GP); HSAB_SEL_K(32, false, 2, GP); }
+            if (s.lab8) HSAB_SEL_K(32, true, 1, 0);
+            HSAB_SEL_K(32, false, 1, 0);
         }
         if (s.r == 16) {
-            if (ex) { if (s.lab8) HSAB_SEL_K(16, true, 2); HSAB_SEL_K(16, false, 2); }
-            if (s.lab8) HSAB_SEL_K(16, true, 1);
-            HSAB_SEL_K(16, false, 1);
+            if (ex) { if (s.lab8) HSAB_SEL_K(16, true, 2, GP); HSAB_SEL_K(16, false, 2, GP); }
+            if (s.lab8) HSAB_SEL_K(16, true, 1, 0);
+            HSAB_SEL_K(16, false, 1, 0);
         }
     }
-    if (s.r >= 32) { if (s.lab8) HSAB_SEL_K(32, true, 0); HSAB_SEL_K(32, false, 0); }
-    if (s.lab8) HSAB_SEL_K(16, true, 0);
-    HSAB_SEL_K(16, false, 0);
+    if (s.r >= 32) { if (s.lab8) HSAB_SEL_K(32, true, 0, 0); HSAB_SEL_K(32, false, 0, 0); }
+    if (s.lab8) HSAB_SEL_K(16, true, 0, 0);
+    HSAB_SEL_K(16, false, 0, 0);
 #undef HSAB_SEL_K
 }
 
