@@ -57,13 +57,17 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
     const int32_t* __restrict__ ctx_len, int32_t* __restrict__ blk_idx, int32_t* __restrict__ tok_idx,
     float* __restrict__ tok_score, uint32_t* __restrict__ gkeys, int32_t* __restrict__ cnt,
     int32_t* __restrict__ blk_copy, int parts,
-    int units, int heads, int Hkv, int G_arg, int dk, int bs, int r, int kb, int kt, int max_ctx, int nb_cap,
+    int units, int heads, int Hkv, int G_arg, int dk, int bs_arg, int r_arg, int kb, int kt, int max_ctx, int nb_cap,
     int bs_shift, int agg_sum, int sink, int local) {
     // PTB / PTT: key slots per thread of the block / token top-k
     using SelB = TopK<SEL_WAVES, PTB>;
     using SelT = TopK<SEL_WAVES, PTT>;
+    // the benchmark layers' instances (SPEC 2) also fix the block size (16
+    // with groups of 4, 32 on the latent layer); SPEC >= 1 has r == KK
+    constexpr int BSC = SPEC == 2 ? (GC == 32 ? 32 : 16) : 0;
+    const int bs = BSC ? BSC : bs_arg, r = SPEC >= 1 ? KK : r_arg;
     // candidate i sits in slot i / bs of the block list (a shift when bs is a power of two)
-    auto slot_of = [&](int i) { return bs_shift >= 0 ? (i >> bs_shift) : i / bs; };
+    auto slot_of = [&](int i) { return BSC ? i / BSC : (bs_shift >= 0 ? (i >> bs_shift) : i / bs); };
     __shared__ uint32_t s_key[MAX_CAND];
     __shared__ int32_t s_blk[MAX_KB];
     // A fragments [head tile][step][lane]: uint2 per lane for KK = 16,
@@ -359,11 +363,12 @@ hipError_t launch_t(const Shape& s, int mode, const uint16_t* q, const float* bl
                                              tok_idx, tok_score, gkeys, cnt, blk_copy, parts, units, shift, st)
     // the benchmark layers' pairs also have instances for label rows of one
     // matrix step (r == 16 or r == 32)
-    // (and, when the slot counts are exact and the group is the layer's,
-    // 32 query heads on the latent pair, 4 on the others, with both fixed)
+    // (and, when the slot counts are exact and the group and block size are
+    // the layer's, 32 query heads and 32-token blocks on the latent pair, 4
+    // and 16 on the others, with all of them fixed)
     if constexpr (PTB != PTT) {
         constexpr int GP = PTB == 2 && PTT == 4 ? 32 : 4;
-        const bool ex = s.G == GP && (!(mode & 1) || (s.nb_cap + SEL_THREADS - 1) / SEL_THREADS == PTB) &&
+        const bool ex = s.G == GP && s.bs == (GP == 32 ? 32 : 16) && (!(mode & 1) || (s.nb_cap + SEL_THREADS - 1) / SEL_THREADS == PTB) &&
                         (!(mode & 2) || (s.kb * s.bs + SEL_THREADS - 1) / SEL_THREADS == PTT);
         if (s.r == 32) {
             if (ex) { if (s.lab8) HSAB_SEL_K(32, true, 2, GP); HSAB_SEL_K(32, false, 2, GP); }
