@@ -39,14 +39,17 @@ namespace {
 
 // MASKED: the token list is the union of the heads' own token sets (per-head
 // selection) and tok_mask gives, per entry, the heads that attend it.
-template <int D, int G, bool MASKED, int TPS>
+// NSC: the split count fixed at compile time (the list then holds exactly
+// NSC * TPS entries); 0: from the arguments
+template <int D, int G, bool MASKED, int TPS, int NSC>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TPS == 128 && G <= 4 ? 4 : 1)))
 void attend_gqa_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const int32_t* __restrict__ tok_idx, const uint32_t* __restrict__ tok_mask,
     const int32_t* __restrict__ ctx_len, const int32_t* __restrict__ slot_of, int n_slots,
-    float* __restrict__ part_ml, float* __restrict__ part_acc, int Hkv, int bs, int kt,
-    int max_ctx, int nb_cap, int n_splits, int units, float scale2, int slot_rows) {
+    float* __restrict__ part_ml, float* __restrict__ part_acc, int Hkv, int bs, int kt_arg,
+    int max_ctx, int nb_cap, int n_splits_arg, int units, float scale2, int slot_rows) {
+    const int n_splits = NSC ? NSC : n_splits_arg, kt = NSC ? NSC * TPS : kt_arg;
     constexpr int LPT = D / 8;                         // lanes per token (8 channels each)
     constexpr int TPI = 64 / LPT;                      // tokens per wave load = lane groups per wave
     constexpr int TPW = TPS / 4;                       // tokens per wave
@@ -482,11 +485,15 @@ hipError_t launch_gqa_tps(const Shape& s, const uint16_t* q, const uint16_t* K, 
     if (unit_rows * D * 2 > 0xffffffffull) return hipErrorInvalidValue;
     const dim3 grid(((units + 7) / 8) * 8 * ns);
     if (tok_mask)
-        hipLaunchKernelGGL((attend_gqa_kernel<D, G, true, TPS>), grid, dim3(256), 0, st, q, K, V, tok_idx, tok_mask,
+        hipLaunchKernelGGL((attend_gqa_kernel<D, G, true, TPS, 0>), grid, dim3(256), 0, st, q, K, V, tok_idx, tok_mask,
+                           ctx_len, slot_of, n_slots, part_ml, part_acc, s.Hkv, s.bs, list_len, s.max_ctx, s.nb_cap,
+                           ns, units, s.sm_scale * LOG2E, 2 * s.bs);
+    else if (ns == 8 && list_len == 8 * TPS)   // the 48k and 96k layers: 8 splits
+        hipLaunchKernelGGL((attend_gqa_kernel<D, G, false, TPS, 8>), grid, dim3(256), 0, st, q, K, V, tok_idx, tok_mask,
                            ctx_len, slot_of, n_slots, part_ml, part_acc, s.Hkv, s.bs, list_len, s.max_ctx, s.nb_cap,
                            ns, units, s.sm_scale * LOG2E, 2 * s.bs);
     else
-        hipLaunchKernelGGL((attend_gqa_kernel<D, G, false, TPS>), grid, dim3(256), 0, st, q, K, V, tok_idx, tok_mask,
+        hipLaunchKernelGGL((attend_gqa_kernel<D, G, false, TPS, 0>), grid, dim3(256), 0, st, q, K, V, tok_idx, tok_mask,
                            ctx_len, slot_of, n_slots, part_ml, part_acc, s.Hkv, s.bs, list_len, s.max_ctx, s.nb_cap,
                            ns, units, s.sm_scale * LOG2E, 2 * s.bs);
     return hipGetLastError();

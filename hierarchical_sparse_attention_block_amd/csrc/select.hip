@@ -57,7 +57,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
     const int32_t* __restrict__ ctx_len, int32_t* __restrict__ blk_idx, int32_t* __restrict__ tok_idx,
     float* __restrict__ tok_score, uint32_t* __restrict__ gkeys, int32_t* __restrict__ cnt,
     int32_t* __restrict__ blk_copy, int parts,
-    int units, int heads, int Hkv, int G_arg, int dk, int bs_arg, int r_arg, int kb, int kt, int max_ctx, int nb_cap,
+    int units, int heads, int Hkv, int G_arg, int dk, int bs_arg, int r_arg, int kb_arg, int kt, int max_ctx, int nb_cap_arg,
     int bs_shift, int agg_sum, int sink, int local) {
     // PTB / PTT: key slots per thread of the block / token top-k
     using SelB = TopK<SEL_WAVES, PTB>;
@@ -66,6 +66,9 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(
     // with groups of 4, 32 on the latent layer); SPEC >= 1 has r == KK
     constexpr int BSC = SPEC == 2 ? (GC == 32 ? 32 : 16) : 0;
     const int bs = BSC ? BSC : bs_arg, r = SPEC >= 1 ? KK : r_arg;
+    // SPEC 2 also has exactly PTB * 1024 block slots and PTT * 1024 candidates
+    const int nb_cap = SPEC == 2 ? PTB * SEL_THREADS : nb_cap_arg;
+    const int kb = SPEC == 2 ? PTT * SEL_THREADS / BSC : kb_arg;
     // candidate i sits in slot i / bs of the block list (a shift when bs is a power of two)
     auto slot_of = [&](int i) { return BSC ? i / BSC : (bs_shift >= 0 ? (i >> bs_shift) : i / bs); };
     __shared__ uint32_t s_key[MAX_CAND];
@@ -368,7 +371,8 @@ hipError_t launch_t(const Shape& s, int mode, const uint16_t* q, const float* bl
     // and 16 on the others, with all of them fixed)
     if constexpr (PTB != PTT) {
         constexpr int GP = PTB == 2 && PTT == 4 ? 32 : 4;
-        const bool ex = s.G == GP && s.bs == (GP == 32 ? 32 : 16) && (!(mode & 1) || (s.nb_cap + SEL_THREADS - 1) / SEL_THREADS == PTB) &&
+        const bool ex = s.G == GP && s.bs == (GP == 32 ? 32 : 16) && s.nb_cap == PTB * SEL_THREADS &&
+                        s.kb * s.bs == PTT * SEL_THREADS && (!(mode & 1) || (s.nb_cap + SEL_THREADS - 1) / SEL_THREADS == PTB) &&
                         (!(mode & 2) || (s.kb * s.bs + SEL_THREADS - 1) / SEL_THREADS == PTT);
         if (s.r == 32) {
             if (ex) { if (s.lab8) HSAB_SEL_K(32, true, 2, GP); HSAB_SEL_K(32, false, 2, GP); }
